@@ -1,0 +1,127 @@
+"""One AdaHOP GEMM call, composed from the oracle's steps.
+
+TEST INFRASTRUCTURE ONLY (see ``oracle/__init__.py``).
+
+Follows the four-stage pipeline of "AdaHOP: Fast and Accurate Low-Precision
+Training via Outlier-Pattern-Aware Rotation" (arXiv 2604.02525), Fig. 9 and
+the appendix list of its kernels: FOID picks the outlier lines; the residual
+(those lines zeroed) is rotated by the 32-point IHT along the inner dimension
+and quantized to MXFP4; the residual product runs on the dequantized operands;
+the outlier product runs in high precision on the extracted bf16 lines and is
+scatter-added into the result. Fig. 5 fixes which product each pattern pair
+gets.
+
+Frames. A linear layer Y = X W^T has three products (Table 1's columns):
+  FWD   C = Y  [T, Dout]  = A B with A = X [T,Din],     B = W^T,  K = Din
+  DGRAD C = dX [T, Din]   = A B with A = GY [T,Dout],   B = W,    K = Dout
+  WGRAD C = dW [Dout,Din] = A B with A = GY^T,          B = X,    K = T
+Packed operands are K-contiguous: A as [m][K], B as [n][K].
+"""
+import numpy as np
+
+from . import (COLS, ROWS, dequant, foid, gemm_bf16, gemm_mx, iht_quant, route as
+               route_of, scan_target)
+
+# Per op: (m, n, K) from (T, Din, Dout); the axis of each stored tensor that the
+# contraction runs along; and whether the textbook operand is the stored tensor
+# transposed.
+_SHAPES = {
+    "FWD": lambda T, Din, Dout: (T, Dout, Din),
+    "DGRAD": lambda T, Din, Dout: (T, Din, Dout),
+    "WGRAD": lambda T, Din, Dout: (Dout, Din, T),
+}
+_CONTRACT = {"FWD": (COLS, COLS), "DGRAD": (COLS, ROWS), "WGRAD": (ROWS, ROWS)}
+# A(i,t) = lhs[i,t] unless a_trans; B(t,j) = rhs[t,j] unless b_trans.
+_TRANS = {"FWD": (0, 1), "DGRAD": (0, 0), "WGRAD": (1, 0)}
+
+
+def gemm(op, lhs, rhs, T, Din, Dout, pat_lhs="N", pat_rhs="N", route=None, k=64,
+         rows=None, cols=None, probe=64):
+    """Reference result of one call on outputs rows x cols (all if None).
+
+    Returns a dict with the route, the FOID indices, the packed operands A and
+    B (codes, scales), the gathered bf16 lines, C (fp64) and absC (the sum of
+    |products| per output, used for the accumulation-error bound).
+    """
+    lhs = np.ascontiguousarray(lhs)
+    rhs = np.ascontiguousarray(rhs)
+    m, n, K = _SHAPES[op](T, Din, Dout)
+    r = route or route_of(op, pat_lhs, pat_rhs)
+    rows = np.arange(m, dtype=np.int64) if rows is None else np.asarray(rows, dtype=np.int64)
+    cols = np.arange(n, dtype=np.int64) if cols is None else np.asarray(cols, dtype=np.int64)
+    a_trans, b_trans = _TRANS[op]
+    out = {"route": r, "m": m, "n": n, "K": K, "idx": None,
+           "a_gathered": None, "b_gathered": None}
+
+    if r == "BF16":
+        # Both operands hurt: the plain high-precision product (Fig. 5).
+        C, absC = gemm_bf16(lhs, a_trans, rhs, b_trans, K, rows, cols)
+        out.update(C=C, absC=absC)
+        return out
+
+    # Stage 1, FOID: which stored tensor and axis hold the extracted lines.
+    zero = {0: None, 1: None}           # tensor -> (idx, axis)
+    if r in ("OE_LEFT", "OE_RIGHT", "OE_INNER"):
+        tensor, axis = scan_target(op, r)
+        idx = foid(lhs if tensor == 0 else rhs, axis, k, probe)
+        out["idx"] = idx
+        zero[tensor] = (idx, axis)
+        if r == "OE_INNER":
+            # The matching inner lines of the other operand leave the residual too.
+            # Inner lines of the rhs are indexed along its contraction axis.
+            zero[1] = (idx, _CONTRACT[op][1])
+
+    # Stage 2, IHT + MXFP4 quantization of both residuals.
+    had = 0 if r == "MXFP4" else 32
+    packed = []
+    for t, src in ((0, lhs), (1, rhs)):
+        z = zero[t]
+        codes, scales, gathered = iht_quant(src, _CONTRACT[op][t], had,
+                                            None if z is None else z[0],
+                                            ROWS if z is None else z[1])
+        packed.append((codes, scales))
+        out["a_gathered" if t == 0 else "b_gathered"] = gathered
+    (ac, as_), (bc, bs) = packed
+    out.update(a_codes=ac, a_scales=as_, b_codes=bc, b_scales=bs)
+
+    # Stage 3, the residual product on the dequantized operands.
+    C, absC = gemm_mx(ac, as_, bc, bs, rows, cols)
+
+    # Stage 3 (outlier half) + stage 4: the bf16 outlier product, scatter-added.
+    idx = out["idx"]
+    if r == "OE_LEFT":
+        # Rows idx of A, gathered as A-rows: A_g(p,t).
+        g = out["a_gathered"]
+        g_trans = 1 if op == "WGRAD" else 0     # GY columns come as [T][k]
+        hit = np.nonzero(np.isin(rows, idx))[0]
+        if hit.size:
+            pos = np.searchsorted(idx, rows[hit])
+            oe, oabs = gemm_bf16(g, g_trans, rhs, b_trans, K, pos, cols)
+            C[hit, :] += oe
+            absC[hit, :] += oabs
+    elif r == "OE_RIGHT":
+        g = out["b_gathered"]
+        g_trans = 1 if op == "FWD" else 0       # W rows come as [k][Din]
+        hit = np.nonzero(np.isin(cols, idx))[0]
+        if hit.size:
+            pos = np.searchsorted(idx, cols[hit])
+            oe, oabs = gemm_bf16(lhs, a_trans, g, g_trans, K, rows, pos)
+            C[:, hit] += oe
+            absC[:, hit] += oabs
+    elif r == "OE_INNER":
+        ga, gb = out["a_gathered"], out["b_gathered"]
+        kk = idx.size
+        # A_g(i,p): FWD/DGRAD lhs columns [m][k]; WGRAD GY rows [k][Dout] (transposed).
+        ga_trans = 1 if op == "WGRAD" else 0
+        # B_g(p,j): FWD W columns [Dout][k] (transposed); DGRAD W rows, WGRAD X rows [k][n].
+        gb_trans = 1 if op == "FWD" else 0
+        oe, oabs = gemm_bf16(ga, ga_trans, gb, gb_trans, kk, rows, cols)
+        C += oe
+        absC += oabs
+    out.update(C=C, absC=absC)
+    return out
+
+
+def dequantized_product(a_codes, a_scales, b_codes, b_scales) -> np.ndarray:
+    """Full fp64 product deq(A) deq(B)^T via a library matmul (small sizes)."""
+    return dequant(a_codes, a_scales) @ dequant(b_codes, b_scales).T

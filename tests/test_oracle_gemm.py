@@ -1,0 +1,188 @@
+"""Pins of the oracle's products: the MXFP4 residual product against exact
+integer and rational arithmetic, the bf16 product against a library matmul,
+and the outlier split (extracted lines + residual = full product) exactly."""
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle import pipeline
+from conftest import read_golden
+
+
+GRID = {int(c, 16): float(v) for c, v in (ln.split() for ln in read_golden("e2m1_grid.txt"))}
+
+
+def decode(codes, scales):
+    """Independent decode from the OCP grid fixture (not the oracle's)."""
+    outer, K = codes.shape[0], codes.shape[1] * 2
+    nib = np.stack([codes & 15, codes >> 4], axis=-1).reshape(outer, K)
+    vals = np.vectorize(GRID.get)(nib)
+    return vals * np.ldexp(1.0, np.repeat(scales.astype(np.int64) - 127, 32, axis=1))
+
+
+def rand_packed(rng, outer, K, scale_lo=120, scale_hi=134):
+    codes = rng.integers(0, 256, size=(outer, K // 2), dtype=np.uint8)
+    scales = rng.integers(scale_lo, scale_hi, size=(outer, K // 32), dtype=np.uint8)
+    return codes, scales
+
+
+def test_integer_special_case():
+    """Scales 2^0 and integer grid values only: an integer matmul, exactly."""
+    rng = np.random.default_rng(0)
+    ints = [c for c, v in GRID.items() if float(v).is_integer()]
+    m, n, K = 13, 9, 96
+    a = rng.choice(ints, size=(m, K)); b = rng.choice(ints, size=(n, K))
+    pack = lambda x: (x[:, 0::2] | (x[:, 1::2] << 4)).astype(np.uint8)
+    ones = lambda r: np.full((r, K // 32), 127, dtype=np.uint8)
+    C, absC = oracle.gemm_mx(pack(a), ones(m), pack(b), ones(n))
+    va = np.vectorize(GRID.get)(a).astype(np.int64); vb = np.vectorize(GRID.get)(b).astype(np.int64)
+    assert np.array_equal(C, (va @ vb.T).astype(np.float64))
+    assert np.array_equal(absC, (np.abs(va) @ np.abs(vb).T).astype(np.float64))
+
+
+def test_rational_exact_small():
+    rng = np.random.default_rng(1)
+    m, n, K = 5, 4, 64
+    ac, as_ = rand_packed(rng, m, K, 100, 150)
+    bc, bs = rand_packed(rng, n, K, 100, 150)
+    C, _ = oracle.gemm_mx(ac, as_, bc, bs)
+    A, B = decode(ac, as_), decode(bc, bs)
+    for i in range(m):
+        for j in range(n):
+            exact = sum(Fraction(A[i, t]) * Fraction(B[j, t]) for t in range(K))
+            assert C[i, j] == float(exact)
+
+
+def test_matches_library_matmul_and_selection():
+    rng = np.random.default_rng(2)
+    m, n, K = 70, 50, 256
+    ac, as_ = rand_packed(rng, m, K)
+    bc, bs = rand_packed(rng, n, K)
+    ref = decode(ac, as_) @ decode(bc, bs).T
+    rows = np.array([0, 5, 69, 33]); cols = np.array([49, 0, 7])
+    C, _ = oracle.gemm_mx(ac, as_, bc, bs, rows, cols)
+    assert np.allclose(C, ref[np.ix_(rows, cols)], rtol=1e-14, atol=1e-300)
+    Cf, _ = oracle.gemm_mx(ac, as_, bc, bs)
+    assert np.allclose(Cf, ref, rtol=1e-13, atol=1e-12 * np.abs(ref).max())
+
+
+def bf(x):
+    return (np.asarray(x, dtype=np.float32).view(np.uint32) >> 16).astype(np.uint16)
+
+
+@pytest.mark.parametrize("a_trans,b_trans", [(0, 0), (0, 1), (1, 0), (1, 1)])
+def test_bf16_product_layouts(a_trans, b_trans):
+    rng = np.random.default_rng(3)
+    m, n, K = 11, 7, 40
+    A = bf(rng.standard_normal((m, K))); B = bf(rng.standard_normal((K, n)))
+    a = A.T.copy() if a_trans else A
+    b = B.T.copy() if b_trans else B
+    C, _ = oracle.gemm_bf16(a, a_trans, b, b_trans, K, np.arange(m), np.arange(n))
+    ref = oracle.bf16_to_f64(A) @ oracle.bf16_to_f64(B)
+    assert np.allclose(C, ref, rtol=1e-13, atol=1e-13)
+
+
+def int_bf16(rng, shape, lo=-6, hi=7):
+    return bf(rng.integers(lo, hi, size=shape).astype(np.float32))
+
+
+def exact_product(op, lhs, rhs):
+    L, R = oracle.bf16_to_f64(lhs), oracle.bf16_to_f64(rhs)
+    return {"FWD": lambda: L @ R.T, "DGRAD": lambda: L @ R, "WGRAD": lambda: L.T @ R}[op]()
+
+
+@pytest.mark.parametrize("op,pat_lhs,pat_rhs,route", [
+    ("FWD", "R", "N", "OE_LEFT"), ("FWD", "N", "R", "OE_RIGHT"), ("FWD", "C", "N", "OE_INNER"),
+    ("DGRAD", "R", "N", "OE_LEFT"), ("DGRAD", "N", "C", "OE_RIGHT"), ("DGRAD", "C", "N", "OE_INNER"),
+    ("WGRAD", "C", "N", "OE_LEFT"), ("WGRAD", "R", "C", "OE_RIGHT"), ("WGRAD", "R", "N", "OE_INNER"),
+])
+def test_outlier_split_identity(op, pat_lhs, pat_rhs, route):
+    """On every extracted line the result is the exact bf16 product of the
+    original operands (the residual contributes exactly zero there); for
+    inner extraction, result - residual product = the exact rank-k term."""
+    rng = np.random.default_rng(hash((op, route)) % 2**32)
+    T, Din, Dout = 96, 64, 128
+    shapes = {"FWD": ((T, Din), (Dout, Din)), "DGRAD": ((T, Dout), (Dout, Din)),
+              "WGRAD": ((T, Dout), (T, Din))}[op]
+    lhs = int_bf16(rng, shapes[0]); rhs = int_bf16(rng, shapes[1])
+    k = 8
+    r = pipeline.gemm(op, lhs, rhs, T, Din, Dout, pat_lhs, pat_rhs, route=route, k=k)
+    assert r["route"] == route
+    idx = r["idx"]
+    assert idx.size == k and np.all(np.diff(idx) > 0)
+    exact = exact_product(op, lhs, rhs)
+    C = r["C"]
+    res, _ = oracle.gemm_mx(r["a_codes"], r["a_scales"], r["b_codes"], r["b_scales"])
+    if route == "OE_LEFT":
+        assert np.all(res[idx, :] == 0)
+        assert np.array_equal(C[idx, :], exact[idx, :])
+        rest = np.setdiff1d(np.arange(r["m"]), idx)
+        assert np.array_equal(C[rest], res[rest])
+    elif route == "OE_RIGHT":
+        assert np.all(res[:, idx] == 0)
+        assert np.array_equal(C[:, idx], exact[:, idx])
+        rest = np.setdiff1d(np.arange(r["n"]), idx)
+        assert np.array_equal(C[:, rest], res[:, rest])
+    else:
+        # Inner: A[:, idx] B[idx, :] exactly, from the original values.
+        L, R = oracle.bf16_to_f64(lhs), oracle.bf16_to_f64(rhs)
+        Ai = {"FWD": L, "DGRAD": L, "WGRAD": L.T}[op][:, idx]
+        Bi = {"FWD": R.T, "DGRAD": R, "WGRAD": R}[op][idx, :]
+        assert np.array_equal(C - res, Ai @ Bi)
+    # The gathered lines are the source bits, laid out [k][len] for rows and
+    # [len][k] for columns.
+    tensor, axis = oracle.scan_target(op, route)
+    g = r["a_gathered"] if tensor == 0 else r["b_gathered"]
+    src = lhs if tensor == 0 else rhs
+    assert np.array_equal(g, src[idx, :] if axis == oracle.ROWS else src[:, idx])
+
+
+def test_split_identity_unquantized():
+    """The bookkeeping itself: A = A_res + (extracted lines put back), for
+    rows and columns, on random bf16 data (fp64, exact)."""
+    rng = np.random.default_rng(4)
+    t = bf(rng.standard_normal((64, 96)))
+    idx = np.array([3, 10, 40], dtype=np.int32)
+    for axis in (oracle.ROWS, oracle.COLS):
+        # hadamard 0, contraction along the other axis: residual lines are zero codes.
+        contract = oracle.COLS if axis == oracle.ROWS else oracle.ROWS
+        codes, scales, g = oracle.iht_quant(t, contract, 0, idx, axis)
+        deq = oracle.dequant(codes, scales)      # [outer][K]
+        if axis == oracle.ROWS:
+            assert np.all(deq[idx, :] == 0)
+            assert np.array_equal(g, t[idx, :])
+        else:
+            assert np.all(deq[idx, :] == 0)      # outer = columns here
+            assert np.array_equal(g, t[:, idx])
+    # Zeroing inner lines equals quantizing a copy with those entries zeroed.
+    z = t.copy(); z[:, idx] = 0
+    c1, s1, _ = oracle.iht_quant(t, oracle.COLS, 32, idx, oracle.COLS)
+    c2, s2, _ = oracle.iht_quant(z, oracle.COLS, 32)
+    assert np.array_equal(c1, c2) and np.array_equal(s1, s2)
+
+
+def test_bf16_route_is_exact_product():
+    rng = np.random.default_rng(5)
+    lhs = bf(rng.standard_normal((64, 32))); rhs = bf(rng.standard_normal((48, 32)))
+    r = pipeline.gemm("FWD", lhs, rhs, 64, 32, 48, "R", "R")
+    assert r["route"] == "BF16"
+    assert np.allclose(r["C"], exact_product("FWD", lhs, rhs), rtol=1e-13, atol=1e-12)
+
+
+@pytest.mark.parametrize("op", ["FWD", "DGRAD", "WGRAD"])
+def test_pipeline_close_to_exact(op):
+    """A quantized product stays within MXFP4 noise of the exact one, and the
+    packed operands follow each op's contraction direction."""
+    rng = np.random.default_rng(6)
+    T, Din, Dout = 128, 96, 64
+    shapes = {"FWD": ((T, Din), (Dout, Din)), "DGRAD": ((T, Dout), (Dout, Din)),
+              "WGRAD": ((T, Dout), (T, Din))}[op]
+    lhs = bf(rng.standard_normal(shapes[0])); rhs = bf(rng.standard_normal(shapes[1]))
+    r = pipeline.gemm(op, lhs, rhs, T, Din, Dout, "N", "N")
+    ex = exact_product(op, lhs, rhs)
+    assert r["route"] == "IHT"
+    assert r["a_codes"].shape == (r["m"], r["K"] // 2) and r["b_codes"].shape == (r["n"], r["K"] // 2)
+    err = np.linalg.norm(r["C"] - ex) / np.linalg.norm(ex)
+    assert 0.02 < err < 0.3
