@@ -1,0 +1,268 @@
+/*
+ * adahop.h -- C ABI of the AdaHOP per-GEMM hot path on MI355X (gfx950).
+ *
+ * The method is the one of "AdaHOP: Fast and Accurate Low-Precision Training
+ * via Outlier-Pattern-Aware Rotation" (arXiv 2604.02525). Its Fig. 9 and the
+ * appendix list of its kernels give four stages per GEMM:
+ *   1. FOID: the outlier lines of one operand, chosen by the variance of their
+ *      first 64 elements (adahop_detect);
+ *   2. IHT and quantization: zero those lines, rotate the residual by a
+ *      32-point Hadamard transform along the inner dimension, quantize to
+ *      MXFP4 (adahop_iht_quant);
+ *   3. the fused MXFP4 + BF16 GEMM: the residual product on FP4 matrix cores
+ *      and the outlier product in bf16 (adahop_gemm_mx);
+ *   4. the fused scatter-add of the outlier product into the result (inside
+ *      adahop_gemm_mx's epilogue).
+ * Fig. 5 routes each of a linear layer's three products (forward, input
+ * gradient, weight gradient) by its operand pattern pair to IHT, OE-Left,
+ * OE-Right or BF16 (adahop_route); adahop_gemm runs the whole path for one
+ * product.
+ *
+ * Conventions
+ *   - Every tensor pointer is a DEVICE pointer owned by the caller. The
+ *     library never allocates, frees or synchronizes device memory; scratch
+ *     space is the caller's workspace. Every launch is enqueued on `stream`
+ *     (a hipStream_t, NULL = the null stream) and the call returns at once.
+ *   - bf16 tensors are uint16 bit patterns, row-major, leading dimension `ld`
+ *     in elements (ld >= cols). A bf16 input quantized along its rows
+ *     (contraction along columns) must have 16-byte aligned rows: base
+ *     pointer 16-byte aligned and ld % 8 == 0. Packed code buffers must be
+ *     16-byte aligned.
+ *   - Textbook frame of a product: C[m,n] = A[m,K] * B[K,n], K the inner
+ *     (contraction) dimension.
+ *   - MXFP4 operand (OCP Microscaling v1.0 MXFP4): 4-bit E2M1 codes, two per
+ *     byte, element 2j in the low nibble, stored [outer][K/2]; one E8M0 scale
+ *     byte per 32 consecutive K-elements, stored [outer][K/32]. K runs
+ *     contiguously. For A, outer = m (its rows); for B, outer = n (its
+ *     columns).
+ *   - Outlier index sets are int32, ascending, unique, on the device.
+ *   - Errors: argument errors are found on the host before any launch and
+ *     return ADAHOP_ERR_INVALID (or ADAHOP_ERR_UNSUPPORTED for a valid but
+ *     unimplemented case) with a message in adahop_last_error(); a too-small
+ *     workspace returns ADAHOP_ERR_WORKSPACE; a failed launch returns
+ *     ADAHOP_ERR_HIP. Non-finite inputs are not supported (results
+ *     unspecified). Outputs must not alias inputs.
+ *   - Thread safety: calls on different streams may run concurrently;
+ *     adahop_last_error() is per host thread.
+ */
+#ifndef ADAHOP_H
+#define ADAHOP_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define ADAHOP_API __attribute__((visibility("default")))
+
+typedef enum {
+  ADAHOP_OK = 0,
+  ADAHOP_ERR_INVALID = 1,     /* bad argument (detected before any launch) */
+  ADAHOP_ERR_UNSUPPORTED = 2, /* valid but not implemented (alignment, sizes) */
+  ADAHOP_ERR_WORKSPACE = 3,   /* workspace missing or too small */
+  ADAHOP_ERR_HIP = 4          /* a HIP runtime call or launch failed */
+} adahop_status;
+
+/* Outlier pattern of a stored tensor (Table 1's R / C / N). */
+typedef enum { ADAHOP_PAT_NONE = 0, ADAHOP_PAT_ROW = 1, ADAHOP_PAT_COL = 2 } adahop_pattern;
+
+/* The three products of a linear layer Y = X W^T (Table 1's columns):
+ * FWD   Y  [T,Dout]    = X [T,Din] * W^T       (lhs X,  rhs W [Dout,Din])
+ * DGRAD dX [T,Din]     = GY [T,Dout] * W       (lhs GY, rhs W [Dout,Din])
+ * WGRAD dW [Dout,Din]  = GY^T * X              (lhs GY, rhs X [T,Din]) */
+typedef enum { ADAHOP_OP_FWD = 0, ADAHOP_OP_DGRAD = 1, ADAHOP_OP_WGRAD = 2 } adahop_op;
+
+/* Path of one product (Fig. 5). OE_INNER extracts inner-dimension lines of
+ * both operands into a dense rank-k bf16 term; MXFP4 is plain quantization
+ * without rotation or extraction (a baseline). */
+typedef enum {
+  ADAHOP_ROUTE_AUTO = -1,
+  ADAHOP_ROUTE_BF16 = 0,
+  ADAHOP_ROUTE_IHT = 1,
+  ADAHOP_ROUTE_OE_LEFT = 2,
+  ADAHOP_ROUTE_OE_RIGHT = 3,
+  ADAHOP_ROUTE_OE_INNER = 4,
+  ADAHOP_ROUTE_MXFP4 = 5
+} adahop_route_t;
+
+typedef enum { ADAHOP_AXIS_ROWS = 0, ADAHOP_AXIS_COLS = 1 } adahop_axis;
+typedef enum { ADAHOP_OUT_BF16 = 0, ADAHOP_OUT_F32 = 1 } adahop_out_dtype;
+
+ADAHOP_API const char* adahop_status_string(int status);
+/* Detail of the last failure on this host thread ("" if none). */
+ADAHOP_API const char* adahop_last_error(void);
+ADAHOP_API int adahop_version(void);
+
+/* ---------------------------------------------------------------------------
+ * Routing (host only, pure). Fig. 5 routes each product by the pattern pair
+ * of its operands; Fig. 2 and the abstract say IHT (mixing along the inner
+ * dimension) suppresses outliers that lie along the inner dimension and not
+ * those along the outer one. Rule, in the textbook frame: A is hurt if its
+ * outlier lines are rows, B if its outlier lines are columns; neither -> IHT,
+ * A only -> OE_LEFT, B only -> OE_RIGHT, both -> BF16. Patterns are given in
+ * each tensor's storage frame (as in Table 1); a tensor used transposed swaps
+ * ROW and COL. Returns ADAHOP_ROUTE_AUTO for an invalid op or pattern. */
+ADAHOP_API adahop_route_t adahop_route(adahop_op op, adahop_pattern pat_lhs,
+                                       adahop_pattern pat_rhs);
+
+/* ---------------------------------------------------------------------------
+ * FOID (appendix, kernel 1; Fig. 9). Candidates are the rows (axis ROWS:
+ * statistics over t[r, 0:P]) or the columns (axis COLS: t[0:P, c]) of the
+ * bf16 tensor t [rows, cols], P = min(probe, line length). Each candidate's
+ * score is the population variance of those P values, computed in fp64 in
+ * index order (sum, mean, then sum of squared deviations). The k candidates
+ * with the largest score (ties: lower index first) are written to idx_out
+ * (device int32[k]) in ascending order. Deterministic. Needs
+ * adahop_detect_workspace_size(...) bytes of workspace.
+ * Errors: INVALID if t/idx_out is NULL, rows/cols < 1, ld < cols, probe < 1,
+ * k < 1 or k > number of candidates; UNSUPPORTED if k > 1024. */
+ADAHOP_API size_t adahop_detect_workspace_size(int64_t rows, int64_t cols, adahop_axis axis,
+                                               int32_t k);
+ADAHOP_API adahop_status adahop_detect(const uint16_t* t, int64_t rows, int64_t cols,
+                                       int64_t ld, adahop_axis axis, int32_t probe,
+                                       int32_t k, int32_t* idx_out, void* ws,
+                                       size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Zero + gather + IHT + MXFP4 quantization (appendix, kernel 2; abstract).
+ * src is bf16 [rows, cols]. contract COLS: 32-blocks run along each row
+ * (K = cols, outer = rows); contract ROWS: 32-blocks run down each column
+ * (K = rows, outer = cols). K must be a multiple of 32.
+ * Zeroing: the nzero lines zero_idx (device, ascending, unique) -- rows of
+ * src if zero_axis is ROWS, columns if COLS -- are treated as +0 (the
+ * residual with the outliers removed). gathered (device, may be NULL when
+ * nzero > 0 and the lines are not needed) receives a compact bf16 copy of
+ * those lines: [nzero][cols] for rows, [rows][nzero] for columns.
+ * Rotation: hadamard_block 32 applies the orthonormal 32-point Walsh-Hadamard
+ * transform (Sylvester order, fp32 butterflies with strides 1,2,4,8,16, then
+ * one multiply by fp32(1/sqrt(32))) to each block; 0 applies none.
+ * Quantization (OCP MX v1.0): scale exponent s = floor(log2(block amax)) - 2,
+ * clamped to [-127, 127], stored as the byte s + 127 (0x00 for an all-zero
+ * block); each element's code is the sign bit and the E2M1 magnitude nearest
+ * to |y| / 2^s, ties to the even code, saturating at 6.
+ * Output codes [outer][K/2] and scales [outer][K/32] (device).
+ * Errors: INVALID for NULL src/codes/scales, bad sizes, K % 32 != 0,
+ * hadamard_block not in {0, 32}, nzero < 0, or zero_idx NULL with nzero > 0;
+ * UNSUPPORTED if codes is not 16-byte aligned, or (contract COLS) src rows
+ * or gathered are not 16-byte aligned. Indices are not validated
+ * on the device: out-of-range or unsorted zero_idx gives unspecified results. */
+ADAHOP_API adahop_status adahop_iht_quant(const uint16_t* src, int64_t rows, int64_t cols,
+                                          int64_t ld, adahop_axis contract,
+                                          int32_t hadamard_block, const int32_t* zero_idx,
+                                          int32_t nzero, adahop_axis zero_axis,
+                                          uint8_t* codes, uint8_t* scales, uint16_t* gathered,
+                                          void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Fused MXFP4 + BF16 GEMM with the scatter-add epilogue (appendix, kernels 3
+ * and 4). */
+typedef struct {
+  const uint8_t* codes;   /* [outer][K/2] */
+  const uint8_t* scales;  /* [outer][K/32] */
+  int64_t outer;          /* m for A, n for B */
+  int64_t K;
+} adahop_mx_operand;
+
+/* A bf16 factor of the outlier product, seen as [outer][inner]: element
+ * (r, t) sits at ptr[r * ld + t] if inner_contiguous, else ptr[t * ld + r]. */
+typedef struct {
+  const uint16_t* ptr;
+  int64_t ld;
+  int32_t inner_contiguous;
+  int32_t reserved;
+} adahop_bf16_view;
+
+/* The outlier (OE) term, P = a * b^T contracted over the views' inner index:
+ *   OE_LEFT : a = the k extracted rows of A ([k][K]), b = B in bf16 ([n][K]);
+ *             C[idx[p], j] += P[p][j].
+ *   OE_RIGHT: a = A in bf16 ([m][K]), b = the k extracted columns of B
+ *             ([k][K]); C[i, idx[p]] += P[i][p].
+ *   OE_INNER: a = A's k extracted columns ([m][k]), b = B's k extracted rows
+ *             ([n][k]); C[i, j] += P[i][j].
+ * The add happens on fp32 values before the single rounding of C. */
+typedef struct {
+  adahop_route_t route;   /* OE_LEFT, OE_RIGHT or OE_INNER */
+  int32_t k;
+  const int32_t* idx;     /* device [k]; unused (may be NULL) for OE_INNER */
+  adahop_bf16_view a;
+  adahop_bf16_view b;
+} adahop_oe;
+
+/* C[m,n] (row-major, leading dim ldc, bf16 or fp32) = deq(A) * deq(B)^T with
+ * fp32 accumulation, plus the OE term if oe != NULL. Needs
+ * adahop_gemm_mx_workspace_size(...) bytes (0 without OE_LEFT/OE_RIGHT).
+ * Errors: INVALID for NULL pointers, K mismatch, K % 32 != 0, ldc < n, bad
+ * OE descriptors; UNSUPPORTED for k > 1024. */
+ADAHOP_API size_t adahop_gemm_mx_workspace_size(int64_t m, int64_t n, int64_t K,
+                                                const adahop_oe* oe);
+ADAHOP_API adahop_status adahop_gemm_mx(const adahop_mx_operand* A,
+                                        const adahop_mx_operand* B, const adahop_oe* oe,
+                                        void* C, int64_t ldc, adahop_out_dtype out_dtype,
+                                        void* ws, size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * One AdaHOP product end to end: route, FOID on the operand and axis the route
+ * extracts, zero + gather + IHT + MXFP4 on both operands (along each one's
+ * contraction axis), the fused GEMM and the scatter-add.
+ *   FWD  : lhs X [T,Din],  rhs W [Dout,Din] -> out Y  [T,Dout]
+ *   DGRAD: lhs GY [T,Dout], rhs W [Dout,Din] -> out dX [T,Din]
+ *   WGRAD: lhs GY [T,Dout], rhs X [T,Din]    -> out dW [Dout,Din]
+ * lhs, rhs and out are contiguous row-major. route AUTO applies adahop_route
+ * to (pat_lhs, pat_rhs); oe_rank is the number of extracted lines (64 on the
+ * pages, Fig. 10). The contraction length (Din, Dout or T) must be a
+ * multiple of 32. The workspace holds, after the call, the quantized
+ * operands and the outlier lines at the offsets adahop_gemm_plan reports.
+ * Errors: as for the stage calls; INVALID for a bad op or route, or an OE
+ * route with oe_rank < 1 or above the number of candidate lines. */
+typedef struct {
+  adahop_route_t route;   /* resolved route */
+  int64_t m, n, K;        /* textbook-frame sizes */
+  int32_t k;              /* extracted lines (0 without OE) */
+  int32_t scan_tensor;    /* 0 = lhs, 1 = rhs, -1 = no FOID */
+  adahop_axis scan_axis;  /* candidate lines: rows or columns of that tensor */
+  int32_t reserved;
+  size_t ws_bytes;        /* workspace the call needs */
+  /* Byte offsets into the workspace (SIZE_MAX if absent): */
+  size_t off_idx;         /* int32 [k] FOID indices */
+  size_t off_a_codes, off_a_scales;   /* A packed: [m][K/2], [m][K/32] */
+  size_t off_b_codes, off_b_scales;   /* B packed: [n][K/2], [n][K/32] */
+  size_t off_lhs_lines;   /* bf16 lines gathered from lhs (layout as adahop_iht_quant) */
+  size_t off_rhs_lines;   /* bf16 lines gathered from rhs */
+} adahop_plan;
+
+ADAHOP_API adahop_status adahop_gemm_plan(adahop_op op, int64_t T, int64_t Din, int64_t Dout,
+                                          adahop_pattern pat_lhs, adahop_pattern pat_rhs,
+                                          adahop_route_t route, int32_t oe_rank,
+                                          adahop_plan* plan);
+ADAHOP_API size_t adahop_gemm_workspace_size(adahop_op op, int64_t T, int64_t Din,
+                                             int64_t Dout, adahop_pattern pat_lhs,
+                                             adahop_pattern pat_rhs, adahop_route_t route,
+                                             int32_t oe_rank);
+ADAHOP_API adahop_status adahop_gemm(adahop_op op, const uint16_t* lhs, const uint16_t* rhs,
+                                     int64_t T, int64_t Din, int64_t Dout,
+                                     adahop_pattern pat_lhs, adahop_pattern pat_rhs,
+                                     adahop_route_t route, int32_t oe_rank, void* out,
+                                     adahop_out_dtype out_dtype, void* ws, size_t ws_bytes,
+                                     void* stream);
+
+/* As adahop_gemm, and if stage_events is not NULL it must hold
+ * ADAHOP_STAGE_EVENTS created hipEvent_t handles: events[0] is recorded on
+ * `stream` before the first launch and events[1..5] after the FOID, lhs
+ * quantization, rhs quantization, outlier product and GEMM stages (a stage
+ * that does not run records its event right after the previous one). */
+#define ADAHOP_STAGE_EVENTS 6
+ADAHOP_API adahop_status adahop_gemm_timed(adahop_op op, const uint16_t* lhs,
+                                           const uint16_t* rhs, int64_t T, int64_t Din,
+                                           int64_t Dout, adahop_pattern pat_lhs,
+                                           adahop_pattern pat_rhs, adahop_route_t route,
+                                           int32_t oe_rank, void* out,
+                                           adahop_out_dtype out_dtype, void* ws,
+                                           size_t ws_bytes, void* stream,
+                                           void* const* stage_events);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* ADAHOP_H */

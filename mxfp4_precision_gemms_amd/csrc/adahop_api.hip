@@ -1,0 +1,466 @@
+// Host side of the AdaHOP library: argument checks, routing, workspace plans
+// and the launch sequence of one product. Every check runs before the first
+// launch; the library never allocates or synchronizes.
+#include <climits>
+#include <cstring>
+#include <string>
+
+#include "adahop_internal.h"
+
+namespace adahop {
+
+static thread_local std::string g_last_error;
+
+void set_error(const std::string& msg) { g_last_error = msg; }
+
+adahop_status fail(adahop_status st, const std::string& msg) {
+  g_last_error = msg;
+  return st;
+}
+
+adahop_status check_launch(const char* what) {
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess)
+    return fail(ADAHOP_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
+  return ADAHOP_OK;
+}
+
+namespace {
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Storage-frame description of one product (the textbook frame is C = A B).
+struct OpShape {
+  int64_t m, n, K;
+  int64_t lhs_rows, lhs_cols, rhs_rows, rhs_cols;
+  int lhs_contract, rhs_contract;   // axis of the stored tensor the contraction runs along
+  bool lhs_transposed, rhs_transposed;   // textbook operand = stored tensor transposed
+};
+
+bool op_shape(adahop_op op, int64_t T, int64_t Din, int64_t Dout, OpShape* s) {
+  switch (op) {
+    case ADAHOP_OP_FWD:     // Y = X W^T: A = X, B = W^T
+      *s = {T, Dout, Din, T, Din, Dout, Din, ADAHOP_AXIS_COLS, ADAHOP_AXIS_COLS, false, true};
+      return true;
+    case ADAHOP_OP_DGRAD:   // dX = GY W: A = GY, B = W
+      *s = {T, Din, Dout, T, Dout, Dout, Din, ADAHOP_AXIS_COLS, ADAHOP_AXIS_ROWS, false, false};
+      return true;
+    case ADAHOP_OP_WGRAD:   // dW = GY^T X: A = GY^T, B = X
+      *s = {Dout, Din, T, T, Dout, T, Din, ADAHOP_AXIS_ROWS, ADAHOP_AXIS_ROWS, true, false};
+      return true;
+  }
+  return false;
+}
+
+adahop_pattern transposed(adahop_pattern p) {
+  return p == ADAHOP_PAT_ROW ? ADAHOP_PAT_COL : p == ADAHOP_PAT_COL ? ADAHOP_PAT_ROW : p;
+}
+
+bool valid_pattern(int p) { return p >= ADAHOP_PAT_NONE && p <= ADAHOP_PAT_COL; }
+
+// View of a stored [rows, cols] tensor as (outer, t) with t along `contract`.
+Bf16View stored_view(const uint16_t* p, int64_t cols, int contract) {
+  return {p, cols, contract == ADAHOP_AXIS_COLS ? 1 : 0};
+}
+
+// Gathered lines (adahop_iht_quant layout): rows -> [k][cols], columns ->
+// [rows][k]. As (line p, position x along the line):
+Bf16View lines_by_line(const uint16_t* g, int zero_axis, int64_t cols, int32_t k) {
+  return zero_axis == ADAHOP_AXIS_ROWS ? Bf16View{g, cols, 1} : Bf16View{g, k, 0};
+}
+// ... and as (position x, line p):
+Bf16View lines_by_position(const uint16_t* g, int zero_axis, int64_t cols, int32_t k) {
+  return zero_axis == ADAHOP_AXIS_ROWS ? Bf16View{g, cols, 0} : Bf16View{g, k, 1};
+}
+
+struct Plan {
+  adahop_plan pub;
+  OpShape shape;
+  bool zero_lhs = false, zero_rhs = false;
+  int lhs_zero_axis = ADAHOP_AXIS_ROWS, rhs_zero_axis = ADAHOP_AXIS_ROWS;
+  int splits = 0;
+  size_t off_foid = SIZE_MAX, off_partials = SIZE_MAX;
+  size_t foid_bytes = 0;
+};
+
+constexpr size_t kNone = SIZE_MAX;
+
+adahop_status make_plan(adahop_op op, int64_t T, int64_t Din, int64_t Dout,
+                        adahop_pattern pat_lhs, adahop_pattern pat_rhs, adahop_route_t route,
+                        int32_t oe_rank, Plan* P) {
+  std::memset(&P->pub, 0, sizeof(P->pub));
+  if (!op_shape(op, T, Din, Dout, &P->shape)) return fail(ADAHOP_ERR_INVALID, "invalid op");
+  if (T < 1 || Din < 1 || Dout < 1) return fail(ADAHOP_ERR_INVALID, "sizes must be >= 1");
+  if (!valid_pattern(pat_lhs) || !valid_pattern(pat_rhs))
+    return fail(ADAHOP_ERR_INVALID, "invalid pattern");
+  if (route == ADAHOP_ROUTE_AUTO) route = adahop_route(op, pat_lhs, pat_rhs);
+  if (route < ADAHOP_ROUTE_BF16 || route > ADAHOP_ROUTE_MXFP4)
+    return fail(ADAHOP_ERR_INVALID, "invalid route");
+  const OpShape& s = P->shape;
+  if (route != ADAHOP_ROUTE_BF16 && s.K % 32 != 0)
+    return fail(ADAHOP_ERR_INVALID, "contraction length " + std::to_string(s.K) +
+                                        " is not a multiple of 32");
+  adahop_plan& pb = P->pub;
+  pb.route = route;
+  pb.m = s.m; pb.n = s.n; pb.K = s.K;
+  pb.scan_tensor = -1;
+  pb.scan_axis = ADAHOP_AXIS_ROWS;
+  pb.off_idx = pb.off_a_codes = pb.off_a_scales = pb.off_b_codes = pb.off_b_scales = kNone;
+  pb.off_lhs_lines = pb.off_rhs_lines = kNone;
+  if (route == ADAHOP_ROUTE_BF16) { pb.ws_bytes = 0; return ADAHOP_OK; }
+
+  const bool oe = route == ADAHOP_ROUTE_OE_LEFT || route == ADAHOP_ROUTE_OE_RIGHT ||
+                  route == ADAHOP_ROUTE_OE_INNER;
+  if (oe) {
+    // OE_LEFT: rows of A; OE_RIGHT: columns of B; OE_INNER: A's columns (lhs
+    // lines across its contraction axis) and the matching rows of B.
+    if (route == ADAHOP_ROUTE_OE_LEFT) {
+      pb.scan_tensor = 0;
+      pb.scan_axis = (adahop_axis)(s.lhs_contract == ADAHOP_AXIS_COLS ? ADAHOP_AXIS_ROWS
+                                                                       : ADAHOP_AXIS_COLS);
+    } else if (route == ADAHOP_ROUTE_OE_RIGHT) {
+      pb.scan_tensor = 1;
+      pb.scan_axis = (adahop_axis)(s.rhs_contract == ADAHOP_AXIS_COLS ? ADAHOP_AXIS_ROWS
+                                                                       : ADAHOP_AXIS_COLS);
+    } else {
+      pb.scan_tensor = 0;
+      pb.scan_axis = (adahop_axis)s.lhs_contract;
+    }
+    const int64_t rows = pb.scan_tensor == 0 ? s.lhs_rows : s.rhs_rows;
+    const int64_t cols = pb.scan_tensor == 0 ? s.lhs_cols : s.rhs_cols;
+    const int64_t ncand = pb.scan_axis == ADAHOP_AXIS_ROWS ? rows : cols;
+    if (oe_rank < 1 || oe_rank > ncand)
+      return fail(ADAHOP_ERR_INVALID, "oe_rank " + std::to_string(oe_rank) +
+                                          " outside [1, " + std::to_string(ncand) + "]");
+    if (oe_rank > kMaxK) return fail(ADAHOP_ERR_UNSUPPORTED, "oe_rank above 1024");
+    pb.k = oe_rank;
+    if (pb.scan_tensor == 0) { P->zero_lhs = true; P->lhs_zero_axis = pb.scan_axis; }
+    else { P->zero_rhs = true; P->rhs_zero_axis = pb.scan_axis; }
+    if (route == ADAHOP_ROUTE_OE_INNER) { P->zero_rhs = true; P->rhs_zero_axis = s.rhs_contract; }
+    P->foid_bytes = foid_workspace_bytes(ncand, oe_rank);
+  }
+
+  size_t off = 0;
+  auto take = [&](size_t bytes) { size_t o = off; off += align_up(bytes, kAlign); return o; };
+  if (oe) {
+    pb.off_idx = take(sizeof(int32_t) * (size_t)pb.k);
+    if (P->foid_bytes) P->off_foid = take(P->foid_bytes);
+  }
+  pb.off_a_codes = take((size_t)s.m * (size_t)(s.K / 2));
+  pb.off_a_scales = take((size_t)s.m * (size_t)(s.K / 32));
+  pb.off_b_codes = take((size_t)s.n * (size_t)(s.K / 2));
+  pb.off_b_scales = take((size_t)s.n * (size_t)(s.K / 32));
+  auto line_len = [&](bool lhs, int axis) {
+    const int64_t rows = lhs ? s.lhs_rows : s.rhs_rows, cols = lhs ? s.lhs_cols : s.rhs_cols;
+    return axis == ADAHOP_AXIS_ROWS ? cols : rows;
+  };
+  if (P->zero_lhs) pb.off_lhs_lines = take(2 * (size_t)pb.k * (size_t)line_len(true, P->lhs_zero_axis));
+  if (P->zero_rhs) pb.off_rhs_lines = take(2 * (size_t)pb.k * (size_t)line_len(false, P->rhs_zero_axis));
+  if (route == ADAHOP_ROUTE_OE_LEFT || route == ADAHOP_ROUTE_OE_RIGHT) {
+    const int64_t nx = route == ADAHOP_ROUTE_OE_LEFT ? pb.k : s.m;
+    const int64_t ny = route == ADAHOP_ROUTE_OE_LEFT ? s.n : pb.k;
+    P->splits = oe_splits(nx, ny, s.K);
+    P->off_partials = take(sizeof(float) * (size_t)P->splits * (size_t)nx * (size_t)ny);
+  }
+  pb.ws_bytes = off;
+  return ADAHOP_OK;
+}
+
+struct Events {
+  void* const* ev;
+  hipStream_t stream;
+  adahop_status record(int i) const {
+    if (!ev) return ADAHOP_OK;
+    hipError_t e = hipEventRecord(static_cast<hipEvent_t>(ev[i]), stream);
+    return e == hipSuccess ? ADAHOP_OK
+                           : fail(ADAHOP_ERR_HIP, std::string("hipEventRecord: ") +
+                                                      hipGetErrorString(e));
+  }
+};
+
+#define ADAHOP_TRY(x)                      \
+  do {                                     \
+    adahop_status _st = (x);               \
+    if (_st != ADAHOP_OK) return _st;      \
+  } while (0)
+
+adahop_status run_gemm(adahop_op op, const uint16_t* lhs, const uint16_t* rhs, int64_t T,
+                       int64_t Din, int64_t Dout, adahop_pattern pat_lhs,
+                       adahop_pattern pat_rhs, adahop_route_t route, int32_t oe_rank,
+                       void* out, adahop_out_dtype out_dtype, void* ws, size_t ws_bytes,
+                       hipStream_t stream, void* const* events) {
+  set_error("");
+  if (!lhs || !rhs || !out) return fail(ADAHOP_ERR_INVALID, "null lhs, rhs or out");
+  if (out_dtype != ADAHOP_OUT_BF16 && out_dtype != ADAHOP_OUT_F32)
+    return fail(ADAHOP_ERR_INVALID, "invalid out_dtype");
+  Plan P;
+  ADAHOP_TRY(make_plan(op, T, Din, Dout, pat_lhs, pat_rhs, route, oe_rank, &P));
+  const adahop_plan& pb = P.pub;
+  const OpShape& s = P.shape;
+  if (pb.ws_bytes > 0 && (ws == nullptr || ws_bytes < pb.ws_bytes))
+    return fail(ADAHOP_ERR_WORKSPACE, "workspace too small: need " + std::to_string(pb.ws_bytes) +
+                                          " bytes");
+  if (pb.route != ADAHOP_ROUTE_BF16) {
+    const bool lhs_ok = s.lhs_contract == ADAHOP_AXIS_ROWS || (aligned16(lhs) && s.lhs_cols % 8 == 0);
+    const bool rhs_ok = s.rhs_contract == ADAHOP_AXIS_ROWS || (aligned16(rhs) && s.rhs_cols % 8 == 0);
+    if (!lhs_ok || !rhs_ok || (ws && !aligned16(ws)))
+      return fail(ADAHOP_ERR_UNSUPPORTED,
+                  "an operand quantized along its rows must be 16-byte aligned with a row length "
+                  "% 8 == 0, and the workspace 16-byte aligned");
+  }
+  const Events E{events, stream};
+  const int out_f32 = out_dtype == ADAHOP_OUT_F32 ? 1 : 0;
+  ADAHOP_TRY(E.record(0));
+
+  if (pb.route == ADAHOP_ROUTE_BF16) {
+    for (int i = 1; i <= 4; ++i) ADAHOP_TRY(E.record(i));
+    ADAHOP_TRY(bf16_gemm_launch(stored_view(lhs, s.lhs_cols, s.lhs_contract),
+                                stored_view(rhs, s.rhs_cols, s.rhs_contract), s.m, s.n, s.K, out,
+                                s.n, out_f32, stream));
+    return E.record(5);
+  }
+
+  char* w = static_cast<char*>(ws);
+  int32_t* idx = pb.off_idx != kNone ? reinterpret_cast<int32_t*>(w + pb.off_idx) : nullptr;
+  if (idx) {
+    const bool l = pb.scan_tensor == 0;
+    ADAHOP_TRY(foid_launch(l ? lhs : rhs, l ? s.lhs_rows : s.rhs_rows, l ? s.lhs_cols : s.rhs_cols,
+                           l ? s.lhs_cols : s.rhs_cols, pb.scan_axis, 64, pb.k, idx,
+                           P.off_foid != kNone ? w + P.off_foid : nullptr, P.foid_bytes, stream));
+  }
+  ADAHOP_TRY(E.record(1));
+  const int had = pb.route == ADAHOP_ROUTE_MXFP4 ? 0 : 32;
+  uint8_t* ac = reinterpret_cast<uint8_t*>(w + pb.off_a_codes);
+  uint8_t* as = reinterpret_cast<uint8_t*>(w + pb.off_a_scales);
+  uint8_t* bc = reinterpret_cast<uint8_t*>(w + pb.off_b_codes);
+  uint8_t* bs = reinterpret_cast<uint8_t*>(w + pb.off_b_scales);
+  uint16_t* ll = pb.off_lhs_lines != kNone ? reinterpret_cast<uint16_t*>(w + pb.off_lhs_lines) : nullptr;
+  uint16_t* rl = pb.off_rhs_lines != kNone ? reinterpret_cast<uint16_t*>(w + pb.off_rhs_lines) : nullptr;
+  ADAHOP_TRY(iht_quant_launch(lhs, s.lhs_rows, s.lhs_cols, s.lhs_cols, s.lhs_contract, had,
+                              P.zero_lhs ? idx : nullptr, P.zero_lhs ? pb.k : 0, P.lhs_zero_axis,
+                              ac, as, ll, stream));
+  ADAHOP_TRY(E.record(2));
+  ADAHOP_TRY(iht_quant_launch(rhs, s.rhs_rows, s.rhs_cols, s.rhs_cols, s.rhs_contract, had,
+                              P.zero_rhs ? idx : nullptr, P.zero_rhs ? pb.k : 0, P.rhs_zero_axis,
+                              bc, bs, rl, stream));
+  ADAHOP_TRY(E.record(3));
+
+  OeEpilogue oe{};
+  oe.mode = 0;
+  if (pb.route == ADAHOP_ROUTE_OE_LEFT || pb.route == ADAHOP_ROUTE_OE_RIGHT) {
+    float* partials = reinterpret_cast<float*>(w + P.off_partials);
+    Bf16View X, Y;
+    int64_t nx, ny;
+    if (pb.route == ADAHOP_ROUTE_OE_LEFT) {
+      X = lines_by_line(ll, P.lhs_zero_axis, s.lhs_cols, pb.k);       // (p, t)
+      Y = stored_view(rhs, s.rhs_cols, s.rhs_contract);               // (j, t)
+      nx = pb.k; ny = s.n;
+    } else {
+      X = stored_view(lhs, s.lhs_cols, s.lhs_contract);               // (i, t)
+      Y = lines_by_line(rl, P.rhs_zero_axis, s.rhs_cols, pb.k);       // (p, t)
+      nx = s.m; ny = pb.k;
+    }
+    ADAHOP_TRY(oe_product_launch(X, Y, nx, ny, s.K, P.splits, partials, stream));
+    oe.mode = pb.route;
+    oe.k = pb.k;
+    oe.idx = idx;
+    oe.partials = partials;
+    oe.splits = P.splits;
+  } else if (pb.route == ADAHOP_ROUTE_OE_INNER) {
+    oe.mode = ADAHOP_ROUTE_OE_INNER;
+    oe.k = pb.k;
+    oe.a = lines_by_position(ll, P.lhs_zero_axis, s.lhs_cols, pb.k);  // (i, p)
+    oe.b = lines_by_position(rl, P.rhs_zero_axis, s.rhs_cols, pb.k);  // (j, p)
+  }
+  ADAHOP_TRY(E.record(4));
+  ADAHOP_TRY(gemm_mx_launch(ac, as, bc, bs, s.m, s.n, s.K, oe, out, s.n, out_f32, stream));
+  return E.record(5);
+}
+
+}  // namespace
+}  // namespace adahop
+
+using namespace adahop;
+
+extern "C" {
+
+const char* adahop_status_string(int status) {
+  switch (status) {
+    case ADAHOP_OK: return "ok";
+    case ADAHOP_ERR_INVALID: return "invalid argument";
+    case ADAHOP_ERR_UNSUPPORTED: return "unsupported";
+    case ADAHOP_ERR_WORKSPACE: return "workspace too small";
+    case ADAHOP_ERR_HIP: return "HIP error";
+  }
+  return "unknown status";
+}
+
+const char* adahop_last_error(void) { return g_last_error.c_str(); }
+
+int adahop_version(void) { return 1; }
+
+adahop_route_t adahop_route(adahop_op op, adahop_pattern pat_lhs, adahop_pattern pat_rhs) {
+  OpShape s;
+  if (!op_shape(op, 1, 1, 1, &s) || !valid_pattern(pat_lhs) || !valid_pattern(pat_rhs))
+    return ADAHOP_ROUTE_AUTO;
+  // Patterns of the textbook operands A and B.
+  const adahop_pattern a = s.lhs_transposed ? transposed(pat_lhs) : pat_lhs;
+  const adahop_pattern b = s.rhs_transposed ? transposed(pat_rhs) : pat_rhs;
+  // Outlier lines along the outer dimension (A's rows, B's columns) are what
+  // mixing along the inner dimension cannot spread.
+  const bool a_outer = a == ADAHOP_PAT_ROW;
+  const bool b_outer = b == ADAHOP_PAT_COL;
+  if (a_outer && b_outer) return ADAHOP_ROUTE_BF16;
+  if (a_outer) return ADAHOP_ROUTE_OE_LEFT;
+  if (b_outer) return ADAHOP_ROUTE_OE_RIGHT;
+  return ADAHOP_ROUTE_IHT;
+}
+
+size_t adahop_detect_workspace_size(int64_t rows, int64_t cols, adahop_axis axis, int32_t k) {
+  if (rows < 1 || cols < 1 || k < 1) return 0;
+  return foid_workspace_bytes(axis == ADAHOP_AXIS_ROWS ? rows : cols, k);
+}
+
+adahop_status adahop_detect(const uint16_t* t, int64_t rows, int64_t cols, int64_t ld,
+                            adahop_axis axis, int32_t probe, int32_t k, int32_t* idx_out,
+                            void* ws, size_t ws_bytes, void* stream) {
+  set_error("");
+  if (!t || !idx_out) return fail(ADAHOP_ERR_INVALID, "adahop_detect: null pointer");
+  if (rows < 1 || cols < 1 || ld < cols) return fail(ADAHOP_ERR_INVALID, "adahop_detect: bad sizes");
+  if (axis != ADAHOP_AXIS_ROWS && axis != ADAHOP_AXIS_COLS)
+    return fail(ADAHOP_ERR_INVALID, "adahop_detect: bad axis");
+  if (probe < 1) return fail(ADAHOP_ERR_INVALID, "adahop_detect: probe < 1");
+  const int64_t ncand = axis == ADAHOP_AXIS_ROWS ? rows : cols;
+  if (k < 1 || k > ncand) return fail(ADAHOP_ERR_INVALID, "adahop_detect: k outside [1, candidates]");
+  if (k > kMaxK) return fail(ADAHOP_ERR_UNSUPPORTED, "adahop_detect: k above 1024");
+  return foid_launch(t, rows, cols, ld, axis, probe, k, idx_out, ws, ws_bytes,
+                     static_cast<hipStream_t>(stream));
+}
+
+adahop_status adahop_iht_quant(const uint16_t* src, int64_t rows, int64_t cols, int64_t ld,
+                               adahop_axis contract, int32_t hadamard_block,
+                               const int32_t* zero_idx, int32_t nzero, adahop_axis zero_axis,
+                               uint8_t* codes, uint8_t* scales, uint16_t* gathered,
+                               void* stream) {
+  set_error("");
+  if (!src || !codes || !scales) return fail(ADAHOP_ERR_INVALID, "adahop_iht_quant: null pointer");
+  if (rows < 1 || cols < 1 || ld < cols) return fail(ADAHOP_ERR_INVALID, "adahop_iht_quant: bad sizes");
+  if (contract != ADAHOP_AXIS_ROWS && contract != ADAHOP_AXIS_COLS)
+    return fail(ADAHOP_ERR_INVALID, "adahop_iht_quant: bad contraction axis");
+  const int64_t K = contract == ADAHOP_AXIS_COLS ? cols : rows;
+  if (K % 32 != 0) return fail(ADAHOP_ERR_INVALID, "adahop_iht_quant: K % 32 != 0");
+  if (hadamard_block != 0 && hadamard_block != 32)
+    return fail(ADAHOP_ERR_INVALID, "adahop_iht_quant: hadamard_block must be 0 or 32");
+  if (nzero < 0 || (nzero > 0 && !zero_idx))
+    return fail(ADAHOP_ERR_INVALID, "adahop_iht_quant: bad zero list");
+  if (nzero > 0 && zero_axis != ADAHOP_AXIS_ROWS && zero_axis != ADAHOP_AXIS_COLS)
+    return fail(ADAHOP_ERR_INVALID, "adahop_iht_quant: bad zero axis");
+  // Blocks along rows are read 16 bytes at a time; blocks down columns one
+  // element per lane. Codes are written 16 bytes (or 4 bytes) at a time.
+  if (contract == ADAHOP_AXIS_COLS && (!aligned16(src) || ld % 8 != 0 || !aligned16(gathered)))
+    return fail(ADAHOP_ERR_UNSUPPORTED, "adahop_iht_quant: rows must be 16-byte aligned");
+  if (!aligned16(codes))
+    return fail(ADAHOP_ERR_UNSUPPORTED, "adahop_iht_quant: codes must be 16-byte aligned");
+  return iht_quant_launch(src, rows, cols, ld, contract, hadamard_block, zero_idx, nzero,
+                          zero_axis, codes, scales, gathered, static_cast<hipStream_t>(stream));
+}
+
+size_t adahop_gemm_mx_workspace_size(int64_t m, int64_t n, int64_t K, const adahop_oe* oe) {
+  if (!oe || (oe->route != ADAHOP_ROUTE_OE_LEFT && oe->route != ADAHOP_ROUTE_OE_RIGHT)) return 0;
+  if (m < 1 || n < 1 || K < 1 || oe->k < 1) return 0;
+  const int64_t nx = oe->route == ADAHOP_ROUTE_OE_LEFT ? oe->k : m;
+  const int64_t ny = oe->route == ADAHOP_ROUTE_OE_LEFT ? n : oe->k;
+  return align_up(sizeof(float) * (size_t)oe_splits(nx, ny, K) * (size_t)nx * (size_t)ny, kAlign);
+}
+
+adahop_status adahop_gemm_mx(const adahop_mx_operand* A, const adahop_mx_operand* B,
+                             const adahop_oe* oe, void* C, int64_t ldc,
+                             adahop_out_dtype out_dtype, void* ws, size_t ws_bytes,
+                             void* stream) {
+  set_error("");
+  if (!A || !B || !C || !A->codes || !A->scales || !B->codes || !B->scales)
+    return fail(ADAHOP_ERR_INVALID, "adahop_gemm_mx: null pointer");
+  if (A->outer < 1 || B->outer < 1 || A->K != B->K || A->K < 32 || A->K % 32 != 0)
+    return fail(ADAHOP_ERR_INVALID, "adahop_gemm_mx: bad sizes (K must match and be a multiple of 32)");
+  if (ldc < B->outer) return fail(ADAHOP_ERR_INVALID, "adahop_gemm_mx: ldc < n");
+  if (out_dtype != ADAHOP_OUT_BF16 && out_dtype != ADAHOP_OUT_F32)
+    return fail(ADAHOP_ERR_INVALID, "adahop_gemm_mx: bad out_dtype");
+  if (!aligned16(A->codes) || !aligned16(B->codes))
+    return fail(ADAHOP_ERR_UNSUPPORTED, "adahop_gemm_mx: codes must be 16-byte aligned");
+  const int64_t m = A->outer, n = B->outer, K = A->K;
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  OeEpilogue e{};
+  if (oe) {
+    if (oe->k < 1 || !oe->a.ptr || !oe->b.ptr)
+      return fail(ADAHOP_ERR_INVALID, "adahop_gemm_mx: bad outlier descriptor");
+    if (oe->k > kMaxK) return fail(ADAHOP_ERR_UNSUPPORTED, "adahop_gemm_mx: k above 1024");
+    const Bf16View X{oe->a.ptr, oe->a.ld, oe->a.inner_contiguous};
+    const Bf16View Y{oe->b.ptr, oe->b.ld, oe->b.inner_contiguous};
+    if (oe->route == ADAHOP_ROUTE_OE_LEFT || oe->route == ADAHOP_ROUTE_OE_RIGHT) {
+      if (!oe->idx) return fail(ADAHOP_ERR_INVALID, "adahop_gemm_mx: null idx");
+      if (oe->k > (oe->route == ADAHOP_ROUTE_OE_LEFT ? m : n))
+        return fail(ADAHOP_ERR_INVALID, "adahop_gemm_mx: k above the number of lines");
+      const int64_t nx = oe->route == ADAHOP_ROUTE_OE_LEFT ? oe->k : m;
+      const int64_t ny = oe->route == ADAHOP_ROUTE_OE_LEFT ? n : oe->k;
+      const size_t need = adahop_gemm_mx_workspace_size(m, n, K, oe);
+      if (!ws || ws_bytes < need)
+        return fail(ADAHOP_ERR_WORKSPACE, "adahop_gemm_mx: workspace too small: need " +
+                                              std::to_string(need) + " bytes");
+      const int splits = oe_splits(nx, ny, K);
+      ADAHOP_TRY(oe_product_launch(X, Y, nx, ny, K, splits, static_cast<float*>(ws), st));
+      e.mode = oe->route;
+      e.k = oe->k;
+      e.idx = oe->idx;
+      e.partials = static_cast<const float*>(ws);
+      e.splits = splits;
+    } else if (oe->route == ADAHOP_ROUTE_OE_INNER) {
+      e.mode = ADAHOP_ROUTE_OE_INNER;
+      e.k = oe->k;
+      e.a = X;
+      e.b = Y;
+    } else {
+      return fail(ADAHOP_ERR_INVALID, "adahop_gemm_mx: outlier route must be OE_LEFT, OE_RIGHT or OE_INNER");
+    }
+  }
+  return gemm_mx_launch(A->codes, A->scales, B->codes, B->scales, m, n, K, e, C, ldc,
+                        out_dtype == ADAHOP_OUT_F32 ? 1 : 0, st);
+}
+
+adahop_status adahop_gemm_plan(adahop_op op, int64_t T, int64_t Din, int64_t Dout,
+                               adahop_pattern pat_lhs, adahop_pattern pat_rhs,
+                               adahop_route_t route, int32_t oe_rank, adahop_plan* plan) {
+  set_error("");
+  if (!plan) return fail(ADAHOP_ERR_INVALID, "adahop_gemm_plan: null plan");
+  Plan P;
+  ADAHOP_TRY(make_plan(op, T, Din, Dout, pat_lhs, pat_rhs, route, oe_rank, &P));
+  *plan = P.pub;
+  return ADAHOP_OK;
+}
+
+size_t adahop_gemm_workspace_size(adahop_op op, int64_t T, int64_t Din, int64_t Dout,
+                                  adahop_pattern pat_lhs, adahop_pattern pat_rhs,
+                                  adahop_route_t route, int32_t oe_rank) {
+  Plan P;
+  if (make_plan(op, T, Din, Dout, pat_lhs, pat_rhs, route, oe_rank, &P) != ADAHOP_OK) return 0;
+  return P.pub.ws_bytes;
+}
+
+adahop_status adahop_gemm(adahop_op op, const uint16_t* lhs, const uint16_t* rhs, int64_t T,
+                          int64_t Din, int64_t Dout, adahop_pattern pat_lhs,
+                          adahop_pattern pat_rhs, adahop_route_t route, int32_t oe_rank,
+                          void* out, adahop_out_dtype out_dtype, void* ws, size_t ws_bytes,
+                          void* stream) {
+  return run_gemm(op, lhs, rhs, T, Din, Dout, pat_lhs, pat_rhs, route, oe_rank, out, out_dtype,
+                  ws, ws_bytes, static_cast<hipStream_t>(stream), nullptr);
+}
+
+adahop_status adahop_gemm_timed(adahop_op op, const uint16_t* lhs, const uint16_t* rhs,
+                                int64_t T, int64_t Din, int64_t Dout, adahop_pattern pat_lhs,
+                                adahop_pattern pat_rhs, adahop_route_t route, int32_t oe_rank,
+                                void* out, adahop_out_dtype out_dtype, void* ws,
+                                size_t ws_bytes, void* stream, void* const* stage_events) {
+  return run_gemm(op, lhs, rhs, T, Din, Dout, pat_lhs, pat_rhs, route, oe_rank, out, out_dtype,
+                  ws, ws_bytes, static_cast<hipStream_t>(stream), stage_events);
+}
+
+}  // extern "C"

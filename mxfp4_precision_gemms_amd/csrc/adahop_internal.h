@@ -1,0 +1,64 @@
+// Internal declarations of the AdaHOP HIP library (gfx950). Not installed.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstddef>
+#include <cstdint>
+#include <string>
+
+#include "../../include/adahop.h"
+
+namespace adahop {
+
+// Per-thread error detail, set by fail().
+void set_error(const std::string& msg);
+adahop_status fail(adahop_status st, const std::string& msg);
+adahop_status check_launch(const char* what);
+
+inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+constexpr size_t kAlign = 256;
+constexpr int kMaxK = 1024;  // largest outlier rank (FOID top-k, OE lines)
+
+// ---- FOID -----------------------------------------------------------------
+size_t foid_workspace_bytes(int64_t ncand, int32_t k);
+adahop_status foid_launch(const uint16_t* t, int64_t rows, int64_t cols, int64_t ld, int axis,
+                          int32_t probe, int32_t k, int32_t* idx_out, void* ws, size_t ws_bytes,
+                          hipStream_t stream);
+
+// ---- zero + gather + IHT + MXFP4 ------------------------------------------
+adahop_status iht_quant_launch(const uint16_t* src, int64_t rows, int64_t cols, int64_t ld,
+                               int contract, int32_t hadamard_block, const int32_t* zero_idx,
+                               int32_t nzero, int zero_axis, uint8_t* codes, uint8_t* scales,
+                               uint16_t* gathered, hipStream_t stream);
+
+// ---- outlier product (bf16 MFMA) ------------------------------------------
+// P_s[x][y] = sum over t in split s of X(x, t) * Y(y, t), fp32, for s < splits.
+// Partials are laid out [splits][nx][ny].
+struct Bf16View {
+  const uint16_t* ptr;
+  int64_t ld;
+  int inner_contiguous;
+};
+int oe_splits(int64_t nx, int64_t ny, int64_t K);
+adahop_status oe_product_launch(Bf16View X, Bf16View Y, int64_t nx, int64_t ny, int64_t K,
+                                int splits, float* partials, hipStream_t stream);
+// Full bf16 product written to C (the BF16 route): C[i][j] = sum_t X(i,t) Y(j,t).
+adahop_status bf16_gemm_launch(Bf16View X, Bf16View Y, int64_t m, int64_t n, int64_t K,
+                               void* C, int64_t ldc, int out_f32, hipStream_t stream);
+
+// ---- FP4 GEMM with the OE epilogue ----------------------------------------
+struct OeEpilogue {
+  int mode;                 // 0 none, ADAHOP_ROUTE_OE_LEFT / _OE_RIGHT / _OE_INNER
+  int32_t k;
+  const int32_t* idx;       // OE_LEFT / OE_RIGHT
+  const float* partials;    // OE_LEFT: [splits][k][n]; OE_RIGHT: [splits][m][k]
+  int splits;
+  Bf16View a, b;            // OE_INNER factors: a [m][k], b [n][k]
+};
+adahop_status gemm_mx_launch(const uint8_t* a_codes, const uint8_t* a_scales,
+                             const uint8_t* b_codes, const uint8_t* b_scales, int64_t m,
+                             int64_t n, int64_t K, const OeEpilogue& oe, void* C, int64_t ldc,
+                             int out_f32, hipStream_t stream);
+
+}  // namespace adahop

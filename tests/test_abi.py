@@ -1,0 +1,111 @@
+"""The C ABI on the host: the library loads, exports every declared symbol,
+and its host-only paths (routing, plans, argument checks) behave as the
+header states. No GPU: nothing here launches a kernel."""
+import ctypes
+import itertools
+import os
+import re
+
+import pytest
+
+import mxfp4_precision_gemms_amd as A
+import oracle
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                      "include", "adahop.h")
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"ADAHOP_API\s+[^;(]*?\b(adahop_\w+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol():
+    syms = declared_symbols()
+    assert len(syms) >= 12, syms
+    lib = A.lib()
+    for s in syms:
+        assert hasattr(lib, s), s
+    assert set(syms) == set(A.SIGNATURES), set(syms) ^ set(A.SIGNATURES)
+
+
+def test_status_strings():
+    lib = A.lib()
+    for st, word in ((0, b"ok"), (1, b"invalid"), (3, b"workspace"), (4, b"HIP")):
+        assert word in lib.adahop_status_string(st)
+    assert lib.adahop_version() >= 1
+
+
+def test_route_matches_oracle_on_every_cell():
+    for op in ("FWD", "DGRAD", "WGRAD"):
+        for pl, pr in itertools.product("NRC", repeat=2):
+            assert A.adahop_route(op, pl, pr) == oracle.route(op, pl, pr), (op, pl, pr)
+    assert A.lib().adahop_route(7, 0, 0) == -1
+    assert A.lib().adahop_route(0, 3, 0) == -1
+
+
+@pytest.mark.parametrize("op,pl,pr", [("FWD", "R", "N"), ("FWD", "N", "R"), ("DGRAD", "R", "N"),
+                                      ("DGRAD", "N", "C"), ("WGRAD", "C", "N"),
+                                      ("WGRAD", "R", "C")])
+def test_plan_scan_target_matches_oracle(op, pl, pr):
+    p = A.adahop_gemm_plan(op, 256, 128, 192, pl, pr, None, 8)
+    r = oracle.route(op, pl, pr)
+    assert A.ROUTE_NAME[p.route] == r
+    assert (p.scan_tensor, p.scan_axis) == oracle.scan_target(op, r)
+    m, n, K = {"FWD": (256, 192, 128), "DGRAD": (256, 128, 192), "WGRAD": (192, 128, 256)}[op]
+    assert (p.m, p.n, p.K, p.k) == (m, n, K, 8)
+    assert p.ws_bytes > 0 and p.ws_bytes % 256 == 0
+    offs = [p.off_idx, p.off_a_codes, p.off_a_scales, p.off_b_codes, p.off_b_scales]
+    assert all(o % 256 == 0 and o < p.ws_bytes for o in offs)
+
+
+def test_plan_errors():
+    with pytest.raises(A.AdahopError) as e:
+        A.adahop_gemm_plan("FWD", 64, 100, 64)             # K = Din = 100
+    assert e.value.status == 1 and "multiple of 32" in str(e.value)
+    with pytest.raises(A.AdahopError) as e:
+        A.adahop_gemm_plan("WGRAD", 64, 64, 64, "R", "C", None, 65)   # k > 64 columns of X
+    assert e.value.status == 1
+    with pytest.raises(A.AdahopError) as e:
+        A.adahop_gemm_plan("WGRAD", 4096, 4096, 64, "R", "C", None, 2000)
+    assert e.value.status == 2                               # above 1024
+    # The BF16 route needs no workspace and accepts any K.
+    assert A.adahop_gemm_plan("FWD", 64, 100, 64, "R", "R").ws_bytes == 0
+
+
+def test_argument_checks_return_before_any_launch():
+    lib = A.lib()
+    fake = ctypes.c_void_p(256)   # never dereferenced: every call below fails its checks first
+    # K % 32 != 0
+    assert lib.adahop_iht_quant(fake, 32, 33, 33, 1, 32, None, 0, 0, fake, fake, None, None) == 1
+    # bad hadamard block
+    assert lib.adahop_iht_quant(fake, 32, 64, 64, 1, 16, None, 0, 0, fake, fake, None, None) == 1
+    # zero list without pointer
+    assert lib.adahop_iht_quant(fake, 32, 64, 64, 1, 32, None, 3, 0, fake, fake, None, None) == 1
+    # ld < cols
+    assert lib.adahop_iht_quant(fake, 32, 64, 32, 1, 32, None, 0, 0, fake, fake, None, None) == 1
+    # misaligned rows (blocks along rows), misaligned codes
+    assert lib.adahop_iht_quant(ctypes.c_void_p(258), 32, 64, 64, 1, 32, None, 0, 0, fake, fake,
+                                None, None) == 2
+    assert lib.adahop_iht_quant(fake, 64, 30, 30, 0, 32, None, 0, 0, ctypes.c_void_p(260), fake,
+                                None, None) == 2
+    # FOID: k > candidates, probe < 1, null
+    assert lib.adahop_detect(fake, 10, 20, 20, 0, 64, 11, fake, None, 0, None) == 1
+    assert lib.adahop_detect(fake, 10, 20, 20, 0, 0, 5, fake, None, 0, None) == 1
+    assert lib.adahop_detect(None, 10, 20, 20, 0, 64, 5, fake, None, 0, None) == 1
+    assert lib.adahop_detect(fake, 3000, 20, 20, 0, 64, 2000, fake, None, 0, None) == 2
+    # GEMM: workspace too small, K mismatch
+    assert lib.adahop_gemm(0, fake, fake, 64, 64, 64, 0, 0, -1, 64, fake, 0, None, 0, None) == 3
+    Aop = A.MxOperand(256, 256, 64, 64)
+    Bop = A.MxOperand(256, 256, 64, 96)
+    assert lib.adahop_gemm_mx(ctypes.byref(Aop), ctypes.byref(Bop), None, fake, 64, 0, None, 0,
+                              None) == 1
+    assert b"K" in lib.adahop_last_error()
+
+
+def test_workspace_sizes():
+    assert A.adahop_detect_workspace_size(100, 64, "ROWS", 10) == 0          # one level
+    assert A.adahop_detect_workspace_size(65536, 64, "ROWS", 64) > 0         # several levels
+    ws = A.adahop_gemm_workspace_size("WGRAD", 32768, 14336, 4096, "R", "C", None, 64)
+    # packed operands: (4096 + 14336) x 32768 x 17/32 bytes, plus lines and partials
+    assert 0.5e9 > ws > (4096 + 14336) * 32768 * 17 // 32

@@ -1,0 +1,309 @@
+"""GPU vs oracle parity of each stage and of whole AdaHOP products, on seeded
+inputs, at sizes the oracle finishes in seconds (several tiles plus ragged
+tails). Bit-exact: FOID indices, MXFP4 codes and scales, gathered lines.
+Outputs: the GEMM bar in tests/parity.py."""
+import numpy as np
+import pytest
+import torch
+
+import mxfp4_precision_gemms_amd as A
+import oracle
+import synth
+from oracle import pipeline
+from parity import bf16_to_f32, check_bf16, check_f32, f32_to_bf16_rne
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+def dev_bf16(x: np.ndarray) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).to(DEV).view(torch.bfloat16)
+
+
+def host(t: torch.Tensor) -> np.ndarray:
+    t = t.detach().cpu()
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).numpy().view(np.uint16)
+    return t.numpy()
+
+
+def rand_bf16(rng, shape, scale=1.0, planted=None, factor=50.0):
+    x = (rng.standard_normal(shape) * scale).astype(np.float32)
+    if planted is not None:
+        axis, lines = planted
+        if axis == 0:
+            x[lines, :] *= factor
+        else:
+            x[:, lines] *= factor
+    return f32_to_bf16_rne(x)
+
+
+# --------------------------------------------------------------------------
+# IHT + MXFP4 quantization (with zeroing and gathering)
+# --------------------------------------------------------------------------
+QUANT_CASES = [
+    # rows, cols, contract, hadamard, zero_axis, nzero
+    (64, 512, "COLS", 32, None, 0),
+    (37, 96, "COLS", 32, None, 0),          # ragged rows, K = 96
+    (300, 4160, "COLS", 32, "ROWS", 7),     # K spans 3 workgroup chunks, ragged
+    (300, 4160, "COLS", 32, "COLS", 9),
+    (128, 2048, "COLS", 0, "ROWS", 5),      # no rotation (plain MXFP4)
+    (96, 200, "ROWS", 32, None, 0),         # K = 96 down columns, ragged outer
+    (544, 130, "ROWS", 32, "COLS", 6),
+    (544, 130, "ROWS", 32, "ROWS", 11),
+    (1024, 64, "ROWS", 0, "COLS", 3),
+    (32, 8, "ROWS", 32, None, 0),           # one block per column
+]
+
+
+@pytest.mark.parametrize("case", QUANT_CASES, ids=[str(c) for c in QUANT_CASES])
+def test_iht_quant_bit_exact(case):
+    rows, cols, contract, had, zaxis, nz = case
+    rng = np.random.default_rng(rows * 7 + cols)
+    src = rand_bf16(rng, (rows, cols), planted=(1, rng.choice(cols, 2, replace=False)))
+    zidx = None
+    if nz:
+        dim = rows if zaxis == "ROWS" else cols
+        zidx = np.sort(rng.choice(dim, nz, replace=False)).astype(np.int32)
+    say("iht_quant", case)
+    codes, scales, gathered = A.adahop_iht_quant(
+        dev_bf16(src), contract, had,
+        None if zidx is None else torch.from_numpy(zidx).to(DEV), zaxis or "ROWS")
+    torch.cuda.synchronize()
+    rc, rs, rg = oracle.iht_quant(src, oracle.COLS if contract == "COLS" else oracle.ROWS, had,
+                                  zidx, oracle.ROWS if zaxis in (None, "ROWS") else oracle.COLS)
+    assert np.array_equal(host(codes), rc)
+    assert np.array_equal(host(scales), rs)
+    if nz:
+        assert np.array_equal(host(gathered), rg)
+
+
+def all_finite_bf16(limit_exp=None):
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    exp = (bits >> 7) & 0xFF
+    keep = exp != 0xFF
+    if limit_exp is not None:
+        keep &= exp < limit_exp
+    return bits[keep]
+
+
+@pytest.mark.parametrize("had", [0, 32])
+@pytest.mark.parametrize("contract", ["COLS", "ROWS"])
+def test_iht_quant_every_bf16_pattern(had, contract):
+    """Every finite bf16 value (subnormals, signed zeros, extremes) in random
+    blocks; with the rotation the magnitudes stay below 2^100 so that no
+    butterfly overflows (non-finite inputs are outside the contract)."""
+    vals = all_finite_bf16(None if had == 0 else 127 + 100)
+    rng = np.random.default_rng(had + len(contract))
+    reps = []
+    for _ in range(3):
+        reps.append(rng.permutation(vals))
+    # Also whole blocks of tiny values so that a block scale clamps.
+    tiny = vals[((vals >> 7) & 0xFF) < 3]
+    reps.append(rng.permutation(np.tile(tiny, 4)))
+    flat = np.concatenate(reps)
+    flat = flat[: flat.size // 4096 * 4096]
+    src = flat.reshape(-1, 256) if contract == "COLS" else flat.reshape(256, -1)
+    say("iht_quant every bf16", had, contract, src.shape)
+    codes, scales, _ = A.adahop_iht_quant(dev_bf16(src), contract, had)
+    torch.cuda.synchronize()
+    rc, rs, _ = oracle.iht_quant(src, oracle.COLS if contract == "COLS" else oracle.ROWS, had)
+    assert np.array_equal(host(scales), rs)
+    assert np.array_equal(host(codes), rc)
+
+
+# --------------------------------------------------------------------------
+# FOID
+# --------------------------------------------------------------------------
+FOID_CASES = [
+    # rows, cols, axis, k, probe, integer-valued (ties)
+    (64, 512, "COLS", 16, 64, False),
+    (200, 333, "COLS", 40, 64, True),
+    (333, 200, "ROWS", 40, 64, True),
+    (40, 1000, "COLS", 64, 64, False),       # columns shorter than the probe (P = 40)
+    (100, 5000, "COLS", 64, 64, False),      # two selection levels
+    (70000, 64, "ROWS", 64, 64, False),      # three levels
+    (9000, 128, "ROWS", 1024, 64, True),     # k at its maximum
+    (128, 300, "COLS", 300, 64, False),      # k = all candidates
+    (96, 256, "ROWS", 7, 16, True),          # shorter probe
+]
+
+
+@pytest.mark.parametrize("case", FOID_CASES, ids=[str(c) for c in FOID_CASES])
+def test_foid_bit_exact(case):
+    rows, cols, axis, k, probe, ints = case
+    rng = np.random.default_rng(rows + cols + k)
+    if ints:
+        t = f32_to_bf16_rne(rng.integers(-3, 4, size=(rows, cols)).astype(np.float32))
+    else:
+        dim = cols if axis == "COLS" else rows
+        lines = rng.choice(dim, min(dim, 2 * k), replace=False)
+        t = rand_bf16(rng, (rows, cols), planted=(1 if axis == "COLS" else 0, lines),
+                      factor=rng.uniform(1, 3))
+    say("foid", case)
+    idx = A.adahop_detect(dev_bf16(t), axis, k, probe)
+    torch.cuda.synchronize()
+    ref = oracle.foid(t, oracle.COLS if axis == "COLS" else oracle.ROWS, k, probe)
+    assert np.array_equal(host(idx), ref)
+
+
+# --------------------------------------------------------------------------
+# Pre-quantized GEMM with and without the outlier term
+# --------------------------------------------------------------------------
+def packed_operands(rng, m, n, K):
+    a = rand_bf16(rng, (m, K), planted=(1, rng.choice(K, 3, replace=False)))
+    b = rand_bf16(rng, (n, K), scale=0.02)
+    ac, as_, _ = oracle.iht_quant(a, oracle.COLS, 32)
+    bc, bs, _ = oracle.iht_quant(b, oracle.COLS, 32)
+    return a, b, ac, as_, bc, bs
+
+
+GEMM_CASES = [(256, 128, 128), (512, 384, 512), (300, 200, 96), (33, 1000, 160), (1024, 256, 1024)]
+
+
+@pytest.mark.parametrize("m,n,K", GEMM_CASES)
+def test_gemm_mx(m, n, K):
+    rng = np.random.default_rng(m + n + K)
+    _, _, ac, as_, bc, bs = packed_operands(rng, m, n, K)
+    ref, absC = oracle.gemm_mx(ac, as_, bc, bs)
+    d = [torch.from_numpy(x).to(DEV) for x in (ac, as_, bc, bs)]
+    say("gemm_mx f32", m, n, K)
+    c32 = A.adahop_gemm_mx(*d, out_dtype=torch.float32)
+    say("gemm_mx bf16", m, n, K)
+    c16 = A.adahop_gemm_mx(*d, out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    C32, C16 = host(c32), host(c16)
+    check_f32(C32, ref, absC, K, "gemm f32")
+    check_bf16(C16, ref, absC, K, "gemm bf16")
+    # One rounding: the bf16 output is the fp32 result rounded to nearest even.
+    assert np.array_equal(C16, f32_to_bf16_rne(C32))
+
+
+@pytest.mark.parametrize("route", ["OE_LEFT", "OE_RIGHT", "OE_INNER"])
+def test_gemm_mx_outlier_term(route):
+    m, n, K, k = 320, 192, 256, 12
+    rng = np.random.default_rng(5)
+    a, b, ac, as_, bc, bs = packed_operands(rng, m, n, K)
+    ref, absC = oracle.gemm_mx(ac, as_, bc, bs)
+    if route == "OE_LEFT":
+        idx = np.sort(rng.choice(m, k, replace=False)).astype(np.int32)
+        la = rand_bf16(rng, (k, K))                      # (p, t)
+        oe_ref, oe_abs = oracle.gemm_bf16(la, 0, b, 1, K, np.arange(k), np.arange(n))
+        ref[idx, :] += oe_ref; absC[idx, :] += oe_abs
+        oe = {"route": route, "k": k, "idx": torch.from_numpy(idx).to(DEV),
+              "a": (dev_bf16(la), True), "b": (dev_bf16(b), True)}
+    elif route == "OE_RIGHT":
+        idx = np.sort(rng.choice(n, k, replace=False)).astype(np.int32)
+        lbT = rand_bf16(rng, (K, k))                     # (t, p) stored t-major
+        oe_ref, oe_abs = oracle.gemm_bf16(a, 0, lbT, 0, K, np.arange(m), np.arange(k))
+        ref[:, idx] += oe_ref; absC[:, idx] += oe_abs
+        oe = {"route": route, "k": k, "idx": torch.from_numpy(idx).to(DEV),
+              "a": (dev_bf16(a), True), "b": (dev_bf16(lbT), False)}
+    else:
+        ga = rand_bf16(rng, (m, k)); gb = rand_bf16(rng, (n, k))
+        oe_ref, oe_abs = oracle.gemm_bf16(ga, 0, gb, 1, k, np.arange(m), np.arange(n))
+        ref += oe_ref; absC += oe_abs
+        oe = {"route": route, "k": k, "a": (dev_bf16(ga), True), "b": (dev_bf16(gb), True)}
+    d = [torch.from_numpy(x).to(DEV) for x in (ac, as_, bc, bs)]
+    say("gemm_mx outlier", route)
+    c32 = A.adahop_gemm_mx(*d, oe=oe, out_dtype=torch.float32)
+    c16 = A.adahop_gemm_mx(*d, oe=oe, out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    check_f32(host(c32), ref, absC, K, route)
+    check_bf16(host(c16), ref, absC, K, route)
+    assert np.array_equal(host(c16), f32_to_bf16_rne(host(c32)))
+
+
+# --------------------------------------------------------------------------
+# Whole products: every op x route family, bit-exact intermediates
+# --------------------------------------------------------------------------
+def operands(op, T, Din, Dout, pl, pr, seed):
+    shapes = {"FWD": ((T, Din), (Dout, Din)), "DGRAD": ((T, Dout), (Dout, Din)),
+              "WGRAD": ((T, Dout), (T, Din))}[op]
+    sig = {"FWD": (1.0, 0.02), "DGRAD": (1e-3, 0.02), "WGRAD": (1e-3, 1.0)}[op]
+    out = []
+    for t, (pat, shape, s) in enumerate(zip((pl, pr), shapes, sig)):
+        axis = {"R": 0, "C": 1, "N": -1}[pat]
+        dim = shape[0] if pat == "R" else shape[1]
+        lines = synth.pick_lines(seed, 50 + t, dim, max(1, dim // 100)) if pat != "N" else None
+        out.append(synth.fill_bf16(shape[0], shape[1], seed, 60 + t, s, axis, lines, 50.0))
+    return out
+
+
+def run_and_compare(op, lhs, rhs, T, Din, Dout, pl, pr, route, k, rows=None, cols=None):
+    say("adahop_gemm", op, (T, Din, Dout), pl + pr, route, k)
+    plan = A.adahop_gemm_plan(op, T, Din, Dout, pl, pr, route, k)
+    ws = torch.zeros(max(plan.ws_bytes, 1), dtype=torch.uint8, device=DEV)
+    L, R = dev_bf16(lhs), dev_bf16(rhs)
+    c32 = A.adahop_gemm(op, L, R, pl, pr, route, k, out_dtype=torch.float32, ws=ws)
+    c16 = A.adahop_gemm(op, L, R, pl, pr, route, k, out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    ref = pipeline.gemm(op, lhs, rhs, T, Din, Dout, pl, pr, route=route, k=k, rows=rows, cols=cols)
+    assert A.ROUTE_NAME[plan.route] == ref["route"]
+    if ref["route"] != "BF16":
+        v = A.workspace_views(ws, plan)
+        if ref["idx"] is not None:
+            assert np.array_equal(host(v["idx"]), ref["idx"])
+        for key in ("a_codes", "a_scales", "b_codes", "b_scales"):
+            assert np.array_equal(host(v[key]), ref[key]), key
+    C32, C16 = host(c32), host(c16)
+    if rows is not None:
+        C32 = C32[np.ix_(rows, cols)]
+        C16 = C16[np.ix_(rows, cols)]
+    K = ref["K"]
+    check_f32(C32, ref["C"], ref["absC"], K, f"{op} {ref['route']} f32")
+    rel, loose = check_bf16(C16, ref["C"], ref["absC"], K, f"{op} {ref['route']} bf16")
+    assert np.array_equal(C16, f32_to_bf16_rne(C32))
+    return ref
+
+
+FULL_CASES = [
+    # op, T, Din, Dout, pl, pr, route, k
+    ("FWD", 256, 512, 512, "C", "N", None, 64),
+    ("FWD", 256, 512, 512, "C", "N", "OE_INNER", 16),
+    ("FWD", 256, 512, 512, "C", "N", "MXFP4", 64),
+    ("FWD", 300, 256, 200, "R", "N", None, 8),          # OE_LEFT (X rows)
+    ("FWD", 300, 256, 200, "N", "R", None, 8),          # OE_RIGHT (W rows)
+    ("FWD", 96, 64, 80, "R", "R", None, 8),             # BF16
+    ("DGRAD", 512, 384, 256, "R", "N", None, 8),        # OE_LEFT (GY rows)
+    ("DGRAD", 512, 384, 256, "N", "N", None, 64),       # IHT, W column-major
+    ("DGRAD", 320, 192, 256, "N", "C", None, 8),        # OE_RIGHT (W cols)
+    ("DGRAD", 320, 192, 256, "C", "N", "OE_INNER", 8),
+    ("WGRAD", 512, 384, 256, "R", "C", None, 8),        # OE_RIGHT (X cols)
+    ("WGRAD", 512, 384, 256, "C", "N", None, 8),        # OE_LEFT (GY cols)
+    ("WGRAD", 416, 160, 96, "R", "N", "OE_INNER", 8),
+    ("WGRAD", 128, 96, 64, "C", "C", None, 8),          # BF16
+]
+
+
+@pytest.mark.parametrize("case", FULL_CASES, ids=[str(c) for c in FULL_CASES])
+def test_full_product(case):
+    op, T, Din, Dout, pl, pr, route, k = case
+    lhs, rhs = operands(op, T, Din, Dout, pl, pr, seed=T + Din)
+    run_and_compare(op, lhs, rhs, T, Din, Dout, pl, pr, route, k)
+
+
+def test_deterministic_reruns():
+    op, T, Din, Dout = "WGRAD", 1024, 768, 512
+    lhs, rhs = operands(op, T, Din, Dout, "R", "C", 3)
+    L, R = dev_bf16(lhs), dev_bf16(rhs)
+    say("determinism")
+    a = A.adahop_gemm(op, L, R, "R", "C", None, 16)
+    b = A.adahop_gemm(op, L, R, "R", "C", None, 16)
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+def test_stage_events_record():
+    op, T, Din, Dout = "WGRAD", 512, 384, 256
+    lhs, rhs = operands(op, T, Din, Dout, "R", "C", 4)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(A.STAGE_EVENTS)]
+    say("stage events")
+    A.adahop_gemm(op, dev_bf16(lhs), dev_bf16(rhs), "R", "C", None, 8, stage_events=ev)
+    torch.cuda.synchronize()
+    times = [ev[i].elapsed_time(ev[i + 1]) for i in range(A.STAGE_EVENTS - 1)]
+    assert all(t >= 0 for t in times)
