@@ -1,0 +1,230 @@
+"""Benchmark of one AdaHOP product (FOID + IHT + MXFP4 quantization + fused
+FP4/bf16 GEMM + scatter-add) on one MI355X.
+
+Default workload: the Llama3.1-8B down_proj weight gradient dW = GY^T X over
+32768 tokens (seq 4096 x batch 8), GY [32768,4096] Row-wise (0.5% of rows
+x100), X [32768,14336] Column-wise (1% of columns x50): RC pair -> OE-Right
+with rank 64, i.e. every stage of the path runs. A step is one adahop_gemm
+call on inputs already resident in HBM.
+
+Prints one JSON line: effective TFLOP/s (2 m n K / wall time of the call),
+ms per call, per-stage times from HIP events recorded by the library on the
+call's stream, the roofline of the dominant kernel (the fused GEMM) and the
+oracle timed on the host's cores on a bounded sample.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = ("effective TFLOPS per AdaHOP GEMM (FOID+IHT+quant+GEMM+OE) and % MXFP4 MFMA peak")
+PEAK_FP4_TFLOPS = 10100.0      # MI355X dense MXFP4 matrix-core peak
+PEAK_HBM_GBS = 8000.0
+
+
+def workloads():
+    from synth import workloads as W
+    out = {"l8b_down_wgrad": (W.l31_8b_down_wgrad(), 0)}
+    g = W.l31_8b_gateup_fwd_dgrad()
+    out["l8b_gateup_fwd"] = (g, 0)
+    out["l8b_gateup_dgrad"] = (g, 1)
+    out["l1b_up_fwd"] = (W.l32_1b_up_fwd(), 0)
+    out["tiny_fwd"] = (W.tiny_fwd(), 0)
+    for bs in (1, 2, 4, 8, 16):
+        t = W.l31_8b_oproj_triplet(bs)
+        for i, name in enumerate(("fwd", "dgrad", "wgrad")):
+            out[f"l8b_oproj_bs{bs}_{name}"] = (t, i)
+    return out
+
+
+def gemm_dims(op, T, Din, Dout):
+    return {"FWD": (T, Dout, Din), "DGRAD": (T, Din, Dout), "WGRAD": (Dout, Din, T)}[op]
+
+
+def cpu_baseline(op, lhs, rhs, T, Din, Dout, call, m, n, K, budget_s=12.0):
+    """The oracle, as it stands, on a bounded sample of the same call,
+    extrapolated to the full call: FOID in full; zero+IHT+quantization of
+    both operands on a slab of contraction blocks (scaled by K / slab); the
+    fp64 product of the dequantized operands on an output tile over that
+    slab (scaled by m n K / (tile x slab)); the outlier product is inside the
+    residual-product estimate's margin and is not timed separately."""
+    import numpy as np
+
+    import oracle
+
+    t_all = time.perf_counter()
+    route = call.route or oracle.route(op, call.pat_lhs, call.pat_rhs)
+    t0 = time.perf_counter()
+    idx = None
+    if route in ("OE_LEFT", "OE_RIGHT", "OE_INNER"):
+        tensor, axis = oracle.scan_target(op, route)
+        idx = oracle.foid(lhs if tensor == 0 else rhs, axis, call.k)
+    t_foid = time.perf_counter() - t0
+
+    contract = {"FWD": (1, 1), "DGRAD": (1, 0), "WGRAD": (0, 0)}[op]
+    slab = min(K, 2048)
+    def cut(x, c):      # the first `slab` contraction positions of a stored operand
+        return np.ascontiguousarray(x[:, :slab] if c == oracle.COLS else x[:slab, :])
+    t0 = time.perf_counter()
+    ac, as_, _ = oracle.iht_quant(cut(lhs, contract[0]), contract[0], 32)
+    bc, bs, _ = oracle.iht_quant(cut(rhs, contract[1]), contract[1], 32)
+    t_k2 = (time.perf_counter() - t0) * (K / slab)
+
+    # Output tile grown until the product takes a measurable share of the budget.
+    side, t_g = 64, 0.0
+    while True:
+        rows = np.arange(min(side, m)); cols = np.arange(min(side, n))
+        t0 = time.perf_counter()
+        oracle.gemm_mx(ac, as_, bc, bs, rows, cols)
+        t_g = time.perf_counter() - t0
+        done = time.perf_counter() - t_all
+        if t_g > budget_s / 4 or side >= min(m, n) or done + 4 * t_g > budget_s:
+            break
+        side *= 2
+    t_gemm = t_g * (m * n * K) / (rows.size * cols.size * slab)
+    total = t_foid + t_k2 + t_gemm
+    return {
+        "value": 2.0 * m * n * K / total / 1e12,
+        "unit": "TFLOP/s",
+        "cores": oracle.max_threads(),
+        "kind": "oracle",
+        "sample": (f"FOID in full ({t_foid:.2f}s); IHT+quant of both operands on the first "
+                   f"{slab} of K={K} contraction positions, x{K / slab:.0f}; fp64 product on a "
+                   f"{rows.size}x{cols.size} output tile over that slab, "
+                   f"x{m * n * K / (rows.size * cols.size * slab):.3g}; "
+                   f"extrapolated call time {total:.1f}s"),
+        "sample_wall_s": round(time.perf_counter() - t_all, 2),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="l8b_down_wgrad")
+    ap.add_argument("--out-dtype", default="bf16", choices=["bf16", "f32"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-bf16-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
+              "(the path has no collectives; see the sharding note in the design document)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import mxfp4_precision_gemms_amd as A
+
+    wls = workloads()
+    if args.workload not in wls:
+        sys.exit(f"unknown workload {args.workload}; choose from {sorted(wls)}")
+    wl, ci = wls[args.workload]
+    call = wl.calls[ci]
+    op = call.op
+    T, Din, Dout = wl.T, wl.Din, wl.Dout
+    m, n, K = gemm_dims(op, T, Din, Dout)
+    dev = torch.device("cuda:0")
+    print(f"# workload {wl.name} call {ci}: {op} m={m} n={n} K={K}", file=sys.stderr, flush=True)
+
+    t0 = time.perf_counter()
+    lhs_np = wl.tensors[call.lhs].make(0)
+    rhs_np = wl.tensors[call.rhs].make(0)
+    to_dev = lambda x: torch.from_numpy(x.view(np.int16)).to(dev).view(torch.bfloat16)
+    lhs, rhs = to_dev(lhs_np), to_dev(rhs_np)
+    print(f"# inputs ready in {time.perf_counter() - t0:.1f}s", file=sys.stderr, flush=True)
+
+    out_dtype = torch.bfloat16 if args.out_dtype == "bf16" else torch.float32
+    plan = A.adahop_gemm_plan(op, T, Din, Dout, call.pat_lhs, call.pat_rhs, call.route, call.k)
+    route = A.ROUTE_NAME[plan.route]
+    ws = torch.empty(max(plan.ws_bytes, 1), dtype=torch.uint8, device=dev)
+    out_shape = {"FWD": (T, Dout), "DGRAD": (T, Din), "WGRAD": (Dout, Din)}[op]
+    out = torch.empty(out_shape, dtype=out_dtype, device=dev)
+
+    def step(events=None):
+        A.adahop_gemm(op, lhs, rhs, call.pat_lhs, call.pat_rhs, call.route, call.k,
+                      out=out, ws=ws, stage_events=events)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(A.STAGE_EVENTS)]
+          for _ in range(args.steps)]
+    for e in ev:                       # create the underlying events outside the timed region
+        for x in e:
+            x.record()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(ev[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall / args.steps * 1e3
+
+    stage_ms = {}
+    for si, name in enumerate(A.STAGES):
+        stage_ms[name] = float(np.mean([e[si].elapsed_time(e[si + 1]) for e in ev]))
+    call_ms = float(np.mean([e[0].elapsed_time(e[-1]) for e in ev]))
+    flops = 2.0 * m * n * K
+    value = flops / (ms_per_step / 1e3) / 1e12
+    gemm_ms = stage_ms["gemm"]
+    achieved = flops / (gemm_ms / 1e3) / 1e12
+
+    result = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "mxfp4",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "op": op, "route": route, "m": m, "n": n, "K": K,
+                   "oe_rank": plan.k, "pattern_pair": call.pat_lhs + call.pat_rhs,
+                   "out_dtype": args.out_dtype},
+        "pct_mxfp4_peak": round(100 * value / PEAK_FP4_TFLOPS, 2),
+        "stages_ms": {k: round(v, 4) for k, v in stage_ms.items()},
+        "call_ms_events": round(call_ms, 4),
+        "roofline": {"bound": "mfma", "kernel": "gemm_mx_kernel (+ scatter-add epilogue)",
+                     "achieved": round(achieved, 1), "peak": PEAK_FP4_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP4_TFLOPS, 4),
+                     "traffic": None},
+    }
+
+    if not args.no_bf16_baseline:
+        # All-bf16 reference product on hipBLASLt (torch.matmul), same shapes.
+        a2 = {"FWD": lambda: (lhs, rhs.t().contiguous()),
+              "DGRAD": lambda: (lhs, rhs),
+              "WGRAD": lambda: (lhs.t().contiguous(), rhs)}[op]()
+        for _ in range(3):
+            torch.matmul(*a2)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(max(3, args.steps // 2)):
+            torch.matmul(*a2)
+        torch.cuda.synchronize()
+        bms = (time.perf_counter() - t0) / max(3, args.steps // 2) * 1e3
+        result["bf16_matmul_ms"] = round(bms, 4)
+        result["speedup_vs_bf16_matmul"] = round(bms / ms_per_step, 3)
+        del a2
+
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(op, lhs_np, rhs_np, T, Din, Dout, call, m, n, K)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

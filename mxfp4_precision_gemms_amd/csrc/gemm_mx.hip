@@ -25,6 +25,8 @@
 //   scatter-add). Inner extraction (rank-k term on every output) runs as extra
 //   bf16 MFMAs on the tile's own accumulators. No atomics: results are
 //   deterministic.
+#include <utility>
+
 #include "adahop_internal.h"
 
 namespace adahop {
@@ -43,6 +45,17 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float v) {
 // Row of a 32x32 MFMA accumulator held in register v by lane l (column l%32).
 __device__ __forceinline__ int acc_row(int v, int lane) {
   return 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+}
+
+// Calls f(std::integral_constant<int, 0>) ... f(<N-1>): loops whose index
+// must be a compile-time constant (register arrays stay in registers).
+template <typename F, int... Is>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, Is...>) {
+  (f(std::integral_constant<int, Is>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
 }
 
 // ---------------------------------------------------------------------------
@@ -92,6 +105,9 @@ __device__ __forceinline__ uint16_t view_at(const uint16_t* p, int64_t ld, int i
   return inner ? p[r * ld + t] : p[t * ld + r];
 }
 
+// KAligned: K % 128 == 0, so every stage is whole and a row's 4 scale bytes of
+// a stage form one aligned dword.
+template <bool KAligned>
 __global__ void __launch_bounds__(kGemmThreads, 2) gemm_mx_kernel(GemmArgs g) {
   __shared__ __attribute__((aligned(16))) uint8_t s_a[2][kLdsA];
   __shared__ __attribute__((aligned(16))) uint8_t s_b[2][kLdsB];
@@ -125,42 +141,45 @@ __global__ void __launch_bounds__(kGemmThreads, 2) gemm_mx_kernel(GemmArgs g) {
   // Global -> register staging: A 4 chunks, B 2 chunks of 16 bytes per thread.
   uint4 ra[4], rb[2];
   uint32_t rsa = 0, rsb = 0;
+  // A stage's 4 scale bytes of one row; past K they read as 0 (their codes are 0 too).
+  auto load_scales = [&](const uint8_t* sc, int64_t row, int64_t sb0) -> uint32_t {
+    if (KAligned) return *reinterpret_cast<const uint32_t*>(sc + row * Ks + sb0);
+    uint32_t v = 0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int64_t col = sb0 + q < Ks ? sb0 + q : Ks - 1;
+      const uint32_t b = sc[row * Ks + col];
+      v |= (sb0 + q < Ks ? b : 0u) << (8 * q);
+    }
+    return v;
+  };
   auto load_stage = [&](int kt) {
     const int64_t kb0 = (int64_t)kt * BKB;
     const int c = tid & 3;
-    const bool kin = kb0 + c * 16 < Kb;
+    const bool kin = KAligned || kb0 + c * 16 < Kb;
+    const int64_t kc = kin ? kb0 + c * 16 : 0;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       int64_t row = m0 + (tid >> 2) + 64 * i;
       row = row < g.m ? row : g.m - 1;
-      ra[i] = kin ? *reinterpret_cast<const uint4*>(g.a_codes + row * Kb + kb0 + c * 16)
-                  : make_uint4(0, 0, 0, 0);
+      const uint4 q = *reinterpret_cast<const uint4*>(g.a_codes + row * Kb + kc);
+      ra[i] = kin ? q : make_uint4(0, 0, 0, 0);
     }
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       int64_t row = n0 + (tid >> 2) + 64 * i;
       row = row < g.n ? row : g.n - 1;
-      rb[i] = kin ? *reinterpret_cast<const uint4*>(g.b_codes + row * Kb + kb0 + c * 16)
-                  : make_uint4(0, 0, 0, 0);
+      const uint4 q = *reinterpret_cast<const uint4*>(g.b_codes + row * Kb + kc);
+      rb[i] = kin ? q : make_uint4(0, 0, 0, 0);
     }
     const int64_t sb0 = (int64_t)kt * 4;
     {
       int64_t row = m0 + tid;
-      row = row < g.m ? row : g.m - 1;
-      uint32_t v = 0;
-#pragma unroll
-      for (int q = 0; q < 4; ++q)
-        if (sb0 + q < Ks) v |= (uint32_t)g.a_scales[row * Ks + sb0 + q] << (8 * q);
-      rsa = v;
+      rsa = load_scales(g.a_scales, row < g.m ? row : g.m - 1, sb0);
     }
-    if (tid < BN) {
-      int64_t row = n0 + tid;
-      row = row < g.n ? row : g.n - 1;
-      uint32_t v = 0;
-#pragma unroll
-      for (int q = 0; q < 4; ++q)
-        if (sb0 + q < Ks) v |= (uint32_t)g.b_scales[row * Ks + sb0 + q] << (8 * q);
-      rsb = v;
+    {
+      int64_t row = n0 + (tid & (BN - 1));
+      rsb = load_scales(g.b_scales, row < g.n ? row : g.n - 1, sb0);
     }
   };
   auto store_stage = [&](int buf) {
@@ -221,6 +240,9 @@ __global__ void __launch_bounds__(kGemmThreads, 2) gemm_mx_kernel(GemmArgs g) {
           acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
               fa[i], fb[j], acc[i][j], 4, 4, 0, sa[i], 0, sb[j]);
     }
+    // Keep the next stage's LDS stores (which wait for its global loads) after
+    // this stage's matrix-core work, so the load latency overlaps the MFMAs.
+    __builtin_amdgcn_sched_barrier(0);
     if (kt + 1 < nk) store_stage(buf ^ 1);
     __syncthreads();
   }
@@ -279,34 +301,32 @@ __global__ void __launch_bounds__(kGemmThreads, 2) gemm_mx_kernel(GemmArgs g) {
   }
 
   const int64_t pstride = oe_rows ? (int64_t)g.oe_k * g.n : g.m * (int64_t)g.oe_k;
-#pragma unroll
-  for (int i = 0; i < FM; ++i) {
-#pragma unroll
-    for (int j = 0; j < FN; ++j) {
-      const int lc = wn * WN + j * 32 + lrow;
+  static_for<FM>([&](auto I) {
+    static_for<FN>([&](auto J) {
+      const int lc = wn * WN + J * 32 + lrow;
       const int64_t col = n0 + lc;
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int lr = wm * WM + i * 32 + acc_row(v, lane);
+      static_for<16>([&](auto V) {
+        const int lr = wm * WM + I * 32 + acc_row(V, lane);
         const int64_t row = m0 + lr;
-        if (row >= g.m || col >= g.n) continue;
-        float val = acc[i][j][v];
+        float val = acc[I][J][(int)V];
         if (any_oe) {
           const int p = s_pos[oe_rows ? lr : lc];
-          if (p >= 0) {
+          if (p >= 0 && row < g.m && col < g.n) {
             const int64_t off = oe_rows ? (int64_t)p * g.n + col : row * g.oe_k + p;
-            float s = 0.0f;
-            for (int sp = 0; sp < g.oe_splits; ++sp) s += g.oe_partials[sp * pstride + off];
-            val += s;
+            float sum = 0.0f;
+            for (int sp = 0; sp < g.oe_splits; ++sp) sum += g.oe_partials[sp * pstride + off];
+            val += sum;
           }
         }
-        if (g.out_f32)
-          static_cast<float*>(g.C)[row * g.ldc + col] = val;
-        else
-          static_cast<uint16_t*>(g.C)[row * g.ldc + col] = f32_to_bf16_rne(val);
-      }
-    }
-  }
+        if (row < g.m && col < g.n) {
+          if (g.out_f32)
+            static_cast<float*>(g.C)[row * g.ldc + col] = val;
+          else
+            static_cast<uint16_t*>(g.C)[row * g.ldc + col] = f32_to_bf16_rne(val);
+        }
+      });
+    });
+  });
 }
 
 // ---------------------------------------------------------------------------
@@ -430,7 +450,12 @@ adahop_status gemm_mx_launch(const uint8_t* a_codes, const uint8_t* a_scales,
   g.oe_splits = oe.splits;
   g.ia_ptr = oe.a.ptr; g.ia_ld = oe.a.ld; g.ia_inner = oe.a.inner_contiguous;
   g.ib_ptr = oe.b.ptr; g.ib_ld = oe.b.ld; g.ib_inner = oe.b.inner_contiguous;
-  gemm_mx_kernel<<<dim3((unsigned)(tiles_m * tiles_n)), dim3(kGemmThreads), 0, stream>>>(g);
+  const dim3 grid((unsigned)(tiles_m * tiles_n)), block(kGemmThreads);
+  const bool scales4 = ((reinterpret_cast<uintptr_t>(a_scales) | reinterpret_cast<uintptr_t>(b_scales)) & 3u) == 0;
+  if (K % 128 == 0 && scales4)
+    gemm_mx_kernel<true><<<grid, block, 0, stream>>>(g);
+  else
+    gemm_mx_kernel<false><<<grid, block, 0, stream>>>(g);
   return check_launch("gemm_mx");
 }
 
