@@ -160,7 +160,7 @@ adahop_status make_plan(adahop_op op, int64_t T, int64_t Din, int64_t Dout,
     const int64_t nx = route == ADAHOP_ROUTE_OE_LEFT ? pb.k : s.m;
     const int64_t ny = route == ADAHOP_ROUTE_OE_LEFT ? s.n : pb.k;
     P->splits = oe_splits(nx, ny, s.K);
-    P->off_partials = take(sizeof(float) * (size_t)P->splits * (size_t)nx * (size_t)ny);
+    P->off_partials = take(sizeof(float) * (size_t)(P->splits + 1) * (size_t)nx * (size_t)ny);
   }
   pb.ws_bytes = off;
   return ADAHOP_OK;
@@ -370,7 +370,7 @@ size_t adahop_gemm_mx_workspace_size(int64_t m, int64_t n, int64_t K, const adah
   if (m < 1 || n < 1 || K < 1 || oe->k < 1) return 0;
   const int64_t nx = oe->route == ADAHOP_ROUTE_OE_LEFT ? oe->k : m;
   const int64_t ny = oe->route == ADAHOP_ROUTE_OE_LEFT ? n : oe->k;
-  return align_up(sizeof(float) * (size_t)oe_splits(nx, ny, K) * (size_t)nx * (size_t)ny, kAlign);
+  return align_up(sizeof(float) * (size_t)(oe_splits(nx, ny, K) + 1) * (size_t)nx * (size_t)ny, kAlign);
 }
 
 adahop_status adahop_gemm_mx(const adahop_mx_operand* A, const adahop_mx_operand* B,

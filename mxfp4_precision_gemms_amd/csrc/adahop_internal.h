@@ -33,8 +33,9 @@ adahop_status iht_quant_launch(const uint16_t* src, int64_t rows, int64_t cols, 
                                uint16_t* gathered, hipStream_t stream);
 
 // ---- outlier product (bf16 MFMA) ------------------------------------------
-// P_s[x][y] = sum over t in split s of X(x, t) * Y(y, t), fp32, for s < splits.
-// Partials are laid out [splits][nx][ny].
+// P_s[x][y] = sum over t in split s of X(x, t) * Y(y, t), fp32, for s < splits,
+// laid out [splits][nx][ny] in `partials`, followed by their sum P [nx][ny]
+// (so `partials` holds (splits + 1) * nx * ny floats).
 struct Bf16View {
   const uint16_t* ptr;
   int64_t ld;
@@ -52,7 +53,7 @@ struct OeEpilogue {
   int mode;                 // 0 none, ADAHOP_ROUTE_OE_LEFT / _OE_RIGHT / _OE_INNER
   int32_t k;
   const int32_t* idx;       // OE_LEFT / OE_RIGHT
-  const float* partials;    // OE_LEFT: [splits][k][n]; OE_RIGHT: [splits][m][k]
+  const float* partials;    // OE_LEFT: [splits][k][n]; OE_RIGHT: [splits][m][k]; then P
   int splits;
   Bf16View a, b;            // OE_INNER factors: a [m][k], b [n][k]
 };

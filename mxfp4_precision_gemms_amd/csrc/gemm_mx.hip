@@ -10,19 +10,20 @@
 //   per lane = per 32-element K block). Lane l of a wave supplies row l%32 of
 //   the 32x64 A block (B: column l%32), K half l/32: 16 bytes of packed codes,
 //   exactly one 32-element MX block, plus that block's scale byte.
-// Tiling: a workgroup of 4 waves computes a 256 x 128 tile of C; each wave a
-//   128 x 64 sub-tile (4 x 2 MFMA blocks, 128 fp32 accumulators per lane).
-//   K advances 128 elements (64 bytes per row) per stage; stages are double
-//   buffered in LDS (A 16 KB + B 8 KB per stage), the next stage's global loads
-//   are in flight while the current one feeds the matrix cores. 16-byte chunks
-//   of a row are XOR-swizzled in LDS so a wave's 16-byte fragment reads hit
-//   distinct banks. Workgroup ids are remapped so that each XCD (ids i, i+8,
-//   ...) works on a contiguous band of tiles that share operand rows in its L2.
+// Tiling: a workgroup of 4 waves computes a 256 x 256 tile of C; each wave a
+//   128 x 128 sub-tile (4 x 4 MFMA blocks, 256 fp32 accumulators per lane,
+//   held in the accumulation registers). K advances 256 elements (128 bytes
+//   per row) per stage; stages are double buffered in LDS (A 32 KB + B 32 KB
+//   per stage) and the next stage's global loads (raw buffer loads over the
+//   tile's rows, which read 0 past the matrix edge) are in flight in
+//   registers during the current stage's 64 MFMAs per wave. LDS rows are
+//   padded to 144 bytes so a wave's 16-byte fragment reads hit distinct banks. Workgroup ids are remapped so that each XCD runs a 4 x 8 block of
+//   tiles at a time, whose operand rows its L2 shares.
 // Outlier product: bf16 matrix cores (v_mfma_f32_32x32x16_bf16), 64 x 64
-//   tiles, K split across workgroups into fp32 partials; the FP4 kernel's
-//   epilogue sums a line's partials in a fixed order and adds them to the
-//   fp32 accumulators before the single rounding to the output type (the
-//   scatter-add). Inner extraction (rank-k term on every output) runs as extra
+//   tiles, K split across workgroups into fp32 partials that a small kernel
+//   sums in a fixed order; the FP4 kernel's epilogue adds a line's reduced
+//   outlier product to the fp32 accumulators before the single rounding to
+//   the output type (the scatter-add). Inner extraction (rank-k term on every output) runs as extra
 //   bf16 MFMAs on the tile's own accumulators. No atomics: results are
 //   deterministic.
 #include <utility>
@@ -61,15 +62,19 @@ __device__ __forceinline__ void static_for(F&& f) {
 // ---------------------------------------------------------------------------
 // FP4 GEMM
 // ---------------------------------------------------------------------------
-constexpr int BM = 256, BN = 128;
-constexpr int BKB = 64;                 // bytes of packed codes per row per stage (128 elements)
+constexpr int BM = 256, BN = 256;
+constexpr int BKB = 128;                // bytes of packed codes per row per stage (256 elements)
+constexpr int SCB = BKB / 16;           // scale bytes per row per stage (8)
+constexpr int LROW = BKB + 16;          // LDS row stride: 144 bytes (9 x 16, odd)
 constexpr int kGemmThreads = 256;
-constexpr int WM = 128, WN = 64;        // wave sub-tile
+constexpr int WM = 128, WN = 128;       // wave sub-tile (2 x 2 waves)
 constexpr int FM = WM / 32, FN = WN / 32;
-constexpr int kLdsA = BM * BKB, kLdsB = BN * BKB;
-
-// 16-byte chunk c (0..3) of LDS row r lives at chunk c ^ swz(r).
-__device__ __forceinline__ int swz(int r) { return ((r >> 1) ^ (r >> 2)) & 3; }
+constexpr int kLdsA = BM * LROW, kLdsB = BN * LROW;
+constexpr int kChunksA = BM * BKB / 16 / kGemmThreads;   // 16-byte chunks per thread per stage
+constexpr int kChunksB = BN * BKB / 16 / kGemmThreads;
+constexpr int kRowsPerPass = kGemmThreads / (BKB / 16);  // rows one pass of the workgroup copies
+constexpr int kGroupM = 4;              // tile rows that run together on one XCD
+constexpr int kBufferFlags = 0x00020000;   // raw buffer descriptor word 3 (gfx9 family)
 
 struct GemmArgs {
   const uint8_t* a_codes;
@@ -85,8 +90,8 @@ struct GemmArgs {
   int oe_mode;
   int oe_k;
   const int32_t* oe_idx;
-  const float* oe_partials;
-  int oe_splits;
+  const float* oe_p;            // reduced outlier product: OE_LEFT [k][n], OE_RIGHT [m][k]
+  int vec_ok;                   // C rows allow 4-element vector stores
   const uint16_t* ia_ptr; int64_t ia_ld; int ia_inner;   // OE_INNER a: (i, p)
   const uint16_t* ib_ptr; int64_t ib_ld; int ib_inner;   // OE_INNER b: (j, p)
 };
@@ -105,148 +110,37 @@ __device__ __forceinline__ uint16_t view_at(const uint16_t* p, int64_t ld, int i
   return inner ? p[r * ld + t] : p[t * ld + r];
 }
 
-// KAligned: K % 128 == 0, so every stage is whole and a row's 4 scale bytes of
-// a stage form one aligned dword.
-template <bool KAligned>
-__global__ void __launch_bounds__(kGemmThreads, 2) gemm_mx_kernel(GemmArgs g) {
-  __shared__ __attribute__((aligned(16))) uint8_t s_a[2][kLdsA];
-  __shared__ __attribute__((aligned(16))) uint8_t s_b[2][kLdsB];
-  __shared__ uint8_t s_sa[2][BM * 4];
-  __shared__ uint8_t s_sb[2][BN * 4];
-  __shared__ int s_pos[BM > BN ? BM : BN];
+// Tile of workgroup `bid`. The hardware deals workgroups round-robin to the 8
+// XCDs (bid % 8); each XCD gets a contiguous band of the logical tile order,
+// and the logical order walks groups of kGroupM tile rows column by column,
+// so the ~32 tiles an XCD runs at once form a 4 x 8 block that shares operand
+// rows in that XCD's L2.
+__device__ __forceinline__ void tile_of(int bid, int tiles_m, int tiles_n, int* tm, int* tn) {
+  const int ntiles = tiles_m * tiles_n;
+  int pid = bid;
+  if (ntiles % 8 == 0) pid = (bid & 7) * (ntiles / 8) + (bid >> 3);
+  const int per_group = kGroupM * tiles_n;
+  const int group = pid / per_group;
+  const int first_m = group * kGroupM;
+  const int gm = tiles_m - first_m < kGroupM ? tiles_m - first_m : kGroupM;
+  const int in_group = pid - group * per_group;
+  *tm = first_m + in_group % gm;
+  *tn = in_group / gm;
+}
 
+// Inner-extraction term and epilogue, shared by both GEMM kernels. `acc` is
+// the wave's 128 x 128 sub-tile of the tile at (m0, n0), computed as C^T
+// blocks: the MFMA's first operand holds B rows (C columns) and its second A
+// rows (C rows), so lane l of block (I, J) holds C row 32 I + l%32 and, in
+// registers 4 G .. 4 G + 3, the four consecutive C columns 32 J + 8 G +
+// 4 (l/32) .. +3 -- one 8-byte bf16 (16-byte fp32) store each.
+__device__ __forceinline__ void gemm_finish(const GemmArgs& g, v16f (&acc)[FM][FN], int64_t m0,
+                                            int64_t n0, int* s_pos) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
-
-  // XCD-aware tile order: hardware places workgroup i on XCD i % 8; give each
-  // XCD a contiguous run of tiles (row-major over tiles_n), so that its L2 sees
-  // the same A rows.
-  const int ntiles = g.tiles_m * g.tiles_n;
-  int pid = blockIdx.x;
-  {
-    const int per = (ntiles + 7) / 8;
-    const int xcd = pid & 7, local = pid >> 3;
-    const int remapped = xcd * per + local;
-    // Fall back to the identity when the last XCD band is short.
-    pid = (ntiles % 8 == 0) ? remapped : pid;
-  }
-  const int tm = pid / g.tiles_n, tn = pid % g.tiles_n;
-  const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
-  const int64_t Kb = g.K / 2;          // bytes per packed row
-  const int64_t Ks = g.K / 32;         // scale bytes per row
-  const int nk = (int)((g.K + 127) / 128);
-
-  // Global -> register staging: A 4 chunks, B 2 chunks of 16 bytes per thread.
-  uint4 ra[4], rb[2];
-  uint32_t rsa = 0, rsb = 0;
-  // A stage's 4 scale bytes of one row; past K they read as 0 (their codes are 0 too).
-  auto load_scales = [&](const uint8_t* sc, int64_t row, int64_t sb0) -> uint32_t {
-    if (KAligned) return *reinterpret_cast<const uint32_t*>(sc + row * Ks + sb0);
-    uint32_t v = 0;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int64_t col = sb0 + q < Ks ? sb0 + q : Ks - 1;
-      const uint32_t b = sc[row * Ks + col];
-      v |= (sb0 + q < Ks ? b : 0u) << (8 * q);
-    }
-    return v;
-  };
-  auto load_stage = [&](int kt) {
-    const int64_t kb0 = (int64_t)kt * BKB;
-    const int c = tid & 3;
-    const bool kin = KAligned || kb0 + c * 16 < Kb;
-    const int64_t kc = kin ? kb0 + c * 16 : 0;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      int64_t row = m0 + (tid >> 2) + 64 * i;
-      row = row < g.m ? row : g.m - 1;
-      const uint4 q = *reinterpret_cast<const uint4*>(g.a_codes + row * Kb + kc);
-      ra[i] = kin ? q : make_uint4(0, 0, 0, 0);
-    }
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      int64_t row = n0 + (tid >> 2) + 64 * i;
-      row = row < g.n ? row : g.n - 1;
-      const uint4 q = *reinterpret_cast<const uint4*>(g.b_codes + row * Kb + kc);
-      rb[i] = kin ? q : make_uint4(0, 0, 0, 0);
-    }
-    const int64_t sb0 = (int64_t)kt * 4;
-    {
-      int64_t row = m0 + tid;
-      rsa = load_scales(g.a_scales, row < g.m ? row : g.m - 1, sb0);
-    }
-    {
-      int64_t row = n0 + (tid & (BN - 1));
-      rsb = load_scales(g.b_scales, row < g.n ? row : g.n - 1, sb0);
-    }
-  };
-  auto store_stage = [&](int buf) {
-    const int c = tid & 3;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = (tid >> 2) + 64 * i;
-      *reinterpret_cast<uint4*>(&s_a[buf][r * BKB + ((c ^ swz(r)) << 4)]) = ra[i];
-    }
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int r = (tid >> 2) + 64 * i;
-      *reinterpret_cast<uint4*>(&s_b[buf][r * BKB + ((c ^ swz(r)) << 4)]) = rb[i];
-    }
-    *reinterpret_cast<uint32_t*>(&s_sa[buf][tid * 4]) = rsa;
-    if (tid < BN) *reinterpret_cast<uint32_t*>(&s_sb[buf][tid * 4]) = rsb;
-  };
-
-  v16f acc[FM][FN];
-#pragma unroll
-  for (int i = 0; i < FM; ++i)
-#pragma unroll
-    for (int j = 0; j < FN; ++j)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
-
-  load_stage(0);
-  store_stage(0);
-  __syncthreads();
-
   const int lrow = lane & 31, khalf = lane >> 5;
-  for (int kt = 0; kt < nk; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < nk) load_stage(kt + 1);
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      const int c = ks * 2 + khalf;
-      v8i fa[FM], fb[FN];
-      int sa[FM], sb[FN];
-#pragma unroll
-      for (int i = 0; i < FM; ++i) {
-        const int r = wm * WM + i * 32 + lrow;
-        const uint4 q = *reinterpret_cast<const uint4*>(&s_a[buf][r * BKB + ((c ^ swz(r)) << 4)]);
-        fa[i] = v8i{(int)q.x, (int)q.y, (int)q.z, (int)q.w, 0, 0, 0, 0};
-        sa[i] = s_sa[buf][r * 4 + c];
-      }
-#pragma unroll
-      for (int j = 0; j < FN; ++j) {
-        const int r = wn * WN + j * 32 + lrow;
-        const uint4 q = *reinterpret_cast<const uint4*>(&s_b[buf][r * BKB + ((c ^ swz(r)) << 4)]);
-        fb[j] = v8i{(int)q.x, (int)q.y, (int)q.z, (int)q.w, 0, 0, 0, 0};
-        sb[j] = s_sb[buf][r * 4 + c];
-      }
-#pragma unroll
-      for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int j = 0; j < FN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-              fa[i], fb[j], acc[i][j], 4, 4, 0, sa[i], 0, sb[j]);
-    }
-    // Keep the next stage's LDS stores (which wait for its global loads) after
-    // this stage's matrix-core work, so the load latency overlaps the MFMAs.
-    __builtin_amdgcn_sched_barrier(0);
-    if (kt + 1 < nk) store_stage(buf ^ 1);
-    __syncthreads();
-  }
-
   // Inner extraction: C += a[:, 0:k] * b[:, 0:k]^T on bf16 matrix cores,
   // 16 extracted lines per MFMA (lane: row l%32, lines 8*(l/32) .. +7).
   if (g.oe_mode == ADAHOP_ROUTE_OE_INNER) {
@@ -274,11 +168,11 @@ __global__ void __launch_bounds__(kGemmThreads, 2) gemm_mx_kernel(GemmArgs g) {
           fb[j][e] = __builtin_bit_cast(__bf16, h);
         }
       }
-#pragma unroll
-      for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int j = 0; j < FN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+      static_for<FM>([&](auto I) {
+        static_for<FN>([&](auto J) {
+          acc[I][J] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[J], fa[I], acc[I][J], 0, 0, 0);
+        });
+      });
     }
   }
 
@@ -300,33 +194,414 @@ __global__ void __launch_bounds__(kGemmThreads, 2) gemm_mx_kernel(GemmArgs g) {
     }
   }
 
-  const int64_t pstride = oe_rows ? (int64_t)g.oe_k * g.n : g.m * (int64_t)g.oe_k;
+  const bool full = m0 + BM <= g.m && n0 + BN <= g.n && g.vec_ok;
   static_for<FM>([&](auto I) {
+    const int lr = wm * WM + I * 32 + lrow;
+    const int64_t row = m0 + lr;
+    const int prow = (any_oe && oe_rows) ? s_pos[lr] : -1;
     static_for<FN>([&](auto J) {
-      const int lc = wn * WN + J * 32 + lrow;
-      const int64_t col = n0 + lc;
-      static_for<16>([&](auto V) {
-        const int lr = wm * WM + I * 32 + acc_row(V, lane);
-        const int64_t row = m0 + lr;
-        float val = acc[I][J][(int)V];
-        if (any_oe) {
-          const int p = s_pos[oe_rows ? lr : lc];
-          if (p >= 0 && row < g.m && col < g.n) {
-            const int64_t off = oe_rows ? (int64_t)p * g.n + col : row * g.oe_k + p;
-            float sum = 0.0f;
-            for (int sp = 0; sp < g.oe_splits; ++sp) sum += g.oe_partials[sp * pstride + off];
-            val += sum;
+      static_for<4>([&](auto G) {
+        const int lc = wn * WN + J * 32 + 8 * G + 4 * khalf;
+        const int64_t col = n0 + lc;
+        float v[4] = {acc[I][J][4 * G + 0], acc[I][J][4 * G + 1], acc[I][J][4 * G + 2],
+                      acc[I][J][4 * G + 3]};
+        if (any_oe && row < g.m) {
+          // scatter-add of the outlier product (the residual there is 0)
+          if (oe_rows) {
+            if (prow >= 0) {
+#pragma unroll
+              for (int e = 0; e < 4; ++e)
+                if (col + e < g.n) v[e] += g.oe_p[(int64_t)prow * g.n + col + e];
+            }
+          } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int p = lc + e < BN ? s_pos[lc + e] : -1;
+              if (p >= 0) v[e] += g.oe_p[row * g.oe_k + p];
+            }
           }
         }
-        if (row < g.m && col < g.n) {
-          if (g.out_f32)
-            static_cast<float*>(g.C)[row * g.ldc + col] = val;
-          else
-            static_cast<uint16_t*>(g.C)[row * g.ldc + col] = f32_to_bf16_rne(val);
+        if (full) {
+          if (g.out_f32) {
+            *reinterpret_cast<float4*>(static_cast<float*>(g.C) + row * g.ldc + col) =
+                make_float4(v[0], v[1], v[2], v[3]);
+          } else {
+            const uint32_t lo = f32_to_bf16_rne(v[0]) | ((uint32_t)f32_to_bf16_rne(v[1]) << 16);
+            const uint32_t hi = f32_to_bf16_rne(v[2]) | ((uint32_t)f32_to_bf16_rne(v[3]) << 16);
+            *reinterpret_cast<uint2*>(static_cast<uint16_t*>(g.C) + row * g.ldc + col) =
+                make_uint2(lo, hi);
+          }
+        } else if (row < g.m) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            if (col + e >= g.n) continue;
+            if (g.out_f32)
+              static_cast<float*>(g.C)[row * g.ldc + col + e] = v[e];
+            else
+              static_cast<uint16_t*>(g.C)[row * g.ldc + col + e] = f32_to_bf16_rne(v[e]);
+          }
         }
       });
     });
   });
+}
+
+// One stage of global data held in registers between its load and its LDS store.
+struct Stage {
+  uint4 a[kChunksA], b[kChunksB];
+  uint2 sa, sb;
+};
+
+typedef unsigned int v4u __attribute__((ext_vector_type(4)));
+typedef unsigned int v2u __attribute__((ext_vector_type(2)));
+
+// Register-staged kernel for any K % 32 == 0 (stages of 256 K-elements, the
+// last one masked). KAligned: K % 256 == 0 and 8-byte aligned scale rows.
+template <bool KAligned>
+__global__ void __launch_bounds__(kGemmThreads, 1) gemm_mx_kernel(GemmArgs g) {
+  // LDS rows are 144 bytes apart: 16-byte chunk c of row r starts at byte
+  // 144 r + 16 c, so the 16-byte units that 8 (or 16) consecutive rows touch
+  // at one chunk are 9 r + c mod 8 (mod 16): all distinct, no bank conflicts,
+  // and a fragment's address differs between K-steps only by an immediate.
+  __shared__ __attribute__((aligned(16))) uint8_t s_a[2][kLdsA];
+  __shared__ __attribute__((aligned(16))) uint8_t s_b[2][kLdsB];
+  __shared__ __attribute__((aligned(8))) uint8_t s_sa[2][BM * SCB];
+  __shared__ __attribute__((aligned(8))) uint8_t s_sb[2][BN * SCB];
+  __shared__ int s_pos[BM > BN ? BM : BN];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  int tm, tn;
+  tile_of(blockIdx.x, g.tiles_m, g.tiles_n, &tm, &tn);
+  const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
+  const int64_t Kb = g.K / 2;          // bytes per packed row
+  const int64_t Ks = g.K / 32;         // scale bytes per row
+  const int nk = (int)((Kb + BKB - 1) / BKB);
+  const int rows_a = (int)(g.m - m0 < BM ? g.m - m0 : BM);
+  const int rows_b = (int)(g.n - n0 < BN ? g.n - n0 : BN);
+
+  // Buffer descriptors over this tile's rows: loads past the last row read 0.
+  const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(g.a_codes + m0 * Kb), 0, (int)(rows_a * Kb), kBufferFlags);
+  const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(g.b_codes + n0 * Kb), 0, (int)(rows_b * Kb), kBufferFlags);
+  const __amdgpu_buffer_rsrc_t rsa = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(g.a_scales + m0 * Ks), 0, (int)(rows_a * Ks), kBufferFlags);
+  const __amdgpu_buffer_rsrc_t rsb = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(g.b_scales + n0 * Ks), 0, (int)(rows_b * Ks), kBufferFlags);
+
+  // Copy pattern: chunk (tid % 8) of rows tid / 8 + 32 i, so 8 lanes read one
+  // row's 128 contiguous bytes.
+  const int c_ld = tid & 7;
+  const int r_ld = tid >> 3;
+  const int voff0 = r_ld * (int)Kb + c_ld * 16;
+  const int vstep = kRowsPerPass * (int)Kb;
+
+  auto load_scales = [&](__amdgpu_buffer_rsrc_t rs, int64_t sb0) -> uint2 {
+    if (KAligned) {
+      const v2u w = __builtin_amdgcn_raw_buffer_load_b64(rs, tid * (int)Ks, (int)sb0, 0);
+      return make_uint2(w.x, w.y);
+    }
+    // K tail: byte loads, bytes past K read as 0 (their codes are 0 too).
+    uint32_t v[2] = {0, 0};
+#pragma unroll
+    for (int q = 0; q < SCB; ++q) {
+      const bool in = sb0 + q < Ks;
+      const uint32_t b = __builtin_amdgcn_raw_buffer_load_b8(rs, tid * (int)Ks + (int)(in ? sb0 + q : 0), 0, 0);
+      v[q >> 2] |= (in ? b : 0u) << (8 * (q & 3));
+    }
+    return make_uint2(v[0], v[1]);
+  };
+  auto load_stage = [&](Stage& st, int kt) {
+    const int64_t kb0 = (int64_t)kt * BKB;
+    const bool kin = KAligned || kb0 + c_ld * 16 < Kb;
+    const int kc = kin ? (int)kb0 : 0;
+#pragma unroll
+    for (int i = 0; i < kChunksA; ++i) {
+      const v4u q = __builtin_amdgcn_raw_buffer_load_b128(ra, voff0 + i * vstep, kc, 0);
+      st.a[i] = kin ? make_uint4(q.x, q.y, q.z, q.w) : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < kChunksB; ++i) {
+      const v4u q = __builtin_amdgcn_raw_buffer_load_b128(rb, voff0 + i * vstep, kc, 0);
+      st.b[i] = kin ? make_uint4(q.x, q.y, q.z, q.w) : make_uint4(0, 0, 0, 0);
+    }
+    st.sa = load_scales(rsa, (int64_t)kt * SCB);
+    st.sb = load_scales(rsb, (int64_t)kt * SCB);
+  };
+  const int w_off = r_ld * LROW + c_ld * 16;     // this thread's LDS store offset (pass 0)
+  auto store_stage = [&](const Stage& st, int buf) {
+#pragma unroll
+    for (int i = 0; i < kChunksA; ++i)
+      *reinterpret_cast<uint4*>(&s_a[buf][w_off + i * kRowsPerPass * LROW]) = st.a[i];
+#pragma unroll
+    for (int i = 0; i < kChunksB; ++i)
+      *reinterpret_cast<uint4*>(&s_b[buf][w_off + i * kRowsPerPass * LROW]) = st.b[i];
+    *reinterpret_cast<uint2*>(&s_sa[buf][tid * SCB]) = st.sa;
+    *reinterpret_cast<uint2*>(&s_sb[buf][tid * SCB]) = st.sb;
+  };
+
+  v16f acc[FM][FN];
+  static_for<FM>([&](auto I) {
+    static_for<FN>([&](auto J) {
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[I][J][v] = 0.0f;
+    });
+  });
+
+  const int lrow = lane & 31, khalf = lane >> 5;
+  const int fa_off = (wm * WM + lrow) * LROW + khalf * 16;   // fragment i, K-step ks: + 32 LROW i + 32 ks
+  const int fb_off = (wn * WN + lrow) * LROW + khalf * 16;
+  const int sa_off = (wm * WM + lrow) * SCB;
+  const int sb_off = (wn * WN + lrow) * SCB;
+  // One stage: 4 K-steps of 64. Lane (row l%32, half l/32) of K-step ks reads
+  // chunk 2 ks + half of its row and scale byte 2 ks + half; each row's 8
+  // scale bytes are read once per stage and pre-shifted by 8 * half, so the
+  // MFMA's opsel picks byte 2 (ks % 2) of dword ks / 2.
+  auto compute = [&](int buf) {
+    const uint8_t* pa = &s_a[buf][fa_off];
+    const uint8_t* pb = &s_b[buf][fb_off];
+    uint2 sca[FM], scb[FN];
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+      const uint2 w = *reinterpret_cast<const uint2*>(&s_sa[buf][sa_off + i * 32 * SCB]);
+      sca[i] = make_uint2(w.x >> (8 * khalf), w.y >> (8 * khalf));
+    }
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      const uint2 w = *reinterpret_cast<const uint2*>(&s_sb[buf][sb_off + j * 32 * SCB]);
+      scb[j] = make_uint2(w.x >> (8 * khalf), w.y >> (8 * khalf));
+    }
+    static_for<4>([&](auto KS) {
+      v8i fa[FM], fb[FN];
+#pragma unroll
+      for (int i = 0; i < FM; ++i) {
+        const uint4 q = *reinterpret_cast<const uint4*>(pa + i * 32 * LROW + 32 * KS);
+        fa[i] = v8i{(int)q.x, (int)q.y, (int)q.z, (int)q.w, 0, 0, 0, 0};
+      }
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        const uint4 q = *reinterpret_cast<const uint4*>(pb + j * 32 * LROW + 32 * KS);
+        fb[j] = v8i{(int)q.x, (int)q.y, (int)q.z, (int)q.w, 0, 0, 0, 0};
+      }
+      constexpr int kSel = 2 * (KS % 2);
+      static_for<FM>([&](auto I) {
+        static_for<FN>([&](auto J) {
+          const int sa_w = KS < 2 ? (int)sca[I].x : (int)sca[I].y;
+          const int sb_w = KS < 2 ? (int)scb[J].x : (int)scb[J].y;
+          acc[I][J] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+              fb[J], fa[I], acc[I][J], 4, 4, kSel, sb_w, kSel, sa_w);
+        });
+      });
+    });
+  };
+
+  // Pipeline: stage kt+1's global loads are in flight in registers while
+  // stage kt feeds the matrix cores from LDS; they go to the other LDS slot
+  // after this stage's MFMAs are issued.
+  Stage st;
+  load_stage(st, 0);
+  store_stage(st, 0);
+  __syncthreads();
+  for (int kt = 0; kt < nk; ++kt) {
+    const int buf = kt & 1;
+    if (kt + 1 < nk) load_stage(st, kt + 1);
+    compute(buf);
+    __builtin_amdgcn_sched_barrier(0);
+    if (kt + 1 < nk) store_stage(st, buf ^ 1);
+    __syncthreads();
+  }
+
+  gemm_finish(g, acc, m0, n0, s_pos);
+}
+
+
+// ---------------------------------------------------------------------------
+// Main kernel for K % 512 == 0: a 4-slot LDS ring filled by direct
+// global->LDS buffer loads (no staging registers), 3 stages ahead of the
+// matrix cores. Stage = 128 K-elements: A and B 256 rows x 64 bytes each plus
+// 4 scale bytes per row. Each wave copies a quarter of a stage with 10 loads
+// (4 + 4 of 1 KB codes, 1 + 1 of 256 B scales); before a stage is consumed,
+// every wave waits until only the two later stages' 20 loads are in flight,
+// then the workgroup barrier publishes the stage. LDS rows of 64 bytes keep
+// their four 16-byte chunks XOR-swizzled by ((r >> 1) ^ (r >> 2)) & 3, so a
+// wave's fragment reads of 8 (or 16) consecutive rows hit distinct banks.
+// ---------------------------------------------------------------------------
+constexpr int RBK = 64;                       // bytes per row per stage
+constexpr int kRingSlots = 4;
+constexpr int kSlotA = BM * RBK, kSlotB = BN * RBK;   // 16 KB each
+constexpr int kLoadsPerStage = 10;            // per wave
+
+// One LDS object per slot: the compiler's alias analysis then sees that the
+// loads in flight into one slot do not touch the slot being read, and adds no
+// wait for them before the reads.
+struct RingSlot {
+  uint8_t a[kSlotA];
+  uint8_t b[kSlotB];
+  uint8_t sa[BM * 4];
+  uint8_t sb[BN * 4];
+};
+__shared__ __attribute__((aligned(1024))) RingSlot g_ring0;
+__shared__ __attribute__((aligned(1024))) RingSlot g_ring1;
+__shared__ __attribute__((aligned(1024))) RingSlot g_ring2;
+__shared__ __attribute__((aligned(1024))) RingSlot g_ring3;
+__shared__ int g_ring_pos[BM > BN ? BM : BN];
+
+template <int S>
+__device__ __forceinline__ RingSlot& ring_slot() {
+  if constexpr (S == 0) return g_ring0;
+  else if constexpr (S == 1) return g_ring1;
+  else if constexpr (S == 2) return g_ring2;
+  else return g_ring3;
+}
+
+// s_waitcnt immediate (gfx9 encoding): vmcnt bits [3:0] and [15:14], expcnt
+// [6:4] (7 = no wait), lgkmcnt [11:8].
+constexpr int waitcnt_imm(int vm, int lgkm) {
+  return (vm & 15) | ((vm >> 4) << 14) | (7 << 4) | ((lgkm & 15) << 8);
+}
+
+__device__ __forceinline__ int ring_swz(int r) { return ((r >> 1) ^ (r >> 2)) & 3; }
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+__global__ void __launch_bounds__(kGemmThreads, 1) gemm_mx_ring_kernel(GemmArgs g) {
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  int tm, tn;
+  tile_of(blockIdx.x, g.tiles_m, g.tiles_n, &tm, &tn);
+  const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
+  const int64_t Kb = g.K / 2;
+  const int64_t Ks = g.K / 32;
+  const int nk = (int)(Kb / RBK);
+  const int rows_a = (int)(g.m - m0 < BM ? g.m - m0 : BM);
+  const int rows_b = (int)(g.n - n0 < BN ? g.n - n0 : BN);
+
+  // Descriptors over this tile's rows: rows past the matrix edge read 0.
+  const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(g.a_codes + m0 * Kb), 0, (int)(rows_a * Kb), kBufferFlags);
+  const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(g.b_codes + n0 * Kb), 0, (int)(rows_b * Kb), kBufferFlags);
+  const __amdgpu_buffer_rsrc_t rsa = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(g.a_scales + m0 * Ks), 0, (int)(rows_a * Ks), kBufferFlags);
+  const __amdgpu_buffer_rsrc_t rsb = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(g.b_scales + n0 * Ks), 0, (int)(rows_b * Ks), kBufferFlags);
+
+  // Load j (0..3) of this wave fills LDS bytes [1024 (4 wave + j), +1024) of a
+  // slot: rows 16 (4 wave + j) + lane / 4, physical chunk lane % 4, which holds
+  // logical chunk (lane % 4) ^ swz(row). The stage offset goes in soffset.
+  const int row0 = 64 * wave + (lane >> 2);
+  const int chunk = (lane & 3) ^ ring_swz(row0);    // swz is the same for rows row0 + 16 j
+  int voff[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) voff[j] = (row0 + 16 * j) * (int)Kb + chunk * 16;
+  const int soff_row = (64 * wave + lane) * (int)Ks;   // scales: row 64 wave + lane
+
+  auto issue = [&](auto S, int kt) {
+    constexpr int slot = decltype(S)::value;
+    const int kb0 = kt * RBK;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          ra, (lds_void*)&ring_slot<slot>().a[1024 * (4 * wave + j)], 16, voff[j], kb0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rb, (lds_void*)&ring_slot<slot>().b[1024 * (4 * wave + j)], 16, voff[j], kb0, 0, 0);
+    }
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsa, (lds_void*)&ring_slot<slot>().sa[256 * wave], 4,
+                                             soff_row, kt * 4, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsb, (lds_void*)&ring_slot<slot>().sb[256 * wave], 4,
+                                             soff_row, kt * 4, 0, 0);
+  };
+
+  v16f acc[FM][FN];
+  static_for<FM>([&](auto I) {
+    static_for<FN>([&](auto J) {
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[I][J][v] = 0.0f;
+    });
+  });
+
+  const int lrow = lane & 31, khalf = lane >> 5;
+  // Fragment i of K-step ks: row wm*128 + 32 i + lrow, chunk (2 ks + half) ^ swz;
+  // swz depends on lrow only, so the two K-steps need one base each and the
+  // four fragments differ by the immediate 2048 i.
+  const int lswz = ring_swz(lrow);
+  const int fa0 = (wm * WM + lrow) * RBK + (((0 + khalf) ^ lswz) << 4);
+  const int fa1 = (wm * WM + lrow) * RBK + (((2 + khalf) ^ lswz) << 4);
+  const int fb0 = (wn * WN + lrow) * RBK + (((0 + khalf) ^ lswz) << 4);
+  const int fb1 = (wn * WN + lrow) * RBK + (((2 + khalf) ^ lswz) << 4);
+  const int sa_off = (wm * WM + lrow) * 4;
+  const int sb_off = (wn * WN + lrow) * 4;
+
+  auto compute = [&](auto S) {
+    constexpr int slot = decltype(S)::value;
+    int sca[FM], scb[FN];
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+      sca[i] = (int)(*reinterpret_cast<const uint32_t*>(&ring_slot<slot>().sa[sa_off + 128 * i]) >> (8 * khalf));
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+      scb[j] = (int)(*reinterpret_cast<const uint32_t*>(&ring_slot<slot>().sb[sb_off + 128 * j]) >> (8 * khalf));
+    static_for<2>([&](auto KS) {
+      const int oa = KS == 0 ? fa0 : fa1;
+      const int ob = KS == 0 ? fb0 : fb1;
+      v8i fa[FM], fb[FN];
+#pragma unroll
+      for (int i = 0; i < FM; ++i) {
+        const uint4 q = *reinterpret_cast<const uint4*>(&ring_slot<slot>().a[oa + 2048 * i]);
+        fa[i] = v8i{(int)q.x, (int)q.y, (int)q.z, (int)q.w, 0, 0, 0, 0};
+      }
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        const uint4 q = *reinterpret_cast<const uint4*>(&ring_slot<slot>().b[ob + 2048 * j]);
+        fb[j] = v8i{(int)q.x, (int)q.y, (int)q.z, (int)q.w, 0, 0, 0, 0};
+      }
+      constexpr int kSel = 2 * KS;   // scale byte 2 ks + half, pre-shifted by 8 half
+      static_for<FM>([&](auto I) {
+        static_for<FN>([&](auto J) {
+          acc[I][J] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+              fb[J], fa[I], acc[I][J], 4, 4, kSel, scb[J], kSel, sca[I]);
+        });
+      });
+    });
+  };
+
+  // Step kt: wait until only this wave's 20 loads of stages kt+1, kt+2 are in
+  // flight (so stage kt has landed), publish the stage, refill the slot freed
+  // by step kt-1, compute. Every step issues exactly one stage of loads -- past
+  // the end it re-loads the last stage into a slot no one reads -- so the
+  // count of loads in flight is the same at every step.
+  auto step = [&](auto S, int kt) {
+    constexpr int slot = decltype(S)::value;
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt(waitcnt_imm(2 * kLoadsPerStage, 0));
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    issue(std::integral_constant<int, (slot + 3) % kRingSlots>{}, kt + 3 < nk ? kt + 3 : nk - 1);
+    compute(S);
+  };
+
+  issue(std::integral_constant<int, 0>{}, 0);
+  issue(std::integral_constant<int, 1>{}, 1);
+  issue(std::integral_constant<int, 2>{}, 2);
+  // nk is a multiple of 4 (K % 512 == 0): one loop exit, so the accumulators
+  // keep their registers across the whole loop.
+  for (int kt = 0; kt < nk; kt += kRingSlots) {
+    step(std::integral_constant<int, 0>{}, kt);
+    step(std::integral_constant<int, 1>{}, kt + 1);
+    step(std::integral_constant<int, 2>{}, kt + 2);
+    step(std::integral_constant<int, 3>{}, kt + 3);
+  }
+  // Drain the trailing loads before the epilogue and before the workgroup's
+  // LDS can be handed to the next workgroup.
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
+  __syncthreads();
+  gemm_finish(g, acc, m0, n0, g_ring_pos);
 }
 
 // ---------------------------------------------------------------------------
@@ -401,6 +676,18 @@ __global__ void __launch_bounds__(kOeThreads) oe_product_kernel(OeArgs g) {
   }
 }
 
+// P[i] = sum over s of partials[s][i], in the order s = 0, 1, ...
+__global__ void __launch_bounds__(256) oe_reduce_kernel(const float* __restrict__ partials,
+                                                         int splits, int64_t count,
+                                                         float* __restrict__ P) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < count;
+       i += (int64_t)gridDim.x * 256) {
+    float s = 0.0f;
+    for (int sp = 0; sp < splits; ++sp) s += partials[sp * count + i];
+    P[i] = s;
+  }
+}
+
 }  // namespace
 
 int oe_splits(int64_t nx, int64_t ny, int64_t K) {
@@ -423,7 +710,13 @@ adahop_status oe_product_launch(Bf16View X, Bf16View Y, int64_t nx, int64_t ny, 
            kchunk_for(K, splits), partials, nullptr, 0, 0};
   const dim3 grid((unsigned)((nx + OT - 1) / OT), (unsigned)((ny + OT - 1) / OT), (unsigned)splits);
   oe_product_kernel<<<grid, dim3(kOeThreads), 0, stream>>>(a);
-  return check_launch("oe_product");
+  adahop_status st = check_launch("oe_product");
+  if (st != ADAHOP_OK) return st;
+  const int64_t count = nx * ny;
+  float* P = partials + (int64_t)splits * count;
+  const int64_t blocks = (count + 255) / 256 < 1024 ? (count + 255) / 256 : 1024;
+  oe_reduce_kernel<<<dim3((unsigned)blocks), dim3(256), 0, stream>>>(partials, splits, count, P);
+  return check_launch("oe_reduce");
 }
 
 adahop_status bf16_gemm_launch(Bf16View X, Bf16View Y, int64_t m, int64_t n, int64_t K,
@@ -446,13 +739,19 @@ adahop_status gemm_mx_launch(const uint8_t* a_codes, const uint8_t* a_scales,
   g.a_codes = a_codes; g.a_scales = a_scales; g.b_codes = b_codes; g.b_scales = b_scales;
   g.m = m; g.n = n; g.K = K; g.C = C; g.ldc = ldc; g.out_f32 = out_f32;
   g.tiles_m = (int)tiles_m; g.tiles_n = (int)tiles_n;
-  g.oe_mode = oe.mode; g.oe_k = oe.k; g.oe_idx = oe.idx; g.oe_partials = oe.partials;
-  g.oe_splits = oe.splits;
+  g.oe_mode = oe.mode; g.oe_k = oe.k; g.oe_idx = oe.idx;
+  g.oe_p = oe.partials ? oe.partials + (int64_t)oe.splits * (oe.mode == ADAHOP_ROUTE_OE_LEFT ? (int64_t)oe.k * n : m * (int64_t)oe.k) : nullptr;
+  g.vec_ok = (ldc % 4 == 0) && ((reinterpret_cast<uintptr_t>(C) & 15u) == 0);
   g.ia_ptr = oe.a.ptr; g.ia_ld = oe.a.ld; g.ia_inner = oe.a.inner_contiguous;
   g.ib_ptr = oe.b.ptr; g.ib_ld = oe.b.ld; g.ib_inner = oe.b.inner_contiguous;
   const dim3 grid((unsigned)(tiles_m * tiles_n)), block(kGemmThreads);
-  const bool scales4 = ((reinterpret_cast<uintptr_t>(a_scales) | reinterpret_cast<uintptr_t>(b_scales)) & 3u) == 0;
-  if (K % 128 == 0 && scales4)
+  const uintptr_t sc_bits = reinterpret_cast<uintptr_t>(a_scales) | reinterpret_cast<uintptr_t>(b_scales);
+  const uintptr_t cd_bits = reinterpret_cast<uintptr_t>(a_codes) | reinterpret_cast<uintptr_t>(b_codes);
+  const bool ring_ok = K % 512 == 0 && (sc_bits & 3u) == 0 && (cd_bits & 15u) == 0 &&
+                       (m < BM ? m : BM) * (K / 2) < 0x7FFFFFFF && (n < BN ? n : BN) * (K / 2) < 0x7FFFFFFF;
+  if (ring_ok)
+    gemm_mx_ring_kernel<<<grid, block, 0, stream>>>(g);
+  else if (K % 256 == 0 && (sc_bits & 7u) == 0)
     gemm_mx_kernel<true><<<grid, block, 0, stream>>>(g);
   else
     gemm_mx_kernel<false><<<grid, block, 0, stream>>>(g);

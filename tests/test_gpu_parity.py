@@ -162,7 +162,10 @@ def packed_operands(rng, m, n, K):
     return a, b, ac, as_, bc, bs
 
 
-GEMM_CASES = [(256, 128, 128), (512, 384, 512), (300, 200, 96), (33, 1000, 160), (1024, 256, 1024)]
+# K % 512 == 0 runs the LDS-ring kernel (ragged edges included), other K the
+# register-staged kernel (K tails included).
+GEMM_CASES = [(256, 128, 128), (512, 384, 512), (300, 200, 96), (33, 1000, 160), (1024, 256, 1024),
+              (300, 520, 1024), (77, 1000, 512), (520, 300, 2048), (256, 256, 768)]
 
 
 @pytest.mark.parametrize("m,n,K", GEMM_CASES)
