@@ -606,74 +606,154 @@ __global__ void __launch_bounds__(kGemmThreads, 1) gemm_mx_ring_kernel(GemmArgs 
 
 // ---------------------------------------------------------------------------
 // bf16 product on matrix cores: P[x][y] = sum_t X(x,t) * Y(y,t), split over K.
-// 64 x 64 tile, 4 waves of 32 x 32, K stage 64, LDS rows padded to 72
-// elements. Loads follow the memory order of each view (contiguous along t
-// for inner-contiguous views, along x otherwise) so that a wave's loads are
-// coalesced either way.
+// Memory-bound (it streams the whole bf16 operand). A workgroup computes a
+// 128 x 64 tile (wave w: rows 32 w .. +31, both 32-column halves) with
+// v_mfma_f32_32x32x16_bf16 over 64-element K stages, double buffered in LDS
+// and prefetched one stage ahead in registers. Global loads are 16 bytes per
+// lane along each view's contiguous direction: a t-contiguous view lands in
+// LDS as [x][t] rows directly; an x-contiguous view is transposed while
+// stored. LDS rows hold 64 t plus 8 of padding (144 bytes).
 // ---------------------------------------------------------------------------
-constexpr int OT = 64, OK = 64, OPAD = 72, kOeThreads = 256;
+constexpr int OX = 128, OY = 64, OK = 64, OPAD = 72, kOeThreads = 256;
 
 struct OeArgs {
-  const uint16_t* x; int64_t xld; int xin;
-  const uint16_t* y; int64_t yld; int yin;
+  const uint16_t* x; int64_t xld;
+  const uint16_t* y; int64_t yld;
   int64_t nx, ny, K, kchunk;
   float* partials;                 // [splits][nx][ny], or nullptr
   void* C; int64_t ldc; int out_f32;   // direct output when partials == nullptr
 };
 
-__device__ __forceinline__ void load_tile_bf16(uint16_t* s, const uint16_t* p, int64_t ld,
-                                               int inner, int64_t r0, int64_t nr, int64_t t0,
-                                               int64_t t1) {
-  const int tid = threadIdx.x;
-  for (int e = tid; e < OT * OK; e += kOeThreads) {
-    int r, t;
-    if (inner) { r = e / OK; t = e % OK; } else { t = e / OT; r = e % OT; }
-    const int64_t gr = r0 + r, gt = t0 + t;
-    uint16_t h = 0;
-    if (gr < nr && gt < t1) h = inner ? p[gr * ld + gt] : p[gt * ld + gr];
-    s[r * OPAD + t] = h;
+// Loads one [R][OK] tile of a view, starting at (r0, t0), into registers and
+// stores it into LDS as [R][OPAD] rows.
+template <int R, bool Inner>
+struct TileLoader {
+  // Each 16-byte chunk: Inner: row r, t-chunk c (8 t); else: t row, x-chunk (8 x).
+  static constexpr int kChunks = R * OK / 8;
+  static constexpr int kPerThread = kChunks / kOeThreads;
+  uint4 v[kPerThread];
+  __device__ __forceinline__ void load(const uint16_t* p, int64_t ld, int64_t r0, int64_t nr,
+                                       int64_t t0, int64_t t1) {
+#pragma unroll
+    for (int i = 0; i < kPerThread; ++i) {
+      const int e = threadIdx.x + i * kOeThreads;
+      int64_t gr, gt;
+      if (Inner) { gr = r0 + e / (OK / 8); gt = t0 + (e % (OK / 8)) * 8; }
+      else       { gt = t0 + e / (R / 8);  gr = r0 + (e % (R / 8)) * 8; }
+      // 8 consecutive elements along the contiguous direction; edges padded with 0.
+      uint4 q = make_uint4(0, 0, 0, 0);
+      if (Inner) {
+        if (gr < nr) {
+          if (gt + 8 <= t1 && ((ld | gt) & 7) == 0 && (reinterpret_cast<uintptr_t>(p) & 15) == 0) {
+            q = *reinterpret_cast<const uint4*>(p + gr * ld + gt);
+          } else {
+            uint16_t h[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) h[j] = gt + j < t1 ? p[gr * ld + gt + j] : 0;
+            q = make_uint4(h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16));
+          }
+        }
+      } else {
+        if (gt < t1) {
+          if (gr + 8 <= nr && ((ld | gr) & 7) == 0 && (reinterpret_cast<uintptr_t>(p) & 15) == 0) {
+            q = *reinterpret_cast<const uint4*>(p + gt * ld + gr);
+          } else {
+            uint16_t h[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) h[j] = gr + j < nr ? p[gt * ld + gr + j] : 0;
+            q = make_uint4(h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16));
+          }
+        }
+      }
+      v[i] = q;
+    }
   }
-}
+  __device__ __forceinline__ void store(uint16_t* s) const {
+#pragma unroll
+    for (int i = 0; i < kPerThread; ++i) {
+      const int e = threadIdx.x + i * kOeThreads;
+      if (Inner) {
+        const int r = e / (OK / 8), c = (e % (OK / 8)) * 8;
+        *reinterpret_cast<uint4*>(&s[r * OPAD + c]) = v[i];
+      } else {
+        const int t = e / (R / 8), r = (e % (R / 8)) * 8;
+        const uint32_t w[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
+#pragma unroll
+        for (int j = 0; j < 8; ++j) s[(r + j) * OPAD + t] = (uint16_t)(w[j >> 1] >> (16 * (j & 1)));
+      }
+    }
+  }
+};
 
+template <bool XIn, bool YIn>
 __global__ void __launch_bounds__(kOeThreads) oe_product_kernel(OeArgs g) {
-  __shared__ __attribute__((aligned(16))) uint16_t sx[OT * OPAD];
-  __shared__ __attribute__((aligned(16))) uint16_t sy[OT * OPAD];
+  __shared__ __attribute__((aligned(16))) uint16_t sx[2][OX * OPAD];
+  __shared__ __attribute__((aligned(16))) uint16_t sy[2][OY * OPAD];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wx = wave >> 1, wy = wave & 1;
-  const int64_t x0 = (int64_t)blockIdx.x * OT, y0 = (int64_t)blockIdx.y * OT;
+  const int64_t x0 = (int64_t)blockIdx.x * OX, y0 = (int64_t)blockIdx.y * OY;
   const int64_t tb = (int64_t)blockIdx.z * g.kchunk;
   const int64_t te = (tb + g.kchunk < g.K) ? tb + g.kchunk : g.K;
-  v16f acc;
+  v16f acc0, acc1;
 #pragma unroll
-  for (int v = 0; v < 16; ++v) acc[v] = 0.0f;
-  for (int64_t t0 = tb; t0 < te; t0 += OK) {
-    __syncthreads();
-    load_tile_bf16(sx, g.x, g.xld, g.xin, x0, g.nx, t0, te);
-    load_tile_bf16(sy, g.y, g.yld, g.yin, y0, g.ny, t0, te);
-    __syncthreads();
+  for (int v = 0; v < 16; ++v) { acc0[v] = 0.0f; acc1[v] = 0.0f; }
+  TileLoader<OX, XIn> lx;
+  TileLoader<OY, YIn> ly;
+  const int nst = (int)((te - tb + OK - 1) / OK);
+  if (nst > 0) {
+    lx.load(g.x, g.xld, x0, g.nx, tb, te);
+    ly.load(g.y, g.yld, y0, g.ny, tb, te);
+    lx.store(sx[0]);
+    ly.store(sy[0]);
+  }
+  __syncthreads();
+  for (int st = 0; st < nst; ++st) {
+    const int buf = st & 1;
+    if (st + 1 < nst) {
+      lx.load(g.x, g.xld, x0, g.nx, tb + (int64_t)(st + 1) * OK, te);
+      ly.load(g.y, g.yld, y0, g.ny, tb + (int64_t)(st + 1) * OK, te);
+    }
 #pragma unroll
     for (int ks = 0; ks < OK; ks += 16) {
       const int off = ks + 8 * (lane >> 5);
-      const uint4 qa = *reinterpret_cast<const uint4*>(&sx[(wx * 32 + (lane & 31)) * OPAD + off]);
-      const uint4 qb = *reinterpret_cast<const uint4*>(&sy[(wy * 32 + (lane & 31)) * OPAD + off]);
+      const uint4 qa = *reinterpret_cast<const uint4*>(&sx[buf][(wave * 32 + (lane & 31)) * OPAD + off]);
+      const uint4 qb0 = *reinterpret_cast<const uint4*>(&sy[buf][(lane & 31) * OPAD + off]);
+      const uint4 qb1 = *reinterpret_cast<const uint4*>(&sy[buf][(32 + (lane & 31)) * OPAD + off]);
       const v8bf fa = __builtin_bit_cast(v8bf, qa);
-      const v8bf fb = __builtin_bit_cast(v8bf, qb);
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa, fb, acc, 0, 0, 0);
+      acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa, __builtin_bit_cast(v8bf, qb0), acc0, 0, 0, 0);
+      acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa, __builtin_bit_cast(v8bf, qb1), acc1, 0, 0, 0);
     }
+    __builtin_amdgcn_sched_barrier(0);
+    if (st + 1 < nst) {
+      lx.store(sx[buf ^ 1]);
+      ly.store(sy[buf ^ 1]);
+    }
+    __syncthreads();
   }
-  const int64_t col = y0 + wy * 32 + (lane & 31);
+  // acc_h: rows x0 + 32 wave + acc_row(v), column y0 + 32 h + lane % 32
 #pragma unroll
-  for (int v = 0; v < 16; ++v) {
-    const int64_t row = x0 + wx * 32 + acc_row(v, lane);
-    if (row >= g.nx || col >= g.ny) continue;
-    if (g.partials) {
-      g.partials[(int64_t)blockIdx.z * g.nx * g.ny + row * g.ny + col] = acc[v];
-    } else if (g.out_f32) {
-      static_cast<float*>(g.C)[row * g.ldc + col] = acc[v];
-    } else {
-      static_cast<uint16_t*>(g.C)[row * g.ldc + col] = f32_to_bf16_rne(acc[v]);
+  for (int h = 0; h < 2; ++h) {
+    const int64_t col = y0 + 32 * h + (lane & 31);
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int64_t row = x0 + wave * 32 + acc_row(v, lane);
+      if (row >= g.nx || col >= g.ny) continue;
+      const float val = h == 0 ? acc0[v] : acc1[v];
+      if (g.partials) {
+        g.partials[(int64_t)blockIdx.z * g.nx * g.ny + row * g.ny + col] = val;
+      } else if (g.out_f32) {
+        static_cast<float*>(g.C)[row * g.ldc + col] = val;
+      } else {
+        static_cast<uint16_t*>(g.C)[row * g.ldc + col] = f32_to_bf16_rne(val);
+      }
     }
   }
+}
+
+void launch_oe(const OeArgs& a, dim3 grid, bool xin, bool yin, hipStream_t stream) {
+  if (xin && yin) oe_product_kernel<true, true><<<grid, dim3(kOeThreads), 0, stream>>>(a);
+  else if (xin) oe_product_kernel<true, false><<<grid, dim3(kOeThreads), 0, stream>>>(a);
+  else if (yin) oe_product_kernel<false, true><<<grid, dim3(kOeThreads), 0, stream>>>(a);
+  else oe_product_kernel<false, false><<<grid, dim3(kOeThreads), 0, stream>>>(a);
 }
 
 // P[i] = sum over s of partials[s][i], in the order s = 0, 1, ...
@@ -691,9 +771,9 @@ __global__ void __launch_bounds__(256) oe_reduce_kernel(const float* __restrict_
 }  // namespace
 
 int oe_splits(int64_t nx, int64_t ny, int64_t K) {
-  const int64_t tiles = ((nx + OT - 1) / OT) * ((ny + OT - 1) / OT);
-  int64_t s = (512 + tiles - 1) / tiles;
-  const int64_t smax = K / 256 > 0 ? K / 256 : 1;   // at least 256 K per split
+  const int64_t tiles = ((nx + OX - 1) / OX) * ((ny + OY - 1) / OY);
+  int64_t s = (512 + tiles - 1) / tiles;            // about 2 workgroups per CU
+  const int64_t smax = K / 512 > 0 ? K / 512 : 1;   // at least 512 K per split
   if (s > smax) s = smax;
   if (s > 64) s = 64;
   return (int)(s < 1 ? 1 : s);
@@ -706,10 +786,11 @@ static int64_t kchunk_for(int64_t K, int splits) {
 
 adahop_status oe_product_launch(Bf16View X, Bf16View Y, int64_t nx, int64_t ny, int64_t K,
                                 int splits, float* partials, hipStream_t stream) {
-  OeArgs a{X.ptr, X.ld, X.inner_contiguous, Y.ptr, Y.ld, Y.inner_contiguous, nx, ny, K,
-           kchunk_for(K, splits), partials, nullptr, 0, 0};
-  const dim3 grid((unsigned)((nx + OT - 1) / OT), (unsigned)((ny + OT - 1) / OT), (unsigned)splits);
-  oe_product_kernel<<<grid, dim3(kOeThreads), 0, stream>>>(a);
+  OeArgs a{X.ptr, X.ld, Y.ptr, Y.ld, nx, ny, K, kchunk_for(K, splits), partials, nullptr, 0, 0};
+  const int64_t gy = (ny + OY - 1) / OY;
+  if (gy > 65535) return fail(ADAHOP_ERR_UNSUPPORTED, "outlier product: too many columns");
+  const dim3 grid((unsigned)((nx + OX - 1) / OX), (unsigned)gy, (unsigned)splits);
+  launch_oe(a, grid, X.inner_contiguous != 0, Y.inner_contiguous != 0, stream);
   adahop_status st = check_launch("oe_product");
   if (st != ADAHOP_OK) return st;
   const int64_t count = nx * ny;
@@ -721,11 +802,11 @@ adahop_status oe_product_launch(Bf16View X, Bf16View Y, int64_t nx, int64_t ny, 
 
 adahop_status bf16_gemm_launch(Bf16View X, Bf16View Y, int64_t m, int64_t n, int64_t K,
                                void* C, int64_t ldc, int out_f32, hipStream_t stream) {
-  const int64_t gx = (m + OT - 1) / OT, gy = (n + OT - 1) / OT;
+  const int64_t gx = (m + OX - 1) / OX, gy = (n + OY - 1) / OY;
   if (gx > 0x7FFFFFFF || gy > 65535) return fail(ADAHOP_ERR_UNSUPPORTED, "bf16 gemm: too large");
-  OeArgs a{X.ptr, X.ld, X.inner_contiguous, Y.ptr, Y.ld, Y.inner_contiguous, m, n, K, K,
-           nullptr, C, ldc, out_f32};
-  oe_product_kernel<<<dim3((unsigned)gx, (unsigned)gy, 1), dim3(kOeThreads), 0, stream>>>(a);
+  OeArgs a{X.ptr, X.ld, Y.ptr, Y.ld, m, n, K, K, nullptr, C, ldc, out_f32};
+  launch_oe(a, dim3((unsigned)gx, (unsigned)gy, 1), X.inner_contiguous != 0,
+            Y.inner_contiguous != 0, stream);
   return check_launch("bf16_gemm");
 }
 

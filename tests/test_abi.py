@@ -104,8 +104,9 @@ def test_argument_checks_return_before_any_launch():
 
 
 def test_workspace_sizes():
-    assert A.adahop_detect_workspace_size(100, 64, "ROWS", 10) == 0          # one level
-    assert A.adahop_detect_workspace_size(65536, 64, "ROWS", 64) > 0         # several levels
+    # fp64 scores for every candidate, plus survivor lists when one level is not enough
+    assert A.adahop_detect_workspace_size(100, 64, "ROWS", 10) == 1024       # 800 B rounded up
+    assert A.adahop_detect_workspace_size(65536, 64, "ROWS", 64) > 65536 * 8
     ws = A.adahop_gemm_workspace_size("WGRAD", 32768, 14336, 4096, "R", "C", None, 64)
     # packed operands: (4096 + 14336) x 32768 x 17/32 bytes, plus lines and partials
     assert 0.5e9 > ws > (4096 + 14336) * 32768 * 17 // 32
