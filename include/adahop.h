@@ -192,9 +192,13 @@ typedef struct {
 
 /* C[m,n] (row-major, leading dim ldc, bf16 or fp32) = deq(A) * deq(B)^T with
  * fp32 accumulation, plus the OE term if oe != NULL. Needs
- * adahop_gemm_mx_workspace_size(...) bytes (0 without OE_LEFT/OE_RIGHT).
+ * adahop_gemm_mx_workspace_size(...) bytes of 16-byte aligned workspace: the
+ * outlier product's partial sums (OE_LEFT/OE_RIGHT) and, when K is a multiple
+ * of 512, a copy of both scale arrays reordered for the GEMM (0 when neither
+ * applies; ws may then be NULL). Its contents after the call are unspecified.
  * Errors: INVALID for NULL pointers, K mismatch, K % 32 != 0, ldc < n, bad
- * OE descriptors; UNSUPPORTED for k > 1024. */
+ * OE descriptors; WORKSPACE for a missing or short workspace; UNSUPPORTED for
+ * k > 1024 or a misaligned workspace. */
 ADAHOP_API size_t adahop_gemm_mx_workspace_size(int64_t m, int64_t n, int64_t K,
                                                 const adahop_oe* oe);
 ADAHOP_API adahop_status adahop_gemm_mx(const adahop_mx_operand* A,

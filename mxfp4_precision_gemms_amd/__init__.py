@@ -199,9 +199,10 @@ def adahop_gemm_mx(a_codes, a_scales, b_codes, b_scales, oe: Optional[dict] = No
         idx = oe.get("idx")
         desc = OeDesc(ROUTE[oe["route"]], oe["k"], _ptr(idx), bf16_view(*oe["a"]),
                       bf16_view(*oe["b"]))
-        need = lib().adahop_gemm_mx_workspace_size(m, n, K, ctypes.byref(desc))
-        if need:
-            ws = torch.empty(need, dtype=torch.uint8, device=dev)
+    need = lib().adahop_gemm_mx_workspace_size(
+        m, n, K, ctypes.byref(desc) if desc is not None else None)
+    if need:
+        ws = torch.empty(need, dtype=torch.uint8, device=dev)
     _check(lib().adahop_gemm_mx(ctypes.byref(A), ctypes.byref(B),
                                 ctypes.byref(desc) if desc is not None else None,
                                 out.data_ptr(), out.stride(0), OUT[out.dtype], _ptr(ws),

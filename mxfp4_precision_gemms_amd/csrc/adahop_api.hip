@@ -79,8 +79,8 @@ struct Plan {
   bool zero_lhs = false, zero_rhs = false;
   int lhs_zero_axis = ADAHOP_AXIS_ROWS, rhs_zero_axis = ADAHOP_AXIS_ROWS;
   int splits = 0;
-  size_t off_foid = SIZE_MAX, off_partials = SIZE_MAX;
-  size_t foid_bytes = 0;
+  size_t off_foid = SIZE_MAX, off_partials = SIZE_MAX, off_gemm = SIZE_MAX;
+  size_t foid_bytes = 0, gemm_bytes = 0;
 };
 
 constexpr size_t kNone = SIZE_MAX;
@@ -162,6 +162,8 @@ adahop_status make_plan(adahop_op op, int64_t T, int64_t Din, int64_t Dout,
     P->splits = oe_splits(nx, ny, s.K);
     P->off_partials = take(sizeof(float) * (size_t)(P->splits + 1) * (size_t)nx * (size_t)ny);
   }
+  P->gemm_bytes = gemm_mx_scratch_bytes(s.m, s.n, s.K);
+  if (P->gemm_bytes) P->off_gemm = take(P->gemm_bytes);
   pb.ws_bytes = off;
   return ADAHOP_OK;
 }
@@ -273,8 +275,21 @@ adahop_status run_gemm(adahop_op op, const uint16_t* lhs, const uint16_t* rhs, i
     oe.b = lines_by_position(rl, P.rhs_zero_axis, s.rhs_cols, pb.k);  // (j, p)
   }
   ADAHOP_TRY(E.record(4));
-  ADAHOP_TRY(gemm_mx_launch(ac, as, bc, bs, s.m, s.n, s.K, oe, out, s.n, out_f32, stream));
+  ADAHOP_TRY(gemm_mx_launch(ac, as, bc, bs, s.m, s.n, s.K, oe, out, s.n, out_f32,
+                            P.off_gemm != kNone ? w + P.off_gemm : nullptr, P.gemm_bytes, stream));
   return E.record(5);
+}
+
+// Workspace of adahop_gemm_mx: the outlier product's partial sums (OE_LEFT,
+// OE_RIGHT) first, then the GEMM's own scratch.
+// Workspace of adahop_gemm_mx: the outlier product's partial sums (OE_LEFT,
+// OE_RIGHT) first, then the GEMM's own scratch.
+size_t gemm_mx_partials_bytes(int64_t m, int64_t n, int64_t K, const adahop_oe* oe) {
+  if (!oe || (oe->route != ADAHOP_ROUTE_OE_LEFT && oe->route != ADAHOP_ROUTE_OE_RIGHT)) return 0;
+  if (oe->k < 1) return 0;
+  const int64_t nx = oe->route == ADAHOP_ROUTE_OE_LEFT ? oe->k : m;
+  const int64_t ny = oe->route == ADAHOP_ROUTE_OE_LEFT ? n : oe->k;
+  return align_up(sizeof(float) * (size_t)(oe_splits(nx, ny, K) + 1) * (size_t)nx * (size_t)ny, kAlign);
 }
 
 }  // namespace
@@ -366,11 +381,8 @@ adahop_status adahop_iht_quant(const uint16_t* src, int64_t rows, int64_t cols, 
 }
 
 size_t adahop_gemm_mx_workspace_size(int64_t m, int64_t n, int64_t K, const adahop_oe* oe) {
-  if (!oe || (oe->route != ADAHOP_ROUTE_OE_LEFT && oe->route != ADAHOP_ROUTE_OE_RIGHT)) return 0;
-  if (m < 1 || n < 1 || K < 1 || oe->k < 1) return 0;
-  const int64_t nx = oe->route == ADAHOP_ROUTE_OE_LEFT ? oe->k : m;
-  const int64_t ny = oe->route == ADAHOP_ROUTE_OE_LEFT ? n : oe->k;
-  return align_up(sizeof(float) * (size_t)(oe_splits(nx, ny, K) + 1) * (size_t)nx * (size_t)ny, kAlign);
+  if (m < 1 || n < 1 || K < 1) return 0;
+  return gemm_mx_partials_bytes(m, n, K, oe) + gemm_mx_scratch_bytes(m, n, K);
 }
 
 adahop_status adahop_gemm_mx(const adahop_mx_operand* A, const adahop_mx_operand* B,
@@ -389,6 +401,13 @@ adahop_status adahop_gemm_mx(const adahop_mx_operand* A, const adahop_mx_operand
     return fail(ADAHOP_ERR_UNSUPPORTED, "adahop_gemm_mx: codes must be 16-byte aligned");
   const int64_t m = A->outer, n = B->outer, K = A->K;
   const hipStream_t st = static_cast<hipStream_t>(stream);
+  const size_t need = adahop_gemm_mx_workspace_size(m, n, K, oe);
+  if (need > 0 && (!ws || ws_bytes < need))
+    return fail(ADAHOP_ERR_WORKSPACE, "adahop_gemm_mx: workspace too small: need " +
+                                          std::to_string(need) + " bytes");
+  if (need > 0 && !aligned16(ws))
+    return fail(ADAHOP_ERR_UNSUPPORTED, "adahop_gemm_mx: the workspace must be 16-byte aligned");
+  const size_t partial_bytes = gemm_mx_partials_bytes(m, n, K, oe);
   OeEpilogue e{};
   if (oe) {
     if (oe->k < 1 || !oe->a.ptr || !oe->b.ptr)
@@ -402,10 +421,6 @@ adahop_status adahop_gemm_mx(const adahop_mx_operand* A, const adahop_mx_operand
         return fail(ADAHOP_ERR_INVALID, "adahop_gemm_mx: k above the number of lines");
       const int64_t nx = oe->route == ADAHOP_ROUTE_OE_LEFT ? oe->k : m;
       const int64_t ny = oe->route == ADAHOP_ROUTE_OE_LEFT ? n : oe->k;
-      const size_t need = adahop_gemm_mx_workspace_size(m, n, K, oe);
-      if (!ws || ws_bytes < need)
-        return fail(ADAHOP_ERR_WORKSPACE, "adahop_gemm_mx: workspace too small: need " +
-                                              std::to_string(need) + " bytes");
       const int splits = oe_splits(nx, ny, K);
       ADAHOP_TRY(oe_product_launch(X, Y, nx, ny, K, splits, static_cast<float*>(ws), st));
       e.mode = oe->route;
@@ -423,7 +438,9 @@ adahop_status adahop_gemm_mx(const adahop_mx_operand* A, const adahop_mx_operand
     }
   }
   return gemm_mx_launch(A->codes, A->scales, B->codes, B->scales, m, n, K, e, C, ldc,
-                        out_dtype == ADAHOP_OUT_F32 ? 1 : 0, st);
+                        out_dtype == ADAHOP_OUT_F32 ? 1 : 0,
+                        need > partial_bytes ? static_cast<char*>(ws) + partial_bytes : nullptr,
+                        need - partial_bytes, st);
 }
 
 adahop_status adahop_gemm_plan(adahop_op op, int64_t T, int64_t Din, int64_t Dout,

@@ -81,6 +81,8 @@ struct GemmArgs {
   const uint8_t* a_scales;
   const uint8_t* b_codes;
   const uint8_t* b_scales;
+  const uint32_t* a_sst;        // stage-major scale copies (main kernel): [K/128][m] words
+  const uint32_t* b_sst;        //   and [K/128][n] words
   int64_t m, n, K;
   void* C;
   int64_t ldc;
@@ -420,12 +422,13 @@ __global__ void __launch_bounds__(kGemmThreads, 1) gemm_mx_kernel(GemmArgs g) {
 
 // ---------------------------------------------------------------------------
 // Main kernel for K % 512 == 0: a 4-slot LDS ring filled by direct
-// global->LDS buffer loads (no staging registers), 3 stages ahead of the
-// matrix cores. Stage = 128 K-elements: A and B 256 rows x 64 bytes each plus
+// global->LDS buffer loads (no staging registers), 4 stages ahead of the
+// matrix cores; each stage's fragments are read into registers during the
+// previous stage's second K-step, so the matrix cores never wait for LDS. Stage = 128 K-elements: A and B 256 rows x 64 bytes each plus
 // 4 scale bytes per row. Each wave copies a quarter of a stage with 10 loads
-// (4 + 4 of 1 KB codes, 1 + 1 of 256 B scales); before a stage is consumed,
-// every wave waits until only the two later stages' 20 loads are in flight,
-// then the workgroup barrier publishes the stage. LDS rows of 64 bytes keep
+// (4 + 4 of 1 KB codes, 1 + 1 of 256 B scales); before a stage is read, every
+// wave waits until only the two later stages' 20 loads are in flight, then
+// the workgroup barrier publishes the stage. LDS rows of 64 bytes keep
 // their four 16-byte chunks XOR-swizzled by ((r >> 1) ^ (r >> 2)) & 3, so a
 // wave's fragment reads of 8 (or 16) consecutive rows hit distinct banks.
 // ---------------------------------------------------------------------------
@@ -465,6 +468,10 @@ constexpr int waitcnt_imm(int vm, int lgkm) {
 
 __device__ __forceinline__ int ring_swz(int r) { return ((r >> 1) ^ (r >> 2)) & 3; }
 
+// A buffer offset past the end of every buffer the main kernel reads (their
+// sizes stay below 2^31 - 16): such a load returns 0 without touching memory.
+constexpr int kPastEnd = 0x7FFFFFF0;
+
 typedef __attribute__((address_space(3))) void lds_void;
 
 __global__ void __launch_bounds__(kGemmThreads, 1) gemm_mx_ring_kernel(GemmArgs g) {
@@ -486,10 +493,13 @@ __global__ void __launch_bounds__(kGemmThreads, 1) gemm_mx_ring_kernel(GemmArgs 
       const_cast<uint8_t*>(g.a_codes + m0 * Kb), 0, (int)(rows_a * Kb), kBufferFlags);
   const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint8_t*>(g.b_codes + n0 * Kb), 0, (int)(rows_b * Kb), kBufferFlags);
+  // Scales come from the stage-major copies: stage kt of rows r0..r0+255 is
+  // one contiguous kilobyte; a row past the matrix edge gets an offset past
+  // the end of the buffer and reads 0.
   const __amdgpu_buffer_rsrc_t rsa = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint8_t*>(g.a_scales + m0 * Ks), 0, (int)(rows_a * Ks), kBufferFlags);
+      const_cast<uint32_t*>(g.a_sst), 0, (int)(g.m * Ks), kBufferFlags);
   const __amdgpu_buffer_rsrc_t rsb = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint8_t*>(g.b_scales + n0 * Ks), 0, (int)(rows_b * Ks), kBufferFlags);
+      const_cast<uint32_t*>(g.b_sst), 0, (int)(g.n * Ks), kBufferFlags);
 
   // Load j (0..3) of this wave fills LDS bytes [1024 (4 wave + j), +1024) of a
   // slot: rows 16 (4 wave + j) + lane / 4, physical chunk lane % 4, which holds
@@ -499,7 +509,10 @@ __global__ void __launch_bounds__(kGemmThreads, 1) gemm_mx_ring_kernel(GemmArgs 
   int voff[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) voff[j] = (row0 + 16 * j) * (int)Kb + chunk * 16;
-  const int soff_row = (64 * wave + lane) * (int)Ks;   // scales: row 64 wave + lane
+  const int srow = 64 * wave + lane;                   // scales: row 64 wave + lane
+  const int soff_a = srow < rows_a ? (int)((m0 + srow) * 4) : kPastEnd;
+  const int soff_b = srow < rows_b ? (int)((n0 + srow) * 4) : kPastEnd;
+  const int sstage_a = (int)(g.m * 4), sstage_b = (int)(g.n * 4);
 
   auto issue = [&](auto S, int kt) {
     constexpr int slot = decltype(S)::value;
@@ -512,9 +525,9 @@ __global__ void __launch_bounds__(kGemmThreads, 1) gemm_mx_ring_kernel(GemmArgs 
           rb, (lds_void*)&ring_slot<slot>().b[1024 * (4 * wave + j)], 16, voff[j], kb0, 0, 0);
     }
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rsa, (lds_void*)&ring_slot<slot>().sa[256 * wave], 4,
-                                             soff_row, kt * 4, 0, 0);
+                                             soff_a, kt * sstage_a, 0, 0);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rsb, (lds_void*)&ring_slot<slot>().sb[256 * wave], 4,
-                                             soff_row, kt * 4, 0, 0);
+                                             soff_b, kt * sstage_b, 0, 0);
   };
 
   v16f acc[FM][FN];
@@ -537,65 +550,92 @@ __global__ void __launch_bounds__(kGemmThreads, 1) gemm_mx_ring_kernel(GemmArgs 
   const int sa_off = (wm * WM + lrow) * 4;
   const int sb_off = (wn * WN + lrow) * 4;
 
-  auto compute = [&](auto S) {
+  // Fragments of one stage (both 64-K steps) and its scale words, held in
+  // registers from the barrier that publishes the stage until its MFMAs.
+  struct Frags {
+    v8i a[2][FM], b[2][FN];
+    int sa[FM], sb[FN];
+  };
+  auto read_frags = [&](auto S, Frags& f) {
     constexpr int slot = decltype(S)::value;
-    int sca[FM], scb[FN];
 #pragma unroll
     for (int i = 0; i < FM; ++i)
-      sca[i] = (int)(*reinterpret_cast<const uint32_t*>(&ring_slot<slot>().sa[sa_off + 128 * i]) >> (8 * khalf));
+      f.sa[i] = (int)(*reinterpret_cast<const uint32_t*>(&ring_slot<slot>().sa[sa_off + 128 * i]) >> (8 * khalf));
 #pragma unroll
     for (int j = 0; j < FN; ++j)
-      scb[j] = (int)(*reinterpret_cast<const uint32_t*>(&ring_slot<slot>().sb[sb_off + 128 * j]) >> (8 * khalf));
-    static_for<2>([&](auto KS) {
-      const int oa = KS == 0 ? fa0 : fa1;
-      const int ob = KS == 0 ? fb0 : fb1;
-      v8i fa[FM], fb[FN];
+      f.sb[j] = (int)(*reinterpret_cast<const uint32_t*>(&ring_slot<slot>().sb[sb_off + 128 * j]) >> (8 * khalf));
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const int oa = ks == 0 ? fa0 : fa1;
+      const int ob = ks == 0 ? fb0 : fb1;
 #pragma unroll
       for (int i = 0; i < FM; ++i) {
         const uint4 q = *reinterpret_cast<const uint4*>(&ring_slot<slot>().a[oa + 2048 * i]);
-        fa[i] = v8i{(int)q.x, (int)q.y, (int)q.z, (int)q.w, 0, 0, 0, 0};
+        f.a[ks][i] = v8i{(int)q.x, (int)q.y, (int)q.z, (int)q.w, 0, 0, 0, 0};
       }
 #pragma unroll
       for (int j = 0; j < FN; ++j) {
         const uint4 q = *reinterpret_cast<const uint4*>(&ring_slot<slot>().b[ob + 2048 * j]);
-        fb[j] = v8i{(int)q.x, (int)q.y, (int)q.z, (int)q.w, 0, 0, 0, 0};
+        f.b[ks][j] = v8i{(int)q.x, (int)q.y, (int)q.z, (int)q.w, 0, 0, 0, 0};
       }
-      constexpr int kSel = 2 * KS;   // scale byte 2 ks + half, pre-shifted by 8 half
-      static_for<FM>([&](auto I) {
-        static_for<FN>([&](auto J) {
-          acc[I][J] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-              fb[J], fa[I], acc[I][J], 4, 4, kSel, scb[J], kSel, sca[I]);
-        });
+    }
+  };
+  // 16 MFMAs of K-step ks: scale byte 2 ks + half, pre-shifted by 8 half.
+  auto mma = [&](const Frags& f, auto KS) {
+    constexpr int kSel = 2 * decltype(KS)::value;
+    static_for<FM>([&](auto I) {
+      static_for<FN>([&](auto J) {
+        acc[I][J] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+            f.b[KS][J], f.a[KS][I], acc[I][J], 4, 4, kSel, f.sb[J], kSel, f.sa[I]);
       });
     });
   };
 
-  // Step kt: wait until only this wave's 20 loads of stages kt+1, kt+2 are in
-  // flight (so stage kt has landed), publish the stage, refill the slot freed
-  // by step kt-1, compute. Every step issues exactly one stage of loads -- past
-  // the end it re-loads the last stage into a slot no one reads -- so the
-  // count of loads in flight is the same at every step.
-  auto step = [&](auto S, int kt) {
+  // Iteration kt (stage kt's fragments in `cur`): K-step 0 of stage kt; wait
+  // until only this wave's 20 loads of stages kt+2, kt+3 are in flight and
+  // sync, which publishes stage kt+1 and guarantees every wave is done with
+  // stage kt's slot; refill that slot with stage kt+4 (past the end: a re-load
+  // of the last stage that no one reads, so every iteration issues 10 loads);
+  // read stage kt+1's fragments into `nxt` while K-step 1 of stage kt runs.
+  auto iteration = [&](auto S, Frags& cur, Frags& nxt, int kt) {
     constexpr int slot = decltype(S)::value;
+    mma(cur, std::integral_constant<int, 0>{});
     __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_s_waitcnt(waitcnt_imm(2 * kLoadsPerStage, 0));
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
-    issue(std::integral_constant<int, (slot + 3) % kRingSlots>{}, kt + 3 < nk ? kt + 3 : nk - 1);
-    compute(S);
+    issue(std::integral_constant<int, slot>{}, kt + 4 < nk ? kt + 4 : nk - 1);
+    __builtin_amdgcn_sched_barrier(0);
+    read_frags(std::integral_constant<int, (slot + 1) % kRingSlots>{}, nxt);
+    mma(cur, std::integral_constant<int, 1>{});
+    // Spread the 24 LDS reads over the first 12 MFMAs (2 after each), so they
+    // complete long before the next stage's first MFMA needs them.
+    static_for<12>([&](auto) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);   // DS read
+    });
+    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+    __builtin_amdgcn_sched_barrier(0);
   };
 
   issue(std::integral_constant<int, 0>{}, 0);
   issue(std::integral_constant<int, 1>{}, 1);
   issue(std::integral_constant<int, 2>{}, 2);
+  issue(std::integral_constant<int, 3>{}, 3);
+  Frags fx, fy;
+  __builtin_amdgcn_s_waitcnt(waitcnt_imm(3 * kLoadsPerStage, 0));
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_sched_barrier(0);
+  read_frags(std::integral_constant<int, 0>{}, fx);
   // nk is a multiple of 4 (K % 512 == 0): one loop exit, so the accumulators
   // keep their registers across the whole loop.
   for (int kt = 0; kt < nk; kt += kRingSlots) {
-    step(std::integral_constant<int, 0>{}, kt);
-    step(std::integral_constant<int, 1>{}, kt + 1);
-    step(std::integral_constant<int, 2>{}, kt + 2);
-    step(std::integral_constant<int, 3>{}, kt + 3);
+    iteration(std::integral_constant<int, 0>{}, fx, fy, kt);
+    iteration(std::integral_constant<int, 1>{}, fy, fx, kt + 1);
+    iteration(std::integral_constant<int, 2>{}, fx, fy, kt + 2);
+    iteration(std::integral_constant<int, 3>{}, fy, fx, kt + 3);
   }
+
   // Drain the trailing loads before the epilogue and before the workgroup's
   // LDS can be handed to the next workgroup.
   __builtin_amdgcn_sched_barrier(0);
@@ -810,10 +850,54 @@ adahop_status bf16_gemm_launch(Bf16View X, Bf16View Y, int64_t m, int64_t n, int
   return check_launch("bf16_gemm");
 }
 
+namespace {
+
+// Stage-major copy of both scale arrays for the main kernel, as 4-byte
+// words (the four block scales of one 128-long stage of one row):
+// dst[c][r] = src[r][c], c < K/128, through a 64 x 64 LDS tile. blockIdx.z
+// picks the operand.
+constexpr int kTr = 64;
+__global__ void __launch_bounds__(256)
+scale_stage_kernel(const uint32_t* __restrict__ sa, int64_t ma, uint32_t* __restrict__ da,
+                   const uint32_t* __restrict__ sb, int64_t nb, uint32_t* __restrict__ db,
+                   int64_t nst) {
+  __shared__ uint32_t tile[kTr][kTr + 1];
+  const uint32_t* src = blockIdx.z ? sb : sa;
+  uint32_t* dst = blockIdx.z ? db : da;
+  const int64_t rows = blockIdx.z ? nb : ma;
+  const int64_t r0 = (int64_t)blockIdx.y * kTr, c0 = (int64_t)blockIdx.x * kTr;
+  if (r0 >= rows) return;                      // the whole workgroup leaves together
+  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+  for (int i = ty; i < kTr; i += 4) {
+    const int64_t r = r0 + i, c = c0 + tx;
+    if (r < rows && c < nst) tile[i][tx] = src[r * nst + c];
+  }
+  __syncthreads();
+  for (int i = ty; i < kTr; i += 4) {
+    const int64_t c = c0 + i, r = r0 + tx;
+    if (r < rows && c < nst) dst[c * rows + r] = tile[tx][i];
+  }
+}
+
+bool ring_shape_ok(int64_t m, int64_t n, int64_t K) {
+  const int64_t big = m > n ? m : n;
+  return K % 512 == 0 && (m < BM ? m : BM) * (K / 2) < 0x7FFFFFFF &&
+         (n < BN ? n : BN) * (K / 2) < 0x7FFFFFFF && big * (K / 32) < 0x7FFFFF00 &&
+         (big + kTr - 1) / kTr <= 65535;
+}
+
+}  // namespace
+
+size_t gemm_mx_scratch_bytes(int64_t m, int64_t n, int64_t K) {
+  if (m < 1 || n < 1 || !ring_shape_ok(m, n, K)) return 0;
+  return align_up((size_t)m * (size_t)(K / 32), kAlign) + align_up((size_t)n * (size_t)(K / 32), kAlign);
+}
+
 adahop_status gemm_mx_launch(const uint8_t* a_codes, const uint8_t* a_scales,
                              const uint8_t* b_codes, const uint8_t* b_scales, int64_t m,
                              int64_t n, int64_t K, const OeEpilogue& oe, void* C, int64_t ldc,
-                             int out_f32, hipStream_t stream) {
+                             int out_f32, void* scratch, size_t scratch_bytes,
+                             hipStream_t stream) {
   const int64_t tiles_m = (m + BM - 1) / BM, tiles_n = (n + BN - 1) / BN;
   if (tiles_m * tiles_n > 0x7FFFFFFF) return fail(ADAHOP_ERR_UNSUPPORTED, "gemm: too large");
   GemmArgs g{};
@@ -828,11 +912,24 @@ adahop_status gemm_mx_launch(const uint8_t* a_codes, const uint8_t* a_scales,
   const dim3 grid((unsigned)(tiles_m * tiles_n)), block(kGemmThreads);
   const uintptr_t sc_bits = reinterpret_cast<uintptr_t>(a_scales) | reinterpret_cast<uintptr_t>(b_scales);
   const uintptr_t cd_bits = reinterpret_cast<uintptr_t>(a_codes) | reinterpret_cast<uintptr_t>(b_codes);
-  const bool ring_ok = K % 512 == 0 && (sc_bits & 3u) == 0 && (cd_bits & 15u) == 0 &&
-                       (m < BM ? m : BM) * (K / 2) < 0x7FFFFFFF && (n < BN ? n : BN) * (K / 2) < 0x7FFFFFFF;
-  if (ring_ok)
+  const bool ring_ok = ring_shape_ok(m, n, K) && (sc_bits & 3u) == 0 && (cd_bits & 15u) == 0;
+  if (ring_ok) {
+    const size_t need = gemm_mx_scratch_bytes(m, n, K);
+    if (scratch == nullptr || scratch_bytes < need || (reinterpret_cast<uintptr_t>(scratch) & 15u))
+      return fail(ADAHOP_ERR_WORKSPACE, "gemm_mx: scale staging needs " + std::to_string(need) +
+                                            " bytes of 16-byte aligned workspace");
+    uint32_t* sst = static_cast<uint32_t*>(scratch);
+    g.a_sst = sst;
+    g.b_sst = sst + align_up((size_t)m * (size_t)(K / 32), kAlign) / 4;
+    const int64_t nst = K / 128, big = m > n ? m : n;
+    const dim3 tgrid((unsigned)((nst + kTr - 1) / kTr), (unsigned)((big + kTr - 1) / kTr), 2);
+    scale_stage_kernel<<<tgrid, dim3(256), 0, stream>>>(
+        reinterpret_cast<const uint32_t*>(a_scales), m, const_cast<uint32_t*>(g.a_sst),
+        reinterpret_cast<const uint32_t*>(b_scales), n, const_cast<uint32_t*>(g.b_sst), nst);
+    const adahop_status st = check_launch("gemm_mx scale staging");
+    if (st != ADAHOP_OK) return st;
     gemm_mx_ring_kernel<<<grid, block, 0, stream>>>(g);
-  else if (K % 256 == 0 && (sc_bits & 7u) == 0)
+  } else if (K % 256 == 0 && (sc_bits & 7u) == 0)
     gemm_mx_kernel<true><<<grid, block, 0, stream>>>(g);
   else
     gemm_mx_kernel<false><<<grid, block, 0, stream>>>(g);

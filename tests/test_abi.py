@@ -110,3 +110,16 @@ def test_workspace_sizes():
     ws = A.adahop_gemm_workspace_size("WGRAD", 32768, 14336, 4096, "R", "C", None, 64)
     # packed operands: (4096 + 14336) x 32768 x 17/32 bytes, plus lines and partials
     assert 0.5e9 > ws > (4096 + 14336) * 32768 * 17 // 32
+
+
+def test_gemm_mx_workspace_size():
+    lib = A.lib()
+    # K % 512 == 0: a reordered copy of both scale arrays (K/32 bytes per row,
+    # each array rounded up to 256 bytes); otherwise nothing without OE.
+    assert lib.adahop_gemm_mx_workspace_size(300, 520, 1024, None) == 9728 + 16640
+    assert lib.adahop_gemm_mx_workspace_size(256, 256, 768, None) == 0
+    assert lib.adahop_gemm_mx_workspace_size(0, 256, 1024, None) == 0
+    # OE_RIGHT adds the outlier product's partial sums in front
+    desc = A.OeDesc(A.ROUTE["OE_RIGHT"], 16, 0, A.Bf16View(0, 0, 1, 0), A.Bf16View(0, 0, 1, 0))
+    with_oe = lib.adahop_gemm_mx_workspace_size(300, 520, 1024, ctypes.byref(desc))
+    assert with_oe > 9728 + 16640 and (with_oe - 9728 - 16640) % 256 == 0
