@@ -15,8 +15,10 @@ oracle timed on the host's cores on a bounded sample.
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 """
 import argparse
+import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -41,6 +43,34 @@ def workloads():
         for i, name in enumerate(("fwd", "dgrad", "wgrad")):
             out[f"l8b_oproj_bs{bs}_{name}"] = (t, i)
     return out
+
+
+# HBM traffic of the GEMM kernel comes from rocprofv3 FETCH_SIZE / WRITE_SIZE
+# passes (recorded with the copy-kernel calibration in this summary); it is
+# reported only while the kernel source is byte-identical to the one counted.
+TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "gemm_mx_ring_l8b_down_wgrad_traffic.md")
+
+
+def measured_traffic(workload_name):
+    """(bytes per launch or None, note)."""
+    try:
+        with open(TRAFFIC_SUMMARY) as f:
+            text = f.read()
+    except OSError:
+        return None, "no counter summary"
+    m = re.search(r"^traffic-record: (\{.*\})$", text, re.M)
+    if not m:
+        return None, "no traffic record in the counter summary"
+    rec = json.loads(m.group(1))
+    if rec["workload"] != workload_name:
+        return None, "counters were taken on another workload"
+    with open(os.path.join(ROOT, rec["source"]), "rb") as f:
+        if hashlib.sha256(f.read()).hexdigest() != rec["source_sha256"]:
+            return None, "kernel source changed since the counters were taken"
+    fetch = rec["fetch_kib"] * 1024 * rec["fetch_scale"]
+    write = rec["write_kib"] * 1024 * rec["write_scale"]
+    return fetch + write, (f"FETCH_SIZE {rec['fetch_kib']} KiB x{rec['fetch_scale']} + WRITE_SIZE "
+                           f"{rec['write_kib']} KiB x{rec['write_scale']} per launch")
 
 
 def gemm_dims(op, T, Din, Dout):
@@ -210,11 +240,15 @@ def main():
         "pct_mxfp4_peak": round(100 * value / PEAK_FP4_TFLOPS, 2),
         "stages_ms": {k: round(v, 4) for k, v in stage_ms.items()},
         "call_ms_events": round(call_ms, 4),
-        "roofline": {"bound": "mfma", "kernel": "gemm_mx_kernel (+ scatter-add epilogue)",
+        "roofline": {"bound": "mfma",
+                     "kernel": "gemm_mx_ring_kernel (FP4 MFMA GEMM, fused scatter-add epilogue)",
                      "achieved": round(achieved, 1), "peak": PEAK_FP4_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP4_TFLOPS, 4),
                      "traffic": None},
     }
+    traffic, note = measured_traffic(wl.name)
+    result["roofline"]["traffic"] = None if traffic is None else round(traffic)
+    result["roofline"]["traffic_note"] = note
 
     if not args.no_bf16_baseline:
         # All-bf16 reference product on hipBLASLt (torch.matmul), same shapes.

@@ -254,7 +254,8 @@ ADAHOP_API adahop_status adahop_gemm(adahop_op op, const uint16_t* lhs, const ui
 /* As adahop_gemm, and if stage_events is not NULL it must hold
  * ADAHOP_STAGE_EVENTS created hipEvent_t handles: events[0] is recorded on
  * `stream` before the first launch and events[1..5] after the FOID, lhs
- * quantization, rhs quantization, outlier product and GEMM stages (a stage
+ * quantization, rhs quantization (which ends with reordering both scale
+ * arrays for the GEMM), outlier product and GEMM stages (a stage
  * that does not run records its event right after the previous one). */
 #define ADAHOP_STAGE_EVENTS 6
 ADAHOP_API adahop_status adahop_gemm_timed(adahop_op op, const uint16_t* lhs,

@@ -245,6 +245,8 @@ adahop_status run_gemm(adahop_op op, const uint16_t* lhs, const uint16_t* rhs, i
   ADAHOP_TRY(iht_quant_launch(rhs, s.rhs_rows, s.rhs_cols, s.rhs_cols, s.rhs_contract, had,
                               P.zero_rhs ? idx : nullptr, P.zero_rhs ? pb.k : 0, P.rhs_zero_axis,
                               bc, bs, rl, stream));
+  void* gemm_scratch = P.off_gemm != kNone ? w + P.off_gemm : nullptr;
+  ADAHOP_TRY(gemm_mx_stage_scales(ac, as, bc, bs, s.m, s.n, s.K, gemm_scratch, P.gemm_bytes, stream));
   ADAHOP_TRY(E.record(3));
 
   OeEpilogue oe{};
@@ -275,8 +277,8 @@ adahop_status run_gemm(adahop_op op, const uint16_t* lhs, const uint16_t* rhs, i
     oe.b = lines_by_position(rl, P.rhs_zero_axis, s.rhs_cols, pb.k);  // (j, p)
   }
   ADAHOP_TRY(E.record(4));
-  ADAHOP_TRY(gemm_mx_launch(ac, as, bc, bs, s.m, s.n, s.K, oe, out, s.n, out_f32,
-                            P.off_gemm != kNone ? w + P.off_gemm : nullptr, P.gemm_bytes, stream));
+  ADAHOP_TRY(gemm_mx_launch(ac, as, bc, bs, s.m, s.n, s.K, oe, out, s.n, out_f32, gemm_scratch,
+                            P.gemm_bytes, stream));
   return E.record(5);
 }
 
@@ -408,6 +410,9 @@ adahop_status adahop_gemm_mx(const adahop_mx_operand* A, const adahop_mx_operand
   if (need > 0 && !aligned16(ws))
     return fail(ADAHOP_ERR_UNSUPPORTED, "adahop_gemm_mx: the workspace must be 16-byte aligned");
   const size_t partial_bytes = gemm_mx_partials_bytes(m, n, K, oe);
+  void* scratch = need > partial_bytes ? static_cast<char*>(ws) + partial_bytes : nullptr;
+  ADAHOP_TRY(gemm_mx_stage_scales(A->codes, A->scales, B->codes, B->scales, m, n, K, scratch,
+                                  need - partial_bytes, st));
   OeEpilogue e{};
   if (oe) {
     if (oe->k < 1 || !oe->a.ptr || !oe->b.ptr)
@@ -438,9 +443,7 @@ adahop_status adahop_gemm_mx(const adahop_mx_operand* A, const adahop_mx_operand
     }
   }
   return gemm_mx_launch(A->codes, A->scales, B->codes, B->scales, m, n, K, e, C, ldc,
-                        out_dtype == ADAHOP_OUT_F32 ? 1 : 0,
-                        need > partial_bytes ? static_cast<char*>(ws) + partial_bytes : nullptr,
-                        need - partial_bytes, st);
+                        out_dtype == ADAHOP_OUT_F32 ? 1 : 0, scratch, need - partial_bytes, st);
 }
 
 adahop_status adahop_gemm_plan(adahop_op op, int64_t T, int64_t Din, int64_t Dout,

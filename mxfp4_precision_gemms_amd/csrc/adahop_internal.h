@@ -58,8 +58,14 @@ struct OeEpilogue {
   Bf16View a, b;            // OE_INNER factors: a [m][k], b [n][k]
 };
 // Workspace the GEMM needs for (m, n, K): stage-major copies of both scale
-// arrays when the main kernel applies (K % 512 == 0), else 0.
+// arrays ([K/128][rows] words) when the main kernel applies (K % 512 == 0),
+// else 0. gemm_mx_stage_scales writes them (nothing to do when the main
+// kernel does not apply); gemm_mx_launch reads them from the same scratch.
 size_t gemm_mx_scratch_bytes(int64_t m, int64_t n, int64_t K);
+adahop_status gemm_mx_stage_scales(const uint8_t* a_codes, const uint8_t* a_scales,
+                                   const uint8_t* b_codes, const uint8_t* b_scales, int64_t m,
+                                   int64_t n, int64_t K, void* scratch, size_t scratch_bytes,
+                                   hipStream_t stream);
 adahop_status gemm_mx_launch(const uint8_t* a_codes, const uint8_t* a_scales,
                              const uint8_t* b_codes, const uint8_t* b_scales, int64_t m,
                              int64_t n, int64_t K, const OeEpilogue& oe, void* C, int64_t ldc,

@@ -893,6 +893,41 @@ size_t gemm_mx_scratch_bytes(int64_t m, int64_t n, int64_t K) {
   return align_up((size_t)m * (size_t)(K / 32), kAlign) + align_up((size_t)n * (size_t)(K / 32), kAlign);
 }
 
+namespace {
+bool ring_applies(const uint8_t* a_codes, const uint8_t* a_scales, const uint8_t* b_codes,
+                  const uint8_t* b_scales, int64_t m, int64_t n, int64_t K) {
+  const uintptr_t sc_bits = reinterpret_cast<uintptr_t>(a_scales) | reinterpret_cast<uintptr_t>(b_scales);
+  const uintptr_t cd_bits = reinterpret_cast<uintptr_t>(a_codes) | reinterpret_cast<uintptr_t>(b_codes);
+  return ring_shape_ok(m, n, K) && (sc_bits & 3u) == 0 && (cd_bits & 15u) == 0;
+}
+
+adahop_status check_scratch(void* scratch, size_t scratch_bytes, size_t need) {
+  if (scratch == nullptr || scratch_bytes < need || (reinterpret_cast<uintptr_t>(scratch) & 15u))
+    return fail(ADAHOP_ERR_WORKSPACE, "gemm_mx: scale staging needs " + std::to_string(need) +
+                                          " bytes of 16-byte aligned workspace");
+  return ADAHOP_OK;
+}
+
+uint32_t* staged_b(void* scratch, int64_t m, int64_t K) {
+  return static_cast<uint32_t*>(scratch) + align_up((size_t)m * (size_t)(K / 32), kAlign) / 4;
+}
+}  // namespace
+
+adahop_status gemm_mx_stage_scales(const uint8_t* a_codes, const uint8_t* a_scales,
+                                   const uint8_t* b_codes, const uint8_t* b_scales, int64_t m,
+                                   int64_t n, int64_t K, void* scratch, size_t scratch_bytes,
+                                   hipStream_t stream) {
+  if (!ring_applies(a_codes, a_scales, b_codes, b_scales, m, n, K)) return ADAHOP_OK;
+  const adahop_status st = check_scratch(scratch, scratch_bytes, gemm_mx_scratch_bytes(m, n, K));
+  if (st != ADAHOP_OK) return st;
+  const int64_t nst = K / 128, big = m > n ? m : n;
+  const dim3 tgrid((unsigned)((nst + kTr - 1) / kTr), (unsigned)((big + kTr - 1) / kTr), 2);
+  scale_stage_kernel<<<tgrid, dim3(256), 0, stream>>>(
+      reinterpret_cast<const uint32_t*>(a_scales), m, static_cast<uint32_t*>(scratch),
+      reinterpret_cast<const uint32_t*>(b_scales), n, staged_b(scratch, m, K), nst);
+  return check_launch("gemm_mx scale staging");
+}
+
 adahop_status gemm_mx_launch(const uint8_t* a_codes, const uint8_t* a_scales,
                              const uint8_t* b_codes, const uint8_t* b_scales, int64_t m,
                              int64_t n, int64_t K, const OeEpilogue& oe, void* C, int64_t ldc,
@@ -911,23 +946,12 @@ adahop_status gemm_mx_launch(const uint8_t* a_codes, const uint8_t* a_scales,
   g.ib_ptr = oe.b.ptr; g.ib_ld = oe.b.ld; g.ib_inner = oe.b.inner_contiguous;
   const dim3 grid((unsigned)(tiles_m * tiles_n)), block(kGemmThreads);
   const uintptr_t sc_bits = reinterpret_cast<uintptr_t>(a_scales) | reinterpret_cast<uintptr_t>(b_scales);
-  const uintptr_t cd_bits = reinterpret_cast<uintptr_t>(a_codes) | reinterpret_cast<uintptr_t>(b_codes);
-  const bool ring_ok = ring_shape_ok(m, n, K) && (sc_bits & 3u) == 0 && (cd_bits & 15u) == 0;
-  if (ring_ok) {
-    const size_t need = gemm_mx_scratch_bytes(m, n, K);
-    if (scratch == nullptr || scratch_bytes < need || (reinterpret_cast<uintptr_t>(scratch) & 15u))
-      return fail(ADAHOP_ERR_WORKSPACE, "gemm_mx: scale staging needs " + std::to_string(need) +
-                                            " bytes of 16-byte aligned workspace");
-    uint32_t* sst = static_cast<uint32_t*>(scratch);
-    g.a_sst = sst;
-    g.b_sst = sst + align_up((size_t)m * (size_t)(K / 32), kAlign) / 4;
-    const int64_t nst = K / 128, big = m > n ? m : n;
-    const dim3 tgrid((unsigned)((nst + kTr - 1) / kTr), (unsigned)((big + kTr - 1) / kTr), 2);
-    scale_stage_kernel<<<tgrid, dim3(256), 0, stream>>>(
-        reinterpret_cast<const uint32_t*>(a_scales), m, const_cast<uint32_t*>(g.a_sst),
-        reinterpret_cast<const uint32_t*>(b_scales), n, const_cast<uint32_t*>(g.b_sst), nst);
-    const adahop_status st = check_launch("gemm_mx scale staging");
+  if (ring_applies(a_codes, a_scales, b_codes, b_scales, m, n, K)) {
+    // The scales were reordered into `scratch` by gemm_mx_stage_scales.
+    const adahop_status st = check_scratch(scratch, scratch_bytes, gemm_mx_scratch_bytes(m, n, K));
     if (st != ADAHOP_OK) return st;
+    g.a_sst = static_cast<const uint32_t*>(scratch);
+    g.b_sst = staged_b(scratch, m, K);
     gemm_mx_ring_kernel<<<grid, block, 0, stream>>>(g);
   } else if (K % 256 == 0 && (sc_bits & 7u) == 0)
     gemm_mx_kernel<true><<<grid, block, 0, stream>>>(g);
