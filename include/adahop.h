@@ -134,7 +134,8 @@ ADAHOP_API adahop_status adahop_detect(const uint16_t* t, int64_t rows, int64_t 
  * src if zero_axis is ROWS, columns if COLS -- are treated as +0 (the
  * residual with the outliers removed). gathered (device, may be NULL when
  * nzero > 0 and the lines are not needed) receives a compact bf16 copy of
- * those lines: [nzero][cols] for rows, [rows][nzero] for columns.
+ * those lines, one line per row: [nzero][cols] for rows, [nzero][rows] for
+ * columns.
  * Rotation: hadamard_block 32 applies the orthonormal 32-point Walsh-Hadamard
  * transform (Sylvester order, fp32 butterflies with strides 1,2,4,8,16, then
  * one multiply by fp32(1/sqrt(32))) to each block; 0 applies none.
@@ -145,9 +146,10 @@ ADAHOP_API adahop_status adahop_detect(const uint16_t* t, int64_t rows, int64_t 
  * Output codes [outer][K/2] and scales [outer][K/32] (device).
  * Errors: INVALID for NULL src/codes/scales, bad sizes, K % 32 != 0,
  * hadamard_block not in {0, 32}, nzero < 0, or zero_idx NULL with nzero > 0;
- * UNSUPPORTED if codes is not 16-byte aligned, or (contract COLS) src rows
- * or gathered are not 16-byte aligned. Indices are not validated
- * on the device: out-of-range or unsorted zero_idx gives unspecified results. */
+ * UNSUPPORTED if codes or gathered are not 16-byte aligned, (contract COLS)
+ * src rows are not 16-byte aligned, or nzero > 1024. Indices are not
+ * validated on the device: unsorted or repeated zero_idx gives unspecified
+ * results, out-of-range entries are ignored. */
 ADAHOP_API adahop_status adahop_iht_quant(const uint16_t* src, int64_t rows, int64_t cols,
                                           int64_t ld, adahop_axis contract,
                                           int32_t hadamard_block, const int32_t* zero_idx,

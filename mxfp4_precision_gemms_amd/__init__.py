@@ -169,7 +169,7 @@ def adahop_iht_quant(src: torch.Tensor, contract, hadamard_block: int = 32,
     za = _axis(zero_axis)
     gathered = None
     if nz and gather:
-        shape = (nz, cols) if za == AXIS["ROWS"] else (rows, nz)
+        shape = (nz, cols) if za == AXIS["ROWS"] else (nz, rows)   # one line per row
         gathered = torch.empty(shape, dtype=torch.bfloat16, device=dev)
     if zero_idx is not None and zero_idx.dtype != torch.int32:
         raise TypeError("zero_idx must be int32")

@@ -63,15 +63,18 @@ Bf16View stored_view(const uint16_t* p, int64_t cols, int contract) {
   return {p, cols, contract == ADAHOP_AXIS_COLS ? 1 : 0};
 }
 
-// Gathered lines (adahop_iht_quant layout): rows -> [k][cols], columns ->
-// [rows][k]. As (line p, position x along the line):
-Bf16View lines_by_line(const uint16_t* g, int zero_axis, int64_t cols, int32_t k) {
-  return zero_axis == ADAHOP_AXIS_ROWS ? Bf16View{g, cols, 1} : Bf16View{g, k, 0};
+// Length of a line of the lhs or rhs along `axis` (a row has cols elements).
+int64_t line_len(const OpShape& s, bool lhs, int axis) {
+  const int64_t rows = lhs ? s.lhs_rows : s.rhs_rows, cols = lhs ? s.lhs_cols : s.rhs_cols;
+  return axis == ADAHOP_AXIS_ROWS ? cols : rows;
 }
+
+// Gathered lines (adahop_iht_quant layout): line-major [k][len], len = the
+// source's cols for extracted rows, its rows for extracted columns. As (line
+// p, position x along the line):
+Bf16View lines_by_line(const uint16_t* g, int64_t len) { return Bf16View{g, len, 1}; }
 // ... and as (position x, line p):
-Bf16View lines_by_position(const uint16_t* g, int zero_axis, int64_t cols, int32_t k) {
-  return zero_axis == ADAHOP_AXIS_ROWS ? Bf16View{g, cols, 0} : Bf16View{g, k, 1};
-}
+Bf16View lines_by_position(const uint16_t* g, int64_t len) { return Bf16View{g, len, 0}; }
 
 struct Plan {
   adahop_plan pub;
@@ -150,12 +153,8 @@ adahop_status make_plan(adahop_op op, int64_t T, int64_t Din, int64_t Dout,
   pb.off_a_scales = take((size_t)s.m * (size_t)(s.K / 32));
   pb.off_b_codes = take((size_t)s.n * (size_t)(s.K / 2));
   pb.off_b_scales = take((size_t)s.n * (size_t)(s.K / 32));
-  auto line_len = [&](bool lhs, int axis) {
-    const int64_t rows = lhs ? s.lhs_rows : s.rhs_rows, cols = lhs ? s.lhs_cols : s.rhs_cols;
-    return axis == ADAHOP_AXIS_ROWS ? cols : rows;
-  };
-  if (P->zero_lhs) pb.off_lhs_lines = take(2 * (size_t)pb.k * (size_t)line_len(true, P->lhs_zero_axis));
-  if (P->zero_rhs) pb.off_rhs_lines = take(2 * (size_t)pb.k * (size_t)line_len(false, P->rhs_zero_axis));
+  if (P->zero_lhs) pb.off_lhs_lines = take(2 * (size_t)pb.k * (size_t)line_len(s, true, P->lhs_zero_axis));
+  if (P->zero_rhs) pb.off_rhs_lines = take(2 * (size_t)pb.k * (size_t)line_len(s, false, P->rhs_zero_axis));
   if (route == ADAHOP_ROUTE_OE_LEFT || route == ADAHOP_ROUTE_OE_RIGHT) {
     const int64_t nx = route == ADAHOP_ROUTE_OE_LEFT ? pb.k : s.m;
     const int64_t ny = route == ADAHOP_ROUTE_OE_LEFT ? s.n : pb.k;
@@ -256,12 +255,12 @@ adahop_status run_gemm(adahop_op op, const uint16_t* lhs, const uint16_t* rhs, i
     Bf16View X, Y;
     int64_t nx, ny;
     if (pb.route == ADAHOP_ROUTE_OE_LEFT) {
-      X = lines_by_line(ll, P.lhs_zero_axis, s.lhs_cols, pb.k);       // (p, t)
+      X = lines_by_line(ll, line_len(s, true, P.lhs_zero_axis));       // (p, t)
       Y = stored_view(rhs, s.rhs_cols, s.rhs_contract);               // (j, t)
       nx = pb.k; ny = s.n;
     } else {
       X = stored_view(lhs, s.lhs_cols, s.lhs_contract);               // (i, t)
-      Y = lines_by_line(rl, P.rhs_zero_axis, s.rhs_cols, pb.k);       // (p, t)
+      Y = lines_by_line(rl, line_len(s, false, P.rhs_zero_axis));      // (p, t)
       nx = s.m; ny = pb.k;
     }
     ADAHOP_TRY(oe_product_launch(X, Y, nx, ny, s.K, P.splits, partials, stream));
@@ -273,8 +272,8 @@ adahop_status run_gemm(adahop_op op, const uint16_t* lhs, const uint16_t* rhs, i
   } else if (pb.route == ADAHOP_ROUTE_OE_INNER) {
     oe.mode = ADAHOP_ROUTE_OE_INNER;
     oe.k = pb.k;
-    oe.a = lines_by_position(ll, P.lhs_zero_axis, s.lhs_cols, pb.k);  // (i, p)
-    oe.b = lines_by_position(rl, P.rhs_zero_axis, s.rhs_cols, pb.k);  // (j, p)
+    oe.a = lines_by_position(ll, line_len(s, true, P.lhs_zero_axis));  // (i, p)
+    oe.b = lines_by_position(rl, line_len(s, false, P.rhs_zero_axis)); // (j, p)
   }
   ADAHOP_TRY(E.record(4));
   ADAHOP_TRY(gemm_mx_launch(ac, as, bc, bs, s.m, s.n, s.K, oe, out, s.n, out_f32, gemm_scratch,
@@ -370,14 +369,16 @@ adahop_status adahop_iht_quant(const uint16_t* src, int64_t rows, int64_t cols, 
     return fail(ADAHOP_ERR_INVALID, "adahop_iht_quant: hadamard_block must be 0 or 32");
   if (nzero < 0 || (nzero > 0 && !zero_idx))
     return fail(ADAHOP_ERR_INVALID, "adahop_iht_quant: bad zero list");
+  if (nzero > kMaxK) return fail(ADAHOP_ERR_UNSUPPORTED, "adahop_iht_quant: more than 1024 lines");
   if (nzero > 0 && zero_axis != ADAHOP_AXIS_ROWS && zero_axis != ADAHOP_AXIS_COLS)
     return fail(ADAHOP_ERR_INVALID, "adahop_iht_quant: bad zero axis");
   // Blocks along rows are read 16 bytes at a time; blocks down columns one
   // element per lane. Codes are written 16 bytes (or 4 bytes) at a time.
-  if (contract == ADAHOP_AXIS_COLS && (!aligned16(src) || ld % 8 != 0 || !aligned16(gathered)))
+  if (contract == ADAHOP_AXIS_COLS && (!aligned16(src) || ld % 8 != 0))
     return fail(ADAHOP_ERR_UNSUPPORTED, "adahop_iht_quant: rows must be 16-byte aligned");
-  if (!aligned16(codes))
-    return fail(ADAHOP_ERR_UNSUPPORTED, "adahop_iht_quant: codes must be 16-byte aligned");
+  if (!aligned16(codes) || !aligned16(gathered))
+    return fail(ADAHOP_ERR_UNSUPPORTED,
+                "adahop_iht_quant: codes and gathered must be 16-byte aligned");
   return iht_quant_launch(src, rows, cols, ld, contract, hadamard_block, zero_idx, nzero,
                           zero_axis, codes, scales, gathered, static_cast<hipStream_t>(stream));
 }

@@ -12,20 +12,21 @@
 //   exactly one 32-element MX block, plus that block's scale byte.
 // Tiling: a workgroup of 4 waves computes a 256 x 256 tile of C; each wave a
 //   128 x 128 sub-tile (4 x 4 MFMA blocks, 256 fp32 accumulators per lane,
-//   held in the accumulation registers). K advances 256 elements (128 bytes
-//   per row) per stage; stages are double buffered in LDS (A 32 KB + B 32 KB
-//   per stage) and the next stage's global loads (raw buffer loads over the
-//   tile's rows, which read 0 past the matrix edge) are in flight in
-//   registers during the current stage's 64 MFMAs per wave. LDS rows are
-//   padded to 144 bytes so a wave's 16-byte fragment reads hit distinct banks. Workgroup ids are remapped so that each XCD runs a 4 x 8 block of
-//   tiles at a time, whose operand rows its L2 shares.
-// Outlier product: bf16 matrix cores (v_mfma_f32_32x32x16_bf16), 64 x 64
+//   held in the accumulation registers). Workgroup ids are remapped so that
+//   each XCD works through a contiguous range of tiles, 4 tile-rows high,
+//   whose operand rows its L2 shares.
+// Main kernel (gemm_mx_ring_kernel, K % 512 == 0): K advances 128 elements
+//   per stage through a 4-slot LDS ring filled by direct global->LDS buffer
+//   loads four stages ahead; the scales come from a stage-major copy made
+//   just before (scale_stage_kernel). Other K: gemm_mx_kernel, 256-element
+//   stages double buffered in LDS with register-staged buffer loads.
+// Outlier product: bf16 matrix cores (v_mfma_f32_32x32x16_bf16), 128 x 64
 //   tiles, K split across workgroups into fp32 partials that a small kernel
 //   sums in a fixed order; the FP4 kernel's epilogue adds a line's reduced
 //   outlier product to the fp32 accumulators before the single rounding to
-//   the output type (the scatter-add). Inner extraction (rank-k term on every output) runs as extra
-//   bf16 MFMAs on the tile's own accumulators. No atomics: results are
-//   deterministic.
+//   the output type (the scatter-add). Inner extraction (a rank-k term on
+//   every output) runs as extra bf16 MFMAs on the tile's own accumulators.
+//   No atomics: results are deterministic.
 #include <utility>
 
 #include "adahop_internal.h"
@@ -650,9 +651,8 @@ __global__ void __launch_bounds__(kGemmThreads, 1) gemm_mx_ring_kernel(GemmArgs 
 // 128 x 64 tile (wave w: rows 32 w .. +31, both 32-column halves) with
 // v_mfma_f32_32x32x16_bf16 over 64-element K stages, double buffered in LDS
 // and prefetched one stage ahead in registers. Global loads are 16 bytes per
-// lane along each view's contiguous direction: a t-contiguous view lands in
-// LDS as [x][t] rows directly; an x-contiguous view is transposed while
-// stored. LDS rows hold 64 t plus 8 of padding (144 bytes).
+// lane along each view's contiguous direction and land in LDS in that same
+// order (OeTile); an x-contiguous view is transposed by the fragment reads.
 // ---------------------------------------------------------------------------
 constexpr int OX = 128, OY = 64, OK = 64, OPAD = 72, kOeThreads = 256;
 
@@ -664,13 +664,24 @@ struct OeArgs {
   void* C; int64_t ldc; int out_f32;   // direct output when partials == nullptr
 };
 
+// LDS tile of a view for one K stage: a t-contiguous (Inner) view is stored
+// as [R][OPAD] rows of t; an x-contiguous view keeps its memory order as
+// [OK][R + 4] rows of x. The x-major pitch (R + 4 elements: 264 or 136 bytes)
+// puts rows t and t + 8 -- read by the two half-waves of one fragment read --
+// 64 bytes apart modulo 256, so those reads are free of bank conflicts.
+template <int R, bool Inner>
+struct OeTile {
+  static constexpr int kElems = Inner ? R * OPAD : OK * (R + 4);
+};
+
 // Loads one [R][OK] tile of a view, starting at (r0, t0), into registers and
-// stores it into LDS as [R][OPAD] rows.
+// stores it into LDS in the OeTile layout.
 template <int R, bool Inner>
 struct TileLoader {
   // Each 16-byte chunk: Inner: row r, t-chunk c (8 t); else: t row, x-chunk (8 x).
   static constexpr int kChunks = R * OK / 8;
   static constexpr int kPerThread = kChunks / kOeThreads;
+  static constexpr int kXPitch = R + 4;
   uint4 v[kPerThread];
   __device__ __forceinline__ void load(const uint16_t* p, int64_t ld, int64_t r0, int64_t nr,
                                        int64_t t0, int64_t t1) {
@@ -717,18 +728,33 @@ struct TileLoader {
         *reinterpret_cast<uint4*>(&s[r * OPAD + c]) = v[i];
       } else {
         const int t = e / (R / 8), r = (e % (R / 8)) * 8;
-        const uint32_t w[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
-#pragma unroll
-        for (int j = 0; j < 8; ++j) s[(r + j) * OPAD + t] = (uint16_t)(w[j >> 1] >> (16 * (j & 1)));
+        uint2* d = reinterpret_cast<uint2*>(&s[t * kXPitch + r]);   // 8-byte aligned
+        d[0] = make_uint2(v[i].x, v[i].y);
+        d[1] = make_uint2(v[i].z, v[i].w);
       }
     }
+  }
+  // The MFMA fragment of row r (of this tile) for t = t0 .. t0 + 7.
+  __device__ __forceinline__ static v8bf frag(const uint16_t* s, int r, int t0) {
+    uint4 q;
+    if (Inner) {
+      q = *reinterpret_cast<const uint4*>(&s[r * OPAD + t0]);
+    } else {
+      uint32_t h[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) h[j] = s[(t0 + j) * kXPitch + r];
+      q = make_uint4(h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16));
+    }
+    return __builtin_bit_cast(v8bf, q);
   }
 };
 
 template <bool XIn, bool YIn>
 __global__ void __launch_bounds__(kOeThreads) oe_product_kernel(OeArgs g) {
-  __shared__ __attribute__((aligned(16))) uint16_t sx[2][OX * OPAD];
-  __shared__ __attribute__((aligned(16))) uint16_t sy[2][OY * OPAD];
+  using LX = TileLoader<OX, XIn>;
+  using LY = TileLoader<OY, YIn>;
+  __shared__ __attribute__((aligned(16))) uint16_t sx[2][OeTile<OX, XIn>::kElems];
+  __shared__ __attribute__((aligned(16))) uint16_t sy[2][OeTile<OY, YIn>::kElems];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t x0 = (int64_t)blockIdx.x * OX, y0 = (int64_t)blockIdx.y * OY;
   const int64_t tb = (int64_t)blockIdx.z * g.kchunk;
@@ -736,8 +762,8 @@ __global__ void __launch_bounds__(kOeThreads) oe_product_kernel(OeArgs g) {
   v16f acc0, acc1;
 #pragma unroll
   for (int v = 0; v < 16; ++v) { acc0[v] = 0.0f; acc1[v] = 0.0f; }
-  TileLoader<OX, XIn> lx;
-  TileLoader<OY, YIn> ly;
+  LX lx;
+  LY ly;
   const int nst = (int)((te - tb + OK - 1) / OK);
   if (nst > 0) {
     lx.load(g.x, g.xld, x0, g.nx, tb, te);
@@ -755,12 +781,11 @@ __global__ void __launch_bounds__(kOeThreads) oe_product_kernel(OeArgs g) {
 #pragma unroll
     for (int ks = 0; ks < OK; ks += 16) {
       const int off = ks + 8 * (lane >> 5);
-      const uint4 qa = *reinterpret_cast<const uint4*>(&sx[buf][(wave * 32 + (lane & 31)) * OPAD + off]);
-      const uint4 qb0 = *reinterpret_cast<const uint4*>(&sy[buf][(lane & 31) * OPAD + off]);
-      const uint4 qb1 = *reinterpret_cast<const uint4*>(&sy[buf][(32 + (lane & 31)) * OPAD + off]);
-      const v8bf fa = __builtin_bit_cast(v8bf, qa);
-      acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa, __builtin_bit_cast(v8bf, qb0), acc0, 0, 0, 0);
-      acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa, __builtin_bit_cast(v8bf, qb1), acc1, 0, 0, 0);
+      const v8bf fa = LX::frag(sx[buf], wave * 32 + (lane & 31), off);
+      const v8bf fb0 = LY::frag(sy[buf], lane & 31, off);
+      const v8bf fb1 = LY::frag(sy[buf], 32 + (lane & 31), off);
+      acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa, fb0, acc0, 0, 0, 0);
+      acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa, fb1, acc1, 0, 0, 0);
     }
     __builtin_amdgcn_sched_barrier(0);
     if (st + 1 < nst) {
@@ -812,7 +837,7 @@ __global__ void __launch_bounds__(256) oe_reduce_kernel(const float* __restrict_
 
 int oe_splits(int64_t nx, int64_t ny, int64_t K) {
   const int64_t tiles = ((nx + OX - 1) / OX) * ((ny + OY - 1) / OY);
-  int64_t s = (512 + tiles - 1) / tiles;            // about 2 workgroups per CU
+  int64_t s = (768 + tiles - 1) / tiles;            // about 3 workgroups per CU
   const int64_t smax = K / 512 > 0 ? K / 512 : 1;   // at least 512 K per split
   if (s > smax) s = smax;
   if (s > 64) s = 64;

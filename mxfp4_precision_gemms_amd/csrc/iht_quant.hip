@@ -13,8 +13,13 @@
 //     Butterfly strides 1 to 8 run in registers, stride 16 across the 2 lanes
 //     by a lane shuffle; the block amax takes one shuffle.
 //   contract ROWS (blocks down a column): one thread owns 4 adjacent columns
-//     of one 32-row block; each row is one 8-byte load, so a wave's row read
-//     is 512 contiguous bytes; each column's butterfly runs in registers.
+//     of one 32-row block; each row is one 8-byte load; each column's
+//     butterfly runs in registers; results are staged in LDS and written as
+//     whole row segments.
+// Extracted lines (the FOID indices) are found without searching: each
+// workgroup reads the index list once, coalesced, before its tile, and marks
+// the lines that fall inside its tile in LDS. The gathered lines are written
+// line-major, [nz][length of a line].
 // Both give bit-identical results to the same fp32 operations done one block
 // at a time: each butterfly output is one rounded fp32 add or subtract, then
 // one rounded multiply by fp32(1/sqrt(32)). The E2M1 codes come from gfx950's
@@ -57,26 +62,6 @@ __device__ __forceinline__ float e8m0_as_f32(int s) {
   return __uint_as_float((uint32_t)(s + 127) << 23);
 }
 
-// Position of v in the ascending list idx[0..n), or -1.
-__device__ __forceinline__ int find_sorted(const int32_t* idx, int n, int64_t v) {
-  int lo = 0, hi = n;
-  while (lo < hi) {
-    int mid = (lo + hi) >> 1;
-    if ((int64_t)idx[mid] < v) lo = mid + 1; else hi = mid;
-  }
-  return (lo < n && (int64_t)idx[lo] == v) ? lo : -1;
-}
-
-// First position with idx[pos] >= v.
-__device__ __forceinline__ int lower_bound(const int32_t* idx, int n, int64_t v) {
-  int lo = 0, hi = n;
-  while (lo < hi) {
-    int mid = (lo + hi) >> 1;
-    if ((int64_t)idx[mid] < v) lo = mid + 1; else hi = mid;
-  }
-  return lo;
-}
-
 constexpr int kRowThreads = 256;
 constexpr int kRowChunk = kRowThreads * 16;  // elements of one row per workgroup
 
@@ -84,20 +69,57 @@ constexpr int kRowChunk = kRowThreads * 16;  // elements of one row per workgrou
 // A lane owns 16 consecutive elements (two 16-byte loads), two lanes form a
 // 32-block: butterfly strides 1..8 in registers, stride 16 by one shuffle.
 __global__ void __launch_bounds__(kRowThreads)
-iht_quant_rowwise_kernel(const uint16_t* __restrict__ src, int64_t K, int64_t ld,
+iht_quant_rowwise_kernel(const uint16_t* __restrict__ src, int64_t rows, int64_t K, int64_t ld,
                          int chunks_per_row, int hadamard, const int32_t* __restrict__ zidx,
                          int nz, int zaxis, uint8_t* __restrict__ codes,
                          uint8_t* __restrict__ scales, uint16_t* __restrict__ gathered) {
+  // Whether this row is an extracted line (zero_axis ROWS: its position in
+  // the index list, else -1); which columns of this chunk are (zero_axis COLS).
+  __shared__ int32_t s_rowpos;
+  __shared__ uint32_t s_cmask[kRowChunk / 32];
+  const int tid = threadIdx.x;
   const int64_t r = blockIdx.x / chunks_per_row;
-  const int64_t col0 = (int64_t)(blockIdx.x % chunks_per_row) * kRowChunk + threadIdx.x * 16;
+  const int64_t cbase = (int64_t)(blockIdx.x % chunks_per_row) * kRowChunk;
+  const int64_t col0 = cbase + tid * 16;
   const bool active = col0 < K;   // K % 32 == 0: both lanes of a block agree
-  const bool upper = (threadIdx.x & 1) != 0;
+  const bool upper = (tid & 1) != 0;
 
+  // This thread's share of the index list, loaded before the row so that
+  // waiting for it does not wait for the row.
+  int zv[kMaxK / kRowThreads];
+#pragma unroll
+  for (int q = 0; q < kMaxK / kRowThreads; ++q) {
+    const int i = tid + q * kRowThreads;
+    zv[q] = i < nz ? zidx[i] : -1;
+  }
   uint4 raw0 = make_uint4(0, 0, 0, 0), raw1 = make_uint4(0, 0, 0, 0);
   if (active) {
     raw0 = *reinterpret_cast<const uint4*>(src + r * ld + col0);
     raw1 = *reinterpret_cast<const uint4*>(src + r * ld + col0 + 8);
   }
+
+  if (tid == 0) s_rowpos = -1;
+  if (tid < kRowChunk / 32) s_cmask[tid] = 0;
+  __syncthreads();
+  if (nz > 0) {
+#pragma unroll
+    for (int q = 0; q < kMaxK / kRowThreads; ++q) {
+      if (zv[q] < 0) continue;
+      const int i = tid + q * kRowThreads;
+      if (zaxis == ADAHOP_AXIS_ROWS) {
+        if (zv[q] == r) s_rowpos = i;
+      } else {
+        const int64_t d = (int64_t)zv[q] - cbase;
+        if (d >= 0 && d < kRowChunk && zv[q] < K) {
+          atomicOr(&s_cmask[d / 32], 1u << (d % 32));
+          // An extracted column: gathered [nz][rows], element (i, r).
+          if (gathered) gathered[(int64_t)i * rows + r] = src[r * ld + zv[q]];
+        }
+      }
+    }
+  }
+  __syncthreads();
+
   const uint32_t w[8] = {raw0.x, raw0.y, raw0.z, raw0.w, raw1.x, raw1.y, raw1.z, raw1.w};
   float y[16];
 #pragma unroll
@@ -105,10 +127,9 @@ iht_quant_rowwise_kernel(const uint16_t* __restrict__ src, int64_t K, int64_t ld
     y[2 * i] = bf16_bits_to_f32(w[i] & 0xFFFFu);
     y[2 * i + 1] = bf16_bits_to_f32(w[i] >> 16);
   }
-
   if (nz > 0 && active) {
     if (zaxis == ADAHOP_AXIS_ROWS) {
-      const int p = find_sorted(zidx, nz, r);
+      const int p = s_rowpos;
       if (p >= 0) {
         if (gathered) {
           *reinterpret_cast<uint4*>(gathered + (int64_t)p * K + col0) = raw0;
@@ -118,19 +139,9 @@ iht_quant_rowwise_kernel(const uint16_t* __restrict__ src, int64_t K, int64_t ld
         for (int i = 0; i < 16; ++i) y[i] = 0.0f;
       }
     } else {
-      // Registers are indexed by unrolled constants only: collect a mask of
-      // the zeroed positions, then select.
-      uint32_t zmask = 0;
-      for (int p = lower_bound(zidx, nz, col0); p < nz && zidx[p] < col0 + 16; ++p) {
-        const int i = (int)(zidx[p] - col0);
-        zmask |= 1u << i;
-        if (gathered) {
-          uint32_t word = 0;
-#pragma unroll
-          for (int q = 0; q < 8; ++q) word = (q == (i >> 1)) ? w[q] : word;
-          gathered[r * nz + p] = (uint16_t)((word >> (16 * (i & 1))) & 0xFFFFu);
-        }
-      }
+      // col0 - cbase is a multiple of 16: this lane's 16 columns sit in one word.
+      const int d = (int)(col0 - cbase);
+      const uint32_t zmask = (s_cmask[d / 32] >> (d % 32)) & 0xFFFFu;
 #pragma unroll
       for (int i = 0; i < 16; ++i) y[i] = ((zmask >> i) & 1u) ? 0.0f : y[i];
     }
@@ -172,103 +183,189 @@ iht_quant_rowwise_kernel(const uint16_t* __restrict__ src, int64_t K, int64_t ld
   }
 }
 
-constexpr int kColLanes = 64;    // columns per workgroup
-constexpr int kColBlocks = 4;    // 32-row blocks per workgroup
+// contract ROWS: a 256-thread workgroup owns 64 output rows (columns of the
+// source) x 16 blocks of 32 contraction positions. Thread t takes the 4
+// adjacent columns 4 (t % 16) .. +3 of block t / 16: each of the block's 32
+// rows is one 8-byte load (16 lanes read 128 contiguous bytes), and the
+// columns are rotated and quantized one after another from registers. Codes
+// and scales go to LDS first, then out as whole row segments: 256 code bytes
+// (16 lanes x 16 bytes) and 16 scale bytes per output row, so every 128-byte
+// line is written once, by one workgroup. Vec: the rows allow aligned 8-byte
+// loads (ld % 4 == 0, base 8-byte aligned); otherwise loads are per element.
+constexpr int kColThreads = 256;
+constexpr int kColGroups = 16;                 // 4-column groups per workgroup
+constexpr int kColOut = 4 * kColGroups;        // output rows per workgroup
+constexpr int kColBlocks = kColThreads / kColGroups;   // 32-row blocks per workgroup
+constexpr int kColPitch = kColBlocks * 16 + 16;        // LDS bytes per output row (padded)
 
-// contract ROWS, 4 columns per thread: thread (x, y) of a 64 x 4 workgroup
-// owns columns 4 (64 blockIdx.x + x) .. +3 of block blockIdx.y * 4 + y. Each
-// row of the block is one 8-byte load (a wave reads 512 contiguous bytes);
-// the columns are then rotated and quantized one after another from
-// registers. Vec: the rows allow aligned 8-byte loads (ld % 4 == 0, base
-// 8-byte aligned); otherwise the loads are per element.
 template <bool Vec>
-__global__ void __launch_bounds__(kColLanes * kColBlocks)
-iht_quant_colwise4_kernel(const uint16_t* __restrict__ src, int64_t K, int64_t outer, int64_t ld,
-                          int hadamard, const int32_t* __restrict__ zidx, int nz, int zaxis,
-                          uint8_t* __restrict__ codes, uint8_t* __restrict__ scales,
-                          uint16_t* __restrict__ gathered) {
-  const int64_t c0 = ((int64_t)blockIdx.x * kColLanes + threadIdx.x) * 4;
-  const int64_t b = (int64_t)blockIdx.y * kColBlocks + threadIdx.y;
-  if (c0 >= outer || b * 32 >= K) return;
+__global__ void __launch_bounds__(kColThreads)
+iht_quant_colwise_kernel(const uint16_t* __restrict__ src, int64_t K, int64_t outer, int64_t ld,
+                         int hadamard, const int32_t* __restrict__ zidx, int nz, int zaxis,
+                         uint8_t* __restrict__ codes, uint8_t* __restrict__ scales,
+                         uint16_t* __restrict__ gathered) {
+  __shared__ __attribute__((aligned(16))) uint8_t s_codes[kColOut * kColPitch];
+  __shared__ __attribute__((aligned(16))) uint8_t s_scales[kColOut * kColBlocks];
+  // Extracted lines inside this tile: rows (zero_axis ROWS) as one bit per
+  // row of each block, columns one bit per column; with their positions in
+  // the index list.
+  __shared__ uint32_t s_rmask[kColBlocks];
+  __shared__ int32_t s_rpos[kColBlocks * 32];
+  __shared__ uint32_t s_cmask[kColOut / 32];
+  __shared__ int32_t s_cpos[kColOut];
+  const int tid = threadIdx.x;
+  const int cg = tid % kColGroups, bi = tid / kColGroups;
+  const int64_t cbase = (int64_t)blockIdx.x * kColOut;
+  const int64_t bbase = (int64_t)blockIdx.y * kColBlocks;
+  const int64_t c0 = cbase + 4 * cg;
+  const int64_t b = bbase + bi;
+  const int64_t nblocks = K / 32;
+  const bool mine = c0 < outer && b < nblocks;
   const int64_t t0 = b * 32;
-  const bool whole = Vec && c0 + 4 <= outer;
 
-  uint32_t w[32][2];
+  // This thread's share of the index list, loaded before the tile so that
+  // waiting for it does not wait for the tile.
+  int zv[kMaxK / kColThreads];
 #pragma unroll
-  for (int j = 0; j < 32; ++j) {
-    if (whole) {
-      const uint2 q = *reinterpret_cast<const uint2*>(src + (t0 + j) * ld + c0);
-      w[j][0] = q.x;
-      w[j][1] = q.y;
-    } else {
-      uint32_t h[4];
-#pragma unroll
-      for (int q = 0; q < 4; ++q) h[q] = c0 + q < outer ? src[(t0 + j) * ld + c0 + q] : 0u;
-      w[j][0] = h[0] | (h[1] << 16);
-      w[j][1] = h[2] | (h[3] << 16);
-    }
+  for (int q = 0; q < kMaxK / kColThreads; ++q) {
+    const int i = tid + q * kColThreads;
+    zv[q] = i < nz ? zidx[i] : -1;
   }
 
-  // Rows of this block that are extracted lines (zero_axis ROWS).
-  uint32_t rmask = 0;
-  if (nz > 0 && zaxis == ADAHOP_AXIS_ROWS) {
-    for (int p = lower_bound(zidx, nz, t0); p < nz && zidx[p] < t0 + 32; ++p) {
-      const int j = (int)(zidx[p] - t0);
-      rmask |= 1u << j;
-      if (gathered) {
+  uint32_t w[32][2];
+  if (mine) {
+    const bool whole = Vec && c0 + 4 <= outer;
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
-          if (c0 + q < outer) gathered[(int64_t)p * outer + c0 + q] = src[(t0 + j) * ld + c0 + q];
+    for (int j = 0; j < 32; ++j) {
+      if (whole) {
+        const uint2 q = *reinterpret_cast<const uint2*>(src + (t0 + j) * ld + c0);
+        w[j][0] = q.x;
+        w[j][1] = q.y;
+      } else {
+        uint32_t h[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) h[q] = c0 + q < outer ? src[(t0 + j) * ld + c0 + q] : 0u;
+        w[j][0] = h[0] | (h[1] << 16);
+        w[j][1] = h[2] | (h[3] << 16);
       }
     }
   }
 
+  if (tid < kColBlocks) s_rmask[tid] = 0;
+  if (tid < kColOut / 32) s_cmask[tid] = 0;
+  __syncthreads();
+  if (nz > 0) {
+    const int64_t lo = zaxis == ADAHOP_AXIS_ROWS ? bbase * 32 : cbase;
+    const int span = zaxis == ADAHOP_AXIS_ROWS ? kColBlocks * 32 : kColOut;
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int64_t c = c0 + q;
-    if (c >= outer) break;
-    float y[32];
-#pragma unroll
-    for (int j = 0; j < 32; ++j) {
-      const uint32_t h = (w[j][q >> 1] >> (16 * (q & 1))) & 0xFFFFu;
-      y[j] = ((rmask >> j) & 1u) ? 0.0f : bf16_bits_to_f32(h);
+    for (int q = 0; q < kMaxK / kColThreads; ++q) {
+      const int64_t d = (int64_t)zv[q] - lo;
+      if (zv[q] >= 0 && d >= 0 && d < span) {
+        const int i = tid + q * kColThreads;
+        if (zaxis == ADAHOP_AXIS_ROWS) {
+          atomicOr(&s_rmask[d / 32], 1u << (d % 32));
+          s_rpos[d] = i;
+        } else {
+          atomicOr(&s_cmask[d / 32], 1u << (d % 32));
+          s_cpos[d] = i;
+        }
+      }
     }
-    if (nz > 0 && zaxis == ADAHOP_AXIS_COLS) {
-      const int p = find_sorted(zidx, nz, c);
-      if (p >= 0) {
-        if (gathered) {
+  }
+  __syncthreads();
+
+  if (mine) {
+    // Extracted rows of this block: gathered [nz][outer], zeroed below.
+    const uint32_t rmask = s_rmask[bi];
+    if (gathered && rmask) {
+      // Registers are indexed by unrolled constants only.
 #pragma unroll
-          for (int j = 0; j < 32; ++j)
-            gathered[(t0 + j) * nz + p] = (uint16_t)((w[j][q >> 1] >> (16 * (q & 1))) & 0xFFFFu);
+      for (int j = 0; j < 32; ++j) {
+        if (!((rmask >> j) & 1u)) continue;
+        const int64_t p = s_rpos[bi * 32 + j];
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          if (c0 + q < outer)
+            gathered[p * outer + c0 + q] = (uint16_t)((w[j][q >> 1] >> (16 * (q & 1))) & 0xFFFFu);
+      }
+    }
+
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int64_t c = c0 + q;
+      if (c >= outer) break;
+      float y[32];
+#pragma unroll
+      for (int j = 0; j < 32; ++j) {
+        const uint32_t h = (w[j][q >> 1] >> (16 * (q & 1))) & 0xFFFFu;
+        y[j] = ((rmask >> j) & 1u) ? 0.0f : bf16_bits_to_f32(h);
+      }
+      const int cl = 4 * cg + q;
+      if ((s_cmask[cl / 32] >> (cl % 32)) & 1u) {
+        // An extracted column: its 32 values of this block go to gathered
+        // [nz][K] as 64 contiguous bytes; the residual column is zero.
+        if (gathered) {
+          uint32_t pk[16];
+#pragma unroll
+          for (int j = 0; j < 16; ++j)
+            pk[j] = ((w[2 * j][q >> 1] >> (16 * (q & 1))) & 0xFFFFu) |
+                    (((w[2 * j + 1][q >> 1] >> (16 * (q & 1))) & 0xFFFFu) << 16);
+          uint4* g = reinterpret_cast<uint4*>(gathered + (int64_t)s_cpos[cl] * K + t0);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) g[j] = make_uint4(pk[4 * j], pk[4 * j + 1], pk[4 * j + 2], pk[4 * j + 3]);
         }
 #pragma unroll
         for (int j = 0; j < 32; ++j) y[j] = 0.0f;
       }
-    }
-    if (hadamard) {
+      if (hadamard) {
 #pragma unroll
-      for (int h = 1; h < 32; h <<= 1) {
+        for (int h = 1; h < 32; h <<= 1) {
 #pragma unroll
-        for (int i = 0; i < 32; ++i) {
-          if (i & h) continue;
-          const float a = y[i], bb = y[i + h];
-          y[i] = a + bb;
-          y[i + h] = a - bb;
+          for (int i = 0; i < 32; ++i) {
+            if (i & h) continue;
+            const float a = y[i], bb = y[i + h];
+            y[i] = a + bb;
+            y[i + h] = a - bb;
+          }
         }
+        const float cst = __uint_as_float(0x3E3504F3u);   // fp32(1/sqrt(32))
+#pragma unroll
+        for (int i = 0; i < 32; ++i) y[i] = y[i] * cst;
       }
-      const float cst = __uint_as_float(0x3E3504F3u);   // fp32(1/sqrt(32))
+      float amax = 0.0f;
 #pragma unroll
-      for (int i = 0; i < 32; ++i) y[i] = y[i] * cst;
+      for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(y[i]));
+      const int sx = block_exponent(amax);
+      const float scale = e8m0_as_f32(sx);
+      const int r = 4 * cg + q;
+      *reinterpret_cast<uint4*>(&s_codes[r * kColPitch + bi * 16]) =
+          make_uint4(pack8_e2m1(y, scale), pack8_e2m1(y + 8, scale), pack8_e2m1(y + 16, scale),
+                     pack8_e2m1(y + 24, scale));
+      s_scales[r * kColBlocks + bi] = (uint8_t)(sx + 127);
     }
-    float amax = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(y[i]));
-    const int sx = block_exponent(amax);
-    const float scale = e8m0_as_f32(sx);
-    *reinterpret_cast<uint4*>(codes + c * (K / 2) + b * 16) =
-        make_uint4(pack8_e2m1(y, scale), pack8_e2m1(y + 8, scale), pack8_e2m1(y + 16, scale),
-                   pack8_e2m1(y + 24, scale));
-    scales[c * (K / 32) + b] = (uint8_t)(sx + 127);
+  }
+  __syncthreads();
+
+  // Write-out: output row r of this tile gets nb consecutive blocks.
+  const int nrow = (int)(outer - cbase < kColOut ? outer - cbase : kColOut);
+  const int nb = (int)(nblocks - bbase < kColBlocks ? nblocks - bbase : kColBlocks);
+  for (int i = tid; i < kColOut * kColBlocks; i += kColThreads) {
+    const int r = i / kColBlocks, ch = i % kColBlocks;
+    if (r < nrow && ch < nb)
+      *reinterpret_cast<uint4*>(codes + (cbase + r) * (K / 2) + (bbase + ch) * 16) =
+          *reinterpret_cast<const uint4*>(&s_codes[r * kColPitch + ch * 16]);
+  }
+  const bool vec_scales = nb == kColBlocks && nblocks % 16 == 0 &&
+                          (reinterpret_cast<uintptr_t>(scales) & 15u) == 0;
+  if (vec_scales) {
+    if (tid < nrow)
+      *reinterpret_cast<uint4*>(scales + (cbase + tid) * nblocks + bbase) =
+          *reinterpret_cast<const uint4*>(&s_scales[tid * kColBlocks]);
+  } else {
+    for (int i = tid; i < kColOut * kColBlocks; i += kColThreads) {
+      const int r = i / kColBlocks, ch = i % kColBlocks;
+      if (r < nrow && ch < nb) scales[(cbase + r) * nblocks + bbase + ch] = s_scales[r * kColBlocks + ch];
+    }
   }
 }
 
@@ -285,20 +382,20 @@ adahop_status iht_quant_launch(const uint16_t* src, int64_t rows, int64_t cols, 
     const int64_t grid = rows * cpr;
     if (grid > 0x7FFFFFFFLL) return fail(ADAHOP_ERR_UNSUPPORTED, "iht_quant: tensor too large");
     iht_quant_rowwise_kernel<<<dim3((unsigned)grid), dim3(kRowThreads), 0, stream>>>(
-        src, K, ld, (int)cpr, had, zero_idx, nzero, zero_axis, codes, scales, gathered);
+        src, rows, K, ld, (int)cpr, had, zero_idx, nzero, zero_axis, codes, scales, gathered);
   } else {
     const int64_t K = rows, outer = cols;
-    const int64_t gx = (outer + 4 * kColLanes - 1) / (4 * kColLanes);
+    const int64_t gx = (outer + kColOut - 1) / kColOut;
     const int64_t gy = (K / 32 + kColBlocks - 1) / kColBlocks;
     if (gx > 0x7FFFFFFFLL || gy > 65535)
       return fail(ADAHOP_ERR_UNSUPPORTED, "iht_quant: tensor too large");
     const bool vec = ld % 4 == 0 && (reinterpret_cast<uintptr_t>(src) & 7u) == 0;
-    const dim3 grid((unsigned)gx, (unsigned)gy), block(kColLanes, kColBlocks);
+    const dim3 grid((unsigned)gx, (unsigned)gy), block(kColThreads);
     if (vec)
-      iht_quant_colwise4_kernel<true><<<grid, block, 0, stream>>>(
+      iht_quant_colwise_kernel<true><<<grid, block, 0, stream>>>(
           src, K, outer, ld, had, zero_idx, nzero, zero_axis, codes, scales, gathered);
     else
-      iht_quant_colwise4_kernel<false><<<grid, block, 0, stream>>>(
+      iht_quant_colwise_kernel<false><<<grid, block, 0, stream>>>(
           src, K, outer, ld, had, zero_idx, nzero, zero_axis, codes, scales, gathered);
   }
   return check_launch("iht_quant");

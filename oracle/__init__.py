@@ -137,7 +137,7 @@ def iht_quant(src: np.ndarray, contract: int, hadamard_block: int = 32,
     scales = np.zeros((outer, K // 32), dtype=np.uint8)
     gathered = None
     if z.size:
-        gathered = np.zeros((z.size, cols) if zero_axis == ROWS else (rows, z.size),
+        gathered = np.zeros((z.size, cols) if zero_axis == ROWS else (z.size, rows),
                             dtype=np.uint16)
     _check(_load().adahop_ref_iht_quant(_ptr(src), rows, cols, cols, contract, hadamard_block,
                                         _ptr(z) if z.size else None, z.size, zero_axis,

@@ -268,12 +268,13 @@ int adahop_ref_iht_quant(const uint16_t* src, int64_t rows, int64_t cols, int64_
     }
   }
   if (gathered && nzero > 0) {
+    /* One extracted line per row of `gathered`, in the source's order. */
     if (zero_axis == REF_AXIS_ROWS) {
       for (int32_t p = 0; p < nzero; ++p)
         for (int64_t c = 0; c < cols; ++c) gathered[p * cols + c] = src[zero_idx[p] * ld + c];
     } else {
-      for (int64_t r = 0; r < rows; ++r)
-        for (int32_t p = 0; p < nzero; ++p) gathered[r * nzero + p] = src[r * ld + zero_idx[p]];
+      for (int32_t p = 0; p < nzero; ++p)
+        for (int64_t r = 0; r < rows; ++r) gathered[p * rows + r] = src[r * ld + zero_idx[p]];
     }
   }
   return 0;

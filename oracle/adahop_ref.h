@@ -61,8 +61,8 @@ void adahop_ref_mx_block(const float y[32], uint8_t codes[16], uint8_t* scale);
  * contract COLS: blocks run along rows (K = cols, outer = rows);
  * contract ROWS: blocks run down columns (K = rows, outer = cols).
  * zero_axis: zero_idx names rows (ROWS) or columns (COLS) of src.
- * gathered (optional): the zeroed lines in bf16, [nzero][cols] for rows,
- * [rows][nzero] for columns. */
+ * gathered (optional): the zeroed lines in bf16, one line per row:
+ * [nzero][cols] for rows, [nzero][rows] for columns. */
 int adahop_ref_iht_quant(const uint16_t* src, int64_t rows, int64_t cols, int64_t ld,
                          int contract, int hadamard_block, const int32_t* zero_idx,
                          int32_t nzero, int zero_axis, uint8_t* codes, uint8_t* scales,

@@ -90,32 +90,28 @@ def gemm(op, lhs, rhs, T, Din, Dout, pat_lhs="N", pat_rhs="N", route=None, k=64,
     # Stage 3 (outlier half) + stage 4: the bf16 outlier product, scatter-added.
     idx = out["idx"]
     if r == "OE_LEFT":
-        # Rows idx of A, gathered as A-rows: A_g(p,t).
+        # Rows idx of A, gathered one line per row: A_g(p,t) = g[p][t].
         g = out["a_gathered"]
-        g_trans = 1 if op == "WGRAD" else 0     # GY columns come as [T][k]
         hit = np.nonzero(np.isin(rows, idx))[0]
         if hit.size:
             pos = np.searchsorted(idx, rows[hit])
-            oe, oabs = gemm_bf16(g, g_trans, rhs, b_trans, K, pos, cols)
+            oe, oabs = gemm_bf16(g, 0, rhs, b_trans, K, pos, cols)
             C[hit, :] += oe
             absC[hit, :] += oabs
     elif r == "OE_RIGHT":
+        # Columns idx of B, one line per row: B_g(t,p) = g[p][t].
         g = out["b_gathered"]
-        g_trans = 1 if op == "FWD" else 0       # W rows come as [k][Din]
         hit = np.nonzero(np.isin(cols, idx))[0]
         if hit.size:
             pos = np.searchsorted(idx, cols[hit])
-            oe, oabs = gemm_bf16(lhs, a_trans, g, g_trans, K, rows, pos)
+            oe, oabs = gemm_bf16(lhs, a_trans, g, 1, K, rows, pos)
             C[:, hit] += oe
             absC[:, hit] += oabs
     elif r == "OE_INNER":
         ga, gb = out["a_gathered"], out["b_gathered"]
         kk = idx.size
-        # A_g(i,p): FWD/DGRAD lhs columns [m][k]; WGRAD GY rows [k][Dout] (transposed).
-        ga_trans = 1 if op == "WGRAD" else 0
-        # B_g(p,j): FWD W columns [Dout][k] (transposed); DGRAD W rows, WGRAD X rows [k][n].
-        gb_trans = 1 if op == "FWD" else 0
-        oe, oabs = gemm_bf16(ga, ga_trans, gb, gb_trans, kk, rows, cols)
+        # Inner lines, one per row: A_g(i,p) = ga[p][i], B_g(p,j) = gb[p][j].
+        oe, oabs = gemm_bf16(ga, 1, gb, 0, kk, rows, cols)
         C += oe
         absC += oabs
     out.update(C=C, absC=absC)

@@ -131,12 +131,11 @@ def test_outlier_split_identity(op, pat_lhs, pat_rhs, route):
         Ai = {"FWD": L, "DGRAD": L, "WGRAD": L.T}[op][:, idx]
         Bi = {"FWD": R.T, "DGRAD": R, "WGRAD": R}[op][idx, :]
         assert np.array_equal(C - res, Ai @ Bi)
-    # The gathered lines are the source bits, laid out [k][len] for rows and
-    # [len][k] for columns.
+    # The gathered lines are the source bits, one line per row: [k][len].
     tensor, axis = oracle.scan_target(op, route)
     g = r["a_gathered"] if tensor == 0 else r["b_gathered"]
     src = lhs if tensor == 0 else rhs
-    assert np.array_equal(g, src[idx, :] if axis == oracle.ROWS else src[:, idx])
+    assert np.array_equal(g, src[idx, :] if axis == oracle.ROWS else src[:, idx].T)
 
 
 def test_split_identity_unquantized():
@@ -155,7 +154,7 @@ def test_split_identity_unquantized():
             assert np.array_equal(g, t[idx, :])
         else:
             assert np.all(deq[idx, :] == 0)      # outer = columns here
-            assert np.array_equal(g, t[:, idx])
+            assert np.array_equal(g, t[:, idx].T)   # one extracted line per row
     # Zeroing inner lines equals quantizing a copy with those entries zeroed.
     z = t.copy(); z[:, idx] = 0
     c1, s1, _ = oracle.iht_quant(t, oracle.COLS, 32, idx, oracle.COLS)
