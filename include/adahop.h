@@ -90,6 +90,14 @@ typedef enum {
 typedef enum { ADAHOP_AXIS_ROWS = 0, ADAHOP_AXIS_COLS = 1 } adahop_axis;
 typedef enum { ADAHOP_OUT_BF16 = 0, ADAHOP_OUT_F32 = 1 } adahop_out_dtype;
 
+/* Layout of packed MXFP4 operands in an adahop_gemm workspace.
+ *   ROWS  : codes [outer][K/2], scales [outer][K/32] (as adahop_iht_quant).
+ *   KCHUNK: K cut into chunks of 128: codes [K/128][outer][64] and scales
+ *           [K/128][outer][4], i.e. chunk c of row r holds K-elements
+ *           128 c .. 128 c + 127 of that row, each chunk of all rows
+ *           contiguous -- the order in which the GEMM streams them. */
+typedef enum { ADAHOP_LAYOUT_ROWS = 0, ADAHOP_LAYOUT_KCHUNK = 1 } adahop_layout;
+
 ADAHOP_API const char* adahop_status_string(int status);
 /* Detail of the last failure on this host thread ("" if none). */
 ADAHOP_API const char* adahop_last_error(void);
@@ -219,7 +227,9 @@ ADAHOP_API adahop_status adahop_gemm_mx(const adahop_mx_operand* A,
  * to (pat_lhs, pat_rhs); oe_rank is the number of extracted lines (64 on the
  * pages, Fig. 10). The contraction length (Din, Dout or T) must be a
  * multiple of 32. The workspace holds, after the call, the quantized
- * operands and the outlier lines at the offsets adahop_gemm_plan reports.
+ * operands and the outlier lines at the offsets adahop_gemm_plan reports;
+ * the operands are in the plan's layout (KCHUNK when the contraction length
+ * is a multiple of 512 and each packed operand is under 2 GiB, else ROWS).
  * Errors: as for the stage calls; INVALID for a bad op or route, or an OE
  * route with oe_rank < 1 or above the number of candidate lines. */
 typedef struct {
@@ -228,12 +238,12 @@ typedef struct {
   int32_t k;              /* extracted lines (0 without OE) */
   int32_t scan_tensor;    /* 0 = lhs, 1 = rhs, -1 = no FOID */
   adahop_axis scan_axis;  /* candidate lines: rows or columns of that tensor */
-  int32_t reserved;
+  adahop_layout layout;   /* layout of the packed operands below */
   size_t ws_bytes;        /* workspace the call needs */
   /* Byte offsets into the workspace (SIZE_MAX if absent): */
   size_t off_idx;         /* int32 [k] FOID indices */
-  size_t off_a_codes, off_a_scales;   /* A packed: [m][K/2], [m][K/32] */
-  size_t off_b_codes, off_b_scales;   /* B packed: [n][K/2], [n][K/32] */
+  size_t off_a_codes, off_a_scales;   /* A packed (outer = m) in `layout` */
+  size_t off_b_codes, off_b_scales;   /* B packed (outer = n) in `layout` */
   size_t off_lhs_lines;   /* bf16 lines gathered from lhs (layout as adahop_iht_quant) */
   size_t off_rhs_lines;   /* bf16 lines gathered from rhs */
 } adahop_plan;

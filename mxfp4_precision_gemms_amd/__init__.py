@@ -52,7 +52,7 @@ class OeDesc(ctypes.Structure):
 
 class Plan(ctypes.Structure):
     _fields_ = [("route", _int), ("m", _i64), ("n", _i64), ("K", _i64), ("k", _i32),
-                ("scan_tensor", _i32), ("scan_axis", _int), ("reserved", _i32),
+                ("scan_tensor", _i32), ("scan_axis", _int), ("layout", _int),
                 ("ws_bytes", _sz), ("off_idx", _sz), ("off_a_codes", _sz),
                 ("off_a_scales", _sz), ("off_b_codes", _sz), ("off_b_scales", _sz),
                 ("off_lhs_lines", _sz), ("off_rhs_lines", _sz)]
@@ -283,8 +283,13 @@ def _event_handle(ev: "torch.cuda.Event") -> int:
     return ev.cuda_event
 
 
+LAYOUT_ROWS, LAYOUT_KCHUNK = 0, 1
+
+
 def workspace_views(ws: torch.Tensor, plan: Plan) -> dict:
-    """The intermediates a call leaves in its workspace, as tensors."""
+    """The intermediates a call leaves in its workspace, as tensors. Packed
+    operands are returned in the row-major layout ([outer][K/2] codes,
+    [outer][K/32] scales); a K-chunked plan's are reordered into it (a copy)."""
     none = (1 << 64) - 1
     m, n, K, k = plan.m, plan.n, plan.K, plan.k
 
@@ -294,16 +299,17 @@ def workspace_views(ws: torch.Tensor, plan: Plan) -> dict:
         nbytes = count * torch.tensor([], dtype=dtype).element_size()
         return ws[off:off + nbytes].view(dtype)
 
-    out = {
-        "idx": region(plan.off_idx, k, torch.int32),
-        "a_codes": region(plan.off_a_codes, m * (K // 2), torch.uint8),
-        "a_scales": region(plan.off_a_scales, m * (K // 32), torch.uint8),
-        "b_codes": region(plan.off_b_codes, n * (K // 2), torch.uint8),
-        "b_scales": region(plan.off_b_scales, n * (K // 32), torch.uint8),
-    }
-    if out["a_codes"] is not None:
-        out["a_codes"] = out["a_codes"].view(m, K // 2)
-        out["a_scales"] = out["a_scales"].view(m, K // 32)
-        out["b_codes"] = out["b_codes"].view(n, K // 2)
-        out["b_scales"] = out["b_scales"].view(n, K // 32)
+    def packed(off_codes, off_scales, outer):
+        codes = region(off_codes, outer * (K // 2), torch.uint8)
+        scales = region(off_scales, outer * (K // 32), torch.uint8)
+        if codes is None:
+            return None, None
+        if plan.layout == LAYOUT_KCHUNK:     # [K/128][outer][64], [K/128][outer][4]
+            codes = codes.view(K // 128, outer, 64).permute(1, 0, 2).reshape(outer, K // 2)
+            scales = scales.view(K // 128, outer, 4).permute(1, 0, 2).reshape(outer, K // 32)
+        return codes.view(outer, K // 2), scales.view(outer, K // 32)
+
+    out = {"idx": region(plan.off_idx, k, torch.int32)}
+    out["a_codes"], out["a_scales"] = packed(plan.off_a_codes, plan.off_a_scales, m)
+    out["b_codes"], out["b_scales"] = packed(plan.off_b_codes, plan.off_b_scales, n)
     return out

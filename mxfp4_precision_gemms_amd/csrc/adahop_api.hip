@@ -108,6 +108,7 @@ adahop_status make_plan(adahop_op op, int64_t T, int64_t Din, int64_t Dout,
   pb.m = s.m; pb.n = s.n; pb.K = s.K;
   pb.scan_tensor = -1;
   pb.scan_axis = ADAHOP_AXIS_ROWS;
+  pb.layout = ADAHOP_LAYOUT_ROWS;
   pb.off_idx = pb.off_a_codes = pb.off_a_scales = pb.off_b_codes = pb.off_b_scales = kNone;
   pb.off_lhs_lines = pb.off_rhs_lines = kNone;
   if (route == ADAHOP_ROUTE_BF16) { pb.ws_bytes = 0; return ADAHOP_OK; }
@@ -161,7 +162,10 @@ adahop_status make_plan(adahop_op op, int64_t T, int64_t Din, int64_t Dout,
     P->splits = oe_splits(nx, ny, s.K);
     P->off_partials = take(sizeof(float) * (size_t)(P->splits + 1) * (size_t)nx * (size_t)ny);
   }
-  P->gemm_bytes = gemm_mx_scratch_bytes(s.m, s.n, s.K);
+  // Operands the main GEMM kernel streams are packed K-chunked by the
+  // quantizers; otherwise row-major, with the GEMM's own scale reordering.
+  pb.layout = gemm_mx_kchunk_ok(s.m, s.n, s.K) ? ADAHOP_LAYOUT_KCHUNK : ADAHOP_LAYOUT_ROWS;
+  P->gemm_bytes = pb.layout == ADAHOP_LAYOUT_ROWS ? gemm_mx_scratch_bytes(s.m, s.n, s.K) : 0;
   if (P->gemm_bytes) P->off_gemm = take(P->gemm_bytes);
   pb.ws_bytes = off;
   return ADAHOP_OK;
@@ -239,13 +243,14 @@ adahop_status run_gemm(adahop_op op, const uint16_t* lhs, const uint16_t* rhs, i
   uint16_t* rl = pb.off_rhs_lines != kNone ? reinterpret_cast<uint16_t*>(w + pb.off_rhs_lines) : nullptr;
   ADAHOP_TRY(iht_quant_launch(lhs, s.lhs_rows, s.lhs_cols, s.lhs_cols, s.lhs_contract, had,
                               P.zero_lhs ? idx : nullptr, P.zero_lhs ? pb.k : 0, P.lhs_zero_axis,
-                              ac, as, ll, stream));
+                              ac, as, ll, pb.layout, stream));
   ADAHOP_TRY(E.record(2));
   ADAHOP_TRY(iht_quant_launch(rhs, s.rhs_rows, s.rhs_cols, s.rhs_cols, s.rhs_contract, had,
                               P.zero_rhs ? idx : nullptr, P.zero_rhs ? pb.k : 0, P.rhs_zero_axis,
-                              bc, bs, rl, stream));
+                              bc, bs, rl, pb.layout, stream));
   void* gemm_scratch = P.off_gemm != kNone ? w + P.off_gemm : nullptr;
-  ADAHOP_TRY(gemm_mx_stage_scales(ac, as, bc, bs, s.m, s.n, s.K, gemm_scratch, P.gemm_bytes, stream));
+  if (pb.layout == ADAHOP_LAYOUT_ROWS)
+    ADAHOP_TRY(gemm_mx_stage_scales(ac, as, bc, bs, s.m, s.n, s.K, gemm_scratch, P.gemm_bytes, stream));
   ADAHOP_TRY(E.record(3));
 
   OeEpilogue oe{};
@@ -276,8 +281,8 @@ adahop_status run_gemm(adahop_op op, const uint16_t* lhs, const uint16_t* rhs, i
     oe.b = lines_by_position(rl, line_len(s, false, P.rhs_zero_axis)); // (j, p)
   }
   ADAHOP_TRY(E.record(4));
-  ADAHOP_TRY(gemm_mx_launch(ac, as, bc, bs, s.m, s.n, s.K, oe, out, s.n, out_f32, gemm_scratch,
-                            P.gemm_bytes, stream));
+  ADAHOP_TRY(gemm_mx_launch(ac, as, bc, bs, s.m, s.n, s.K, pb.layout, oe, out, s.n, out_f32,
+                            gemm_scratch, P.gemm_bytes, stream));
   return E.record(5);
 }
 
@@ -380,7 +385,8 @@ adahop_status adahop_iht_quant(const uint16_t* src, int64_t rows, int64_t cols, 
     return fail(ADAHOP_ERR_UNSUPPORTED,
                 "adahop_iht_quant: codes and gathered must be 16-byte aligned");
   return iht_quant_launch(src, rows, cols, ld, contract, hadamard_block, zero_idx, nzero,
-                          zero_axis, codes, scales, gathered, static_cast<hipStream_t>(stream));
+                          zero_axis, codes, scales, gathered, ADAHOP_LAYOUT_ROWS,
+                          static_cast<hipStream_t>(stream));
 }
 
 size_t adahop_gemm_mx_workspace_size(int64_t m, int64_t n, int64_t K, const adahop_oe* oe) {
@@ -443,7 +449,8 @@ adahop_status adahop_gemm_mx(const adahop_mx_operand* A, const adahop_mx_operand
       return fail(ADAHOP_ERR_INVALID, "adahop_gemm_mx: outlier route must be OE_LEFT, OE_RIGHT or OE_INNER");
     }
   }
-  return gemm_mx_launch(A->codes, A->scales, B->codes, B->scales, m, n, K, e, C, ldc,
+  return gemm_mx_launch(A->codes, A->scales, B->codes, B->scales, m, n, K, ADAHOP_LAYOUT_ROWS, e,
+                        C, ldc,
                         out_dtype == ADAHOP_OUT_F32 ? 1 : 0, scratch, need - partial_bytes, st);
 }
 

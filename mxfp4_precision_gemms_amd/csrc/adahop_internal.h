@@ -30,7 +30,7 @@ adahop_status foid_launch(const uint16_t* t, int64_t rows, int64_t cols, int64_t
 adahop_status iht_quant_launch(const uint16_t* src, int64_t rows, int64_t cols, int64_t ld,
                                int contract, int32_t hadamard_block, const int32_t* zero_idx,
                                int32_t nzero, int zero_axis, uint8_t* codes, uint8_t* scales,
-                               uint16_t* gathered, hipStream_t stream);
+                               uint16_t* gathered, int layout, hipStream_t stream);
 
 // ---- outlier product (bf16 MFMA) ------------------------------------------
 // P_s[x][y] = sum over t in split s of X(x, t) * Y(y, t), fp32, for s < splits,
@@ -62,14 +62,19 @@ struct OeEpilogue {
 // else 0. gemm_mx_stage_scales writes them (nothing to do when the main
 // kernel does not apply); gemm_mx_launch reads them from the same scratch.
 size_t gemm_mx_scratch_bytes(int64_t m, int64_t n, int64_t K);
+// Whether (m, n, K) operands may be packed K-chunked (ADAHOP_LAYOUT_KCHUNK):
+// the main kernel applies and stage offsets fit 31 bits.
+bool gemm_mx_kchunk_ok(int64_t m, int64_t n, int64_t K);
 adahop_status gemm_mx_stage_scales(const uint8_t* a_codes, const uint8_t* a_scales,
                                    const uint8_t* b_codes, const uint8_t* b_scales, int64_t m,
                                    int64_t n, int64_t K, void* scratch, size_t scratch_bytes,
                                    hipStream_t stream);
+// layout ROWS: scales reordered by gemm_mx_stage_scales into `scratch` when
+// the main kernel applies; KCHUNK: operands as ADAHOP_LAYOUT_KCHUNK, no scratch.
 adahop_status gemm_mx_launch(const uint8_t* a_codes, const uint8_t* a_scales,
                              const uint8_t* b_codes, const uint8_t* b_scales, int64_t m,
-                             int64_t n, int64_t K, const OeEpilogue& oe, void* C, int64_t ldc,
-                             int out_f32, void* scratch, size_t scratch_bytes,
+                             int64_t n, int64_t K, int layout, const OeEpilogue& oe, void* C,
+                             int64_t ldc, int out_f32, void* scratch, size_t scratch_bytes,
                              hipStream_t stream);
 
 }  // namespace adahop

@@ -11,12 +11,17 @@
 // row is one 128-byte run, read as 8 16-byte loads when aligned. With the
 // full 64-element probe the values stay in registers between the two passes.
 //
-// Selection without a host round trip and without atomics: a workgroup sorts
-// up to 2048 (score, index) pairs in LDS with a bitonic network on the key
-// (score descending, index ascending) -- a strict total order, so the result
-// is unique -- and keeps its best k. The survivors of all workgroups form the
-// next level; when at most 2048 remain one workgroup takes the best k and
-// sorts their indices ascending. Each level divides the count by 2048 / k.
+// Selection without a host round trip and without atomics, by radix select
+// on the fp64 score bits (scores are >= 0, so their bit patterns order like
+// the values): a workgroup holds 4 or 16 scores per thread in registers, and
+// 16 passes of 4-bit digits (per-thread packed counters, wave and workgroup
+// sums) find the k-th largest score T exactly. Every score above T
+// is kept, and of the scores equal to T the ones with the lowest indices --
+// the key (score descending, index ascending) is a strict total order, so
+// the result is unique. A prefix sum over the threads, which own the
+// candidates in index order, writes the kept indices already sorted. Levels
+// of many workgroups first cut every chunk of 1024 candidates (4096 when
+// k > 256) to its best k, until one workgroup can take the rest.
 #include <climits>
 
 #include "adahop_internal.h"
@@ -27,13 +32,8 @@ namespace adahop {
 namespace {
 
 constexpr int kVarThreads = 256;
-constexpr int kSelThreads = 256;
-constexpr int kChunk = 2048;           // >= 2 * max k, so every level shrinks
 constexpr int kProbe = 64;
 
-__device__ __forceinline__ bool before(double va, int ia, double vb, int ib) {
-  return va > vb || (va == vb && ia < ib);
-}
 
 __device__ __forceinline__ double bf16_to_f64(uint32_t h) {
   return (double)__uint_as_float(h << 16);
@@ -88,101 +88,185 @@ foid_var_kernel(const uint16_t* __restrict__ t, int64_t ld, int axis, int P, int
   var[l] = ss / (double)P;
 }
 
-// Sorts s_var/s_idx[0..n) (n a power of two) so that the best entry comes first.
-__device__ void bitonic_sort_desc(double* s_var, int* s_idx, int n) {
-  for (int size = 2; size <= n; size <<= 1) {
-    for (int stride = size >> 1; stride > 0; stride >>= 1) {
-      __syncthreads();
-      for (int e = threadIdx.x; e < n / 2; e += kSelThreads) {
-        const int i = 2 * stride * (e / stride) + (e % stride);
-        const int j = i + stride;
-        const bool best_first = (i & size) == 0;
-        const double vi = s_var[i], vj = s_var[j];
-        const int ii = s_idx[i], ij = s_idx[j];
-        const bool swap = best_first ? before(vj, ij, vi, ii) : before(vi, ii, vj, ij);
-        if (swap) {
-          s_var[i] = vj; s_var[j] = vi;
-          s_idx[i] = ij; s_idx[j] = ii;
-        }
-      }
-    }
+constexpr int kSelThreads = 256;
+
+// Exclusive prefix sum of v over the workgroup's threads in order; *total
+// receives the sum. Uses s_tmp[THREADS / 64].
+template <int THREADS>
+__device__ __forceinline__ int block_exclusive_scan(int v, int* s_tmp, int* total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int x = v;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(x, off);
+    if (lane >= off) x += y;
+  }
+  if (lane == 63) s_tmp[wave] = x;
+  __syncthreads();
+  int before = 0, sum = 0;
+#pragma unroll
+  for (int w = 0; w < THREADS / 64; ++w) {
+    const int t = s_tmp[w];
+    before += w < wave ? t : 0;
+    sum += t;
   }
   __syncthreads();
+  *total = sum;
+  return before + x - v;
 }
 
-// Ascending sort of s_key[0..n), n a power of two.
-__device__ void bitonic_sort_int_asc(int* s_key, int n) {
-  for (int size = 2; size <= n; size <<= 1) {
-    for (int stride = size >> 1; stride > 0; stride >>= 1) {
-      __syncthreads();
-      for (int e = threadIdx.x; e < n / 2; e += kSelThreads) {
-        const int i = 2 * stride * (e / stride) + (e % stride);
-        const int j = i + stride;
-        const bool up = (i & size) == 0;
-        const int a = s_key[i], b = s_key[j];
-        if (up ? (a > b) : (a < b)) { s_key[i] = b; s_key[j] = a; }
-      }
-    }
-  }
-  __syncthreads();
-}
-
-__device__ __forceinline__ int pow2_at_least(int v) {
-  int n = 1;
-  while (n < v) n <<= 1;
-  return n;
-}
-
-// One selection level over `count` entries: (in_var[i], in_idx ? in_idx[i] : i).
-// Each workgroup keeps the best k of its chunk (sentinels where it has fewer)
-// at out + blockIdx.x * k, or, with final_idx set (one workgroup), writes the
-// best k indices in ascending order.
-__global__ void __launch_bounds__(kSelThreads)
+// One selection over entries (in_var[i], in_idx ? in_idx[i] : i), i < count,
+// in chunks of THREADS * KPT per workgroup (KPT entries per thread); entries
+// with a negative score are padding. Non-final: the chunk's best k entries (all of them if it has
+// fewer, then padding) go to out_var/out_idx + blockIdx.x * k in index order.
+// Final (one workgroup): the best k indices go to final_idx in ascending
+// order (k <= the number of real entries, checked on the host).
+template <int THREADS, int KPT>
+__global__ void __launch_bounds__(THREADS)
 foid_select_kernel(const double* __restrict__ in_var, const int32_t* __restrict__ in_idx,
                    int64_t count, int k, double* __restrict__ out_var,
                    int32_t* __restrict__ out_idx, int32_t* __restrict__ final_idx) {
-  __shared__ double s_var[kChunk];
-  __shared__ int s_idx[kChunk];
-  const int64_t base = (int64_t)blockIdx.x * kChunk;
-  const int valid = (int)(count - base < kChunk ? count - base : kChunk);
-  const int n = pow2_at_least(valid > k ? valid : k);
-  for (int slot = threadIdx.x; slot < n; slot += kSelThreads) {
-    const int64_t g = base + slot;
-    if (slot < valid) {
-      s_var[slot] = in_var[g];
-      s_idx[slot] = in_idx ? in_idx[g] : (int)g;
-    } else {
-      s_var[slot] = -1.0;       // scores are >= 0, so sentinels sort last
-      s_idx[slot] = INT_MAX;
-    }
-  }
-  bitonic_sort_desc(s_var, s_idx, n);
+  constexpr int kWaves = THREADS / 64;
+  __shared__ uint32_t s_cnt[kWaves][16];
+  __shared__ uint32_t s_tot[16];
+  __shared__ int s_tmp[kWaves];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t first = (int64_t)blockIdx.x * THREADS * KPT + (int64_t)tid * KPT;
 
-  if (final_idx == nullptr) {
-    for (int p = threadIdx.x; p < k; p += kSelThreads) {
-      out_var[(int64_t)blockIdx.x * k + p] = s_var[p];
-      out_idx[(int64_t)blockIdx.x * k + p] = s_idx[p];
+  uint64_t key[KPT];
+  uint32_t valid = 0;
+#pragma unroll
+  for (int j = 0; j < KPT; ++j) {
+    const int64_t g = first + j;
+    const double v = g < count ? in_var[g] : -1.0;
+    key[j] = (uint64_t)__double_as_longlong(v);
+    valid |= (v >= 0.0 ? 1u : 0u) << j;
+  }
+  int nvalid;
+  block_exclusive_scan<THREADS>(__popc(valid), s_tmp, &nvalid);
+
+  // T = the k-th largest key; krem = how many keys equal to T are kept.
+  uint64_t prefix = 0, pmask = 0;
+  int krem = k;
+  if (nvalid > k) {
+    for (int pass = 0; pass < 16; ++pass) {
+      const int shift = 60 - 4 * pass;
+        uint64_t c[4] = {0, 0, 0, 0};   // 16 counters of 16 bits: digit d in c[d / 4]
+#pragma unroll
+      for (int j = 0; j < KPT; ++j) {
+        const bool in = ((valid >> j) & 1u) && (key[j] & pmask) == prefix;
+        const int d = (int)((key[j] >> shift) & 15u);
+        const uint64_t inc = in ? (1ull << (16 * (d & 3))) : 0ull;
+        c[0] += (d >> 2) == 0 ? inc : 0ull;
+        c[1] += (d >> 2) == 1 ? inc : 0ull;
+        c[2] += (d >> 2) == 2 ? inc : 0ull;
+        c[3] += (d >> 2) == 3 ? inc : 0ull;
+      }
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) c[q] += __shfl_xor(c[q], off);
+      }
+      if (lane == 0) {
+#pragma unroll
+        for (int d = 0; d < 16; ++d) s_cnt[wave][d] = (uint32_t)((c[d >> 2] >> (16 * (d & 3))) & 0xFFFFu);
+      }
+      __syncthreads();
+      if (tid < 16) {
+        uint32_t t = 0;
+        for (int w = 0; w < kWaves; ++w) t += s_cnt[w][tid];
+        s_tot[tid] = t;
+      }
+      __syncthreads();
+      // The digit of the k-th largest key among those matching the prefix.
+      int cum = 0, dsel = 0;
+      bool found = false;
+#pragma unroll
+      for (int d = 15; d >= 0; --d) {
+        const int t = (int)s_tot[d];
+        if (!found) {
+          if (cum + t >= krem) { dsel = d; found = true; } else { cum += t; }
+        }
+      }
+      krem -= cum;
+      prefix |= (uint64_t)dsel << shift;
+      pmask |= 15ull << shift;
+      __syncthreads();
+    }
+  } else {
+    krem = 0;          // keep every real entry
+  }
+
+  // Kept: real keys above T, and the first krem keys equal to T in index order.
+  uint32_t gt = 0, eq = 0;
+#pragma unroll
+  for (int j = 0; j < KPT; ++j) {
+    if (!((valid >> j) & 1u)) continue;
+    if (nvalid <= k || key[j] > prefix) gt |= 1u << j;
+    else if (key[j] == prefix) eq |= 1u << j;
+  }
+  int eq_total;
+  const int eq_before = block_exclusive_scan<THREADS>(__popc(eq), s_tmp, &eq_total);
+  int take = krem - eq_before;
+  take = take < 0 ? 0 : take;
+  uint32_t keep = gt;
+#pragma unroll
+  for (int j = 0; j < KPT; ++j) {
+    if (((eq >> j) & 1u) && take > 0) { keep |= 1u << j; --take; }
+  }
+  int kept;
+  int pos = block_exclusive_scan<THREADS>(__popc(keep), s_tmp, &kept);
+
+  if (final_idx != nullptr) {
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) {
+      if (!((keep >> j) & 1u)) continue;
+      const int64_t g = first + j;
+      final_idx[pos++] = in_idx ? in_idx[g] : (int32_t)g;
     }
     return;
   }
-  // Final: the first k entries are real candidates (k <= candidates, checked
-  // on the host). Sort their indices ascending in place (the same thread reads
-  // and writes each slot, so s_idx can hold the keys).
-  const int kp = pow2_at_least(k);
-  for (int p = threadIdx.x; p < kp; p += kSelThreads)
-    if (p >= k) s_idx[p] = INT_MAX;
-  bitonic_sort_int_asc(s_idx, kp);
-  for (int p = threadIdx.x; p < k; p += kSelThreads) final_idx[p] = s_idx[p];
+  const int64_t ob = (int64_t)blockIdx.x * k;
+#pragma unroll
+  for (int j = 0; j < KPT; ++j) {
+    if (!((keep >> j) & 1u)) continue;
+    const int64_t g = first + j;
+    out_var[ob + pos] = __longlong_as_double((long long)key[j]);
+    out_idx[ob + pos] = in_idx ? in_idx[g] : (int32_t)g;
+    ++pos;
+  }
+  for (int p = kept + tid; p < k; p += THREADS) {      // fewer than k real entries
+    out_var[ob + p] = -1.0;
+    out_idx[ob + p] = INT_MAX;
+  }
 }
 
-int64_t chunks_of(int64_t n) { return (n + kChunk - 1) / kChunk; }
+// A level keeps k of every chunk of level_chunk(k) >= 4 k entries; the final
+// workgroup takes up to 1024 entries (4 per thread), or 4096 when k > 256.
+int64_t level_chunk(int32_t k) { return k <= 256 ? 1024 : 4096; }
+int64_t final_cap(int32_t k) { return k <= 256 ? 1024 : 4096; }
+int64_t chunks_of(int64_t n, int32_t k) { return (n + level_chunk(k) - 1) / level_chunk(k); }
+
+adahop_status launch_select(bool final_level, const double* in_var, const int32_t* in_idx,
+                            int64_t count, int32_t k, double* out_var, int32_t* out_idx,
+                            int32_t* final_idx, hipStream_t stream) {
+  const bool big = k > 256;
+  const unsigned nb = final_level ? 1u : (unsigned)chunks_of(count, k);
+  if (big)
+    foid_select_kernel<kSelThreads, 16><<<nb, kSelThreads, 0, stream>>>(in_var, in_idx, count, k,
+                                                                        out_var, out_idx, final_idx);
+  else
+    foid_select_kernel<kSelThreads, 4><<<nb, kSelThreads, 0, stream>>>(in_var, in_idx, count, k,
+                                                                       out_var, out_idx, final_idx);
+  return check_launch("foid_select");
+}
 
 }  // namespace
 
 size_t foid_workspace_bytes(int64_t ncand, int32_t k) {
   const size_t var_bytes = align_up(sizeof(double) * (size_t)ncand, kAlign);
-  if (ncand <= kChunk) return var_bytes;
-  const size_t entries = (size_t)chunks_of(ncand) * (size_t)k;
+  if (ncand <= final_cap(k)) return var_bytes;
+  const size_t entries = (size_t)chunks_of(ncand, k) * (size_t)k;
   return var_bytes +
          2 * (align_up(entries * sizeof(double), kAlign) + align_up(entries * sizeof(int32_t), kAlign));
 }
@@ -206,12 +290,9 @@ adahop_status foid_launch(const uint16_t* t, int64_t rows, int64_t cols, int64_t
                                                                               var);
   adahop_status st = check_launch("foid_var");
   if (st != ADAHOP_OK) return st;
-  const dim3 block(kSelThreads);
-  if (ncand <= kChunk) {
-    foid_select_kernel<<<1, block, 0, stream>>>(var, nullptr, ncand, k, nullptr, nullptr, idx_out);
-    return check_launch("foid_select");
-  }
-  const size_t entries = (size_t)chunks_of(ncand) * (size_t)k;
+  if (ncand <= final_cap(k))
+    return launch_select(true, var, nullptr, ncand, k, nullptr, nullptr, idx_out, stream);
+  const size_t entries = (size_t)chunks_of(ncand, k) * (size_t)k;
   double* var_buf[2];
   int32_t* idx_buf[2];
   for (int b = 0; b < 2; ++b) {
@@ -220,26 +301,21 @@ adahop_status foid_launch(const uint16_t* t, int64_t rows, int64_t cols, int64_t
     idx_buf[b] = reinterpret_cast<int32_t*>(p);
     p += align_up(entries * sizeof(int32_t), kAlign);
   }
-  // Level 0 reads the scores with implicit indices; later levels read survivors.
-  int64_t nb = chunks_of(ncand);
-  foid_select_kernel<<<dim3((unsigned)nb), block, 0, stream>>>(var, nullptr, ncand, k, var_buf[0],
-                                                               idx_buf[0], nullptr);
-  st = check_launch("foid_select");
-  if (st != ADAHOP_OK) return st;
+  // Each level divides the count by at least 4, until one workgroup can take
+  // the rest.
+  const double* in_var = var;
+  const int32_t* in_idx = nullptr;
+  int64_t count = ncand;
   int cur = 0;
-  int64_t count = nb * k;
-  while (count > kChunk) {
-    nb = chunks_of(count);
-    foid_select_kernel<<<dim3((unsigned)nb), block, 0, stream>>>(
-        var_buf[cur], idx_buf[cur], count, k, var_buf[cur ^ 1], idx_buf[cur ^ 1], nullptr);
-    st = check_launch("foid_select");
+  while (count > final_cap(k)) {
+    st = launch_select(false, in_var, in_idx, count, k, var_buf[cur], idx_buf[cur], nullptr, stream);
     if (st != ADAHOP_OK) return st;
+    count = chunks_of(count, k) * k;
+    in_var = var_buf[cur];
+    in_idx = idx_buf[cur];
     cur ^= 1;
-    count = nb * k;
   }
-  foid_select_kernel<<<1, block, 0, stream>>>(var_buf[cur], idx_buf[cur], count, k, nullptr,
-                                              nullptr, idx_out);
-  return check_launch("foid_select");
+  return launch_select(true, in_var, in_idx, count, k, nullptr, nullptr, idx_out, stream);
 }
 
 }  // namespace adahop

@@ -475,6 +475,7 @@ constexpr int kPastEnd = 0x7FFFFFF0;
 
 typedef __attribute__((address_space(3))) void lds_void;
 
+template <bool Chunked>
 __global__ void __launch_bounds__(kGemmThreads, 1) gemm_mx_ring_kernel(GemmArgs g) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -490,10 +491,20 @@ __global__ void __launch_bounds__(kGemmThreads, 1) gemm_mx_ring_kernel(GemmArgs 
   const int rows_b = (int)(g.n - n0 < BN ? g.n - n0 : BN);
 
   // Descriptors over this tile's rows: rows past the matrix edge read 0.
-  const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint8_t*>(g.a_codes + m0 * Kb), 0, (int)(rows_a * Kb), kBufferFlags);
-  const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint8_t*>(g.b_codes + n0 * Kb), 0, (int)(rows_b * Kb), kBufferFlags);
+  // Chunked codes ([K/128][rows][64 B]): stage kt of this tile's rows is one
+  // contiguous run; descriptors start at the tile's first row of chunk 0 and
+  // the stage offset goes in soffset. Row-major codes ([rows][K/2]):
+  // descriptors over this tile's rows, the stage offset is the K byte offset.
+  const __amdgpu_buffer_rsrc_t ra = Chunked
+      ? __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(g.a_codes + m0 * RBK), 0,
+                                          (int)((nk * g.m - m0) * RBK), kBufferFlags)
+      : __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(g.a_codes + m0 * Kb), 0,
+                                          (int)(rows_a * Kb), kBufferFlags);
+  const __amdgpu_buffer_rsrc_t rb = Chunked
+      ? __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(g.b_codes + n0 * RBK), 0,
+                                          (int)((nk * g.n - n0) * RBK), kBufferFlags)
+      : __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(g.b_codes + n0 * Kb), 0,
+                                          (int)(rows_b * Kb), kBufferFlags);
   // Scales come from the stage-major copies: stage kt of rows r0..r0+255 is
   // one contiguous kilobyte; a row past the matrix edge gets an offset past
   // the end of the buffer and reads 0.
@@ -507,9 +518,21 @@ __global__ void __launch_bounds__(kGemmThreads, 1) gemm_mx_ring_kernel(GemmArgs 
   // logical chunk (lane % 4) ^ swz(row). The stage offset goes in soffset.
   const int row0 = 64 * wave + (lane >> 2);
   const int chunk = (lane & 3) ^ ring_swz(row0);    // swz is the same for rows row0 + 16 j
-  int voff[4];
+  // A row past the matrix edge reads 0: past its descriptor (row-major) or
+  // at kPastEnd (chunked, where the next rows belong to the next chunk).
+  int voffa[4], voffb[4];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) voff[j] = (row0 + 16 * j) * (int)Kb + chunk * 16;
+  for (int j = 0; j < 4; ++j) {
+    const int r = row0 + 16 * j;
+    if (Chunked) {
+      voffa[j] = r < rows_a ? r * RBK + chunk * 16 : kPastEnd;
+      voffb[j] = r < rows_b ? r * RBK + chunk * 16 : kPastEnd;
+    } else {
+      voffa[j] = voffb[j] = r * (int)Kb + chunk * 16;
+    }
+  }
+  const int stage_a = Chunked ? (int)g.m * RBK : RBK;    // soffset per stage
+  const int stage_b = Chunked ? (int)g.n * RBK : RBK;
   const int srow = 64 * wave + lane;                   // scales: row 64 wave + lane
   const int soff_a = srow < rows_a ? (int)((m0 + srow) * 4) : kPastEnd;
   const int soff_b = srow < rows_b ? (int)((n0 + srow) * 4) : kPastEnd;
@@ -517,13 +540,12 @@ __global__ void __launch_bounds__(kGemmThreads, 1) gemm_mx_ring_kernel(GemmArgs 
 
   auto issue = [&](auto S, int kt) {
     constexpr int slot = decltype(S)::value;
-    const int kb0 = kt * RBK;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          ra, (lds_void*)&ring_slot<slot>().a[1024 * (4 * wave + j)], 16, voff[j], kb0, 0, 0);
+          ra, (lds_void*)&ring_slot<slot>().a[1024 * (4 * wave + j)], 16, voffa[j], kt * stage_a, 0, 0);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rb, (lds_void*)&ring_slot<slot>().b[1024 * (4 * wave + j)], 16, voff[j], kb0, 0, 0);
+          rb, (lds_void*)&ring_slot<slot>().b[1024 * (4 * wave + j)], 16, voffb[j], kt * stage_b, 0, 0);
     }
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rsa, (lds_void*)&ring_slot<slot>().sa[256 * wave], 4,
                                              soff_a, kt * sstage_a, 0, 0);
@@ -606,14 +628,20 @@ __global__ void __launch_bounds__(kGemmThreads, 1) gemm_mx_ring_kernel(GemmArgs 
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
     issue(std::integral_constant<int, slot>{}, kt + 4 < nk ? kt + 4 : nk - 1);
-    __builtin_amdgcn_sched_barrier(0);
     read_frags(std::integral_constant<int, (slot + 1) % kRingSlots>{}, nxt);
     mma(cur, std::integral_constant<int, 1>{});
-    // Spread the 24 LDS reads over the first 12 MFMAs (2 after each), so they
-    // complete long before the next stage's first MFMA needs them.
-    static_for<12>([&](auto) {
+    // One global->LDS load and two LDS reads after each of the first 10
+    // MFMAs, then the rest of the LDS reads: a load that waits for the memory
+    // pipeline holds back few MFMAs, and the fragments land long before the
+    // next stage's first MFMA needs them.
+    static_for<10>([&](auto) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // VMEM read
       __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);   // DS read
+    });
+    static_for<2>([&](auto) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
     });
     __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
     __builtin_amdgcn_sched_barrier(0);
@@ -913,6 +941,11 @@ bool ring_shape_ok(int64_t m, int64_t n, int64_t K) {
 
 }  // namespace
 
+bool gemm_mx_kchunk_ok(int64_t m, int64_t n, int64_t K) {
+  const int64_t big = m > n ? m : n;
+  return ring_shape_ok(m, n, K) && big * (K / 2) < 0x7FFF0000;   // stage offsets fit 31 bits
+}
+
 size_t gemm_mx_scratch_bytes(int64_t m, int64_t n, int64_t K) {
   if (m < 1 || n < 1 || !ring_shape_ok(m, n, K)) return 0;
   return align_up((size_t)m * (size_t)(K / 32), kAlign) + align_up((size_t)n * (size_t)(K / 32), kAlign);
@@ -955,8 +988,8 @@ adahop_status gemm_mx_stage_scales(const uint8_t* a_codes, const uint8_t* a_scal
 
 adahop_status gemm_mx_launch(const uint8_t* a_codes, const uint8_t* a_scales,
                              const uint8_t* b_codes, const uint8_t* b_scales, int64_t m,
-                             int64_t n, int64_t K, const OeEpilogue& oe, void* C, int64_t ldc,
-                             int out_f32, void* scratch, size_t scratch_bytes,
+                             int64_t n, int64_t K, int layout, const OeEpilogue& oe, void* C,
+                             int64_t ldc, int out_f32, void* scratch, size_t scratch_bytes,
                              hipStream_t stream) {
   const int64_t tiles_m = (m + BM - 1) / BM, tiles_n = (n + BN - 1) / BN;
   if (tiles_m * tiles_n > 0x7FFFFFFF) return fail(ADAHOP_ERR_UNSUPPORTED, "gemm: too large");
@@ -971,13 +1004,19 @@ adahop_status gemm_mx_launch(const uint8_t* a_codes, const uint8_t* a_scales,
   g.ib_ptr = oe.b.ptr; g.ib_ld = oe.b.ld; g.ib_inner = oe.b.inner_contiguous;
   const dim3 grid((unsigned)(tiles_m * tiles_n)), block(kGemmThreads);
   const uintptr_t sc_bits = reinterpret_cast<uintptr_t>(a_scales) | reinterpret_cast<uintptr_t>(b_scales);
-  if (ring_applies(a_codes, a_scales, b_codes, b_scales, m, n, K)) {
+  if (layout == ADAHOP_LAYOUT_KCHUNK) {
+    if (!gemm_mx_kchunk_ok(m, n, K) || !ring_applies(a_codes, a_scales, b_codes, b_scales, m, n, K))
+      return fail(ADAHOP_ERR_UNSUPPORTED, "gemm_mx: K-chunked operands need K % 512 == 0 and aligned buffers");
+    g.a_sst = reinterpret_cast<const uint32_t*>(a_scales);
+    g.b_sst = reinterpret_cast<const uint32_t*>(b_scales);
+    gemm_mx_ring_kernel<true><<<grid, block, 0, stream>>>(g);
+  } else if (ring_applies(a_codes, a_scales, b_codes, b_scales, m, n, K)) {
     // The scales were reordered into `scratch` by gemm_mx_stage_scales.
     const adahop_status st = check_scratch(scratch, scratch_bytes, gemm_mx_scratch_bytes(m, n, K));
     if (st != ADAHOP_OK) return st;
     g.a_sst = static_cast<const uint32_t*>(scratch);
     g.b_sst = staged_b(scratch, m, K);
-    gemm_mx_ring_kernel<<<grid, block, 0, stream>>>(g);
+    gemm_mx_ring_kernel<false><<<grid, block, 0, stream>>>(g);
   } else if (K % 256 == 0 && (sc_bits & 7u) == 0)
     gemm_mx_kernel<true><<<grid, block, 0, stream>>>(g);
   else

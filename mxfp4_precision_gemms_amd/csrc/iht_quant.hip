@@ -72,7 +72,8 @@ __global__ void __launch_bounds__(kRowThreads)
 iht_quant_rowwise_kernel(const uint16_t* __restrict__ src, int64_t rows, int64_t K, int64_t ld,
                          int chunks_per_row, int hadamard, const int32_t* __restrict__ zidx,
                          int nz, int zaxis, uint8_t* __restrict__ codes,
-                         uint8_t* __restrict__ scales, uint16_t* __restrict__ gathered) {
+                         uint8_t* __restrict__ scales, uint16_t* __restrict__ gathered,
+                         int kchunk) {
   // Whether this row is an extracted line (zero_axis ROWS: its position in
   // the index list, else -1); which columns of this chunk are (zero_axis COLS).
   __shared__ int32_t s_rowpos;
@@ -178,8 +179,15 @@ iht_quant_rowwise_kernel(const uint16_t* __restrict__ src, int64_t rows, int64_t
   const float scale = e8m0_as_f32(sx);
   const uint32_t lo = pack8_e2m1(y, scale), hi = pack8_e2m1(y + 8, scale);
   if (active) {
-    *reinterpret_cast<uint2*>(codes + r * (K / 2) + col0 / 2) = make_uint2(lo, hi);
-    if (!upper) scales[r * (K / 32) + col0 / 32] = (uint8_t)(sx + 127);
+    if (kchunk) {
+      // [K/128][rows][64]: this lane's 8 bytes and its block's scale byte
+      const int64_t c = col0 / 128, w = col0 % 128;
+      *reinterpret_cast<uint2*>(codes + (c * rows + r) * 64 + w / 2) = make_uint2(lo, hi);
+      if (!upper) scales[(c * rows + r) * 4 + w / 32] = (uint8_t)(sx + 127);
+    } else {
+      *reinterpret_cast<uint2*>(codes + r * (K / 2) + col0 / 2) = make_uint2(lo, hi);
+      if (!upper) scales[r * (K / 32) + col0 / 32] = (uint8_t)(sx + 127);
+    }
   }
 }
 
@@ -203,7 +211,7 @@ __global__ void __launch_bounds__(kColThreads)
 iht_quant_colwise_kernel(const uint16_t* __restrict__ src, int64_t K, int64_t outer, int64_t ld,
                          int hadamard, const int32_t* __restrict__ zidx, int nz, int zaxis,
                          uint8_t* __restrict__ codes, uint8_t* __restrict__ scales,
-                         uint16_t* __restrict__ gathered) {
+                         uint16_t* __restrict__ gathered, int kchunk) {
   __shared__ __attribute__((aligned(16))) uint8_t s_codes[kColOut * kColPitch];
   __shared__ __attribute__((aligned(16))) uint8_t s_scales[kColOut * kColBlocks];
   // Extracted lines inside this tile: rows (zero_axis ROWS) as one bit per
@@ -349,6 +357,25 @@ iht_quant_colwise_kernel(const uint16_t* __restrict__ src, int64_t K, int64_t ou
   // Write-out: output row r of this tile gets nb consecutive blocks.
   const int nrow = (int)(outer - cbase < kColOut ? outer - cbase : kColOut);
   const int nb = (int)(nblocks - bbase < kColBlocks ? nblocks - bbase : kColBlocks);
+  if (kchunk) {
+    // [K/128][outer][64] and [K/128][outer][4]: chunk q of this tile (4
+    // blocks) is 64 consecutive rows x 64 bytes, one contiguous run
+    // (K % 128 == 0, so nb is a multiple of 4).
+    const int64_t c0k = bbase / 4;
+    for (int i = tid; i < kColOut * kColBlocks; i += kColThreads) {
+      const int q = i / (kColOut * 4), r = (i / 4) % kColOut, piece = i % 4;
+      if (r < nrow && 4 * q < nb)
+        *reinterpret_cast<uint4*>(codes + ((c0k + q) * outer + cbase + r) * 64 + piece * 16) =
+            *reinterpret_cast<const uint4*>(&s_codes[r * kColPitch + (4 * q + piece) * 16]);
+    }
+    {
+      const int q = tid / kColOut, r = tid % kColOut;
+      if (r < nrow && 4 * q < nb)
+        *reinterpret_cast<uint32_t*>(scales + ((c0k + q) * outer + cbase + r) * 4) =
+            *reinterpret_cast<const uint32_t*>(&s_scales[r * kColBlocks + 4 * q]);
+    }
+    return;
+  }
   for (int i = tid; i < kColOut * kColBlocks; i += kColThreads) {
     const int r = i / kColBlocks, ch = i % kColBlocks;
     if (r < nrow && ch < nb)
@@ -374,7 +401,11 @@ iht_quant_colwise_kernel(const uint16_t* __restrict__ src, int64_t K, int64_t ou
 adahop_status iht_quant_launch(const uint16_t* src, int64_t rows, int64_t cols, int64_t ld,
                                int contract, int32_t hadamard_block, const int32_t* zero_idx,
                                int32_t nzero, int zero_axis, uint8_t* codes, uint8_t* scales,
-                               uint16_t* gathered, hipStream_t stream) {
+                               uint16_t* gathered, int layout, hipStream_t stream) {
+  const int kchunk = layout == ADAHOP_LAYOUT_KCHUNK ? 1 : 0;
+  const int64_t Kc = contract == ADAHOP_AXIS_COLS ? cols : rows;
+  if (kchunk && (Kc % 128 != 0 || (reinterpret_cast<uintptr_t>(scales) & 3u) != 0))
+    return fail(ADAHOP_ERR_UNSUPPORTED, "iht_quant: K-chunked output needs K % 128 == 0");
   const int had = hadamard_block == 32 ? 1 : 0;
   if (contract == ADAHOP_AXIS_COLS) {
     const int64_t K = cols;
@@ -382,7 +413,8 @@ adahop_status iht_quant_launch(const uint16_t* src, int64_t rows, int64_t cols, 
     const int64_t grid = rows * cpr;
     if (grid > 0x7FFFFFFFLL) return fail(ADAHOP_ERR_UNSUPPORTED, "iht_quant: tensor too large");
     iht_quant_rowwise_kernel<<<dim3((unsigned)grid), dim3(kRowThreads), 0, stream>>>(
-        src, rows, K, ld, (int)cpr, had, zero_idx, nzero, zero_axis, codes, scales, gathered);
+        src, rows, K, ld, (int)cpr, had, zero_idx, nzero, zero_axis, codes, scales, gathered,
+        kchunk);
   } else {
     const int64_t K = rows, outer = cols;
     const int64_t gx = (outer + kColOut - 1) / kColOut;
@@ -393,10 +425,10 @@ adahop_status iht_quant_launch(const uint16_t* src, int64_t rows, int64_t cols, 
     const dim3 grid((unsigned)gx, (unsigned)gy), block(kColThreads);
     if (vec)
       iht_quant_colwise_kernel<true><<<grid, block, 0, stream>>>(
-          src, K, outer, ld, had, zero_idx, nzero, zero_axis, codes, scales, gathered);
+          src, K, outer, ld, had, zero_idx, nzero, zero_axis, codes, scales, gathered, kchunk);
     else
       iht_quant_colwise_kernel<false><<<grid, block, 0, stream>>>(
-          src, K, outer, ld, had, zero_idx, nzero, zero_axis, codes, scales, gathered);
+          src, K, outer, ld, had, zero_idx, nzero, zero_axis, codes, scales, gathered, kchunk);
   }
   return check_launch("iht_quant");
 }

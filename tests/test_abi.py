@@ -123,3 +123,14 @@ def test_gemm_mx_workspace_size():
     desc = A.OeDesc(A.ROUTE["OE_RIGHT"], 16, 0, A.Bf16View(0, 0, 1, 0), A.Bf16View(0, 0, 1, 0))
     with_oe = lib.adahop_gemm_mx_workspace_size(300, 520, 1024, ctypes.byref(desc))
     assert with_oe > 9728 + 16640 and (with_oe - 9728 - 16640) % 256 == 0
+
+
+def test_plan_layout():
+    # Contractions the main GEMM kernel streams are packed K-chunked.
+    assert A.adahop_gemm_plan("WGRAD", 32768, 14336, 4096, "R", "C").layout == A.LAYOUT_KCHUNK
+    assert A.adahop_gemm_plan("FWD", 64, 256, 64, "C", "N").layout == A.LAYOUT_ROWS
+    # K-chunked plans need no scratch for reordering scales: the workspace is
+    # exactly the packed operands, lines, indices and FOID/outlier scratch.
+    p = A.adahop_gemm_plan("FWD", 512, 512, 512, "C", "N")
+    assert p.layout == A.LAYOUT_KCHUNK
+    assert p.ws_bytes == 512 * 256 + 512 * 16 + 512 * 256 + 512 * 16

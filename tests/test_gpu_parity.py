@@ -240,6 +240,8 @@ def operands(op, T, Din, Dout, pl, pr, seed):
 def run_and_compare(op, lhs, rhs, T, Din, Dout, pl, pr, route, k, rows=None, cols=None):
     say("adahop_gemm", op, (T, Din, Dout), pl + pr, route, k)
     plan = A.adahop_gemm_plan(op, T, Din, Dout, pl, pr, route, k)
+    if plan.route != A.ROUTE["BF16"]:
+        assert plan.layout == (A.LAYOUT_KCHUNK if plan.K % 512 == 0 else A.LAYOUT_ROWS)
     ws = torch.zeros(max(plan.ws_bytes, 1), dtype=torch.uint8, device=DEV)
     L, R = dev_bf16(lhs), dev_bf16(rhs)
     c32 = A.adahop_gemm(op, L, R, pl, pr, route, k, out_dtype=torch.float32, ws=ws)
@@ -280,6 +282,12 @@ FULL_CASES = [
     ("WGRAD", 512, 384, 256, "C", "N", None, 8),        # OE_LEFT (GY cols)
     ("WGRAD", 416, 160, 96, "R", "N", "OE_INNER", 8),
     ("WGRAD", 128, 96, 64, "C", "C", None, 8),          # BF16
+    # K % 512 == 0: operands packed K-chunked for the main GEMM kernel
+    ("FWD", 300, 1024, 200, "R", "N", None, 8),         # OE_LEFT, both rows quantized in rows
+    ("DGRAD", 520, 136, 512, "N", "C", None, 8),        # OE_RIGHT, W quantized down columns
+    ("WGRAD", 1024, 200, 72, "R", "C", None, 8),        # OE_RIGHT, both down columns
+    ("WGRAD", 512, 96, 160, "C", "N", None, 8),         # OE_LEFT (GY columns)
+    ("DGRAD", 300, 264, 1536, "N", "N", None, 64),      # IHT, ragged tiles
 ]
 
 
