@@ -63,30 +63,37 @@ __device__ __forceinline__ float e8m0_as_f32(int s) {
 }
 
 constexpr int kRowThreads = 256;
-constexpr int kRowChunk = kRowThreads * 16;  // elements of one row per workgroup
+constexpr int kRowRows = kRowThreads / 64;   // rows per workgroup, one wave each
+constexpr int kRowChunk = 64 * 16;           // columns per workgroup
 
-// contract COLS: src [rows][K], K contiguous. Grid: rows * ceil(K / kRowChunk).
-// A lane owns 16 consecutive elements (two 16-byte loads), two lanes form a
-// 32-block: butterfly strides 1..8 in registers, stride 16 by one shuffle.
+// contract COLS: src [rows][K], K contiguous. A workgroup takes 4 rows x 1024
+// columns, one wave per row. A lane owns 16 consecutive elements (two 16-byte
+// loads), two lanes form a 32-block: butterfly strides 1..8 in registers,
+// stride 16 by one shuffle. Row-major output goes out from registers (a
+// wave's 512 code bytes are contiguous); K-chunked output is staged in LDS
+// and written as runs of 4 rows x 64 bytes, whole lines.
 __global__ void __launch_bounds__(kRowThreads)
 iht_quant_rowwise_kernel(const uint16_t* __restrict__ src, int64_t rows, int64_t K, int64_t ld,
                          int chunks_per_row, int hadamard, const int32_t* __restrict__ zidx,
                          int nz, int zaxis, uint8_t* __restrict__ codes,
                          uint8_t* __restrict__ scales, uint16_t* __restrict__ gathered,
                          int kchunk) {
-  // Whether this row is an extracted line (zero_axis ROWS: its position in
-  // the index list, else -1); which columns of this chunk are (zero_axis COLS).
-  __shared__ int32_t s_rowpos;
+  // Extracted lines inside this tile: each row's position in the index list
+  // (zero_axis ROWS, -1 if none), or a mask of the columns (zero_axis COLS).
+  __shared__ int32_t s_rowpos[kRowRows];
   __shared__ uint32_t s_cmask[kRowChunk / 32];
-  const int tid = threadIdx.x;
-  const int64_t r = blockIdx.x / chunks_per_row;
+  __shared__ __attribute__((aligned(16))) uint8_t s_codes[kRowRows][kRowChunk / 2];
+  __shared__ __attribute__((aligned(16))) uint8_t s_scales[kRowRows][kRowChunk / 32];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t r0 = (int64_t)(blockIdx.x / chunks_per_row) * kRowRows;
+  const int64_t r = r0 + wave;
   const int64_t cbase = (int64_t)(blockIdx.x % chunks_per_row) * kRowChunk;
-  const int64_t col0 = cbase + tid * 16;
-  const bool active = col0 < K;   // K % 32 == 0: both lanes of a block agree
-  const bool upper = (tid & 1) != 0;
+  const int64_t col0 = cbase + lane * 16;
+  const bool active = r < rows && col0 < K;   // K % 32 == 0: both lanes of a block agree
+  const bool upper = (lane & 1) != 0;
 
-  // This thread's share of the index list, loaded before the row so that
-  // waiting for it does not wait for the row.
+  // This thread's share of the index list, loaded before the rows so that
+  // waiting for it does not wait for the rows.
   int zv[kMaxK / kRowThreads];
 #pragma unroll
   for (int q = 0; q < kMaxK / kRowThreads; ++q) {
@@ -99,7 +106,7 @@ iht_quant_rowwise_kernel(const uint16_t* __restrict__ src, int64_t rows, int64_t
     raw1 = *reinterpret_cast<const uint4*>(src + r * ld + col0 + 8);
   }
 
-  if (tid == 0) s_rowpos = -1;
+  if (tid < kRowRows) s_rowpos[tid] = -1;
   if (tid < kRowChunk / 32) s_cmask[tid] = 0;
   __syncthreads();
   if (nz > 0) {
@@ -108,13 +115,16 @@ iht_quant_rowwise_kernel(const uint16_t* __restrict__ src, int64_t rows, int64_t
       if (zv[q] < 0) continue;
       const int i = tid + q * kRowThreads;
       if (zaxis == ADAHOP_AXIS_ROWS) {
-        if (zv[q] == r) s_rowpos = i;
+        if (zv[q] >= r0 && zv[q] < r0 + kRowRows && zv[q] < rows) s_rowpos[zv[q] - r0] = i;
       } else {
         const int64_t d = (int64_t)zv[q] - cbase;
         if (d >= 0 && d < kRowChunk && zv[q] < K) {
           atomicOr(&s_cmask[d / 32], 1u << (d % 32));
-          // An extracted column: gathered [nz][rows], element (i, r).
-          if (gathered) gathered[(int64_t)i * rows + r] = src[r * ld + zv[q]];
+          // An extracted column: gathered [nz][rows], elements (i, r0 .. r0 + 3).
+          if (gathered) {
+            for (int j = 0; j < kRowRows; ++j)
+              if (r0 + j < rows) gathered[(int64_t)i * rows + r0 + j] = src[(r0 + j) * ld + zv[q]];
+          }
         }
       }
     }
@@ -130,7 +140,7 @@ iht_quant_rowwise_kernel(const uint16_t* __restrict__ src, int64_t rows, int64_t
   }
   if (nz > 0 && active) {
     if (zaxis == ADAHOP_AXIS_ROWS) {
-      const int p = s_rowpos;
+      const int p = s_rowpos[wave];
       if (p >= 0) {
         if (gathered) {
           *reinterpret_cast<uint4*>(gathered + (int64_t)p * K + col0) = raw0;
@@ -140,8 +150,8 @@ iht_quant_rowwise_kernel(const uint16_t* __restrict__ src, int64_t rows, int64_t
         for (int i = 0; i < 16; ++i) y[i] = 0.0f;
       }
     } else {
-      // col0 - cbase is a multiple of 16: this lane's 16 columns sit in one word.
-      const int d = (int)(col0 - cbase);
+      // lane * 16 is a multiple of 16: this lane's 16 columns sit in one word.
+      const int d = lane * 16;
       const uint32_t zmask = (s_cmask[d / 32] >> (d % 32)) & 0xFFFFu;
 #pragma unroll
       for (int i = 0; i < 16; ++i) y[i] = ((zmask >> i) & 1u) ? 0.0f : y[i];
@@ -178,16 +188,33 @@ iht_quant_rowwise_kernel(const uint16_t* __restrict__ src, int64_t rows, int64_t
   const int sx = block_exponent(amax);
   const float scale = e8m0_as_f32(sx);
   const uint32_t lo = pack8_e2m1(y, scale), hi = pack8_e2m1(y + 8, scale);
-  if (active) {
-    if (kchunk) {
-      // [K/128][rows][64]: this lane's 8 bytes and its block's scale byte
-      const int64_t c = col0 / 128, w = col0 % 128;
-      *reinterpret_cast<uint2*>(codes + (c * rows + r) * 64 + w / 2) = make_uint2(lo, hi);
-      if (!upper) scales[(c * rows + r) * 4 + w / 32] = (uint8_t)(sx + 127);
-    } else {
+  if (!kchunk) {
+    if (active) {
       *reinterpret_cast<uint2*>(codes + r * (K / 2) + col0 / 2) = make_uint2(lo, hi);
       if (!upper) scales[r * (K / 32) + col0 / 32] = (uint8_t)(sx + 127);
     }
+    return;
+  }
+  // [K/128][rows][64] and [K/128][rows][4]: chunk q of this tile is rows
+  // r0 .. r0 + 3 x 64 bytes, one contiguous run (K % 128 == 0).
+  *reinterpret_cast<uint2*>(&s_codes[wave][lane * 8]) = make_uint2(lo, hi);
+  if (!upper) s_scales[wave][lane / 2] = (uint8_t)(sx + 127);
+  __syncthreads();
+  const int nrow = (int)(rows - r0 < kRowRows ? rows - r0 : kRowRows);
+  const int nch = (int)((K - cbase) / 128 < kRowChunk / 128 ? (K - cbase) / 128 : kRowChunk / 128);
+  const int64_t c0 = cbase / 128;
+  if (tid < (kRowChunk / 128) * kRowRows * 4) {
+    const int q = tid / (kRowRows * 4), piece = tid % (kRowRows * 4);
+    const int row = piece / 4, part = piece % 4;
+    if (q < nch && row < nrow)
+      *reinterpret_cast<uint4*>(codes + ((c0 + q) * rows + r0) * 64 + piece * 16) =
+          *reinterpret_cast<const uint4*>(&s_codes[row][q * 64 + part * 16]);
+  }
+  if (tid < (kRowChunk / 128) * kRowRows) {
+    const int q = tid / kRowRows, row = tid % kRowRows;
+    if (q < nch && row < nrow)
+      *reinterpret_cast<uint32_t*>(scales + ((c0 + q) * rows + r0 + row) * 4) =
+          *reinterpret_cast<const uint32_t*>(&s_scales[row][q * 4]);
   }
 }
 
@@ -410,7 +437,7 @@ adahop_status iht_quant_launch(const uint16_t* src, int64_t rows, int64_t cols, 
   if (contract == ADAHOP_AXIS_COLS) {
     const int64_t K = cols;
     const int64_t cpr = (K + kRowChunk - 1) / kRowChunk;
-    const int64_t grid = rows * cpr;
+    const int64_t grid = (rows + kRowRows - 1) / kRowRows * cpr;
     if (grid > 0x7FFFFFFFLL) return fail(ADAHOP_ERR_UNSUPPORTED, "iht_quant: tensor too large");
     iht_quant_rowwise_kernel<<<dim3((unsigned)grid), dim3(kRowThreads), 0, stream>>>(
         src, rows, K, ld, (int)cpr, had, zero_idx, nzero, zero_axis, codes, scales, gathered,
