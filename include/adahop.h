@@ -95,7 +95,8 @@ typedef enum { ADAHOP_OUT_BF16 = 0, ADAHOP_OUT_F32 = 1 } adahop_out_dtype;
  *   KCHUNK: K cut into chunks of 128: codes [K/128][outer][64] and scales
  *           [K/128][outer][4], i.e. chunk c of row r holds K-elements
  *           128 c .. 128 c + 127 of that row, each chunk of all rows
- *           contiguous -- the order in which the GEMM streams them. */
+ *           contiguous -- the order in which the GEMM streams them. A
+ *           chunk's four scale bytes are its blocks' in the order 0, 2, 1, 3. */
 typedef enum { ADAHOP_LAYOUT_ROWS = 0, ADAHOP_LAYOUT_KCHUNK = 1 } adahop_layout;
 
 ADAHOP_API const char* adahop_status_string(int status);

@@ -306,7 +306,9 @@ def workspace_views(ws: torch.Tensor, plan: Plan) -> dict:
             return None, None
         if plan.layout == LAYOUT_KCHUNK:     # [K/128][outer][64], [K/128][outer][4]
             codes = codes.view(K // 128, outer, 64).permute(1, 0, 2).reshape(outer, K // 2)
-            scales = scales.view(K // 128, outer, 4).permute(1, 0, 2).reshape(outer, K // 32)
+            # a chunk's scale bytes are its blocks' in the order 0, 2, 1, 3
+            scales = scales.view(K // 128, outer, 4)[:, :, [0, 2, 1, 3]]
+            scales = scales.permute(1, 0, 2).reshape(outer, K // 32)
         return codes.view(outer, K // 2), scales.view(outer, K // 32)
 
     out = {"idx": region(plan.off_idx, k, torch.int32)}

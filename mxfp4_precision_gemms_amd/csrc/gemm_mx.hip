@@ -15,7 +15,7 @@
 //   held in the accumulation registers). Workgroup ids are remapped so that
 //   each XCD works through a contiguous range of tiles, 4 tile-rows high,
 //   whose operand rows its L2 shares.
-// Main kernel (gemm_mx_ring_kernel, K % 512 == 0): K advances 128 elements
+// Main kernel (gemm_mx_ring8_kernel, K % 512 == 0): K advances 128 elements
 //   per stage through a 4-slot LDS ring filled by direct global->LDS buffer
 //   loads four stages ahead; the scales come from a stage-major copy made
 //   just before (scale_stage_kernel). Other K: gemm_mx_kernel, 256-element
@@ -137,21 +137,26 @@ __device__ __forceinline__ void tile_of(int bid, int tiles_m, int tiles_n, int* 
 // rows (C rows), so lane l of block (I, J) holds C row 32 I + l%32 and, in
 // registers 4 G .. 4 G + 3, the four consecutive C columns 32 J + 8 G +
 // 4 (l/32) .. +3 -- one 8-byte bf16 (16-byte fp32) store each.
-__device__ __forceinline__ void gemm_finish(const GemmArgs& g, v16f (&acc)[FM][FN], int64_t m0,
+// Epilogue of a workgroup of THREADS threads whose wave w holds the TFM x TFN
+// 32x32 blocks at rows (w / WAVES_N) * TWM, columns (w % WAVES_N) * TWN of
+// the tile, in C^T register layout (lane l: row l % 32; register 4 G + e:
+// column 8 G + 4 (l / 32) + e of the block).
+template <int TFM, int TFN, int TWM, int TWN, int WAVES_N, int THREADS>
+__device__ __forceinline__ void gemm_finish(const GemmArgs& g, v16f (&acc)[TFM][TFN], int64_t m0,
                                             int64_t n0, int* s_pos) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / WAVES_N, wn = wave % WAVES_N;
   const int lrow = lane & 31, khalf = lane >> 5;
   // Inner extraction: C += a[:, 0:k] * b[:, 0:k]^T on bf16 matrix cores,
   // 16 extracted lines per MFMA (lane: row l%32, lines 8*(l/32) .. +7).
   if (g.oe_mode == ADAHOP_ROUTE_OE_INNER) {
     for (int p0 = 0; p0 < g.oe_k; p0 += 16) {
-      v8bf fa[FM], fb[FN];
+      v8bf fa[TFM], fb[TFN];
 #pragma unroll
-      for (int i = 0; i < FM; ++i) {
-        int64_t row = m0 + wm * WM + i * 32 + lrow;
+      for (int i = 0; i < TFM; ++i) {
+        int64_t row = m0 + wm * TWM + i * 32 + lrow;
         row = row < g.m ? row : g.m - 1;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
@@ -161,8 +166,8 @@ __device__ __forceinline__ void gemm_finish(const GemmArgs& g, v16f (&acc)[FM][F
         }
       }
 #pragma unroll
-      for (int j = 0; j < FN; ++j) {
-        int64_t col = n0 + wn * WN + j * 32 + lrow;
+      for (int j = 0; j < TFN; ++j) {
+        int64_t col = n0 + wn * TWN + j * 32 + lrow;
         col = col < g.n ? col : g.n - 1;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
@@ -171,8 +176,8 @@ __device__ __forceinline__ void gemm_finish(const GemmArgs& g, v16f (&acc)[FM][F
           fb[j][e] = __builtin_bit_cast(__bf16, h);
         }
       }
-      static_for<FM>([&](auto I) {
-        static_for<FN>([&](auto J) {
+      static_for<TFM>([&](auto I) {
+        static_for<TFN>([&](auto J) {
           acc[I][J] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[J], fa[I], acc[I][J], 0, 0, 0);
         });
       });
@@ -190,21 +195,21 @@ __device__ __forceinline__ void gemm_finish(const GemmArgs& g, v16f (&acc)[FM][F
     const int hi = lower_bound_i32(g.oe_idx, g.oe_k, lo_v + span);
     any_oe = hi > lo;
     if (any_oe) {
-      for (int q = tid; q < span; q += kGemmThreads) s_pos[q] = -1;
+      for (int q = tid; q < span; q += THREADS) s_pos[q] = -1;
       __syncthreads();
-      for (int p = lo + tid; p < hi; p += kGemmThreads) s_pos[g.oe_idx[p] - lo_v] = p;
+      for (int p = lo + tid; p < hi; p += THREADS) s_pos[g.oe_idx[p] - lo_v] = p;
       __syncthreads();
     }
   }
 
   const bool full = m0 + BM <= g.m && n0 + BN <= g.n && g.vec_ok;
-  static_for<FM>([&](auto I) {
-    const int lr = wm * WM + I * 32 + lrow;
+  static_for<TFM>([&](auto I) {
+    const int lr = wm * TWM + I * 32 + lrow;
     const int64_t row = m0 + lr;
     const int prow = (any_oe && oe_rows) ? s_pos[lr] : -1;
-    static_for<FN>([&](auto J) {
+    static_for<TFN>([&](auto J) {
       static_for<4>([&](auto G) {
-        const int lc = wn * WN + J * 32 + 8 * G + 4 * khalf;
+        const int lc = wn * TWN + J * 32 + 8 * G + 4 * khalf;
         const int64_t col = n0 + lc;
         float v[4] = {acc[I][J][4 * G + 0], acc[I][J][4 * G + 1], acc[I][J][4 * G + 2],
                       acc[I][J][4 * G + 3]};
@@ -417,26 +422,23 @@ __global__ void __launch_bounds__(kGemmThreads, 1) gemm_mx_kernel(GemmArgs g) {
     __syncthreads();
   }
 
-  gemm_finish(g, acc, m0, n0, s_pos);
+  gemm_finish<FM, FN, WM, WN, 2, kGemmThreads>(g, acc, m0, n0, s_pos);
 }
 
 
 // ---------------------------------------------------------------------------
-// Main kernel for K % 512 == 0: a 4-slot LDS ring filled by direct
-// global->LDS buffer loads (no staging registers), 4 stages ahead of the
-// matrix cores; each stage's fragments are read into registers during the
-// previous stage's second K-step, so the matrix cores never wait for LDS. Stage = 128 K-elements: A and B 256 rows x 64 bytes each plus
-// 4 scale bytes per row. Each wave copies a quarter of a stage with 10 loads
-// (4 + 4 of 1 KB codes, 1 + 1 of 256 B scales); before a stage is read, every
-// wave waits until only the two later stages' 20 loads are in flight, then
-// the workgroup barrier publishes the stage. LDS rows of 64 bytes keep
-// their four 16-byte chunks XOR-swizzled by ((r >> 1) ^ (r >> 2)) & 3, so a
-// wave's fragment reads of 8 (or 16) consecutive rows hit distinct banks.
+// Main kernel for K % 512 == 0 (gemm_mx_ring8_kernel): a 4-slot LDS ring
+// filled by direct global->LDS buffer loads (no staging registers), four
+// stages ahead of the matrix cores. Stage = 128 K-elements: A and B 256 rows x
+// 64 bytes each plus 4 scale bytes per row. Before a stage is read, every
+// wave waits until only its loads of the two later stages are in flight, then
+// the workgroup barrier publishes the stage. LDS rows of 64 bytes keep their
+// four 16-byte chunks XOR-swizzled by ((r >> 1) ^ (r >> 2)) & 3, so a wave's
+// fragment reads of 8 (or 16) consecutive rows hit distinct banks.
 // ---------------------------------------------------------------------------
 constexpr int RBK = 64;                       // bytes per row per stage
 constexpr int kRingSlots = 4;
 constexpr int kSlotA = BM * RBK, kSlotB = BN * RBK;   // 16 KB each
-constexpr int kLoadsPerStage = 10;            // per wave
 
 // One LDS object per slot: the compiler's alias analysis then sees that the
 // loads in flight into one slot do not touch the slot being read, and adds no
@@ -475,12 +477,28 @@ constexpr int kPastEnd = 0x7FFFFFF0;
 
 typedef __attribute__((address_space(3))) void lds_void;
 
+// ---------------------------------------------------------------------------
+// 8 waves, two per SIMD: wave w computes rows
+// 128 (w / 4) .. +127, columns 64 (w % 4) .. +63 of the 256 x 256 tile (4 x 2
+// MFMA blocks, 128 accumulators), so while one wave of a SIMD waits -- for a
+// load to be accepted by the memory pipeline or for an LDS read -- the other
+// keeps the matrix core busy. Each wave copies an eighth of a stage with 5
+// loads: 16 rows each of A and B twice (1 KB per load), and a quarter of the
+// A scales (waves 0-3) or of the B scales (waves 4-7). Fragments are double
+// buffered per K-step: the second K-step's are read during the first one's
+// MFMAs, the next stage's first K-step's during the second one's.
+// ---------------------------------------------------------------------------
+constexpr int kRing8Threads = 512;
+constexpr int R8_FM = 4, R8_FN = 2, R8_WM = 128, R8_WN = 64;
+constexpr int kLoads8PerStage = 5;            // per wave
+
 template <bool Chunked>
-__global__ void __launch_bounds__(kGemmThreads, 1) gemm_mx_ring_kernel(GemmArgs g) {
+__global__ void __launch_bounds__(kRing8Threads, 1) gemm_mx_ring8_kernel(GemmArgs g) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  // Wave-uniform (scalar): the scale loads below pick their descriptor by it.
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 2, wn = wave & 3;
   int tm, tn;
   tile_of(blockIdx.x, g.tiles_m, g.tiles_n, &tm, &tn);
   const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
@@ -490,11 +508,6 @@ __global__ void __launch_bounds__(kGemmThreads, 1) gemm_mx_ring_kernel(GemmArgs 
   const int rows_a = (int)(g.m - m0 < BM ? g.m - m0 : BM);
   const int rows_b = (int)(g.n - n0 < BN ? g.n - n0 : BN);
 
-  // Descriptors over this tile's rows: rows past the matrix edge read 0.
-  // Chunked codes ([K/128][rows][64 B]): stage kt of this tile's rows is one
-  // contiguous run; descriptors start at the tile's first row of chunk 0 and
-  // the stage offset goes in soffset. Row-major codes ([rows][K/2]):
-  // descriptors over this tile's rows, the stage offset is the K byte offset.
   const __amdgpu_buffer_rsrc_t ra = Chunked
       ? __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(g.a_codes + m0 * RBK), 0,
                                           (int)((nk * g.m - m0) * RBK), kBufferFlags)
@@ -505,24 +518,19 @@ __global__ void __launch_bounds__(kGemmThreads, 1) gemm_mx_ring_kernel(GemmArgs 
                                           (int)((nk * g.n - n0) * RBK), kBufferFlags)
       : __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(g.b_codes + n0 * Kb), 0,
                                           (int)(rows_b * Kb), kBufferFlags);
-  // Scales come from the stage-major copies: stage kt of rows r0..r0+255 is
-  // one contiguous kilobyte; a row past the matrix edge gets an offset past
-  // the end of the buffer and reads 0.
   const __amdgpu_buffer_rsrc_t rsa = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint32_t*>(g.a_sst), 0, (int)(g.m * Ks), kBufferFlags);
   const __amdgpu_buffer_rsrc_t rsb = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint32_t*>(g.b_sst), 0, (int)(g.n * Ks), kBufferFlags);
 
-  // Load j (0..3) of this wave fills LDS bytes [1024 (4 wave + j), +1024) of a
-  // slot: rows 16 (4 wave + j) + lane / 4, physical chunk lane % 4, which holds
-  // logical chunk (lane % 4) ^ swz(row). The stage offset goes in soffset.
-  const int row0 = 64 * wave + (lane >> 2);
+  // Load j (0, 1) of this wave fills LDS bytes [1024 (2 wave + j), +1024) of
+  // a slot: rows 16 (2 wave + j) + lane / 4, physical chunk lane % 4 holding
+  // logical chunk (lane % 4) ^ swz(row).
+  const int row0 = 32 * wave + (lane >> 2);
   const int chunk = (lane & 3) ^ ring_swz(row0);    // swz is the same for rows row0 + 16 j
-  // A row past the matrix edge reads 0: past its descriptor (row-major) or
-  // at kPastEnd (chunked, where the next rows belong to the next chunk).
-  int voffa[4], voffb[4];
+  int voffa[2], voffb[2];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
+  for (int j = 0; j < 2; ++j) {
     const int r = row0 + 16 * j;
     if (Chunked) {
       voffa[j] = r < rows_a ? r * RBK + chunk * 16 : kPastEnd;
@@ -531,119 +539,116 @@ __global__ void __launch_bounds__(kGemmThreads, 1) gemm_mx_ring_kernel(GemmArgs 
       voffa[j] = voffb[j] = r * (int)Kb + chunk * 16;
     }
   }
-  const int stage_a = Chunked ? (int)g.m * RBK : RBK;    // soffset per stage
+  const int stage_a = Chunked ? (int)g.m * RBK : RBK;
   const int stage_b = Chunked ? (int)g.n * RBK : RBK;
-  const int srow = 64 * wave + lane;                   // scales: row 64 wave + lane
-  const int soff_a = srow < rows_a ? (int)((m0 + srow) * 4) : kPastEnd;
-  const int soff_b = srow < rows_b ? (int)((n0 + srow) * 4) : kPastEnd;
-  const int sstage_a = (int)(g.m * 4), sstage_b = (int)(g.n * 4);
+  // Scales: waves 0-3 copy A rows 64 (w % 4) + lane, waves 4-7 B rows.
+  const bool sc_a = wave < 4;
+  const int srow = 64 * (wave & 3) + lane;
+  const int soff = sc_a ? (srow < rows_a ? (int)((m0 + srow) * 4) : kPastEnd)
+                        : (srow < rows_b ? (int)((n0 + srow) * 4) : kPastEnd);
+  const int sstage = sc_a ? (int)(g.m * 4) : (int)(g.n * 4);
 
   auto issue = [&](auto S, int kt) {
     constexpr int slot = decltype(S)::value;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < 2; ++j) {
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          ra, (lds_void*)&ring_slot<slot>().a[1024 * (4 * wave + j)], 16, voffa[j], kt * stage_a, 0, 0);
+          ra, (lds_void*)&ring_slot<slot>().a[1024 * (2 * wave + j)], 16, voffa[j], kt * stage_a, 0, 0);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rb, (lds_void*)&ring_slot<slot>().b[1024 * (4 * wave + j)], 16, voffb[j], kt * stage_b, 0, 0);
+          rb, (lds_void*)&ring_slot<slot>().b[1024 * (2 * wave + j)], 16, voffb[j], kt * stage_b, 0, 0);
     }
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsa, (lds_void*)&ring_slot<slot>().sa[256 * wave], 4,
-                                             soff_a, kt * sstage_a, 0, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsb, (lds_void*)&ring_slot<slot>().sb[256 * wave], 4,
-                                             soff_b, kt * sstage_b, 0, 0);
+    if (sc_a)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsa, (lds_void*)&ring_slot<slot>().sa[256 * (wave & 3)],
+                                               4, soff, kt * sstage, 0, 0);
+    else
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsb, (lds_void*)&ring_slot<slot>().sb[256 * (wave & 3)],
+                                               4, soff, kt * sstage, 0, 0);
   };
 
-  v16f acc[FM][FN];
-  static_for<FM>([&](auto I) {
-    static_for<FN>([&](auto J) {
+  v16f acc[R8_FM][R8_FN];
+  static_for<R8_FM>([&](auto I) {
+    static_for<R8_FN>([&](auto J) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[I][J][v] = 0.0f;
     });
   });
 
   const int lrow = lane & 31, khalf = lane >> 5;
-  // Fragment i of K-step ks: row wm*128 + 32 i + lrow, chunk (2 ks + half) ^ swz;
-  // swz depends on lrow only, so the two K-steps need one base each and the
-  // four fragments differ by the immediate 2048 i.
   const int lswz = ring_swz(lrow);
-  const int fa0 = (wm * WM + lrow) * RBK + (((0 + khalf) ^ lswz) << 4);
-  const int fa1 = (wm * WM + lrow) * RBK + (((2 + khalf) ^ lswz) << 4);
-  const int fb0 = (wn * WN + lrow) * RBK + (((0 + khalf) ^ lswz) << 4);
-  const int fb1 = (wn * WN + lrow) * RBK + (((2 + khalf) ^ lswz) << 4);
-  const int sa_off = (wm * WM + lrow) * 4;
-  const int sb_off = (wn * WN + lrow) * 4;
+  const int fa_base = (wm * R8_WM + lrow) * RBK, fb_base = (wn * R8_WN + lrow) * RBK;
+  // A stage's scale word of a row holds its four block scales in the order
+  // 0, 2, 1, 3: half h of the wave reads the 16 bits at byte 2 h, which hold
+  // its K-step 0 and K-step 1 scales in bytes 0 and 1 (the MFMA's op_sel).
+  const int sa_off = (wm * R8_WM + lrow) * 4 + 2 * khalf, sb_off = (wn * R8_WN + lrow) * 4 + 2 * khalf;
 
-  // Fragments of one stage (both 64-K steps) and its scale words, held in
-  // registers from the barrier that publishes the stage until its MFMAs.
+  // Fragments of one K-step with the stage's scale words.
   struct Frags {
-    v8i a[2][FM], b[2][FN];
-    int sa[FM], sb[FN];
+    v8i a[R8_FM], b[R8_FN];
+    int sa[R8_FM], sb[R8_FN];
   };
-  auto read_frags = [&](auto S, Frags& f) {
+  auto read_frags = [&](auto S, auto KS, Frags& f) {
     constexpr int slot = decltype(S)::value;
+    constexpr int ks = decltype(KS)::value;
+    const int sw = ((2 * ks + khalf) ^ lswz) << 4;
 #pragma unroll
-    for (int i = 0; i < FM; ++i)
-      f.sa[i] = (int)(*reinterpret_cast<const uint32_t*>(&ring_slot<slot>().sa[sa_off + 128 * i]) >> (8 * khalf));
+    for (int i = 0; i < R8_FM; ++i)
+      f.sa[i] = *reinterpret_cast<const uint16_t*>(&ring_slot<slot>().sa[sa_off + 128 * i]);
 #pragma unroll
-    for (int j = 0; j < FN; ++j)
-      f.sb[j] = (int)(*reinterpret_cast<const uint32_t*>(&ring_slot<slot>().sb[sb_off + 128 * j]) >> (8 * khalf));
+    for (int j = 0; j < R8_FN; ++j)
+      f.sb[j] = *reinterpret_cast<const uint16_t*>(&ring_slot<slot>().sb[sb_off + 128 * j]);
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      const int oa = ks == 0 ? fa0 : fa1;
-      const int ob = ks == 0 ? fb0 : fb1;
+    for (int i = 0; i < R8_FM; ++i) {
+      const uint4 q = *reinterpret_cast<const uint4*>(&ring_slot<slot>().a[fa_base + sw + 2048 * i]);
+      f.a[i] = v8i{(int)q.x, (int)q.y, (int)q.z, (int)q.w, 0, 0, 0, 0};
+    }
 #pragma unroll
-      for (int i = 0; i < FM; ++i) {
-        const uint4 q = *reinterpret_cast<const uint4*>(&ring_slot<slot>().a[oa + 2048 * i]);
-        f.a[ks][i] = v8i{(int)q.x, (int)q.y, (int)q.z, (int)q.w, 0, 0, 0, 0};
-      }
-#pragma unroll
-      for (int j = 0; j < FN; ++j) {
-        const uint4 q = *reinterpret_cast<const uint4*>(&ring_slot<slot>().b[ob + 2048 * j]);
-        f.b[ks][j] = v8i{(int)q.x, (int)q.y, (int)q.z, (int)q.w, 0, 0, 0, 0};
-      }
+    for (int j = 0; j < R8_FN; ++j) {
+      const uint4 q = *reinterpret_cast<const uint4*>(&ring_slot<slot>().b[fb_base + sw + 2048 * j]);
+      f.b[j] = v8i{(int)q.x, (int)q.y, (int)q.z, (int)q.w, 0, 0, 0, 0};
     }
   };
-  // 16 MFMAs of K-step ks: scale byte 2 ks + half, pre-shifted by 8 half.
+  // 8 MFMAs of K-step ks: scale byte ks of the 16 bits read.
   auto mma = [&](const Frags& f, auto KS) {
-    constexpr int kSel = 2 * decltype(KS)::value;
-    static_for<FM>([&](auto I) {
-      static_for<FN>([&](auto J) {
+    constexpr int kSel = decltype(KS)::value;
+    static_for<R8_FM>([&](auto I) {
+      static_for<R8_FN>([&](auto J) {
         acc[I][J] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-            f.b[KS][J], f.a[KS][I], acc[I][J], 4, 4, kSel, f.sb[J], kSel, f.sa[I]);
+            f.b[J], f.a[I], acc[I][J], 4, 4, kSel, f.sb[J], kSel, f.sa[I]);
       });
     });
   };
 
-  // Iteration kt (stage kt's fragments in `cur`): K-step 0 of stage kt; wait
-  // until only this wave's 20 loads of stages kt+2, kt+3 are in flight and
-  // sync, which publishes stage kt+1 and guarantees every wave is done with
-  // stage kt's slot; refill that slot with stage kt+4 (past the end: a re-load
-  // of the last stage that no one reads, so every iteration issues 10 loads);
-  // read stage kt+1's fragments into `nxt` while K-step 1 of stage kt runs.
-  auto iteration = [&](auto S, Frags& cur, Frags& nxt, int kt) {
+  // Stage kt (its K-step 0 fragments in x): read K-step 1 into y during
+  // K-step 0's MFMAs; wait until only this wave's 10 loads of stages kt+2,
+  // kt+3 are in flight and sync, publishing stage kt+1 and freeing slot kt;
+  // refill it with stage kt+4 (past the end: a re-load of the last stage no
+  // one reads) and read stage kt+1's K-step 0 into x during K-step 1's MFMAs.
+  auto stage = [&](auto S, Frags& x, Frags& y, int kt) {
     constexpr int slot = decltype(S)::value;
-    mma(cur, std::integral_constant<int, 0>{});
+    read_frags(std::integral_constant<int, slot>{}, std::integral_constant<int, 1>{}, y);
+    mma(x, std::integral_constant<int, 0>{});
+    static_for<6>([&](auto) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);   // DS read
+    });
+    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
     __builtin_amdgcn_sched_barrier(0);
-    __builtin_amdgcn_s_waitcnt(waitcnt_imm(2 * kLoadsPerStage, 0));
+    __builtin_amdgcn_s_waitcnt(waitcnt_imm(2 * kLoads8PerStage, 0));
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
     issue(std::integral_constant<int, slot>{}, kt + 4 < nk ? kt + 4 : nk - 1);
-    read_frags(std::integral_constant<int, (slot + 1) % kRingSlots>{}, nxt);
-    mma(cur, std::integral_constant<int, 1>{});
-    // One global->LDS load and two LDS reads after each of the first 10
-    // MFMAs, then the rest of the LDS reads: a load that waits for the memory
-    // pipeline holds back few MFMAs, and the fragments land long before the
-    // next stage's first MFMA needs them.
-    static_for<10>([&](auto) {
+    read_frags(std::integral_constant<int, (slot + 1) % kRingSlots>{}, std::integral_constant<int, 0>{}, x);
+    mma(y, std::integral_constant<int, 1>{});
+    static_for<5>([&](auto) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
       __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // VMEM read
       __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);   // DS read
     });
     static_for<2>([&](auto) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     });
-    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
     __builtin_amdgcn_sched_barrier(0);
   };
 
@@ -652,17 +657,16 @@ __global__ void __launch_bounds__(kGemmThreads, 1) gemm_mx_ring_kernel(GemmArgs 
   issue(std::integral_constant<int, 2>{}, 2);
   issue(std::integral_constant<int, 3>{}, 3);
   Frags fx, fy;
-  __builtin_amdgcn_s_waitcnt(waitcnt_imm(3 * kLoadsPerStage, 0));
+  __builtin_amdgcn_s_waitcnt(waitcnt_imm(3 * kLoads8PerStage, 0));
   __builtin_amdgcn_s_barrier();
   __builtin_amdgcn_sched_barrier(0);
-  read_frags(std::integral_constant<int, 0>{}, fx);
-  // nk is a multiple of 4 (K % 512 == 0): one loop exit, so the accumulators
-  // keep their registers across the whole loop.
+  read_frags(std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{}, fx);
+  // nk is a multiple of 4 (K % 512 == 0): one loop exit.
   for (int kt = 0; kt < nk; kt += kRingSlots) {
-    iteration(std::integral_constant<int, 0>{}, fx, fy, kt);
-    iteration(std::integral_constant<int, 1>{}, fy, fx, kt + 1);
-    iteration(std::integral_constant<int, 2>{}, fx, fy, kt + 2);
-    iteration(std::integral_constant<int, 3>{}, fy, fx, kt + 3);
+    stage(std::integral_constant<int, 0>{}, fx, fy, kt);
+    stage(std::integral_constant<int, 1>{}, fx, fy, kt + 1);
+    stage(std::integral_constant<int, 2>{}, fx, fy, kt + 2);
+    stage(std::integral_constant<int, 3>{}, fx, fy, kt + 3);
   }
 
   // Drain the trailing loads before the epilogue and before the workgroup's
@@ -670,7 +674,7 @@ __global__ void __launch_bounds__(kGemmThreads, 1) gemm_mx_ring_kernel(GemmArgs 
   __builtin_amdgcn_sched_barrier(0);
   __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
   __syncthreads();
-  gemm_finish(g, acc, m0, n0, g_ring_pos);
+  gemm_finish<R8_FM, R8_FN, R8_WM, R8_WN, 4, kRing8Threads>(g, acc, m0, n0, g_ring_pos);
 }
 
 // ---------------------------------------------------------------------------
@@ -906,9 +910,9 @@ adahop_status bf16_gemm_launch(Bf16View X, Bf16View Y, int64_t m, int64_t n, int
 namespace {
 
 // Stage-major copy of both scale arrays for the main kernel, as 4-byte
-// words (the four block scales of one 128-long stage of one row):
-// dst[c][r] = src[r][c], c < K/128, through a 64 x 64 LDS tile. blockIdx.z
-// picks the operand.
+// words (the four block scales of one 128-long stage of one row, in the
+// order 0, 2, 1, 3): dst[c][r] = src[r][c], c < K/128, through a 64 x 64 LDS
+// tile. blockIdx.z picks the operand.
 constexpr int kTr = 64;
 __global__ void __launch_bounds__(256)
 scale_stage_kernel(const uint32_t* __restrict__ sa, int64_t ma, uint32_t* __restrict__ da,
@@ -928,7 +932,10 @@ scale_stage_kernel(const uint32_t* __restrict__ sa, int64_t ma, uint32_t* __rest
   __syncthreads();
   for (int i = ty; i < kTr; i += 4) {
     const int64_t c = c0 + i, r = r0 + tx;
-    if (r < rows && c < nst) dst[c * rows + r] = tile[tx][i];
+    if (r < rows && c < nst) {
+      const uint32_t v = tile[tx][i];   // block scales 0, 1, 2, 3 -> stored 0, 2, 1, 3
+      dst[c * rows + r] = (v & 0xFF0000FFu) | ((v >> 8) & 0xFF00u) | ((v << 8) & 0xFF0000u);
+    }
   }
 }
 
@@ -1009,14 +1016,14 @@ adahop_status gemm_mx_launch(const uint8_t* a_codes, const uint8_t* a_scales,
       return fail(ADAHOP_ERR_UNSUPPORTED, "gemm_mx: K-chunked operands need K % 512 == 0 and aligned buffers");
     g.a_sst = reinterpret_cast<const uint32_t*>(a_scales);
     g.b_sst = reinterpret_cast<const uint32_t*>(b_scales);
-    gemm_mx_ring_kernel<true><<<grid, block, 0, stream>>>(g);
+    gemm_mx_ring8_kernel<true><<<grid, dim3(kRing8Threads), 0, stream>>>(g);
   } else if (ring_applies(a_codes, a_scales, b_codes, b_scales, m, n, K)) {
     // The scales were reordered into `scratch` by gemm_mx_stage_scales.
     const adahop_status st = check_scratch(scratch, scratch_bytes, gemm_mx_scratch_bytes(m, n, K));
     if (st != ADAHOP_OK) return st;
     g.a_sst = static_cast<const uint32_t*>(scratch);
     g.b_sst = staged_b(scratch, m, K);
-    gemm_mx_ring_kernel<false><<<grid, block, 0, stream>>>(g);
+    gemm_mx_ring8_kernel<false><<<grid, dim3(kRing8Threads), 0, stream>>>(g);
   } else if (K % 256 == 0 && (sc_bits & 7u) == 0)
     gemm_mx_kernel<true><<<grid, block, 0, stream>>>(g);
   else

@@ -198,7 +198,12 @@ iht_quant_rowwise_kernel(const uint16_t* __restrict__ src, int64_t rows, int64_t
   // [K/128][rows][64] and [K/128][rows][4]: chunk q of this tile is rows
   // r0 .. r0 + 3 x 64 bytes, one contiguous run (K % 128 == 0).
   *reinterpret_cast<uint2*>(&s_codes[wave][lane * 8]) = make_uint2(lo, hi);
-  if (!upper) s_scales[wave][lane / 2] = (uint8_t)(sx + 127);
+  // Scale bytes of a 128-long chunk go in the order 0, 2, 1, 3 (the layout
+  // the GEMM reads 16 bits at a time per half-wave).
+  if (!upper) {
+    const int b = lane / 2;              // block within the workgroup's row
+    s_scales[wave][(b & ~3) | ((b & 1) << 1) | ((b >> 1) & 1)] = (uint8_t)(sx + 127);
+  }
   __syncthreads();
   const int nrow = (int)(rows - r0 < kRowRows ? rows - r0 : kRowRows);
   const int nch = (int)((K - cbase) / 128 < kRowChunk / 128 ? (K - cbase) / 128 : kRowChunk / 128);
@@ -398,8 +403,12 @@ iht_quant_colwise_kernel(const uint16_t* __restrict__ src, int64_t K, int64_t ou
     {
       const int q = tid / kColOut, r = tid % kColOut;
       if (r < nrow && 4 * q < nb)
+      {
+        // block scales 0, 1, 2, 3 of the chunk stored in the order 0, 2, 1, 3
+        const uint32_t v = *reinterpret_cast<const uint32_t*>(&s_scales[r * kColBlocks + 4 * q]);
         *reinterpret_cast<uint32_t*>(scales + ((c0k + q) * outer + cbase + r) * 4) =
-            *reinterpret_cast<const uint32_t*>(&s_scales[r * kColBlocks + 4 * q]);
+            (v & 0xFF0000FFu) | ((v >> 8) & 0xFF00u) | ((v << 8) & 0xFF0000u);
+      }
     }
     return;
   }
