@@ -15,7 +15,8 @@
 // on the fp64 score bits (scores are >= 0, so their bit patterns order like
 // the values): a workgroup holds 4 or 16 scores per thread in registers, and
 // 16 passes of 4-bit digits (per-thread packed counters, wave and workgroup
-// sums) find the k-th largest score T exactly. Every score above T
+// sums) narrow down the k-th largest score; once the digit bin holding it has
+// at most 256 scores, those are ranked exactly one against all. Every score above T
 // is kept, and of the scores equal to T the ones with the lowest indices --
 // the key (score descending, index ascending) is a strict total order, so
 // the result is unique. A prefix sum over the threads, which own the
@@ -89,6 +90,7 @@ foid_var_kernel(const uint16_t* __restrict__ t, int64_t ld, int axis, int P, int
 }
 
 constexpr int kSelThreads = 256;
+constexpr int kExact = 256;   // a digit bin this small is ranked exactly
 
 // Exclusive prefix sum of v over the workgroup's threads in order; *total
 // receives the sum. Uses s_tmp[THREADS / 64].
@@ -129,6 +131,9 @@ foid_select_kernel(const double* __restrict__ in_var, const int32_t* __restrict_
   constexpr int kWaves = THREADS / 64;
   __shared__ uint32_t s_cnt[kWaves][16];
   __shared__ uint32_t s_tot[16];
+  __shared__ uint64_t s_ekey[kExact];
+  __shared__ int s_epos[kExact];
+  __shared__ uint8_t s_esel[kExact];
   __shared__ int s_tmp[kWaves];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t first = (int64_t)blockIdx.x * THREADS * KPT + (int64_t)tid * KPT;
@@ -148,6 +153,7 @@ foid_select_kernel(const double* __restrict__ in_var, const int32_t* __restrict_
   // T = the k-th largest key; krem = how many keys equal to T are kept.
   uint64_t prefix = 0, pmask = 0;
   int krem = k;
+  bool exact = false;   // the k-th key's bin, once small, is ranked exactly
   if (nvalid > k) {
     for (int pass = 0; pass < 16; ++pass) {
       const int shift = 60 - 4 * pass;
@@ -191,28 +197,72 @@ foid_select_kernel(const double* __restrict__ in_var, const int32_t* __restrict_
       krem -= cum;
       prefix |= (uint64_t)dsel << shift;
       pmask |= 15ull << shift;
+      const int m = (int)s_tot[dsel];     // keys in the chosen bin
       __syncthreads();
+      if (m <= kExact) { exact = true; break; }   // the same for every thread
     }
   } else {
     krem = 0;          // keep every real entry
   }
 
-  // Kept: real keys above T, and the first krem keys equal to T in index order.
-  uint32_t gt = 0, eq = 0;
+  uint32_t keep = 0;
+  if (exact) {
+    // Keys in a higher bin are kept; of the m keys in the bin, the krem best
+    // by (key descending, position ascending), ranked one against all.
+    uint32_t in = 0;
 #pragma unroll
-  for (int j = 0; j < KPT; ++j) {
-    if (!((valid >> j) & 1u)) continue;
-    if (nvalid <= k || key[j] > prefix) gt |= 1u << j;
-    else if (key[j] == prefix) eq |= 1u << j;
-  }
-  int eq_total;
-  const int eq_before = block_exclusive_scan<THREADS>(__popc(eq), s_tmp, &eq_total);
-  int take = krem - eq_before;
-  take = take < 0 ? 0 : take;
-  uint32_t keep = gt;
+    for (int j = 0; j < KPT; ++j) {
+      if (!((valid >> j) & 1u)) continue;
+      const uint64_t b = key[j] & pmask;
+      if (b > prefix) keep |= 1u << j;
+      else if (b == prefix) in |= 1u << j;
+    }
+    int m;
+    int p = block_exclusive_scan<THREADS>(__popc(in), s_tmp, &m);
+    const int p0 = p;
 #pragma unroll
-  for (int j = 0; j < KPT; ++j) {
-    if (((eq >> j) & 1u) && take > 0) { keep |= 1u << j; --take; }
+    for (int j = 0; j < KPT; ++j) {
+      if (!((in >> j) & 1u)) continue;
+      s_ekey[p] = key[j];
+      s_epos[p] = tid * KPT + j;
+      ++p;
+    }
+    __syncthreads();
+    for (int t = tid; t < m; t += THREADS) {
+      const uint64_t kt = s_ekey[t];
+      const int pt = s_epos[t];
+      int rank = 0;
+      for (int u = 0; u < m; ++u) {
+        const uint64_t ku = s_ekey[u];
+        rank += (ku > kt || (ku == kt && s_epos[u] < pt)) ? 1 : 0;
+      }
+      s_esel[t] = rank < krem ? 1 : 0;
+    }
+    __syncthreads();
+    p = p0;
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) {
+      if (!((in >> j) & 1u)) continue;
+      if (s_esel[p]) keep |= 1u << j;
+      ++p;
+    }
+  } else {
+    // Kept: real keys above T, and the first krem keys equal to T in index order.
+    uint32_t eq = 0;
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) {
+      if (!((valid >> j) & 1u)) continue;
+      if (nvalid <= k || key[j] > prefix) keep |= 1u << j;
+      else if (key[j] == prefix) eq |= 1u << j;
+    }
+    int eq_total;
+    const int eq_before = block_exclusive_scan<THREADS>(__popc(eq), s_tmp, &eq_total);
+    int take = krem - eq_before;
+    take = take < 0 ? 0 : take;
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) {
+      if (((eq >> j) & 1u) && take > 0) { keep |= 1u << j; --take; }
+    }
   }
   int kept;
   int pos = block_exclusive_scan<THREADS>(__popc(keep), s_tmp, &kept);

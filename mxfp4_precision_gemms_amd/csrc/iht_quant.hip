@@ -24,6 +24,8 @@
 // at a time: each butterfly output is one rounded fp32 add or subtract, then
 // one rounded multiply by fp32(1/sqrt(32)). The E2M1 codes come from gfx950's
 // scaled FP4 convert (see pack8_e2m1).
+#include <type_traits>
+
 #include "adahop_internal.h"
 
 #pragma clang fp contract(off)
@@ -153,8 +155,10 @@ iht_quant_rowwise_kernel(const uint16_t* __restrict__ src, int64_t rows, int64_t
       // lane * 16 is a multiple of 16: this lane's 16 columns sit in one word.
       const int d = lane * 16;
       const uint32_t zmask = (s_cmask[d / 32] >> (d % 32)) & 0xFFFFu;
+      if (zmask) {
 #pragma unroll
-      for (int i = 0; i < 16; ++i) y[i] = ((zmask >> i) & 1u) ? 0.0f : y[i];
+        for (int i = 0; i < 16; ++i) y[i] = ((zmask >> i) & 1u) ? 0.0f : y[i];
+      }
     }
   }
 
@@ -238,10 +242,10 @@ constexpr int kColOut = 4 * kColGroups;        // output rows per workgroup
 constexpr int kColBlocks = kColThreads / kColGroups;   // 32-row blocks per workgroup
 constexpr int kColPitch = kColBlocks * 16 + 16;        // LDS bytes per output row (padded)
 
-template <bool Vec>
+template <bool Vec, bool Had>
 __global__ void __launch_bounds__(kColThreads)
 iht_quant_colwise_kernel(const uint16_t* __restrict__ src, int64_t K, int64_t outer, int64_t ld,
-                         int hadamard, const int32_t* __restrict__ zidx, int nz, int zaxis,
+                         const int32_t* __restrict__ zidx, int nz, int zaxis,
                          uint8_t* __restrict__ codes, uint8_t* __restrict__ scales,
                          uint16_t* __restrict__ gathered, int kchunk) {
   __shared__ __attribute__((aligned(16))) uint8_t s_codes[kColOut * kColPitch];
@@ -275,13 +279,22 @@ iht_quant_colwise_kernel(const uint16_t* __restrict__ src, int64_t K, int64_t ou
   uint32_t w[32][2];
   if (mine) {
     const bool whole = Vec && c0 + 4 <= outer;
+    if (whole) {
+      // Row j of the block is at byte j * ld * 2 from the block's first row:
+      // a scalar offset, so the 32 loads need no per-lane address arithmetic.
+      const uint16_t* blk = src + (bbase * 32) * ld;     // workgroup-uniform
+      const __amdgpu_buffer_rsrc_t rs =
+          __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(blk), 0, 0x7FFFFFFF, 0x00020000);
+      const int voff = (int)((bi * 32 * ld + c0) * 2);
 #pragma unroll
-    for (int j = 0; j < 32; ++j) {
-      if (whole) {
-        const uint2 q = *reinterpret_cast<const uint2*>(src + (t0 + j) * ld + c0);
-        w[j][0] = q.x;
-        w[j][1] = q.y;
-      } else {
+      for (int j = 0; j < 32; ++j) {
+        const auto q = __builtin_amdgcn_raw_buffer_load_b64(rs, voff, (int)(j * ld * 2), 0);
+        w[j][0] = q[0];
+        w[j][1] = q[1];
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < 32; ++j) {
         uint32_t h[4];
 #pragma unroll
         for (int q = 0; q < 4; ++q) h[q] = c0 + q < outer ? src[(t0 + j) * ld + c0 + q] : 0u;
@@ -333,12 +346,15 @@ iht_quant_colwise_kernel(const uint16_t* __restrict__ src, int64_t K, int64_t ou
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int64_t c = c0 + q;
-      if (c >= outer) break;
+      if (c >= outer) continue;
       float y[32];
+      // bf16 -> fp32: the low half shifted up, or the high half masked.
 #pragma unroll
-      for (int j = 0; j < 32; ++j) {
-        const uint32_t h = (w[j][q >> 1] >> (16 * (q & 1))) & 0xFFFFu;
-        y[j] = ((rmask >> j) & 1u) ? 0.0f : bf16_bits_to_f32(h);
+      for (int j = 0; j < 32; ++j)
+        y[j] = __uint_as_float((q & 1) ? (w[j][q >> 1] & 0xFFFF0000u) : (w[j][q >> 1] << 16));
+      if (rmask) {
+#pragma unroll
+        for (int j = 0; j < 32; ++j) y[j] = ((rmask >> j) & 1u) ? 0.0f : y[j];
       }
       const int cl = 4 * cg + q;
       if ((s_cmask[cl / 32] >> (cl % 32)) & 1u) {
@@ -357,7 +373,7 @@ iht_quant_colwise_kernel(const uint16_t* __restrict__ src, int64_t K, int64_t ou
 #pragma unroll
         for (int j = 0; j < 32; ++j) y[j] = 0.0f;
       }
-      if (hadamard) {
+      if (Had) {
 #pragma unroll
         for (int h = 1; h < 32; h <<= 1) {
 #pragma unroll
@@ -457,14 +473,19 @@ adahop_status iht_quant_launch(const uint16_t* src, int64_t rows, int64_t cols, 
     const int64_t gy = (K / 32 + kColBlocks - 1) / kColBlocks;
     if (gx > 0x7FFFFFFFLL || gy > 65535)
       return fail(ADAHOP_ERR_UNSUPPORTED, "iht_quant: tensor too large");
-    const bool vec = ld % 4 == 0 && (reinterpret_cast<uintptr_t>(src) & 7u) == 0;
     const dim3 grid((unsigned)gx, (unsigned)gy), block(kColThreads);
-    if (vec)
-      iht_quant_colwise_kernel<true><<<grid, block, 0, stream>>>(
-          src, K, outer, ld, had, zero_idx, nzero, zero_axis, codes, scales, gathered, kchunk);
-    else
-      iht_quant_colwise_kernel<false><<<grid, block, 0, stream>>>(
-          src, K, outer, ld, had, zero_idx, nzero, zero_axis, codes, scales, gathered, kchunk);
+    // The per-row offsets of the vector path are 32-bit byte offsets from
+    // the workgroup's first row: 512 rows of ld elements must stay below 2^31.
+    const bool vec = ld % 4 == 0 && (reinterpret_cast<uintptr_t>(src) & 7u) == 0 &&
+                     (int64_t)kColBlocks * 32 * ld * 2 < 0x7FFFFFFF;
+    auto go = [&](auto V, auto H) {
+      iht_quant_colwise_kernel<decltype(V)::value, decltype(H)::value><<<grid, block, 0, stream>>>(
+          src, K, outer, ld, zero_idx, nzero, zero_axis, codes, scales, gathered, kchunk);
+    };
+    if (vec && had) go(std::true_type{}, std::true_type{});
+    else if (vec) go(std::true_type{}, std::false_type{});
+    else if (had) go(std::false_type{}, std::true_type{});
+    else go(std::false_type{}, std::false_type{});
   }
   return check_launch("iht_quant");
 }
