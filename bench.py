@@ -241,7 +241,7 @@ def main():
         "stages_ms": {k: round(v, 4) for k, v in stage_ms.items()},
         "call_ms_events": round(call_ms, 4),
         "roofline": {"bound": "mfma",
-                     "kernel": "gemm_mx_ring_kernel (FP4 MFMA GEMM, fused scatter-add epilogue)",
+                     "kernel": "gemm_mx_ring8_kernel (FP4 MFMA GEMM, fused scatter-add epilogue)",
                      "achieved": round(achieved, 1), "peak": PEAK_FP4_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP4_TFLOPS, 4),
                      "traffic": None},
