@@ -165,7 +165,7 @@ adahop_status make_plan(adahop_op op, int64_t T, int64_t Din, int64_t Dout,
   // Operands the main GEMM kernel streams are packed K-chunked by the
   // quantizers; otherwise row-major, with the GEMM's own scale reordering.
   pb.layout = gemm_mx_kchunk_ok(s.m, s.n, s.K) ? ADAHOP_LAYOUT_KCHUNK : ADAHOP_LAYOUT_ROWS;
-  P->gemm_bytes = pb.layout == ADAHOP_LAYOUT_ROWS ? gemm_mx_scratch_bytes(s.m, s.n, s.K) : 0;
+  P->gemm_bytes = gemm_mx_scratch_bytes(s.m, s.n, s.K, pb.layout);
   if (P->gemm_bytes) P->off_gemm = take(P->gemm_bytes);
   pb.ws_bytes = off;
   return ADAHOP_OK;
@@ -288,8 +288,6 @@ adahop_status run_gemm(adahop_op op, const uint16_t* lhs, const uint16_t* rhs, i
 
 // Workspace of adahop_gemm_mx: the outlier product's partial sums (OE_LEFT,
 // OE_RIGHT) first, then the GEMM's own scratch.
-// Workspace of adahop_gemm_mx: the outlier product's partial sums (OE_LEFT,
-// OE_RIGHT) first, then the GEMM's own scratch.
 size_t gemm_mx_partials_bytes(int64_t m, int64_t n, int64_t K, const adahop_oe* oe) {
   if (!oe || (oe->route != ADAHOP_ROUTE_OE_LEFT && oe->route != ADAHOP_ROUTE_OE_RIGHT)) return 0;
   if (oe->k < 1) return 0;
@@ -391,7 +389,7 @@ adahop_status adahop_iht_quant(const uint16_t* src, int64_t rows, int64_t cols, 
 
 size_t adahop_gemm_mx_workspace_size(int64_t m, int64_t n, int64_t K, const adahop_oe* oe) {
   if (m < 1 || n < 1 || K < 1) return 0;
-  return gemm_mx_partials_bytes(m, n, K, oe) + gemm_mx_scratch_bytes(m, n, K);
+  return gemm_mx_partials_bytes(m, n, K, oe) + gemm_mx_scratch_bytes(m, n, K, ADAHOP_LAYOUT_ROWS);
 }
 
 adahop_status adahop_gemm_mx(const adahop_mx_operand* A, const adahop_mx_operand* B,

@@ -57,11 +57,12 @@ struct OeEpilogue {
   int splits;
   Bf16View a, b;            // OE_INNER factors: a [m][k], b [n][k]
 };
-// Workspace the GEMM needs for (m, n, K): stage-major copies of both scale
-// arrays ([K/128][rows] words) when the main kernel applies (K % 512 == 0),
-// else 0. gemm_mx_stage_scales writes them (nothing to do when the main
-// kernel does not apply); gemm_mx_launch reads them from the same scratch.
-size_t gemm_mx_scratch_bytes(int64_t m, int64_t n, int64_t K);
+// Workspace the GEMM needs for (m, n, K) in `layout`, when the main kernel
+// applies (K % 512 == 0), else 0: for ROWS, stage-major copies of both scale
+// arrays ([K/128][rows] words; gemm_mx_stage_scales writes them), then, for
+// both layouts, the fp32 parts of the tiles the main kernel splits along K
+// in its last round (256 KB per part).
+size_t gemm_mx_scratch_bytes(int64_t m, int64_t n, int64_t K, int layout);
 // Whether (m, n, K) operands may be packed K-chunked (ADAHOP_LAYOUT_KCHUNK):
 // the main kernel applies and stage offsets fit 31 bits.
 bool gemm_mx_kchunk_ok(int64_t m, int64_t n, int64_t K);
@@ -70,7 +71,8 @@ adahop_status gemm_mx_stage_scales(const uint8_t* a_codes, const uint8_t* a_scal
                                    int64_t n, int64_t K, void* scratch, size_t scratch_bytes,
                                    hipStream_t stream);
 // layout ROWS: scales reordered by gemm_mx_stage_scales into `scratch` when
-// the main kernel applies; KCHUNK: operands as ADAHOP_LAYOUT_KCHUNK, no scratch.
+// the main kernel applies; KCHUNK: operands as ADAHOP_LAYOUT_KCHUNK. `scratch`
+// holds gemm_mx_scratch_bytes(m, n, K, layout) bytes.
 adahop_status gemm_mx_launch(const uint8_t* a_codes, const uint8_t* a_scales,
                              const uint8_t* b_codes, const uint8_t* b_scales, int64_t m,
                              int64_t n, int64_t K, int layout, const OeEpilogue& oe, void* C,

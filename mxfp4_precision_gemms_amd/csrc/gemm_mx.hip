@@ -35,6 +35,7 @@ namespace adahop {
 namespace {
 
 typedef int v8i __attribute__((ext_vector_type(8)));
+typedef int v4i __attribute__((ext_vector_type(4)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 
@@ -89,6 +90,12 @@ struct GemmArgs {
   int64_t ldc;
   int out_f32;
   int tiles_m, tiles_n;
+  // Last round split along K (main kernel): workgroups from split_full on
+  // each take 1 / split_parts of K of one of the tiles from split_full on and
+  // leave their fp32 sums in split_ws ([tile][part][thread-order]);
+  // gemm_split_fixup_kernel adds the parts and runs the epilogue.
+  int split_full, split_parts;
+  float* split_ws;
   // outlier epilogue
   int oe_mode;
   int oe_k;
@@ -113,15 +120,17 @@ __device__ __forceinline__ uint16_t view_at(const uint16_t* p, int64_t ld, int i
   return inner ? p[r * ld + t] : p[t * ld + r];
 }
 
-// Tile of workgroup `bid`. The hardware deals workgroups round-robin to the 8
-// XCDs (bid % 8); each XCD gets a contiguous band of the logical tile order,
-// and the logical order walks groups of kGroupM tile rows column by column,
-// so the ~32 tiles an XCD runs at once form a 4 x 8 block that shares operand
-// rows in that XCD's L2.
-__device__ __forceinline__ void tile_of(int bid, int tiles_m, int tiles_n, int* tm, int* tn) {
-  const int ntiles = tiles_m * tiles_n;
-  int pid = bid;
-  if (ntiles % 8 == 0) pid = (bid & 7) * (ntiles / 8) + (bid >> 3);
+// Logical position of workgroup `bid` among `count` workgroups. The hardware
+// deals workgroups round-robin to the 8 XCDs (bid % 8); each XCD gets a
+// contiguous band of the logical order.
+__device__ __forceinline__ int xcd_band(int bid, int count) {
+  return count % 8 == 0 ? (bid & 7) * (count / 8) + (bid >> 3) : bid;
+}
+
+// Tile at logical position pid: the logical order walks groups of kGroupM
+// tile rows column by column, so the ~32 tiles an XCD runs at once form a
+// 4 x 8 block that shares operand rows in that XCD's L2.
+__device__ __forceinline__ void tile_at(int pid, int tiles_m, int tiles_n, int* tm, int* tn) {
   const int per_group = kGroupM * tiles_n;
   const int group = pid / per_group;
   const int first_m = group * kGroupM;
@@ -129,6 +138,10 @@ __device__ __forceinline__ void tile_of(int bid, int tiles_m, int tiles_n, int* 
   const int in_group = pid - group * per_group;
   *tm = first_m + in_group % gm;
   *tn = in_group / gm;
+}
+
+__device__ __forceinline__ void tile_of(int bid, int tiles_m, int tiles_n, int* tm, int* tn) {
+  tile_at(xcd_band(bid, tiles_m * tiles_n), tiles_m, tiles_n, tm, tn);
 }
 
 // Inner-extraction term and epilogue, shared by both GEMM kernels. `acc` is
@@ -141,9 +154,9 @@ __device__ __forceinline__ void tile_of(int bid, int tiles_m, int tiles_n, int* 
 // 32x32 blocks at rows (w / WAVES_N) * TWM, columns (w % WAVES_N) * TWN of
 // the tile, in C^T register layout (lane l: row l % 32; register 4 G + e:
 // column 8 G + 4 (l / 32) + e of the block).
-template <int TFM, int TFN, int TWM, int TWN, int WAVES_N, int THREADS>
-__device__ __forceinline__ void gemm_finish(const GemmArgs& g, v16f (&acc)[TFM][TFN], int64_t m0,
-                                            int64_t n0, int* s_pos) {
+template <int TFM, int TFN, int TWM, int TWN, int WAVES_N>
+__device__ __forceinline__ void gemm_inner_term(const GemmArgs& g, v16f (&acc)[TFM][TFN], int64_t m0,
+                                                int64_t n0) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -183,7 +196,17 @@ __device__ __forceinline__ void gemm_finish(const GemmArgs& g, v16f (&acc)[TFM][
       });
     }
   }
+}
 
+// Outer-extraction scatter-add, one rounding to the output type, stores.
+template <int TFM, int TFN, int TWM, int TWN, int WAVES_N, int THREADS>
+__device__ __forceinline__ void gemm_store(const GemmArgs& g, v16f (&acc)[TFM][TFN], int64_t m0,
+                                           int64_t n0, int* s_pos) {
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wm = wave / WAVES_N, wn = wave % WAVES_N;
+  const int lrow = lane & 31, khalf = lane >> 5;
   // Outer extraction: positions of this tile's extracted rows / columns.
   const bool oe_rows = g.oe_mode == ADAHOP_ROUTE_OE_LEFT;
   const bool oe_cols = g.oe_mode == ADAHOP_ROUTE_OE_RIGHT;
@@ -252,6 +275,13 @@ __device__ __forceinline__ void gemm_finish(const GemmArgs& g, v16f (&acc)[TFM][
       });
     });
   });
+}
+
+template <int TFM, int TFN, int TWM, int TWN, int WAVES_N, int THREADS>
+__device__ __forceinline__ void gemm_finish(const GemmArgs& g, v16f (&acc)[TFM][TFN], int64_t m0,
+                                            int64_t n0, int* s_pos) {
+  gemm_inner_term<TFM, TFN, TWM, TWN, WAVES_N>(g, acc, m0, n0);
+  gemm_store<TFM, TFN, TWM, TWN, WAVES_N, THREADS>(g, acc, m0, n0, s_pos);
 }
 
 // One stage of global data held in registers between its load and its LDS store.
@@ -492,6 +522,9 @@ constexpr int kRing8Threads = 512;
 constexpr int R8_FM = 4, R8_FN = 2, R8_WM = 128, R8_WN = 64;
 constexpr int kLoads8PerStage = 5;            // per wave
 
+// A split tile's part in the workspace: a row-major fp32 256 x 256 matrix.
+constexpr int kSplitPartF4 = BM * BN / 4;      // float4 per part (256 KB)
+
 template <bool Chunked>
 __global__ void __launch_bounds__(kRing8Threads, 1) gemm_mx_ring8_kernel(GemmArgs g) {
   const int tid = threadIdx.x;
@@ -499,12 +532,32 @@ __global__ void __launch_bounds__(kRing8Threads, 1) gemm_mx_ring8_kernel(GemmArg
   // Wave-uniform (scalar): the scale loads below pick their descriptor by it.
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 2, wn = wave & 3;
-  int tm, tn;
-  tile_of(blockIdx.x, g.tiles_m, g.tiles_n, &tm, &tn);
+  // Whole tiles first, then the split tiles of the last round: part p of
+  // one takes K stages [p, p + 1) * nk / split_parts.
+  const int bid = blockIdx.x;
+  int tm, tn, part = -1, split_tile = 0;
+  if (bid < g.split_full) {
+    tile_at(xcd_band(bid, g.split_full), g.tiles_m, g.tiles_n, &tm, &tn);
+  } else {
+    const int t = xcd_band(bid - g.split_full, (int)gridDim.x - g.split_full);
+    split_tile = t / g.split_parts;
+    part = t % g.split_parts;
+    tile_at(g.split_full + split_tile, g.tiles_m, g.tiles_n, &tm, &tn);
+  }
+  // All of these are workgroup-uniform; the integer divisions leave them in
+  // vector registers, and the buffer descriptors and offsets built from them
+  // must be scalar (else every load becomes a loop over lanes).
+  tm = __builtin_amdgcn_readfirstlane(tm);
+  tn = __builtin_amdgcn_readfirstlane(tn);
+  part = __builtin_amdgcn_readfirstlane(part);
+  split_tile = __builtin_amdgcn_readfirstlane(split_tile);
   const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
   const int64_t Kb = g.K / 2;
   const int64_t Ks = g.K / 32;
   const int nk = (int)(Kb / RBK);
+  // This workgroup's stages [kt0, kt1): a multiple of 4.
+  const int kt0 = __builtin_amdgcn_readfirstlane(part < 0 ? 0 : part * (nk / g.split_parts));
+  const int kt1 = __builtin_amdgcn_readfirstlane(part < 0 ? nk : kt0 + nk / g.split_parts);
   const int rows_a = (int)(g.m - m0 < BM ? g.m - m0 : BM);
   const int rows_b = (int)(g.n - n0 < BN ? g.n - n0 : BN);
 
@@ -581,10 +634,17 @@ __global__ void __launch_bounds__(kRing8Threads, 1) gemm_mx_ring8_kernel(GemmArg
   // its K-step 0 and K-step 1 scales in bytes 0 and 1 (the MFMA's op_sel).
   const int sa_off = (wm * R8_WM + lrow) * 4 + 2 * khalf, sb_off = (wn * R8_WN + lrow) * 4 + 2 * khalf;
 
-  // Fragments of one K-step with the stage's scale words.
+  // Fragments of one K-step (16 bytes each) with the stage's scale words.
   struct Frags {
-    v8i a[R8_FM], b[R8_FN];
+    v4i a[R8_FM], b[R8_FN];
     int sa[R8_FM], sb[R8_FN];
+  };
+  // Keeps a fragment set live up to this point, so that the other set (read
+  // meanwhile) gets registers of its own: a read into a register that an
+  // in-flight MFMA still reads would have to wait for that MFMA.
+  auto keep = [](const Frags& f) {
+    asm volatile("" ::"v"(f.a[0]), "v"(f.a[1]), "v"(f.a[2]), "v"(f.a[3]), "v"(f.b[0]), "v"(f.b[1]),
+                 "v"(f.sa[0]), "v"(f.sa[1]), "v"(f.sa[2]), "v"(f.sa[3]), "v"(f.sb[0]), "v"(f.sb[1]));
   };
   auto read_frags = [&](auto S, auto KS, Frags& f) {
     constexpr int slot = decltype(S)::value;
@@ -598,13 +658,11 @@ __global__ void __launch_bounds__(kRing8Threads, 1) gemm_mx_ring8_kernel(GemmArg
       f.sb[j] = *reinterpret_cast<const uint16_t*>(&ring_slot<slot>().sb[sb_off + 128 * j]);
 #pragma unroll
     for (int i = 0; i < R8_FM; ++i) {
-      const uint4 q = *reinterpret_cast<const uint4*>(&ring_slot<slot>().a[fa_base + sw + 2048 * i]);
-      f.a[i] = v8i{(int)q.x, (int)q.y, (int)q.z, (int)q.w, 0, 0, 0, 0};
+      f.a[i] = *reinterpret_cast<const v4i*>(&ring_slot<slot>().a[fa_base + sw + 2048 * i]);
     }
 #pragma unroll
     for (int j = 0; j < R8_FN; ++j) {
-      const uint4 q = *reinterpret_cast<const uint4*>(&ring_slot<slot>().b[fb_base + sw + 2048 * j]);
-      f.b[j] = v8i{(int)q.x, (int)q.y, (int)q.z, (int)q.w, 0, 0, 0, 0};
+      f.b[j] = *reinterpret_cast<const v4i*>(&ring_slot<slot>().b[fb_base + sw + 2048 * j]);
     }
   };
   // 8 MFMAs of K-step ks: scale byte ks of the 16 bits read.
@@ -612,8 +670,10 @@ __global__ void __launch_bounds__(kRing8Threads, 1) gemm_mx_ring8_kernel(GemmArg
     constexpr int kSel = decltype(KS)::value;
     static_for<R8_FM>([&](auto I) {
       static_for<R8_FN>([&](auto J) {
+        const v4i fb = f.b[J], fa = f.a[I];
         acc[I][J] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-            f.b[J], f.a[I], acc[I][J], 4, 4, kSel, f.sb[J], kSel, f.sa[I]);
+            v8i{fb[0], fb[1], fb[2], fb[3], 0, 0, 0, 0}, v8i{fa[0], fa[1], fa[2], fa[3], 0, 0, 0, 0},
+            acc[I][J], 4, 4, kSel, f.sb[J], kSel, f.sa[I]);
       });
     });
   };
@@ -621,8 +681,8 @@ __global__ void __launch_bounds__(kRing8Threads, 1) gemm_mx_ring8_kernel(GemmArg
   // Stage kt (its K-step 0 fragments in x): read K-step 1 into y during
   // K-step 0's MFMAs; wait until only this wave's 10 loads of stages kt+2,
   // kt+3 are in flight and sync, publishing stage kt+1 and freeing slot kt;
-  // refill it with stage kt+4 (past the end: a re-load of the last stage no
-  // one reads) and read stage kt+1's K-step 0 into x during K-step 1's MFMAs.
+  // refill it with stage kt+4 (past kt1: a re-load of the last stage no one
+  // reads) and read stage kt+1's K-step 0 into x during K-step 1's MFMAs.
   auto stage = [&](auto S, Frags& x, Frags& y, int kt) {
     constexpr int slot = decltype(S)::value;
     read_frags(std::integral_constant<int, slot>{}, std::integral_constant<int, 1>{}, y);
@@ -633,10 +693,11 @@ __global__ void __launch_bounds__(kRing8Threads, 1) gemm_mx_ring8_kernel(GemmArg
     });
     __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
     __builtin_amdgcn_sched_barrier(0);
+    keep(x);
     __builtin_amdgcn_s_waitcnt(waitcnt_imm(2 * kLoads8PerStage, 0));
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
-    issue(std::integral_constant<int, slot>{}, kt + 4 < nk ? kt + 4 : nk - 1);
+    issue(std::integral_constant<int, slot>{}, kt + 4 < kt1 ? kt + 4 : kt1 - 1);
     read_frags(std::integral_constant<int, (slot + 1) % kRingSlots>{}, std::integral_constant<int, 0>{}, x);
     mma(y, std::integral_constant<int, 1>{});
     static_for<5>([&](auto) {
@@ -650,19 +711,20 @@ __global__ void __launch_bounds__(kRing8Threads, 1) gemm_mx_ring8_kernel(GemmArg
     });
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
     __builtin_amdgcn_sched_barrier(0);
+    keep(y);
   };
 
-  issue(std::integral_constant<int, 0>{}, 0);
-  issue(std::integral_constant<int, 1>{}, 1);
-  issue(std::integral_constant<int, 2>{}, 2);
-  issue(std::integral_constant<int, 3>{}, 3);
+  issue(std::integral_constant<int, 0>{}, kt0);
+  issue(std::integral_constant<int, 1>{}, kt0 + 1);
+  issue(std::integral_constant<int, 2>{}, kt0 + 2);
+  issue(std::integral_constant<int, 3>{}, kt0 + 3);
   Frags fx, fy;
   __builtin_amdgcn_s_waitcnt(waitcnt_imm(3 * kLoads8PerStage, 0));
   __builtin_amdgcn_s_barrier();
   __builtin_amdgcn_sched_barrier(0);
   read_frags(std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{}, fx);
-  // nk is a multiple of 4 (K % 512 == 0): one loop exit.
-  for (int kt = 0; kt < nk; kt += kRingSlots) {
+  // kt1 - kt0 is a multiple of 4: one loop exit.
+  for (int kt = kt0; kt < kt1; kt += kRingSlots) {
     stage(std::integral_constant<int, 0>{}, fx, fy, kt);
     stage(std::integral_constant<int, 1>{}, fx, fy, kt + 1);
     stage(std::integral_constant<int, 2>{}, fx, fy, kt + 2);
@@ -674,7 +736,100 @@ __global__ void __launch_bounds__(kRing8Threads, 1) gemm_mx_ring8_kernel(GemmArg
   __builtin_amdgcn_sched_barrier(0);
   __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
   __syncthreads();
-  gemm_finish<R8_FM, R8_FN, R8_WM, R8_WN, 4, kRing8Threads>(g, acc, m0, n0, g_ring_pos);
+  // The inner-extraction term goes into a whole tile or part 0 of a split
+  // one. A part of a split tile then goes out through the same store code,
+  // as a plain fp32 256 x 256 matrix (one code path keeps the accumulators
+  // in registers); the fixup kernel adds the outer-extraction term.
+  if (part <= 0) gemm_inner_term<R8_FM, R8_FN, R8_WM, R8_WN, 4>(g, acc, m0, n0);
+  GemmArgs ge = g;
+  int64_t em0 = m0, en0 = n0;
+  if (part >= 0) {
+    ge.C = g.split_ws + ((size_t)split_tile * g.split_parts + part) * (size_t)(BM * BN);
+    ge.ldc = BN; ge.m = BM; ge.n = BN; ge.out_f32 = 1; ge.vec_ok = 1; ge.oe_mode = 0;
+    em0 = 0; en0 = 0;
+  }
+  gemm_store<R8_FM, R8_FN, R8_WM, R8_WN, 4, kRing8Threads>(ge, acc, em0, en0, g_ring_pos);
+}
+
+// Adds the parts of the split tiles in part order, adds the outer-extraction
+// term (OE_LEFT rows / OE_RIGHT columns) and writes C with one rounding, as
+// the main kernel's epilogue does for a whole tile. Workgroup b takes rows
+// 16 (b % 16) .. +15 of split tile b / 16; thread t columns 4 (t % 64) .. +3
+// of rows t / 64 + 4 i, so every read of a part is a 1 KB row run.
+constexpr int kFixThreads = 256, kFixRows = 16;
+__global__ void __launch_bounds__(kFixThreads) gemm_split_fixup_kernel(GemmArgs g) {
+  __shared__ int s_pos[BM > BN ? BM : BN];
+  const int tile = blockIdx.x / (BM / kFixRows), band = blockIdx.x % (BM / kFixRows);
+  int tm, tn;
+  tile_at(g.split_full + tile, g.tiles_m, g.tiles_n, &tm, &tn);
+  const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
+  const int tid = threadIdx.x;
+  const bool oe_rows = g.oe_mode == ADAHOP_ROUTE_OE_LEFT;
+  const bool oe_cols = g.oe_mode == ADAHOP_ROUTE_OE_RIGHT;
+  bool any_oe = false;
+  if (oe_rows || oe_cols) {
+    const int64_t lo_v = oe_rows ? m0 : n0;
+    const int span = oe_rows ? BM : BN;
+    const int lo = lower_bound_i32(g.oe_idx, g.oe_k, lo_v);
+    const int hi = lower_bound_i32(g.oe_idx, g.oe_k, lo_v + span);
+    any_oe = hi > lo;
+    if (any_oe) {
+      for (int q = tid; q < span; q += kFixThreads) s_pos[q] = -1;
+      __syncthreads();
+      for (int p = lo + tid; p < hi; p += kFixThreads) s_pos[g.oe_idx[p] - lo_v] = p;
+      __syncthreads();
+    }
+  }
+  const int lc = 4 * (tid % 64);
+  const int64_t col = n0 + lc;
+  const float* part0 = g.split_ws + (size_t)tile * g.split_parts * (size_t)(BM * BN);
+#pragma unroll
+  for (int i = 0; i < kFixRows / 4; ++i) {
+    const int lr = band * kFixRows + tid / 64 + 4 * i;
+    const int64_t row = m0 + lr;
+    if (row >= g.m || col >= g.n) continue;
+    float4 a = *reinterpret_cast<const float4*>(part0 + lr * BN + lc);
+    for (int p = 1; p < g.split_parts; ++p) {
+      const float4 b = *reinterpret_cast<const float4*>(part0 + (size_t)p * (BM * BN) + lr * BN + lc);
+      a.x += b.x; a.y += b.y; a.z += b.z; a.w += b.w;
+    }
+    float v[4] = {a.x, a.y, a.z, a.w};
+    if (any_oe) {
+      if (oe_rows) {
+        const int prow = s_pos[lr];
+        if (prow >= 0) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (col + e < g.n) v[e] += g.oe_p[(int64_t)prow * g.n + col + e];
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int p = s_pos[lc + e];
+          if (p >= 0) v[e] += g.oe_p[row * g.oe_k + p];
+        }
+      }
+    }
+    if (col + 4 <= g.n && g.vec_ok) {
+      if (g.out_f32) {
+        *reinterpret_cast<float4*>(static_cast<float*>(g.C) + row * g.ldc + col) =
+            make_float4(v[0], v[1], v[2], v[3]);
+      } else {
+        const uint32_t lo = f32_to_bf16_rne(v[0]) | ((uint32_t)f32_to_bf16_rne(v[1]) << 16);
+        const uint32_t hi = f32_to_bf16_rne(v[2]) | ((uint32_t)f32_to_bf16_rne(v[3]) << 16);
+        *reinterpret_cast<uint2*>(static_cast<uint16_t*>(g.C) + row * g.ldc + col) = make_uint2(lo, hi);
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        if (col + e >= g.n) continue;
+        if (g.out_f32)
+          static_cast<float*>(g.C)[row * g.ldc + col + e] = v[e];
+        else
+          static_cast<uint16_t*>(g.C)[row * g.ldc + col + e] = f32_to_bf16_rne(v[e]);
+      }
+    }
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -946,6 +1101,38 @@ bool ring_shape_ok(int64_t m, int64_t n, int64_t K) {
          (big + kTr - 1) / kTr <= 65535;
 }
 
+// Split of the main kernel's last round. One 512-thread workgroup runs per
+// CU; when the last round would leave more than half of the CUs idle, its
+// tiles are split along K into up to 4 parts (each a multiple of 4 stages
+// and at least 16), which a fixup kernel adds. kSplitCUs is the CU count of
+// a whole gfx950 (MI355X); on a device with fewer CUs the split is only less
+// useful, never wrong.
+constexpr int64_t kSplitCUs = 256;
+struct TailSplit {
+  int64_t full, split;   // whole tiles, split tiles
+  int parts;
+};
+TailSplit tail_split(int64_t m, int64_t n, int64_t K) {
+  const int64_t tiles = ((m + BM - 1) / BM) * ((n + BN - 1) / BN);
+  const int64_t rem = tiles % kSplitCUs, nk = K / 128;
+  int parts = 1;
+  if (rem > 0 && 2 * rem <= kSplitCUs) {
+    parts = (int)(kSplitCUs / rem < 4 ? kSplitCUs / rem : 4);
+    while (parts > 1 && (nk % (4 * parts) != 0 || nk / parts < 16)) --parts;
+  }
+  if (parts < 2) return {tiles, 0, 1};
+  return {tiles - rem, rem, parts};
+}
+
+size_t split_ws_bytes(int64_t m, int64_t n, int64_t K) {
+  const TailSplit ts = tail_split(m, n, K);
+  return (size_t)ts.split * (size_t)ts.parts * (size_t)kSplitPartF4 * sizeof(float4);
+}
+
+size_t staging_bytes(int64_t m, int64_t n, int64_t K) {
+  return align_up((size_t)m * (size_t)(K / 32), kAlign) + align_up((size_t)n * (size_t)(K / 32), kAlign);
+}
+
 }  // namespace
 
 bool gemm_mx_kchunk_ok(int64_t m, int64_t n, int64_t K) {
@@ -953,9 +1140,9 @@ bool gemm_mx_kchunk_ok(int64_t m, int64_t n, int64_t K) {
   return ring_shape_ok(m, n, K) && big * (K / 2) < 0x7FFF0000;   // stage offsets fit 31 bits
 }
 
-size_t gemm_mx_scratch_bytes(int64_t m, int64_t n, int64_t K) {
+size_t gemm_mx_scratch_bytes(int64_t m, int64_t n, int64_t K, int layout) {
   if (m < 1 || n < 1 || !ring_shape_ok(m, n, K)) return 0;
-  return align_up((size_t)m * (size_t)(K / 32), kAlign) + align_up((size_t)n * (size_t)(K / 32), kAlign);
+  return (layout == ADAHOP_LAYOUT_ROWS ? staging_bytes(m, n, K) : 0) + split_ws_bytes(m, n, K);
 }
 
 namespace {
@@ -967,8 +1154,9 @@ bool ring_applies(const uint8_t* a_codes, const uint8_t* a_scales, const uint8_t
 }
 
 adahop_status check_scratch(void* scratch, size_t scratch_bytes, size_t need) {
+  if (need == 0) return ADAHOP_OK;
   if (scratch == nullptr || scratch_bytes < need || (reinterpret_cast<uintptr_t>(scratch) & 15u))
-    return fail(ADAHOP_ERR_WORKSPACE, "gemm_mx: scale staging needs " + std::to_string(need) +
+    return fail(ADAHOP_ERR_WORKSPACE, "gemm_mx: the main kernel needs " + std::to_string(need) +
                                           " bytes of 16-byte aligned workspace");
   return ADAHOP_OK;
 }
@@ -983,7 +1171,8 @@ adahop_status gemm_mx_stage_scales(const uint8_t* a_codes, const uint8_t* a_scal
                                    int64_t n, int64_t K, void* scratch, size_t scratch_bytes,
                                    hipStream_t stream) {
   if (!ring_applies(a_codes, a_scales, b_codes, b_scales, m, n, K)) return ADAHOP_OK;
-  const adahop_status st = check_scratch(scratch, scratch_bytes, gemm_mx_scratch_bytes(m, n, K));
+  const adahop_status st =
+      check_scratch(scratch, scratch_bytes, gemm_mx_scratch_bytes(m, n, K, ADAHOP_LAYOUT_ROWS));
   if (st != ADAHOP_OK) return st;
   const int64_t nst = K / 128, big = m > n ? m : n;
   const dim3 tgrid((unsigned)((nst + kTr - 1) / kTr), (unsigned)((big + kTr - 1) / kTr), 2);
@@ -1011,19 +1200,37 @@ adahop_status gemm_mx_launch(const uint8_t* a_codes, const uint8_t* a_scales,
   g.ib_ptr = oe.b.ptr; g.ib_ld = oe.b.ld; g.ib_inner = oe.b.inner_contiguous;
   const dim3 grid((unsigned)(tiles_m * tiles_n)), block(kGemmThreads);
   const uintptr_t sc_bits = reinterpret_cast<uintptr_t>(a_scales) | reinterpret_cast<uintptr_t>(b_scales);
-  if (layout == ADAHOP_LAYOUT_KCHUNK) {
-    if (!gemm_mx_kchunk_ok(m, n, K) || !ring_applies(a_codes, a_scales, b_codes, b_scales, m, n, K))
-      return fail(ADAHOP_ERR_UNSUPPORTED, "gemm_mx: K-chunked operands need K % 512 == 0 and aligned buffers");
-    g.a_sst = reinterpret_cast<const uint32_t*>(a_scales);
-    g.b_sst = reinterpret_cast<const uint32_t*>(b_scales);
-    gemm_mx_ring8_kernel<true><<<grid, dim3(kRing8Threads), 0, stream>>>(g);
-  } else if (ring_applies(a_codes, a_scales, b_codes, b_scales, m, n, K)) {
-    // The scales were reordered into `scratch` by gemm_mx_stage_scales.
-    const adahop_status st = check_scratch(scratch, scratch_bytes, gemm_mx_scratch_bytes(m, n, K));
+  const bool kchunk = layout == ADAHOP_LAYOUT_KCHUNK;
+  if (kchunk && (!gemm_mx_kchunk_ok(m, n, K) || !ring_applies(a_codes, a_scales, b_codes, b_scales, m, n, K)))
+    return fail(ADAHOP_ERR_UNSUPPORTED, "gemm_mx: K-chunked operands need K % 512 == 0 and aligned buffers");
+  if (kchunk || ring_applies(a_codes, a_scales, b_codes, b_scales, m, n, K)) {
+    const adahop_status st = check_scratch(scratch, scratch_bytes, gemm_mx_scratch_bytes(m, n, K, layout));
     if (st != ADAHOP_OK) return st;
-    g.a_sst = static_cast<const uint32_t*>(scratch);
-    g.b_sst = staged_b(scratch, m, K);
-    gemm_mx_ring8_kernel<false><<<grid, dim3(kRing8Threads), 0, stream>>>(g);
+    if (kchunk) {
+      g.a_sst = reinterpret_cast<const uint32_t*>(a_scales);
+      g.b_sst = reinterpret_cast<const uint32_t*>(b_scales);
+    } else {
+      // The scales were reordered into `scratch` by gemm_mx_stage_scales.
+      g.a_sst = static_cast<const uint32_t*>(scratch);
+      g.b_sst = staged_b(scratch, m, K);
+    }
+    const TailSplit ts = tail_split(m, n, K);
+    g.split_full = (int)ts.full;
+    g.split_parts = ts.parts;
+    g.split_ws = ts.split ? reinterpret_cast<float*>(static_cast<char*>(scratch) +
+                                                     (kchunk ? 0 : staging_bytes(m, n, K)))
+                          : nullptr;
+    const dim3 rgrid((unsigned)(ts.full + ts.split * ts.parts));
+    if (kchunk)
+      gemm_mx_ring8_kernel<true><<<rgrid, dim3(kRing8Threads), 0, stream>>>(g);
+    else
+      gemm_mx_ring8_kernel<false><<<rgrid, dim3(kRing8Threads), 0, stream>>>(g);
+    if (ts.split) {
+      const adahop_status ls = check_launch("gemm_mx");
+      if (ls != ADAHOP_OK) return ls;
+      gemm_split_fixup_kernel<<<dim3((unsigned)(ts.split * (BM / kFixRows))), dim3(kFixThreads), 0,
+                                stream>>>(g);
+    }
   } else if (K % 256 == 0 && (sc_bits & 7u) == 0)
     gemm_mx_kernel<true><<<grid, block, 0, stream>>>(g);
   else

@@ -237,7 +237,7 @@ iht_quant_rowwise_kernel(const uint16_t* __restrict__ src, int64_t rows, int64_t
 // line is written once, by one workgroup. Vec: the rows allow aligned 8-byte
 // loads (ld % 4 == 0, base 8-byte aligned); otherwise loads are per element.
 constexpr int kColThreads = 256;
-constexpr int kColGroups = 16;                 // 4-column groups per workgroup
+constexpr int kColGroups = 64;                 // 4-column groups per workgroup
 constexpr int kColOut = 4 * kColGroups;        // output rows per workgroup
 constexpr int kColBlocks = kColThreads / kColGroups;   // 32-row blocks per workgroup
 constexpr int kColPitch = kColBlocks * 16 + 16;        // LDS bytes per output row (padded)
@@ -328,21 +328,51 @@ iht_quant_colwise_kernel(const uint16_t* __restrict__ src, int64_t K, int64_t ou
   __syncthreads();
 
   if (mine) {
-    // Extracted rows of this block: gathered [nz][outer], zeroed below.
+    // Extracted lines held by this thread: rows of its block (bit j = row
+    // t0 + j) and its own 4 columns (bit q = column c0 + q).
     const uint32_t rmask = s_rmask[bi];
-    if (gathered && rmask) {
-      // Registers are indexed by unrolled constants only.
+    const uint32_t cbits = (s_cmask[(4 * cg) / 32] >> ((4 * cg) % 32)) & 0xFu;
+    // Gather, then clear in the packed words (an extracted element is +0 in
+    // the residual). The test is wave-uniform, so waves holding no extracted
+    // line skip all of it; a per-lane test would be turned into selects on
+    // every word.
+    if (__builtin_amdgcn_ballot_w64((rmask | cbits) != 0) != 0) {
+      if (gathered) {
+        // Rows: gathered [nz][outer]. Registers are indexed by unrolled
+        // constants only.
+#pragma unroll
+        for (int j = 0; j < 32; ++j) {
+          if (!((rmask >> j) & 1u)) continue;
+          const int64_t p = s_rpos[bi * 32 + j];
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            if (c0 + q < outer)
+              gathered[p * outer + c0 + q] = (uint16_t)((w[j][q >> 1] >> (16 * (q & 1))) & 0xFFFFu);
+        }
+        // Columns: gathered [nz][K], this block's 32 values as 64
+        // contiguous bytes.
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          if (!((cbits >> q) & 1u) || c0 + q >= outer) continue;
+          uint32_t pk[16];
+#pragma unroll
+          for (int j = 0; j < 16; ++j)
+            pk[j] = ((w[2 * j][q >> 1] >> (16 * (q & 1))) & 0xFFFFu) |
+                    (((w[2 * j + 1][q >> 1] >> (16 * (q & 1))) & 0xFFFFu) << 16);
+          uint4* g = reinterpret_cast<uint4*>(gathered + (int64_t)s_cpos[4 * cg + q] * K + t0);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) g[j] = make_uint4(pk[4 * j], pk[4 * j + 1], pk[4 * j + 2], pk[4 * j + 3]);
+        }
+      }
+      const uint32_t m0 = ((cbits & 1u) ? 0u : 0x0000FFFFu) | ((cbits & 2u) ? 0u : 0xFFFF0000u);
+      const uint32_t m1 = ((cbits & 4u) ? 0u : 0x0000FFFFu) | ((cbits & 8u) ? 0u : 0xFFFF0000u);
 #pragma unroll
       for (int j = 0; j < 32; ++j) {
-        if (!((rmask >> j) & 1u)) continue;
-        const int64_t p = s_rpos[bi * 32 + j];
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-          if (c0 + q < outer)
-            gathered[p * outer + c0 + q] = (uint16_t)((w[j][q >> 1] >> (16 * (q & 1))) & 0xFFFFu);
+        const bool z = (rmask >> j) & 1u;
+        w[j][0] = z ? 0u : (w[j][0] & m0);
+        w[j][1] = z ? 0u : (w[j][1] & m1);
       }
     }
-
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int64_t c = c0 + q;
@@ -352,27 +382,6 @@ iht_quant_colwise_kernel(const uint16_t* __restrict__ src, int64_t K, int64_t ou
 #pragma unroll
       for (int j = 0; j < 32; ++j)
         y[j] = __uint_as_float((q & 1) ? (w[j][q >> 1] & 0xFFFF0000u) : (w[j][q >> 1] << 16));
-      if (rmask) {
-#pragma unroll
-        for (int j = 0; j < 32; ++j) y[j] = ((rmask >> j) & 1u) ? 0.0f : y[j];
-      }
-      const int cl = 4 * cg + q;
-      if ((s_cmask[cl / 32] >> (cl % 32)) & 1u) {
-        // An extracted column: its 32 values of this block go to gathered
-        // [nz][K] as 64 contiguous bytes; the residual column is zero.
-        if (gathered) {
-          uint32_t pk[16];
-#pragma unroll
-          for (int j = 0; j < 16; ++j)
-            pk[j] = ((w[2 * j][q >> 1] >> (16 * (q & 1))) & 0xFFFFu) |
-                    (((w[2 * j + 1][q >> 1] >> (16 * (q & 1))) & 0xFFFFu) << 16);
-          uint4* g = reinterpret_cast<uint4*>(gathered + (int64_t)s_cpos[cl] * K + t0);
-#pragma unroll
-          for (int j = 0; j < 4; ++j) g[j] = make_uint4(pk[4 * j], pk[4 * j + 1], pk[4 * j + 2], pk[4 * j + 3]);
-        }
-#pragma unroll
-        for (int j = 0; j < 32; ++j) y[j] = 0.0f;
-      }
       if (Had) {
 #pragma unroll
         for (int h = 1; h < 32; h <<= 1) {
@@ -434,12 +443,12 @@ iht_quant_colwise_kernel(const uint16_t* __restrict__ src, int64_t K, int64_t ou
       *reinterpret_cast<uint4*>(codes + (cbase + r) * (K / 2) + (bbase + ch) * 16) =
           *reinterpret_cast<const uint4*>(&s_codes[r * kColPitch + ch * 16]);
   }
-  const bool vec_scales = nb == kColBlocks && nblocks % 16 == 0 &&
-                          (reinterpret_cast<uintptr_t>(scales) & 15u) == 0;
+  const bool vec_scales = nb == kColBlocks && nblocks % kColBlocks == 0 &&
+                          (reinterpret_cast<uintptr_t>(scales) & (kColBlocks - 1)) == 0;
   if (vec_scales) {
     if (tid < nrow)
-      *reinterpret_cast<uint4*>(scales + (cbase + tid) * nblocks + bbase) =
-          *reinterpret_cast<const uint4*>(&s_scales[tid * kColBlocks]);
+      *reinterpret_cast<uint32_t*>(scales + (cbase + tid) * nblocks + bbase) =
+          *reinterpret_cast<const uint32_t*>(&s_scales[tid * kColBlocks]);
   } else {
     for (int i = tid; i < kColOut * kColBlocks; i += kColThreads) {
       const int r = i / kColBlocks, ch = i % kColBlocks;

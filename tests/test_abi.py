@@ -123,6 +123,23 @@ def test_gemm_mx_workspace_size():
     desc = A.OeDesc(A.ROUTE["OE_RIGHT"], 16, 0, A.Bf16View(0, 0, 1, 0), A.Bf16View(0, 0, 1, 0))
     with_oe = lib.adahop_gemm_mx_workspace_size(300, 520, 1024, ctypes.byref(desc))
     assert with_oe > 9728 + 16640 and (with_oe - 9728 - 16640) % 256 == 0
+    # Last round split along K (the round holds at most 128 of the 256 tiles a
+    # full gfx950 runs at once): 256 KB of fp32 per tile part, after the
+    # scale copies. 300 x 520: 6 tiles; K = 4096: 2 parts of 16 stages;
+    # K = 8192: 4 parts; K = 2048: parts would be under 16 stages, no split.
+    split = lambda tiles, parts: tiles * parts * 256 * 256 * 4
+    scales = lambda rows, K: -(-rows * K // 32 // 256) * 256
+    assert lib.adahop_gemm_mx_workspace_size(300, 520, 4096, None) == \
+        scales(300, 4096) + scales(520, 4096) + split(6, 2)
+    assert lib.adahop_gemm_mx_workspace_size(300, 520, 8192, None) == \
+        scales(300, 8192) + scales(520, 8192) + split(6, 4)
+    assert lib.adahop_gemm_mx_workspace_size(300, 520, 2048, None) == scales(300, 2048) + scales(520, 2048)
+    # 896 tiles = 3 full rounds + 128: those 128 split in 2
+    assert lib.adahop_gemm_mx_workspace_size(4096, 14336, 32768, None) == \
+        scales(4096, 32768) + scales(14336, 32768) + split(128, 2)
+    # 1024 tiles fill 4 rounds: no split
+    assert lib.adahop_gemm_mx_workspace_size(4096, 16384, 32768, None) == \
+        scales(4096, 32768) + scales(16384, 32768)
 
 
 def test_plan_layout():

@@ -163,9 +163,12 @@ def packed_operands(rng, m, n, K):
 
 
 # K % 512 == 0 runs the LDS-ring kernel (ragged edges included), other K the
-# register-staged kernel (K tails included).
+# register-staged kernel (K tails included). With few tiles and K of 4096 or
+# more, the ring kernel splits its tiles along K into 2 (300 x 520 x 4096) or
+# 4 (520 x 300 x 8192) parts that the fixup kernel adds.
 GEMM_CASES = [(256, 128, 128), (512, 384, 512), (300, 200, 96), (33, 1000, 160), (1024, 256, 1024),
-              (300, 520, 1024), (77, 1000, 512), (520, 300, 2048), (256, 256, 768)]
+              (300, 520, 1024), (77, 1000, 512), (520, 300, 2048), (256, 256, 768),
+              (300, 520, 4096), (520, 300, 8192)]
 
 
 @pytest.mark.parametrize("m,n,K", GEMM_CASES)
@@ -186,9 +189,11 @@ def test_gemm_mx(m, n, K):
     assert np.array_equal(C16, f32_to_bf16_rne(C32))
 
 
+@pytest.mark.parametrize("K", [256, 4096])
 @pytest.mark.parametrize("route", ["OE_LEFT", "OE_RIGHT", "OE_INNER"])
-def test_gemm_mx_outlier_term(route):
-    m, n, K, k = 320, 192, 256, 12
+def test_gemm_mx_outlier_term(route, K):
+    # K = 4096: two K-halves per tile, the outlier term added once by the fixup.
+    m, n, k = 320, 192, 12
     rng = np.random.default_rng(5)
     a, b, ac, as_, bc, bs = packed_operands(rng, m, n, K)
     ref, absC = oracle.gemm_mx(ac, as_, bc, bs)
@@ -212,7 +217,7 @@ def test_gemm_mx_outlier_term(route):
         ref += oe_ref; absC += oe_abs
         oe = {"route": route, "k": k, "a": (dev_bf16(ga), True), "b": (dev_bf16(gb), True)}
     d = [torch.from_numpy(x).to(DEV) for x in (ac, as_, bc, bs)]
-    say("gemm_mx outlier", route)
+    say("gemm_mx outlier", route, K)
     c32 = A.adahop_gemm_mx(*d, oe=oe, out_dtype=torch.float32)
     c16 = A.adahop_gemm_mx(*d, oe=oe, out_dtype=torch.bfloat16)
     torch.cuda.synchronize()
@@ -288,6 +293,9 @@ FULL_CASES = [
     ("WGRAD", 1024, 200, 72, "R", "C", None, 8),        # OE_RIGHT, both down columns
     ("WGRAD", 512, 96, 160, "C", "N", None, 8),         # OE_LEFT (GY columns)
     ("DGRAD", 300, 264, 1536, "N", "N", None, 64),      # IHT, ragged tiles
+    # few tiles, long K: the main kernel splits each tile along K
+    ("WGRAD", 4096, 200, 300, "R", "C", None, 8),       # OE_RIGHT, 2 parts
+    ("FWD", 256, 8192, 520, "C", "N", "OE_INNER", 16),  # inner term, 4 parts
 ]
 
 
@@ -299,7 +307,8 @@ def test_full_product(case):
 
 
 def test_deterministic_reruns():
-    op, T, Din, Dout = "WGRAD", 1024, 768, 512
+    # K = 4096 over 6 tiles: the K-split path, whose parts are added in order.
+    op, T, Din, Dout = "WGRAD", 4096, 768, 512
     lhs, rhs = operands(op, T, Din, Dout, "R", "C", 3)
     L, R = dev_bf16(lhs), dev_bf16(rhs)
     say("determinism")
