@@ -10,16 +10,19 @@
 //   per lane = per 32-element K block). Lane l of a wave supplies row l%32 of
 //   the 32x64 A block (B: column l%32), K half l/32: 16 bytes of packed codes,
 //   exactly one 32-element MX block, plus that block's scale byte.
-// Tiling: a workgroup of 4 waves computes a 256 x 256 tile of C; each wave a
-//   128 x 128 sub-tile (4 x 4 MFMA blocks, 256 fp32 accumulators per lane,
-//   held in the accumulation registers). Workgroup ids are remapped so that
-//   each XCD works through a contiguous range of tiles, 4 tile-rows high,
-//   whose operand rows its L2 shares.
+// Tiling: a workgroup computes a 256 x 256 tile of C: in the main kernel 8
+//   waves of 128 x 64 (4 x 2 MFMA blocks, 128 fp32 accumulators per lane),
+//   two per SIMD; in the fallback kernel 4 waves of 128 x 128. Workgroup ids
+//   are remapped so that each XCD works through a contiguous range of tiles,
+//   4 tile-rows high, whose operand rows its L2 shares.
 // Main kernel (gemm_mx_ring8_kernel, K % 512 == 0): K advances 128 elements
 //   per stage through a 4-slot LDS ring filled by direct global->LDS buffer
-//   loads four stages ahead; the scales come from a stage-major copy made
-//   just before (scale_stage_kernel). Other K: gemm_mx_kernel, 256-element
-//   stages double buffered in LDS with register-staged buffer loads.
+//   loads four stages ahead; the scales come K-chunked from the quantizers
+//   or from a stage-major copy made just before (scale_stage_kernel). One
+//   workgroup runs per CU; a last round of tiles that would leave more than
+//   half of the 256 CUs idle is split along K, and gemm_split_fixup_kernel
+//   adds the parts. Other K: gemm_mx_kernel, 256-element stages double
+//   buffered in LDS with register-staged buffer loads.
 // Outlier product: bf16 matrix cores (v_mfma_f32_32x32x16_bf16), 128 x 64
 //   tiles, K split across workgroups into fp32 partials that a small kernel
 //   sums in a fixed order; the FP4 kernel's epilogue adds a line's reduced

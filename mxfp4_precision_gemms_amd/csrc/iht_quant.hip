@@ -227,15 +227,16 @@ iht_quant_rowwise_kernel(const uint16_t* __restrict__ src, int64_t rows, int64_t
   }
 }
 
-// contract ROWS: a 256-thread workgroup owns 64 output rows (columns of the
-// source) x 16 blocks of 32 contraction positions. Thread t takes the 4
-// adjacent columns 4 (t % 16) .. +3 of block t / 16: each of the block's 32
-// rows is one 8-byte load (16 lanes read 128 contiguous bytes), and the
-// columns are rotated and quantized one after another from registers. Codes
-// and scales go to LDS first, then out as whole row segments: 256 code bytes
-// (16 lanes x 16 bytes) and 16 scale bytes per output row, so every 128-byte
-// line is written once, by one workgroup. Vec: the rows allow aligned 8-byte
-// loads (ld % 4 == 0, base 8-byte aligned); otherwise loads are per element.
+// contract ROWS: a 256-thread workgroup owns 256 output rows (columns of the
+// source) x 4 blocks of 32 contraction positions, one block per wave. Thread
+// t takes the 4 adjacent columns 4 (t % 64) .. +3 of block t / 64: each of
+// the block's 32 rows is one 8-byte load (a wave reads 512 contiguous bytes
+// of a row), and the columns are rotated and quantized one after another
+// from registers. Codes and scales go to LDS first, then out as whole
+// segments: K-chunked, the tile's 128 contraction positions are one chunk,
+// 256 rows x 64 bytes contiguous; row-major, 64 code bytes and 4 scale bytes
+// per output row. Vec: the rows allow aligned 8-byte loads (ld % 4 == 0,
+// base 8-byte aligned); otherwise loads are per element.
 constexpr int kColThreads = 256;
 constexpr int kColGroups = 64;                 // 4-column groups per workgroup
 constexpr int kColOut = 4 * kColGroups;        // output rows per workgroup
