@@ -239,6 +239,13 @@ def main():
                    "out_dtype": args.out_dtype},
         "pct_mxfp4_peak": round(100 * value / PEAK_FP4_TFLOPS, 2),
         "stages_ms": {k: round(v, 4) for k, v in stage_ms.items()},
+        "stages_note": ("the operand FOID does not scan is quantized on a second stream, beside "
+                        "FOID, the other quantization and the outlier product: its slot is empty "
+                        "and the other slots overlap it; gemm is the MFMA kernel plus, when its "
+                        "last round is split along K, the fixup kernel")
+                       if route in ("OE_LEFT", "OE_RIGHT") else
+                       ("gemm is the MFMA kernel plus, when its last round is split along K, "
+                        "the fixup kernel"),
         "call_ms_events": round(call_ms, 4),
         "roofline": {"bound": "mfma",
                      "kernel": "gemm_mx_ring8_kernel (FP4 MFMA GEMM, fused scatter-add epilogue)",

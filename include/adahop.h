@@ -44,6 +44,12 @@
  *     unspecified). Outputs must not alias inputs.
  *   - Thread safety: calls on different streams may run concurrently;
  *     adahop_last_error() is per host thread.
+ *   - adahop_gemm with OE_LEFT or OE_RIGHT quantizes the operand FOID does
+ *     not scan on a second stream the library creates once per device
+ *     (default priority), forked from `stream` with an event and joined back
+ *     before the GEMM, so that it runs beside FOID, the other quantization
+ *     and the outlier product; the call's completion stays ordered on
+ *     `stream`.
  */
 #ifndef ADAHOP_H
 #define ADAHOP_H
@@ -272,7 +278,10 @@ ADAHOP_API adahop_status adahop_gemm(adahop_op op, const uint16_t* lhs, const ui
  * `stream` before the first launch and events[1..5] after the FOID, lhs
  * quantization, rhs quantization (which ends with reordering both scale
  * arrays for the GEMM), outlier product and GEMM stages (a stage
- * that does not run records its event right after the previous one). */
+ * that does not run records its event right after the previous one). With
+ * OE_LEFT and OE_RIGHT the operand FOID does not scan is quantized on a
+ * second stream: its stage is empty here, the ROWS-layout scale reordering
+ * falls in the GEMM stage, and the other stages overlap with it. */
 #define ADAHOP_STAGE_EVENTS 6
 ADAHOP_API adahop_status adahop_gemm_timed(adahop_op op, const uint16_t* lhs,
                                            const uint16_t* rhs, int64_t T, int64_t Din,

@@ -3,6 +3,7 @@
 // launch; the library never allocates or synchronizes.
 #include <climits>
 #include <cstring>
+#include <mutex>
 #include <string>
 
 #include "adahop_internal.h"
@@ -189,6 +190,41 @@ struct Events {
     if (_st != ADAHOP_OK) return _st;      \
   } while (0)
 
+// A second stream per device, for the quantization of the operand FOID does
+// not scan, beside FOID (latency-bound, few CUs) and the stages after it.
+// Created once per device at the default priority; `mu` is held from the
+// fork to the join, so that concurrent calls on one device do not re-record
+// the two events in between.
+struct SideStream {
+  std::mutex mu;
+  hipStream_t stream = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+  bool tried = false;
+};
+constexpr int kMaxDevices = 64;
+SideStream g_side[kMaxDevices];
+
+// The current device's side stream, or nullptr if it cannot be had (the
+// stages then run one after another on the caller's stream). Call with
+// g_side[dev].mu held.
+SideStream* side_stream_locked(int dev) {
+  SideStream& ss = g_side[dev];
+  if (!ss.tried) {
+    ss.tried = true;
+    if (hipStreamCreateWithFlags(&ss.stream, hipStreamNonBlocking) != hipSuccess ||
+        hipEventCreateWithFlags(&ss.fork, hipEventDisableTiming) != hipSuccess ||
+        hipEventCreateWithFlags(&ss.join, hipEventDisableTiming) != hipSuccess) {
+      (void)hipGetLastError();
+      ss.stream = nullptr;
+    }
+  }
+  return ss.stream ? &ss : nullptr;
+}
+
+adahop_status hip_ok(hipError_t e, const char* what) {
+  return e == hipSuccess ? ADAHOP_OK : fail(ADAHOP_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+
 adahop_status run_gemm(adahop_op op, const uint16_t* lhs, const uint16_t* rhs, int64_t T,
                        int64_t Din, int64_t Dout, adahop_pattern pat_lhs,
                        adahop_pattern pat_rhs, adahop_route_t route, int32_t oe_rank,
@@ -227,13 +263,6 @@ adahop_status run_gemm(adahop_op op, const uint16_t* lhs, const uint16_t* rhs, i
 
   char* w = static_cast<char*>(ws);
   int32_t* idx = pb.off_idx != kNone ? reinterpret_cast<int32_t*>(w + pb.off_idx) : nullptr;
-  if (idx) {
-    const bool l = pb.scan_tensor == 0;
-    ADAHOP_TRY(foid_launch(l ? lhs : rhs, l ? s.lhs_rows : s.rhs_rows, l ? s.lhs_cols : s.rhs_cols,
-                           l ? s.lhs_cols : s.rhs_cols, pb.scan_axis, 64, pb.k, idx,
-                           P.off_foid != kNone ? w + P.off_foid : nullptr, P.foid_bytes, stream));
-  }
-  ADAHOP_TRY(E.record(1));
   const int had = pb.route == ADAHOP_ROUTE_MXFP4 ? 0 : 32;
   uint8_t* ac = reinterpret_cast<uint8_t*>(w + pb.off_a_codes);
   uint8_t* as = reinterpret_cast<uint8_t*>(w + pb.off_a_scales);
@@ -241,17 +270,68 @@ adahop_status run_gemm(adahop_op op, const uint16_t* lhs, const uint16_t* rhs, i
   uint8_t* bs = reinterpret_cast<uint8_t*>(w + pb.off_b_scales);
   uint16_t* ll = pb.off_lhs_lines != kNone ? reinterpret_cast<uint16_t*>(w + pb.off_lhs_lines) : nullptr;
   uint16_t* rl = pb.off_rhs_lines != kNone ? reinterpret_cast<uint16_t*>(w + pb.off_rhs_lines) : nullptr;
-  ADAHOP_TRY(iht_quant_launch(lhs, s.lhs_rows, s.lhs_cols, s.lhs_cols, s.lhs_contract, had,
-                              P.zero_lhs ? idx : nullptr, P.zero_lhs ? pb.k : 0, P.lhs_zero_axis,
-                              ac, as, ll, pb.layout, stream));
-  ADAHOP_TRY(E.record(2));
-  ADAHOP_TRY(iht_quant_launch(rhs, s.rhs_rows, s.rhs_cols, s.rhs_cols, s.rhs_contract, had,
-                              P.zero_rhs ? idx : nullptr, P.zero_rhs ? pb.k : 0, P.rhs_zero_axis,
-                              bc, bs, rl, pb.layout, stream));
+  const bool scan_lhs = pb.scan_tensor == 0;
+  auto foid = [&](hipStream_t st) {
+    return foid_launch(scan_lhs ? lhs : rhs, scan_lhs ? s.lhs_rows : s.rhs_rows,
+                       scan_lhs ? s.lhs_cols : s.rhs_cols, scan_lhs ? s.lhs_cols : s.rhs_cols,
+                       pb.scan_axis, 64, pb.k, idx, P.off_foid != kNone ? w + P.off_foid : nullptr,
+                       P.foid_bytes, st);
+  };
+  auto quant_lhs = [&](hipStream_t st) {
+    return iht_quant_launch(lhs, s.lhs_rows, s.lhs_cols, s.lhs_cols, s.lhs_contract, had,
+                            P.zero_lhs ? idx : nullptr, P.zero_lhs ? pb.k : 0, P.lhs_zero_axis,
+                            ac, as, ll, pb.layout, st);
+  };
+  auto quant_rhs = [&](hipStream_t st) {
+    return iht_quant_launch(rhs, s.rhs_rows, s.rhs_cols, s.rhs_cols, s.rhs_contract, had,
+                            P.zero_rhs ? idx : nullptr, P.zero_rhs ? pb.k : 0, P.rhs_zero_axis,
+                            bc, bs, rl, pb.layout, st);
+  };
+  // OE_LEFT / OE_RIGHT zero lines of the scanned operand only, and only the
+  // GEMM reads the other operand's packed form: that operand is quantized on
+  // the side stream while FOID, the scanned operand's quantization and the
+  // outlier product run on the caller's stream; the join comes right before
+  // the GEMM (and the ROWS-layout scale reordering).
+  std::unique_lock<std::mutex> side_lock;
+  SideStream* side = nullptr;
+  if (idx && (scan_lhs ? !P.zero_rhs : !P.zero_lhs)) {
+    int dev = 0;
+    if (hipGetDevice(&dev) == hipSuccess && dev >= 0 && dev < kMaxDevices) {
+      side_lock = std::unique_lock<std::mutex>(g_side[dev].mu);
+      side = side_stream_locked(dev);
+      if (!side) side_lock.unlock();
+    }
+  }
+  if (side) {
+    ADAHOP_TRY(hip_ok(hipEventRecord(side->fork, stream), "hipEventRecord"));
+    ADAHOP_TRY(hip_ok(hipStreamWaitEvent(side->stream, side->fork, 0), "hipStreamWaitEvent"));
+    ADAHOP_TRY(scan_lhs ? quant_rhs(side->stream) : quant_lhs(side->stream));
+    ADAHOP_TRY(hip_ok(hipEventRecord(side->join, side->stream), "hipEventRecord"));
+    ADAHOP_TRY(foid(stream));
+    ADAHOP_TRY(E.record(1));
+    // The other operand's stage is empty on this stream.
+    if (scan_lhs) {
+      ADAHOP_TRY(quant_lhs(stream));
+      ADAHOP_TRY(E.record(2));
+      ADAHOP_TRY(E.record(3));
+    } else {
+      ADAHOP_TRY(E.record(2));
+      ADAHOP_TRY(quant_rhs(stream));
+      ADAHOP_TRY(E.record(3));
+    }
+  } else {
+    if (idx) ADAHOP_TRY(foid(stream));
+    ADAHOP_TRY(E.record(1));
+    ADAHOP_TRY(quant_lhs(stream));
+    ADAHOP_TRY(E.record(2));
+    ADAHOP_TRY(quant_rhs(stream));
+  }
   void* gemm_scratch = P.off_gemm != kNone ? w + P.off_gemm : nullptr;
-  if (pb.layout == ADAHOP_LAYOUT_ROWS)
-    ADAHOP_TRY(gemm_mx_stage_scales(ac, as, bc, bs, s.m, s.n, s.K, gemm_scratch, P.gemm_bytes, stream));
-  ADAHOP_TRY(E.record(3));
+  if (!side) {
+    if (pb.layout == ADAHOP_LAYOUT_ROWS)
+      ADAHOP_TRY(gemm_mx_stage_scales(ac, as, bc, bs, s.m, s.n, s.K, gemm_scratch, P.gemm_bytes, stream));
+    ADAHOP_TRY(E.record(3));
+  }
 
   OeEpilogue oe{};
   oe.mode = 0;
@@ -281,6 +361,12 @@ adahop_status run_gemm(adahop_op op, const uint16_t* lhs, const uint16_t* rhs, i
     oe.b = lines_by_position(rl, line_len(s, false, P.rhs_zero_axis)); // (j, p)
   }
   ADAHOP_TRY(E.record(4));
+  if (side) {
+    ADAHOP_TRY(hip_ok(hipStreamWaitEvent(stream, side->join, 0), "hipStreamWaitEvent"));
+    side_lock.unlock();
+    if (pb.layout == ADAHOP_LAYOUT_ROWS)
+      ADAHOP_TRY(gemm_mx_stage_scales(ac, as, bc, bs, s.m, s.n, s.K, gemm_scratch, P.gemm_bytes, stream));
+  }
   ADAHOP_TRY(gemm_mx_launch(ac, as, bc, bs, s.m, s.n, s.K, pb.layout, oe, out, s.n, out_f32,
                             gemm_scratch, P.gemm_bytes, stream));
   return E.record(5);
