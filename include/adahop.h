@@ -130,7 +130,10 @@ ADAHOP_API adahop_route_t adahop_route(adahop_op op, adahop_pattern pat_lhs,
  * index order (sum, mean, then sum of squared deviations). The k candidates
  * with the largest score (ties: lower index first) are written to idx_out
  * (device int32[k]) in ascending order. Deterministic. Needs
- * adahop_detect_workspace_size(...) bytes of workspace.
+ * adahop_detect_workspace_size(...) bytes of workspace: none up to 1024
+ * candidates (4096 when k > 256), else the survivor lists of the selection
+ * levels (k scores and indices per chunk of 1024, or 4096, candidates; two
+ * lists) and 256 bytes for a counter; ws may be NULL when the size is 0.
  * Errors: INVALID if t/idx_out is NULL, rows/cols < 1, ld < cols, probe < 1,
  * k < 1 or k > number of candidates; UNSUPPORTED if k > 1024. */
 ADAHOP_API size_t adahop_detect_workspace_size(int64_t rows, int64_t cols, adahop_axis axis,

@@ -191,7 +191,7 @@ struct Events {
   } while (0)
 
 // A second stream per device, for the quantization of the operand FOID does
-// not scan, beside FOID (latency-bound, few CUs) and the stages after it.
+// not scan, beside FOID and the stages after it.
 // Created once per device at the default priority; `mu` is held from the
 // fork to the join, so that concurrent calls on one device do not re-record
 // the two events in between.
@@ -303,6 +303,9 @@ adahop_status run_gemm(adahop_op op, const uint16_t* lhs, const uint16_t* rhs, i
     }
   }
   if (side) {
+    // Forked before FOID: FOID (latency-bound, few workgroups) runs beside
+    // the other operand's quantization, and the scanned operand's
+    // quantization after it overlaps that quantization's tail.
     ADAHOP_TRY(hip_ok(hipEventRecord(side->fork, stream), "hipEventRecord"));
     ADAHOP_TRY(hip_ok(hipStreamWaitEvent(side->stream, side->fork, 0), "hipStreamWaitEvent"));
     ADAHOP_TRY(scan_lhs ? quant_rhs(side->stream) : quant_lhs(side->stream));

@@ -10,19 +10,18 @@
 // are read coalesced (consecutive lanes = consecutive columns); a candidate
 // row is one 128-byte run, read as 8 16-byte loads when aligned. With the
 // full 64-element probe the values stay in registers between the two passes.
+// The first selection level computes the scores itself, in registers.
 //
 // Selection without a host round trip and without atomics, by radix select
-// on the fp64 score bits (scores are >= 0, so their bit patterns order like
-// the values): a workgroup holds 4 or 16 scores per thread in registers, and
-// 16 passes of 4-bit digits (per-thread packed counters, wave and workgroup
-// sums) narrow down the k-th largest score; once the digit bin holding it has
-// at most 256 scores, those are ranked exactly one against all. Every score above T
-// is kept, and of the scores equal to T the ones with the lowest indices --
-// the key (score descending, index ascending) is a strict total order, so
-// the result is unique. A prefix sum over the threads, which own the
-// candidates in index order, writes the kept indices already sorted. Levels
-// of many workgroups first cut every chunk of 1024 candidates (4096 when
-// k > 256) to its best k, until one workgroup can take the rest.
+// on the fp64 score bits (see foid_select_kernel): 512-thread workgroups,
+// digit counts by wave ballots, one barrier per 4-bit digit. Every score
+// above the k-th largest, T, is kept, and of the scores equal to T the ones
+// with the lowest indices -- the key (score descending, index ascending) is
+// a strict total order, so the result is unique. A prefix sum over the
+// threads, which own the candidates in index order, writes the kept indices
+// already sorted. Levels of many workgroups first cut every chunk of 1024
+// candidates (4096 when k > 256) to its best k, until one workgroup can take
+// the rest.
 #include <climits>
 
 #include "adahop_internal.h"
@@ -32,20 +31,18 @@
 namespace adahop {
 namespace {
 
-constexpr int kVarThreads = 256;
 constexpr int kProbe = 64;
-
 
 __device__ __forceinline__ double bf16_to_f64(uint32_t h) {
   return (double)__uint_as_float(h << 16);
 }
 
-// Variance of candidate lines; var[l] for l < ncand.
-__global__ void __launch_bounds__(kVarThreads)
-foid_var_kernel(const uint16_t* __restrict__ t, int64_t ld, int axis, int P, int64_t ncand,
-                double* __restrict__ var) {
-  const int64_t l = (int64_t)blockIdx.x * kVarThreads + threadIdx.x;
-  if (l >= ncand) return;
+// Variance of candidate line l over its first P elements: fp64, two passes
+// in index order (sum -> mean -> sum of squared deviations), each operation
+// separately rounded.
+// Out of line: the selection kernel calls it only off its fast path.
+__device__ __attribute__((noinline)) double candidate_variance(const uint16_t* __restrict__ t, int64_t ld, int axis, int P,
+                                     int64_t l) {
   if (P == kProbe) {
     // Values in registers: 32 dwords of bf16 pairs.
     uint32_t w[kProbe / 2];
@@ -73,8 +70,7 @@ foid_var_kernel(const uint16_t* __restrict__ t, int64_t ld, int axis, int P, int
       const double d = bf16_to_f64((w[i / 2] >> (16 * (i & 1))) & 0xFFFFu) - mean;
       ss += d * d;
     }
-    var[l] = ss / (double)kProbe;
-    return;
+    return ss / (double)kProbe;
   }
   double sum = 0.0;
   for (int i = 0; i < P; ++i)
@@ -86,11 +82,71 @@ foid_var_kernel(const uint16_t* __restrict__ t, int64_t ld, int axis, int P, int
         bf16_to_f64(axis == ADAHOP_AXIS_ROWS ? t[l * ld + i] : t[(int64_t)i * ld + l]) - mean;
     ss += d * d;
   }
-  var[l] = ss / (double)P;
+  return ss / (double)P;
 }
 
-constexpr int kSelThreads = 256;
-constexpr int kExact = 256;   // a digit bin this small is ranked exactly
+// Scores of the two adjacent candidates c, c + 1 with the full 64-element
+// probe. Columns: each row is one 4-byte load holding both, so a wave reads
+// 256 contiguous bytes per row; rows: 8 16-byte loads per row. Same
+// operations, in the same order, as candidate_variance.
+// `fence` marks the packed words as changed between the two passes, so the
+// 128 fp64 conversions are redone rather than kept live in registers.
+template <typename Lo, typename Hi, typename Fence>
+__device__ __forceinline__ void pair_stats(Lo lo, Hi hi, Fence fence, double* v0, double* v1) {
+  double s0 = 0.0, s1 = 0.0;
+#pragma unroll
+  for (int i = 0; i < kProbe; ++i) {
+    s0 += bf16_to_f64(lo(i));
+    s1 += bf16_to_f64(hi(i));
+  }
+  fence();
+  const double m0 = s0 / (double)kProbe, m1 = s1 / (double)kProbe;
+  double q0 = 0.0, q1 = 0.0;
+#pragma unroll
+  for (int i = 0; i < kProbe; ++i) {
+    const double d0 = bf16_to_f64(lo(i)) - m0;
+    const double d1 = bf16_to_f64(hi(i)) - m1;
+    q0 += d0 * d0;
+    q1 += d1 * d1;
+  }
+  *v0 = q0 / (double)kProbe;
+  *v1 = q1 / (double)kProbe;
+}
+
+__device__ __forceinline__ void pair_variance(const uint16_t* __restrict__ t, int64_t ld, int axis,
+                                              int64_t c, double* v0, double* v1) {
+  if (axis == ADAHOP_AXIS_COLS) {
+    uint32_t w[kProbe];
+    const uint32_t* p = reinterpret_cast<const uint32_t*>(t + c);
+#pragma unroll
+    for (int i = 0; i < kProbe; ++i) w[i] = p[(int64_t)i * (ld / 2)];
+    pair_stats([&](int i) { return w[i] & 0xFFFFu; }, [&](int i) { return w[i] >> 16; },
+               [&]() {
+#pragma unroll
+                 for (int i = 0; i < kProbe; ++i) asm volatile("" : "+v"(w[i]));
+               },
+               v0, v1);
+  } else {
+    uint32_t r0[kProbe / 2], r1[kProbe / 2];
+#pragma unroll
+    for (int q = 0; q < kProbe / 8; ++q) {
+      const uint4 a = *reinterpret_cast<const uint4*>(t + c * ld + 8 * q);
+      const uint4 b = *reinterpret_cast<const uint4*>(t + (c + 1) * ld + 8 * q);
+      r0[4 * q] = a.x; r0[4 * q + 1] = a.y; r0[4 * q + 2] = a.z; r0[4 * q + 3] = a.w;
+      r1[4 * q] = b.x; r1[4 * q + 1] = b.y; r1[4 * q + 2] = b.z; r1[4 * q + 3] = b.w;
+    }
+    pair_stats([&](int i) { return (r0[i / 2] >> (16 * (i & 1))) & 0xFFFFu; },
+               [&](int i) { return (r1[i / 2] >> (16 * (i & 1))) & 0xFFFFu; },
+               [&]() {
+#pragma unroll
+                 for (int i = 0; i < kProbe / 2; ++i) asm volatile("" : "+v"(r0[i]), "+v"(r1[i]));
+               },
+               v0, v1);
+  }
+}
+
+constexpr int kSelThreads = 512;
+constexpr int kSelWaves = kSelThreads / 64;
 
 // Exclusive prefix sum of v over the workgroup's threads in order; *total
 // receives the sum. Uses s_tmp[THREADS / 64].
@@ -117,208 +173,207 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* s_tmp, int* tota
   return before + x - v;
 }
 
-// One selection over entries (in_var[i], in_idx ? in_idx[i] : i), i < count,
-// in chunks of THREADS * KPT per workgroup (KPT entries per thread); entries
-// with a negative score are padding. Non-final: the chunk's best k entries (all of them if it has
-// fewer, then padding) go to out_var/out_idx + blockIdx.x * k in index order.
-// Final (one workgroup): the best k indices go to final_idx in ascending
-// order (k <= the number of real entries, checked on the host).
-template <int THREADS, int KPT>
-__global__ void __launch_bounds__(THREADS)
-foid_select_kernel(const double* __restrict__ in_var, const int32_t* __restrict__ in_idx,
-                   int64_t count, int k, double* __restrict__ out_var,
-                   int32_t* __restrict__ out_idx, int32_t* __restrict__ final_idx) {
-  constexpr int kWaves = THREADS / 64;
-  __shared__ uint32_t s_cnt[kWaves][16];
-  __shared__ uint32_t s_tot[16];
-  __shared__ uint64_t s_ekey[kExact];
-  __shared__ int s_epos[kExact];
-  __shared__ uint8_t s_esel[kExact];
-  __shared__ int s_tmp[kWaves];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int64_t first = (int64_t)blockIdx.x * THREADS * KPT + (int64_t)tid * KPT;
+// Inputs of one selection. Level 0 (t != nullptr) scores candidate lines
+// [0, count) itself; later levels read (in_var[i], in_idx[i]), i < count,
+// where a negative score is padding.
+struct SelectArgs {
+  const uint16_t* t; int64_t ld; int axis; int P;
+  const double* in_var; const int32_t* in_idx;
+  int64_t count;
+  int k;
+  double* out_var; int32_t* out_idx;   // non-final: k entries per workgroup
+  int32_t* final_idx;                  // final (one workgroup): the k indices, ascending
+};
 
+// Selection over chunks of 512 * KPT entries per workgroup, thread t owning
+// entries 512 * KPT * b + KPT t .. + KPT - 1 in index order. Radix select
+// on the fp64 score bits (scores are >= 0, so their bit patterns order like
+// the values), 4 bits per pass from the top: lane d of every wave counts the
+// wave's keys in the current bin whose next digit is d (one ballot per digit
+// and key slot), one barrier publishes the 16 x 16 counts, and every wave
+// sums them and picks the digit of the krem-th largest key itself. The pass
+// loop ends once the chosen bin holds exactly the keys still needed (all of
+// them kept), else after 16 passes with T, the k-th largest key: every key
+// above T is kept and, of the keys equal to T, the ones with the lowest
+// indices -- the key (score descending, index ascending) is a strict total
+// order, so the result is unique. A prefix sum over the threads writes the
+// kept entries already sorted by index.
+template <int KPT>
+__device__ __forceinline__ void select_block(const SelectArgs& a, int block,
+                                             uint32_t (*s_cnt)[kSelWaves][16], int* s_tmp) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t first = (int64_t)block * kSelThreads * KPT + (int64_t)tid * KPT;
+
+  double v[KPT];
+  const bool pair = KPT == 2 && a.t && a.P == kProbe && first + 1 < a.count &&
+                    (a.axis == ADAHOP_AXIS_COLS
+                         ? (a.ld & 1) == 0 && (reinterpret_cast<uintptr_t>(a.t) & 3) == 0
+                         : (a.ld & 7) == 0 && (reinterpret_cast<uintptr_t>(a.t) & 15) == 0);
+  if (pair) {
+    pair_variance(a.t, a.ld, a.axis, first, &v[0], &v[KPT - 1]);
+  } else {
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) {
+      const int64_t g = first + j;
+      v[j] = -1.0;
+      if (g < a.count) v[j] = a.t ? candidate_variance(a.t, a.ld, a.axis, a.P, g) : a.in_var[g];
+    }
+  }
   uint64_t key[KPT];
   uint32_t valid = 0;
 #pragma unroll
   for (int j = 0; j < KPT; ++j) {
-    const int64_t g = first + j;
-    const double v = g < count ? in_var[g] : -1.0;
-    key[j] = (uint64_t)__double_as_longlong(v);
-    valid |= (v >= 0.0 ? 1u : 0u) << j;
+    key[j] = (uint64_t)__double_as_longlong(v[j]);
+    valid |= (v[j] >= 0.0 ? 1u : 0u) << j;
   }
-  int nvalid;
-  block_exclusive_scan<THREADS>(__popc(valid), s_tmp, &nvalid);
 
-  // T = the k-th largest key; krem = how many keys equal to T are kept.
   uint64_t prefix = 0, pmask = 0;
-  int krem = k;
-  bool exact = false;   // the k-th key's bin, once small, is ranked exactly
-  if (nvalid > k) {
-    for (int pass = 0; pass < 16; ++pass) {
-      const int shift = 60 - 4 * pass;
-        uint64_t c[4] = {0, 0, 0, 0};   // 16 counters of 16 bits: digit d in c[d / 4]
+  int krem = a.k;
+  bool keep_all = false, bin_kept = false;
+  for (int pass = 0; pass < 16; ++pass) {
+    const int shift = 60 - 4 * pass;
+    // Per key: in the current bin?, and its next digit; then per digit one
+    // compare into a lane mask, ANDed with the bin mask and counted.
+    uint64_t inb[KPT];
+    uint32_t dig[KPT];
 #pragma unroll
-      for (int j = 0; j < KPT; ++j) {
-        const bool in = ((valid >> j) & 1u) && (key[j] & pmask) == prefix;
-        const int d = (int)((key[j] >> shift) & 15u);
-        const uint64_t inc = in ? (1ull << (16 * (d & 3))) : 0ull;
-        c[0] += (d >> 2) == 0 ? inc : 0ull;
-        c[1] += (d >> 2) == 1 ? inc : 0ull;
-        c[2] += (d >> 2) == 2 ? inc : 0ull;
-        c[3] += (d >> 2) == 3 ? inc : 0ull;
-      }
-#pragma unroll
-      for (int off = 32; off >= 1; off >>= 1) {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) c[q] += __shfl_xor(c[q], off);
-      }
-      if (lane == 0) {
-#pragma unroll
-        for (int d = 0; d < 16; ++d) s_cnt[wave][d] = (uint32_t)((c[d >> 2] >> (16 * (d & 3))) & 0xFFFFu);
-      }
-      __syncthreads();
-      if (tid < 16) {
-        uint32_t t = 0;
-        for (int w = 0; w < kWaves; ++w) t += s_cnt[w][tid];
-        s_tot[tid] = t;
-      }
-      __syncthreads();
-      // The digit of the k-th largest key among those matching the prefix.
-      int cum = 0, dsel = 0;
-      bool found = false;
-#pragma unroll
-      for (int d = 15; d >= 0; --d) {
-        const int t = (int)s_tot[d];
-        if (!found) {
-          if (cum + t >= krem) { dsel = d; found = true; } else { cum += t; }
-        }
-      }
-      krem -= cum;
-      prefix |= (uint64_t)dsel << shift;
-      pmask |= 15ull << shift;
-      const int m = (int)s_tot[dsel];     // keys in the chosen bin
-      __syncthreads();
-      if (m <= kExact) { exact = true; break; }   // the same for every thread
+    for (int j = 0; j < KPT; ++j) {
+      inb[j] = __builtin_amdgcn_ballot_w64(((valid >> j) & 1u) && (key[j] & pmask) == prefix);
+      dig[j] = (uint32_t)(key[j] >> shift) & 15u;
     }
-  } else {
-    krem = 0;          // keep every real entry
+    uint32_t cnt[16];
+#pragma unroll
+    for (int d = 0; d < 16; ++d) {
+      cnt[d] = 0;
+#pragma unroll
+      for (int j = 0; j < KPT; ++j)
+        cnt[d] += (uint32_t)__popcll(__builtin_amdgcn_ballot_w64(dig[j] == (uint32_t)d) & inb[j]);
+    }
+    if (lane == 0) {
+#pragma unroll
+      for (int d = 0; d < 16; ++d) s_cnt[pass & 1][wave][d] = cnt[d];
+    }
+    __syncthreads();
+    uint32_t tot = 0;
+    if (lane < 16) {
+#pragma unroll
+      for (int w = 0; w < kSelWaves; ++w) tot += s_cnt[pass & 1][w][lane];
+    }
+    // Digit of the krem-th largest key in the bin, from digit 15 down
+    // (wave-uniform: read lane by lane).
+    int cum = 0, dsel = 0, m = 0, all = 0;
+    bool found = false;
+#pragma unroll
+    for (int d = 15; d >= 0; --d) {
+      const int td = __builtin_amdgcn_readlane((int)tot, d);
+      all += td;
+      if (!found) {
+        if (cum + td >= krem) { dsel = d; m = td; found = true; } else { cum += td; }
+      }
+    }
+    if (pass == 0 && all <= a.k) { keep_all = true; break; }   // every real entry is kept
+    krem -= cum;
+    prefix |= (uint64_t)dsel << shift;
+    pmask |= 15ull << shift;
+    if (m == krem) { bin_kept = true; break; }
   }
 
-  uint32_t keep = 0;
-  if (exact) {
-    // Keys in a higher bin are kept; of the m keys in the bin, the krem best
-    // by (key descending, position ascending), ranked one against all.
-    uint32_t in = 0;
+  uint32_t keep = 0, eq = 0;
 #pragma unroll
-    for (int j = 0; j < KPT; ++j) {
-      if (!((valid >> j) & 1u)) continue;
-      const uint64_t b = key[j] & pmask;
-      if (b > prefix) keep |= 1u << j;
-      else if (b == prefix) in |= 1u << j;
-    }
-    int m;
-    int p = block_exclusive_scan<THREADS>(__popc(in), s_tmp, &m);
-    const int p0 = p;
-#pragma unroll
-    for (int j = 0; j < KPT; ++j) {
-      if (!((in >> j) & 1u)) continue;
-      s_ekey[p] = key[j];
-      s_epos[p] = tid * KPT + j;
-      ++p;
-    }
-    __syncthreads();
-    for (int t = tid; t < m; t += THREADS) {
-      const uint64_t kt = s_ekey[t];
-      const int pt = s_epos[t];
-      int rank = 0;
-      for (int u = 0; u < m; ++u) {
-        const uint64_t ku = s_ekey[u];
-        rank += (ku > kt || (ku == kt && s_epos[u] < pt)) ? 1 : 0;
-      }
-      s_esel[t] = rank < krem ? 1 : 0;
-    }
-    __syncthreads();
-    p = p0;
-#pragma unroll
-    for (int j = 0; j < KPT; ++j) {
-      if (!((in >> j) & 1u)) continue;
-      if (s_esel[p]) keep |= 1u << j;
-      ++p;
-    }
-  } else {
-    // Kept: real keys above T, and the first krem keys equal to T in index order.
-    uint32_t eq = 0;
-#pragma unroll
-    for (int j = 0; j < KPT; ++j) {
-      if (!((valid >> j) & 1u)) continue;
-      if (nvalid <= k || key[j] > prefix) keep |= 1u << j;
-      else if (key[j] == prefix) eq |= 1u << j;
-    }
+  for (int j = 0; j < KPT; ++j) {
+    if (!((valid >> j) & 1u)) continue;
+    const uint64_t b = key[j] & pmask;
+    if (keep_all || b > prefix || (bin_kept && b == prefix)) keep |= 1u << j;
+    else if (!bin_kept && key[j] == prefix) eq |= 1u << j;
+  }
+  if (!keep_all && !bin_kept) {
+    // All 16 digits decided: prefix is T; the first krem keys equal to T.
     int eq_total;
-    const int eq_before = block_exclusive_scan<THREADS>(__popc(eq), s_tmp, &eq_total);
+    const int eq_before = block_exclusive_scan<kSelThreads>(__popc(eq), s_tmp, &eq_total);
     int take = krem - eq_before;
-    take = take < 0 ? 0 : take;
 #pragma unroll
     for (int j = 0; j < KPT; ++j) {
       if (((eq >> j) & 1u) && take > 0) { keep |= 1u << j; --take; }
     }
   }
   int kept;
-  int pos = block_exclusive_scan<THREADS>(__popc(keep), s_tmp, &kept);
+  int pos = block_exclusive_scan<kSelThreads>(__popc(keep), s_tmp, &kept);
 
-  if (final_idx != nullptr) {
+  if (a.final_idx != nullptr) {
 #pragma unroll
     for (int j = 0; j < KPT; ++j) {
       if (!((keep >> j) & 1u)) continue;
       const int64_t g = first + j;
-      final_idx[pos++] = in_idx ? in_idx[g] : (int32_t)g;
+      a.final_idx[pos++] = a.in_idx ? a.in_idx[g] : (int32_t)g;
     }
     return;
   }
-  const int64_t ob = (int64_t)blockIdx.x * k;
+  const int64_t ob = (int64_t)block * a.k;
 #pragma unroll
   for (int j = 0; j < KPT; ++j) {
     if (!((keep >> j) & 1u)) continue;
     const int64_t g = first + j;
-    out_var[ob + pos] = __longlong_as_double((long long)key[j]);
-    out_idx[ob + pos] = in_idx ? in_idx[g] : (int32_t)g;
+    a.out_var[ob + pos] = __longlong_as_double((long long)key[j]);
+    a.out_idx[ob + pos] = a.in_idx ? a.in_idx[g] : (int32_t)g;
     ++pos;
   }
-  for (int p = kept + tid; p < k; p += THREADS) {      // fewer than k real entries
-    out_var[ob + p] = -1.0;
-    out_idx[ob + p] = INT_MAX;
+  for (int p = kept + tid; p < a.k; p += kSelThreads) {      // fewer than k real entries
+    a.out_var[ob + p] = -1.0;
+    a.out_idx[ob + p] = INT_MAX;
   }
 }
 
+// One level of selection, workgroup b taking chunk b. With `counter` (zero
+// at launch), the level is the last before the final one, and the level's
+// last workgroup to finish runs the final selection `fin` over all
+// survivors: every workgroup publishes its survivors (device-scope release)
+// before counting itself in, and the one that counts last acquires them. No
+// workgroup waits for another, and the final selection starts as soon as
+// the level ends, without a second dispatch.
+template <int KPT>
+__global__ void __launch_bounds__(kSelThreads) foid_select_kernel(SelectArgs a, SelectArgs fin,
+                                                                  unsigned* counter) {
+  __shared__ uint32_t s_cnt[2][kSelWaves][16];
+  __shared__ int s_tmp[kSelWaves];
+  __shared__ int s_last;
+  select_block<KPT>(a, blockIdx.x, s_cnt, s_tmp);
+  if (counter == nullptr) return;
+  __threadfence();
+  __syncthreads();
+  if (threadIdx.x == 0) s_last = atomicAdd(counter, 1u) == gridDim.x - 1 ? 1 : 0;
+  __syncthreads();
+  if (!s_last) return;
+  __threadfence();
+  select_block<KPT>(fin, 0, s_cnt, s_tmp);
+}
+
+__global__ void foid_zero_kernel(unsigned* counter) { *counter = 0u; }
+
 // A level keeps k of every chunk of level_chunk(k) >= 4 k entries; the final
-// workgroup takes up to 1024 entries (4 per thread), or 4096 when k > 256.
+// workgroup takes up to 1024 entries (2 per thread), or 4096 when k > 256.
 int64_t level_chunk(int32_t k) { return k <= 256 ? 1024 : 4096; }
 int64_t final_cap(int32_t k) { return k <= 256 ? 1024 : 4096; }
 int64_t chunks_of(int64_t n, int32_t k) { return (n + level_chunk(k) - 1) / level_chunk(k); }
 
-adahop_status launch_select(bool final_level, const double* in_var, const int32_t* in_idx,
-                            int64_t count, int32_t k, double* out_var, int32_t* out_idx,
-                            int32_t* final_idx, hipStream_t stream) {
-  const bool big = k > 256;
-  const unsigned nb = final_level ? 1u : (unsigned)chunks_of(count, k);
-  if (big)
-    foid_select_kernel<kSelThreads, 16><<<nb, kSelThreads, 0, stream>>>(in_var, in_idx, count, k,
-                                                                        out_var, out_idx, final_idx);
+adahop_status launch_select(bool final_level, const SelectArgs& a, const SelectArgs& fin,
+                            unsigned* counter, hipStream_t stream) {
+  const unsigned nb = final_level ? 1u : (unsigned)chunks_of(a.count, a.k);
+  if (a.k > 256)
+    foid_select_kernel<8><<<nb, kSelThreads, 0, stream>>>(a, fin, counter);
   else
-    foid_select_kernel<kSelThreads, 4><<<nb, kSelThreads, 0, stream>>>(in_var, in_idx, count, k,
-                                                                       out_var, out_idx, final_idx);
+    foid_select_kernel<2><<<nb, kSelThreads, 0, stream>>>(a, fin, counter);
   return check_launch("foid_select");
 }
 
 }  // namespace
 
 size_t foid_workspace_bytes(int64_t ncand, int32_t k) {
-  const size_t var_bytes = align_up(sizeof(double) * (size_t)ncand, kAlign);
-  if (ncand <= final_cap(k)) return var_bytes;
+  if (ncand <= final_cap(k)) return 0;
+  // The levels' survivors, double buffered (level 0 scores in registers),
+  // then the counter of the level that runs the final selection.
   const size_t entries = (size_t)chunks_of(ncand, k) * (size_t)k;
-  return var_bytes +
-         2 * (align_up(entries * sizeof(double), kAlign) + align_up(entries * sizeof(int32_t), kAlign));
+  return 2 * (align_up(entries * sizeof(double), kAlign) + align_up(entries * sizeof(int32_t), kAlign)) +
+         kAlign;
 }
 
 adahop_status foid_launch(const uint16_t* t, int64_t rows, int64_t cols, int64_t ld, int axis,
@@ -328,21 +383,19 @@ adahop_status foid_launch(const uint16_t* t, int64_t rows, int64_t cols, int64_t
   const int64_t len = axis == ADAHOP_AXIS_ROWS ? cols : rows;
   const int P = (int)(probe < len ? probe : len);
   const size_t need = foid_workspace_bytes(ncand, k);
-  if (ws == nullptr || ws_bytes < need)
+  if (need > 0 && (ws == nullptr || ws_bytes < need))
     return fail(ADAHOP_ERR_WORKSPACE, "adahop_detect: workspace too small (need " +
                                           std::to_string(need) + " bytes)");
-  char* p = static_cast<char*>(ws);
-  double* var = reinterpret_cast<double*>(p);
-  p += align_up(sizeof(double) * (size_t)ncand, kAlign);
-  const int64_t vblocks = (ncand + kVarThreads - 1) / kVarThreads;
-  if (vblocks > 0x7FFFFFFF) return fail(ADAHOP_ERR_UNSUPPORTED, "adahop_detect: too many candidates");
-  foid_var_kernel<<<dim3((unsigned)vblocks), dim3(kVarThreads), 0, stream>>>(t, ld, axis, P, ncand,
-                                                                              var);
-  adahop_status st = check_launch("foid_var");
-  if (st != ADAHOP_OK) return st;
-  if (ncand <= final_cap(k))
-    return launch_select(true, var, nullptr, ncand, k, nullptr, nullptr, idx_out, stream);
+  if (chunks_of(ncand, k) > 0x7FFFFFFF)
+    return fail(ADAHOP_ERR_UNSUPPORTED, "adahop_detect: too many candidates");
+  SelectArgs a{t, ld, axis, P, nullptr, nullptr, ncand, k, nullptr, nullptr, nullptr};
+  const SelectArgs none{};
+  if (ncand <= final_cap(k)) {
+    a.final_idx = idx_out;
+    return launch_select(true, a, none, nullptr, stream);
+  }
   const size_t entries = (size_t)chunks_of(ncand, k) * (size_t)k;
+  char* p = static_cast<char*>(ws);
   double* var_buf[2];
   int32_t* idx_buf[2];
   for (int b = 0; b < 2; ++b) {
@@ -351,21 +404,29 @@ adahop_status foid_launch(const uint16_t* t, int64_t rows, int64_t cols, int64_t
     idx_buf[b] = reinterpret_cast<int32_t*>(p);
     p += align_up(entries * sizeof(int32_t), kAlign);
   }
+  unsigned* counter = reinterpret_cast<unsigned*>(p);
   // Each level divides the count by at least 4, until one workgroup can take
-  // the rest.
-  const double* in_var = var;
-  const int32_t* in_idx = nullptr;
-  int64_t count = ncand;
+  // the rest; level 0 scores the candidates itself, and the last level before
+  // the final one runs it too.
   int cur = 0;
-  while (count > final_cap(k)) {
-    st = launch_select(false, in_var, in_idx, count, k, var_buf[cur], idx_buf[cur], nullptr, stream);
+  while (true) {
+    a.out_var = var_buf[cur];
+    a.out_idx = idx_buf[cur];
+    const SelectArgs next{nullptr, 0, 0, 0, var_buf[cur], idx_buf[cur], chunks_of(a.count, k) * k, k,
+                          nullptr, nullptr, nullptr};
+    if (next.count <= final_cap(k)) {
+      SelectArgs fin = next;
+      fin.final_idx = idx_out;
+      foid_zero_kernel<<<1, 1, 0, stream>>>(counter);
+      const adahop_status st = check_launch("foid_zero");
+      if (st != ADAHOP_OK) return st;
+      return launch_select(false, a, fin, counter, stream);
+    }
+    const adahop_status st = launch_select(false, a, none, nullptr, stream);
     if (st != ADAHOP_OK) return st;
-    count = chunks_of(count, k) * k;
-    in_var = var_buf[cur];
-    in_idx = idx_buf[cur];
+    a = next;
     cur ^= 1;
   }
-  return launch_select(true, in_var, in_idx, count, k, nullptr, nullptr, idx_out, stream);
 }
 
 }  // namespace adahop

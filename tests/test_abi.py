@@ -104,9 +104,17 @@ def test_argument_checks_return_before_any_launch():
 
 
 def test_workspace_sizes():
-    # fp64 scores for every candidate, plus survivor lists when one level is not enough
-    assert A.adahop_detect_workspace_size(100, 64, "ROWS", 10) == 1024       # 800 B rounded up
-    assert A.adahop_detect_workspace_size(65536, 64, "ROWS", 64) > 65536 * 8
+    # Scores stay in registers; survivor lists (fp64 score + int32 index, k per
+    # chunk of 1024 candidates, two lists, each array rounded up to 256 bytes)
+    # when one workgroup cannot take every candidate.
+    assert A.adahop_detect_workspace_size(100, 64, "ROWS", 10) == 0
+    assert A.adahop_detect_workspace_size(64, 1024, "COLS", 64) == 0
+    r256 = lambda b: -(-b // 256) * 256
+    surv = lambda e: 2 * (r256(8 * e) + r256(4 * e)) + 256      # + a 256-byte counter slot
+    assert A.adahop_detect_workspace_size(65536, 64, "ROWS", 64) == surv(64 * 64)
+    assert A.adahop_detect_workspace_size(64, 14336, "COLS", 64) == surv(14 * 64)
+    # k > 256: chunks of 4096
+    assert A.adahop_detect_workspace_size(20000, 64, "ROWS", 300) == surv(5 * 300)
     ws = A.adahop_gemm_workspace_size("WGRAD", 32768, 14336, 4096, "R", "C", None, 64)
     # packed operands: (4096 + 14336) x 32768 x 17/32 bytes, plus lines and partials
     assert 0.5e9 > ws > (4096 + 14336) * 32768 * 17 // 32

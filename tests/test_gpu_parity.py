@@ -130,6 +130,8 @@ FOID_CASES = [
     (9000, 128, "ROWS", 1024, 64, True),     # k at its maximum
     (128, 300, "COLS", 300, 64, False),      # k = all candidates
     (96, 256, "ROWS", 7, 16, True),          # shorter probe
+    (64, 14336, "COLS", 64, 64, False),      # Llama3.1-8B d_ff columns: 14 chunks, then one
+    (1024, 64, "ROWS", 64, 64, True),        # exactly one chunk: scores and selection in one launch
 ]
 
 
