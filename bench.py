@@ -255,7 +255,9 @@ def main():
                         "the fixup kernel"),
         "call_ms_events": round(call_ms, 4),
         "roofline": {"bound": "mfma",
-                     "kernel": "gemm_mx_ring8_kernel (FP4 MFMA GEMM, fused scatter-add epilogue)",
+                     "kernel": ("gemm_mx_ring8_kernel + gemm_split_fixup_kernel (FP4 MFMA GEMM, "
+                                "fused scatter-add epilogue; the fixup adds the K-parts of a "
+                                "split last round)"),
                      "achieved": round(achieved, 1), "peak": PEAK_FP4_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP4_TFLOPS, 4),
                      "traffic": None},
