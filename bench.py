@@ -282,6 +282,31 @@ def main():
         result["bf16_matmul_ms"] = round(bms, 4)
         result["speedup_vs_bf16_matmul"] = round(bms / ms_per_step, 3)
         del a2
+        # hipBLASLt's own MXFP4 GEMM (torch._scaled_mm on packed E2M1 codes
+        # with unit E8M0 scales), same m, n, K: a library reference for the
+        # GEMM stage alone.
+        try:
+            f4 = torch.float4_e2m1fn_x2
+            e8 = torch.float8_e8m0fnu
+            qa = torch.randint(0, 256, (m, K // 2), dtype=torch.uint8, device=dev).view(f4)
+            qb = torch.randint(0, 256, (n, K // 2), dtype=torch.uint8, device=dev).view(f4)
+            sa = torch.full((m, K // 32), 127, dtype=torch.uint8, device=dev).view(e8)
+            sb = torch.full((n, K // 32), 127, dtype=torch.uint8, device=dev).view(e8)
+            mm = lambda: torch._scaled_mm(qa, qb.t(), sa, sb, out_dtype=torch.bfloat16)
+            for _ in range(3):
+                mm()
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for _ in range(max(3, args.steps // 2)):
+                mm()
+            torch.cuda.synchronize()
+            fms = (time.perf_counter() - t0) / max(3, args.steps // 2) * 1e3
+            result["hipblaslt_mxfp4_gemm_ms"] = round(fms, 4)
+            result["gemm_stage_speedup_vs_hipblaslt_mxfp4"] = round(fms / gemm_ms, 3)
+            del qa, qb, sa, sb
+        except Exception as ex:          # no MXFP4 GEMM in this torch build
+            result["hipblaslt_mxfp4_gemm_ms"] = None
+            print(f"# hipBLASLt MXFP4 reference unavailable: {type(ex).__name__}", file=sys.stderr)
 
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(op, lhs_np, rhs_np, T, Din, Dout, call, m, n, K)

@@ -93,11 +93,11 @@ struct GemmArgs {
   int64_t ldc;
   int out_f32;
   int tiles_m, tiles_n;
-  // Last round split along K (main kernel): workgroups from split_full on
-  // each take 1 / split_parts of K of one of the tiles from split_full on and
-  // leave their fp32 sums in split_ws ([tile][part][thread-order]);
-  // gemm_split_fixup_kernel adds the parts and runs the epilogue.
-  int split_full, split_parts;
+  // Last round split along K (main kernel): work items from split_full on
+  // each take 1 / split_parts of K of one of the split_count tiles from
+  // split_full on and leave their fp32 sums in split_ws ([tile][part][256 x
+  // 256]); gemm_split_fixup_kernel adds the parts and runs the epilogue.
+  int split_full, split_count, split_parts;   // whole tiles, split tiles, parts per split tile
   float* split_ws;
   // outlier epilogue
   int oe_mode;
@@ -528,6 +528,22 @@ constexpr int kLoads8PerStage = 5;            // per wave
 // A split tile's part in the workspace: a row-major fp32 256 x 256 matrix.
 constexpr int kSplitPartF4 = BM * BN / 4;      // float4 per part (256 KB)
 
+// One work item: a whole tile, or one K-part of a split tile of the last round.
+struct RingItem {
+  int tm, tn;
+  int part, split_tile;          // part < 0: a whole tile
+  int kt0, kt1;                  // K stages [kt0, kt1), a multiple of 4 apart
+  int64_t m0, n0;
+  __amdgpu_buffer_rsrc_t ra, rb;
+  int voffa[2], voffb[2], soff;
+};
+
+// Persistent: one workgroup per CU (gridDim.x <= number of items) takes the
+// work items r * gridDim.x + p(b), r = 0, 1, ..., where p spreads each round
+// over the XCDs in contiguous bands (xcd_band). Whole tiles come first, the
+// split parts of the last round after them. Before a tile's epilogue the
+// next item's first four stages are already in flight, so the ring refills
+// while the accumulators are stored.
 template <bool Chunked>
 __global__ void __launch_bounds__(kRing8Threads, 1) gemm_mx_ring8_kernel(GemmArgs g) {
   const int tid = threadIdx.x;
@@ -535,99 +551,108 @@ __global__ void __launch_bounds__(kRing8Threads, 1) gemm_mx_ring8_kernel(GemmArg
   // Wave-uniform (scalar): the scale loads below pick their descriptor by it.
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 2, wn = wave & 3;
-  // Whole tiles first, then the split tiles of the last round: part p of
-  // one takes K stages [p, p + 1) * nk / split_parts.
-  const int bid = blockIdx.x;
-  int tm, tn, part = -1, split_tile = 0;
-  if (bid < g.split_full) {
-    tile_at(xcd_band(bid, g.split_full), g.tiles_m, g.tiles_n, &tm, &tn);
-  } else {
-    const int t = xcd_band(bid - g.split_full, (int)gridDim.x - g.split_full);
-    split_tile = t / g.split_parts;
-    part = t % g.split_parts;
-    tile_at(g.split_full + split_tile, g.tiles_m, g.tiles_n, &tm, &tn);
-  }
-  // All of these are workgroup-uniform; the integer divisions leave them in
-  // vector registers, and the buffer descriptors and offsets built from them
-  // must be scalar (else every load becomes a loop over lanes).
-  tm = __builtin_amdgcn_readfirstlane(tm);
-  tn = __builtin_amdgcn_readfirstlane(tn);
-  part = __builtin_amdgcn_readfirstlane(part);
-  split_tile = __builtin_amdgcn_readfirstlane(split_tile);
-  const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
   const int64_t Kb = g.K / 2;
   const int64_t Ks = g.K / 32;
   const int nk = (int)(Kb / RBK);
-  // This workgroup's stages [kt0, kt1): a multiple of 4.
-  const int kt0 = __builtin_amdgcn_readfirstlane(part < 0 ? 0 : part * (nk / g.split_parts));
-  const int kt1 = __builtin_amdgcn_readfirstlane(part < 0 ? nk : kt0 + nk / g.split_parts);
-  const int rows_a = (int)(g.m - m0 < BM ? g.m - m0 : BM);
-  const int rows_b = (int)(g.n - n0 < BN ? g.n - n0 : BN);
+  const int items = g.split_full + g.split_count * g.split_parts;
+  const int G = gridDim.x, bid = blockIdx.x;
 
-  const __amdgpu_buffer_rsrc_t ra = Chunked
-      ? __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(g.a_codes + m0 * RBK), 0,
-                                          (int)((nk * g.m - m0) * RBK), kBufferFlags)
-      : __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(g.a_codes + m0 * Kb), 0,
-                                          (int)(rows_a * Kb), kBufferFlags);
-  const __amdgpu_buffer_rsrc_t rb = Chunked
-      ? __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(g.b_codes + n0 * RBK), 0,
-                                          (int)((nk * g.n - n0) * RBK), kBufferFlags)
-      : __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(g.b_codes + n0 * Kb), 0,
-                                          (int)(rows_b * Kb), kBufferFlags);
   const __amdgpu_buffer_rsrc_t rsa = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint32_t*>(g.a_sst), 0, (int)(g.m * Ks), kBufferFlags);
   const __amdgpu_buffer_rsrc_t rsb = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint32_t*>(g.b_sst), 0, (int)(g.n * Ks), kBufferFlags);
-
   // Load j (0, 1) of this wave fills LDS bytes [1024 (2 wave + j), +1024) of
   // a slot: rows 16 (2 wave + j) + lane / 4, physical chunk lane % 4 holding
   // logical chunk (lane % 4) ^ swz(row).
   const int row0 = 32 * wave + (lane >> 2);
   const int chunk = (lane & 3) ^ ring_swz(row0);    // swz is the same for rows row0 + 16 j
-  int voffa[2], voffb[2];
-#pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int r = row0 + 16 * j;
-    if (Chunked) {
-      voffa[j] = r < rows_a ? r * RBK + chunk * 16 : kPastEnd;
-      voffb[j] = r < rows_b ? r * RBK + chunk * 16 : kPastEnd;
-    } else {
-      voffa[j] = voffb[j] = r * (int)Kb + chunk * 16;
-    }
-  }
   const int stage_a = Chunked ? (int)g.m * RBK : RBK;
   const int stage_b = Chunked ? (int)g.n * RBK : RBK;
   // Scales: waves 0-3 copy A rows 64 (w % 4) + lane, waves 4-7 B rows.
   const bool sc_a = wave < 4;
   const int srow = 64 * (wave & 3) + lane;
-  const int soff = sc_a ? (srow < rows_a ? (int)((m0 + srow) * 4) : kPastEnd)
-                        : (srow < rows_b ? (int)((n0 + srow) * 4) : kPastEnd);
   const int sstage = sc_a ? (int)(g.m * 4) : (int)(g.n * 4);
 
-  auto issue = [&](auto S, int kt) {
+  // Item of round r for this workgroup, or -1.
+  auto item_of = [&](int r) {
+    const int base = r * G;
+    if (base >= items) return -1;
+    const int cnt = items - base < G ? items - base : G;
+    return bid < cnt ? base + xcd_band(bid, cnt) : -1;
+  };
+  auto setup = [&](int item) {
+    RingItem it;
+    int tm, tn, part = -1, split_tile = 0;
+    if (item < g.split_full) {
+      tile_at(item, g.tiles_m, g.tiles_n, &tm, &tn);
+    } else {
+      const int t = item - g.split_full;
+      split_tile = t / g.split_parts;
+      part = t % g.split_parts;
+      tile_at(g.split_full + split_tile, g.tiles_m, g.tiles_n, &tm, &tn);
+    }
+    // All of these are workgroup-uniform; the integer divisions leave them in
+    // vector registers, and the buffer descriptors and offsets built from
+    // them must be scalar (else every load becomes a loop over lanes).
+    it.tm = __builtin_amdgcn_readfirstlane(tm);
+    it.tn = __builtin_amdgcn_readfirstlane(tn);
+    it.part = __builtin_amdgcn_readfirstlane(part);
+    it.split_tile = __builtin_amdgcn_readfirstlane(split_tile);
+    it.kt0 = __builtin_amdgcn_readfirstlane(it.part < 0 ? 0 : it.part * (nk / g.split_parts));
+    it.kt1 = __builtin_amdgcn_readfirstlane(it.part < 0 ? nk : it.kt0 + nk / g.split_parts);
+    it.m0 = (int64_t)it.tm * BM;
+    it.n0 = (int64_t)it.tn * BN;
+    const int rows_a = (int)(g.m - it.m0 < BM ? g.m - it.m0 : BM);
+    const int rows_b = (int)(g.n - it.n0 < BN ? g.n - it.n0 : BN);
+    it.ra = Chunked
+        ? __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(g.a_codes + it.m0 * RBK), 0,
+                                            (int)((nk * g.m - it.m0) * RBK), kBufferFlags)
+        : __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(g.a_codes + it.m0 * Kb), 0,
+                                            (int)(rows_a * Kb), kBufferFlags);
+    it.rb = Chunked
+        ? __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(g.b_codes + it.n0 * RBK), 0,
+                                            (int)((nk * g.n - it.n0) * RBK), kBufferFlags)
+        : __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(g.b_codes + it.n0 * Kb), 0,
+                                            (int)(rows_b * Kb), kBufferFlags);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int r = row0 + 16 * j;
+      if (Chunked) {
+        it.voffa[j] = r < rows_a ? r * RBK + chunk * 16 : kPastEnd;
+        it.voffb[j] = r < rows_b ? r * RBK + chunk * 16 : kPastEnd;
+      } else {
+        it.voffa[j] = it.voffb[j] = r * (int)Kb + chunk * 16;
+      }
+    }
+    it.soff = sc_a ? (srow < rows_a ? (int)((it.m0 + srow) * 4) : kPastEnd)
+                   : (srow < rows_b ? (int)((it.n0 + srow) * 4) : kPastEnd);
+    return it;
+  };
+
+  auto issue = [&](const RingItem& it, auto S, int kt) {
     constexpr int slot = decltype(S)::value;
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          ra, (lds_void*)&ring_slot<slot>().a[1024 * (2 * wave + j)], 16, voffa[j], kt * stage_a, 0, 0);
+          it.ra, (lds_void*)&ring_slot<slot>().a[1024 * (2 * wave + j)], 16, it.voffa[j], kt * stage_a, 0, 0);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rb, (lds_void*)&ring_slot<slot>().b[1024 * (2 * wave + j)], 16, voffb[j], kt * stage_b, 0, 0);
+          it.rb, (lds_void*)&ring_slot<slot>().b[1024 * (2 * wave + j)], 16, it.voffb[j], kt * stage_b, 0, 0);
     }
     if (sc_a)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rsa, (lds_void*)&ring_slot<slot>().sa[256 * (wave & 3)],
-                                               4, soff, kt * sstage, 0, 0);
+                                               4, it.soff, kt * sstage, 0, 0);
     else
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rsb, (lds_void*)&ring_slot<slot>().sb[256 * (wave & 3)],
-                                               4, soff, kt * sstage, 0, 0);
+                                               4, it.soff, kt * sstage, 0, 0);
+  };
+  auto issue_first4 = [&](const RingItem& it) {
+    issue(it, std::integral_constant<int, 0>{}, it.kt0);
+    issue(it, std::integral_constant<int, 1>{}, it.kt0 + 1);
+    issue(it, std::integral_constant<int, 2>{}, it.kt0 + 2);
+    issue(it, std::integral_constant<int, 3>{}, it.kt0 + 3);
   };
 
   v16f acc[R8_FM][R8_FN];
-  static_for<R8_FM>([&](auto I) {
-    static_for<R8_FN>([&](auto J) {
-#pragma unroll
-      for (int v = 0; v < 16; ++v) acc[I][J][v] = 0.0f;
-    });
-  });
 
   const int lrow = lane & 31, khalf = lane >> 5;
   const int lswz = ring_swz(lrow);
@@ -686,7 +711,7 @@ __global__ void __launch_bounds__(kRing8Threads, 1) gemm_mx_ring8_kernel(GemmArg
   // kt+3 are in flight and sync, publishing stage kt+1 and freeing slot kt;
   // refill it with stage kt+4 (past kt1: a re-load of the last stage no one
   // reads) and read stage kt+1's K-step 0 into x during K-step 1's MFMAs.
-  auto stage = [&](auto S, Frags& x, Frags& y, int kt) {
+  auto stage = [&](const RingItem& it, auto S, Frags& x, Frags& y, int kt) {
     constexpr int slot = decltype(S)::value;
     read_frags(std::integral_constant<int, slot>{}, std::integral_constant<int, 1>{}, y);
     mma(x, std::integral_constant<int, 0>{});
@@ -700,7 +725,7 @@ __global__ void __launch_bounds__(kRing8Threads, 1) gemm_mx_ring8_kernel(GemmArg
     __builtin_amdgcn_s_waitcnt(waitcnt_imm(2 * kLoads8PerStage, 0));
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
-    issue(std::integral_constant<int, slot>{}, kt + 4 < kt1 ? kt + 4 : kt1 - 1);
+    issue(it, std::integral_constant<int, slot>{}, kt + 4 < it.kt1 ? kt + 4 : it.kt1 - 1);
     read_frags(std::integral_constant<int, (slot + 1) % kRingSlots>{}, std::integral_constant<int, 0>{}, x);
     mma(y, std::integral_constant<int, 1>{});
     static_for<5>([&](auto) {
@@ -717,41 +742,60 @@ __global__ void __launch_bounds__(kRing8Threads, 1) gemm_mx_ring8_kernel(GemmArg
     keep(y);
   };
 
-  issue(std::integral_constant<int, 0>{}, kt0);
-  issue(std::integral_constant<int, 1>{}, kt0 + 1);
-  issue(std::integral_constant<int, 2>{}, kt0 + 2);
-  issue(std::integral_constant<int, 3>{}, kt0 + 3);
-  Frags fx, fy;
-  __builtin_amdgcn_s_waitcnt(waitcnt_imm(3 * kLoads8PerStage, 0));
-  __builtin_amdgcn_s_barrier();
-  __builtin_amdgcn_sched_barrier(0);
-  read_frags(std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{}, fx);
-  // kt1 - kt0 is a multiple of 4: one loop exit.
-  for (int kt = kt0; kt < kt1; kt += kRingSlots) {
-    stage(std::integral_constant<int, 0>{}, fx, fy, kt);
-    stage(std::integral_constant<int, 1>{}, fx, fy, kt + 1);
-    stage(std::integral_constant<int, 2>{}, fx, fy, kt + 2);
-    stage(std::integral_constant<int, 3>{}, fx, fy, kt + 3);
-  }
+  int item = item_of(0);
+  if (item < 0) return;
+  issue_first4(setup(item));
+  for (int r = 0;; ++r) {
+    // Only the item index is carried over: the item's descriptors are built
+    // again here from scalars (carried through the loop they would end up in
+    // vector registers).
+    item = __builtin_amdgcn_readfirstlane(item);
+    const RingItem cur = setup(item);
+    static_for<R8_FM>([&](auto I) {
+      static_for<R8_FN>([&](auto J) {
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[I][J][v] = 0.0f;
+      });
+    });
+    Frags fx, fy;
+    __builtin_amdgcn_s_waitcnt(waitcnt_imm(3 * kLoads8PerStage, 0));
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    read_frags(std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{}, fx);
+    for (int kt = cur.kt0; kt < cur.kt1; kt += kRingSlots) {
+      stage(cur, std::integral_constant<int, 0>{}, fx, fy, kt);
+      stage(cur, std::integral_constant<int, 1>{}, fx, fy, kt + 1);
+      stage(cur, std::integral_constant<int, 2>{}, fx, fy, kt + 2);
+      stage(cur, std::integral_constant<int, 3>{}, fx, fy, kt + 3);
+    }
 
-  // Drain the trailing loads before the epilogue and before the workgroup's
-  // LDS can be handed to the next workgroup.
-  __builtin_amdgcn_sched_barrier(0);
-  __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
-  __syncthreads();
-  // The inner-extraction term goes into a whole tile or part 0 of a split
-  // one. A part of a split tile then goes out through the same store code,
-  // as a plain fp32 256 x 256 matrix (one code path keeps the accumulators
-  // in registers); the fixup kernel adds the outer-extraction term.
-  if (part <= 0) gemm_inner_term<R8_FM, R8_FN, R8_WM, R8_WN, 4>(g, acc, m0, n0);
-  GemmArgs ge = g;
-  int64_t em0 = m0, en0 = n0;
-  if (part >= 0) {
-    ge.C = g.split_ws + ((size_t)split_tile * g.split_parts + part) * (size_t)(BM * BN);
-    ge.ldc = BN; ge.m = BM; ge.n = BN; ge.out_f32 = 1; ge.vec_ok = 1; ge.oe_mode = 0;
-    em0 = 0; en0 = 0;
+    // Every wave's last reads and loads of the ring are done before it is
+    // refilled with the next item's first stages (or handed on).
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
+    __syncthreads();
+    const int next = item_of(r + 1);
+    if (next >= 0) issue_first4(setup(next));
+
+    // The inner-extraction term goes into a whole tile or part 0 of a split
+    // one. A part of a split tile then goes out through the same store code,
+    // as a plain fp32 256 x 256 matrix (one code path keeps the accumulators
+    // in registers); the fixup kernel adds the outer-extraction term.
+    if (cur.part <= 0) gemm_inner_term<R8_FM, R8_FN, R8_WM, R8_WN, 4>(g, acc, cur.m0, cur.n0);
+    GemmArgs ge = g;
+    int64_t em0 = cur.m0, en0 = cur.n0;
+    if (cur.part >= 0) {
+      ge.C = g.split_ws + ((size_t)cur.split_tile * g.split_parts + cur.part) * (size_t)(BM * BN);
+      ge.ldc = BN; ge.m = BM; ge.n = BN; ge.out_f32 = 1; ge.vec_ok = 1; ge.oe_mode = 0;
+      em0 = 0; en0 = 0;
+    }
+    gemm_store<R8_FM, R8_FN, R8_WM, R8_WN, 4, kRing8Threads>(ge, acc, em0, en0, g_ring_pos);
+    if (next < 0) break;
+    // The stores and the epilogue's loads are not ordered with the next
+    // item's ring loads in the counter: wait for all of them.
+    __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
+    item = next;
   }
-  gemm_store<R8_FM, R8_FN, R8_WM, R8_WN, 4, kRing8Threads>(ge, acc, em0, en0, g_ring_pos);
 }
 
 // Adds the parts of the split tiles in part order, adds the outer-extraction
@@ -1219,11 +1263,14 @@ adahop_status gemm_mx_launch(const uint8_t* a_codes, const uint8_t* a_scales,
     }
     const TailSplit ts = tail_split(m, n, K);
     g.split_full = (int)ts.full;
+    g.split_count = (int)ts.split;
     g.split_parts = ts.parts;
     g.split_ws = ts.split ? reinterpret_cast<float*>(static_cast<char*>(scratch) +
                                                      (kchunk ? 0 : staging_bytes(m, n, K)))
                           : nullptr;
-    const dim3 rgrid((unsigned)(ts.full + ts.split * ts.parts));
+    // Persistent: at most one workgroup per CU of a whole gfx950.
+    const int64_t items = ts.full + ts.split * ts.parts;
+    const dim3 rgrid((unsigned)(items < kSplitCUs ? items : kSplitCUs));
     if (kchunk)
       gemm_mx_ring8_kernel<true><<<rgrid, dim3(kRing8Threads), 0, stream>>>(g);
     else
