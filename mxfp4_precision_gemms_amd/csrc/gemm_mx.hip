@@ -42,10 +42,16 @@ typedef int v4i __attribute__((ext_vector_type(4)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 
+// gfx950 converts to bf16 in hardware, rounding to nearest even (finite
+// inputs; the tests check it against the integer rounding rule).
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float v) {
-  uint32_t u = __float_as_uint(v);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
+  return __builtin_bit_cast(uint16_t, (__bf16)v);
+}
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+// Two values in one conversion: a in the low half, b in the high half.
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  const bf16x2 p = {(__bf16)a, (__bf16)b};
+  return __builtin_bit_cast(uint32_t, p);
 }
 
 // Row of a 32x32 MFMA accumulator held in register v by lane l (column l%32).
@@ -228,54 +234,79 @@ __device__ __forceinline__ void gemm_store(const GemmArgs& g, v16f (&acc)[TFM][T
     }
   }
 
+  // Addresses: one row pointer per 32-row block I (the only 64-bit products);
+  // within a block every store is that pointer plus a constant offset.
   const bool full = m0 + BM <= g.m && n0 + BN <= g.n && g.vec_ok;
+  const int lc0 = wn * TWN + 4 * khalf;                 // tile column of (J, G) = lc0 + 32 J + 8 G
+  const int64_t col0 = n0 + lc0;
   static_for<TFM>([&](auto I) {
     const int lr = wm * TWM + I * 32 + lrow;
     const int64_t row = m0 + lr;
     const int prow = (any_oe && oe_rows) ? s_pos[lr] : -1;
+    // Outlier product values for this row: OE_LEFT its extracted row's
+    // values from column col0 on, OE_RIGHT its row of k values.
+    const float* oe_row = nullptr;
+    if (any_oe && row < g.m) {
+      if (oe_rows) { if (prow >= 0) oe_row = g.oe_p + (int64_t)prow * g.n + col0; }
+      else oe_row = g.oe_p + row * g.oe_k;
+    }
+    const int64_t off = row * g.ldc + col0;
+    float* cf = static_cast<float*>(g.C) + off;
+    uint16_t* cb = static_cast<uint16_t*>(g.C) + off;
     static_for<TFN>([&](auto J) {
+      float v[4][4];
       static_for<4>([&](auto G) {
-        const int lc = wn * TWN + J * 32 + 8 * G + 4 * khalf;
-        const int64_t col = n0 + lc;
-        float v[4] = {acc[I][J][4 * G + 0], acc[I][J][4 * G + 1], acc[I][J][4 * G + 2],
-                      acc[I][J][4 * G + 3]};
-        if (any_oe && row < g.m) {
+        constexpr int dc = 32 * decltype(J)::value + 8 * decltype(G)::value;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[G][e] = acc[I][J][4 * G + e];
+        if (oe_row != nullptr) {
           // scatter-add of the outlier product (the residual there is 0)
           if (oe_rows) {
-            if (prow >= 0) {
 #pragma unroll
-              for (int e = 0; e < 4; ++e)
-                if (col + e < g.n) v[e] += g.oe_p[(int64_t)prow * g.n + col + e];
-            }
+            for (int e = 0; e < 4; ++e)
+              if (col0 + dc + e < g.n) v[G][e] += oe_row[dc + e];
           } else {
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-              const int p = lc + e < BN ? s_pos[lc + e] : -1;
-              if (p >= 0) v[e] += g.oe_p[row * g.oe_k + p];
+              const int p = lc0 + dc + e < BN ? s_pos[lc0 + dc + e] : -1;
+              if (p >= 0) v[G][e] += oe_row[p];
             }
           }
         }
-        if (full) {
-          if (g.out_f32) {
-            *reinterpret_cast<float4*>(static_cast<float*>(g.C) + row * g.ldc + col) =
-                make_float4(v[0], v[1], v[2], v[3]);
-          } else {
-            const uint32_t lo = f32_to_bf16_rne(v[0]) | ((uint32_t)f32_to_bf16_rne(v[1]) << 16);
-            const uint32_t hi = f32_to_bf16_rne(v[2]) | ((uint32_t)f32_to_bf16_rne(v[3]) << 16);
-            *reinterpret_cast<uint2*>(static_cast<uint16_t*>(g.C) + row * g.ldc + col) =
-                make_uint2(lo, hi);
-          }
-        } else if (row < g.m) {
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            if (col + e >= g.n) continue;
-            if (g.out_f32)
-              static_cast<float*>(g.C)[row * g.ldc + col + e] = v[e];
-            else
-              static_cast<uint16_t*>(g.C)[row * g.ldc + col + e] = f32_to_bf16_rne(v[e]);
-          }
-        }
       });
+      if (full && !g.out_f32) {
+        // Lanes l and l + 32 hold the same row, column quads 8 G and 8 G + 4:
+        // one swap of half-waves per pair of quads gives lane l columns
+        // 16 P .. +7 and lane l + 32 columns 16 P + 8 .. +15, so each lane
+        // stores 16 contiguous bytes (2.4x fewer store cycles than 8-byte
+        // pieces, measured).
+        uint16_t* cbs = cb + 4 * khalf;                 // row pointer at column n0 + wn * TWN + 8 khalf
+        static_for<2>([&](auto P) {
+          constexpr int q = 2 * decltype(P)::value;
+          const auto a = __builtin_amdgcn_permlane32_swap(pack_bf16x2(v[q][0], v[q][1]),
+                                                          pack_bf16x2(v[q + 1][0], v[q + 1][1]), false, false);
+          const auto b = __builtin_amdgcn_permlane32_swap(pack_bf16x2(v[q][2], v[q][3]),
+                                                          pack_bf16x2(v[q + 1][2], v[q + 1][3]), false, false);
+          *reinterpret_cast<uint4*>(cbs + 32 * decltype(J)::value + 16 * decltype(P)::value) =
+              make_uint4(a[0], b[0], a[1], b[1]);
+        });
+      } else {
+        static_for<4>([&](auto G) {
+          constexpr int dc = 32 * decltype(J)::value + 8 * decltype(G)::value;
+          if (full) {
+            *reinterpret_cast<float4*>(cf + dc) = make_float4(v[G][0], v[G][1], v[G][2], v[G][3]);
+          } else if (row < g.m) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              if (col0 + dc + e >= g.n) continue;
+              if (g.out_f32)
+                cf[dc + e] = v[G][e];
+              else
+                cb[dc + e] = f32_to_bf16_rne(v[G][e]);
+            }
+          }
+        });
+      }
     });
   });
 }
