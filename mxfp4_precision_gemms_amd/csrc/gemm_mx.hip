@@ -110,7 +110,7 @@ struct GemmArgs {
   int oe_k;
   const int32_t* oe_idx;
   const float* oe_p;            // reduced outlier product: OE_LEFT [k][n], OE_RIGHT [m][k]
-  int vec_ok;                   // C rows allow 4-element vector stores
+  int vec_ok;                   // C rows allow 16-byte stores (ldc % 4 fp32 / % 8 bf16, C aligned)
   const uint16_t* ia_ptr; int64_t ia_ld; int ia_inner;   // OE_INNER a: (i, p)
   const uint16_t* ib_ptr; int64_t ib_ld; int ib_inner;   // OE_INNER b: (j, p)
 };
@@ -1273,7 +1273,8 @@ adahop_status gemm_mx_launch(const uint8_t* a_codes, const uint8_t* a_scales,
   g.tiles_m = (int)tiles_m; g.tiles_n = (int)tiles_n;
   g.oe_mode = oe.mode; g.oe_k = oe.k; g.oe_idx = oe.idx;
   g.oe_p = oe.partials ? oe.partials + (int64_t)oe.splits * (oe.mode == ADAHOP_ROUTE_OE_LEFT ? (int64_t)oe.k * n : m * (int64_t)oe.k) : nullptr;
-  g.vec_ok = (ldc % 4 == 0) && ((reinterpret_cast<uintptr_t>(C) & 15u) == 0);
+  // Whole-tile rows take 16-byte stores: 4 fp32 or 8 bf16 values.
+  g.vec_ok = (ldc % (out_f32 ? 4 : 8) == 0) && ((reinterpret_cast<uintptr_t>(C) & 15u) == 0);
   g.ia_ptr = oe.a.ptr; g.ia_ld = oe.a.ld; g.ia_inner = oe.a.inner_contiguous;
   g.ib_ptr = oe.b.ptr; g.ib_ld = oe.b.ld; g.ib_inner = oe.b.inner_contiguous;
   const dim3 grid((unsigned)(tiles_m * tiles_n)), block(kGemmThreads);

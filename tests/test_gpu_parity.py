@@ -170,7 +170,8 @@ def packed_operands(rng, m, n, K):
 # 4 (520 x 300 x 8192) parts that the fixup kernel adds.
 GEMM_CASES = [(256, 128, 128), (512, 384, 512), (300, 200, 96), (33, 1000, 160), (1024, 256, 1024),
               (300, 520, 1024), (77, 1000, 512), (520, 300, 2048), (256, 256, 768),
-              (300, 520, 4096), (520, 300, 8192)]
+              (300, 520, 4096), (520, 300, 8192),
+              (300, 260, 512), (260, 516, 1024)]   # n % 8 == 4: bf16 rows not 16-byte aligned
 
 
 @pytest.mark.parametrize("m,n,K", GEMM_CASES)
