@@ -259,6 +259,8 @@ typedef struct {
   size_t off_b_codes, off_b_scales;   /* B packed (outer = n) in `layout` */
   size_t off_lhs_lines;   /* bf16 lines gathered from lhs (layout as adahop_iht_quant) */
   size_t off_rhs_lines;   /* bf16 lines gathered from rhs */
+  int32_t fused_oe;       /* 1: the OE_LEFT / OE_RIGHT outlier product is formed while the
+                             operand FOID does not scan is quantized (one read of it) */
 } adahop_plan;
 
 ADAHOP_API adahop_status adahop_gemm_plan(adahop_op op, int64_t T, int64_t Din, int64_t Dout,

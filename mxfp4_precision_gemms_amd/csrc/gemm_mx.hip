@@ -1123,7 +1123,10 @@ adahop_status oe_product_launch(Bf16View X, Bf16View Y, int64_t nx, int64_t ny, 
   launch_oe(a, grid, X.inner_contiguous != 0, Y.inner_contiguous != 0, stream);
   adahop_status st = check_launch("oe_product");
   if (st != ADAHOP_OK) return st;
-  const int64_t count = nx * ny;
+  return oe_reduce_launch(partials, splits, nx * ny, stream);
+}
+
+adahop_status oe_reduce_launch(float* partials, int splits, int64_t count, hipStream_t stream) {
   float* P = partials + (int64_t)splits * count;
   const int64_t blocks = (count + 255) / 256 < 1024 ? (count + 255) / 256 : 1024;
   oe_reduce_kernel<<<dim3((unsigned)blocks), dim3(256), 0, stream>>>(partials, splits, count, P);

@@ -309,6 +309,34 @@ def test_full_product(case):
     run_and_compare(op, lhs, rhs, T, Din, Dout, pl, pr, route, k)
 
 
+# Operands of at least 2048 tiles (256 columns x 128 contraction rows) that
+# FOID does not scan and that are quantized down their columns form the
+# outlier product in the same pass. Sampled outputs plus every outlier line.
+FUSED_CASES = [
+    # op, T, Din, Dout, pl, pr, k
+    ("WGRAD", 16384, 136, 4002, "R", "C", 40),    # OE_RIGHT, GY rows % 4 != 0 (element loads)
+    ("WGRAD", 16416, 4096, 72, "C", "N", 64),     # OE_LEFT, X; a last tile of one block, ROWS layout
+    ("DGRAD", 256, 4096, 16384, "R", "N", 24),    # OE_LEFT, W down its columns
+]
+
+
+@pytest.mark.parametrize("case", FUSED_CASES, ids=[str(c) for c in FUSED_CASES])
+def test_full_product_fused_outlier_product(case):
+    op, T, Din, Dout, pl, pr, k = case
+    plan = A.adahop_gemm_plan(op, T, Din, Dout, pl, pr, None, k)
+    assert plan.fused_oe == 1
+    lhs, rhs = operands(op, T, Din, Dout, pl, pr, seed=T + Din + k)
+    route = A.ROUTE_NAME[plan.route]
+    tensor, axis = oracle.scan_target(op, route)
+    idx = oracle.foid(lhs if tensor == 0 else rhs, axis, k)
+    rng = np.random.default_rng(T + k)
+    rows = np.unique(np.concatenate([rng.choice(plan.m, 40, replace=False),
+                                     idx if route == "OE_LEFT" else []]).astype(np.int64))
+    cols = np.unique(np.concatenate([rng.choice(plan.n, min(40, plan.n), replace=False),
+                                     idx if route == "OE_RIGHT" else []]).astype(np.int64))
+    run_and_compare(op, lhs, rhs, T, Din, Dout, pl, pr, None, k, rows=rows, cols=cols)
+
+
 def test_deterministic_reruns():
     # K = 4096 over 6 tiles: the K-split path, whose parts are added in order.
     op, T, Din, Dout = "WGRAD", 4096, 768, 512
