@@ -1086,10 +1086,32 @@ void launch_oe(const OeArgs& a, dim3 grid, bool xin, bool yin, hipStream_t strea
   else oe_product_kernel<false, false><<<grid, dim3(kOeThreads), 0, stream>>>(a);
 }
 
-// P[i] = sum over s of partials[s][i], in the order s = 0, 1, ...
+// P[i] = sum over s of partials[s][i], in the order s = 0, 1, ... Four
+// consecutive sums per thread (16-byte loads when count % 4 == 0), eight
+// partial arrays' loads in flight before their adds.
 __global__ void __launch_bounds__(256) oe_reduce_kernel(const float* __restrict__ partials,
                                                          int splits, int64_t count,
                                                          float* __restrict__ P) {
+  const int64_t n4 = (count % 4 == 0) ? count / 4 : 0;
+  const float4* p4 = reinterpret_cast<const float4*>(partials);
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n4;
+       i += (int64_t)gridDim.x * 256) {
+    float4 s = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    int sp = 0;
+    for (; sp + 8 <= splits; sp += 8) {
+      float4 v[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) v[j] = p4[(int64_t)(sp + j) * n4 + i];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) { s.x += v[j].x; s.y += v[j].y; s.z += v[j].z; s.w += v[j].w; }
+    }
+    for (; sp < splits; ++sp) {
+      const float4 v = p4[(int64_t)sp * n4 + i];
+      s.x += v.x; s.y += v.y; s.z += v.z; s.w += v.w;
+    }
+    reinterpret_cast<float4*>(P)[i] = s;
+  }
+  if (n4 > 0) return;
   for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < count;
        i += (int64_t)gridDim.x * 256) {
     float s = 0.0f;
@@ -1128,7 +1150,8 @@ adahop_status oe_product_launch(Bf16View X, Bf16View Y, int64_t nx, int64_t ny, 
 
 adahop_status oe_reduce_launch(float* partials, int splits, int64_t count, hipStream_t stream) {
   float* P = partials + (int64_t)splits * count;
-  const int64_t blocks = (count + 255) / 256 < 1024 ? (count + 255) / 256 : 1024;
+  const int64_t items = count % 4 == 0 ? count / 4 : count;
+  const int64_t blocks = (items + 255) / 256 < 1024 ? (items + 255) / 256 : 1024;
   oe_reduce_kernel<<<dim3((unsigned)blocks), dim3(256), 0, stream>>>(partials, splits, count, P);
   return check_launch("oe_reduce");
 }
