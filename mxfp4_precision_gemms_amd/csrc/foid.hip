@@ -254,24 +254,27 @@ __device__ __forceinline__ void select_block(const SelectArgs& a, int block,
       for (int d = 0; d < 16; ++d) s_cnt[pass & 1][wave][d] = cnt[d];
     }
     __syncthreads();
-    uint32_t tot = 0;
+    int tot = 0;
     if (lane < 16) {
 #pragma unroll
-      for (int w = 0; w < kSelWaves; ++w) tot += s_cnt[pass & 1][w][lane];
+      for (int w = 0; w < kSelWaves; ++w) tot += (int)s_cnt[pass & 1][w][lane];
     }
-    // Digit of the krem-th largest key in the bin, from digit 15 down
-    // (wave-uniform: read lane by lane).
-    int cum = 0, dsel = 0, m = 0, all = 0;
-    bool found = false;
+    // Lane d < 16: keys of the bin with next digit >= d (a suffix sum over
+    // lanes d .. 15). The digit of the krem-th largest key is the largest d
+    // whose suffix holds at least krem keys; the keys above it are those of
+    // digits d + 1 .. 15. Wave-uniform throughout.
+    int suf = tot;
 #pragma unroll
-    for (int d = 15; d >= 0; --d) {
-      const int td = __builtin_amdgcn_readlane((int)tot, d);
-      all += td;
-      if (!found) {
-        if (cum + td >= krem) { dsel = d; m = td; found = true; } else { cum += td; }
-      }
+    for (int off = 1; off < 16; off <<= 1) {
+      const int y = __shfl_down(suf, off, 64);
+      if (lane + off < 16) suf += y;
     }
+    const int all = __builtin_amdgcn_readfirstlane(suf);
     if (pass == 0 && all <= a.k) { keep_all = true; break; }   // every real entry is kept
+    const uint64_t ge = __builtin_amdgcn_ballot_w64(lane < 16 && suf >= krem);
+    const int dsel = ge ? 63 - __builtin_clzll(ge) : 0;   // ge is never empty here
+    const int m = __builtin_amdgcn_readlane(tot, dsel);
+    const int cum = dsel < 15 ? __builtin_amdgcn_readlane(suf, dsel + 1) : 0;
     krem -= cum;
     prefix |= (uint64_t)dsel << shift;
     pmask |= 15ull << shift;
