@@ -49,7 +49,10 @@
  *     (default priority), forked from `stream` with an event and joined back
  *     before the GEMM, so that it runs beside FOID, the other quantization
  *     and the outlier product; the call's completion stays ordered on
- *     `stream`.
+ *     `stream`. Where that operand is quantized down its columns, is at
+ *     least 128 MiB and k <= 64 (the plan's fused_oe), everything runs on
+ *     `stream` instead: its quantization comes after the scanned operand's
+ *     and forms the outlier product in the same pass, so it is read once.
  */
 #ifndef ADAHOP_H
 #define ADAHOP_H
@@ -286,7 +289,11 @@ ADAHOP_API adahop_status adahop_gemm(adahop_op op, const uint16_t* lhs, const ui
  * that does not run records its event right after the previous one). With
  * OE_LEFT and OE_RIGHT the operand FOID does not scan is quantized on a
  * second stream: its stage is empty here, the ROWS-layout scale reordering
- * falls in the GEMM stage, and the other stages overlap with it. */
+ * falls in the GEMM stage, and the other stages overlap with it. When the
+ * plan reports fused_oe, events[2..4] instead follow the scanned operand's
+ * quantization, the other operand's quantization with the outlier
+ * product's partial sums, and the reduction of those sums (the scale
+ * reordering falls in the GEMM stage). */
 #define ADAHOP_STAGE_EVENTS 6
 ADAHOP_API adahop_status adahop_gemm_timed(adahop_op op, const uint16_t* lhs,
                                            const uint16_t* rhs, int64_t T, int64_t Din,

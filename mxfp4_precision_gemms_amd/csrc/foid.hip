@@ -12,9 +12,9 @@
 // full 64-element probe the values stay in registers between the two passes.
 // The first selection level computes the scores itself, in registers.
 //
-// Selection without a host round trip and without atomics, by radix select
-// on the fp64 score bits (see foid_select_kernel): 512-thread workgroups,
-// digit counts by wave ballots, one barrier per 4-bit digit. Every score
+// Selection without a host round trip, by radix select on the fp64 score
+// bits (see foid_select_kernel): 512-thread workgroups, digit counts by
+// integer adds in LDS, one barrier per 4-bit digit. Every score
 // above the k-th largest, T, is kept, and of the scores equal to T the ones
 // with the lowest indices -- the key (score descending, index ascending) is
 // a strict total order, so the result is unique. A prefix sum over the
@@ -188,10 +188,11 @@ struct SelectArgs {
 // Selection over chunks of 512 * KPT entries per workgroup, thread t owning
 // entries 512 * KPT * b + KPT t .. + KPT - 1 in index order. Radix select
 // on the fp64 score bits (scores are >= 0, so their bit patterns order like
-// the values), 4 bits per pass from the top: lane d of every wave counts the
-// wave's keys in the current bin whose next digit is d (one ballot per digit
-// and key slot), one barrier publishes the 16 x 16 counts, and every wave
-// sums them and picks the digit of the krem-th largest key itself. The pass
+// the values), 4 bits per pass from the top: every key in the current bin
+// adds one to its wave's LDS counter of its next digit, one barrier publishes
+// the 8 x 16 counts, and every wave sums them and picks the digit of the
+// krem-th largest key itself (integer counts: the order of the adds does not
+// matter). The pass
 // loop ends once the chosen bin holds exactly the keys still needed (all of
 // them kept), else after 16 passes with T, the k-th largest key: every key
 // above T is kept and, of the keys equal to T, the ones with the lowest
@@ -230,34 +231,26 @@ __device__ __forceinline__ void select_block(const SelectArgs& a, int block,
   uint64_t prefix = 0, pmask = 0;
   int krem = a.k;
   bool keep_all = false, bin_kept = false;
+  // Each wave counts into its own row of 16 digit counters in LDS, double
+  // buffered: a wave clears its row of the next pass's buffer only after the
+  // barrier that ends every wave's reads of it, and its own adds come after
+  // its clear in program order.
+  if (lane < 16) s_cnt[0][wave][lane] = 0;
   for (int pass = 0; pass < 16; ++pass) {
     const int shift = 60 - 4 * pass;
-    // Per key: in the current bin?, and its next digit; then per digit one
-    // compare into a lane mask, ANDed with the bin mask and counted.
-    uint64_t inb[KPT];
-    uint32_t dig[KPT];
+    const int buf = pass & 1;
+    // Per key in the current bin: one LDS add to the counter of its next digit.
 #pragma unroll
     for (int j = 0; j < KPT; ++j) {
-      inb[j] = __builtin_amdgcn_ballot_w64(((valid >> j) & 1u) && (key[j] & pmask) == prefix);
-      dig[j] = (uint32_t)(key[j] >> shift) & 15u;
-    }
-    uint32_t cnt[16];
-#pragma unroll
-    for (int d = 0; d < 16; ++d) {
-      cnt[d] = 0;
-#pragma unroll
-      for (int j = 0; j < KPT; ++j)
-        cnt[d] += (uint32_t)__popcll(__builtin_amdgcn_ballot_w64(dig[j] == (uint32_t)d) & inb[j]);
-    }
-    if (lane == 0) {
-#pragma unroll
-      for (int d = 0; d < 16; ++d) s_cnt[pass & 1][wave][d] = cnt[d];
+      if (((valid >> j) & 1u) && (key[j] & pmask) == prefix)
+        atomicAdd(&s_cnt[buf][wave][(uint32_t)(key[j] >> shift) & 15u], 1u);
     }
     __syncthreads();
+    if (lane < 16) s_cnt[buf ^ 1][wave][lane] = 0;
     int tot = 0;
     if (lane < 16) {
 #pragma unroll
-      for (int w = 0; w < kSelWaves; ++w) tot += (int)s_cnt[pass & 1][w][lane];
+      for (int w = 0; w < kSelWaves; ++w) tot += (int)s_cnt[buf][w][lane];
     }
     // Lane d < 16: keys of the bin with next digit >= d (a suffix sum over
     // lanes d .. 15). The digit of the krem-th largest key is the largest d
