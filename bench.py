@@ -219,13 +219,8 @@ def main():
         step(ev[i])
     torch.cuda.synchronize()
 
-    stage_names = A.STAGES
-    if plan.fused_oe:
-        scanned, other = ("lhs", "rhs") if plan.scan_tensor == 0 else ("rhs", "lhs")
-        stage_names = ("foid", f"quant_{scanned}", f"quant_{other}_with_oe_partials", "oe_reduce",
-                       "gemm")
     stage_ms = {}
-    for si, name in enumerate(stage_names):
+    for si, name in enumerate(A.STAGES):
         stage_ms[name] = float(np.mean([e[si].elapsed_time(e[si + 1]) for e in ev]))
     call_ms = float(np.mean([e[0].elapsed_time(e[-1]) for e in ev]))
     flops = 2.0 * m * n * K
@@ -251,12 +246,7 @@ def main():
                    "out_dtype": args.out_dtype},
         "pct_mxfp4_peak": round(100 * value / PEAK_FP4_TFLOPS, 2),
         "stages_ms": {k: round(v, 4) for k, v in stage_ms.items()},
-        "stages_note": ("one read of the operand FOID does not scan: its quantization, after "
-                        "the scanned operand's, also forms the outlier product's partial sums, "
-                        "which oe_reduce adds in order; gemm is the MFMA kernel plus, when its "
-                        "last round is split along K, the fixup kernel")
-                       if plan.fused_oe else
-                       ("the operand FOID does not scan is quantized on a second stream, beside "
+        "stages_note": ("the operand FOID does not scan is quantized on a second stream, beside "
                         "FOID, the other quantization and the outlier product: its slot is empty "
                         "and the other slots overlap it; gemm is the MFMA kernel plus, when its "
                         "last round is split along K, the fixup kernel")

@@ -49,10 +49,7 @@
  *     (default priority), forked from `stream` with an event and joined back
  *     before the GEMM, so that it runs beside FOID, the other quantization
  *     and the outlier product; the call's completion stays ordered on
- *     `stream`. Where that operand is quantized down its columns, is at
- *     least 128 MiB and k <= 64 (the plan's fused_oe), everything runs on
- *     `stream` instead: its quantization comes after the scanned operand's
- *     and forms the outlier product in the same pass, so it is read once.
+ *     `stream`.
  */
 #ifndef ADAHOP_H
 #define ADAHOP_H
@@ -262,8 +259,6 @@ typedef struct {
   size_t off_b_codes, off_b_scales;   /* B packed (outer = n) in `layout` */
   size_t off_lhs_lines;   /* bf16 lines gathered from lhs (layout as adahop_iht_quant) */
   size_t off_rhs_lines;   /* bf16 lines gathered from rhs */
-  int32_t fused_oe;       /* 1: the OE_LEFT / OE_RIGHT outlier product is formed while the
-                             operand FOID does not scan is quantized (one read of it) */
 } adahop_plan;
 
 ADAHOP_API adahop_status adahop_gemm_plan(adahop_op op, int64_t T, int64_t Din, int64_t Dout,
@@ -289,11 +284,7 @@ ADAHOP_API adahop_status adahop_gemm(adahop_op op, const uint16_t* lhs, const ui
  * that does not run records its event right after the previous one). With
  * OE_LEFT and OE_RIGHT the operand FOID does not scan is quantized on a
  * second stream: its stage is empty here, the ROWS-layout scale reordering
- * falls in the GEMM stage, and the other stages overlap with it. When the
- * plan reports fused_oe, events[2..4] instead follow the scanned operand's
- * quantization, the other operand's quantization with the outlier
- * product's partial sums, and the reduction of those sums (the scale
- * reordering falls in the GEMM stage). */
+ * falls in the GEMM stage, and the other stages overlap with it. */
 #define ADAHOP_STAGE_EVENTS 6
 ADAHOP_API adahop_status adahop_gemm_timed(adahop_op op, const uint16_t* lhs,
                                            const uint16_t* rhs, int64_t T, int64_t Din,

@@ -55,7 +55,7 @@ class Plan(ctypes.Structure):
                 ("scan_tensor", _i32), ("scan_axis", _int), ("layout", _int),
                 ("ws_bytes", _sz), ("off_idx", _sz), ("off_a_codes", _sz),
                 ("off_a_scales", _sz), ("off_b_codes", _sz), ("off_b_scales", _sz),
-                ("off_lhs_lines", _sz), ("off_rhs_lines", _sz), ("fused_oe", _i32)]
+                ("off_lhs_lines", _sz), ("off_rhs_lines", _sz)]
 
 
 # Exported symbols and their C signatures (argtypes, restype).

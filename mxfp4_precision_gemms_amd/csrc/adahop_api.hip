@@ -83,7 +83,6 @@ struct Plan {
   bool zero_lhs = false, zero_rhs = false;
   int lhs_zero_axis = ADAHOP_AXIS_ROWS, rhs_zero_axis = ADAHOP_AXIS_ROWS;
   int splits = 0;
-  int fused_groups = 0;   // > 0: outlier product fused into the other operand's quantization
   size_t off_foid = SIZE_MAX, off_partials = SIZE_MAX, off_gemm = SIZE_MAX;
   size_t foid_bytes = 0, gemm_bytes = 0;
 };
@@ -161,16 +160,7 @@ adahop_status make_plan(adahop_op op, int64_t T, int64_t Din, int64_t Dout,
   if (route == ADAHOP_ROUTE_OE_LEFT || route == ADAHOP_ROUTE_OE_RIGHT) {
     const int64_t nx = route == ADAHOP_ROUTE_OE_LEFT ? pb.k : s.m;
     const int64_t ny = route == ADAHOP_ROUTE_OE_LEFT ? s.n : pb.k;
-    // The operand FOID does not scan, when it is quantized down its columns,
-    // can form the outlier product in the same pass.
-    const bool other_lhs = pb.scan_tensor == 1;
-    const int other_contract = other_lhs ? s.lhs_contract : s.rhs_contract;
-    int tiles_per_wg = 0;
-    if (other_contract == ADAHOP_AXIS_ROWS)
-      P->fused_groups = iht_quant_oe_groups(s.K, other_lhs ? s.lhs_cols : s.rhs_cols, pb.k,
-                                            &tiles_per_wg);
-    pb.fused_oe = P->fused_groups > 0 ? 1 : 0;
-    P->splits = P->fused_groups > 0 ? P->fused_groups : oe_splits(nx, ny, s.K);
+    P->splits = oe_splits(nx, ny, s.K);
     P->off_partials = take(sizeof(float) * (size_t)(P->splits + 1) * (size_t)nx * (size_t)ny);
   }
   // Operands the main GEMM kernel streams are packed K-chunked by the
@@ -302,39 +292,6 @@ adahop_status run_gemm(adahop_op op, const uint16_t* lhs, const uint16_t* rhs, i
   // the side stream while FOID, the scanned operand's quantization and the
   // outlier product run on the caller's stream; the join comes right before
   // the GEMM (and the ROWS-layout scale reordering).
-  if (P.fused_groups > 0) {
-    // One read of the operand FOID does not scan: FOID, the scanned
-    // operand's quantization (which gathers the lines), then the other
-    // operand's quantization with the outlier product's partial sums, and
-    // their reduction.
-    float* partials = reinterpret_cast<float*>(w + P.off_partials);
-    ADAHOP_TRY(foid(stream));
-    ADAHOP_TRY(E.record(1));
-    ADAHOP_TRY(scan_lhs ? quant_lhs(stream) : quant_rhs(stream));
-    ADAHOP_TRY(E.record(2));
-    if (scan_lhs)
-      ADAHOP_TRY(iht_quant_oe_launch(rhs, s.rhs_rows, s.rhs_cols, s.rhs_cols, bc, bs, pb.layout, ll,
-                                     pb.k, 1, partials, stream));
-    else
-      ADAHOP_TRY(iht_quant_oe_launch(lhs, s.lhs_rows, s.lhs_cols, s.lhs_cols, ac, as, pb.layout, rl,
-                                     pb.k, 0, partials, stream));
-    ADAHOP_TRY(E.record(3));
-    ADAHOP_TRY(oe_reduce_launch(partials, P.splits, (int64_t)pb.k * (scan_lhs ? s.n : s.m), stream));
-    ADAHOP_TRY(E.record(4));
-    void* gemm_scratch = P.off_gemm != kNone ? w + P.off_gemm : nullptr;
-    if (pb.layout == ADAHOP_LAYOUT_ROWS)
-      ADAHOP_TRY(gemm_mx_stage_scales(ac, as, bc, bs, s.m, s.n, s.K, gemm_scratch, P.gemm_bytes, stream));
-    OeEpilogue oe{};
-    oe.mode = pb.route;
-    oe.k = pb.k;
-    oe.idx = idx;
-    oe.partials = partials;
-    oe.splits = P.splits;
-    ADAHOP_TRY(gemm_mx_launch(ac, as, bc, bs, s.m, s.n, s.K, pb.layout, oe, out, s.n, out_f32,
-                              gemm_scratch, P.gemm_bytes, stream));
-    return E.record(5);
-  }
-
   std::unique_lock<std::mutex> side_lock;
   SideStream* side = nullptr;
   if (idx && (scan_lhs ? !P.zero_rhs : !P.zero_lhs)) {

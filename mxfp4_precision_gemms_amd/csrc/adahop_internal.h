@@ -31,19 +31,6 @@ adahop_status iht_quant_launch(const uint16_t* src, int64_t rows, int64_t cols, 
                                int contract, int32_t hadamard_block, const int32_t* zero_idx,
                                int32_t nzero, int zero_axis, uint8_t* codes, uint8_t* scales,
                                uint16_t* gathered, int layout, hipStream_t stream);
-// The same quantization down the columns of src ([K = rows][outer = cols]),
-// fused with the outlier product of those values and the k extracted lines
-// (bf16 [k][K], 16-byte aligned): partial sums over groups of contraction
-// positions, [groups][outer][k] (or [groups][k][outer] with by_line), for
-// oe_reduce_launch. iht_quant_oe_groups gives the number of groups, 0 where
-// the fused form does not apply (k above kFusedOeMaxK, or an operand too
-// small to gain from it).
-constexpr int kFusedOeMaxK = 64;
-int iht_quant_oe_groups(int64_t K, int64_t outer, int32_t k, int* tiles_per_wg);
-adahop_status iht_quant_oe_launch(const uint16_t* src, int64_t rows, int64_t cols, int64_t ld,
-                                  uint8_t* codes, uint8_t* scales, int layout,
-                                  const uint16_t* lines, int32_t k, int by_line, float* partials,
-                                  hipStream_t stream);
 
 // ---- outlier product (bf16 MFMA) ------------------------------------------
 // P_s[x][y] = sum over t in split s of X(x, t) * Y(y, t), fp32, for s < splits,

@@ -159,25 +159,3 @@ def test_plan_layout():
     p = A.adahop_gemm_plan("FWD", 512, 512, 512, "C", "N")
     assert p.layout == A.LAYOUT_KCHUNK
     assert p.ws_bytes == 512 * 256 + 512 * 16 + 512 * 256 + 512 * 16
-
-
-def test_plan_fused_outlier_product():
-    # The outlier product is formed inside the quantization of the operand
-    # FOID does not scan when that operand is quantized down its columns, has
-    # at least 2048 tiles of 256 columns x 128 contraction rows, and k <= 64.
-    fused = lambda *a: A.adahop_gemm_plan(*a).fused_oe
-    assert fused("WGRAD", 32768, 14336, 4096, "R", "C", None, 64) == 1   # GY 4096 cols x 256 tiles
-    assert fused("WGRAD", 32768, 4096, 4096, "R", "C", None, 64) == 1    # o-proj bs8
-    assert fused("WGRAD", 32768, 14336, 4096, "R", "C", None, 65) == 0   # k above 64
-    assert fused("WGRAD", 16384, 136, 3840, "R", "C", None, 40) == 0     # 15 x 128 tiles
-    assert fused("WGRAD", 16384, 136, 3841, "R", "C", None, 40) == 1     # 16 x 128 tiles
-    assert fused("WGRAD", 16416, 4096, 72, "C", "N", None, 64) == 1      # OE_LEFT, X columns
-    assert fused("DGRAD", 256, 4096, 16384, "R", "N", None, 24) == 1     # OE_LEFT, W down columns
-    # DGRAD o-proj: W is only 32 x 16 tiles; FWD OE_RIGHT quantizes X along rows
-    assert fused("DGRAD", 32768, 4096, 4096, "R", "N", None, 64) == 0
-    assert fused("FWD", 32768, 4096, 16384, "N", "R", None, 64) == 0
-    assert fused("FWD", 256, 512, 512, "C", "N", None, 64) == 0          # IHT
-    # Partial sums: one [outer][k] fp32 array per group of tiles, plus their sum.
-    a = A.adahop_gemm_plan("WGRAD", 32768, 14336, 4096, "R", "C", None, 64)
-    b = A.adahop_gemm_plan("WGRAD", 32768, 14336, 4096, "R", "C", None, 65)
-    assert a.ws_bytes > 0 and b.ws_bytes > 0

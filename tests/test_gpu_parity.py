@@ -309,22 +309,21 @@ def test_full_product(case):
     run_and_compare(op, lhs, rhs, T, Din, Dout, pl, pr, route, k)
 
 
-# Operands of at least 2048 tiles (256 columns x 128 contraction rows) that
-# FOID does not scan and that are quantized down their columns form the
-# outlier product in the same pass. Sampled outputs plus every outlier line.
-FUSED_CASES = [
+# Long contractions with operands of 128 MiB and more that FOID does not
+# scan: the outlier product over many K splits, ragged edges. Sampled
+# outputs plus every outlier line.
+LONG_K_CASES = [
     # op, T, Din, Dout, pl, pr, k
-    ("WGRAD", 16384, 136, 4002, "R", "C", 40),    # OE_RIGHT, GY rows % 4 != 0 (element loads)
-    ("WGRAD", 16416, 4096, 72, "C", "N", 64),     # OE_LEFT, X; a last tile of one block, ROWS layout
+    ("WGRAD", 16384, 136, 4002, "R", "C", 40),    # OE_RIGHT, GY rows % 4 != 0
+    ("WGRAD", 16416, 4096, 72, "C", "N", 64),     # OE_LEFT, X; K % 128 == 32, ROWS layout
     ("DGRAD", 256, 4096, 16384, "R", "N", 24),    # OE_LEFT, W down its columns
 ]
 
 
-@pytest.mark.parametrize("case", FUSED_CASES, ids=[str(c) for c in FUSED_CASES])
-def test_full_product_fused_outlier_product(case):
+@pytest.mark.parametrize("case", LONG_K_CASES, ids=[str(c) for c in LONG_K_CASES])
+def test_full_product_long_k(case):
     op, T, Din, Dout, pl, pr, k = case
     plan = A.adahop_gemm_plan(op, T, Din, Dout, pl, pr, None, k)
-    assert plan.fused_oe == 1
     lhs, rhs = operands(op, T, Din, Dout, pl, pr, seed=T + Din + k)
     route = A.ROUTE_NAME[plan.route]
     tensor, axis = oracle.scan_target(op, route)
