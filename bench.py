@@ -13,6 +13,9 @@ call's stream, the roofline of the dominant kernel (the fused GEMM) and the
 oracle timed on the host's cores on a bounded sample.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+`--rank-sweep` prints instead the latency and error of the product at
+outlier ranks 0-256 and in plain MXFP4 (the pages' variant study, Fig. 10).
 """
 import argparse
 import hashlib
@@ -133,6 +136,59 @@ def cpu_baseline(op, lhs, rhs, T, Din, Dout, call, m, n, K, budget_s=12.0):
     }
 
 
+def rank_sweep(A, torch, np, wl, call, lhs, rhs, m, n, K, args):
+    """Error and latency against the outlier rank (the pages' variant study,
+    Fig. 10, on synthetic tensors). Rank 0 is the IHT route with nothing
+    extracted; MXFP4 is the plain format without rotation or extraction. The
+    error is measured on the fp32 output (before the bf16 rounding) against
+    the fp32 product of the same bf16 operands; the latency is that of the
+    call with bf16 output."""
+    op, T, Din, Dout = call.op, wl.T, wl.Din, wl.Dout
+    dev = lhs.device
+    base = A.ROUTE_NAME[A.adahop_gemm_plan(op, T, Din, Dout, call.pat_lhs, call.pat_rhs,
+                                           call.route, call.k).route]
+    if base not in ("OE_LEFT", "OE_RIGHT"):
+        sys.exit(f"rank sweep: workload {wl.name} routes to {base}, not an outer OE route")
+    torch.backends.cuda.matmul.allow_tf32 = False
+    a, b = {"FWD": lambda: (lhs.float(), rhs.float().t().contiguous()),
+            "DGRAD": lambda: (lhs.float(), rhs.float()),
+            "WGRAD": lambda: (lhs.float().t().contiguous(), rhs.float())}[op]()
+    ref = torch.matmul(a, b)
+    del a, b
+    ref_sq = float((ref.double() ** 2).sum())
+    out_shape = {"FWD": (T, Dout), "DGRAD": (T, Din), "WGRAD": (Dout, Din)}[op]
+    rows = []
+    for name, route, k in ([("MXFP4", "MXFP4", 0), ("IHT", "IHT", 0)] +
+                           [(f"{base} k={k}", base, k) for k in (16, 32, 64, 128, 256)]):
+        plan = A.adahop_gemm_plan(op, T, Din, Dout, call.pat_lhs, call.pat_rhs, route, max(k, 1))
+        ws = torch.empty(max(plan.ws_bytes, 1), dtype=torch.uint8, device=dev)
+        o32 = torch.empty(out_shape, dtype=torch.float32, device=dev)
+        o16 = torch.empty(out_shape, dtype=torch.bfloat16, device=dev)
+        kk = max(k, 1)
+        A.adahop_gemm(op, lhs, rhs, call.pat_lhs, call.pat_rhs, route, kk, out=o32, ws=ws)
+        torch.cuda.synchronize()
+        err = (o32 - ref).double()
+        sq = float((err ** 2).sum())
+        del err
+        for _ in range(args.warmup):
+            A.adahop_gemm(op, lhs, rhs, call.pat_lhs, call.pat_rhs, route, kk, out=o16, ws=ws)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            A.adahop_gemm(op, lhs, rhs, call.pat_lhs, call.pat_rhs, route, kk, out=o16, ws=ws)
+        torch.cuda.synchronize()
+        ms = (time.perf_counter() - t0) / args.steps * 1e3
+        rows.append({"variant": name, "route": route, "k": k, "ms": round(ms, 4),
+                     "mse": sq / ref.numel(), "rel_frobenius": (sq / ref_sq) ** 0.5})
+        print(f"# {name}: {ms:.4f} ms, rel. Frobenius error {(sq / ref_sq) ** 0.5:.4e}",
+              file=sys.stderr, flush=True)
+        del ws, o32, o16
+    print(json.dumps({"rank_sweep": rows, "workload": wl.name, "op": op, "m": m, "n": n, "K": K,
+                      "reference": "fp32 product of the bf16 operands (torch.matmul, no TF32)",
+                      "error_on": "fp32 output", "latency_on": "bf16 output",
+                      "steps": args.steps, "warmup": args.warmup}))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -142,6 +198,10 @@ def main():
     ap.add_argument("--out-dtype", default="bf16", choices=["bf16", "f32"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-bf16-baseline", action="store_true")
+    ap.add_argument("--rank-sweep", action="store_true",
+                    help="instead of the timed line: for outlier ranks 0 (IHT alone), 16, 32, 64, "
+                         "128, 256 and plain MXFP4, print the call's latency and its error against "
+                         "an fp32 product of the same bf16 operands")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a 1 GiB device-to-device copy 3 times (a known-size reference "
                          "for HBM byte counters) and exit")
@@ -183,6 +243,10 @@ def main():
     to_dev = lambda x: torch.from_numpy(x.view(np.int16)).to(dev).view(torch.bfloat16)
     lhs, rhs = to_dev(lhs_np), to_dev(rhs_np)
     print(f"# inputs ready in {time.perf_counter() - t0:.1f}s", file=sys.stderr, flush=True)
+
+    if args.rank_sweep:
+        rank_sweep(A, torch, np, wl, call, lhs, rhs, m, n, K, args)
+        return
 
     out_dtype = torch.bfloat16 if args.out_dtype == "bf16" else torch.float32
     plan = A.adahop_gemm_plan(op, T, Din, Dout, call.pat_lhs, call.pat_rhs, call.route, call.k)
