@@ -123,6 +123,32 @@ ADAHOP_API adahop_route_t adahop_route(adahop_op op, adahop_pattern pat_lhs,
                                        adahop_pattern pat_rhs);
 
 /* ---------------------------------------------------------------------------
+ * Pattern calibration (Table 1 names the three patterns; Fig. 4 and Fig. 8
+ * show them on real tensors, and the pages give no numeric test). Reading
+ * used here: a tensor is Row-wise when a few rows carry far more energy than
+ * the typical row, Column-wise likewise for columns, None otherwise,
+ * measured with FOID's own line score.
+ *
+ * adahop_line_scores writes each line's FOID score (the probe variance
+ * defined below for adahop_detect, bit for bit) to scores_out, a DEVICE
+ * array of fp64 [rows] (axis ROWS) or [cols] (axis COLS). Enqueued on
+ * `stream`; no workspace. Errors as adahop_detect's argument checks.
+ *
+ * adahop_classify_pattern (host only, pure) takes HOST copies of a tensor's
+ * row scores and column scores and compares, per axis, r = max / median
+ * (the median is the lower one: the element of rank (n - 1) / 2 in
+ * ascending order): if the larger r is below `threshold` the pattern is
+ * NONE, else ROW when r_rows >= r_cols and COL otherwise. A zero median with
+ * a positive maximum counts as an infinite ratio; an all-zero axis as 1.
+ * Returns ADAHOP_PAT_NONE for null pointers or empty arrays. */
+ADAHOP_API adahop_status adahop_line_scores(const uint16_t* t, int64_t rows, int64_t cols,
+                                            int64_t ld, adahop_axis axis, int32_t probe,
+                                            double* scores_out, void* stream);
+ADAHOP_API adahop_pattern adahop_classify_pattern(const double* row_scores, int64_t rows,
+                                                  const double* col_scores, int64_t cols,
+                                                  double threshold);
+
+/* ---------------------------------------------------------------------------
  * FOID (appendix, kernel 1; Fig. 9). Candidates are the rows (axis ROWS:
  * statistics over t[r, 0:P]) or the columns (axis COLS: t[0:P, c]) of the
  * bf16 tensor t [rows, cols], P = min(probe, line length). Each candidate's

@@ -11,6 +11,7 @@ import ctypes
 import os
 from typing import Optional, Sequence
 
+import numpy as np
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -66,6 +67,9 @@ SIGNATURES = {
     "adahop_route": ([_int, _int, _int], _int),
     "adahop_detect_workspace_size": ([_i64, _i64, _int, _i32], _sz),
     "adahop_detect": ([_p, _i64, _i64, _i64, _int, _i32, _i32, _p, _p, _sz, _p], _int),
+    "adahop_line_scores": ([_p, _i64, _i64, _i64, _int, _i32, _p, _p], _int),
+    "adahop_classify_pattern": ([ctypes.POINTER(ctypes.c_double), _i64,
+                                 ctypes.POINTER(ctypes.c_double), _i64, ctypes.c_double], _int),
     "adahop_iht_quant": ([_p, _i64, _i64, _i64, _int, _i32, _p, _i32, _int, _p, _p, _p, _p],
                          _int),
     "adahop_gemm_mx_workspace_size": ([_i64, _i64, _i64, ctypes.POINTER(OeDesc)], _sz),
@@ -152,6 +156,40 @@ def adahop_detect(t: torch.Tensor, axis, k: int, probe: int = 64,
                                idx_out.data_ptr(), _ptr(ws), 0 if ws is None else ws.numel(),
                                _stream(t.device)))
     return idx_out[:k]
+
+
+def adahop_line_scores(t: torch.Tensor, axis, probe: int = 64,
+                       out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """FOID's score of every row (axis ROWS) or column (COLS) of t: fp64 on the device."""
+    ptr = _bf16_ptr(t, "t")
+    rows, cols = t.shape
+    n = rows if _axis(axis) == AXIS["ROWS"] else cols
+    if out is None:
+        out = torch.empty(n, dtype=torch.float64, device=t.device)
+    _check(lib().adahop_line_scores(ptr, rows, cols, t.stride(0), _axis(axis), probe,
+                                    out.data_ptr(), _stream(t.device)))
+    return out
+
+
+CLASSIFY_THRESHOLD = 8.0
+
+
+def adahop_classify_pattern(row_scores, col_scores, threshold: float = CLASSIFY_THRESHOLD) -> str:
+    """"R", "C" or "N" from a tensor's row and column scores (host copies are made)."""
+    r = np.ascontiguousarray(torch.as_tensor(row_scores).detach().cpu().numpy(), dtype=np.float64)
+    c = np.ascontiguousarray(torch.as_tensor(col_scores).detach().cpu().numpy(), dtype=np.float64)
+    dp = ctypes.POINTER(ctypes.c_double)
+    p = lib().adahop_classify_pattern(r.ctypes.data_as(dp), r.size, c.ctypes.data_as(dp), c.size,
+                                      float(threshold))
+    return {v: k for k, v in PAT.items()}[p]
+
+
+def adahop_calibrate(t: torch.Tensor, probe: int = 64,
+                     threshold: float = CLASSIFY_THRESHOLD) -> str:
+    """The pattern of a bf16 tensor from its row and column scores."""
+    rs = adahop_line_scores(t, "ROWS", probe)
+    cs = adahop_line_scores(t, "COLS", probe)
+    return adahop_classify_pattern(rs, cs, threshold)
 
 
 def adahop_iht_quant(src: torch.Tensor, contract, hadamard_block: int = 32,

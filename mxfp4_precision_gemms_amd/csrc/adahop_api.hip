@@ -4,7 +4,10 @@
 #include <climits>
 #include <cstring>
 #include <mutex>
+#include <algorithm>
+#include <limits>
 #include <string>
+#include <vector>
 
 #include "adahop_internal.h"
 
@@ -443,6 +446,38 @@ adahop_status adahop_detect(const uint16_t* t, int64_t rows, int64_t cols, int64
   if (k > kMaxK) return fail(ADAHOP_ERR_UNSUPPORTED, "adahop_detect: k above 1024");
   return foid_launch(t, rows, cols, ld, axis, probe, k, idx_out, ws, ws_bytes,
                      static_cast<hipStream_t>(stream));
+}
+
+adahop_status adahop_line_scores(const uint16_t* t, int64_t rows, int64_t cols, int64_t ld,
+                                 adahop_axis axis, int32_t probe, double* scores_out,
+                                 void* stream) {
+  set_error("");
+  if (!t || !scores_out) return fail(ADAHOP_ERR_INVALID, "adahop_line_scores: null pointer");
+  if (rows < 1 || cols < 1 || ld < cols)
+    return fail(ADAHOP_ERR_INVALID, "adahop_line_scores: bad sizes");
+  if (axis != ADAHOP_AXIS_ROWS && axis != ADAHOP_AXIS_COLS)
+    return fail(ADAHOP_ERR_INVALID, "adahop_line_scores: bad axis");
+  if (probe < 1) return fail(ADAHOP_ERR_INVALID, "adahop_line_scores: probe < 1");
+  return line_scores_launch(t, rows, cols, ld, axis, probe, scores_out,
+                            static_cast<hipStream_t>(stream));
+}
+
+adahop_pattern adahop_classify_pattern(const double* row_scores, int64_t rows,
+                                       const double* col_scores, int64_t cols,
+                                       double threshold) {
+  if (!row_scores || !col_scores || rows < 1 || cols < 1) return ADAHOP_PAT_NONE;
+  // max / lower median of one axis' scores
+  auto ratio = [](const double* v, int64_t n) {
+    std::vector<double> s(v, v + n);
+    std::nth_element(s.begin(), s.begin() + (n - 1) / 2, s.end());
+    const double med = s[(size_t)((n - 1) / 2)];
+    const double mx = *std::max_element(v, v + n);
+    if (med > 0.0) return mx / med;
+    return mx > 0.0 ? std::numeric_limits<double>::infinity() : 1.0;
+  };
+  const double rr = ratio(row_scores, rows), rc = ratio(col_scores, cols);
+  if ((rr > rc ? rr : rc) < threshold) return ADAHOP_PAT_NONE;
+  return rr >= rc ? ADAHOP_PAT_ROW : ADAHOP_PAT_COL;
 }
 
 adahop_status adahop_iht_quant(const uint16_t* src, int64_t rows, int64_t cols, int64_t ld,

@@ -22,6 +22,9 @@ constexpr int kMaxK = 1024;  // largest outlier rank (FOID top-k, OE lines)
 
 // ---- FOID -----------------------------------------------------------------
 size_t foid_workspace_bytes(int64_t ncand, int32_t k);
+// FOID's score of every candidate line, fp64 [ncand], on the device.
+adahop_status line_scores_launch(const uint16_t* t, int64_t rows, int64_t cols, int64_t ld, int axis,
+                                 int32_t probe, double* out, hipStream_t stream);
 adahop_status foid_launch(const uint16_t* t, int64_t rows, int64_t cols, int64_t ld, int axis,
                           int32_t probe, int32_t k, int32_t* idx_out, void* ws, size_t ws_bytes,
                           hipStream_t stream);

@@ -345,6 +345,15 @@ __global__ void __launch_bounds__(kSelThreads) foid_select_kernel(SelectArgs a, 
 
 __global__ void foid_zero_kernel(unsigned* counter) { *counter = 0u; }
 
+// Every candidate's score on its own: one thread per line, the same
+// candidate_variance the selection levels fall back to.
+__global__ void __launch_bounds__(256) line_scores_kernel(const uint16_t* __restrict__ t, int64_t ld,
+                                                          int axis, int P, int64_t ncand,
+                                                          double* __restrict__ out) {
+  const int64_t l = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (l < ncand) out[l] = candidate_variance(t, ld, axis, P, l);
+}
+
 // A level keeps k of every chunk of level_chunk(k) >= 4 k entries; the final
 // workgroup takes up to 1024 entries (2 per thread), or 4096 when k > 256.
 int64_t level_chunk(int32_t k) { return k <= 256 ? 1024 : 4096; }
@@ -362,6 +371,17 @@ adahop_status launch_select(bool final_level, const SelectArgs& a, const SelectA
 }
 
 }  // namespace
+
+adahop_status line_scores_launch(const uint16_t* t, int64_t rows, int64_t cols, int64_t ld, int axis,
+                                 int32_t probe, double* out, hipStream_t stream) {
+  const int64_t ncand = axis == ADAHOP_AXIS_ROWS ? rows : cols;
+  const int64_t len = axis == ADAHOP_AXIS_ROWS ? cols : rows;
+  const int P = (int)(probe < len ? probe : len);
+  const int64_t blocks = (ncand + 255) / 256;
+  if (blocks > 0x7FFFFFFF) return fail(ADAHOP_ERR_UNSUPPORTED, "adahop_line_scores: too many lines");
+  line_scores_kernel<<<dim3((unsigned)blocks), dim3(256), 0, stream>>>(t, ld, axis, P, ncand, out);
+  return check_launch("line_scores");
+}
 
 size_t foid_workspace_bytes(int64_t ncand, int32_t k) {
   if (ncand <= final_cap(k)) return 0;

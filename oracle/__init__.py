@@ -100,6 +100,36 @@ def foid(t: np.ndarray, axis: int, k: int, probe: int = 64, return_var: bool = F
     return (idx[:k], var) if return_var else idx[:k]
 
 
+def line_scores(t: np.ndarray, axis: int, probe: int = 64) -> np.ndarray:
+    """FOID's score of every row (ROWS) or column (COLS) of t: the probe
+    variance that FOID ranks (its var_out), fp64."""
+    return foid(t, axis, 1, probe=probe, return_var=True)[1]
+
+
+def classify_pattern(row_scores, col_scores, threshold: float) -> str:
+    """Pattern of a tensor from its line scores: "R", "C" or "N".
+
+    Table 1 of the AdaHOP pages names the patterns (a few outlier rows, a few
+    outlier columns, or none) and Fig. 4 / Fig. 8 show them; the pages give
+    no numeric test. Reading: per axis, r = largest score / lower median
+    score (the element of rank (n - 1) // 2 in ascending order); "N" when the
+    larger r is below the threshold, else "R" if r_rows >= r_cols, else "C".
+    A zero median with a positive maximum is an infinite ratio; an all-zero
+    axis has ratio 1.
+    """
+    def ratio(v):
+        s = sorted(float(x) for x in v)
+        med, top = s[(len(s) - 1) // 2], s[-1]
+        if med > 0.0:
+            return top / med
+        return float("inf") if top > 0.0 else 1.0
+
+    rr, rc = ratio(row_scores), ratio(col_scores)
+    if max(rr, rc) < threshold:
+        return "N"
+    return "R" if rr >= rc else "C"
+
+
 def fwht32(y: np.ndarray) -> np.ndarray:
     y = np.ascontiguousarray(y, dtype=np.float32).copy()
     assert y.shape == (32,)

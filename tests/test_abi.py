@@ -94,6 +94,11 @@ def test_argument_checks_return_before_any_launch():
     assert lib.adahop_detect(fake, 10, 20, 20, 0, 0, 5, fake, None, 0, None) == 1
     assert lib.adahop_detect(None, 10, 20, 20, 0, 64, 5, fake, None, 0, None) == 1
     assert lib.adahop_detect(fake, 3000, 20, 20, 0, 64, 2000, fake, None, 0, None) == 2
+    # line scores: null output, bad axis, probe < 1, ld < cols
+    assert lib.adahop_line_scores(fake, 10, 20, 20, 0, 64, None, None) == 1
+    assert lib.adahop_line_scores(fake, 10, 20, 20, 2, 64, fake, None) == 1
+    assert lib.adahop_line_scores(fake, 10, 20, 20, 1, 0, fake, None) == 1
+    assert lib.adahop_line_scores(fake, 10, 20, 19, 1, 64, fake, None) == 1
     # GEMM: workspace too small, K mismatch
     assert lib.adahop_gemm(0, fake, fake, 64, 64, 64, 0, 0, -1, 64, fake, 0, None, 0, None) == 3
     Aop = A.MxOperand(256, 256, 64, 64)
@@ -159,3 +164,26 @@ def test_plan_layout():
     p = A.adahop_gemm_plan("FWD", 512, 512, 512, "C", "N")
     assert p.layout == A.LAYOUT_KCHUNK
     assert p.ws_bytes == 512 * 256 + 512 * 16 + 512 * 256 + 512 * 16
+
+
+def test_classify_pattern_matches_oracle():
+    # The host classifier against the oracle's rule on random score arrays,
+    # planted maxima, ties at the threshold and degenerate axes.
+    import numpy as np
+    import oracle
+    rng = np.random.default_rng(5)
+    cases = [([1, 2, 3, 16], [1, 1]), ([1, 2, 3, 15.9], [1, 1]), ([0, 0, 0, 1], [1, 1]),
+             ([0, 0, 0, 0], [0, 0]), ([1, 1], [1, 1, 100]), ([5.0], [5.0])]
+    for _ in range(200):
+        n, m = int(rng.integers(1, 300)), int(rng.integers(1, 300))
+        r = rng.chisquare(63, n) / 63
+        c = rng.chisquare(63, m) / 63
+        if rng.random() < 0.5:
+            r[rng.integers(0, n)] *= float(rng.choice([2, 10, 1000]))
+        if rng.random() < 0.5:
+            c[rng.integers(0, m)] *= float(rng.choice([2, 10, 1000]))
+        cases.append((r, c))
+    for r, c in cases:
+        for th in (2.0, 8.0, 50.0):
+            assert A.adahop_classify_pattern(r, c, th) == oracle.classify_pattern(r, c, th), (r, c, th)
+    assert A.lib().adahop_classify_pattern(None, 3, None, 3, 8.0) == 0
