@@ -336,6 +336,39 @@ def test_full_product_long_k(case):
     run_and_compare(op, lhs, rhs, T, Din, Dout, pl, pr, None, k, rows=rows, cols=cols)
 
 
+# Degenerate inputs: all-zero operands (every FOID score 0, so the lowest
+# indices win; zero codes and scale bytes; C = 0), constant operands (every
+# score 0 again, nonzero products), and k equal to the number of candidate
+# lines (the FP4 residual is all zero and C is the bf16 outlier product).
+DEGENERATE_CASES = [
+    # op, T, Din, Dout, pl, pr, route, k, fill
+    ("WGRAD", 512, 200, 136, "R", "C", None, 16, "zeros"),
+    ("DGRAD", 256, 320, 512, "R", "N", None, 8, "zeros"),
+    ("FWD", 256, 512, 264, "C", "N", None, 64, "zeros"),
+    ("WGRAD", 512, 96, 160, "R", "C", None, 32, "const"),
+    ("FWD", 300, 256, 200, "R", "N", "OE_INNER", 16, "const"),
+    ("WGRAD", 1024, 64, 200, "R", "C", None, 64, "planted"),      # k = all 64 of X's columns
+    ("DGRAD", 96, 512, 1024, "R", "N", None, 96, "planted"),      # k = all 96 of GY's rows
+]
+
+
+@pytest.mark.parametrize("case", DEGENERATE_CASES, ids=[str(c) for c in DEGENERATE_CASES])
+def test_full_product_degenerate(case):
+    op, T, Din, Dout, pl, pr, route, k, fill = case
+    if fill == "planted":
+        lhs, rhs = operands(op, T, Din, Dout, pl, pr, seed=T + k)
+    else:
+        lhs, rhs = operands(op, T, Din, Dout, pl, pr, seed=1)
+        # +0 is 0x0000; 1.5 is 0x3FC0 in bf16
+        lhs = np.full_like(lhs, 0 if fill == "zeros" else 0x3FC0)
+        rhs = np.full_like(rhs, 0 if fill == "zeros" else 0x3FC0)
+    ref = run_and_compare(op, lhs, rhs, T, Din, Dout, pl, pr, route, k)
+    if fill == "zeros":
+        assert not np.any(ref["C"])
+    if ref["idx"] is not None and fill != "planted":
+        assert np.array_equal(ref["idx"], np.arange(k))
+
+
 def test_deterministic_reruns():
     # K = 4096 over 6 tiles: the K-split path, whose parts are added in order.
     op, T, Din, Dout = "WGRAD", 4096, 768, 512
