@@ -10,7 +10,9 @@
 // are read coalesced (consecutive lanes = consecutive columns); a candidate
 // row is one 128-byte run, read as 8 16-byte loads when aligned. With the
 // full 64-element probe the values stay in registers between the two passes.
-// The first selection level computes the scores itself, in registers.
+// The first selection level computes the scores itself, in registers;
+// line_scores_kernel writes every candidate's score out on its own (the
+// pattern calibration's input).
 //
 // Selection without a host round trip, by radix select on the fp64 score
 // bits (see foid_select_kernel): 512-thread workgroups, digit counts by
