@@ -1,0 +1,46 @@
+"""Seeded random whole products against the oracle: every op, pattern pair
+and route, sizes from 1 to about 700 (the contraction a multiple of 32),
+outlier ranks from 1 to the number of candidate lines. Bit-exact route,
+FOID indices, codes and scales; the GEMM bar on the output (tests/parity.py)."""
+import numpy as np
+import pytest
+
+import mxfp4_precision_gemms_amd as A
+from test_gpu_parity import operands, run_and_compare
+
+pytestmark = pytest.mark.gpu
+
+OPS = ("FWD", "DGRAD", "WGRAD")
+PATS = ("N", "R", "C")
+ROUTES = (None, None, None, "IHT", "MXFP4", "OE_LEFT", "OE_RIGHT", "OE_INNER", "BF16")
+
+
+def random_case(i):
+    rng = np.random.default_rng(9000 + i)
+    op = OPS[i % 3]
+    dims = [int(rng.integers(1, 700)) for _ in range(3)]
+    T, Din, Dout = dims
+    # the contraction length is a multiple of 32
+    c = {"FWD": 1, "DGRAD": 2, "WGRAD": 0}[op]
+    dims[c] = 32 * int(rng.integers(1, 22))
+    T, Din, Dout = dims
+    pl, pr = PATS[int(rng.integers(0, 3))], PATS[int(rng.integers(0, 3))]
+    route = ROUTES[int(rng.integers(0, len(ROUTES)))]
+    plan = A.adahop_gemm_plan(op, T, Din, Dout, pl, pr, route, 1)
+    k = 1
+    if plan.scan_tensor >= 0:
+        shape = {"FWD": ((T, Din), (Dout, Din)), "DGRAD": ((T, Dout), (Dout, Din)),
+                 "WGRAD": ((T, Dout), (T, Din))}[op][plan.scan_tensor]
+        ncand = shape[0] if plan.scan_axis == 0 else shape[1]
+        k = int(rng.integers(1, min(ncand, 128) + 1))
+    return op, T, Din, Dout, pl, pr, route, k
+
+
+CASES = [random_case(i) for i in range(36)]
+
+
+@pytest.mark.parametrize("case", CASES, ids=[str(c) for c in CASES])
+def test_random_product(case):
+    op, T, Din, Dout, pl, pr, route, k = case
+    lhs, rhs = operands(op, T, Din, Dout, pl, pr, seed=T * 7 + Din * 3 + Dout)
+    run_and_compare(op, lhs, rhs, T, Din, Dout, pl, pr, route, k)
