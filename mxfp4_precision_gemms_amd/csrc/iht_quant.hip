@@ -11,7 +11,7 @@
 //   contract COLS (blocks along a row, K contiguous in memory): one thread
 //     owns 16 consecutive elements (two 16-byte loads); 2 lanes form a block.
 //     Butterfly strides 1 to 8 run in registers, stride 16 across the 2 lanes
-//     by a lane shuffle; the block amax takes one shuffle.
+//     by a DPP lane swap; the block amax takes one more.
 //   contract ROWS (blocks down a column): one thread owns 4 adjacent columns
 //     of one 32-row block; each row is one 8-byte load; each column's
 //     butterfly runs in registers; results are staged in LDS and written as
@@ -58,6 +58,12 @@ __device__ __forceinline__ uint32_t pack8_e2m1(const float* y, float scale) {
   w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, y[4], y[5], scale, 2);
   w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, y[6], y[7], scale, 3);
   return w;
+}
+
+// The value held by lane l ^ 1 (DPP quad permutation [1, 0, 3, 2]: a VALU
+// operand modifier, no LDS traffic).
+__device__ __forceinline__ float pair_swap(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, true));
 }
 
 __device__ __forceinline__ float e8m0_as_f32(int s) {
@@ -174,11 +180,14 @@ iht_quant_rowwise_kernel(const uint16_t* __restrict__ src, int64_t rows, int64_t
         y[i + h] = a - b;
       }
     }
-    // stride 16: the two lanes of the block
+    // stride 16: the two lanes of the block. The lower lane forms y + o, the
+    // upper one o - y, both as o + (+-y): negation is exact and addition
+    // commutes, so the sums are the same bits.
+    const uint32_t neg = upper ? 0x80000000u : 0u;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      const float o = __shfl_xor(y[i], 1);
-      y[i] = upper ? (o - y[i]) : (y[i] + o);
+      const float o = pair_swap(y[i]);
+      y[i] = o + __uint_as_float(__float_as_uint(y[i]) ^ neg);
     }
     const float c = __uint_as_float(0x3E3504F3u);   // fp32(1/sqrt(32))
 #pragma unroll
@@ -188,7 +197,7 @@ iht_quant_rowwise_kernel(const uint16_t* __restrict__ src, int64_t rows, int64_t
   float amax = 0.0f;
 #pragma unroll
   for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(y[i]));
-  amax = fmaxf(amax, __shfl_xor(amax, 1));
+  amax = fmaxf(amax, pair_swap(amax));
   const int sx = block_exponent(amax);
   const float scale = e8m0_as_f32(sx);
   const uint32_t lo = pack8_e2m1(y, scale), hi = pack8_e2m1(y + 8, scale);
