@@ -1,0 +1,86 @@
+"""Calls on different streams and from different host threads: the
+library's per-device second stream is shared under a lock, each call's
+fork and join stay ordered on its own stream, and every result equals the
+same call run alone."""
+import threading
+
+import numpy as np
+import pytest
+import torch
+
+import mxfp4_precision_gemms_amd as A
+from test_gpu_parity import operands
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+CASES = [
+    # op, T, Din, Dout, pl, pr, k  (OE_RIGHT / OE_LEFT: the second stream is used)
+    ("WGRAD", 1024, 384, 512, "R", "C", 16),
+    ("DGRAD", 512, 640, 1024, "R", "N", 8),
+    ("WGRAD", 2048, 256, 200, "C", "N", 32),
+    ("FWD", 300, 1024, 200, "R", "N", 8),
+]
+
+
+def dev_bf16(x):
+    return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).to(DEV).view(torch.bfloat16)
+
+
+def inputs():
+    out = []
+    for i, (op, T, Din, Dout, pl, pr, k) in enumerate(CASES):
+        lhs, rhs = operands(op, T, Din, Dout, pl, pr, seed=77 + i)
+        out.append((op, dev_bf16(lhs), dev_bf16(rhs), pl, pr, k))
+    return out
+
+
+def call(c, stream=None):
+    op, L, R, pl, pr, k = c
+    with torch.cuda.stream(stream or torch.cuda.current_stream()):
+        return A.adahop_gemm(op, L, R, pl, pr, None, k)
+
+
+def test_concurrent_streams_match_serial():
+    data = inputs()
+    ref = [call(c) for c in data]
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream() for _ in data]
+    for s in streams:
+        s.wait_stream(torch.cuda.current_stream())
+    for _ in range(3):
+        got = [call(c, s) for c, s in zip(data, streams)]
+        for s in streams:
+            torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        for r, g in zip(ref, got):
+            assert torch.equal(r.view(torch.int16), g.view(torch.int16))
+
+
+def test_host_threads_match_serial():
+    data = inputs()
+    ref = [call(c) for c in data]
+    torch.cuda.synchronize()
+    results = [None] * len(data)
+    errors = []
+
+    def worker(i):
+        try:
+            s = torch.cuda.Stream()
+            outs = []
+            for _ in range(4):
+                outs.append(call(data[i], s))
+            s.synchronize()
+            results[i] = outs
+        except Exception as e:   # reported below, on the main thread
+            errors.append(e)
+
+    threads = [threading.Thread(target=worker, args=(i,)) for i in range(len(data))]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    assert not errors, errors
+    for r, outs in zip(ref, results):
+        for g in outs:
+            assert torch.equal(r.view(torch.int16), g.view(torch.int16))
