@@ -187,3 +187,44 @@ def test_classify_pattern_matches_oracle():
         for th in (2.0, 8.0, 50.0):
             assert A.adahop_classify_pattern(r, c, th) == oracle.classify_pattern(r, c, th), (r, c, th)
     assert A.lib().adahop_classify_pattern(None, 3, None, 3, 8.0) == 0
+
+
+def test_header_is_plain_c_and_links(tmp_path):
+    # include/adahop.h as strict C11, linked against the built library, with
+    # host-only calls (no device is touched).
+    import os
+    import shutil
+    import subprocess
+    if shutil.which("gcc") is None:
+        pytest.skip("gcc not available")
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    libdir = os.path.join(root, "mxfp4_precision_gemms_amd")
+    src = tmp_path / "abi.c"
+    src.write_text(r'''
+#include "adahop.h"
+#include <stdio.h>
+#include <string.h>
+int main(void) {
+  if (adahop_route(ADAHOP_OP_WGRAD, ADAHOP_PAT_ROW, ADAHOP_PAT_COL) != ADAHOP_ROUTE_OE_RIGHT) return 1;
+  if (adahop_route(ADAHOP_OP_FWD, ADAHOP_PAT_COL, ADAHOP_PAT_NONE) != ADAHOP_ROUTE_IHT) return 2;
+  adahop_plan p;
+  if (adahop_gemm_plan(ADAHOP_OP_WGRAD, 32768, 14336, 4096, ADAHOP_PAT_ROW, ADAHOP_PAT_COL,
+                       ADAHOP_ROUTE_AUTO, 64, &p) != ADAHOP_OK) return 3;
+  if (p.route != ADAHOP_ROUTE_OE_RIGHT || p.k != 64 || p.ws_bytes == 0 ||
+      p.ws_bytes != adahop_gemm_workspace_size(ADAHOP_OP_WGRAD, 32768, 14336, 4096, ADAHOP_PAT_ROW,
+                                               ADAHOP_PAT_COL, ADAHOP_ROUTE_AUTO, 64)) return 4;
+  const double rows[4] = {1, 2, 3, 16}, cols[2] = {1, 1};
+  if (adahop_classify_pattern(rows, 4, cols, 2, 8.0) != ADAHOP_PAT_ROW) return 5;
+  if (adahop_detect(NULL, 10, 20, 20, ADAHOP_AXIS_ROWS, 64, 5, NULL, NULL, 0, NULL) != ADAHOP_ERR_INVALID) return 6;
+  if (strlen(adahop_last_error()) == 0) return 7;
+  printf("%s\n", adahop_status_string(ADAHOP_ERR_WORKSPACE));
+  return 0;
+}
+''')
+    exe = tmp_path / "abi"
+    subprocess.run(["gcc", "-std=c11", "-Wall", "-Wextra", "-pedantic", "-Werror",
+                    "-I" + os.path.join(root, "include"), str(src), "-L" + libdir, "-ladahop",
+                    "-Wl,-rpath," + libdir, "-o", str(exe)], check=True)
+    r = subprocess.run([str(exe)], capture_output=True, text=True)
+    assert r.returncode == 0, (r.returncode, r.stdout, r.stderr)
+    assert "workspace" in r.stdout
