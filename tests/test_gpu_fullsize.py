@@ -58,6 +58,9 @@ CALLS = [
     ("l31_8b_oproj_triplet_bs1", 2),
     ("l31_8b_oproj_triplet_bs16", 0), ("l31_8b_oproj_triplet_bs16", 1),
     ("l31_8b_oproj_triplet_bs16", 2),
+    ("l31_8b_oproj_triplet_bs2", 2), ("l31_8b_oproj_triplet_bs4", 1),
+    ("l31_8b_oproj_triplet_bs8", 0), ("l31_8b_oproj_triplet_bs8", 1),
+    ("l31_8b_oproj_triplet_bs8", 2),
 ]
 
 
