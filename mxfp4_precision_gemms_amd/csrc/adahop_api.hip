@@ -1,11 +1,11 @@
 // Host side of the AdaHOP library: argument checks, routing, workspace plans
 // and the launch sequence of one product. Every check runs before the first
 // launch; the library never allocates or synchronizes.
+#include <algorithm>
 #include <climits>
 #include <cstring>
-#include <mutex>
-#include <algorithm>
 #include <limits>
+#include <mutex>
 #include <string>
 #include <vector>
 
