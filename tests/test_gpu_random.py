@@ -1,7 +1,9 @@
 """Seeded random whole products against the oracle: every op, pattern pair
-and route, sizes from 1 to about 700 (the contraction a multiple of 32),
-outlier ranks from 1 to the number of candidate lines. Bit-exact route,
-FOID indices, codes and scales; the GEMM bar on the output (tests/parity.py)."""
+and route; small sizes (1 to about 700, the contraction a multiple of 32,
+every output checked) and larger ones (up to ~3000 with the contraction up
+to 8192, sampled outputs plus outlier lines), outlier ranks from 1 to the
+number of candidate lines. Bit-exact route, FOID indices, codes and scales;
+the GEMM bar on the output (tests/parity.py)."""
 import numpy as np
 import pytest
 
@@ -44,3 +46,52 @@ def test_random_product(case):
     op, T, Din, Dout, pl, pr, route, k = case
     lhs, rhs = operands(op, T, Din, Dout, pl, pr, seed=T * 7 + Din * 3 + Dout)
     run_and_compare(op, lhs, rhs, T, Din, Dout, pl, pr, route, k)
+
+
+ROUTES_LARGE = (None, None, "IHT", "MXFP4", "OE_LEFT", "OE_RIGHT", "OE_INNER")
+
+
+def random_large_case(i):
+    """Sizes up to ~3000 with the contraction up to 8192 (K-chunked packing,
+    K splits of the last round of tiles, ragged tiles), ranks up to 256."""
+    rng = np.random.default_rng(50000 + i)
+    op = OPS[i % 3]
+    dims = [int(rng.integers(1, 3000)) for _ in range(3)]
+    c = {"FWD": 1, "DGRAD": 2, "WGRAD": 0}[op]
+    dims[c] = int(rng.choice([512, 1024, 1536, 2048, 4096, 8192, 128 * int(rng.integers(1, 64))]))
+    T, Din, Dout = dims
+    pl, pr = PATS[int(rng.integers(0, 3))], PATS[int(rng.integers(0, 3))]
+    route = ROUTES_LARGE[int(rng.integers(0, len(ROUTES_LARGE)))]
+    plan = A.adahop_gemm_plan(op, T, Din, Dout, pl, pr, route, 1)
+    k = 1
+    if plan.scan_tensor >= 0:
+        shape = {"FWD": ((T, Din), (Dout, Din)), "DGRAD": ((T, Dout), (Dout, Din)),
+                 "WGRAD": ((T, Dout), (T, Din))}[op][plan.scan_tensor]
+        ncand = shape[0] if plan.scan_axis == 0 else shape[1]
+        k = int(rng.integers(1, min(ncand, 256) + 1))
+    return op, T, Din, Dout, pl, pr, route, k
+
+
+LARGE_CASES = [random_large_case(i) for i in range(24)]
+
+
+@pytest.mark.parametrize("case", LARGE_CASES, ids=[str(c) for c in LARGE_CASES])
+def test_random_large_product(case):
+    import oracle
+    op, T, Din, Dout, pl, pr, route, k = case
+    lhs, rhs = operands(op, T, Din, Dout, pl, pr, seed=T + Din + Dout)
+    plan = A.adahop_gemm_plan(op, T, Din, Dout, pl, pr, route, k)
+    rng = np.random.default_rng(T * Din)
+    rows = np.unique(rng.choice(plan.m, min(24, plan.m), replace=False))
+    cols = np.unique(rng.choice(plan.n, min(24, plan.n), replace=False))
+    rname = A.ROUTE_NAME[plan.route]
+    if rname in ("OE_LEFT", "OE_RIGHT"):
+        # every sampled set also holds outlier lines, where the scatter-add lands
+        tensor, axis = oracle.scan_target(op, rname)
+        idx = oracle.foid(lhs if tensor == 0 else rhs, axis, k)
+        if rname == "OE_LEFT":
+            rows = np.unique(np.concatenate([rows, idx[:8]]))
+        else:
+            cols = np.unique(np.concatenate([cols, idx[:8]]))
+    run_and_compare(op, lhs, rhs, T, Din, Dout, pl, pr, route, k,
+                    rows=rows.astype(np.int64), cols=cols.astype(np.int64))
