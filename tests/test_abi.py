@@ -228,3 +228,39 @@ int main(void) {
     r = subprocess.run([str(exe)], capture_output=True, text=True)
     assert r.returncode == 0, (r.returncode, r.stdout, r.stderr)
     assert "workspace" in r.stdout
+
+
+@pytest.mark.parametrize("op", ["FWD", "DGRAD", "WGRAD"])
+@pytest.mark.parametrize("pl,pr,route", [("C", "N", None), ("R", "N", None), ("N", "R", None),
+                                         ("N", "C", None), ("R", "C", None), ("C", "N", "OE_INNER"),
+                                         ("N", "N", "MXFP4")])
+@pytest.mark.parametrize("dims", [(256, 128, 192), (4096, 1024, 512), (320, 544, 1056)])
+def test_plan_regions_do_not_overlap(op, pl, pr, route, dims):
+    # The regions the plan reports (indices, both packed operands, gathered
+    # lines) lie inside the workspace without overlapping, each sized from the
+    # plan's own m, n, K, k.
+    T, Din, Dout = dims
+    p = A.adahop_gemm_plan(op, T, Din, Dout, pl, pr, route, 8)
+    if A.ROUTE_NAME[p.route] == "BF16":
+        assert p.ws_bytes == 0
+        return
+    none = (1 << 64) - 1
+    lines = {"FWD": (T, Din, Dout, Din), "DGRAD": (T, Dout, Dout, Din), "WGRAD": (T, Dout, T, Din)}[op]
+    lhs_rows, lhs_cols, rhs_rows, rhs_cols = lines
+    regions = [(p.off_a_codes, p.m * p.K // 2), (p.off_a_scales, p.m * p.K // 32),
+               (p.off_b_codes, p.n * p.K // 2), (p.off_b_scales, p.n * p.K // 32)]
+    if p.off_idx != none:
+        regions.append((p.off_idx, 4 * p.k))
+    # gathered lines: k lines of the extracted axis (a row holds cols
+    # elements, a column rows); the lhs is scanned along the plan's axis, the
+    # rhs along it too (OE_RIGHT) or along its contraction (OE_INNER)
+    rhs_contract = {"FWD": 1, "DGRAD": 0, "WGRAD": 0}[op]
+    if p.off_lhs_lines != none:
+        regions.append((p.off_lhs_lines, 2 * p.k * (lhs_cols if p.scan_axis == 0 else lhs_rows)))
+    if p.off_rhs_lines != none:
+        ax = p.scan_axis if p.scan_tensor == 1 else rhs_contract
+        regions.append((p.off_rhs_lines, 2 * p.k * (rhs_cols if ax == 0 else rhs_rows)))
+    regions.sort()
+    for (o1, s1), (o2, _) in zip(regions, regions[1:]):
+        assert o1 + s1 <= o2, regions
+    assert regions[-1][0] + regions[-1][1] <= p.ws_bytes
