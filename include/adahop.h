@@ -242,12 +242,13 @@ typedef struct {
  * outlier product's partial sums (OE_LEFT/OE_RIGHT) and, when K is a multiple
  * of 512, a copy of both scale arrays reordered for the GEMM plus, when the
  * last round of 256 x 256 tiles is split along K (at most 128 tiles left
- * over from whole rounds of 256, K / 128 a multiple of 8), 256 KB of fp32
- * partial sums per tile part (0 when none applies; ws may then be NULL). Its
- * contents after the call are unspecified.
- * Errors: INVALID for NULL pointers, K mismatch, K % 32 != 0, ldc < n, bad
- * OE descriptors; WORKSPACE for a missing or short workspace; UNSUPPORTED for
- * k > 1024 or a misaligned workspace. */
+ * over from whole rounds of 256, K / 128 a multiple of 8 and at least 32),
+ * 256 KB of fp32 partial sums per tile part (0 when none applies; ws may then
+ * be NULL). Its contents after the call are unspecified.
+ * Errors: INVALID for NULL pointers, K mismatch, K % 32 != 0, ldc < n, a bad
+ * out_dtype, bad OE descriptors; WORKSPACE for a missing or short workspace;
+ * UNSUPPORTED for k > 1024, codes not 16-byte aligned or a misaligned
+ * workspace. */
 ADAHOP_API size_t adahop_gemm_mx_workspace_size(int64_t m, int64_t n, int64_t K,
                                                 const adahop_oe* oe);
 ADAHOP_API adahop_status adahop_gemm_mx(const adahop_mx_operand* A,
