@@ -88,6 +88,10 @@ struct Plan {
   int splits = 0;
   size_t off_foid = SIZE_MAX, off_partials = SIZE_MAX, off_gemm = SIZE_MAX;
   size_t foid_bytes = 0, gemm_bytes = 0;
+  // BF16 route on the ring kernel: K-major copies of the operands that are
+  // not contiguous along K.
+  bool bf16_ring = false;
+  size_t off_lhs_t = SIZE_MAX, off_rhs_t = SIZE_MAX;
 };
 
 constexpr size_t kNone = SIZE_MAX;
@@ -115,7 +119,22 @@ adahop_status make_plan(adahop_op op, int64_t T, int64_t Din, int64_t Dout,
   pb.layout = ADAHOP_LAYOUT_ROWS;
   pb.off_idx = pb.off_a_codes = pb.off_a_scales = pb.off_b_codes = pb.off_b_scales = kNone;
   pb.off_lhs_lines = pb.off_rhs_lines = kNone;
-  if (route == ADAHOP_ROUTE_BF16) { pb.ws_bytes = 0; return ADAHOP_OK; }
+  if (route == ADAHOP_ROUTE_BF16) {
+    // K % 128 == 0: the ring kernel on bf16 matrix cores, on operands
+    // transposed into the workspace where they are not contiguous along K.
+    pb.ws_bytes = 0;
+    if (bf16_ring_ok(s.m, s.n, s.K)) {
+      size_t off = 0;
+      auto take = [&](size_t bytes) { size_t o = off; off += align_up(bytes, kAlign); return o; };
+      P->bf16_ring = true;
+      if (s.lhs_contract == ADAHOP_AXIS_ROWS) P->off_lhs_t = take(2 * (size_t)s.m * (size_t)s.K);
+      if (s.rhs_contract == ADAHOP_AXIS_ROWS) P->off_rhs_t = take(2 * (size_t)s.n * (size_t)s.K);
+      P->gemm_bytes = bf16_ring_scratch_bytes(s.m, s.n, s.K);
+      if (P->gemm_bytes) P->off_gemm = take(P->gemm_bytes);
+      pb.ws_bytes = off;
+    }
+    return ADAHOP_OK;
+  }
 
   const bool oe = route == ADAHOP_ROUTE_OE_LEFT || route == ADAHOP_ROUTE_OE_RIGHT ||
                   route == ADAHOP_ROUTE_OE_INNER;
@@ -257,7 +276,33 @@ adahop_status run_gemm(adahop_op op, const uint16_t* lhs, const uint16_t* rhs, i
   ADAHOP_TRY(E.record(0));
 
   if (pb.route == ADAHOP_ROUTE_BF16) {
-    for (int i = 1; i <= 4; ++i) ADAHOP_TRY(E.record(i));
+    ADAHOP_TRY(E.record(1));
+    // The ring kernel needs 16-byte aligned operands and workspace; with
+    // any of them misaligned the product runs on the tile kernel instead.
+    const bool lhs_k = s.lhs_contract == ADAHOP_AXIS_COLS, rhs_k = s.rhs_contract == ADAHOP_AXIS_COLS;
+    if (P.bf16_ring && (!lhs_k || aligned16(lhs)) && (!rhs_k || aligned16(rhs)) &&
+        (pb.ws_bytes == 0 || aligned16(ws))) {
+      char* w = static_cast<char*>(ws);
+      const uint16_t* a = lhs;
+      const uint16_t* b = rhs;
+      if (!lhs_k) {
+        uint16_t* t = reinterpret_cast<uint16_t*>(w + P.off_lhs_t);
+        ADAHOP_TRY(bf16_transpose_launch(lhs, s.lhs_rows, s.lhs_cols, s.lhs_cols, t, stream));
+        a = t;
+      }
+      ADAHOP_TRY(E.record(2));
+      if (!rhs_k) {
+        uint16_t* t = reinterpret_cast<uint16_t*>(w + P.off_rhs_t);
+        ADAHOP_TRY(bf16_transpose_launch(rhs, s.rhs_rows, s.rhs_cols, s.rhs_cols, t, stream));
+        b = t;
+      }
+      ADAHOP_TRY(E.record(3));
+      ADAHOP_TRY(E.record(4));
+      ADAHOP_TRY(bf16_ring_launch(a, b, s.m, s.n, s.K, out, s.n, out_f32,
+                                  P.gemm_bytes ? w + P.off_gemm : nullptr, P.gemm_bytes, stream));
+      return E.record(5);
+    }
+    for (int i = 2; i <= 4; ++i) ADAHOP_TRY(E.record(i));
     ADAHOP_TRY(bf16_gemm_launch(stored_view(lhs, s.lhs_cols, s.lhs_contract),
                                 stored_view(rhs, s.rhs_cols, s.rhs_contract), s.m, s.n, s.K, out,
                                 s.n, out_f32, stream));

@@ -575,14 +575,23 @@ struct RingItem {
 // split parts of the last round after them. Before a tile's epilogue the
 // next item's first four stages are already in flight, so the ring refills
 // while the accumulators are stored.
-template <bool Chunked>
+//
+// Bf16: the operands are plain bf16 rows (A [m, K], B [n, K], row stride K),
+// no scales. A 64-byte stage row is then 32 elements and a 16-byte fragment
+// is the 8 bf16 that v_mfma_f32_32x32x16_bf16 takes per lane (k = 8 (l / 32)
+// .. +7 of a 16-deep step) -- the FP4 fragment's place in the row, so the
+// ring, the swizzle and the fragment reads are the same; each wave issues 4
+// loads per stage instead of 5.
+template <bool Chunked, bool Bf16>
 __global__ void __launch_bounds__(kRing8Threads, 1) gemm_mx_ring8_kernel(GemmArgs g) {
+  static_assert(!(Chunked && Bf16), "bf16 operands come in rows");
+  constexpr int kLoads = Bf16 ? 4 : kLoads8PerStage;   // per wave per stage
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   // Wave-uniform (scalar): the scale loads below pick their descriptor by it.
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 2, wn = wave & 3;
-  const int64_t Kb = g.K / 2;
+  const int64_t Kb = Bf16 ? g.K * 2 : g.K / 2;         // bytes per row
   const int64_t Ks = g.K / 32;
   const int nk = (int)(Kb / RBK);
   const int items = g.split_full + g.split_count * g.split_parts;
@@ -669,12 +678,14 @@ __global__ void __launch_bounds__(kRing8Threads, 1) gemm_mx_ring8_kernel(GemmArg
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
           it.rb, (lds_void*)&ring_slot<slot>().b[1024 * (2 * wave + j)], 16, it.voffb[j], kt * stage_b, 0, 0);
     }
-    if (sc_a)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsa, (lds_void*)&ring_slot<slot>().sa[256 * (wave & 3)],
-                                               4, it.soff, kt * sstage, 0, 0);
-    else
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsb, (lds_void*)&ring_slot<slot>().sb[256 * (wave & 3)],
-                                               4, it.soff, kt * sstage, 0, 0);
+    if constexpr (!Bf16) {
+      if (sc_a)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsa, (lds_void*)&ring_slot<slot>().sa[256 * (wave & 3)],
+                                                 4, it.soff, kt * sstage, 0, 0);
+      else
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsb, (lds_void*)&ring_slot<slot>().sb[256 * (wave & 3)],
+                                                 4, it.soff, kt * sstage, 0, 0);
+    }
   };
   auto issue_first4 = [&](const RingItem& it) {
     issue(it, std::integral_constant<int, 0>{}, it.kt0);
@@ -702,19 +713,24 @@ __global__ void __launch_bounds__(kRing8Threads, 1) gemm_mx_ring8_kernel(GemmArg
   // meanwhile) gets registers of its own: a read into a register that an
   // in-flight MFMA still reads would have to wait for that MFMA.
   auto keep = [](const Frags& f) {
-    asm volatile("" ::"v"(f.a[0]), "v"(f.a[1]), "v"(f.a[2]), "v"(f.a[3]), "v"(f.b[0]), "v"(f.b[1]),
-                 "v"(f.sa[0]), "v"(f.sa[1]), "v"(f.sa[2]), "v"(f.sa[3]), "v"(f.sb[0]), "v"(f.sb[1]));
+    if constexpr (Bf16)
+      asm volatile("" ::"v"(f.a[0]), "v"(f.a[1]), "v"(f.a[2]), "v"(f.a[3]), "v"(f.b[0]), "v"(f.b[1]));
+    else
+      asm volatile("" ::"v"(f.a[0]), "v"(f.a[1]), "v"(f.a[2]), "v"(f.a[3]), "v"(f.b[0]), "v"(f.b[1]),
+                   "v"(f.sa[0]), "v"(f.sa[1]), "v"(f.sa[2]), "v"(f.sa[3]), "v"(f.sb[0]), "v"(f.sb[1]));
   };
   auto read_frags = [&](auto S, auto KS, Frags& f) {
     constexpr int slot = decltype(S)::value;
     constexpr int ks = decltype(KS)::value;
     const int sw = ((2 * ks + khalf) ^ lswz) << 4;
+    if constexpr (!Bf16) {
 #pragma unroll
-    for (int i = 0; i < R8_FM; ++i)
-      f.sa[i] = *reinterpret_cast<const uint16_t*>(&ring_slot<slot>().sa[sa_off + 128 * i]);
+      for (int i = 0; i < R8_FM; ++i)
+        f.sa[i] = *reinterpret_cast<const uint16_t*>(&ring_slot<slot>().sa[sa_off + 128 * i]);
 #pragma unroll
-    for (int j = 0; j < R8_FN; ++j)
-      f.sb[j] = *reinterpret_cast<const uint16_t*>(&ring_slot<slot>().sb[sb_off + 128 * j]);
+      for (int j = 0; j < R8_FN; ++j)
+        f.sb[j] = *reinterpret_cast<const uint16_t*>(&ring_slot<slot>().sb[sb_off + 128 * j]);
+    }
 #pragma unroll
     for (int i = 0; i < R8_FM; ++i) {
       f.a[i] = *reinterpret_cast<const v4i*>(&ring_slot<slot>().a[fa_base + sw + 2048 * i]);
@@ -730,9 +746,13 @@ __global__ void __launch_bounds__(kRing8Threads, 1) gemm_mx_ring8_kernel(GemmArg
     static_for<R8_FM>([&](auto I) {
       static_for<R8_FN>([&](auto J) {
         const v4i fb = f.b[J], fa = f.a[I];
-        acc[I][J] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-            v8i{fb[0], fb[1], fb[2], fb[3], 0, 0, 0, 0}, v8i{fa[0], fa[1], fa[2], fa[3], 0, 0, 0, 0},
-            acc[I][J], 4, 4, kSel, f.sb[J], kSel, f.sa[I]);
+        if constexpr (Bf16)
+          acc[I][J] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+              __builtin_bit_cast(v8bf, fb), __builtin_bit_cast(v8bf, fa), acc[I][J], 0, 0, 0);
+        else
+          acc[I][J] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+              v8i{fb[0], fb[1], fb[2], fb[3], 0, 0, 0, 0}, v8i{fa[0], fa[1], fa[2], fa[3], 0, 0, 0, 0},
+              acc[I][J], 4, 4, kSel, f.sb[J], kSel, f.sa[I]);
       });
     });
   };
@@ -746,29 +766,44 @@ __global__ void __launch_bounds__(kRing8Threads, 1) gemm_mx_ring8_kernel(GemmArg
     constexpr int slot = decltype(S)::value;
     read_frags(std::integral_constant<int, slot>{}, std::integral_constant<int, 1>{}, y);
     mma(x, std::integral_constant<int, 0>{});
+    // 8 MFMAs with the 12 (bf16: 6) fragment and scale reads between them.
     static_for<6>([&](auto) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);   // DS read
+      __builtin_amdgcn_sched_group_barrier(0x100, Bf16 ? 1 : 2, 0);   // DS read
     });
     __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
     __builtin_amdgcn_sched_barrier(0);
     keep(x);
-    __builtin_amdgcn_s_waitcnt(waitcnt_imm(2 * kLoads8PerStage, 0));
+    __builtin_amdgcn_s_waitcnt(waitcnt_imm(2 * kLoads, 0));
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
     issue(it, std::integral_constant<int, slot>{}, kt + 4 < it.kt1 ? kt + 4 : it.kt1 - 1);
     read_frags(std::integral_constant<int, (slot + 1) % kRingSlots>{}, std::integral_constant<int, 0>{}, x);
     mma(y, std::integral_constant<int, 1>{});
-    static_for<5>([&](auto) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
-      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // VMEM read
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);   // DS read
-    });
-    static_for<2>([&](auto) {
+    if constexpr (Bf16) {
+      // 8 MFMAs with the 4 ring loads and 6 fragment reads between them.
+      static_for<4>([&](auto) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // VMEM read
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // DS read
+      });
+      static_for<2>([&](auto) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      });
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+    } else {
+      static_for<5>([&](auto) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // VMEM read
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);   // DS read
+      });
+      static_for<2>([&](auto) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      });
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-    });
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    }
     __builtin_amdgcn_sched_barrier(0);
     keep(y);
   };
@@ -789,7 +824,7 @@ __global__ void __launch_bounds__(kRing8Threads, 1) gemm_mx_ring8_kernel(GemmArg
       });
     });
     Frags fx, fy;
-    __builtin_amdgcn_s_waitcnt(waitcnt_imm(3 * kLoads8PerStage, 0));
+    __builtin_amdgcn_s_waitcnt(waitcnt_imm(3 * kLoads, 0));
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
     read_frags(std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{}, fx);
@@ -1216,9 +1251,10 @@ struct TailSplit {
   int64_t full, split;   // whole tiles, split tiles
   int parts;
 };
-TailSplit tail_split(int64_t m, int64_t n, int64_t K) {
+// nk: the number of ring stages along K (K / 128 for FP4, K / 32 for bf16).
+TailSplit tail_split(int64_t m, int64_t n, int64_t nk) {
   const int64_t tiles = ((m + BM - 1) / BM) * ((n + BN - 1) / BN);
-  const int64_t rem = tiles % kSplitCUs, nk = K / 128;
+  const int64_t rem = tiles % kSplitCUs;
   int parts = 1;
   if (rem > 0 && 2 * rem <= kSplitCUs) {
     parts = (int)(kSplitCUs / rem < 4 ? kSplitCUs / rem : 4);
@@ -1228,8 +1264,8 @@ TailSplit tail_split(int64_t m, int64_t n, int64_t K) {
   return {tiles - rem, rem, parts};
 }
 
-size_t split_ws_bytes(int64_t m, int64_t n, int64_t K) {
-  const TailSplit ts = tail_split(m, n, K);
+size_t split_ws_bytes(int64_t m, int64_t n, int64_t nk) {
+  const TailSplit ts = tail_split(m, n, nk);
   return (size_t)ts.split * (size_t)ts.parts * (size_t)kSplitPartF4 * sizeof(float4);
 }
 
@@ -1246,7 +1282,7 @@ bool gemm_mx_kchunk_ok(int64_t m, int64_t n, int64_t K) {
 
 size_t gemm_mx_scratch_bytes(int64_t m, int64_t n, int64_t K, int layout) {
   if (m < 1 || n < 1 || !ring_shape_ok(m, n, K)) return 0;
-  return (layout == ADAHOP_LAYOUT_ROWS ? staging_bytes(m, n, K) : 0) + split_ws_bytes(m, n, K);
+  return (layout == ADAHOP_LAYOUT_ROWS ? staging_bytes(m, n, K) : 0) + split_ws_bytes(m, n, K / 128);
 }
 
 namespace {
@@ -1319,7 +1355,7 @@ adahop_status gemm_mx_launch(const uint8_t* a_codes, const uint8_t* a_scales,
       g.a_sst = static_cast<const uint32_t*>(scratch);
       g.b_sst = staged_b(scratch, m, K);
     }
-    const TailSplit ts = tail_split(m, n, K);
+    const TailSplit ts = tail_split(m, n, K / 128);
     g.split_full = (int)ts.full;
     g.split_count = (int)ts.split;
     g.split_parts = ts.parts;
@@ -1330,9 +1366,9 @@ adahop_status gemm_mx_launch(const uint8_t* a_codes, const uint8_t* a_scales,
     const int64_t items = ts.full + ts.split * ts.parts;
     const dim3 rgrid((unsigned)(items < kSplitCUs ? items : kSplitCUs));
     if (kchunk)
-      gemm_mx_ring8_kernel<true><<<rgrid, dim3(kRing8Threads), 0, stream>>>(g);
+      gemm_mx_ring8_kernel<true, false><<<rgrid, dim3(kRing8Threads), 0, stream>>>(g);
     else
-      gemm_mx_ring8_kernel<false><<<rgrid, dim3(kRing8Threads), 0, stream>>>(g);
+      gemm_mx_ring8_kernel<false, false><<<rgrid, dim3(kRing8Threads), 0, stream>>>(g);
     if (ts.split) {
       const adahop_status ls = check_launch("gemm_mx");
       if (ls != ADAHOP_OK) return ls;
@@ -1344,6 +1380,120 @@ adahop_status gemm_mx_launch(const uint8_t* a_codes, const uint8_t* a_scales,
   else
     gemm_mx_kernel<false><<<grid, block, 0, stream>>>(g);
   return check_launch("gemm_mx");
+}
+
+// ---------------------------------------------------------------------------
+// BF16 route on the ring kernel: operands bf16 in rows of K (row stride K),
+// ring stages of 32 elements. A bf16 tile row of one workgroup is 2 K bytes,
+// so 256 of them must stay below kPastEnd.
+// ---------------------------------------------------------------------------
+bool bf16_ring_ok(int64_t m, int64_t n, int64_t K) {
+  const int64_t tiles = ((m + BM - 1) / BM) * ((n + BN - 1) / BN);
+  return m >= 1 && n >= 1 && K % 128 == 0 && K > 0 && (int64_t)BM * 2 * K < kPastEnd &&
+         tiles <= 0x7FFFFFFF;
+}
+
+size_t bf16_ring_scratch_bytes(int64_t m, int64_t n, int64_t K) {
+  return bf16_ring_ok(m, n, K) ? split_ws_bytes(m, n, K / 32) : 0;
+}
+
+adahop_status bf16_ring_launch(const uint16_t* a, const uint16_t* b, int64_t m, int64_t n,
+                               int64_t K, void* C, int64_t ldc, int out_f32, void* scratch,
+                               size_t scratch_bytes, hipStream_t stream) {
+  if (!bf16_ring_ok(m, n, K) || ((reinterpret_cast<uintptr_t>(a) | reinterpret_cast<uintptr_t>(b)) & 15u))
+    return fail(ADAHOP_ERR_UNSUPPORTED, "bf16 ring: K % 128 != 0, too long or misaligned operands");
+  const adahop_status st = check_scratch(scratch, scratch_bytes, bf16_ring_scratch_bytes(m, n, K));
+  if (st != ADAHOP_OK) return st;
+  GemmArgs g{};
+  g.a_codes = reinterpret_cast<const uint8_t*>(a);
+  g.b_codes = reinterpret_cast<const uint8_t*>(b);
+  g.m = m; g.n = n; g.K = K; g.C = C; g.ldc = ldc; g.out_f32 = out_f32;
+  g.tiles_m = (int)((m + BM - 1) / BM); g.tiles_n = (int)((n + BN - 1) / BN);
+  g.oe_mode = 0;
+  g.vec_ok = (ldc % (out_f32 ? 4 : 8) == 0) && ((reinterpret_cast<uintptr_t>(C) & 15u) == 0);
+  const TailSplit ts = tail_split(m, n, K / 32);
+  g.split_full = (int)ts.full;
+  g.split_count = (int)ts.split;
+  g.split_parts = ts.parts;
+  g.split_ws = ts.split ? static_cast<float*>(scratch) : nullptr;
+  const int64_t items = ts.full + ts.split * ts.parts;
+  const dim3 rgrid((unsigned)(items < kSplitCUs ? items : kSplitCUs));
+  gemm_mx_ring8_kernel<false, true><<<rgrid, dim3(kRing8Threads), 0, stream>>>(g);
+  if (ts.split) {
+    const adahop_status ls = check_launch("bf16 ring");
+    if (ls != ADAHOP_OK) return ls;
+    gemm_split_fixup_kernel<<<dim3((unsigned)(ts.split * (BM / kFixRows))), dim3(kFixThreads), 0,
+                              stream>>>(g);
+  }
+  return check_launch("bf16 ring");
+}
+
+namespace {
+// dst[c][r] = src[r][c] for a bf16 [rows, cols] matrix (leading dim ld);
+// dst is [cols, rows], leading dim rows. 64 x 64 tiles through LDS: thread t
+// copies 16-byte chunk t % 8 of tile rows t / 8 and t / 8 + 32 in, then
+// writes the 8 tile rows 8 (t % 8) .. +7 of tile columns t / 8 and t / 8 +
+// 32 out. Chunk q of tile row r sits at chunk q ^ ((r / 8) % 8), so the
+// column reads of a wave (8 rows 8 apart, one chunk group each) fall in
+// distinct banks.
+constexpr int kTT = 64;
+__global__ void __launch_bounds__(256)
+bf16_transpose_kernel(const uint16_t* __restrict__ src, int64_t rows, int64_t cols, int64_t ld,
+                      uint16_t* __restrict__ dst, int vec_in, int vec_out) {
+  __shared__ __attribute__((aligned(16))) uint16_t tile[kTT * kTT];
+  const int64_t r0 = (int64_t)blockIdx.x * kTT, c0 = (int64_t)blockIdx.y * kTT;
+  const int t = threadIdx.x, q = t & 7, rr = t >> 3;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int r = rr + 32 * h;
+    const int64_t gr = r0 + r, gc = c0 + 8 * q;
+    uint4 v = make_uint4(0, 0, 0, 0);
+    if (gr < rows) {
+      if (vec_in && gc + 8 <= cols) {
+        v = *reinterpret_cast<const uint4*>(src + gr * ld + gc);
+      } else {
+        uint16_t e[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) e[j] = gc + j < cols ? src[gr * ld + gc + j] : 0;
+        v = make_uint4(e[0] | (uint32_t)e[1] << 16, e[2] | (uint32_t)e[3] << 16,
+                       e[4] | (uint32_t)e[5] << 16, e[6] | (uint32_t)e[7] << 16);
+      }
+    }
+    *reinterpret_cast<uint4*>(&tile[r * kTT + 8 * (q ^ ((r >> 3) & 7))]) = v;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int c = rr + 32 * h;
+    const int64_t gc = c0 + c, gr = r0 + 8 * q;
+    if (gc >= cols) continue;
+    uint16_t e[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) e[j] = tile[(8 * q + j) * kTT + 8 * ((c >> 3) ^ q) + (c & 7)];
+    uint16_t* out = dst + gc * rows + gr;
+    if (vec_out && gr + 8 <= rows) {
+      *reinterpret_cast<uint4*>(out) =
+          make_uint4(e[0] | (uint32_t)e[1] << 16, e[2] | (uint32_t)e[3] << 16,
+                     e[4] | (uint32_t)e[5] << 16, e[6] | (uint32_t)e[7] << 16);
+    } else {
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        if (gr + j < rows) out[j] = e[j];
+    }
+  }
+}
+}  // namespace
+
+adahop_status bf16_transpose_launch(const uint16_t* src, int64_t rows, int64_t cols, int64_t ld,
+                                    uint16_t* dst, hipStream_t stream) {
+  const int64_t gx = (rows + kTT - 1) / kTT, gy = (cols + kTT - 1) / kTT;
+  if (rows < 1 || cols < 1 || ld < cols || gx > 0x7FFFFFFF || gy > 65535)
+    return fail(ADAHOP_ERR_UNSUPPORTED, "bf16 transpose: bad or too large shape");
+  const int vec_in = ld % 8 == 0 && (reinterpret_cast<uintptr_t>(src) & 15u) == 0;
+  const int vec_out = rows % 8 == 0 && (reinterpret_cast<uintptr_t>(dst) & 15u) == 0;
+  bf16_transpose_kernel<<<dim3((unsigned)gx, (unsigned)gy), dim3(256), 0, stream>>>(
+      src, rows, cols, ld, dst, vec_in, vec_out);
+  return check_launch("bf16 transpose");
 }
 
 }  // namespace adahop

@@ -69,8 +69,24 @@ def test_plan_errors():
     with pytest.raises(A.AdahopError) as e:
         A.adahop_gemm_plan("WGRAD", 4096, 4096, 64, "R", "C", None, 2000)
     assert e.value.status == 2                               # above 1024
-    # The BF16 route needs no workspace and accepts any K.
+    # The BF16 route accepts any K; with K % 128 != 0 it needs no workspace.
     assert A.adahop_gemm_plan("FWD", 64, 100, 64, "R", "R").ws_bytes == 0
+
+
+def test_bf16_route_workspace():
+    # K % 128 == 0: the ring kernel. FWD operands are contiguous along K, and
+    # 2 tiles with 16 stages of 32 along K are not split: nothing.
+    assert A.adahop_gemm_plan("FWD", 300, 512, 200, "N", "N", "BF16").ws_bytes == 0
+    # WGRAD: K-major copies of GY^T [Dout, T] and X^T [Din, T] (multiples of
+    # 256 bytes), then the one tile split along K in 2 parts of 256 KB (32
+    # stages: 4 parts of 8 would be too short, 3 do not divide them).
+    p = A.adahop_gemm_plan("WGRAD", 1024, 200, 72, "C", "C")
+    assert A.ROUTE_NAME[p.route] == "BF16"
+    assert p.ws_bytes == 2 * 72 * 1024 + 2 * 200 * 1024 + 2 * 262144
+    # DGRAD: W^T [Din, Dout] only (2 * 132 * 384 = 101376 = 396 * 256).
+    assert A.adahop_gemm_plan("DGRAD", 520, 132, 384, "N", "N", "BF16").ws_bytes == 101376
+    # 2 tiles, 64 stages: each split along K in 4 parts of 256 KB.
+    assert A.adahop_gemm_plan("FWD", 300, 2048, 200, "N", "N", "BF16").ws_bytes == 2 * 4 * 262144
 
 
 def test_argument_checks_return_before_any_launch():
@@ -241,10 +257,15 @@ def test_plan_regions_do_not_overlap(op, pl, pr, route, dims):
     # plan's own m, n, K, k.
     T, Din, Dout = dims
     p = A.adahop_gemm_plan(op, T, Din, Dout, pl, pr, route, 8)
-    if A.ROUTE_NAME[p.route] == "BF16":
-        assert p.ws_bytes == 0
-        return
     none = (1 << 64) - 1
+    if A.ROUTE_NAME[p.route] == "BF16":
+        # No packed operands; with K % 128 == 0, K-major copies of the
+        # operands not contiguous along K (DGRAD: W; WGRAD: both).
+        assert all(o == none for o in (p.off_idx, p.off_a_codes, p.off_a_scales, p.off_b_codes,
+                                       p.off_b_scales, p.off_lhs_lines, p.off_rhs_lines))
+        copies = {"FWD": 0, "DGRAD": 2 * p.n * p.K, "WGRAD": 2 * (p.m + p.n) * p.K}[op]
+        assert p.ws_bytes >= copies if p.K % 128 == 0 else p.ws_bytes == 0
+        return
     lines = {"FWD": (T, Din, Dout, Din), "DGRAD": (T, Dout, Dout, Din), "WGRAD": (T, Dout, T, Din)}[op]
     lhs_rows, lhs_cols, rhs_rows, rhs_cols = lines
     regions = [(p.off_a_codes, p.m * p.K // 2), (p.off_a_scales, p.m * p.K // 32),
