@@ -16,8 +16,12 @@ oracle timed on the host's cores on a bounded sample.
 
 `--rank-sweep` prints instead the latency and error of the product at
 outlier ranks 0-256 and in plain MXFP4 (the pages' variant study, Fig. 10).
+`--route NAME` times the workload's product on another route, e.g. BF16
+(the all-bf16 route; its roofline is then the bf16 GEMM's, against the bf16
+peak).
 """
 import argparse
+import dataclasses
 import hashlib
 import json
 import os
@@ -30,6 +34,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = ("effective TFLOPS per AdaHOP GEMM (FOID+IHT+quant+GEMM+OE) and % MXFP4 MFMA peak")
 PEAK_FP4_TFLOPS = 10100.0      # MI355X dense MXFP4 matrix-core peak
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 matrix-core peak
 PEAK_HBM_GBS = 8000.0
 
 
@@ -196,6 +201,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="l8b_down_wgrad")
     ap.add_argument("--out-dtype", default="bf16", choices=["bf16", "f32"])
+    ap.add_argument("--route", default=None,
+                    choices=["IHT", "OE_LEFT", "OE_RIGHT", "OE_INNER", "MXFP4", "BF16"],
+                    help="time the workload's product on this route instead of the one its "
+                         "pattern pair selects (BF16: the all-bf16 route)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-bf16-baseline", action="store_true")
     ap.add_argument("--rank-sweep", action="store_true",
@@ -231,6 +240,8 @@ def main():
         sys.exit(f"unknown workload {args.workload}; choose from {sorted(wls)}")
     wl, ci = wls[args.workload]
     call = wl.calls[ci]
+    if args.route is not None:
+        call = dataclasses.replace(call, route=args.route)
     op = call.op
     T, Din, Dout = wl.T, wl.Din, wl.Dout
     m, n, K = gemm_dims(op, T, Din, Dout)
@@ -291,6 +302,8 @@ def main():
     value = flops / (ms_per_step / 1e3) / 1e12
     gemm_ms = stage_ms["gemm"]
     achieved = flops / (gemm_ms / 1e3) / 1e12
+    bf16 = route == "BF16"
+    peak = PEAK_BF16_TFLOPS if bf16 else PEAK_FP4_TFLOPS
 
     result = {
         "metric": METRIC,
@@ -303,14 +316,17 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "mxfp4",
+        "dtype": "bf16" if bf16 else "mxfp4",
         "data": "synthetic",
         "config": {"workload": wl.name, "op": op, "route": route, "m": m, "n": n, "K": K,
                    "oe_rank": plan.k, "pattern_pair": call.pat_lhs + call.pat_rhs,
                    "out_dtype": args.out_dtype},
         "pct_mxfp4_peak": round(100 * value / PEAK_FP4_TFLOPS, 2),
         "stages_ms": {k: round(v, 4) for k, v in stage_ms.items()},
-        "stages_note": ("the operand FOID does not scan is quantized on a second stream, beside "
+        "stages_note": ("quant_lhs and quant_rhs are the K-major copies of the operands that are "
+                        "not contiguous along K; gemm is the bf16 MFMA kernel plus, when its last "
+                        "round is split along K, the fixup kernel") if bf16 else
+                       ("the operand FOID does not scan is quantized on a second stream, beside "
                         "FOID, the other quantization and the outlier product: its slot is empty "
                         "and the other slots overlap it; gemm is the MFMA kernel plus, when its "
                         "last round is split along K, the fixup kernel")
@@ -319,16 +335,22 @@ def main():
                         "the fixup kernel"),
         "call_ms_events": round(call_ms, 4),
         "roofline": {"bound": "mfma",
-                     "kernel": ("gemm_mx_ring8_kernel + gemm_split_fixup_kernel (FP4 MFMA GEMM, "
+                     "kernel": ("gemm_mx_ring8_kernel<bf16> + gemm_split_fixup_kernel (bf16 MFMA "
+                                "GEMM; the fixup adds the K-parts of a split last round)") if bf16 else
+                               ("gemm_mx_ring8_kernel + gemm_split_fixup_kernel (FP4 MFMA GEMM, "
                                 "fused scatter-add epilogue; the fixup adds the K-parts of a "
                                 "split last round)"),
-                     "achieved": round(achieved, 1), "peak": PEAK_FP4_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP4_TFLOPS, 4),
+                     "achieved": round(achieved, 1), "peak": peak,
+                     "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
                      "traffic": None},
     }
-    traffic, note = measured_traffic(wl.name)
-    result["roofline"]["traffic"] = None if traffic is None else round(traffic)
-    result["roofline"]["traffic_note"] = note
+    if bf16:
+        del result["pct_mxfp4_peak"]
+        result["roofline"]["traffic_note"] = "HBM counters not taken for the bf16 kernel"
+    else:
+        traffic, note = measured_traffic(wl.name)
+        result["roofline"]["traffic"] = None if traffic is None else round(traffic)
+        result["roofline"]["traffic_note"] = note
 
     if not args.no_bf16_baseline:
         # All-bf16 reference product on hipBLASLt (torch.matmul), same shapes.
@@ -350,6 +372,8 @@ def main():
         # with unit E8M0 scales), same m, n, K: a library reference for the
         # GEMM stage alone.
         try:
+            if bf16:
+                raise NotImplementedError("the BF16 route has no MXFP4 GEMM stage")
             f4 = torch.float4_e2m1fn_x2
             e8 = torch.float8_e8m0fnu
             qa = torch.randint(0, 256, (m, K // 2), dtype=torch.uint8, device=dev).view(f4)
@@ -370,7 +394,9 @@ def main():
             del qa, qb, sa, sb
         except Exception as ex:          # no MXFP4 GEMM in this torch build
             result["hipblaslt_mxfp4_gemm_ms"] = None
-            print(f"# hipBLASLt MXFP4 reference unavailable: {type(ex).__name__}", file=sys.stderr)
+            if not bf16:
+                print(f"# hipBLASLt MXFP4 reference unavailable: {type(ex).__name__}",
+                      file=sys.stderr)
 
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(op, lhs_np, rhs_np, T, Din, Dout, call, m, n, K)

@@ -131,3 +131,47 @@ def test_full_size_call(name, ci):
     rel16, loose = check_bf16(C16, ref["C"], ref["absC"], K, f"{name} {op} bf16")
     say(f"  {route} m={m} n={n} K={K}: sampled {rows.size}x{cols.size}, rel f32 {rel:.2e}, "
         f"rel bf16 {rel16:.2e}, elements under the ulp+gamma rule {loose}")
+
+
+BF16_CALLS = [
+    ("l31_8b_down_wgrad", 0),                                   # WGRAD: GY and X transposed
+    ("l31_8b_gateup_fwd_dgrad", 0), ("l31_8b_gateup_fwd_dgrad", 1),   # FWD; DGRAD: W transposed
+    ("l31_8b_oproj_triplet_bs1", 0),                            # 1024 x 4096 x 4096
+]
+
+
+@pytest.mark.parametrize("name,ci", BF16_CALLS, ids=[f"{n}-{c}" for n, c in BF16_CALLS])
+def test_full_size_bf16_route(name, ci):
+    # The same products forced onto the BF16 route (the ring kernel on bf16
+    # matrix cores at these sizes), as the benchmark's --route BF16 times
+    # them: sampled outputs against the oracle's fp64 product, and one
+    # rounding over the whole output.
+    wl = workload(name)
+    call = wl.calls[ci]
+    op, T, Din, Dout = call.op, wl.T, wl.Din, wl.Dout
+    say("full size BF16 route", name, ci, op, (T, Din, Dout))
+    lhs = wl.tensors[call.lhs].make(0)
+    rhs = wl.tensors[call.rhs].make(0)
+    plan = A.adahop_gemm_plan(op, T, Din, Dout, call.pat_lhs, call.pat_rhs, "BF16", 1)
+    m, n, K = plan.m, plan.n, plan.K
+    assert K % 128 == 0
+    ws = torch.empty(max(plan.ws_bytes, 1), dtype=torch.uint8, device=DEV)
+    L, R = dev_bf16(lhs), dev_bf16(rhs)
+    c32 = A.adahop_gemm(op, L, R, call.pat_lhs, call.pat_rhs, "BF16", 1,
+                        out_dtype=torch.float32, ws=ws)
+    c16 = A.adahop_gemm(op, L, R, call.pat_lhs, call.pat_rhs, "BF16", 1,
+                        out_dtype=torch.bfloat16, ws=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(c32.to(torch.bfloat16).view(torch.int16), c16.view(torch.int16))
+    del L, R
+    rng = np.random.default_rng(2000 + ci)
+    rows, cols = sample_lines(rng, m, 48), sample_lines(rng, n, 48)
+    ref = pipeline.gemm(op, lhs, rhs, T, Din, Dout, call.pat_lhs, call.pat_rhs,
+                        route="BF16", k=1, rows=rows, cols=cols)
+    assert ref["route"] == "BF16"
+    C32 = host(c32[torch.from_numpy(rows).to(DEV)][:, torch.from_numpy(cols).to(DEV)])
+    C16 = host(c16[torch.from_numpy(rows).to(DEV)][:, torch.from_numpy(cols).to(DEV)])
+    rel = check_f32(C32, ref["C"], ref["absC"], K, f"{name} {op} BF16 f32")
+    rel16, loose = check_bf16(C16, ref["C"], ref["absC"], K, f"{name} {op} BF16 bf16")
+    say(f"  BF16 m={m} n={n} K={K}: sampled {rows.size}x{cols.size}, rel f32 {rel:.2e}, "
+        f"rel bf16 {rel16:.2e}, elements under the ulp+gamma rule {loose}")
