@@ -271,7 +271,14 @@ ADAHOP_API adahop_status adahop_gemm_mx(const adahop_mx_operand* A,
  * the operands are in the plan's layout (KCHUNK when the contraction length
  * is a multiple of 512 and each packed operand is under 2 GiB, else ROWS).
  * Errors: as for the stage calls; INVALID for a bad op or route, or an OE
- * route with oe_rank < 1 or above the number of candidate lines. */
+ * route with oe_rank < 1 or above the number of candidate lines.
+ * Route BF16 (both operands hurt) computes the plain product on bf16 matrix
+ * cores with fp32 accumulation and no packed operands (oe_rank is ignored).
+ * When the contraction length is a multiple of 128 its workspace holds
+ * K-major bf16 copies of the operands that are not contiguous along K (DGRAD:
+ * W; WGRAD: GY and X) and the fp32 parts of tiles split along K; otherwise it
+ * needs none. With an operand or the workspace not 16-byte aligned it runs
+ * on a slower tile kernel instead. */
 typedef struct {
   adahop_route_t route;   /* resolved route */
   int64_t m, n, K;        /* textbook-frame sizes */
@@ -311,7 +318,8 @@ ADAHOP_API adahop_status adahop_gemm(adahop_op op, const uint16_t* lhs, const ui
  * that does not run records its event right after the previous one). With
  * OE_LEFT and OE_RIGHT the operand FOID does not scan is quantized on a
  * second stream: its stage is empty here, the ROWS-layout scale reordering
- * falls in the GEMM stage, and the other stages overlap with it. */
+ * falls in the GEMM stage, and the other stages overlap with it. With route
+ * BF16 the lhs and rhs stages are the operands' K-major copies. */
 #define ADAHOP_STAGE_EVENTS 6
 ADAHOP_API adahop_status adahop_gemm_timed(adahop_op op, const uint16_t* lhs,
                                            const uint16_t* rhs, int64_t T, int64_t Din,
