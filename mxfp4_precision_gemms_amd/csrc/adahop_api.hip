@@ -88,9 +88,10 @@ struct Plan {
   int splits = 0;
   size_t off_foid = SIZE_MAX, off_partials = SIZE_MAX, off_gemm = SIZE_MAX;
   size_t foid_bytes = 0, gemm_bytes = 0;
-  // BF16 route on the ring kernel: K-major copies of the operands that are
-  // not contiguous along K.
+  // BF16 route on the ring kernel: operands not contiguous along K are read
+  // in place (across K) or, where that does not apply, from K-major copies.
   bool bf16_ring = false;
+  bool lhs_across = false, rhs_across = false;
   size_t off_lhs_t = SIZE_MAX, off_rhs_t = SIZE_MAX;
 };
 
@@ -120,15 +121,23 @@ adahop_status make_plan(adahop_op op, int64_t T, int64_t Din, int64_t Dout,
   pb.off_idx = pb.off_a_codes = pb.off_a_scales = pb.off_b_codes = pb.off_b_scales = kNone;
   pb.off_lhs_lines = pb.off_rhs_lines = kNone;
   if (route == ADAHOP_ROUTE_BF16) {
-    // K % 128 == 0: the ring kernel on bf16 matrix cores, on operands
-    // transposed into the workspace where they are not contiguous along K.
+    // K % 128 == 0: the ring kernel on bf16 matrix cores. An operand not
+    // contiguous along K ([K, cols] stored) is read in place when its row
+    // length is a multiple of 8 and it is under 2 GiB, else transposed into
+    // the workspace first.
     pb.ws_bytes = 0;
     if (bf16_ring_ok(s.m, s.n, s.K)) {
       size_t off = 0;
       auto take = [&](size_t bytes) { size_t o = off; off += align_up(bytes, kAlign); return o; };
       P->bf16_ring = true;
-      if (s.lhs_contract == ADAHOP_AXIS_ROWS) P->off_lhs_t = take(2 * (size_t)s.m * (size_t)s.K);
-      if (s.rhs_contract == ADAHOP_AXIS_ROWS) P->off_rhs_t = take(2 * (size_t)s.n * (size_t)s.K);
+      if (s.lhs_contract == ADAHOP_AXIS_ROWS) {
+        P->lhs_across = bf16_ring_across_ok(s.K, s.lhs_cols);
+        if (!P->lhs_across) P->off_lhs_t = take(2 * (size_t)s.m * (size_t)s.K);
+      }
+      if (s.rhs_contract == ADAHOP_AXIS_ROWS) {
+        P->rhs_across = bf16_ring_across_ok(s.K, s.rhs_cols);
+        if (!P->rhs_across) P->off_rhs_t = take(2 * (size_t)s.n * (size_t)s.K);
+      }
       P->gemm_bytes = bf16_ring_scratch_bytes(s.m, s.n, s.K);
       if (P->gemm_bytes) P->off_gemm = take(P->gemm_bytes);
       pb.ws_bytes = off;
@@ -279,26 +288,27 @@ adahop_status run_gemm(adahop_op op, const uint16_t* lhs, const uint16_t* rhs, i
     ADAHOP_TRY(E.record(1));
     // The ring kernel needs 16-byte aligned operands and workspace; with
     // any of them misaligned the product runs on the tile kernel instead.
-    const bool lhs_k = s.lhs_contract == ADAHOP_AXIS_COLS, rhs_k = s.rhs_contract == ADAHOP_AXIS_COLS;
-    if (P.bf16_ring && (!lhs_k || aligned16(lhs)) && (!rhs_k || aligned16(rhs)) &&
+    const bool lhs_copy = P.off_lhs_t != kNone, rhs_copy = P.off_rhs_t != kNone;
+    if (P.bf16_ring && (lhs_copy || aligned16(lhs)) && (rhs_copy || aligned16(rhs)) &&
         (pb.ws_bytes == 0 || aligned16(ws))) {
       char* w = static_cast<char*>(ws);
       const uint16_t* a = lhs;
       const uint16_t* b = rhs;
-      if (!lhs_k) {
+      if (lhs_copy) {
         uint16_t* t = reinterpret_cast<uint16_t*>(w + P.off_lhs_t);
         ADAHOP_TRY(bf16_transpose_launch(lhs, s.lhs_rows, s.lhs_cols, s.lhs_cols, t, stream));
         a = t;
       }
       ADAHOP_TRY(E.record(2));
-      if (!rhs_k) {
+      if (rhs_copy) {
         uint16_t* t = reinterpret_cast<uint16_t*>(w + P.off_rhs_t);
         ADAHOP_TRY(bf16_transpose_launch(rhs, s.rhs_rows, s.rhs_cols, s.rhs_cols, t, stream));
         b = t;
       }
       ADAHOP_TRY(E.record(3));
       ADAHOP_TRY(E.record(4));
-      ADAHOP_TRY(bf16_ring_launch(a, b, s.m, s.n, s.K, out, s.n, out_f32,
+      ADAHOP_TRY(bf16_ring_launch(a, P.lhs_across, s.lhs_cols, b, P.rhs_across, s.rhs_cols,
+                                  s.m, s.n, s.K, out, s.n, out_f32,
                                   P.gemm_bytes ? w + P.off_gemm : nullptr, P.gemm_bytes, stream));
       return E.record(5);
     }

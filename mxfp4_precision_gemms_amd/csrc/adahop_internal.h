@@ -53,15 +53,20 @@ adahop_status oe_reduce_launch(float* partials, int splits, int64_t count, hipSt
 // Full bf16 product written to C (the BF16 route): C[i][j] = sum_t X(i,t) Y(j,t).
 adahop_status bf16_gemm_launch(Bf16View X, Bf16View Y, int64_t m, int64_t n, int64_t K,
                                void* C, int64_t ldc, int out_f32, hipStream_t stream);
-// The same product on the FP4 GEMM's ring kernel with bf16 matrix cores:
-// a [m, K] and b [n, K] row-major (row stride K, 16-byte aligned), K % 128
-// == 0 (bf16_ring_ok); `scratch` holds bf16_ring_scratch_bytes(m, n, K)
-// bytes (the split tiles' fp32 parts, 16-byte aligned).
+// The same product on the FP4 GEMM's ring kernel with bf16 matrix cores,
+// K % 128 == 0 (bf16_ring_ok). Each operand is 16-byte aligned and either
+// along K (a [m, K] row-major, row stride K) or, with *_across, stored
+// across K (a [K, lda] row-major holding a(i, t) at t * lda + i; lda % 8 ==
+// 0 and under 2 GiB: bf16_ring_across_ok). `scratch` holds
+// bf16_ring_scratch_bytes(m, n, K) bytes (the split tiles' fp32 parts,
+// 16-byte aligned).
 bool bf16_ring_ok(int64_t m, int64_t n, int64_t K);
+bool bf16_ring_across_ok(int64_t K, int64_t ld);
 size_t bf16_ring_scratch_bytes(int64_t m, int64_t n, int64_t K);
-adahop_status bf16_ring_launch(const uint16_t* a, const uint16_t* b, int64_t m, int64_t n,
-                               int64_t K, void* C, int64_t ldc, int out_f32, void* scratch,
-                               size_t scratch_bytes, hipStream_t stream);
+adahop_status bf16_ring_launch(const uint16_t* a, int a_across, int64_t lda, const uint16_t* b,
+                               int b_across, int64_t ldb, int64_t m, int64_t n, int64_t K, void* C,
+                               int64_t ldc, int out_f32, void* scratch, size_t scratch_bytes,
+                               hipStream_t stream);
 // dst [cols, rows] (leading dim rows) = transpose of src [rows, cols]
 // (leading dim ld).
 adahop_status bf16_transpose_launch(const uint16_t* src, int64_t rows, int64_t cols, int64_t ld,

@@ -41,6 +41,8 @@ typedef int v8i __attribute__((ext_vector_type(8)));
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef short v4s16 __attribute__((ext_vector_type(4)));
+typedef int v2i __attribute__((ext_vector_type(2)));
 
 // gfx950 converts to bf16 in hardware, rounding to nearest even (finite
 // inputs; the tests check it against the integer rounding rule).
@@ -113,6 +115,8 @@ struct GemmArgs {
   int vec_ok;                   // C rows allow 16-byte stores (ldc % 4 fp32 / % 8 bf16, C aligned)
   const uint16_t* ia_ptr; int64_t ia_ld; int ia_inner;   // OE_INNER a: (i, p)
   const uint16_t* ib_ptr; int64_t ib_ld; int ib_inner;   // OE_INNER b: (j, p)
+  // bf16 operands stored across K ([K][ld], ring kernel): bytes per stored row
+  int64_t a_ldb, b_ldb;
 };
 
 __device__ __forceinline__ int lower_bound_i32(const int32_t* idx, int n, int64_t v) {
@@ -582,10 +586,27 @@ struct RingItem {
 // .. +7 of a 16-deep step) -- the FP4 fragment's place in the row, so the
 // ring, the swizzle and the fragment reads are the same; each wave issues 4
 // loads per stage instead of 5.
-template <bool Chunked, bool Bf16>
+//
+// TA / TB (bf16 only): that operand is stored across K, [K][ld] with the
+// tile's 256 rows (of C) contiguous. A slot then holds 32 K-rows of 512
+// bytes; LDS-DMA load j of wave w fills K-rows 2 (2 w + j) + l / 32, lane l
+// putting logical 16-byte chunk (l % 32) ^ 4 h(k) at physical chunk l % 32,
+// h(k) = (k & 3) | ((k >> 3) & 1) << 2. A fragment is two
+// ds_read_b64_tr_b16: within each group of 16 lanes, lane i receives element
+// t of its result from the 4 elements at the address of lane 4 t + i / 4,
+// element i % 4. Lane L of group G addresses K-row 8 (G / 2) + 4 r + L / 4
+// (read r = 0, 1) and the 4 columns 16 (G % 2) + 4 (L % 4) .. +3 of the
+// 32-column block, so lane 16 G + i receives column 16 (G % 2) + i, K-rows
+// 8 (G / 2) + 4 r .. +3: the MFMA's layout. The swizzle puts the 8 K-rows
+// one read touches in 8 different 64-byte column groups.
+template <bool Chunked, bool Bf16, bool TA = false, bool TB = false>
 __global__ void __launch_bounds__(kRing8Threads, 1) gemm_mx_ring8_kernel(GemmArgs g) {
   static_assert(!(Chunked && Bf16), "bf16 operands come in rows");
+  static_assert(Bf16 || (!TA && !TB), "only bf16 operands are read across K");
   constexpr int kLoads = Bf16 ? 4 : kLoads8PerStage;   // per wave per stage
+  // LDS reads per K-step: fragments (two per operand block stored across K)
+  // and, for FP4, the scale words.
+  constexpr int kDs = (TA ? 2 : 1) * R8_FM + (TB ? 2 : 1) * R8_FN + (Bf16 ? 0 : R8_FM + R8_FN);
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   // Wave-uniform (scalar): the scale loads below pick their descriptor by it.
@@ -606,8 +627,14 @@ __global__ void __launch_bounds__(kRing8Threads, 1) gemm_mx_ring8_kernel(GemmArg
   // logical chunk (lane % 4) ^ swz(row).
   const int row0 = 32 * wave + (lane >> 2);
   const int chunk = (lane & 3) ^ ring_swz(row0);    // swz is the same for rows row0 + 16 j
-  const int stage_a = Chunked ? (int)g.m * RBK : RBK;
-  const int stage_b = Chunked ? (int)g.n * RBK : RBK;
+  const int stage_a = TA ? 32 * (int)g.a_ldb : Chunked ? (int)g.m * RBK : RBK;
+  const int stage_b = TB ? 32 * (int)g.b_ldb : Chunked ? (int)g.n * RBK : RBK;
+  // Operand stored across K: this lane's load j offset within a stage.
+  auto tr_voff = [&](int j, int64_t ldb) {
+    const int k = 2 * (2 * wave + j) + (lane >> 5);
+    const int h = (k & 3) | (((k >> 3) & 1) << 2);
+    return k * (int)ldb + 16 * ((lane & 31) ^ (4 * h));
+  };
   // Scales: waves 0-3 copy A rows 64 (w % 4) + lane, waves 4-7 B rows.
   const bool sc_a = wave < 4;
   const int srow = 64 * (wave & 3) + lane;
@@ -644,12 +671,21 @@ __global__ void __launch_bounds__(kRing8Threads, 1) gemm_mx_ring8_kernel(GemmArg
     it.n0 = (int64_t)it.tn * BN;
     const int rows_a = (int)(g.m - it.m0 < BM ? g.m - it.m0 : BM);
     const int rows_b = (int)(g.n - it.n0 < BN ? g.n - it.n0 : BN);
-    it.ra = Chunked
+    // Stored across K: the buffer starts at the tile's first column and runs
+    // to the end of the operand (columns past m or n read other columns or 0;
+    // they only reach rows of C that are not stored).
+    it.ra = TA
+        ? __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(g.a_codes + it.m0 * 2), 0,
+                                            (int)(g.K * g.a_ldb - it.m0 * 2), kBufferFlags)
+        : Chunked
         ? __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(g.a_codes + it.m0 * RBK), 0,
                                             (int)((nk * g.m - it.m0) * RBK), kBufferFlags)
         : __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(g.a_codes + it.m0 * Kb), 0,
                                             (int)(rows_a * Kb), kBufferFlags);
-    it.rb = Chunked
+    it.rb = TB
+        ? __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(g.b_codes + it.n0 * 2), 0,
+                                            (int)(g.K * g.b_ldb - it.n0 * 2), kBufferFlags)
+        : Chunked
         ? __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(g.b_codes + it.n0 * RBK), 0,
                                             (int)((nk * g.n - it.n0) * RBK), kBufferFlags)
         : __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(g.b_codes + it.n0 * Kb), 0,
@@ -661,7 +697,8 @@ __global__ void __launch_bounds__(kRing8Threads, 1) gemm_mx_ring8_kernel(GemmArg
         it.voffa[j] = r < rows_a ? r * RBK + chunk * 16 : kPastEnd;
         it.voffb[j] = r < rows_b ? r * RBK + chunk * 16 : kPastEnd;
       } else {
-        it.voffa[j] = it.voffb[j] = r * (int)Kb + chunk * 16;
+        it.voffa[j] = TA ? tr_voff(j, g.a_ldb) : r * (int)Kb + chunk * 16;
+        it.voffb[j] = TB ? tr_voff(j, g.b_ldb) : r * (int)Kb + chunk * 16;
       }
     }
     it.soff = sc_a ? (srow < rows_a ? (int)((it.m0 + srow) * 4) : kPastEnd)
@@ -704,6 +741,25 @@ __global__ void __launch_bounds__(kRing8Threads, 1) gemm_mx_ring8_kernel(GemmArg
   // its K-step 0 and K-step 1 scales in bytes 0 and 1 (the MFMA's op_sel).
   const int sa_off = (wm * R8_WM + lrow) * 4 + 2 * khalf, sb_off = (wn * R8_WN + lrow) * 4 + 2 * khalf;
 
+  // Operands stored across K: per-lane fragment offsets in a slot (K-step 0,
+  // read r = 0) of the MFMA blocks i (A) and j (B).
+  const int tL = lane & 15, tG = lane >> 4;
+  const int th = (tL >> 2) + 4 * (tG >> 1);
+  const int tbase = (8 * (tG >> 1) + (tL >> 2)) * 512 + 16 * (2 * (tG & 1) + ((tL & 3) >> 1)) +
+                    8 * (tL & 1);
+  int toff_a[R8_FM], toff_b[R8_FN];
+#pragma unroll
+  for (int i = 0; i < R8_FM; ++i) toff_a[i] = tbase + 64 * ((4 * wm + i) ^ th);
+#pragma unroll
+  for (int j = 0; j < R8_FN; ++j) toff_b[j] = tbase + 64 * ((2 * wn + j) ^ th);
+  auto tr_frag = [](const uint8_t* p) {
+    typedef __attribute__((address_space(3))) v4s16 lds_v4s16;
+    const v4s16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s16*)(p));
+    const v4s16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s16*)(p + 2048));
+    const v2i l = __builtin_bit_cast(v2i, lo), h = __builtin_bit_cast(v2i, hi);
+    return v4i{l[0], l[1], h[0], h[1]};
+  };
+
   // Fragments of one K-step (16 bytes each) with the stage's scale words.
   struct Frags {
     v4i a[R8_FM], b[R8_FN];
@@ -733,11 +789,17 @@ __global__ void __launch_bounds__(kRing8Threads, 1) gemm_mx_ring8_kernel(GemmArg
     }
 #pragma unroll
     for (int i = 0; i < R8_FM; ++i) {
-      f.a[i] = *reinterpret_cast<const v4i*>(&ring_slot<slot>().a[fa_base + sw + 2048 * i]);
+      if constexpr (TA)
+        f.a[i] = tr_frag(&ring_slot<slot>().a[toff_a[i] + 8192 * ks]);
+      else
+        f.a[i] = *reinterpret_cast<const v4i*>(&ring_slot<slot>().a[fa_base + sw + 2048 * i]);
     }
 #pragma unroll
     for (int j = 0; j < R8_FN; ++j) {
-      f.b[j] = *reinterpret_cast<const v4i*>(&ring_slot<slot>().b[fb_base + sw + 2048 * j]);
+      if constexpr (TB)
+        f.b[j] = tr_frag(&ring_slot<slot>().b[toff_b[j] + 8192 * ks]);
+      else
+        f.b[j] = *reinterpret_cast<const v4i*>(&ring_slot<slot>().b[fb_base + sw + 2048 * j]);
     }
   };
   // 8 MFMAs of K-step ks: scale byte ks of the 16 bits read.
@@ -766,10 +828,11 @@ __global__ void __launch_bounds__(kRing8Threads, 1) gemm_mx_ring8_kernel(GemmArg
     constexpr int slot = decltype(S)::value;
     read_frags(std::integral_constant<int, slot>{}, std::integral_constant<int, 1>{}, y);
     mma(x, std::integral_constant<int, 0>{});
-    // 8 MFMAs with the 12 (bf16: 6) fragment and scale reads between them.
-    static_for<6>([&](auto) {
+    // 8 MFMAs with the kDs fragment (and scale) reads between them.
+    static_for<6>([&](auto S) {
+      constexpr int s = decltype(S)::value;
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
-      __builtin_amdgcn_sched_group_barrier(0x100, Bf16 ? 1 : 2, 0);   // DS read
+      __builtin_amdgcn_sched_group_barrier(0x100, kDs / 6 + (s < kDs % 6 ? 1 : 0), 0);   // DS read
     });
     __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
     __builtin_amdgcn_sched_barrier(0);
@@ -781,15 +844,12 @@ __global__ void __launch_bounds__(kRing8Threads, 1) gemm_mx_ring8_kernel(GemmArg
     read_frags(std::integral_constant<int, (slot + 1) % kRingSlots>{}, std::integral_constant<int, 0>{}, x);
     mma(y, std::integral_constant<int, 1>{});
     if constexpr (Bf16) {
-      // 8 MFMAs with the 4 ring loads and 6 fragment reads between them.
-      static_for<4>([&](auto) {
+      // 8 MFMAs with the 4 ring loads and kDs fragment reads between them.
+      static_for<6>([&](auto S) {
+        constexpr int s = decltype(S)::value;
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
-        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // VMEM read
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // DS read
-      });
-      static_for<2>([&](auto) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        if constexpr (s < 4) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // VMEM read
+        __builtin_amdgcn_sched_group_barrier(0x100, kDs / 6 + (s < kDs % 6 ? 1 : 0), 0);   // DS read
       });
       __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
     } else {
@@ -1397,16 +1457,27 @@ size_t bf16_ring_scratch_bytes(int64_t m, int64_t n, int64_t K) {
   return bf16_ring_ok(m, n, K) ? split_ws_bytes(m, n, K / 32) : 0;
 }
 
-adahop_status bf16_ring_launch(const uint16_t* a, const uint16_t* b, int64_t m, int64_t n,
-                               int64_t K, void* C, int64_t ldc, int out_f32, void* scratch,
-                               size_t scratch_bytes, hipStream_t stream) {
+bool bf16_ring_across_ok(int64_t K, int64_t ld) {
+  return ld >= 1 && ld % 8 == 0 && K * ld * 2 < kPastEnd;
+}
+
+adahop_status bf16_ring_launch(const uint16_t* a, int a_across, int64_t lda, const uint16_t* b,
+                               int b_across, int64_t ldb, int64_t m, int64_t n, int64_t K, void* C,
+                               int64_t ldc, int out_f32, void* scratch, size_t scratch_bytes,
+                               hipStream_t stream) {
   if (!bf16_ring_ok(m, n, K) || ((reinterpret_cast<uintptr_t>(a) | reinterpret_cast<uintptr_t>(b)) & 15u))
     return fail(ADAHOP_ERR_UNSUPPORTED, "bf16 ring: K % 128 != 0, too long or misaligned operands");
+  if ((a_across && (lda < m || !bf16_ring_across_ok(K, lda))) ||
+      (b_across && (ldb < n || !bf16_ring_across_ok(K, ldb))))
+    return fail(ADAHOP_ERR_UNSUPPORTED, "bf16 ring: an operand stored across K needs ld % 8 == 0, "
+                                        "ld >= its rows of C and under 2 GiB");
   const adahop_status st = check_scratch(scratch, scratch_bytes, bf16_ring_scratch_bytes(m, n, K));
   if (st != ADAHOP_OK) return st;
   GemmArgs g{};
   g.a_codes = reinterpret_cast<const uint8_t*>(a);
   g.b_codes = reinterpret_cast<const uint8_t*>(b);
+  g.a_ldb = 2 * lda;
+  g.b_ldb = 2 * ldb;
   g.m = m; g.n = n; g.K = K; g.C = C; g.ldc = ldc; g.out_f32 = out_f32;
   g.tiles_m = (int)((m + BM - 1) / BM); g.tiles_n = (int)((n + BN - 1) / BN);
   g.oe_mode = 0;
@@ -1418,7 +1489,14 @@ adahop_status bf16_ring_launch(const uint16_t* a, const uint16_t* b, int64_t m, 
   g.split_ws = ts.split ? static_cast<float*>(scratch) : nullptr;
   const int64_t items = ts.full + ts.split * ts.parts;
   const dim3 rgrid((unsigned)(items < kSplitCUs ? items : kSplitCUs));
-  gemm_mx_ring8_kernel<false, true><<<rgrid, dim3(kRing8Threads), 0, stream>>>(g);
+  if (a_across && b_across)
+    gemm_mx_ring8_kernel<false, true, true, true><<<rgrid, dim3(kRing8Threads), 0, stream>>>(g);
+  else if (a_across)
+    gemm_mx_ring8_kernel<false, true, true, false><<<rgrid, dim3(kRing8Threads), 0, stream>>>(g);
+  else if (b_across)
+    gemm_mx_ring8_kernel<false, true, false, true><<<rgrid, dim3(kRing8Threads), 0, stream>>>(g);
+  else
+    gemm_mx_ring8_kernel<false, true><<<rgrid, dim3(kRing8Threads), 0, stream>>>(g);
   if (ts.split) {
     const adahop_status ls = check_launch("bf16 ring");
     if (ls != ADAHOP_OK) return ls;

@@ -77,14 +77,19 @@ def test_bf16_route_workspace():
     # K % 128 == 0: the ring kernel. FWD operands are contiguous along K, and
     # 2 tiles with 16 stages of 32 along K are not split: nothing.
     assert A.adahop_gemm_plan("FWD", 300, 512, 200, "N", "N", "BF16").ws_bytes == 0
-    # WGRAD: K-major copies of GY^T [Dout, T] and X^T [Din, T] (multiples of
-    # 256 bytes), then the one tile split along K in 2 parts of 256 KB (32
-    # stages: 4 parts of 8 would be too short, 3 do not divide them).
+    # WGRAD: GY and X read in place (rows of 72 and 200, multiples of 8); the
+    # one tile split along K in 2 parts of 256 KB (32 stages: 4 parts of 8
+    # would be too short, 3 do not divide them).
     p = A.adahop_gemm_plan("WGRAD", 1024, 200, 72, "C", "C")
     assert A.ROUTE_NAME[p.route] == "BF16"
-    assert p.ws_bytes == 2 * 72 * 1024 + 2 * 200 * 1024 + 2 * 262144
-    # DGRAD: W^T [Din, Dout] only (2 * 132 * 384 = 101376 = 396 * 256).
+    assert p.ws_bytes == 2 * 262144
+    # X's rows of 100 are not: a K-major copy of X^T [100, 1024] (204800 =
+    # 800 * 256 bytes), then the split parts.
+    assert A.adahop_gemm_plan("WGRAD", 1024, 100, 72, "C", "C").ws_bytes == 204800 + 2 * 262144
+    # DGRAD: W [384, 132] copied to W^T [132, 384] (101376 = 396 * 256); with
+    # rows of 136 it is read in place.
     assert A.adahop_gemm_plan("DGRAD", 520, 132, 384, "N", "N", "BF16").ws_bytes == 101376
+    assert A.adahop_gemm_plan("DGRAD", 520, 136, 384, "N", "N", "BF16").ws_bytes == 0
     # 2 tiles, 64 stages: each split along K in 4 parts of 256 KB.
     assert A.adahop_gemm_plan("FWD", 300, 2048, 200, "N", "N", "BF16").ws_bytes == 2 * 4 * 262144
 
@@ -260,10 +265,13 @@ def test_plan_regions_do_not_overlap(op, pl, pr, route, dims):
     none = (1 << 64) - 1
     if A.ROUTE_NAME[p.route] == "BF16":
         # No packed operands; with K % 128 == 0, K-major copies of the
-        # operands not contiguous along K (DGRAD: W; WGRAD: both).
+        # operands not contiguous along K (DGRAD: W; WGRAD: both) whose row
+        # length is not a multiple of 8 (the others are read in place).
         assert all(o == none for o in (p.off_idx, p.off_a_codes, p.off_a_scales, p.off_b_codes,
                                        p.off_b_scales, p.off_lhs_lines, p.off_rhs_lines))
-        copies = {"FWD": 0, "DGRAD": 2 * p.n * p.K, "WGRAD": 2 * (p.m + p.n) * p.K}[op]
+        copy = lambda rows, ld: 2 * rows * p.K if ld % 8 else 0
+        copies = {"FWD": 0, "DGRAD": copy(p.n, Din),
+                  "WGRAD": copy(p.m, Dout) + copy(p.n, Din)}[op]
         assert p.ws_bytes >= copies if p.K % 128 == 0 else p.ws_bytes == 0
         return
     lines = {"FWD": (T, Din, Dout, Din), "DGRAD": (T, Dout, Dout, Din), "WGRAD": (T, Dout, T, Din)}[op]

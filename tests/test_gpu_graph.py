@@ -37,7 +37,7 @@ CASES = [
     ("WGRAD", 4096, 768, 512, "R", "C", "OE_RIGHT"),   # second stream; K = 4096: split last round
     ("FWD", 1024, 1024, 520, "R", "N", "OE_LEFT"),     # second stream, FOID over 1024 rows
     ("FWD", 512, 2048, 384, "C", "N", "OE_INNER"),     # asked for: both operands zeroed, one stream
-    ("WGRAD", 2048, 320, 300, "C", "C", "BF16"),       # both copied K-major; 4 tiles in 4 K-parts
+    ("WGRAD", 2048, 320, 300, "C", "C", "BF16"),       # X in place, GY copied; 4 tiles in 4 K-parts
 ]
 
 

@@ -289,12 +289,16 @@ FULL_CASES = [
     ("WGRAD", 512, 384, 256, "R", "C", None, 8),        # OE_RIGHT (X cols)
     ("WGRAD", 512, 384, 256, "C", "N", None, 8),        # OE_LEFT (GY cols)
     ("WGRAD", 416, 160, 96, "R", "N", "OE_INNER", 8),
-    ("WGRAD", 128, 96, 64, "C", "C", None, 8),          # BF16 (ring kernel, both transposed)
-    # BF16 route, K % 128 == 0: the ring kernel on bf16 matrix cores, the
-    # operands that are not contiguous along K transposed first
+    ("WGRAD", 128, 96, 64, "C", "C", None, 8),          # BF16 (ring kernel, both in place)
+    # BF16 route, K % 128 == 0: the ring kernel on bf16 matrix cores; an
+    # operand not contiguous along K is read across K in place, or from a
+    # K-major copy when its row length is not a multiple of 8
     ("FWD", 300, 512, 200, "R", "R", None, 8),          # both contiguous, ragged tiles
-    ("DGRAD", 520, 132, 384, "N", "N", "BF16", 8),      # W transposed, row length % 8 != 0
-    ("WGRAD", 1024, 200, 72, "C", "C", None, 8),        # GY and X transposed
+    ("DGRAD", 520, 132, 384, "N", "N", "BF16", 8),      # W copied (rows of 132)
+    ("DGRAD", 520, 136, 384, "N", "N", "BF16", 8),      # W in place
+    ("WGRAD", 1024, 200, 72, "C", "C", None, 8),        # GY and X in place, split tile
+    ("WGRAD", 512, 100, 96, "C", "C", None, 8),         # GY in place, X copied
+    ("WGRAD", 512, 96, 100, "C", "C", None, 8),         # GY copied, X in place
     ("FWD", 300, 2048, 200, "N", "N", "BF16", 8),       # 2 tiles split along K in 4 parts
     ("FWD", 200, 160, 72, "R", "R", None, 8),           # K % 128 != 0: the tile kernel
     # K % 512 == 0: operands packed K-chunked for the main GEMM kernel

@@ -20,7 +20,7 @@ CASES = [
     ("DGRAD", 512, 640, 1024, "R", "N", 8),
     ("WGRAD", 2048, 256, 200, "C", "N", 32),
     ("FWD", 300, 1024, 200, "R", "N", 8),
-    ("WGRAD", 2048, 320, 300, "C", "C", 8),     # BF16: K-major copies, split tiles
+    ("WGRAD", 2048, 320, 300, "C", "C", 8),     # BF16: X in place, GY copied, split tiles
 ]
 
 
