@@ -323,9 +323,10 @@ def main():
                    "out_dtype": args.out_dtype},
         "pct_mxfp4_peak": round(100 * value / PEAK_FP4_TFLOPS, 2),
         "stages_ms": {k: round(v, 4) for k, v in stage_ms.items()},
-        "stages_note": ("quant_lhs and quant_rhs are the K-major copies of the operands that are "
-                        "not contiguous along K; gemm is the bf16 MFMA kernel plus, when its last "
-                        "round is split along K, the fixup kernel") if bf16 else
+        "stages_note": ("quant_lhs and quant_rhs are the K-major copies of operands stored "
+                        "across K that cannot be read in place (empty when there are none); gemm "
+                        "is the bf16 MFMA kernel plus, when its last round is split along K, the "
+                        "fixup kernel") if bf16 else
                        ("the operand FOID does not scan is quantized on a second stream, beside "
                         "FOID, the other quantization and the outlier product: its slot is empty "
                         "and the other slots overlap it; gemm is the MFMA kernel plus, when its "

@@ -274,11 +274,12 @@ ADAHOP_API adahop_status adahop_gemm_mx(const adahop_mx_operand* A,
  * route with oe_rank < 1 or above the number of candidate lines.
  * Route BF16 (both operands hurt) computes the plain product on bf16 matrix
  * cores with fp32 accumulation and no packed operands (oe_rank is ignored).
- * When the contraction length is a multiple of 128 its workspace holds
- * K-major bf16 copies of the operands that are not contiguous along K (DGRAD:
- * W; WGRAD: GY and X) and the fp32 parts of tiles split along K; otherwise it
- * needs none. With an operand or the workspace not 16-byte aligned it runs
- * on a slower tile kernel instead. */
+ * When the contraction length is a multiple of 128 an operand not
+ * contiguous along K (DGRAD: W; WGRAD: GY and X) is read in place if its
+ * row length is a multiple of 8 and it is under 2 GiB; the workspace holds
+ * K-major bf16 copies of the others and the fp32 parts of tiles split along
+ * K. Otherwise it needs none. With an operand or the workspace not 16-byte
+ * aligned it runs on a slower tile kernel instead. */
 typedef struct {
   adahop_route_t route;   /* resolved route */
   int64_t m, n, K;        /* textbook-frame sizes */
@@ -319,7 +320,7 @@ ADAHOP_API adahop_status adahop_gemm(adahop_op op, const uint16_t* lhs, const ui
  * OE_LEFT and OE_RIGHT the operand FOID does not scan is quantized on a
  * second stream: its stage is empty here, the ROWS-layout scale reordering
  * falls in the GEMM stage, and the other stages overlap with it. With route
- * BF16 the lhs and rhs stages are the operands' K-major copies. */
+ * BF16 the lhs and rhs stages are the operands' K-major copies, if any. */
 #define ADAHOP_STAGE_EVENTS 6
 ADAHOP_API adahop_status adahop_gemm_timed(adahop_op op, const uint16_t* lhs,
                                            const uint16_t* rhs, int64_t T, int64_t Din,
