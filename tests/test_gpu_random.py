@@ -95,3 +95,36 @@ def test_random_large_product(case):
             cols = np.unique(np.concatenate([cols, idx[:8]]))
     run_and_compare(op, lhs, rhs, T, Din, Dout, pl, pr, route, k,
                     rows=rows.astype(np.int64), cols=cols.astype(np.int64))
+
+
+def random_bf16_case(i):
+    """The BF16 route: sizes up to ~1500 with ragged tiles, the contraction a
+    multiple of 128 (the ring kernel; operands stored across K read in place
+    when their rows are a multiple of 8 elements, else copied) or, one case
+    in four, only of 32 (the tile kernel)."""
+    rng = np.random.default_rng(70000 + i)
+    op = OPS[i % 3]
+    dims = [int(rng.integers(1, 1500)) for _ in range(3)]
+    c = {"FWD": 1, "DGRAD": 2, "WGRAD": 0}[op]
+    dims[c] = 32 * int(rng.integers(1, 64)) if i % 4 == 3 else 128 * int(rng.integers(1, 24))
+    for d in range(3):
+        if d != c and rng.random() < 0.5:
+            dims[d] = 8 * max(1, dims[d] // 8)      # rows a multiple of 8: read in place
+    T, Din, Dout = dims
+    return op, T, Din, Dout
+
+
+BF16_CASES = [random_bf16_case(i) for i in range(16)]
+
+
+@pytest.mark.parametrize("case", BF16_CASES, ids=[str(c) for c in BF16_CASES])
+def test_random_bf16_route(case):
+    op, T, Din, Dout = case
+    lhs, rhs = operands(op, T, Din, Dout, "N", "N", seed=T + 2 * Din + 3 * Dout)
+    plan = A.adahop_gemm_plan(op, T, Din, Dout, "N", "N", "BF16", 1)
+    rows = cols = None
+    if plan.m * plan.n > 512 * 512:
+        rng = np.random.default_rng(T * Dout)
+        rows = np.unique(rng.choice(plan.m, min(48, plan.m), replace=False)).astype(np.int64)
+        cols = np.unique(rng.choice(plan.n, min(48, plan.n), replace=False)).astype(np.int64)
+    run_and_compare(op, lhs, rhs, T, Din, Dout, "N", "N", "BF16", 1, rows=rows, cols=cols)
