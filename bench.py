@@ -198,7 +198,8 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=30,
+                    help="untimed calls first; the clock takes about 20 calls of this size to settle")
     ap.add_argument("--workload", default="l8b_down_wgrad")
     ap.add_argument("--out-dtype", default="bf16", choices=["bf16", "f32"])
     ap.add_argument("--route", default=None,
@@ -354,21 +355,35 @@ def main():
         result["roofline"]["traffic_note"] = note
 
     if not args.no_bf16_baseline:
-        # All-bf16 reference product on hipBLASLt (torch.matmul), same shapes.
-        a2 = {"FWD": lambda: (lhs, rhs.t().contiguous()),
-              "DGRAD": lambda: (lhs, rhs),
-              "WGRAD": lambda: (lhs.t().contiguous(), rhs)}[op]()
-        for _ in range(3):
-            torch.matmul(*a2)
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        for _ in range(max(3, args.steps // 2)):
-            torch.matmul(*a2)
-        torch.cuda.synchronize()
-        bms = (time.perf_counter() - t0) / max(3, args.steps // 2) * 1e3
-        result["bf16_matmul_ms"] = round(bms, 4)
-        result["speedup_vs_bf16_matmul"] = round(bms / ms_per_step, 3)
-        del a2
+        # All-bf16 reference product on hipBLASLt (torch.matmul, 2-D), same
+        # shapes, in the faster of two operand arrangements: the stored
+        # tensors as (transposed) views, or the transposed operand made
+        # contiguous beforehand (its copy not timed).
+        arrangements = {
+            "FWD": (("X, W^T view", lambda: (lhs, rhs.t())),
+                    ("X, W^T contiguous", lambda: (lhs, rhs.t().contiguous()))),
+            "DGRAD": (("GY, W", lambda: (lhs, rhs)),
+                      ("GY, W column-major", lambda: (lhs, rhs.t().contiguous().t()))),
+            "WGRAD": (("GY^T view, X", lambda: (lhs.t(), rhs)),
+                      ("GY^T contiguous, X", lambda: (lhs.t().contiguous(), rhs))),
+        }[op]
+        best = None
+        for name, make in arrangements:
+            a2 = make()
+            for _ in range(3):
+                torch.matmul(*a2)
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for _ in range(max(3, args.steps // 2)):
+                torch.matmul(*a2)
+            torch.cuda.synchronize()
+            bms = (time.perf_counter() - t0) / max(3, args.steps // 2) * 1e3
+            del a2
+            if best is None or bms < best[1]:
+                best = (name, bms)
+        result["bf16_matmul_ms"] = round(best[1], 4)
+        result["bf16_matmul_operands"] = best[0]
+        result["speedup_vs_bf16_matmul"] = round(best[1] / ms_per_step, 3)
         # hipBLASLt's own MXFP4 GEMM (torch._scaled_mm on packed E2M1 codes
         # with unit E8M0 scales), same m, n, K: a library reference for the
         # GEMM stage alone.
