@@ -90,6 +90,12 @@ def test_bf16_route_workspace():
     # rows of 136 it is read in place.
     assert A.adahop_gemm_plan("DGRAD", 520, 132, 384, "N", "N", "BF16").ws_bytes == 101376
     assert A.adahop_gemm_plan("DGRAD", 520, 136, 384, "N", "N", "BF16").ws_bytes == 0
+    # Forward with 8192 rows or more on one side: the other operand (fewer
+    # rows) is copied across K, W^T [256, 200] (102400 = 400 * 256 bytes) or
+    # X^T [256, 200]; with fewer rows on both sides nothing is copied.
+    assert A.adahop_gemm_plan("FWD", 8192, 256, 200, "R", "R").ws_bytes == 102400
+    assert A.adahop_gemm_plan("FWD", 200, 256, 8192, "R", "R").ws_bytes == 102400
+    assert A.adahop_gemm_plan("FWD", 8000, 256, 200, "R", "R").ws_bytes == 0
     # 2 tiles, 64 stages: each split along K in 4 parts of 256 KB.
     assert A.adahop_gemm_plan("FWD", 300, 2048, 200, "N", "N", "BF16").ws_bytes == 2 * 4 * 262144
 

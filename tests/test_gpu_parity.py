@@ -300,6 +300,8 @@ FULL_CASES = [
     ("WGRAD", 512, 100, 96, "C", "C", None, 8),         # GY in place, X copied
     ("WGRAD", 512, 96, 100, "C", "C", None, 8),         # GY copied, X in place
     ("FWD", 300, 2048, 200, "N", "N", "BF16", 8),       # 2 tiles split along K in 4 parts
+    ("FWD", 8192, 256, 200, "R", "R", None, 8),         # W copied across K (8192 rows of X)
+    ("FWD", 200, 256, 8192, "R", "R", None, 8),         # X copied across K (8192 rows of W)
     ("FWD", 200, 160, 72, "R", "R", None, 8),           # K % 128 != 0: the tile kernel
     # K % 512 == 0: operands packed K-chunked for the main GEMM kernel
     ("FWD", 300, 1024, 200, "R", "N", None, 8),         # OE_LEFT, both rows quantized in rows
