@@ -277,9 +277,11 @@ ADAHOP_API adahop_status adahop_gemm_mx(const adahop_mx_operand* A,
  * When the contraction length is a multiple of 128 an operand not
  * contiguous along K (DGRAD: W; WGRAD: GY and X) is read in place if its
  * row length is a multiple of 8 and it is under 2 GiB; the workspace holds
- * K-major bf16 copies of the others and the fp32 parts of tiles split along
- * K. Otherwise it needs none. With an operand or the workspace not 16-byte
- * aligned it runs on a slower tile kernel instead. */
+ * K-major bf16 copies of the others, for a forward with 8192 or more rows on
+ * one side a copy across K of the other operand (read faster that way), and
+ * the fp32 parts of tiles split along K. Otherwise it needs none. With an
+ * operand or the workspace not 16-byte aligned it runs on a slower tile
+ * kernel instead. */
 typedef struct {
   adahop_route_t route;   /* resolved route */
   int64_t m, n, K;        /* textbook-frame sizes */
