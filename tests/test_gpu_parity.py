@@ -403,3 +403,21 @@ def test_stage_events_record():
     torch.cuda.synchronize()
     times = [ev[i].elapsed_time(ev[i + 1]) for i in range(A.STAGE_EVENTS - 1)]
     assert all(t >= 0 for t in times)
+
+
+@pytest.mark.parametrize("case", [("FWD", 8192, 256, 200), ("WGRAD", 512, 100, 96)],
+                         ids=["fwd-copy-across", "wgrad-in-place-and-copy"])
+def test_stage_events_bf16_route(case):
+    # The timed call on the BF16 route (its copies in the operand stages)
+    # gives the untimed call's output bit for bit, with ordered events.
+    op, T, Din, Dout = case
+    lhs, rhs = operands(op, T, Din, Dout, "N", "N", 5)
+    L, R = dev_bf16(lhs), dev_bf16(rhs)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(A.STAGE_EVENTS)]
+    say("stage events BF16", case)
+    timed = A.adahop_gemm(op, L, R, "N", "N", "BF16", 1, stage_events=ev)
+    plain = A.adahop_gemm(op, L, R, "N", "N", "BF16", 1)
+    torch.cuda.synchronize()
+    assert torch.equal(timed.view(torch.int16), plain.view(torch.int16))
+    times = [ev[i].elapsed_time(ev[i + 1]) for i in range(A.STAGE_EVENTS - 1)]
+    assert all(t >= 0 for t in times)
