@@ -217,9 +217,9 @@ def main():
                          "for HBM byte counters) and exit")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
-              "(the path has no collectives; see the sharding note in the design document)",
-              file=sys.stderr)
+        print(f"bench.py: the library runs one product on one GPU; --gpus {args.gpus} is not "
+              "supported (the path has no collectives: a data-parallel job runs one call per "
+              "GPU on its own shard)", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
