@@ -57,12 +57,13 @@ def workloads():
 # passes (recorded with the copy-kernel calibration in this summary); it is
 # reported only while the kernel source is byte-identical to the one counted.
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "gemm_mx_ring_l8b_down_wgrad_traffic.md")
+TRAFFIC_SUMMARY_BF16 = os.path.join(ROOT, "profiles", "bf16_ring_l8b_down_wgrad_traffic.md")
 
 
-def measured_traffic(workload_name):
+def measured_traffic(workload_name, summary=TRAFFIC_SUMMARY):
     """(bytes per launch or None, note)."""
     try:
-        with open(TRAFFIC_SUMMARY) as f:
+        with open(summary) as f:
             text = f.read()
     except OSError:
         return None, "no counter summary"
@@ -348,11 +349,9 @@ def main():
     }
     if bf16:
         del result["pct_mxfp4_peak"]
-        result["roofline"]["traffic_note"] = "HBM counters not taken for the bf16 kernel"
-    else:
-        traffic, note = measured_traffic(wl.name)
-        result["roofline"]["traffic"] = None if traffic is None else round(traffic)
-        result["roofline"]["traffic_note"] = note
+    traffic, note = measured_traffic(wl.name, TRAFFIC_SUMMARY_BF16 if bf16 else TRAFFIC_SUMMARY)
+    result["roofline"]["traffic"] = None if traffic is None else round(traffic)
+    result["roofline"]["traffic_note"] = note
 
     if not args.no_bf16_baseline:
         # All-bf16 reference product on hipBLASLt (torch.matmul, 2-D), same
