@@ -165,7 +165,12 @@ adahop_status make_plan(adahop_op op, int64_t T, int64_t Din, int64_t Dout,
       P->gemm_bytes = bf16_ring_scratch_bytes(s.m, s.n, s.K);
       if (P->gemm_bytes) P->off_gemm = take(P->gemm_bytes);
       pb.ws_bytes = off;
+      if ((P->off_lhs_t != kNone && !bf16_transpose_fits(s.lhs_rows, s.lhs_cols)) ||
+          (P->off_rhs_t != kNone && !bf16_transpose_fits(s.rhs_rows, s.rhs_cols)))
+        return fail(ADAHOP_ERR_UNSUPPORTED, "operand too wide for the K-major copy");
     }
+    // The tile kernel that runs when the ring kernel does not apply.
+    if (!oe_product_fits(s.m, s.n)) return fail(ADAHOP_ERR_UNSUPPORTED, "bf16 product too wide");
     return ADAHOP_OK;
   }
 
@@ -193,6 +198,7 @@ adahop_status make_plan(adahop_op op, int64_t T, int64_t Din, int64_t Dout,
       return fail(ADAHOP_ERR_INVALID, "oe_rank " + std::to_string(oe_rank) +
                                           " outside [1, " + std::to_string(ncand) + "]");
     if (oe_rank > kMaxK) return fail(ADAHOP_ERR_UNSUPPORTED, "oe_rank above 1024");
+    if (!foid_fits(ncand, oe_rank)) return fail(ADAHOP_ERR_UNSUPPORTED, "too many FOID candidates");
     pb.k = oe_rank;
     if (pb.scan_tensor == 0) { P->zero_lhs = true; P->lhs_zero_axis = pb.scan_axis; }
     else { P->zero_rhs = true; P->rhs_zero_axis = pb.scan_axis; }
@@ -217,6 +223,16 @@ adahop_status make_plan(adahop_op op, int64_t T, int64_t Din, int64_t Dout,
     const int64_t ny = route == ADAHOP_ROUTE_OE_LEFT ? s.n : pb.k;
     P->splits = oe_splits(nx, ny, s.K);
     P->off_partials = take(sizeof(float) * (size_t)(P->splits + 1) * (size_t)nx * (size_t)ny);
+  }
+  // Shapes a launcher would refuse are rejected here, before the call's
+  // first launch.
+  if (!iht_quant_fits(s.lhs_rows, s.lhs_cols, s.lhs_contract) ||
+      !iht_quant_fits(s.rhs_rows, s.rhs_cols, s.rhs_contract) || !gemm_mx_fits(s.m, s.n))
+    return fail(ADAHOP_ERR_UNSUPPORTED, "operands too large for the quantizer or GEMM grids");
+  if (route == ADAHOP_ROUTE_OE_LEFT || route == ADAHOP_ROUTE_OE_RIGHT) {
+    const int64_t nx = route == ADAHOP_ROUTE_OE_LEFT ? pb.k : s.m;
+    const int64_t ny = route == ADAHOP_ROUTE_OE_LEFT ? s.n : pb.k;
+    if (!oe_product_fits(nx, ny)) return fail(ADAHOP_ERR_UNSUPPORTED, "outlier product too wide");
   }
   // Operands the main GEMM kernel streams are packed K-chunked by the
   // quantizers; otherwise row-major, with the GEMM's own scale reordering.
@@ -279,6 +295,36 @@ SideStream* side_stream_locked(int dev) {
 adahop_status hip_ok(hipError_t e, const char* what) {
   return e == hipSuccess ? ADAHOP_OK : fail(ADAHOP_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
 }
+
+// Held from the fork of the side stream to its join. However the call ends
+// after the fork (an error included), the caller's stream waits for
+// everything enqueued on the side stream before the device's lock is
+// released: no work of the call outlives its return unordered, and a
+// captured call never leaves the side stream forked.
+struct SideJoin {
+  SideStream* side = nullptr;
+  hipStream_t stream = nullptr;
+  std::unique_lock<std::mutex> lock;
+  bool joined = false;
+  adahop_status join() {
+    if (!side || joined) return ADAHOP_OK;
+    joined = true;
+    adahop_status st = hip_ok(hipEventRecord(side->join, side->stream), "hipEventRecord");
+    if (st == ADAHOP_OK) st = hip_ok(hipStreamWaitEvent(stream, side->join, 0), "hipStreamWaitEvent");
+    return st;
+  }
+  ~SideJoin() {
+    if (side && !joined) {
+      // Error path: keep the message of the error being returned.
+      const std::string msg = adahop_last_error();
+      joined = true;
+      if (hipEventRecord(side->join, side->stream) == hipSuccess)
+        (void)hipStreamWaitEvent(stream, side->join, 0);
+      (void)hipGetLastError();
+      set_error(msg);
+    }
+  }
+};
 
 adahop_status run_gemm(adahop_op op, const uint16_t* lhs, const uint16_t* rhs, int64_t T,
                        int64_t Din, int64_t Dout, adahop_pattern pat_lhs,
@@ -374,14 +420,14 @@ adahop_status run_gemm(adahop_op op, const uint16_t* lhs, const uint16_t* rhs, i
   // the side stream while FOID, the scanned operand's quantization and the
   // outlier product run on the caller's stream; the join comes right before
   // the GEMM (and the ROWS-layout scale reordering).
-  std::unique_lock<std::mutex> side_lock;
+  SideJoin sj;
   SideStream* side = nullptr;
   if (idx && (scan_lhs ? !P.zero_rhs : !P.zero_lhs)) {
     int dev = 0;
     if (hipGetDevice(&dev) == hipSuccess && dev >= 0 && dev < kMaxDevices) {
-      side_lock = std::unique_lock<std::mutex>(g_side[dev].mu);
+      sj.lock = std::unique_lock<std::mutex>(g_side[dev].mu);
       side = side_stream_locked(dev);
-      if (!side) side_lock.unlock();
+      if (!side) sj.lock.unlock();
     }
   }
   if (side) {
@@ -390,8 +436,10 @@ adahop_status run_gemm(adahop_op op, const uint16_t* lhs, const uint16_t* rhs, i
     // quantization after it overlaps that quantization's tail.
     ADAHOP_TRY(hip_ok(hipEventRecord(side->fork, stream), "hipEventRecord"));
     ADAHOP_TRY(hip_ok(hipStreamWaitEvent(side->stream, side->fork, 0), "hipStreamWaitEvent"));
+    // From here on the join is owed, on every path.
+    sj.side = side;
+    sj.stream = stream;
     ADAHOP_TRY(scan_lhs ? quant_rhs(side->stream) : quant_lhs(side->stream));
-    ADAHOP_TRY(hip_ok(hipEventRecord(side->join, side->stream), "hipEventRecord"));
     ADAHOP_TRY(foid(stream));
     ADAHOP_TRY(E.record(1));
     // The other operand's stage is empty on this stream.
@@ -447,8 +495,8 @@ adahop_status run_gemm(adahop_op op, const uint16_t* lhs, const uint16_t* rhs, i
   }
   ADAHOP_TRY(E.record(4));
   if (side) {
-    ADAHOP_TRY(hip_ok(hipStreamWaitEvent(stream, side->join, 0), "hipStreamWaitEvent"));
-    side_lock.unlock();
+    ADAHOP_TRY(sj.join());
+    sj.lock.unlock();
     if (pb.layout == ADAHOP_LAYOUT_ROWS)
       ADAHOP_TRY(gemm_mx_stage_scales(ac, as, bc, bs, s.m, s.n, s.K, gemm_scratch, P.gemm_bytes, stream));
   }
@@ -467,6 +515,24 @@ size_t gemm_mx_partials_bytes(int64_t m, int64_t n, int64_t K, const adahop_oe* 
   return align_up(sizeof(float) * (size_t)(oe_splits(nx, ny, K) + 1) * (size_t)nx * (size_t)ny, kAlign);
 }
 
+}  // namespace
+}  // namespace adahop
+
+namespace adahop {
+namespace {
+adahop_status detect_checks(const uint16_t* t, int64_t rows, int64_t cols, int64_t ld,
+                            adahop_axis axis, int32_t probe, int32_t k, int32_t* idx_out) {
+  if (!t || !idx_out) return fail(ADAHOP_ERR_INVALID, "adahop_detect: null pointer");
+  if (rows < 1 || cols < 1 || ld < cols) return fail(ADAHOP_ERR_INVALID, "adahop_detect: bad sizes");
+  if (axis != ADAHOP_AXIS_ROWS && axis != ADAHOP_AXIS_COLS)
+    return fail(ADAHOP_ERR_INVALID, "adahop_detect: bad axis");
+  if (probe < 1) return fail(ADAHOP_ERR_INVALID, "adahop_detect: probe < 1");
+  const int64_t ncand = axis == ADAHOP_AXIS_ROWS ? rows : cols;
+  if (k < 1 || k > ncand) return fail(ADAHOP_ERR_INVALID, "adahop_detect: k outside [1, candidates]");
+  if (k > kMaxK) return fail(ADAHOP_ERR_UNSUPPORTED, "adahop_detect: k above 1024");
+  if (!foid_fits(ncand, k)) return fail(ADAHOP_ERR_UNSUPPORTED, "adahop_detect: too many candidates");
+  return ADAHOP_OK;
+}
 }  // namespace
 }  // namespace adahop
 
@@ -515,14 +581,7 @@ adahop_status adahop_detect(const uint16_t* t, int64_t rows, int64_t cols, int64
                             adahop_axis axis, int32_t probe, int32_t k, int32_t* idx_out,
                             void* ws, size_t ws_bytes, void* stream) {
   set_error("");
-  if (!t || !idx_out) return fail(ADAHOP_ERR_INVALID, "adahop_detect: null pointer");
-  if (rows < 1 || cols < 1 || ld < cols) return fail(ADAHOP_ERR_INVALID, "adahop_detect: bad sizes");
-  if (axis != ADAHOP_AXIS_ROWS && axis != ADAHOP_AXIS_COLS)
-    return fail(ADAHOP_ERR_INVALID, "adahop_detect: bad axis");
-  if (probe < 1) return fail(ADAHOP_ERR_INVALID, "adahop_detect: probe < 1");
-  const int64_t ncand = axis == ADAHOP_AXIS_ROWS ? rows : cols;
-  if (k < 1 || k > ncand) return fail(ADAHOP_ERR_INVALID, "adahop_detect: k outside [1, candidates]");
-  if (k > kMaxK) return fail(ADAHOP_ERR_UNSUPPORTED, "adahop_detect: k above 1024");
+  ADAHOP_TRY(detect_checks(t, rows, cols, ld, axis, probe, k, idx_out));
   return foid_launch(t, rows, cols, ld, axis, probe, k, idx_out, ws, ws_bytes,
                      static_cast<hipStream_t>(stream));
 }
@@ -617,39 +676,49 @@ adahop_status adahop_gemm_mx(const adahop_mx_operand* A, const adahop_mx_operand
                                           std::to_string(need) + " bytes");
   if (need > 0 && !aligned16(ws))
     return fail(ADAHOP_ERR_UNSUPPORTED, "adahop_gemm_mx: the workspace must be 16-byte aligned");
-  const size_t partial_bytes = gemm_mx_partials_bytes(m, n, K, oe);
-  void* scratch = need > partial_bytes ? static_cast<char*>(ws) + partial_bytes : nullptr;
-  ADAHOP_TRY(gemm_mx_stage_scales(A->codes, A->scales, B->codes, B->scales, m, n, K, scratch,
-                                  need - partial_bytes, st));
+  if (!gemm_mx_fits(m, n)) return fail(ADAHOP_ERR_UNSUPPORTED, "adahop_gemm_mx: too many output tiles");
+  // Every check of the outlier descriptor comes before the first launch.
   OeEpilogue e{};
+  int64_t oe_nx = 0, oe_ny = 0;
   if (oe) {
+    if (oe->route != ADAHOP_ROUTE_OE_LEFT && oe->route != ADAHOP_ROUTE_OE_RIGHT &&
+        oe->route != ADAHOP_ROUTE_OE_INNER)
+      return fail(ADAHOP_ERR_INVALID, "adahop_gemm_mx: outlier route must be OE_LEFT, OE_RIGHT or OE_INNER");
     if (oe->k < 1 || !oe->a.ptr || !oe->b.ptr)
       return fail(ADAHOP_ERR_INVALID, "adahop_gemm_mx: bad outlier descriptor");
     if (oe->k > kMaxK) return fail(ADAHOP_ERR_UNSUPPORTED, "adahop_gemm_mx: k above 1024");
+    if (oe->a.ld < 1 || oe->b.ld < 1)
+      return fail(ADAHOP_ERR_INVALID, "adahop_gemm_mx: outlier views need ld >= 1");
     const Bf16View X{oe->a.ptr, oe->a.ld, oe->a.inner_contiguous};
     const Bf16View Y{oe->b.ptr, oe->b.ld, oe->b.inner_contiguous};
     if (oe->route == ADAHOP_ROUTE_OE_LEFT || oe->route == ADAHOP_ROUTE_OE_RIGHT) {
       if (!oe->idx) return fail(ADAHOP_ERR_INVALID, "adahop_gemm_mx: null idx");
       if (oe->k > (oe->route == ADAHOP_ROUTE_OE_LEFT ? m : n))
         return fail(ADAHOP_ERR_INVALID, "adahop_gemm_mx: k above the number of lines");
-      const int64_t nx = oe->route == ADAHOP_ROUTE_OE_LEFT ? oe->k : m;
-      const int64_t ny = oe->route == ADAHOP_ROUTE_OE_LEFT ? n : oe->k;
-      const int splits = oe_splits(nx, ny, K);
-      ADAHOP_TRY(oe_product_launch(X, Y, nx, ny, K, splits, static_cast<float*>(ws), st));
+      oe_nx = oe->route == ADAHOP_ROUTE_OE_LEFT ? oe->k : m;
+      oe_ny = oe->route == ADAHOP_ROUTE_OE_LEFT ? n : oe->k;
+      if (!oe_product_fits(oe_nx, oe_ny))
+        return fail(ADAHOP_ERR_UNSUPPORTED, "adahop_gemm_mx: outlier product too wide");
       e.mode = oe->route;
       e.k = oe->k;
       e.idx = oe->idx;
       e.partials = static_cast<const float*>(ws);
-      e.splits = splits;
-    } else if (oe->route == ADAHOP_ROUTE_OE_INNER) {
+      e.splits = oe_splits(oe_nx, oe_ny, K);
+      e.a = X;
+      e.b = Y;
+    } else {
       e.mode = ADAHOP_ROUTE_OE_INNER;
       e.k = oe->k;
       e.a = X;
       e.b = Y;
-    } else {
-      return fail(ADAHOP_ERR_INVALID, "adahop_gemm_mx: outlier route must be OE_LEFT, OE_RIGHT or OE_INNER");
     }
   }
+  const size_t partial_bytes = gemm_mx_partials_bytes(m, n, K, oe);
+  void* scratch = need > partial_bytes ? static_cast<char*>(ws) + partial_bytes : nullptr;
+  ADAHOP_TRY(gemm_mx_stage_scales(A->codes, A->scales, B->codes, B->scales, m, n, K, scratch,
+                                  need - partial_bytes, st));
+  if (e.mode == ADAHOP_ROUTE_OE_LEFT || e.mode == ADAHOP_ROUTE_OE_RIGHT)
+    ADAHOP_TRY(oe_product_launch(e.a, e.b, oe_nx, oe_ny, K, e.splits, static_cast<float*>(ws), st));
   return gemm_mx_launch(A->codes, A->scales, B->codes, B->scales, m, n, K, ADAHOP_LAYOUT_ROWS, e,
                         C, ldc,
                         out_dtype == ADAHOP_OUT_F32 ? 1 : 0, scratch, need - partial_bytes, st);

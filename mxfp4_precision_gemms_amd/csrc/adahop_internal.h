@@ -22,6 +22,8 @@ constexpr int kMaxK = 1024;  // largest outlier rank (FOID top-k, OE lines)
 
 // ---- FOID -----------------------------------------------------------------
 size_t foid_workspace_bytes(int64_t ncand, int32_t k);
+// Whether foid_launch's grid fits (false: it would return UNSUPPORTED).
+bool foid_fits(int64_t ncand, int32_t k);
 // FOID's score of every candidate line, fp64 [ncand], on the device.
 adahop_status line_scores_launch(const uint16_t* t, int64_t rows, int64_t cols, int64_t ld, int axis,
                                  int32_t probe, double* out, hipStream_t stream);
@@ -30,6 +32,8 @@ adahop_status foid_launch(const uint16_t* t, int64_t rows, int64_t cols, int64_t
                           hipStream_t stream);
 
 // ---- zero + gather + IHT + MXFP4 ------------------------------------------
+// Whether iht_quant_launch's grid fits (false: it would return UNSUPPORTED).
+bool iht_quant_fits(int64_t rows, int64_t cols, int contract);
 adahop_status iht_quant_launch(const uint16_t* src, int64_t rows, int64_t cols, int64_t ld,
                                int contract, int32_t hadamard_block, const int32_t* zero_idx,
                                int32_t nzero, int zero_axis, uint8_t* codes, uint8_t* scales,
@@ -45,6 +49,9 @@ struct Bf16View {
   int inner_contiguous;
 };
 int oe_splits(int64_t nx, int64_t ny, int64_t K);
+// Whether the outlier product's grid fits (false: oe_product_launch would
+// return UNSUPPORTED).
+bool oe_product_fits(int64_t nx, int64_t ny);
 adahop_status oe_product_launch(Bf16View X, Bf16View Y, int64_t nx, int64_t ny, int64_t K,
                                 int splits, float* partials, hipStream_t stream);
 // P = sum over s < splits of partials[s] (each `count` floats), in the order
@@ -71,6 +78,7 @@ adahop_status bf16_ring_launch(const uint16_t* a, int a_across, int64_t lda, con
 // (leading dim ld).
 adahop_status bf16_transpose_launch(const uint16_t* src, int64_t rows, int64_t cols, int64_t ld,
                                     uint16_t* dst, hipStream_t stream);
+bool bf16_transpose_fits(int64_t rows, int64_t cols);
 
 // ---- FP4 GEMM with the OE epilogue ----------------------------------------
 struct OeEpilogue {
@@ -90,6 +98,9 @@ size_t gemm_mx_scratch_bytes(int64_t m, int64_t n, int64_t K, int layout);
 // Whether (m, n, K) operands may be packed K-chunked (ADAHOP_LAYOUT_KCHUNK):
 // the main kernel applies and stage offsets fit 31 bits.
 bool gemm_mx_kchunk_ok(int64_t m, int64_t n, int64_t K);
+// Whether the GEMM's tile count fits (false: gemm_mx_launch would return
+// UNSUPPORTED).
+bool gemm_mx_fits(int64_t m, int64_t n);
 adahop_status gemm_mx_stage_scales(const uint8_t* a_codes, const uint8_t* a_scales,
                                    const uint8_t* b_codes, const uint8_t* b_scales, int64_t m,
                                    int64_t n, int64_t K, void* scratch, size_t scratch_bytes,

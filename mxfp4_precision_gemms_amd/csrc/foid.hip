@@ -385,6 +385,8 @@ adahop_status line_scores_launch(const uint16_t* t, int64_t rows, int64_t cols, 
   return check_launch("line_scores");
 }
 
+bool foid_fits(int64_t ncand, int32_t k) { return ncand >= 1 && k >= 1 && chunks_of(ncand, k) <= 0x7FFFFFFF; }
+
 size_t foid_workspace_bytes(int64_t ncand, int32_t k) {
   if (ncand <= final_cap(k)) return 0;
   // The levels' survivors, double buffered (level 0 scores in registers),
@@ -404,7 +406,7 @@ adahop_status foid_launch(const uint16_t* t, int64_t rows, int64_t cols, int64_t
   if (need > 0 && (ws == nullptr || ws_bytes < need))
     return fail(ADAHOP_ERR_WORKSPACE, "adahop_detect: workspace too small (need " +
                                           std::to_string(need) + " bytes)");
-  if (chunks_of(ncand, k) > 0x7FFFFFFF)
+  if (!foid_fits(ncand, k))
     return fail(ADAHOP_ERR_UNSUPPORTED, "adahop_detect: too many candidates");
   SelectArgs a{t, ld, axis, P, nullptr, nullptr, ncand, k, nullptr, nullptr, nullptr};
   const SelectArgs none{};

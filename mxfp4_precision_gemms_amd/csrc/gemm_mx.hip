@@ -629,11 +629,15 @@ __global__ void __launch_bounds__(kRing8Threads, 1) gemm_mx_ring8_kernel(GemmArg
   const int chunk = (lane & 3) ^ ring_swz(row0);    // swz is the same for rows row0 + 16 j
   const int stage_a = TA ? 32 * (int)g.a_ldb : Chunked ? (int)g.m * RBK : RBK;
   const int stage_b = TB ? 32 * (int)g.b_ldb : Chunked ? (int)g.n * RBK : RBK;
-  // Operand stored across K: this lane's load j offset within a stage.
-  auto tr_voff = [&](int j, int64_t ldb) {
+  // Operand stored across K: this lane's load j offset within a stage, or
+  // past the end of the buffer when its 16-byte chunk (8 columns; ld is a
+  // multiple of 8) starts at or beyond the operand's last column, so that a
+  // ragged tile reads nothing outside the operand whatever K-row it is on.
+  auto tr_voff = [&](int j, int64_t ldb, int64_t c0) {
     const int k = 2 * (2 * wave + j) + (lane >> 5);
     const int h = (k & 3) | (((k >> 3) & 1) << 2);
-    return k * (int)ldb + 16 * ((lane & 31) ^ (4 * h));
+    const int chunk = (lane & 31) ^ (4 * h);
+    return 8 * (int64_t)chunk < ldb / 2 - c0 ? k * (int)ldb + 16 * chunk : kPastEnd;
   };
   // Scales: waves 0-3 copy A rows 64 (w % 4) + lane, waves 4-7 B rows.
   const bool sc_a = wave < 4;
@@ -672,8 +676,9 @@ __global__ void __launch_bounds__(kRing8Threads, 1) gemm_mx_ring8_kernel(GemmArg
     const int rows_a = (int)(g.m - it.m0 < BM ? g.m - it.m0 : BM);
     const int rows_b = (int)(g.n - it.n0 < BN ? g.n - it.n0 : BN);
     // Stored across K: the buffer starts at the tile's first column and runs
-    // to the end of the operand (columns past m or n read other columns or 0;
-    // they only reach rows of C that are not stored).
+    // to the end of the operand (columns past m but below ld read other
+    // columns, which only reach rows of C that are not stored; lanes past ld
+    // read 0).
     it.ra = TA
         ? __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(g.a_codes + it.m0 * 2), 0,
                                             (int)(g.K * g.a_ldb - it.m0 * 2), kBufferFlags)
@@ -697,8 +702,8 @@ __global__ void __launch_bounds__(kRing8Threads, 1) gemm_mx_ring8_kernel(GemmArg
         it.voffa[j] = r < rows_a ? r * RBK + chunk * 16 : kPastEnd;
         it.voffb[j] = r < rows_b ? r * RBK + chunk * 16 : kPastEnd;
       } else {
-        it.voffa[j] = TA ? tr_voff(j, g.a_ldb) : r * (int)Kb + chunk * 16;
-        it.voffb[j] = TB ? tr_voff(j, g.b_ldb) : r * (int)Kb + chunk * 16;
+        it.voffa[j] = TA ? tr_voff(j, g.a_ldb, it.m0) : r * (int)Kb + chunk * 16;
+        it.voffb[j] = TB ? tr_voff(j, g.b_ldb, it.n0) : r * (int)Kb + chunk * 16;
       }
     }
     it.soff = sc_a ? (srow < rows_a ? (int)((it.m0 + srow) * 4) : kPastEnd)
@@ -1226,6 +1231,10 @@ int oe_splits(int64_t nx, int64_t ny, int64_t K) {
   return (int)(s < 1 ? 1 : s);
 }
 
+bool oe_product_fits(int64_t nx, int64_t ny) {
+  return nx >= 1 && ny >= 1 && (ny + OY - 1) / OY <= 65535 && (nx + OX - 1) / OX <= 0x7FFFFFFF;
+}
+
 static int64_t kchunk_for(int64_t K, int splits) {
   int64_t c = (K + splits - 1) / splits;
   return (c + OK - 1) / OK * OK;
@@ -1235,7 +1244,7 @@ adahop_status oe_product_launch(Bf16View X, Bf16View Y, int64_t nx, int64_t ny, 
                                 int splits, float* partials, hipStream_t stream) {
   OeArgs a{X.ptr, X.ld, Y.ptr, Y.ld, nx, ny, K, kchunk_for(K, splits), partials, nullptr, 0, 0};
   const int64_t gy = (ny + OY - 1) / OY;
-  if (gy > 65535) return fail(ADAHOP_ERR_UNSUPPORTED, "outlier product: too many columns");
+  if (!oe_product_fits(nx, ny)) return fail(ADAHOP_ERR_UNSUPPORTED, "outlier product: too many columns");
   const dim3 grid((unsigned)((nx + OX - 1) / OX), (unsigned)gy, (unsigned)splits);
   launch_oe(a, grid, X.inner_contiguous != 0, Y.inner_contiguous != 0, stream);
   adahop_status st = check_launch("oe_product");
@@ -1335,6 +1344,10 @@ size_t staging_bytes(int64_t m, int64_t n, int64_t K) {
 
 }  // namespace
 
+bool gemm_mx_fits(int64_t m, int64_t n) {
+  return m >= 1 && n >= 1 && ((m + BM - 1) / BM) * ((n + BN - 1) / BN) <= 0x7FFFFFFF;
+}
+
 bool gemm_mx_kchunk_ok(int64_t m, int64_t n, int64_t K) {
   const int64_t big = m > n ? m : n;
   return ring_shape_ok(m, n, K) && big * (K / 2) < 0x7FFF0000;   // stage offsets fit 31 bits
@@ -1388,7 +1401,7 @@ adahop_status gemm_mx_launch(const uint8_t* a_codes, const uint8_t* a_scales,
                              int64_t ldc, int out_f32, void* scratch, size_t scratch_bytes,
                              hipStream_t stream) {
   const int64_t tiles_m = (m + BM - 1) / BM, tiles_n = (n + BN - 1) / BN;
-  if (tiles_m * tiles_n > 0x7FFFFFFF) return fail(ADAHOP_ERR_UNSUPPORTED, "gemm: too large");
+  if (!gemm_mx_fits(m, n)) return fail(ADAHOP_ERR_UNSUPPORTED, "gemm: too large");
   GemmArgs g{};
   g.a_codes = a_codes; g.a_scales = a_scales; g.b_codes = b_codes; g.b_scales = b_scales;
   g.m = m; g.n = n; g.K = K; g.C = C; g.ldc = ldc; g.out_f32 = out_f32;
@@ -1562,11 +1575,15 @@ bf16_transpose_kernel(const uint16_t* __restrict__ src, int64_t rows, int64_t co
 }
 }  // namespace
 
+bool bf16_transpose_fits(int64_t rows, int64_t cols) {
+  return rows >= 1 && cols >= 1 && (rows + kTT - 1) / kTT <= 0x7FFFFFFF && (cols + kTT - 1) / kTT <= 65535;
+}
+
 adahop_status bf16_transpose_launch(const uint16_t* src, int64_t rows, int64_t cols, int64_t ld,
                                     uint16_t* dst, hipStream_t stream) {
-  const int64_t gx = (rows + kTT - 1) / kTT, gy = (cols + kTT - 1) / kTT;
-  if (rows < 1 || cols < 1 || ld < cols || gx > 0x7FFFFFFF || gy > 65535)
+  if (ld < cols || !bf16_transpose_fits(rows, cols))
     return fail(ADAHOP_ERR_UNSUPPORTED, "bf16 transpose: bad or too large shape");
+  const int64_t gx = (rows + kTT - 1) / kTT, gy = (cols + kTT - 1) / kTT;
   const int vec_in = ld % 8 == 0 && (reinterpret_cast<uintptr_t>(src) & 15u) == 0;
   const int vec_out = rows % 8 == 0 && (reinterpret_cast<uintptr_t>(dst) & 15u) == 0;
   bf16_transpose_kernel<<<dim3((unsigned)gx, (unsigned)gy), dim3(256), 0, stream>>>(

@@ -469,6 +469,16 @@ iht_quant_colwise_kernel(const uint16_t* __restrict__ src, int64_t K, int64_t ou
 
 }  // namespace
 
+bool iht_quant_fits(int64_t rows, int64_t cols, int contract) {
+  if (rows < 1 || cols < 1) return false;
+  if (contract == ADAHOP_AXIS_COLS) {
+    const int64_t cpr = (cols + kRowChunk - 1) / kRowChunk;
+    return (rows + kRowRows - 1) / kRowRows * cpr <= 0x7FFFFFFFLL;
+  }
+  return (cols + kColOut - 1) / kColOut <= 0x7FFFFFFFLL &&
+         (rows / 32 + kColBlocks - 1) / kColBlocks <= 65535;
+}
+
 adahop_status iht_quant_launch(const uint16_t* src, int64_t rows, int64_t cols, int64_t ld,
                                int contract, int32_t hadamard_block, const int32_t* zero_idx,
                                int32_t nzero, int zero_axis, uint8_t* codes, uint8_t* scales,

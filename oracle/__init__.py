@@ -51,6 +51,9 @@ def _load():
         "adahop_ref_gemm_mx": ([_p, _p, _p, _p, _i64, _p, _i64, _p, _i64, _p, _p], _int),
         "adahop_ref_gemm_bf16": ([_p, _i64, _int, _p, _i64, _int, _i64, _p, _i64, _p, _i64,
                                   _p, _p], _int),
+        "adahop_ref_walk_mx": ([_p, _p, _p, _p, _i64, _i64, _p, _i64, _p, _i64, _p, _p], _int),
+        "adahop_ref_walk_bf16": ([_p, _i64, _int, _p, _i64, _int, _i64, _i64, _p, _i64, _p, _i64,
+                                  _p, _p], _int),
         "adahop_ref_dequant": ([_p, _p, _i64, _i64, _p], _int),
         "adahop_ref_max_threads": ([], _int),
     }
@@ -208,6 +211,35 @@ def gemm_bf16(a, a_trans, b, b_trans, K, rows, cols):
                                         int(b_trans), K, _ptr(rows), rows.size, _ptr(cols),
                                         cols.size, _ptr(C), _ptr(A)), "gemm_bf16")
     return C, A
+
+
+def walk_mx(a_codes, a_scales, b_codes, b_scales, step, rows=None, cols=None):
+    """Running-error terms (walk, rmax) of an fp32 accumulation of the packed
+    product, `step` products at a time in contraction order (a tolerance for
+    the tests; see adahop_ref.h)."""
+    K = a_codes.shape[1] * 2
+    rows = _idx64(rows, a_codes.shape[0])
+    cols = _idx64(cols, b_codes.shape[0])
+    W = np.zeros((rows.size, cols.size), dtype=np.float64)
+    R = np.zeros_like(W)
+    args = [np.ascontiguousarray(x) for x in (a_codes, a_scales, b_codes, b_scales)]
+    _check(_load().adahop_ref_walk_mx(*[_ptr(x) for x in args], K, step, _ptr(rows), rows.size,
+                                      _ptr(cols), cols.size, _ptr(W), _ptr(R)), "walk_mx")
+    return W, R
+
+
+def walk_bf16(a, a_trans, b, b_trans, K, step, rows, cols):
+    """As walk_mx, for the bf16 product of gemm_bf16."""
+    a = np.ascontiguousarray(a)
+    b = np.ascontiguousarray(b)
+    rows = np.ascontiguousarray(rows, dtype=np.int64)
+    cols = np.ascontiguousarray(cols, dtype=np.int64)
+    W = np.zeros((rows.size, cols.size), dtype=np.float64)
+    R = np.zeros_like(W)
+    _check(_load().adahop_ref_walk_bf16(_ptr(a), a.shape[1], int(a_trans), _ptr(b), b.shape[1],
+                                        int(b_trans), K, step, _ptr(rows), rows.size, _ptr(cols),
+                                        cols.size, _ptr(W), _ptr(R)), "walk_bf16")
+    return W, R
 
 
 def dequant(codes, scales) -> np.ndarray:

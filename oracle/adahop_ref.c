@@ -354,6 +354,85 @@ int adahop_ref_gemm_bf16(const uint16_t* a, int64_t lda, int a_trans,
   return 0;
 }
 
+/* ------------------------------------------------------------------------ */
+/* Running-error terms of an fp32 accumulation (test tolerance, not part of   */
+/* the method). An accumulator that adds the products of a contraction in     */
+/* index order, `step` at a time, rounds after each addition, so its error is */
+/* at most u times the sum of the magnitudes of the partial sums it holds     */
+/* (first order, Higham, "Accuracy and Stability of Numerical Algorithms",    */
+/* recursive summation). With S_j the exact partial sum of the first j*step   */
+/* products and R_j = max over i <= j of |S_i|:                               */
+/*   walk = sum over j of (|S_j| + R_j),  rmax = R at the last j.             */
+/* A run that starts over at some earlier position s (the contraction cut     */
+/* into contiguous parts that are added afterwards) holds S_j - S_s, and      */
+/* |S_j - S_s| <= |S_j| + R_j: walk bounds its partial sums as well.          */
+/* ------------------------------------------------------------------------ */
+static void walk_terms(const double* prod, int64_t K, int64_t step, double* walk, double* rmax) {
+  double s = 0.0, w = 0.0, r = 0.0;
+  for (int64_t t0 = 0; t0 < K; t0 += step) {
+    int64_t t1 = t0 + step < K ? t0 + step : K;
+    for (int64_t t = t0; t < t1; ++t) s += prod[t];
+    double as = fabs(s);
+    if (as > r) r = as;
+    w += as + r;
+  }
+  *walk = w;
+  *rmax = r;
+}
+
+int adahop_ref_walk_mx(const uint8_t* a_codes, const uint8_t* a_scales,
+                       const uint8_t* b_codes, const uint8_t* b_scales, int64_t K, int64_t step,
+                       const int64_t* rows, int64_t nrows, const int64_t* cols, int64_t ncols,
+                       double* walk, double* rmax) {
+  if (!a_codes || !a_scales || !b_codes || !b_scales || !rows || !cols || !walk || !rmax) return -1;
+  if (K < 32 || K % 32 != 0 || step < 1 || nrows < 0 || ncols < 0) return -1;
+  int64_t nblk = K / 32;
+#pragma omp parallel
+  {
+    double* prod = (double*)malloc(sizeof(double) * (size_t)K);
+#pragma omp for schedule(dynamic, 1)
+    for (int64_t a = 0; a < nrows; ++a) {
+      const uint8_t* ar = a_codes + rows[a] * (K / 2);
+      const uint8_t* as = a_scales + rows[a] * nblk;
+      for (int64_t bcol = 0; bcol < ncols; ++bcol) {
+        const uint8_t* br = b_codes + cols[bcol] * (K / 2);
+        const uint8_t* bs = b_scales + cols[bcol] * nblk;
+        for (int64_t t = 0; t < K; ++t)
+          prod[t] = code_at(ar, t) * code_at(br, t) *
+                    ldexp(1.0, ((int)as[t / 32] - 127) + ((int)bs[t / 32] - 127));
+        walk_terms(prod, K, step, &walk[a * ncols + bcol], &rmax[a * ncols + bcol]);
+      }
+    }
+    free(prod);
+  }
+  return 0;
+}
+
+int adahop_ref_walk_bf16(const uint16_t* a, int64_t lda, int a_trans,
+                         const uint16_t* b, int64_t ldb, int b_trans, int64_t K, int64_t step,
+                         const int64_t* rows, int64_t nrows, const int64_t* cols, int64_t ncols,
+                         double* walk, double* rmax) {
+  if (!a || !b || !rows || !cols || !walk || !rmax || K < 0 || step < 1 || nrows < 0 || ncols < 0)
+    return -1;
+#pragma omp parallel
+  {
+    double* prod = (double*)malloc(sizeof(double) * (size_t)(K > 0 ? K : 1));
+#pragma omp for schedule(dynamic, 1)
+    for (int64_t x = 0; x < nrows; ++x) {
+      int64_t i = rows[x];
+      for (int64_t y = 0; y < ncols; ++y) {
+        int64_t j = cols[y];
+        for (int64_t t = 0; t < K; ++t)
+          prod[t] = (double)bf16_to_f32(a_trans ? a[t * lda + i] : a[i * lda + t]) *
+                    (double)bf16_to_f32(b_trans ? b[j * ldb + t] : b[t * ldb + j]);
+        walk_terms(prod, K, step, &walk[x * ncols + y], &rmax[x * ncols + y]);
+      }
+    }
+    free(prod);
+  }
+  return 0;
+}
+
 int adahop_ref_dequant(const uint8_t* codes, const uint8_t* scales, int64_t outer, int64_t K,
                        double* out) {
   if (!codes || !scales || !out || outer < 0 || K % 32 != 0) return -1;

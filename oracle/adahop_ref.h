@@ -83,6 +83,22 @@ int adahop_ref_gemm_bf16(const uint16_t* a, int64_t lda, int a_trans,
                          const int64_t* rows, int64_t nrows, const int64_t* cols, int64_t ncols,
                          double* C, double* absC);
 
+/* Running-error terms of an fp32 accumulation of the same products, on
+ * selected outputs (a test tolerance, not part of the method): with S_j the
+ * exact sum of the first j*step products in contraction order and
+ * R_j = max_{i<=j} |S_i|, walk = sum_j (|S_j| + R_j) and rmax = the last R_j.
+ * u * walk bounds, to first order, the rounding error of an fp32 accumulator
+ * that adds `step` products (or fewer) at a time in contraction order, also
+ * when the contraction is cut into contiguous parts added afterwards. */
+int adahop_ref_walk_mx(const uint8_t* a_codes, const uint8_t* a_scales,
+                       const uint8_t* b_codes, const uint8_t* b_scales, int64_t K, int64_t step,
+                       const int64_t* rows, int64_t nrows, const int64_t* cols, int64_t ncols,
+                       double* walk, double* rmax);
+int adahop_ref_walk_bf16(const uint16_t* a, int64_t lda, int a_trans,
+                         const uint16_t* b, int64_t ldb, int b_trans, int64_t K, int64_t step,
+                         const int64_t* rows, int64_t nrows, const int64_t* cols, int64_t ncols,
+                         double* walk, double* rmax);
+
 /* Dequantize a packed operand to fp64 [outer][K]. */
 int adahop_ref_dequant(const uint8_t* codes, const uint8_t* scales, int64_t outer, int64_t K,
                        double* out);

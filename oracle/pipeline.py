@@ -20,7 +20,14 @@ Packed operands are K-contiguous: A as [m][K], B as [n][K].
 import numpy as np
 
 from . import (COLS, ROWS, dequant, foid, gemm_bf16, gemm_mx, iht_quant, route as
-               route_of, scan_target)
+               route_of, scan_target, walk_bf16, walk_mx)
+
+# Granularity of the running-error terms that bound an fp32 accumulator (a
+# tolerance for comparisons, not part of the method): the FP4 product is
+# accumulated at most one 32-element MX block at a time (each block's products
+# share one scale and sum exactly), the bf16 products 8 at a time at most.
+FP4_STEP = 32
+BF16_STEP = 8
 
 # Per op: (m, n, K) from (T, Din, Dout); the axis of each stored tensor that the
 # contraction runs along; and whether the textbook operand is the stored tensor
@@ -40,8 +47,10 @@ def gemm(op, lhs, rhs, T, Din, Dout, pat_lhs="N", pat_rhs="N", route=None, k=64,
     """Reference result of one call on outputs rows x cols (all if None).
 
     Returns a dict with the route, the FOID indices, the packed operands A and
-    B (codes, scales), the gathered bf16 lines, C (fp64) and absC (the sum of
-    |products| per output, used for the accumulation-error bound).
+    B (codes, scales), the gathered bf16 lines, C (fp64), and per output the
+    terms of the fp32 accumulation-error bound: absC (the sum of |products|),
+    walk and rmax (running-error terms, FP4_STEP / BF16_STEP at a time) and
+    k_inner (the rank of an inner outlier term added after the residual).
     """
     lhs = np.ascontiguousarray(lhs)
     rhs = np.ascontiguousarray(rhs)
@@ -53,10 +62,12 @@ def gemm(op, lhs, rhs, T, Din, Dout, pat_lhs="N", pat_rhs="N", route=None, k=64,
     out = {"route": r, "m": m, "n": n, "K": K, "idx": None,
            "a_gathered": None, "b_gathered": None}
 
+    out["k_inner"] = 0
     if r == "BF16":
         # Both operands hurt: the plain high-precision product (Fig. 5).
         C, absC = gemm_bf16(lhs, a_trans, rhs, b_trans, K, rows, cols)
-        out.update(C=C, absC=absC)
+        walk, rmax = walk_bf16(lhs, a_trans, rhs, b_trans, K, BF16_STEP, rows, cols)
+        out.update(C=C, absC=absC, walk=walk, rmax=rmax)
         return out
 
     # Stage 1, FOID: which stored tensor and axis hold the extracted lines.
@@ -86,6 +97,7 @@ def gemm(op, lhs, rhs, T, Din, Dout, pat_lhs="N", pat_rhs="N", route=None, k=64,
 
     # Stage 3, the residual product on the dequantized operands.
     C, absC = gemm_mx(ac, as_, bc, bs, rows, cols)
+    walk, rmax = walk_mx(ac, as_, bc, bs, FP4_STEP, rows, cols)
 
     # Stage 3 (outlier half) + stage 4: the bf16 outlier product, scatter-added.
     idx = out["idx"]
@@ -98,6 +110,9 @@ def gemm(op, lhs, rhs, T, Din, Dout, pat_lhs="N", pat_rhs="N", route=None, k=64,
             oe, oabs = gemm_bf16(g, 0, rhs, b_trans, K, pos, cols)
             C[hit, :] += oe
             absC[hit, :] += oabs
+            w, rm = walk_bf16(g, 0, rhs, b_trans, K, BF16_STEP, pos, cols)
+            walk[hit, :] += w
+            rmax[hit, :] += rm
     elif r == "OE_RIGHT":
         # Columns idx of B, one line per row: B_g(t,p) = g[p][t].
         g = out["b_gathered"]
@@ -107,6 +122,9 @@ def gemm(op, lhs, rhs, T, Din, Dout, pat_lhs="N", pat_rhs="N", route=None, k=64,
             oe, oabs = gemm_bf16(lhs, a_trans, g, 1, K, rows, pos)
             C[:, hit] += oe
             absC[:, hit] += oabs
+            w, rm = walk_bf16(lhs, a_trans, g, 1, K, BF16_STEP, rows, pos)
+            walk[:, hit] += w
+            rmax[:, hit] += rm
     elif r == "OE_INNER":
         ga, gb = out["a_gathered"], out["b_gathered"]
         kk = idx.size
@@ -114,7 +132,11 @@ def gemm(op, lhs, rhs, T, Din, Dout, pat_lhs="N", pat_rhs="N", route=None, k=64,
         oe, oabs = gemm_bf16(ga, 1, gb, 0, kk, rows, cols)
         C += oe
         absC += oabs
-    out.update(C=C, absC=absC)
+        w, rm = walk_bf16(ga, 1, gb, 0, kk, BF16_STEP, rows, cols)
+        walk += w
+        rmax += rm
+        out["k_inner"] = kk
+    out.update(C=C, absC=absC, walk=walk, rmax=rmax)
     return out
 
 

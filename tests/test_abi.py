@@ -135,6 +135,40 @@ def test_argument_checks_return_before_any_launch():
     assert b"K" in lib.adahop_last_error()
 
 
+def _gpu_visible():
+    import torch
+    return torch.cuda.device_count() > 0
+
+
+@pytest.mark.skipif(_gpu_visible(), reason="fake device pointers: only where no GPU could be reached")
+def test_gemm_mx_outlier_descriptor_checked_before_any_launch():
+    # K = 512 takes the main kernel, whose scale reordering is a launch: every
+    # descriptor error must come back as INVALID (or UNSUPPORTED) before it.
+    # Without a device a launch would fail with ADAHOP_ERR_HIP instead.
+    lib = A.lib()
+    fake = ctypes.c_void_p(256)
+    ws = ctypes.c_void_p(1 << 20)
+    Aop = A.MxOperand(256, 256, 64, 512)
+    Bop = A.MxOperand(256, 256, 64, 512)
+    view = A.Bf16View(256, 512, 1, 0)
+    null_view = A.Bf16View(None, 512, 1, 0)
+    cases = [
+        (A.OeDesc(A.ROUTE["IHT"], 8, 256, view, view), 1),            # not an outlier route
+        (A.OeDesc(A.ROUTE["OE_RIGHT"], 0, 256, view, view), 1),       # k < 1
+        (A.OeDesc(A.ROUTE["OE_RIGHT"], 65, 256, view, view), 1),      # k above n = 64
+        (A.OeDesc(A.ROUTE["OE_LEFT"], 65, 256, view, view), 1),       # k above m = 64
+        (A.OeDesc(A.ROUTE["OE_LEFT"], 8, None, view, view), 1),       # null idx
+        (A.OeDesc(A.ROUTE["OE_INNER"], 8, None, null_view, view), 1),  # null factor
+        (A.OeDesc(A.ROUTE["OE_RIGHT"], 8, 256, A.Bf16View(256, 0, 1, 0), view), 1),   # ld < 1
+        (A.OeDesc(A.ROUTE["OE_RIGHT"], 2000, 256, view, view), 2),    # k above 1024
+    ]
+    for desc, want in cases:
+        got = lib.adahop_gemm_mx(ctypes.byref(Aop), ctypes.byref(Bop), ctypes.byref(desc), fake, 64,
+                                 0, ws, 1 << 30, None)
+        assert got == want, (desc.route, desc.k, got, lib.adahop_last_error())
+        assert lib.adahop_last_error()
+
+
 def test_workspace_sizes():
     # Scores stay in registers; survivor lists (fp64 score + int32 index, k per
     # chunk of 1024 candidates, two lists, each array rounded up to 256 bytes)

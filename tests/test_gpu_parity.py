@@ -10,7 +10,8 @@ import mxfp4_precision_gemms_amd as A
 import oracle
 import synth
 from oracle import pipeline
-from parity import bf16_to_f32, check_bf16, check_f32, f32_to_bf16_rne
+from oracle.pipeline import BF16_STEP, FP4_STEP
+from parity import bf16_to_f32, check_bf16, check_f32, describe, f32_to_bf16_rne, gamma, gamma_of
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -179,6 +180,8 @@ def test_gemm_mx(m, n, K):
     rng = np.random.default_rng(m + n + K)
     _, _, ac, as_, bc, bs = packed_operands(rng, m, n, K)
     ref, absC = oracle.gemm_mx(ac, as_, bc, bs)
+    walk, rmax = oracle.walk_mx(ac, as_, bc, bs, FP4_STEP)
+    g = gamma(absC, walk, rmax)
     d = [torch.from_numpy(x).to(DEV) for x in (ac, as_, bc, bs)]
     say("gemm_mx f32", m, n, K)
     c32 = A.adahop_gemm_mx(*d, out_dtype=torch.float32)
@@ -186,8 +189,8 @@ def test_gemm_mx(m, n, K):
     c16 = A.adahop_gemm_mx(*d, out_dtype=torch.bfloat16)
     torch.cuda.synchronize()
     C32, C16 = host(c32), host(c16)
-    check_f32(C32, ref, absC, K, "gemm f32")
-    check_bf16(C16, ref, absC, K, "gemm bf16")
+    check_f32(C32, ref, g, "gemm f32")
+    say("  " + describe(check_bf16(C16, ref, g, "gemm bf16")))
     # One rounding: the bf16 output is the fp32 result rounded to nearest even.
     assert np.array_equal(C16, f32_to_bf16_rne(C32))
 
@@ -200,32 +203,38 @@ def test_gemm_mx_outlier_term(route, K):
     rng = np.random.default_rng(5)
     a, b, ac, as_, bc, bs = packed_operands(rng, m, n, K)
     ref, absC = oracle.gemm_mx(ac, as_, bc, bs)
+    walk, rmax = oracle.walk_mx(ac, as_, bc, bs, FP4_STEP)
+    k_inner = 0
     if route == "OE_LEFT":
         idx = np.sort(rng.choice(m, k, replace=False)).astype(np.int32)
         la = rand_bf16(rng, (k, K))                      # (p, t)
         oe_ref, oe_abs = oracle.gemm_bf16(la, 0, b, 1, K, np.arange(k), np.arange(n))
-        ref[idx, :] += oe_ref; absC[idx, :] += oe_abs
+        w, r = oracle.walk_bf16(la, 0, b, 1, K, BF16_STEP, np.arange(k), np.arange(n))
+        ref[idx, :] += oe_ref; absC[idx, :] += oe_abs; walk[idx, :] += w; rmax[idx, :] += r
         oe = {"route": route, "k": k, "idx": torch.from_numpy(idx).to(DEV),
               "a": (dev_bf16(la), True), "b": (dev_bf16(b), True)}
     elif route == "OE_RIGHT":
         idx = np.sort(rng.choice(n, k, replace=False)).astype(np.int32)
         lbT = rand_bf16(rng, (K, k))                     # (t, p) stored t-major
         oe_ref, oe_abs = oracle.gemm_bf16(a, 0, lbT, 0, K, np.arange(m), np.arange(k))
-        ref[:, idx] += oe_ref; absC[:, idx] += oe_abs
+        w, r = oracle.walk_bf16(a, 0, lbT, 0, K, BF16_STEP, np.arange(m), np.arange(k))
+        ref[:, idx] += oe_ref; absC[:, idx] += oe_abs; walk[:, idx] += w; rmax[:, idx] += r
         oe = {"route": route, "k": k, "idx": torch.from_numpy(idx).to(DEV),
               "a": (dev_bf16(a), True), "b": (dev_bf16(lbT), False)}
     else:
         ga = rand_bf16(rng, (m, k)); gb = rand_bf16(rng, (n, k))
         oe_ref, oe_abs = oracle.gemm_bf16(ga, 0, gb, 1, k, np.arange(m), np.arange(n))
-        ref += oe_ref; absC += oe_abs
+        w, r = oracle.walk_bf16(ga, 0, gb, 1, k, BF16_STEP, np.arange(m), np.arange(n))
+        ref += oe_ref; absC += oe_abs; walk += w; rmax += r; k_inner = k
         oe = {"route": route, "k": k, "a": (dev_bf16(ga), True), "b": (dev_bf16(gb), True)}
     d = [torch.from_numpy(x).to(DEV) for x in (ac, as_, bc, bs)]
     say("gemm_mx outlier", route, K)
     c32 = A.adahop_gemm_mx(*d, oe=oe, out_dtype=torch.float32)
     c16 = A.adahop_gemm_mx(*d, oe=oe, out_dtype=torch.bfloat16)
     torch.cuda.synchronize()
-    check_f32(host(c32), ref, absC, K, route)
-    check_bf16(host(c16), ref, absC, K, route)
+    g = gamma(absC, walk, rmax, k_inner)
+    check_f32(host(c32), ref, g, route)
+    say("  " + describe(check_bf16(host(c16), ref, g, route)))
     assert np.array_equal(host(c16), f32_to_bf16_rne(host(c32)))
 
 
@@ -267,9 +276,9 @@ def run_and_compare(op, lhs, rhs, T, Din, Dout, pl, pr, route, k, rows=None, col
     if rows is not None:
         C32 = C32[np.ix_(rows, cols)]
         C16 = C16[np.ix_(rows, cols)]
-    K = ref["K"]
-    check_f32(C32, ref["C"], ref["absC"], K, f"{op} {ref['route']} f32")
-    rel, loose = check_bf16(C16, ref["C"], ref["absC"], K, f"{op} {ref['route']} bf16")
+    g = gamma_of(ref)
+    check_f32(C32, ref["C"], g, f"{op} {ref['route']} f32")
+    say("  " + describe(check_bf16(C16, ref["C"], g, f"{op} {ref['route']} bf16")))
     assert np.array_equal(C16, f32_to_bf16_rne(C32))
     return ref
 

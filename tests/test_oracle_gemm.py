@@ -185,3 +185,121 @@ def test_pipeline_close_to_exact(op):
     assert r["a_codes"].shape == (r["m"], r["K"] // 2) and r["b_codes"].shape == (r["n"], r["K"] // 2)
     err = np.linalg.norm(r["C"] - ex) / np.linalg.norm(ex)
     assert 0.02 < err < 0.3
+
+
+# ---------------------------------------------------------------------------
+# Running-error terms (the tolerance of the GPU comparisons)
+# ---------------------------------------------------------------------------
+def _walk_direct(prod, step):
+    """Straight from the definition, in Python floats: S_j, R_j, walk, rmax."""
+    s, r, w = 0.0, 0.0, 0.0
+    for t0 in range(0, len(prod), step):
+        s += float(sum(prod[t0:t0 + step]))
+        r = max(r, abs(s))
+        w += abs(s) + r
+    return w, r
+
+
+def test_walk_closed_form():
+    # Every product equal to 1 (E2M1 code 0x2 = 1.0, unit scales): S_j = j*step,
+    # R_j = S_j, so walk = 2 * step * n(n+1)/2 with n = K/step, and rmax = K.
+    K, step = 256, 32
+    codes = np.full((3, K // 2), 0x22, dtype=np.uint8)
+    scales = np.full((3, K // 32), 127, dtype=np.uint8)
+    W, R = oracle.walk_mx(codes, scales, codes, scales, step)
+    n = K // step
+    assert np.all(W == step * n * (n + 1)) and np.all(R == K)
+    # Alternating blocks of +1 and -1 (code 0xA = -1.0 in the high and low
+    # nibbles): S_j alternates 32, 0, 32, 0, ...; R_j = 32; walk = sum of
+    # |S_j| + 32 = 32 * (n/2) + 32 n.
+    b = codes.copy()
+    b[:, 16:32] = 0xAA
+    b[:, 48:64] = 0xAA
+    b[:, 80:96] = 0xAA
+    b[:, 112:128] = 0xAA
+    W, R = oracle.walk_mx(codes, scales, b, scales, 32)
+    assert np.all(W == 32 * 4 + 32 * 8) and np.all(R == 32)
+
+
+def test_walk_bf16_matches_definition():
+    rng = np.random.default_rng(11)
+    m, n, K = 6, 5, 100                      # K not a multiple of the step: a short last group
+    a = rng.standard_normal((m, K)).astype(np.float32)
+    b = rng.standard_normal((K, n)).astype(np.float32)
+    from parity import f32_to_bf16_rne, bf16_to_f32
+    a16, b16 = f32_to_bf16_rne(a), f32_to_bf16_rne(b)
+    W, R = oracle.walk_bf16(a16, 0, b16, 0, K, 8, np.arange(m), np.arange(n))
+    av, bv = bf16_to_f32(a16).astype(np.float64), bf16_to_f32(b16).astype(np.float64)
+    for i in range(m):
+        for j in range(n):
+            w, r = _walk_direct(av[i] * bv[:, j], 8)
+            assert W[i, j] == pytest.approx(w, rel=1e-12) and R[i, j] == pytest.approx(r, rel=1e-12)
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_walk_bounds_simulated_fp32_accumulators(seed):
+    # fp32 accumulators of the shapes the GPU kernels use, simulated with
+    # numpy float32: groups of `step` products summed with several fp32
+    # roundings inside a group, added in contraction order, the contraction
+    # cut into 1-4 contiguous parts added at the end. Every result must lie
+    # within u (walk + C_INT sum|ab| + 72 rmax) of the exact sum -- and that
+    # bound must be far tighter than the plain (K/step) u sum|ab|.
+    from parity import C_INT, U
+    rng = np.random.default_rng(100 + seed)
+    K, step = 8192, 32
+    worst, ratio = 0.0, []
+    for trial in range(60):
+        x = rng.standard_normal(K) * rng.standard_normal(K)
+        if trial % 3 == 0:
+            x -= x.mean()                            # cancellation
+        if trial % 5 == 0:
+            x[rng.integers(0, K, 8)] *= 1e4          # a few huge products
+        exact = float(np.sum(x.astype(np.float64)))
+        parts = int(rng.integers(1, 5))
+        cuts = [0] + sorted(rng.choice(np.arange(step, K, step), parts - 1, replace=False).tolist()) + [K]
+        total = np.float32(0.0)
+        for p in range(parts):
+            acc = np.float32(0.0)
+            for t0 in range(cuts[p], cuts[p + 1], step):
+                g = x[t0:t0 + step].astype(np.float32)
+                inner = np.float32(0.0)
+                for v in g:                          # worst case: every product rounded in
+                    inner = np.float32(inner + v)
+                acc = np.float32(acc + inner)
+            total = np.float32(total + acc)
+        w, r = _walk_direct(x, step)
+        bound = U * (w + C_INT * float(np.sum(np.abs(x))) + 72 * r)
+        # roundings inside a group are bounded by step * u * sum|x| over it in
+        # this worst-case simulation; the kernels round at most C_INT times
+        inner_extra = (step - C_INT) * U * float(np.sum(np.abs(x)))
+        err = abs(float(total) - exact)
+        assert err <= bound + inner_extra, (trial, err, bound)
+        worst = max(worst, err / (bound + inner_extra))
+        ratio.append(w / ((K / step) * float(np.sum(np.abs(x)))))
+    assert worst < 1.0
+    assert np.median(ratio) < 0.2
+
+
+def test_walk_bounds_one_rounding_per_group():
+    # The model the GEMM bar uses: each group's products summed exactly, one
+    # fp32 rounding per group addition, parts added afterwards. Here the bound
+    # without the inner-group allowance must hold on its own.
+    from parity import C_INT, U
+    rng = np.random.default_rng(7)
+    K, step = 32768, 32
+    for trial in range(40):
+        x = rng.standard_normal(K) * rng.standard_normal(K)
+        if trial % 2:
+            x -= x.mean()
+        groups = x.reshape(-1, step).sum(axis=1)          # exact enough in fp64
+        parts = int(rng.integers(1, 5))
+        cuts = np.linspace(0, groups.size, parts + 1).astype(int)
+        total = np.float32(0.0)
+        for p in range(parts):
+            acc = np.float32(0.0)
+            for gsum in groups[cuts[p]:cuts[p + 1]]:
+                acc = np.float32(acc + np.float32(gsum))
+            total = np.float32(total + acc)
+        w, r = _walk_direct(x, step)
+        bound = U * (w + C_INT * float(np.sum(np.abs(x))) + 72 * r)
+        assert abs(float(total) - float(np.sum(x))) <= bound

@@ -8,16 +8,19 @@ with C_q the fp64 product of the dequantized MXFP4 operands (quantized along
 the contraction dim, without or with the 32-point IHT) and C_exact the fp64
 product of the bf16 operands; A, B are [512,512] N(0,1) with 1% of lines x50;
 five seeds. IHT mixes A's columns and B's rows (the inner lines):
-  - one operand with inner outliers, the other clean (CN, NR): clearly
-    positive on every seed;
+  - one operand with inner outliers, the other clean (CN, NR): above 20 %
+    on every seed (measured minimum 22.9 %, NR);
   - one inner side and one outer side (CC, RR): positive on average (the
     outer lines dominate the error and IHT leaves them as they are);
   - no inner outliers (NN, NC, RN, RC): zero on average, since an orthogonal
     mix of an iid Gaussian block is iid Gaussian (RC, both outer, is noisy:
     a few intersection entries dominate the error);
-  - inner outliers on both sides (CR): not pinned; when both operands'
-    outliers share a 32-block, both rotated blocks are outlier-dominated and
-    the sign depends on the seed.
+  - inner outliers on both sides (CR): measured, not pinned: -11.6, -27.9,
+    -12.8, +32.1, -38.2 % on seeds 0-4 (mean -11.7 %). Rotating both
+    operands' outlier-hit blocks spreads each outlier over its 32 entries, so
+    the ordinary values that share a block with an outlier are lost on both
+    sides of every product that meets one; the sign depends on how the two
+    sides' outlier blocks line up.
 Magnitudes are not printed on the pages: the thresholds are ours."""
 import numpy as np
 import pytest
@@ -55,13 +58,22 @@ def improvement(pa, pb, seed):
 def test_improvement_sign(pair):
     vals = [improvement(pair[0], pair[1], s) for s in range(5)]
     if pair in ONE_SIDED:
-        assert min(vals) > 15, vals
+        assert min(vals) > 20, vals
     elif pair in MIXED:
         assert np.mean(vals) > 10, vals
     elif pair in NEUTRAL:
         assert abs(np.mean(vals)) < 5, vals
     else:
         assert abs(np.mean(vals)) < 10, vals
+
+
+def test_improvement_cr_recorded():
+    # CR (inner outliers on both operands) is a measured result, not a pinned
+    # sign: the mean over the five seeds is negative (-11.7 %), four seeds of
+    # five below zero.
+    vals = [improvement("C", "R", s) for s in range(5)]
+    print("CR improvement per seed (%):", [round(v, 1) for v in vals])
+    assert all(np.isfinite(vals)) and np.mean(vals) < 0 and sum(v < 0 for v in vals) == 4, vals
 
 
 def test_rotation_along_the_wrong_axis_is_neutral():
