@@ -21,8 +21,10 @@
  * Conventions
  *   - Every tensor pointer is a DEVICE pointer owned by the caller. The
  *     library never allocates, frees or synchronizes device memory; scratch
- *     space is the caller's workspace. Every launch is enqueued on `stream`
- *     (a hipStream_t, NULL = the null stream) and the call returns at once.
+ *     space is the caller's workspace (adahop_detect_noalloc alone uses a
+ *     static device array of the library instead). Every launch is enqueued
+ *     on `stream` (a hipStream_t, NULL = the null stream) and the call
+ *     returns at once.
  *   - bf16 tensors are uint16 bit patterns, row-major, leading dimension `ld`
  *     in elements (ld >= cols). A bf16 input quantized along its rows
  *     (contraction along columns) must have 16-byte aligned rows: base
@@ -168,6 +170,24 @@ ADAHOP_API adahop_status adahop_detect(const uint16_t* t, int64_t rows, int64_t 
                                        int64_t ld, adahop_axis axis, int32_t probe,
                                        int32_t k, int32_t* idx_out, void* ws,
                                        size_t ws_bytes, void* stream);
+
+/* FOID without a workspace, for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation). Same arguments, checks and result as adahop_detect; the
+ * selection's scratch (what adahop_detect_workspace_size reports) lives in a
+ * static device array of adahop_detect_noalloc_max_bytes() bytes (1 MiB),
+ * one per GPU, that the library holds until the process ends. The call
+ * itself allocates nothing and clears what must start at zero with a kernel,
+ * not a memset. Errors: as adahop_detect, and UNSUPPORTED when the
+ * selection needs more scratch than that (e.g. k = 1024 over more than about
+ * 170 000 candidates; k = 64 over more than about 1.4 million). Every call
+ * on one GPU shares that GPU's array: calls that overlap in time on one GPU
+ * (different streams or host threads without ordering) race and give
+ * unspecified indices; order them on one stream. */
+ADAHOP_API size_t adahop_detect_noalloc_max_bytes(void);
+ADAHOP_API adahop_status adahop_detect_noalloc(const uint16_t* t, int64_t rows, int64_t cols,
+                                               int64_t ld, adahop_axis axis, int32_t probe,
+                                               int32_t k, int32_t* idx_out, void* stream);
 
 /* ---------------------------------------------------------------------------
  * Zero + gather + IHT + MXFP4 quantization (appendix, kernel 2; abstract).

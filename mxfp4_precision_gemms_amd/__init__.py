@@ -67,6 +67,8 @@ SIGNATURES = {
     "adahop_route": ([_int, _int, _int], _int),
     "adahop_detect_workspace_size": ([_i64, _i64, _int, _i32], _sz),
     "adahop_detect": ([_p, _i64, _i64, _i64, _int, _i32, _i32, _p, _p, _sz, _p], _int),
+    "adahop_detect_noalloc_max_bytes": ([], _sz),
+    "adahop_detect_noalloc": ([_p, _i64, _i64, _i64, _int, _i32, _i32, _p, _p], _int),
     "adahop_line_scores": ([_p, _i64, _i64, _i64, _int, _i32, _p, _p], _int),
     "adahop_classify_pattern": ([ctypes.POINTER(ctypes.c_double), _i64,
                                  ctypes.POINTER(ctypes.c_double), _i64, ctypes.c_double], _int),
@@ -155,6 +157,19 @@ def adahop_detect(t: torch.Tensor, axis, k: int, probe: int = 64,
     _check(lib().adahop_detect(ptr, rows, cols, t.stride(0), _axis(axis), probe, k,
                                idx_out.data_ptr(), _ptr(ws), 0 if ws is None else ws.numel(),
                                _stream(t.device)))
+    return idx_out[:k]
+
+
+def adahop_detect_noalloc(t: torch.Tensor, axis, k: int, probe: int = 64,
+                          idx_out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """FOID with the library's static scratch (no workspace): int32 [k]
+    indices, ascending. Pass idx_out to keep the call free of allocation."""
+    ptr = _bf16_ptr(t, "t")
+    rows, cols = t.shape
+    if idx_out is None:
+        idx_out = torch.empty(max(k, 1), dtype=torch.int32, device=t.device)
+    _check(lib().adahop_detect_noalloc(ptr, rows, cols, t.stride(0), _axis(axis), probe, k,
+                                       idx_out.data_ptr(), _stream(t.device)))
     return idx_out[:k]
 
 

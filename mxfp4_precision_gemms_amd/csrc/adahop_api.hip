@@ -533,6 +533,36 @@ adahop_status detect_checks(const uint16_t* t, int64_t rows, int64_t cols, int64
   if (!foid_fits(ncand, k)) return fail(ADAHOP_ERR_UNSUPPORTED, "adahop_detect: too many candidates");
   return ADAHOP_OK;
 }
+
+// Scratch of adahop_detect_noalloc: FOID's survivor lists and counter, in
+// one array per GPU that the library holds until the process ends. In host
+// code `scratch` names a host-side stand-in, never the device memory: its
+// device address comes from hipGetSymbolAddress, once per device.
+constexpr size_t kNoAllocScratchBytes = size_t(1) << 20;
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+struct NoAllocScratch {
+  std::mutex mu;
+  void* ptr[kMaxDevices] = {};
+};
+NoAllocScratch g_noalloc;
+
+// The current device's address of `scratch`, looked up on its first use with
+// that device current.
+adahop_status noalloc_scratch(void** out) {
+  int dev = 0;
+  ADAHOP_TRY(hip_ok(hipGetDevice(&dev), "hipGetDevice"));
+  if (dev < 0 || dev >= kMaxDevices) return fail(ADAHOP_ERR_UNSUPPORTED, "device index out of range");
+  std::lock_guard<std::mutex> g(g_noalloc.mu);
+  if (!g_noalloc.ptr[dev]) {
+    void* p = nullptr;
+    ADAHOP_TRY(hip_ok(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)), "hipGetSymbolAddress"));
+    if (!p) return fail(ADAHOP_ERR_HIP, "hipGetSymbolAddress returned no address");
+    g_noalloc.ptr[dev] = p;
+  }
+  *out = g_noalloc.ptr[dev];
+  return ADAHOP_OK;
+}
 }  // namespace
 }  // namespace adahop
 
@@ -583,6 +613,25 @@ adahop_status adahop_detect(const uint16_t* t, int64_t rows, int64_t cols, int64
   set_error("");
   ADAHOP_TRY(detect_checks(t, rows, cols, ld, axis, probe, k, idx_out));
   return foid_launch(t, rows, cols, ld, axis, probe, k, idx_out, ws, ws_bytes,
+                     static_cast<hipStream_t>(stream));
+}
+
+size_t adahop_detect_noalloc_max_bytes(void) { return kNoAllocScratchBytes; }
+
+adahop_status adahop_detect_noalloc(const uint16_t* t, int64_t rows, int64_t cols, int64_t ld,
+                                    adahop_axis axis, int32_t probe, int32_t k,
+                                    int32_t* idx_out, void* stream) {
+  set_error("");
+  ADAHOP_TRY(detect_checks(t, rows, cols, ld, axis, probe, k, idx_out));
+  const size_t need = foid_workspace_bytes(axis == ADAHOP_AXIS_ROWS ? rows : cols, k);
+  if (need > kNoAllocScratchBytes)
+    return fail(ADAHOP_ERR_UNSUPPORTED,
+                "adahop_detect_noalloc: this selection needs " + std::to_string(need) +
+                    " bytes of scratch, above the library's static " +
+                    std::to_string(kNoAllocScratchBytes) + "; call adahop_detect with a workspace");
+  void* ws = nullptr;
+  if (need > 0) ADAHOP_TRY(noalloc_scratch(&ws));
+  return foid_launch(t, rows, cols, ld, axis, probe, k, idx_out, ws, need,
                      static_cast<hipStream_t>(stream));
 }
 
