@@ -143,3 +143,75 @@ def gemm(op, lhs, rhs, T, Din, Dout, pat_lhs="N", pat_rhs="N", route=None, k=64,
 def dequantized_product(a_codes, a_scales, b_codes, b_scales) -> np.ndarray:
     """Full fp64 product deq(A) deq(B)^T via a library matmul (small sizes)."""
     return dequant(a_codes, a_scales) @ dequant(b_codes, b_scales).T
+
+
+# ---------------------------------------------------------------------------
+# Saved forward context (appendix item on IHT and quantization: for the
+# activation of the forward path, the quantized residual and the bf16 outlier
+# tensor are kept for backpropagation).
+#
+# Reading: the backward's only product that reads the activation X [T, Din]
+# is the weight gradient dW = GY^T X, which contracts over T. What is kept is
+# therefore X in the form that product consumes: FOID's extracted columns
+# (when the weight gradient's route extracts X's columns, OE-Right), the
+# residual with those columns zeroed, rotated and MXFP4-quantized along T, and
+# the extracted columns in bf16. Routes that would need X in bf16 in the
+# backward (BF16; OE-Left, whose outlier product multiplies GY's lines by the
+# whole of X; OE-Inner, which cuts X's rows) keep no context.
+# ---------------------------------------------------------------------------
+CONTEXT_ROUTES = ("IHT", "MXFP4", "OE_RIGHT")
+
+
+def forward_context(X, pat_gy="N", pat_x="N", route=None, k=64, probe=64):
+    """The context kept for the weight gradient of X [T, Din]: dict with the
+    weight gradient's route, idx (or None), codes [Din][T/2], scales
+    [Din][T/32] (blocks along T, one row per column of X) and lines [k][T]
+    (X's extracted columns, bf16) or None."""
+    X = np.ascontiguousarray(X)
+    r = route or route_of("WGRAD", pat_gy, pat_x)
+    if r not in CONTEXT_ROUTES:
+        raise ValueError(f"no context for a weight gradient on route {r}")
+    idx = None
+    if r == "OE_RIGHT":
+        tensor, axis = scan_target("WGRAD", r)
+        assert tensor == 1 and axis == COLS      # X's columns
+        idx = foid(X, COLS, k, probe)
+    had = 0 if r == "MXFP4" else 32
+    codes, scales, lines = iht_quant(X, ROWS, had, idx, COLS)
+    return {"route": r, "idx": idx, "codes": codes, "scales": scales, "lines": lines}
+
+
+def context_bytes(T, Din, k, route):
+    """Bytes of the context's arrays (without alignment): indices, codes,
+    scales and lines."""
+    ext = route == "OE_RIGHT"
+    return (4 * k if ext else 0) + Din * T // 2 + Din * T // 32 + (2 * k * T if ext else 0)
+
+
+def wgrad_from_context(GY, ctx, T, Din, Dout, pat_gy="N", rows=None, cols=None):
+    """dW = GY^T X with X taken from its saved context: the weight gradient's
+    remaining steps (GY's quantization along T, the residual product, the
+    outlier product GY^T X[:, idx] on the kept lines, the scatter-add), as in
+    gemm() for the same route."""
+    GY = np.ascontiguousarray(GY)
+    r = ctx["route"]
+    m, n, K = Dout, Din, T
+    rows = np.arange(m, dtype=np.int64) if rows is None else np.asarray(rows, dtype=np.int64)
+    cols = np.arange(n, dtype=np.int64) if cols is None else np.asarray(cols, dtype=np.int64)
+    had = 0 if r == "MXFP4" else 32
+    ac, as_, _ = iht_quant(GY, ROWS, had)
+    C, absC = gemm_mx(ac, as_, ctx["codes"], ctx["scales"], rows, cols)
+    walk, rmax = walk_mx(ac, as_, ctx["codes"], ctx["scales"], FP4_STEP, rows, cols)
+    if r == "OE_RIGHT":
+        idx, g = ctx["idx"], ctx["lines"]
+        hit = np.nonzero(np.isin(cols, idx))[0]
+        if hit.size:
+            pos = np.searchsorted(idx, cols[hit])
+            oe, oabs = gemm_bf16(GY, 1, g, 1, K, rows, pos)
+            C[:, hit] += oe
+            absC[:, hit] += oabs
+            w, rm = walk_bf16(GY, 1, g, 1, K, BF16_STEP, rows, pos)
+            walk[:, hit] += w
+            rmax[:, hit] += rm
+    return {"route": r, "m": m, "n": n, "K": K, "a_codes": ac, "a_scales": as_, "C": C,
+            "absC": absC, "walk": walk, "rmax": rmax, "k_inner": 0}
