@@ -333,6 +333,65 @@ ADAHOP_API adahop_status adahop_gemm(adahop_op op, const uint16_t* lhs, const ui
                                      adahop_out_dtype out_dtype, void* ws, size_t ws_bytes,
                                      void* stream);
 
+/* ---------------------------------------------------------------------------
+ * Saved forward context (appendix, kernel 2: for the activation of the
+ * forward path, the quantized residual and the bf16 outlier tensor are kept
+ * for backpropagation). The only backward product that reads the activation
+ * X [T, Din] is the weight gradient dW = GY^T X, contracting over T, so the
+ * context keeps X in the form that product consumes: the k columns its FOID
+ * extracts (route OE_RIGHT), the residual with those columns zeroed, rotated
+ * (FWHT-32, not for route MXFP4) and MXFP4-quantized along T, and those
+ * columns in bf16 -- 17/32 bytes per element plus 2 k T for the lines, up to
+ * 3.76x less than X in bf16. adahop_gemm_wgrad_ctx then computes the weight
+ * gradient from GY and the context alone, bit for bit what adahop_gemm
+ * (WGRAD, GY, X, ...) computes from X.
+ *
+ * pat_gy, pat_x, route and oe_rank are those of the weight gradient
+ * (route AUTO applies adahop_route(WGRAD, pat_gy, pat_x)); the context
+ * holds X for routes IHT, MXFP4 and OE_RIGHT. Routes BF16, OE_LEFT and
+ * OE_INNER read X in bf16 in the backward (the outlier product of OE_LEFT
+ * multiplies GY's lines by the whole of X) and return UNSUPPORTED.
+ *
+ * The context is one caller-owned device buffer of ctx_bytes (16-byte
+ * aligned) at the plan's offsets: idx int32 [k] (SIZE_MAX without
+ * extraction), codes and scales of X's residual with outer = Din, K = T in
+ * the plan's layout (KCHUNK when T is a multiple of 512, as adahop_gemm's
+ * weight gradient packs it), lines bf16 [k][T] (X's extracted columns, one
+ * per row). adahop_ctx_save needs save_ws_bytes of workspace (FOID's
+ * selection scratch; 0: ws may be NULL), adahop_gemm_wgrad_ctx
+ * wgrad_ws_bytes (GY's packed form, the outlier product's partial sums and
+ * the GEMM's scratch). Errors as adahop_gemm; INVALID for a context smaller
+ * than its plan. stage_events: as adahop_gemm_timed (NULL for none); the FOID
+ * and rhs stages are empty. */
+typedef struct {
+  adahop_route_t route;   /* the weight gradient's resolved route */
+  int64_t T, Din, Dout;
+  int32_t k;              /* extracted columns of X (0 without extraction) */
+  adahop_layout layout;   /* layout of the kept codes and scales */
+  size_t ctx_bytes;
+  size_t off_idx, off_codes, off_scales, off_lines;   /* SIZE_MAX if absent */
+  size_t save_ws_bytes;   /* workspace of adahop_ctx_save */
+  size_t wgrad_ws_bytes;  /* workspace of adahop_gemm_wgrad_ctx */
+} adahop_ctx_plan_t;
+
+ADAHOP_API adahop_status adahop_ctx_plan(int64_t T, int64_t Din, int64_t Dout,
+                                         adahop_pattern pat_gy, adahop_pattern pat_x,
+                                         adahop_route_t route, int32_t oe_rank,
+                                         adahop_ctx_plan_t* plan);
+ADAHOP_API adahop_status adahop_ctx_save(const uint16_t* X, int64_t T, int64_t Din,
+                                         int64_t Dout, adahop_pattern pat_gy,
+                                         adahop_pattern pat_x, adahop_route_t route,
+                                         int32_t oe_rank, void* ctx, size_t ctx_bytes,
+                                         void* ws, size_t ws_bytes, void* stream);
+ADAHOP_API adahop_status adahop_gemm_wgrad_ctx(const uint16_t* GY, const void* ctx,
+                                               size_t ctx_bytes, int64_t T, int64_t Din,
+                                               int64_t Dout, adahop_pattern pat_gy,
+                                               adahop_pattern pat_x, adahop_route_t route,
+                                               int32_t oe_rank, void* out,
+                                               adahop_out_dtype out_dtype, void* ws,
+                                               size_t ws_bytes, void* stream,
+                                               void* const* stage_events);
+
 /* As adahop_gemm, and if stage_events is not NULL it must hold
  * ADAHOP_STAGE_EVENTS created hipEvent_t handles: events[0] is recorded on
  * `stream` before the first launch and events[1..5] after the FOID, lhs

@@ -59,6 +59,13 @@ class Plan(ctypes.Structure):
                 ("off_lhs_lines", _sz), ("off_rhs_lines", _sz)]
 
 
+class CtxPlan(ctypes.Structure):
+    _fields_ = [("route", _int), ("T", _i64), ("Din", _i64), ("Dout", _i64), ("k", _i32),
+                ("layout", _int), ("ctx_bytes", _sz), ("off_idx", _sz), ("off_codes", _sz),
+                ("off_scales", _sz), ("off_lines", _sz), ("save_ws_bytes", _sz),
+                ("wgrad_ws_bytes", _sz)]
+
+
 # Exported symbols and their C signatures (argtypes, restype).
 SIGNATURES = {
     "adahop_status_string": ([_int], ctypes.c_char_p),
@@ -84,6 +91,11 @@ SIGNATURES = {
                      _sz, _p], _int),
     "adahop_gemm_timed": ([_int, _p, _p, _i64, _i64, _i64, _int, _int, _int, _i32, _p, _int,
                            _p, _sz, _p, _p], _int),
+    "adahop_ctx_plan": ([_i64, _i64, _i64, _int, _int, _int, _i32, ctypes.POINTER(CtxPlan)], _int),
+    "adahop_ctx_save": ([_p, _i64, _i64, _i64, _int, _int, _int, _i32, _p, _sz, _p, _sz, _p],
+                        _int),
+    "adahop_gemm_wgrad_ctx": ([_p, _p, _sz, _i64, _i64, _i64, _int, _int, _int, _i32, _p, _int,
+                               _p, _sz, _p, _p], _int),
 }
 
 _lib = None
@@ -339,6 +351,17 @@ def _event_handle(ev: "torch.cuda.Event") -> int:
 LAYOUT_ROWS, LAYOUT_KCHUNK = 0, 1
 
 
+def unpack_packed(codes: torch.Tensor, scales: torch.Tensor, outer: int, K: int, layout: int):
+    """Packed operand bytes in `layout` as row-major ([outer][K/2] codes,
+    [outer][K/32] scales); a K-chunked operand is reordered (a copy)."""
+    if layout == LAYOUT_KCHUNK:     # [K/128][outer][64], [K/128][outer][4]
+        codes = codes.view(K // 128, outer, 64).permute(1, 0, 2).reshape(outer, K // 2)
+        # a chunk's scale bytes are its blocks' in the order 0, 2, 1, 3
+        scales = scales.view(K // 128, outer, 4)[:, :, [0, 2, 1, 3]]
+        scales = scales.permute(1, 0, 2).reshape(outer, K // 32)
+    return codes.view(outer, K // 2), scales.view(outer, K // 32)
+
+
 def workspace_views(ws: torch.Tensor, plan: Plan) -> dict:
     """The intermediates a call leaves in its workspace, as tensors. Packed
     operands are returned in the row-major layout ([outer][K/2] codes,
@@ -357,14 +380,86 @@ def workspace_views(ws: torch.Tensor, plan: Plan) -> dict:
         scales = region(off_scales, outer * (K // 32), torch.uint8)
         if codes is None:
             return None, None
-        if plan.layout == LAYOUT_KCHUNK:     # [K/128][outer][64], [K/128][outer][4]
-            codes = codes.view(K // 128, outer, 64).permute(1, 0, 2).reshape(outer, K // 2)
-            # a chunk's scale bytes are its blocks' in the order 0, 2, 1, 3
-            scales = scales.view(K // 128, outer, 4)[:, :, [0, 2, 1, 3]]
-            scales = scales.permute(1, 0, 2).reshape(outer, K // 32)
-        return codes.view(outer, K // 2), scales.view(outer, K // 32)
+        return unpack_packed(codes, scales, outer, K, plan.layout)
 
     out = {"idx": region(plan.off_idx, k, torch.int32)}
     out["a_codes"], out["a_scales"] = packed(plan.off_a_codes, plan.off_a_scales, m)
     out["b_codes"], out["b_scales"] = packed(plan.off_b_codes, plan.off_b_scales, n)
     return out
+
+
+# ---------------------------------------------------------------------------
+# Saved forward context of the activation X for the weight gradient
+# ---------------------------------------------------------------------------
+def adahop_ctx_plan(T: int, Din: int, Dout: int, pat_gy="N", pat_x="N",
+                    route: Optional[str] = None, oe_rank: int = 64) -> CtxPlan:
+    p = CtxPlan()
+    _check(lib().adahop_ctx_plan(T, Din, Dout, PAT[pat_gy], PAT[pat_x], ROUTE[route or "AUTO"],
+                                 oe_rank, ctypes.byref(p)))
+    return p
+
+
+def adahop_ctx_save(X: torch.Tensor, Dout: int, pat_gy="N", pat_x="N",
+                    route: Optional[str] = None, oe_rank: int = 64,
+                    ctx: Optional[torch.Tensor] = None,
+                    ws: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """The context X [T, Din] keeps for its weight gradient (uint8 device
+    buffer laid out as adahop_ctx_plan says)."""
+    _bf16_ptr(X, "X")
+    if not X.is_contiguous():
+        raise ValueError("X must be contiguous")
+    T, Din = X.shape
+    plan = adahop_ctx_plan(T, Din, Dout, pat_gy, pat_x, route, oe_rank)
+    if ctx is None:
+        ctx = torch.empty(max(plan.ctx_bytes, 1), dtype=torch.uint8, device=X.device)
+    if ws is None and plan.save_ws_bytes:
+        ws = torch.empty(plan.save_ws_bytes, dtype=torch.uint8, device=X.device)
+    _check(lib().adahop_ctx_save(X.data_ptr(), T, Din, Dout, PAT[pat_gy], PAT[pat_x],
+                                 ROUTE[route or "AUTO"], oe_rank, ctx.data_ptr(), ctx.numel(),
+                                 _ptr(ws), 0 if ws is None else ws.numel(), _stream(X.device)))
+    return ctx
+
+
+def adahop_gemm_wgrad_ctx(GY: torch.Tensor, ctx: torch.Tensor, Din: int, pat_gy="N", pat_x="N",
+                          route: Optional[str] = None, oe_rank: int = 64,
+                          out_dtype=torch.bfloat16, out: Optional[torch.Tensor] = None,
+                          ws: Optional[torch.Tensor] = None,
+                          stage_events: Optional[Sequence] = None) -> torch.Tensor:
+    """dW [Dout, Din] = GY^T X with X taken from its saved context."""
+    _bf16_ptr(GY, "GY")
+    if not GY.is_contiguous():
+        raise ValueError("GY must be contiguous")
+    if ctx.dtype != torch.uint8 or not ctx.is_cuda:
+        raise TypeError("ctx must be a uint8 device tensor")
+    T, Dout = GY.shape
+    plan = adahop_ctx_plan(T, Din, Dout, pat_gy, pat_x, route, oe_rank)
+    if out is None:
+        out = torch.empty((Dout, Din), dtype=out_dtype, device=GY.device)
+    if ws is None and plan.wgrad_ws_bytes:
+        ws = torch.empty(plan.wgrad_ws_bytes, dtype=torch.uint8, device=GY.device)
+    handles = None
+    if stage_events is not None:
+        if len(stage_events) != STAGE_EVENTS:
+            raise ValueError(f"stage_events needs {STAGE_EVENTS} events")
+        handles = (ctypes.c_void_p * STAGE_EVENTS)(*[_event_handle(e) for e in stage_events])
+    _check(lib().adahop_gemm_wgrad_ctx(GY.data_ptr(), ctx.data_ptr(), ctx.numel(), T, Din, Dout,
+                                       PAT[pat_gy], PAT[pat_x], ROUTE[route or "AUTO"], oe_rank,
+                                       out.data_ptr(), OUT[out.dtype], _ptr(ws),
+                                       0 if ws is None else ws.numel(), _stream(GY.device),
+                                       handles))
+    return out
+
+
+def ctx_views(ctx: torch.Tensor, plan: CtxPlan) -> dict:
+    """The arrays of a saved context as tensors: idx [k] (or None), codes
+    [Din][T/2] and scales [Din][T/32] row-major (reordered from K-chunked if
+    needed), lines [k][T] bf16 bits (or None)."""
+    none = (1 << 64) - 1
+    T, Din, k = plan.T, plan.Din, plan.k
+    codes = ctx[plan.off_codes:plan.off_codes + Din * T // 2]
+    scales = ctx[plan.off_scales:plan.off_scales + Din * T // 32]
+    c, sc = unpack_packed(codes, scales, Din, T, plan.layout)
+    return {"idx": None if plan.off_idx == none else ctx[plan.off_idx:plan.off_idx + 4 * k].view(torch.int32),
+            "codes": c, "scales": sc,
+            "lines": None if plan.off_lines == none
+            else ctx[plan.off_lines:plan.off_lines + 2 * k * T].view(torch.int16).view(k, T)}

@@ -95,14 +95,21 @@ struct Plan {
   bool a_across = false, b_across = false;
   int64_t a_ld = 0, b_ld = 0;
   size_t off_lhs_t = SIZE_MAX, off_rhs_t = SIZE_MAX;
+  // The rhs (X of a weight gradient) comes from a saved forward context:
+  // its indices, packed residual and lines are at these offsets of the
+  // context buffer, and the workspace holds none of them.
+  bool rhs_in_ctx = false;
+  size_t ctx_off_idx = SIZE_MAX, ctx_off_codes = SIZE_MAX, ctx_off_scales = SIZE_MAX,
+         ctx_off_lines = SIZE_MAX, ctx_bytes = 0;
 };
 
 constexpr size_t kNone = SIZE_MAX;
 
 adahop_status make_plan(adahop_op op, int64_t T, int64_t Din, int64_t Dout,
                         adahop_pattern pat_lhs, adahop_pattern pat_rhs, adahop_route_t route,
-                        int32_t oe_rank, Plan* P) {
+                        int32_t oe_rank, Plan* P, bool rhs_in_ctx = false) {
   std::memset(&P->pub, 0, sizeof(P->pub));
+  P->rhs_in_ctx = rhs_in_ctx;
   if (!op_shape(op, T, Din, Dout, &P->shape)) return fail(ADAHOP_ERR_INVALID, "invalid op");
   if (T < 1 || Din < 1 || Dout < 1) return fail(ADAHOP_ERR_INVALID, "sizes must be >= 1");
   if (!valid_pattern(pat_lhs) || !valid_pattern(pat_rhs))
@@ -115,6 +122,10 @@ adahop_status make_plan(adahop_op op, int64_t T, int64_t Din, int64_t Dout,
     return fail(ADAHOP_ERR_INVALID, "contraction length " + std::to_string(s.K) +
                                         " is not a multiple of 32");
   adahop_plan& pb = P->pub;
+  if (rhs_in_ctx && (route == ADAHOP_ROUTE_BF16 || route == ADAHOP_ROUTE_OE_LEFT ||
+                     route == ADAHOP_ROUTE_OE_INNER))
+    return fail(ADAHOP_ERR_UNSUPPORTED, "a weight gradient on this route reads X in bf16: "
+                                        "no context can stand in for it");
   pb.route = route;
   pb.m = s.m; pb.n = s.n; pb.K = s.K;
   pb.scan_tensor = -1;
@@ -208,16 +219,34 @@ adahop_status make_plan(adahop_op op, int64_t T, int64_t Din, int64_t Dout,
 
   size_t off = 0;
   auto take = [&](size_t bytes) { size_t o = off; off += align_up(bytes, kAlign); return o; };
-  if (oe) {
+  if (rhs_in_ctx) {
+    // Only a weight gradient whose route leaves X's lines alone or extracts
+    // X's columns (FOID over X) can take X from a context: its indices,
+    // packed residual and lines live there, laid out like this.
+    if (op != ADAHOP_OP_WGRAD || P->zero_lhs)
+      return fail(ADAHOP_ERR_UNSUPPORTED, "a context holds X for a weight gradient on route IHT, "
+                                          "MXFP4 or OE_RIGHT only");
+    size_t c = 0;
+    auto ctake = [&](size_t bytes) { size_t o = c; c += align_up(bytes, kAlign); return o; };
+    if (oe) P->ctx_off_idx = ctake(sizeof(int32_t) * (size_t)pb.k);
+    P->ctx_off_codes = ctake((size_t)s.n * (size_t)(s.K / 2));
+    P->ctx_off_scales = ctake((size_t)s.n * (size_t)(s.K / 32));
+    if (P->zero_rhs)
+      P->ctx_off_lines = ctake(2 * (size_t)pb.k * (size_t)line_len(s, false, P->rhs_zero_axis));
+    P->ctx_bytes = c;
+  } else if (oe) {
     pb.off_idx = take(sizeof(int32_t) * (size_t)pb.k);
     if (P->foid_bytes) P->off_foid = take(P->foid_bytes);
   }
   pb.off_a_codes = take((size_t)s.m * (size_t)(s.K / 2));
   pb.off_a_scales = take((size_t)s.m * (size_t)(s.K / 32));
-  pb.off_b_codes = take((size_t)s.n * (size_t)(s.K / 2));
-  pb.off_b_scales = take((size_t)s.n * (size_t)(s.K / 32));
+  if (!rhs_in_ctx) {
+    pb.off_b_codes = take((size_t)s.n * (size_t)(s.K / 2));
+    pb.off_b_scales = take((size_t)s.n * (size_t)(s.K / 32));
+  }
   if (P->zero_lhs) pb.off_lhs_lines = take(2 * (size_t)pb.k * (size_t)line_len(s, true, P->lhs_zero_axis));
-  if (P->zero_rhs) pb.off_rhs_lines = take(2 * (size_t)pb.k * (size_t)line_len(s, false, P->rhs_zero_axis));
+  if (P->zero_rhs && !rhs_in_ctx)
+    pb.off_rhs_lines = take(2 * (size_t)pb.k * (size_t)line_len(s, false, P->rhs_zero_axis));
   if (route == ADAHOP_ROUTE_OE_LEFT || route == ADAHOP_ROUTE_OE_RIGHT) {
     const int64_t nx = route == ADAHOP_ROUTE_OE_LEFT ? pb.k : s.m;
     const int64_t ny = route == ADAHOP_ROUTE_OE_LEFT ? s.n : pb.k;
@@ -326,17 +355,31 @@ struct SideJoin {
   }
 };
 
+// A weight gradient's rhs taken from a saved forward context.
+struct CtxIn {
+  const uint8_t* base;
+  size_t bytes;
+};
+
 adahop_status run_gemm(adahop_op op, const uint16_t* lhs, const uint16_t* rhs, int64_t T,
                        int64_t Din, int64_t Dout, adahop_pattern pat_lhs,
                        adahop_pattern pat_rhs, adahop_route_t route, int32_t oe_rank,
                        void* out, adahop_out_dtype out_dtype, void* ws, size_t ws_bytes,
-                       hipStream_t stream, void* const* events) {
+                       hipStream_t stream, void* const* events, const CtxIn* ctx = nullptr) {
   set_error("");
-  if (!lhs || !rhs || !out) return fail(ADAHOP_ERR_INVALID, "null lhs, rhs or out");
+  if (!lhs || (!rhs && !ctx) || !out) return fail(ADAHOP_ERR_INVALID, "null lhs, rhs or out");
   if (out_dtype != ADAHOP_OUT_BF16 && out_dtype != ADAHOP_OUT_F32)
     return fail(ADAHOP_ERR_INVALID, "invalid out_dtype");
   Plan P;
-  ADAHOP_TRY(make_plan(op, T, Din, Dout, pat_lhs, pat_rhs, route, oe_rank, &P));
+  ADAHOP_TRY(make_plan(op, T, Din, Dout, pat_lhs, pat_rhs, route, oe_rank, &P, ctx != nullptr));
+  if (ctx) {
+    if (!ctx->base) return fail(ADAHOP_ERR_INVALID, "null context");
+    if (ctx->bytes < P.ctx_bytes)
+      return fail(ADAHOP_ERR_INVALID, "context smaller than its plan: " + std::to_string(P.ctx_bytes) +
+                                          " bytes");
+    if (reinterpret_cast<uintptr_t>(ctx->base) & 15u)
+      return fail(ADAHOP_ERR_UNSUPPORTED, "the context must be 16-byte aligned");
+  }
   const adahop_plan& pb = P.pub;
   const OpShape& s = P.shape;
   if (pb.ws_bytes > 0 && (ws == nullptr || ws_bytes < pb.ws_bytes))
@@ -398,6 +441,14 @@ adahop_status run_gemm(adahop_op op, const uint16_t* lhs, const uint16_t* rhs, i
   uint8_t* bs = reinterpret_cast<uint8_t*>(w + pb.off_b_scales);
   uint16_t* ll = pb.off_lhs_lines != kNone ? reinterpret_cast<uint16_t*>(w + pb.off_lhs_lines) : nullptr;
   uint16_t* rl = pb.off_rhs_lines != kNone ? reinterpret_cast<uint16_t*>(w + pb.off_rhs_lines) : nullptr;
+  if (ctx) {
+    // X's indices, packed residual and lines as the forward kept them (read only).
+    uint8_t* c = const_cast<uint8_t*>(ctx->base);
+    idx = P.ctx_off_idx != kNone ? reinterpret_cast<int32_t*>(c + P.ctx_off_idx) : nullptr;
+    bc = c + P.ctx_off_codes;
+    bs = c + P.ctx_off_scales;
+    rl = P.ctx_off_lines != kNone ? reinterpret_cast<uint16_t*>(c + P.ctx_off_lines) : nullptr;
+  }
   const bool scan_lhs = pb.scan_tensor == 0;
   auto foid = [&](hipStream_t st) {
     return foid_launch(scan_lhs ? lhs : rhs, scan_lhs ? s.lhs_rows : s.rhs_rows,
@@ -422,7 +473,12 @@ adahop_status run_gemm(adahop_op op, const uint16_t* lhs, const uint16_t* rhs, i
   // the GEMM (and the ROWS-layout scale reordering).
   SideJoin sj;
   SideStream* side = nullptr;
-  if (idx && (scan_lhs ? !P.zero_rhs : !P.zero_lhs)) {
+  if (ctx) {
+    // Only the lhs is left to quantize: FOID and the rhs came with the context.
+    ADAHOP_TRY(E.record(1));
+    ADAHOP_TRY(quant_lhs(stream));
+    ADAHOP_TRY(E.record(2));
+  } else if (idx && (scan_lhs ? !P.zero_rhs : !P.zero_lhs)) {
     int dev = 0;
     if (hipGetDevice(&dev) == hipSuccess && dev >= 0 && dev < kMaxDevices) {
       sj.lock = std::unique_lock<std::mutex>(g_side[dev].mu);
@@ -452,7 +508,7 @@ adahop_status run_gemm(adahop_op op, const uint16_t* lhs, const uint16_t* rhs, i
       ADAHOP_TRY(quant_rhs(stream));
       ADAHOP_TRY(E.record(3));
     }
-  } else {
+  } else if (!ctx) {
     if (idx) ADAHOP_TRY(foid(stream));
     ADAHOP_TRY(E.record(1));
     ADAHOP_TRY(quant_lhs(stream));
@@ -799,6 +855,74 @@ adahop_status adahop_gemm(adahop_op op, const uint16_t* lhs, const uint16_t* rhs
                           void* stream) {
   return run_gemm(op, lhs, rhs, T, Din, Dout, pat_lhs, pat_rhs, route, oe_rank, out, out_dtype,
                   ws, ws_bytes, static_cast<hipStream_t>(stream), nullptr);
+}
+
+adahop_status adahop_ctx_plan(int64_t T, int64_t Din, int64_t Dout, adahop_pattern pat_gy,
+                              adahop_pattern pat_x, adahop_route_t route, int32_t oe_rank,
+                              adahop_ctx_plan_t* plan) {
+  set_error("");
+  if (!plan) return fail(ADAHOP_ERR_INVALID, "adahop_ctx_plan: null plan");
+  Plan P;
+  ADAHOP_TRY(make_plan(ADAHOP_OP_WGRAD, T, Din, Dout, pat_gy, pat_x, route, oe_rank, &P, true));
+  std::memset(plan, 0, sizeof(*plan));
+  plan->route = P.pub.route;
+  plan->T = T; plan->Din = Din; plan->Dout = Dout;
+  plan->k = P.pub.k;
+  plan->layout = P.pub.layout;
+  plan->ctx_bytes = P.ctx_bytes;
+  plan->off_idx = P.ctx_off_idx;
+  plan->off_codes = P.ctx_off_codes;
+  plan->off_scales = P.ctx_off_scales;
+  plan->off_lines = P.ctx_off_lines;
+  plan->save_ws_bytes = P.foid_bytes;
+  plan->wgrad_ws_bytes = P.pub.ws_bytes;
+  return ADAHOP_OK;
+}
+
+adahop_status adahop_ctx_save(const uint16_t* X, int64_t T, int64_t Din, int64_t Dout,
+                              adahop_pattern pat_gy, adahop_pattern pat_x, adahop_route_t route,
+                              int32_t oe_rank, void* ctx, size_t ctx_bytes, void* ws,
+                              size_t ws_bytes, void* stream) {
+  set_error("");
+  if (!X || !ctx) return fail(ADAHOP_ERR_INVALID, "adahop_ctx_save: null X or context");
+  Plan P;
+  ADAHOP_TRY(make_plan(ADAHOP_OP_WGRAD, T, Din, Dout, pat_gy, pat_x, route, oe_rank, &P, true));
+  if (ctx_bytes < P.ctx_bytes)
+    return fail(ADAHOP_ERR_INVALID, "adahop_ctx_save: the context needs " +
+                                        std::to_string(P.ctx_bytes) + " bytes");
+  if (reinterpret_cast<uintptr_t>(ctx) & 15u)
+    return fail(ADAHOP_ERR_UNSUPPORTED, "adahop_ctx_save: the context must be 16-byte aligned");
+  if (P.foid_bytes > 0 && (!ws || ws_bytes < P.foid_bytes))
+    return fail(ADAHOP_ERR_WORKSPACE, "adahop_ctx_save: workspace too small: need " +
+                                          std::to_string(P.foid_bytes) + " bytes");
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  const adahop_plan& pb = P.pub;
+  uint8_t* c = static_cast<uint8_t*>(ctx);
+  int32_t* idx = P.ctx_off_idx != kNone ? reinterpret_cast<int32_t*>(c + P.ctx_off_idx) : nullptr;
+  uint16_t* lines = P.ctx_off_lines != kNone ? reinterpret_cast<uint16_t*>(c + P.ctx_off_lines) : nullptr;
+  // X [T, Din]: FOID over its columns (the weight gradient's OE-Right), then
+  // the residual quantized along T (down the columns) with those columns
+  // zeroed and copied out, in the layout the weight gradient's GEMM streams.
+  if (idx)
+    ADAHOP_TRY(foid_launch(X, T, Din, Din, ADAHOP_AXIS_COLS, 64, pb.k, idx, ws, P.foid_bytes, st));
+  return iht_quant_launch(X, T, Din, Din, ADAHOP_AXIS_ROWS,
+                          pb.route == ADAHOP_ROUTE_MXFP4 ? 0 : 32, idx, idx ? pb.k : 0,
+                          ADAHOP_AXIS_COLS, c + P.ctx_off_codes, c + P.ctx_off_scales, lines,
+                          pb.layout, st);
+}
+
+adahop_status adahop_gemm_wgrad_ctx(const uint16_t* GY, const void* ctx, size_t ctx_bytes,
+                                    int64_t T, int64_t Din, int64_t Dout, adahop_pattern pat_gy,
+                                    adahop_pattern pat_x, adahop_route_t route, int32_t oe_rank,
+                                    void* out, adahop_out_dtype out_dtype, void* ws,
+                                    size_t ws_bytes, void* stream, void* const* stage_events) {
+  if (!ctx) {
+    set_error("");
+    return fail(ADAHOP_ERR_INVALID, "adahop_gemm_wgrad_ctx: null context");
+  }
+  const CtxIn in{static_cast<const uint8_t*>(ctx), ctx_bytes};
+  return run_gemm(ADAHOP_OP_WGRAD, GY, nullptr, T, Din, Dout, pat_gy, pat_x, route, oe_rank, out,
+                  out_dtype, ws, ws_bytes, static_cast<hipStream_t>(stream), stage_events, &in);
 }
 
 adahop_status adahop_gemm_timed(adahop_op op, const uint16_t* lhs, const uint16_t* rhs,

@@ -333,3 +333,45 @@ def test_plan_regions_do_not_overlap(op, pl, pr, route, dims):
     for (o1, s1), (o2, _) in zip(regions, regions[1:]):
         assert o1 + s1 <= o2, regions
     assert regions[-1][0] + regions[-1][1] <= p.ws_bytes
+
+
+def test_ctx_plan_layout_and_errors():
+    # The context of X [T, Din] for dW [Dout, Din]: idx, codes, scales, lines,
+    # each 256-byte aligned, without overlap; its weight-gradient workspace
+    # holds no packed X, so it is smaller than the plain call's by at least X.
+    none = (1 << 64) - 1
+    r256 = lambda b: -(-b // 256) * 256
+    for T, Din, Dout, pg, px, route, k in ((32768, 14336, 4096, "R", "C", None, 64),
+                                           (1024, 384, 256, "R", "C", None, 8),
+                                           (256, 96, 64, "N", "N", None, 1),
+                                           (1024, 384, 256, "R", "C", "MXFP4", 8)):
+        p = A.adahop_ctx_plan(T, Din, Dout, pg, px, route, k)
+        full = A.adahop_gemm_plan("WGRAD", T, Din, Dout, pg, px, route, k)
+        assert p.route == full.route and p.layout == full.layout and (p.T, p.Din, p.Dout) == (T, Din, Dout)
+        ext = A.ROUTE_NAME[p.route] == "OE_RIGHT"
+        assert p.k == (k if ext else 0)
+        want = (r256(4 * k) if ext else 0) + r256(Din * T // 2) + r256(Din * T // 32) + \
+            (r256(2 * k * T) if ext else 0)
+        assert p.ctx_bytes == want
+        assert (p.off_idx != none) == ext and (p.off_lines != none) == ext
+        regs = sorted(r for r in ((p.off_idx, 4 * k), (p.off_codes, Din * T // 2),
+                                  (p.off_scales, Din * T // 32), (p.off_lines, 2 * k * T)) if r[0] != none)
+        for (o1, s1), (o2, _) in zip(regs, regs[1:]):
+            assert o1 + s1 <= o2
+        assert regs[-1][0] + regs[-1][1] <= p.ctx_bytes
+        assert p.wgrad_ws_bytes + Din * T // 2 <= full.ws_bytes
+        assert p.save_ws_bytes == (A.adahop_detect_workspace_size(T, Din, "COLS", k) if ext else 0)
+    # routes whose backward reads X in bf16 keep no context
+    for pg, px, route in (("C", "C", None), ("R", "C", "OE_LEFT"), ("R", "C", "OE_INNER"),
+                          ("R", "C", "BF16")):
+        with pytest.raises(A.AdahopError) as e:
+            A.adahop_ctx_plan(1024, 384, 256, pg, px, route, 8)
+        assert e.value.status == 2, (pg, px, route)
+    lib = A.lib()
+    fake = ctypes.c_void_p(256)
+    # null context; a context smaller than its plan (both before any launch)
+    assert lib.adahop_ctx_save(fake, 1024, 384, 256, 1, 2, -1, 8, None, 0, fake, 1 << 20, None) == 1
+    assert lib.adahop_gemm_wgrad_ctx(fake, None, 0, 1024, 384, 256, 1, 2, -1, 8, fake, 0, fake,
+                                     1 << 30, None, None) == 1
+    assert lib.adahop_gemm_wgrad_ctx(fake, fake, 100, 1024, 384, 256, 1, 2, -1, 8, fake, 0, fake,
+                                     1 << 30, None, None) == 1
