@@ -16,6 +16,20 @@ oracle timed on the host's cores on a bounded sample.
 
 `--rank-sweep` prints instead the latency and error of the product at
 outlier ranks 0-256 and in plain MXFP4 (the pages' variant study, Fig. 10).
+`--sweep-oproj` prints one line per batch size 1..16 and product of the
+Llama3.1-8B o_proj triplet (Fig. 6 per batch size, Table 3's rows): the
+AdaHOP route, plain MXFP4, this library's BF16 route and hipBLASLt's bf16
+GEMM. `--from-context` times a weight gradient from the saved forward
+context of X (adahop_gemm_wgrad_ctx) instead of from X.
+
+Timing: W untimed warm-up calls (preceded by untimed calls for --settle-ms
+of wall time so that the clock has settled, reported as settle_calls), then
+K calls back to back timed by the host clock around a device
+synchronization (value, ms_per_step); per-call HIP events on the call's
+stream give the median and p10/p90 of the same calls back to back, and
+again with a 512 MB buffer written between calls (outside each call's
+events) so that no operand is left in the L2 or the 256 MB Infinity
+Cache.
 `--route NAME` times the workload's product on another route, e.g. BF16
 (the all-bf16 route; its roofline is then the bf16 GEMM's, against the bf16
 peak).
@@ -82,6 +96,54 @@ def measured_traffic(workload_name, summary=TRAFFIC_SUMMARY):
                            f"{rec['write_kib']} KiB x{rec['write_scale']} per launch")
 
 
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def quantiles(ms):
+    import numpy as np
+    a = np.asarray(ms, dtype=np.float64)
+    return {"median": round(float(np.median(a)), 4), "p10": round(float(np.percentile(a, 10)), 4),
+            "p90": round(float(np.percentile(a, 90)), 4)}
+
+
+def settle(torch, step, settle_ms):
+    """Untimed calls until settle_ms of wall time has passed (the shader clock
+    takes a few tens of calls of a millisecond to reach its steady state)."""
+    n, t0 = 0, time.perf_counter()
+    while (time.perf_counter() - t0) * 1e3 < settle_ms:
+        step()
+        n += 1
+        if n % 8 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+    return n
+
+
+def per_call_ms(torch, step, steps, flush=None):
+    """Per-call times from HIP events on the current stream (the library
+    enqueues every launch of a call there, its second stream joined back)."""
+    ev = []
+    for _ in range(steps):
+        if flush is not None:
+            flush()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        step()
+        e1.record()
+        ev.append((e0, e1))
+    torch.cuda.synchronize()
+    return [a.elapsed_time(b) for a, b in ev]
+
+
 def gemm_dims(op, T, Din, Dout):
     return {"FWD": (T, Dout, Din), "DGRAD": (T, Din, Dout), "WGRAD": (Dout, Din, T)}[op]
 
@@ -132,6 +194,7 @@ def cpu_baseline(op, lhs, rhs, T, Din, Dout, call, m, n, K, budget_s=12.0):
         "value": 2.0 * m * n * K / total / 1e12,
         "unit": "TFLOP/s",
         "cores": oracle.max_threads(),
+        "cpu_model": cpu_model(),
         "kind": "oracle",
         "sample": (f"FOID in full ({t_foid:.2f}s); IHT+quant of both operands on the first "
                    f"{slab} of K={K} contraction positions, x{K / slab:.0f}; fp64 product on a "
@@ -195,6 +258,132 @@ def rank_sweep(A, torch, np, wl, call, lhs, rhs, m, n, K, args):
                       "steps": args.steps, "warmup": args.warmup}))
 
 
+def mfma_ceiling(torch, np, args):
+    """The FP4 matrix cores' steady-state rate and shader clock with no memory
+    traffic (libadahop_probe.so): one workgroup per CU, 8 independent scaled
+    32x32x64 FP4 MFMAs per wave on switching register operands, launches of
+    about 0.1 s back to back. The practical ceiling under the device's power
+    limit for any FP4 kernel, against the nominal 10.1 PFLOP/s (2.4 GHz)."""
+    import ctypes
+    lib = ctypes.CDLL(os.path.join(ROOT, "mxfp4_precision_gemms_amd", "libadahop_probe.so"))
+    for fn in (lib.adahop_probe_mfma_fp4, lib.adahop_probe_lds_read):
+        fn.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
+                       ctypes.c_void_p]
+    blocks = torch.cuda.get_device_properties(0).multi_processor_count
+    iters, launches = 400000, 5
+    scratch = torch.empty(blocks * 16 + 2048, dtype=torch.uint8, device="cuda:0")
+    cyc = np.zeros(launches)
+    tick = np.zeros(launches)
+    rc = lib.adahop_probe_mfma_fp4(blocks, iters, launches, scratch.data_ptr(), cyc.ctypes.data,
+                                   tick.ctypes.data)
+    if rc != 0:
+        sys.exit(f"mfma probe failed: hipError {rc}")
+    mfmas_per_wave = 8 * iters
+    clock = cyc / tick * 0.1                              # GHz (ticks at 100 MHz)
+    util = mfmas_per_wave * 2 * 32 / cyc                  # 2 waves per SIMD, 32 cycles per MFMA
+    tflops = blocks * 8 * mfmas_per_wave * 131072 / (tick / 1e8) / 1e12
+    lit = 20000
+    lc, lt = np.zeros(3), np.zeros(3)
+    rc = lib.adahop_probe_lds_read(blocks, lit, 3, scratch.data_ptr(), lc.ctypes.data, lt.ctypes.data)
+    if rc != 0:
+        sys.exit(f"lds probe failed: hipError {rc}")
+    lds_bpc = 8 * 512 * 16 * lit / lc                   # bytes per shader clock per CU
+    print(json.dumps({"lds_read": {"bytes_per_clk_per_cu": [round(float(b), 1) for b in lds_bpc],
+                                   "clock_ghz": [round(float(c), 3) for c in lc / lt * 0.1]},
+                      "mfma_ceiling": {
+        "kernel": "8 x v_mfma_scale_f32_32x32x64_f8f6f4 (E2M1 x E2M1) per wave per iteration, "
+                  "register operands, 8 waves per CU",
+        "cus": blocks, "launch_ms": [round(float(t) / 1e5, 2) for t in tick],
+        "clock_ghz": [round(float(c), 3) for c in clock],
+        "mfma_busy": [round(float(u), 4) for u in util],
+        "tflops": [round(float(t), 1) for t in tflops],
+        "frac_of_nominal_peak": [round(float(t) / PEAK_FP4_TFLOPS, 4) for t in tflops]}}), flush=True)
+
+
+def sweep_oproj(A, torch, np, args):
+    """One JSON line per (batch size, product) of the Llama3.1-8B o_proj
+    triplet: effective TFLOP/s of the AdaHOP route with its GEMM stage's
+    roofline fraction, beside plain MXFP4 (no rotation, no extraction), this
+    library's BF16 route and hipBLASLt's bf16 GEMM (2-D torch.matmul, the
+    faster of two operand arrangements), all on the same synthetic tensors,
+    per-call medians over back-to-back calls."""
+    from synth import workloads as W
+    dev = torch.device("cuda:0")
+    to_dev = lambda x: torch.from_numpy(x.view(np.int16)).to(dev).view(torch.bfloat16)
+    for bs in (1, 2, 4, 8, 16):
+        wl = W.l31_8b_oproj_triplet(bs)
+        T, Din, Dout = wl.T, wl.Din, wl.Dout
+        tens = {k: to_dev(v.make(0)) for k, v in wl.tensors.items()}
+        for call in wl.calls:
+            op = call.op
+            m, n, K = gemm_dims(op, T, Din, Dout)
+            flops = 2.0 * m * n * K
+            lhs, rhs = tens[call.lhs], tens[call.rhs]
+            out_shape = {"FWD": (T, Dout), "DGRAD": (T, Din), "WGRAD": (Dout, Din)}[op]
+            out = torch.empty(out_shape, dtype=torch.bfloat16, device=dev)
+            line = {"sweep": "llama3.1-8b_oproj", "bs": bs, "op": op, "m": m, "n": n, "K": K,
+                    "pattern_pair": call.pat_lhs + call.pat_rhs}
+            for label, route in (("adahop", call.route), ("mxfp4", "MXFP4"), ("bf16_route", "BF16")):
+                plan = A.adahop_gemm_plan(op, T, Din, Dout, call.pat_lhs, call.pat_rhs, route, call.k)
+                ws = torch.empty(max(plan.ws_bytes, 1), dtype=torch.uint8, device=dev)
+                step = lambda ev=None: A.adahop_gemm(op, lhs, rhs, call.pat_lhs, call.pat_rhs, route,
+                                                     call.k, out=out, ws=ws, stage_events=ev)
+                settle(torch, step, args.settle_ms / 4)
+                for _ in range(args.warmup):
+                    step()
+                ms = float(np.median(per_call_ms(torch, step, args.steps)))
+                entry = {"route": A.ROUTE_NAME[plan.route], "ms": round(ms, 4),
+                         "tflops": round(flops / ms / 1e9, 1)}
+                if label == "adahop":
+                    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(A.STAGE_EVENTS)]
+                           for _ in range(args.steps)]
+                    for e in evs:
+                        step(e)
+                    torch.cuda.synchronize()
+                    gms = float(np.median([e[4].elapsed_time(e[5]) for e in evs]))
+                    entry["gemm_stage_ms"] = round(gms, 4)
+                    entry["gemm_frac_mxfp4_peak"] = round(flops / gms / 1e9 / PEAK_FP4_TFLOPS, 4)
+                    entry["pct_mxfp4_peak"] = round(100 * flops / ms / 1e9 / PEAK_FP4_TFLOPS, 2)
+                line[label] = entry
+                del ws
+            if op == "WGRAD":
+                cplan = A.adahop_ctx_plan(T, Din, Dout, call.pat_lhs, call.pat_rhs, call.route, call.k)
+                ctx = A.adahop_ctx_save(rhs, Dout, call.pat_lhs, call.pat_rhs, call.route, call.k)
+                ws = torch.empty(max(cplan.wgrad_ws_bytes, 1), dtype=torch.uint8, device=dev)
+                step = lambda: A.adahop_gemm_wgrad_ctx(lhs, ctx, Din, call.pat_lhs, call.pat_rhs,
+                                                       call.route, call.k, out=out, ws=ws)
+                for _ in range(args.warmup):
+                    step()
+                ms = float(np.median(per_call_ms(torch, step, args.steps)))
+                save = lambda: A.adahop_ctx_save(rhs, Dout, call.pat_lhs, call.pat_rhs, call.route,
+                                                 call.k, ctx=ctx)
+                for _ in range(3):
+                    save()
+                sms = float(np.median(per_call_ms(torch, save, args.steps)))
+                line["adahop_from_context"] = {"ms": round(ms, 4), "tflops": round(flops / ms / 1e9, 1),
+                                               "ctx_save_ms": round(sms, 4),
+                                               "ctx_mib": round(cplan.ctx_bytes / 2 ** 20, 1),
+                                               "x_bf16_mib": round(2 * T * Din / 2 ** 20, 1)}
+                del ctx, ws
+            arr = {"FWD": ((lambda: (lhs, rhs.t())), (lambda: (lhs, rhs.t().contiguous()))),
+                   "DGRAD": ((lambda: (lhs, rhs)), (lambda: (lhs, rhs.t().contiguous().t()))),
+                   "WGRAD": ((lambda: (lhs.t(), rhs)), (lambda: (lhs.t().contiguous(), rhs)))}[op]
+            best = None
+            for mk in arr:
+                a2 = mk()
+                for _ in range(3):
+                    torch.matmul(*a2)
+                ms = float(np.median(per_call_ms(torch, lambda: torch.matmul(*a2), args.steps)))
+                best = ms if best is None else min(best, ms)
+                del a2
+            line["hipblaslt_bf16"] = {"ms": round(best, 4), "tflops": round(flops / best / 1e9, 1)}
+            line["speedup_vs_hipblaslt_bf16"] = round(best / line["adahop"]["ms"], 3)
+            line["speedup_vs_bf16_route"] = round(line["bf16_route"]["ms"] / line["adahop"]["ms"], 3)
+            line["adahop_vs_mxfp4"] = round(line["mxfp4"]["ms"] / line["adahop"]["ms"], 3)
+            print(json.dumps(line), flush=True)
+        del tens
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -213,6 +402,20 @@ def main():
                     help="instead of the timed line: for outlier ranks 0 (IHT alone), 16, 32, 64, "
                          "128, 256 and plain MXFP4, print the call's latency and its error against "
                          "an fp32 product of the same bf16 operands")
+    ap.add_argument("--settle-ms", type=float, default=300.0,
+                    help="untimed calls for this much wall time before the warm-up calls, so that "
+                         "the shader clock has reached its steady state (0: none)")
+    ap.add_argument("--no-flush-timing", action="store_true",
+                    help="skip the per-call timing with the caches flushed between calls")
+    ap.add_argument("--sweep-oproj", action="store_true",
+                    help="instead of the timed line: the o_proj triplet at batch sizes 1-16 against "
+                         "plain MXFP4, the BF16 route and hipBLASLt bf16, one JSON line each")
+    ap.add_argument("--from-context", action="store_true",
+                    help="time a weight gradient from the saved forward context of X "
+                         "(adahop_gemm_wgrad_ctx) instead of from X")
+    ap.add_argument("--mfma-ceiling", action="store_true",
+                    help="instead of the timed line: the FP4 matrix cores' rate and clock with no "
+                         "memory traffic (the practical ceiling under the power limit)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a 1 GiB device-to-device copy 3 times (a known-size reference "
                          "for HBM byte counters) and exit")
@@ -235,6 +438,13 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"copy_calibration_bytes": 1 << 30, "copies": 3}))
+        return
+
+    if args.sweep_oproj:
+        sweep_oproj(A, torch, np, args)
+        return
+    if args.mfma_ceiling:
+        mfma_ceiling(torch, np, args)
         return
 
     wls = workloads()
@@ -264,14 +474,33 @@ def main():
     out_dtype = torch.bfloat16 if args.out_dtype == "bf16" else torch.float32
     plan = A.adahop_gemm_plan(op, T, Din, Dout, call.pat_lhs, call.pat_rhs, call.route, call.k)
     route = A.ROUTE_NAME[plan.route]
-    ws = torch.empty(max(plan.ws_bytes, 1), dtype=torch.uint8, device=dev)
     out_shape = {"FWD": (T, Dout), "DGRAD": (T, Din), "WGRAD": (Dout, Din)}[op]
     out = torch.empty(out_shape, dtype=out_dtype, device=dev)
+    ctx_info = None
+    if args.from_context:
+        if op != "WGRAD":
+            sys.exit("--from-context applies to weight-gradient workloads")
+        cplan = A.adahop_ctx_plan(T, Din, Dout, call.pat_lhs, call.pat_rhs, call.route, call.k)
+        ctx = A.adahop_ctx_save(rhs, Dout, call.pat_lhs, call.pat_rhs, call.route, call.k)
+        ws = torch.empty(max(cplan.wgrad_ws_bytes, 1), dtype=torch.uint8, device=dev)
+        save = lambda: A.adahop_ctx_save(rhs, Dout, call.pat_lhs, call.pat_rhs, call.route, call.k,
+                                         ctx=ctx)
+        for _ in range(3):
+            save()
+        ctx_info = {"ctx_save_ms": quantiles(per_call_ms(torch, save, args.steps)),
+                    "ctx_bytes": cplan.ctx_bytes, "x_bf16_bytes": 2 * T * Din}
 
-    def step(events=None):
-        A.adahop_gemm(op, lhs, rhs, call.pat_lhs, call.pat_rhs, call.route, call.k,
-                      out=out, ws=ws, stage_events=events)
+        def step(events=None):
+            A.adahop_gemm_wgrad_ctx(lhs, ctx, Din, call.pat_lhs, call.pat_rhs, call.route, call.k,
+                                    out=out, ws=ws, stage_events=events)
+    else:
+        ws = torch.empty(max(plan.ws_bytes, 1), dtype=torch.uint8, device=dev)
 
+        def step(events=None):
+            A.adahop_gemm(op, lhs, rhs, call.pat_lhs, call.pat_rhs, call.route, call.k,
+                          out=out, ws=ws, stage_events=events)
+
+    settle_calls = settle(torch, step, args.settle_ms) if args.settle_ms > 0 else 0
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -282,6 +511,16 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_per_step = wall / args.steps * 1e3
+
+    # The same number of calls again, each between HIP events: back to back,
+    # then with the caches flushed before every call (outside its events).
+    per_call = quantiles(per_call_ms(torch, step, args.steps))
+    per_call_flushed = None
+    if not args.no_flush_timing:
+        scratch = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+        flush = lambda: scratch.fill_(1)
+        per_call_flushed = quantiles(per_call_ms(torch, step, args.steps, flush))
+        del scratch
 
     # Stage breakdown and the GEMM's own rate, from a second run of the same
     # steps with HIP events between the stages (each event record adds a few
@@ -302,7 +541,8 @@ def main():
     call_ms = float(np.mean([e[0].elapsed_time(e[-1]) for e in ev]))
     flops = 2.0 * m * n * K
     value = flops / (ms_per_step / 1e3) / 1e12
-    gemm_ms = stage_ms["gemm"]
+    # The GEMM kernel's own time: median over the steps of its stage events.
+    gemm_ms = float(np.median([e[4].elapsed_time(e[5]) for e in ev]))
     achieved = flops / (gemm_ms / 1e3) / 1e12
     bf16 = route == "BF16"
     peak = PEAK_BF16_TFLOPS if bf16 else PEAK_FP4_TFLOPS
@@ -314,7 +554,10 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "settle_calls": settle_calls,
         "ms_per_step": round(ms_per_step, 4),
+        "per_call_ms": per_call,
+        "per_call_ms_cache_flushed": per_call_flushed,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -337,6 +580,7 @@ def main():
                        ("gemm is the MFMA kernel plus, when its last round is split along K, "
                         "the fixup kernel"),
         "call_ms_events": round(call_ms, 4),
+        "gemm_stage_ms_median": round(gemm_ms, 4),
         "roofline": {"bound": "mfma",
                      "kernel": ("gemm_mx_ring8_kernel<bf16> + gemm_split_fixup_kernel (bf16 MFMA "
                                 "GEMM; the fixup adds the K-parts of a split last round)") if bf16 else
@@ -349,6 +593,12 @@ def main():
     }
     if bf16:
         del result["pct_mxfp4_peak"]
+    if ctx_info is not None:
+        result["config"]["from_context"] = True
+        result["context"] = ctx_info
+        result["stages_note"] = ("weight gradient from the saved forward context of X: FOID and X's "
+                                 "quantization ran in the forward (context save, timed apart in "
+                                 "context.ctx_save_ms); quant_lhs is GY's")
     traffic, note = measured_traffic(wl.name, TRAFFIC_SUMMARY_BF16 if bf16 else TRAFFIC_SUMMARY)
     result["roofline"]["traffic"] = None if traffic is None else round(traffic)
     result["roofline"]["traffic_note"] = note

@@ -261,8 +261,9 @@ typedef struct {
  * adahop_gemm_mx_workspace_size(...) bytes of 16-byte aligned workspace: the
  * outlier product's partial sums (OE_LEFT/OE_RIGHT) and, when K is a multiple
  * of 512, a copy of both scale arrays reordered for the GEMM plus, when the
- * last round of 256 x 256 tiles is split along K (at most 128 tiles left
- * over from whole rounds of 256, K / 128 a multiple of 8 and at least 32),
+ * last round of 256 x 256 tiles is split along K (at most half a round left
+ * over from whole rounds of one tile per compute unit of the current device
+ * -- 256 on an MI355X --, K / 128 a multiple of 8 and at least 32),
  * 256 KB of fp32 partial sums per tile part (0 when none applies; ws may then
  * be NULL). Its contents after the call are unspecified.
  * Errors: INVALID for NULL pointers, K mismatch, K % 32 != 0, ldc < n, a bad

@@ -12,6 +12,10 @@ ROOT = os.path.dirname(HERE)
 SRC = os.path.join(HERE, "csrc")
 OUT = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libadahop.so")
+# Measurement probe of the FP4 matrix cores' clock ceiling (bench.py
+# --mfma-ceiling); not part of the AdaHOP path, built as its own library.
+PROBE_SRC = "probe_mfma.hip"
+PROBE_LIB = os.path.join(HERE, "libadahop_probe.so")
 SOURCES = ["adahop_api.hip", "foid.hip", "iht_quant.hip", "gemm_mx.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
@@ -48,6 +52,10 @@ def build(verbose: bool = False) -> str:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
     os.replace(tmp, LIB)
+    pobj = _compile(PROBE_SRC, verbose)
+    ptmp = PROBE_LIB + ".tmp"
+    subprocess.run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", pobj, "-o", ptmp], check=True)
+    os.replace(ptmp, PROBE_LIB)
     return LIB
 
 

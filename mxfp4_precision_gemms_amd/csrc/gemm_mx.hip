@@ -30,6 +30,7 @@
 //   the output type (the scatter-add). Inner extraction (a rank-k term on
 //   every output) runs as extra bf16 MFMAs on the tile's own accumulators.
 //   No atomics: results are deterministic.
+#include <mutex>
 #include <utility>
 
 #include "adahop_internal.h"
@@ -1312,10 +1313,29 @@ bool ring_shape_ok(int64_t m, int64_t n, int64_t K) {
 // Split of the main kernel's last round. One 512-thread workgroup runs per
 // CU; when the last round would leave more than half of the CUs idle, its
 // tiles are split along K into up to 4 parts (each a multiple of 4 stages
-// and at least 16), which a fixup kernel adds. kSplitCUs is the CU count of
-// a whole gfx950 (MI355X); on a device with fewer CUs the split is only less
-// useful, never wrong.
-constexpr int64_t kSplitCUs = 256;
+// and at least 16), which a fixup kernel adds. The CU count is the current
+// device's, queried once per device (256 on a whole gfx950, and when no
+// device can be queried, e.g. for a plan made without a GPU).
+constexpr int64_t kDefaultCUs = 256;
+int64_t device_cus() {
+  static std::mutex mu;
+  static int cus[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
+    (void)hipGetLastError();
+    return kDefaultCUs;
+  }
+  std::lock_guard<std::mutex> g(mu);
+  if (cus[dev] == 0) {
+    int v = 0;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v < 1) {
+      (void)hipGetLastError();
+      v = (int)kDefaultCUs;
+    }
+    cus[dev] = v;
+  }
+  return cus[dev];
+}
 struct TailSplit {
   int64_t full, split;   // whole tiles, split tiles
   int parts;
@@ -1323,10 +1343,11 @@ struct TailSplit {
 // nk: the number of ring stages along K (K / 128 for FP4, K / 32 for bf16).
 TailSplit tail_split(int64_t m, int64_t n, int64_t nk) {
   const int64_t tiles = ((m + BM - 1) / BM) * ((n + BN - 1) / BN);
-  const int64_t rem = tiles % kSplitCUs;
+  const int64_t cus = device_cus();
+  const int64_t rem = tiles % cus;
   int parts = 1;
-  if (rem > 0 && 2 * rem <= kSplitCUs) {
-    parts = (int)(kSplitCUs / rem < 4 ? kSplitCUs / rem : 4);
+  if (rem > 0 && 2 * rem <= cus) {
+    parts = (int)(cus / rem < 4 ? cus / rem : 4);
     while (parts > 1 && (nk % (4 * parts) != 0 || nk / parts < 16)) --parts;
   }
   if (parts < 2) return {tiles, 0, 1};
@@ -1435,9 +1456,9 @@ adahop_status gemm_mx_launch(const uint8_t* a_codes, const uint8_t* a_scales,
     g.split_ws = ts.split ? reinterpret_cast<float*>(static_cast<char*>(scratch) +
                                                      (kchunk ? 0 : staging_bytes(m, n, K)))
                           : nullptr;
-    // Persistent: at most one workgroup per CU of a whole gfx950.
-    const int64_t items = ts.full + ts.split * ts.parts;
-    const dim3 rgrid((unsigned)(items < kSplitCUs ? items : kSplitCUs));
+    // Persistent: at most one workgroup per CU.
+    const int64_t items = ts.full + ts.split * ts.parts, cus = device_cus();
+    const dim3 rgrid((unsigned)(items < cus ? items : cus));
     if (kchunk)
       gemm_mx_ring8_kernel<true, false><<<rgrid, dim3(kRing8Threads), 0, stream>>>(g);
     else
@@ -1500,8 +1521,8 @@ adahop_status bf16_ring_launch(const uint16_t* a, int a_across, int64_t lda, con
   g.split_count = (int)ts.split;
   g.split_parts = ts.parts;
   g.split_ws = ts.split ? static_cast<float*>(scratch) : nullptr;
-  const int64_t items = ts.full + ts.split * ts.parts;
-  const dim3 rgrid((unsigned)(items < kSplitCUs ? items : kSplitCUs));
+  const int64_t items = ts.full + ts.split * ts.parts, cus = device_cus();
+  const dim3 rgrid((unsigned)(items < cus ? items : cus));
   if (a_across && b_across)
     gemm_mx_ring8_kernel<false, true, true, true><<<rgrid, dim3(kRing8Threads), 0, stream>>>(g);
   else if (a_across)
