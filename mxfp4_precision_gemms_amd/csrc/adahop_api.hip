@@ -105,6 +105,21 @@ struct Plan {
 
 constexpr size_t kNone = SIZE_MAX;
 
+// The outer outlier product's factors of a plan (OE_LEFT: X the gathered
+// rows of A, Y the rhs as stored; OE_RIGHT: X the lhs as stored, Y the
+// gathered columns of B), on the given tensors and gathered lines.
+void oe_views(const Plan& P, const uint16_t* lhs, const uint16_t* rhs, const uint16_t* ll,
+              const uint16_t* rl, Bf16View* X, Bf16View* Y) {
+  const OpShape& s = P.shape;
+  if (P.pub.route == ADAHOP_ROUTE_OE_LEFT) {
+    *X = lines_by_line(ll, line_len(s, true, P.lhs_zero_axis));       // (p, t)
+    *Y = stored_view(rhs, s.rhs_cols, s.rhs_contract);               // (j, t)
+  } else {
+    *X = stored_view(lhs, s.lhs_cols, s.lhs_contract);               // (i, t)
+    *Y = lines_by_line(rl, line_len(s, false, P.rhs_zero_axis));      // (p, t)
+  }
+}
+
 adahop_status make_plan(adahop_op op, int64_t T, int64_t Din, int64_t Dout,
                         adahop_pattern pat_lhs, adahop_pattern pat_rhs, adahop_route_t route,
                         int32_t oe_rank, Plan* P, bool rhs_in_ctx = false) {
@@ -251,7 +266,15 @@ adahop_status make_plan(adahop_op op, int64_t T, int64_t Din, int64_t Dout,
     const int64_t nx = route == ADAHOP_ROUTE_OE_LEFT ? pb.k : s.m;
     const int64_t ny = route == ADAHOP_ROUTE_OE_LEFT ? s.n : pb.k;
     P->splits = oe_splits(nx, ny, s.K);
-    P->off_partials = take(sizeof(float) * (size_t)(P->splits + 1) * (size_t)nx * (size_t)ny);
+    // Room for the outlier product run either way: before the GEMM (its
+    // partial sums and their sum) or inside it (partial sums and the
+    // extracted lines' residuals), whichever the call's pointers allow.
+    size_t bytes = sizeof(float) * (size_t)(P->splits + 1) * (size_t)nx * (size_t)ny;
+    Bf16View X, Y;
+    oe_views(*P, nullptr, nullptr, nullptr, nullptr, &X, &Y);
+    const int fp = oe_fused_parts(s.m, s.n, s.K, route, pb.k, X, Y, false);
+    if (fp > 0) bytes = std::max(bytes, oe_fused_bytes(s.m, s.n, route, pb.k, fp));
+    P->off_partials = take(bytes);
   }
   // Shapes a launcher would refuse are rejected here, before the call's
   // first launch.
@@ -527,22 +550,26 @@ adahop_status run_gemm(adahop_op op, const uint16_t* lhs, const uint16_t* rhs, i
   if (pb.route == ADAHOP_ROUTE_OE_LEFT || pb.route == ADAHOP_ROUTE_OE_RIGHT) {
     float* partials = reinterpret_cast<float*>(w + P.off_partials);
     Bf16View X, Y;
-    int64_t nx, ny;
-    if (pb.route == ADAHOP_ROUTE_OE_LEFT) {
-      X = lines_by_line(ll, line_len(s, true, P.lhs_zero_axis));       // (p, t)
-      Y = stored_view(rhs, s.rhs_cols, s.rhs_contract);               // (j, t)
-      nx = pb.k; ny = s.n;
-    } else {
-      X = stored_view(lhs, s.lhs_cols, s.lhs_contract);               // (i, t)
-      Y = lines_by_line(rl, line_len(s, false, P.rhs_zero_axis));      // (p, t)
-      nx = s.m; ny = pb.k;
-    }
-    ADAHOP_TRY(oe_product_launch(X, Y, nx, ny, s.K, P.splits, partials, stream));
+    oe_views(P, lhs, rhs, ll, rl, &X, &Y);
+    const int64_t nx = pb.route == ADAHOP_ROUTE_OE_LEFT ? pb.k : s.m;
+    const int64_t ny = pb.route == ADAHOP_ROUTE_OE_LEFT ? s.n : pb.k;
     oe.mode = pb.route;
     oe.k = pb.k;
     oe.idx = idx;
-    oe.partials = partials;
-    oe.splits = P.splits;
+    oe.a = X;
+    oe.b = Y;
+    // Inside the GEMM launch when the main kernel runs and the factors
+    // allow it; else as its own kernels, before the GEMM.
+    oe.fused_parts = gemm_mx_ring_used(ac, as, bc, bs, s.m, s.n, s.K, pb.layout)
+                         ? oe_fused_parts(s.m, s.n, s.K, pb.route, pb.k, X, Y, true)
+                         : 0;
+    if (oe.fused_parts > 0) {
+      oe.fused_ws = partials;
+    } else {
+      ADAHOP_TRY(oe_product_launch(X, Y, nx, ny, s.K, P.splits, partials, stream));
+      oe.partials = partials;
+      oe.splits = P.splits;
+    }
   } else if (pb.route == ADAHOP_ROUTE_OE_INNER) {
     oe.mode = ADAHOP_ROUTE_OE_INNER;
     oe.k = pb.k;
@@ -568,7 +595,12 @@ size_t gemm_mx_partials_bytes(int64_t m, int64_t n, int64_t K, const adahop_oe* 
   if (oe->k < 1) return 0;
   const int64_t nx = oe->route == ADAHOP_ROUTE_OE_LEFT ? oe->k : m;
   const int64_t ny = oe->route == ADAHOP_ROUTE_OE_LEFT ? n : oe->k;
-  return align_up(sizeof(float) * (size_t)(oe_splits(nx, ny, K) + 1) * (size_t)nx * (size_t)ny, kAlign);
+  size_t bytes = align_up(sizeof(float) * (size_t)(oe_splits(nx, ny, K) + 1) * (size_t)nx * (size_t)ny, kAlign);
+  const Bf16View X{oe->a.ptr, oe->a.ld, oe->a.inner_contiguous};
+  const Bf16View Y{oe->b.ptr, oe->b.ld, oe->b.inner_contiguous};
+  const int fp = oe_fused_parts(m, n, K, oe->route, oe->k, X, Y, false);
+  if (fp > 0) bytes = std::max(bytes, oe_fused_bytes(m, n, oe->route, oe->k, fp));
+  return bytes;
 }
 
 }  // namespace
@@ -820,9 +852,18 @@ adahop_status adahop_gemm_mx(const adahop_mx_operand* A, const adahop_mx_operand
   }
   const size_t partial_bytes = gemm_mx_partials_bytes(m, n, K, oe);
   void* scratch = need > partial_bytes ? static_cast<char*>(ws) + partial_bytes : nullptr;
+  if (e.mode == ADAHOP_ROUTE_OE_LEFT || e.mode == ADAHOP_ROUTE_OE_RIGHT) {
+    e.fused_parts = gemm_mx_ring_used(A->codes, A->scales, B->codes, B->scales, m, n, K, ADAHOP_LAYOUT_ROWS)
+                        ? oe_fused_parts(m, n, K, e.mode, e.k, e.a, e.b, true)
+                        : 0;
+    if (e.fused_parts > 0) {
+      e.fused_ws = static_cast<float*>(ws);
+      e.partials = nullptr;
+    }
+  }
   ADAHOP_TRY(gemm_mx_stage_scales(A->codes, A->scales, B->codes, B->scales, m, n, K, scratch,
                                   need - partial_bytes, st));
-  if (e.mode == ADAHOP_ROUTE_OE_LEFT || e.mode == ADAHOP_ROUTE_OE_RIGHT)
+  if ((e.mode == ADAHOP_ROUTE_OE_LEFT || e.mode == ADAHOP_ROUTE_OE_RIGHT) && e.fused_parts == 0)
     ADAHOP_TRY(oe_product_launch(e.a, e.b, oe_nx, oe_ny, K, e.splits, static_cast<float*>(ws), st));
   return gemm_mx_launch(A->codes, A->scales, B->codes, B->scales, m, n, K, ADAHOP_LAYOUT_ROWS, e,
                         C, ldc,

@@ -87,8 +87,29 @@ struct OeEpilogue {
   const int32_t* idx;       // OE_LEFT / OE_RIGHT
   const float* partials;    // OE_LEFT: [splits][k][n]; OE_RIGHT: [splits][m][k]; then P
   int splits;
-  Bf16View a, b;            // OE_INNER factors: a [m][k], b [n][k]
+  Bf16View a, b;            // OE_INNER factors: a [m][k], b [n][k]; OE_LEFT / OE_RIGHT:
+                            // the outlier product's factors, as for oe_product_launch
+  // OE_LEFT / OE_RIGHT computed inside the GEMM launch (fused_parts > 0, from
+  // oe_fused_parts): `fused_ws` holds oe_fused_bytes(...) bytes, 16-byte
+  // aligned, for the partial sums and the extracted lines' residual.
+  int fused_parts;
+  float* fused_ws;
 };
+// K-parts of the outer outlier product (OE_LEFT / OE_RIGHT, X = a, Y = b as
+// in oe_product_launch) when it runs as work items of the main GEMM kernel,
+// or 0 when it runs as oe_product_kernel before the GEMM: k <= 64, the main
+// kernel applies to (m, n, K), the wide factor (a for OE_RIGHT, b for
+// OE_LEFT) is stored across K with a row of a multiple of 8 elements under
+// 2 GiB, the lines (the other factor) run along K in rows of a multiple of 8
+// elements; with check_ptrs, both 16-byte aligned.
+int oe_fused_parts(int64_t m, int64_t n, int64_t K, int mode, int32_t k, Bf16View a, Bf16View b,
+                   bool check_ptrs);
+// Whether gemm_mx_launch runs the main (ring) kernel for these operands.
+bool gemm_mx_ring_used(const uint8_t* a_codes, const uint8_t* a_scales, const uint8_t* b_codes,
+                       const uint8_t* b_scales, int64_t m, int64_t n, int64_t K, int layout);
+// Workspace of the fused outlier product: parts x wide x k partial sums plus
+// wide x k residuals, fp32.
+size_t oe_fused_bytes(int64_t m, int64_t n, int mode, int32_t k, int parts);
 // Workspace the GEMM needs for (m, n, K) in `layout`, when the main kernel
 // applies (K % 512 == 0), else 0: for ROWS, stage-major copies of both scale
 // arrays ([K/128][rows] words; gemm_mx_stage_scales writes them), then, for

@@ -118,6 +118,20 @@ struct GemmArgs {
   const uint16_t* ib_ptr; int64_t ib_ld; int ib_inner;   // OE_INNER b: (j, p)
   // bf16 operands stored across K ([K][ld], ring kernel): bytes per stored row
   int64_t a_ldb, b_ldb;
+  // Outer outlier product run inside the main kernel (OE_LEFT / OE_RIGHT with
+  // oe_items > 0): item e computes, for the 256-wide block e % oe_tiles_w of
+  // the operand stored across K ("wide": A for OE_RIGHT, B for OE_LEFT) and
+  // K-part e / oe_tiles_w (oe_kst bf16 stages of 32), the partial sums
+  // P_s(w, p) = sum_t wide(w, t) line(p, t) of its <= 64 lines, written to
+  // oe_part ([s][w][p] for OE_RIGHT, [s][p][w] for OE_LEFT, fp32). The tile
+  // epilogues then leave C's extracted lines to oe_scatter_kernel and keep
+  // their fp32 residual there in oe_res ([w][p] / [p][w]).
+  int oe_items, oe_tiles_w, oe_kst;
+  const uint8_t* oe_wide;
+  int64_t oe_wide_ldb, oe_wide_n;
+  const uint8_t* oe_lines;       // [k][K] bf16
+  float* oe_part;
+  float* oe_res;
 };
 
 __device__ __forceinline__ int lower_bound_i32(const int32_t* idx, int n, int64_t v) {
@@ -249,11 +263,20 @@ __device__ __forceinline__ void gemm_store(const GemmArgs& g, v16f (&acc)[TFM][T
     const int64_t row = m0 + lr;
     const int prow = (any_oe && oe_rows) ? s_pos[lr] : -1;
     // Outlier product values for this row: OE_LEFT its extracted row's
-    // values from column col0 on, OE_RIGHT its row of k values.
+    // values from column col0 on, OE_RIGHT its row of k values. With the
+    // product computed inside the kernel (oe_res), the residual of the
+    // extracted lines goes to oe_res instead, for oe_scatter_kernel.
     const float* oe_row = nullptr;
+    float* res_row = nullptr;
     if (any_oe && row < g.m) {
-      if (oe_rows) { if (prow >= 0) oe_row = g.oe_p + (int64_t)prow * g.n + col0; }
-      else oe_row = g.oe_p + row * g.oe_k;
+      if (g.oe_res) {
+        if (oe_rows) { if (prow >= 0) res_row = g.oe_res + (int64_t)prow * g.n + col0; }
+        else res_row = g.oe_res + row * g.oe_k;
+      } else if (oe_rows) {
+        if (prow >= 0) oe_row = g.oe_p + (int64_t)prow * g.n + col0;
+      } else {
+        oe_row = g.oe_p + row * g.oe_k;
+      }
     }
     const int64_t off = row * g.ldc + col0;
     float* cf = static_cast<float*>(g.C) + off;
@@ -275,6 +298,18 @@ __device__ __forceinline__ void gemm_store(const GemmArgs& g, v16f (&acc)[TFM][T
             for (int e = 0; e < 4; ++e) {
               const int p = lc0 + dc + e < BN ? s_pos[lc0 + dc + e] : -1;
               if (p >= 0) v[G][e] += oe_row[p];
+            }
+          }
+        } else if (res_row != nullptr) {
+          if (oe_rows) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              if (col0 + dc + e < g.n) res_row[dc + e] = v[G][e];
+          } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int p = lc0 + dc + e < BN ? s_pos[lc0 + dc + e] : -1;
+              if (p >= 0) res_row[p] = v[G][e];
             }
           }
         }
@@ -874,14 +909,194 @@ __global__ void __launch_bounds__(kRing8Threads, 1) gemm_mx_ring8_kernel(GemmArg
     keep(y);
   };
 
-  int item = item_of(0);
-  if (item < 0) return;
-  issue_first4(setup(item));
-  for (int r = 0;; ++r) {
-    // Only the item index is carried over: the item's descriptors are built
+  // The outer outlier product's items (FP4 kernel with oe_items > 0): each
+  // workgroup b < oe_items runs item b once, before its tile round
+  // (b / oe_tiles_w) % 4 (or after its last one): at any time about a
+  // quarter of the items stream the bf16 operand from memory while the other
+  // workgroups keep the matrix cores busy, and the items that run together
+  // cover whole rows of it (all wide blocks of one K-part). Work w of the
+  // sequence: >= 0 a tile item, kOeWork the outlier item, kNoWork none.
+  constexpr int kNoWork = -1, kOeWork = -2;
+  const bool has_oe = !Bf16 && bid < g.oe_items;
+  const int my_rounds = items > bid ? (items - bid + G - 1) / G : 0;
+  const int oe_slot = has_oe ? (bid / g.oe_tiles_w) & 3 : 0;
+  const int oe_at = has_oe ? (oe_slot < my_rounds ? oe_slot : my_rounds) : -1;
+  auto work_at = [&](int q) {
+    if (has_oe) {
+      if (q == oe_at) return kOeWork;
+      if (q > oe_at) --q;
+    }
+    return item_of(q);
+  };
+  // Outlier item e = bid: 256-wide block e % oe_tiles_w of the operand
+  // stored across K (A-side of the slot, read as in TA mode), K-part
+  // e / oe_tiles_w; its lines ([k][K] bf16 rows) in the B-side rows 0 .. 63.
+  // The outlier item's per-lane offsets are computed inside its branch from
+  // a lane id the compiler cannot see through: hoisted out of the work loop
+  // they would stay live across the tiles' K loop, which has no registers to
+  // spare.
+  auto opaque_lane = [&]() {
+    int l = lane;
+    asm volatile("" : "+v"(l));
+    return l;
+  };
+  auto setup_oe = [&]() {
+    RingItem it;
+    const int ol = opaque_lane();
+    const int orow0 = 32 * wave + (ol >> 2);
+    const int ochunk = (ol & 3) ^ ring_swz(orow0);
+    auto otr_voff = [&](int j, int64_t ldb, int64_t c0) {
+      const int k = 2 * (2 * wave + j) + (ol >> 5);
+      const int h = (k & 3) | (((k >> 3) & 1) << 2);
+      const int c = (ol & 31) ^ (4 * h);
+      return 8 * (int64_t)c < ldb / 2 - c0 ? k * (int)ldb + 16 * c : kPastEnd;
+    };
+    const int wt = __builtin_amdgcn_readfirstlane(bid % g.oe_tiles_w);
+    const int sp = __builtin_amdgcn_readfirstlane(bid / g.oe_tiles_w);
+    it.tm = wt; it.tn = 0; it.part = sp; it.split_tile = 0;
+    it.kt0 = __builtin_amdgcn_readfirstlane(sp * g.oe_kst);
+    it.kt1 = __builtin_amdgcn_readfirstlane(it.kt0 + g.oe_kst);
+    it.m0 = (int64_t)wt * BM;
+    it.n0 = 0;
+    it.ra = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(g.oe_wide + it.m0 * 2), 0,
+                                              (int)(g.K * g.oe_wide_ldb - it.m0 * 2), kBufferFlags);
+    it.rb = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(g.oe_lines), 0,
+                                              (int)(g.oe_k * g.K * 2), kBufferFlags);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int r = orow0 + 16 * j;
+      it.voffa[j] = otr_voff(j, g.oe_wide_ldb, it.m0);
+      it.voffb[j] = r < g.oe_k ? r * (int)(2 * g.K) + ochunk * 16 : kPastEnd;
+    }
+    it.soff = kPastEnd;
+    return it;
+  };
+  // Waves 0 and 1 also copy the stage's 64 line rows (4 loads per stage),
+  // the others only their share of the wide operand (2 loads).
+  auto issue_oe = [&](const RingItem& it, auto S, int kt) {
+    constexpr int slot = decltype(S)::value;
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          it.ra, (lds_void*)&ring_slot<slot>().a[1024 * (2 * wave + j)], 16, it.voffa[j],
+          kt * 32 * (int)g.oe_wide_ldb, 0, 0);
+    if (wave < 2) {
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            it.rb, (lds_void*)&ring_slot<slot>().b[1024 * (2 * wave + j)], 16, it.voffb[j], kt * RBK, 0, 0);
+    }
+  };
+  // Waits until only this wave's loads of the `later` stages after the one
+  // wanted are in flight (4 or 2 loads per stage, as above).
+  auto oe_wait = [&](auto Later) {
+    constexpr int later = decltype(Later)::value;
+    if (wave < 2) __builtin_amdgcn_s_waitcnt(waitcnt_imm(4 * later, 0));
+    else __builtin_amdgcn_s_waitcnt(waitcnt_imm(2 * later, 0));
+  };
+  auto issue_first4_oe = [&](const RingItem& it) {
+    issue_oe(it, std::integral_constant<int, 0>{}, it.kt0);
+    issue_oe(it, std::integral_constant<int, 1>{}, it.kt0 + 1);
+    issue_oe(it, std::integral_constant<int, 2>{}, it.kt0 + 2);
+    issue_oe(it, std::integral_constant<int, 3>{}, it.kt0 + 3);
+  };
+  auto issue_work = [&](int w) {
+    if (w == kOeWork) issue_first4_oe(setup_oe());
+    else if (w >= 0) issue_first4(setup(w));
+  };
+  // One bf16 stage (32 K-elements, two 16-deep steps) of the outlier item:
+  // wave w's 32 wide rows (block w of the slot, transposing reads) against
+  // the 64 lines; then, once every wave has its loads of the next stage and
+  // no wave reads this slot any more, the slot is refilled 4 stages ahead.
+  // Fragment offsets of the outlier item (block `wave` of the wide operand,
+  // read transposed; rows 0 .. 63 of the lines), from the opaque lane id.
+  struct OeOff {
+    int w, n;
+    int swz;
+  };
+  auto oe_offsets = [&]() {
+    const int ol = opaque_lane();
+    const int oL = ol & 15, oG = ol >> 4;
+    const int oth = (oL >> 2) + 4 * (oG >> 1);
+    const int obase = (8 * (oG >> 1) + (oL >> 2)) * 512 + 16 * (2 * (oG & 1) + ((oL & 3) >> 1)) +
+                      8 * (oL & 1);
+    const int orow = ol & 31;
+    return OeOff{obase + 64 * (wave ^ oth), orow * RBK, ring_swz(orow) | ((ol >> 5) << 8)};
+  };
+  auto oe_stage = [&](const RingItem& it, auto S, v16f (&oacc)[2], const OeOff& o, int kt) {
+    constexpr int slot = decltype(S)::value;
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const v4i fw = tr_frag(&ring_slot<slot>().a[o.w + 8192 * ks]);
+      const int sw = ((2 * ks + (o.swz >> 8)) ^ (o.swz & 3)) << 4;
+      const v4i fn0 = *reinterpret_cast<const v4i*>(&ring_slot<slot>().b[o.n + sw]);
+      const v4i fn1 = *reinterpret_cast<const v4i*>(&ring_slot<slot>().b[o.n + sw + 2048]);
+      oacc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf, fn0),
+                                                        __builtin_bit_cast(v8bf, fw), oacc[0], 0, 0, 0);
+      oacc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf, fn1),
+                                                        __builtin_bit_cast(v8bf, fw), oacc[1], 0, 0, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    oe_wait(std::integral_constant<int, 2>{});
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    issue_oe(it, std::integral_constant<int, slot>{}, kt + 4 < it.kt1 ? kt + 4 : it.kt1 - 1);
+  };
+
+  int work = work_at(0);
+  if (work == kNoWork) return;
+  issue_work(work);
+  for (int q = 0;; ++q) {
+    // Only the work index is carried over: the item's descriptors are built
     // again here from scalars (carried through the loop they would end up in
     // vector registers).
-    item = __builtin_amdgcn_readfirstlane(item);
+    work = __builtin_amdgcn_readfirstlane(work);
+    if constexpr (!Bf16) {
+      if (work == kOeWork) {
+        const RingItem cur = setup_oe();
+        v16f oacc[2];
+#pragma unroll
+        for (int v = 0; v < 16; ++v) { oacc[0][v] = 0.0f; oacc[1][v] = 0.0f; }
+        oe_wait(std::integral_constant<int, 3>{});
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+        const OeOff o = oe_offsets();
+        for (int kt = cur.kt0; kt < cur.kt1; kt += kRingSlots) {
+          oe_stage(cur, std::integral_constant<int, 0>{}, oacc, o, kt);
+          oe_stage(cur, std::integral_constant<int, 1>{}, oacc, o, kt + 1);
+          oe_stage(cur, std::integral_constant<int, 2>{}, oacc, o, kt + 2);
+          oe_stage(cur, std::integral_constant<int, 3>{}, oacc, o, kt + 3);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
+        __syncthreads();
+        const int next = work_at(q + 1);
+        issue_work(next);
+        // Partial sums of K-part cur.part: lane l holds wide row w (column
+        // l % 32 of the MFMA result), register v line 32 j + acc_row(v, l).
+        const int ol = opaque_lane();
+        const int64_t w = cur.m0 + 32 * wave + (ol & 31);
+        if (w < g.oe_wide_n) {
+          const bool right = g.oe_mode == ADAHOP_ROUTE_OE_RIGHT;
+#pragma unroll
+          for (int j = 0; j < 2; ++j) {
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+              const int p = 32 * j + acc_row(v, ol);
+              if (p >= g.oe_k) continue;
+              const int64_t at = right ? ((int64_t)cur.part * g.oe_wide_n + w) * g.oe_k + p
+                                       : ((int64_t)cur.part * g.oe_k + p) * g.oe_wide_n + w;
+              g.oe_part[at] = oacc[j][v];
+            }
+          }
+        }
+        if (next == kNoWork) break;
+        __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
+        work = next;
+        continue;
+      }
+    }
+    const int item = work;
     const RingItem cur = setup(item);
     static_for<R8_FM>([&](auto I) {
       static_for<R8_FN>([&](auto J) {
@@ -906,8 +1121,8 @@ __global__ void __launch_bounds__(kRing8Threads, 1) gemm_mx_ring8_kernel(GemmArg
     __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
     __syncthreads();
-    const int next = item_of(r + 1);
-    if (next >= 0) issue_first4(setup(next));
+    const int next = work_at(q + 1);
+    issue_work(next);
 
     // The inner-extraction term goes into a whole tile or part 0 of a split
     // one. A part of a split tile then goes out through the same store code,
@@ -922,11 +1137,11 @@ __global__ void __launch_bounds__(kRing8Threads, 1) gemm_mx_ring8_kernel(GemmArg
       em0 = 0; en0 = 0;
     }
     gemm_store<R8_FM, R8_FN, R8_WM, R8_WN, 4, kRing8Threads>(ge, acc, em0, en0, g_ring_pos);
-    if (next < 0) break;
+    if (next == kNoWork) break;
     // The stores and the epilogue's loads are not ordered with the next
     // item's ring loads in the counter: wait for all of them.
     __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
-    item = next;
+    work = next;
   }
 }
 
@@ -973,7 +1188,24 @@ __global__ void __launch_bounds__(kFixThreads) gemm_split_fixup_kernel(GemmArgs 
       a.x += b.x; a.y += b.y; a.z += b.z; a.w += b.w;
     }
     float v[4] = {a.x, a.y, a.z, a.w};
-    if (any_oe) {
+    if (any_oe && g.oe_res) {
+      // The outlier product was computed in the main kernel: keep the
+      // residual of the extracted lines for oe_scatter_kernel.
+      if (oe_rows) {
+        const int prow = s_pos[lr];
+        if (prow >= 0) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (col + e < g.n) g.oe_res[(int64_t)prow * g.n + col + e] = v[e];
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int p = s_pos[lc + e];
+          if (p >= 0) g.oe_res[row * g.oe_k + p] = v[e];
+        }
+      }
+    } else if (any_oe) {
       if (oe_rows) {
         const int prow = s_pos[lr];
         if (prow >= 0) {
@@ -1009,6 +1241,28 @@ __global__ void __launch_bounds__(kFixThreads) gemm_split_fixup_kernel(GemmArgs 
       }
     }
   }
+}
+
+// The outer outlier product computed inside the main kernel, scattered into
+// C: for every wide index w and line p, C at (w, idx[p]) (OE_RIGHT) or
+// (idx[p], w) (OE_LEFT) becomes the extracted line's fp32 residual, kept by
+// the tile epilogue or the fixup, plus the partial sums added in part order,
+// rounded once. Thread t takes (w, p) in the partials' own order, so the
+// reads of every part are coalesced.
+__global__ void __launch_bounds__(256) oe_scatter_kernel(GemmArgs g, int parts) {
+  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t count = g.oe_wide_n * g.oe_k;
+  if (t >= count) return;
+  float sum = g.oe_part[t];
+  for (int s = 1; s < parts; ++s) sum += g.oe_part[(int64_t)s * count + t];
+  const float v = g.oe_res[t] + sum;
+  const bool right = g.oe_mode == ADAHOP_ROUTE_OE_RIGHT;
+  const int64_t w = right ? t / g.oe_k : t % g.oe_wide_n;
+  const int p = (int)(right ? t % g.oe_k : t / g.oe_wide_n);
+  const int64_t row = right ? w : g.oe_idx[p];
+  const int64_t col = right ? g.oe_idx[p] : w;
+  if (g.out_f32) static_cast<float*>(g.C)[row * g.ldc + col] = v;
+  else static_cast<uint16_t*>(g.C)[row * g.ldc + col] = f32_to_bf16_rne(v);
 }
 
 // ---------------------------------------------------------------------------
@@ -1400,6 +1654,41 @@ uint32_t* staged_b(void* scratch, int64_t m, int64_t K) {
 }
 }  // namespace
 
+bool gemm_mx_ring_used(const uint8_t* a_codes, const uint8_t* a_scales, const uint8_t* b_codes,
+                       const uint8_t* b_scales, int64_t m, int64_t n, int64_t K, int layout) {
+  if (layout == ADAHOP_LAYOUT_KCHUNK) return gemm_mx_kchunk_ok(m, n, K);
+  return ring_applies(a_codes, a_scales, b_codes, b_scales, m, n, K);
+}
+
+int oe_fused_parts(int64_t m, int64_t n, int64_t K, int mode, int32_t k, Bf16View a, Bf16View b,
+                   bool check_ptrs) {
+  if ((mode != ADAHOP_ROUTE_OE_LEFT && mode != ADAHOP_ROUTE_OE_RIGHT) || k < 1 || k > 64) return 0;
+  if (!ring_shape_ok(m, n, K)) return 0;
+  const bool right = mode == ADAHOP_ROUTE_OE_RIGHT;
+  const Bf16View wide = right ? a : b, lines = right ? b : a;
+  const int64_t wide_n = right ? m : n;
+  if (wide.inner_contiguous || wide.ld % 8 != 0 || wide.ld < wide_n || K * wide.ld * 2 >= kPastEnd)
+    return 0;
+  if (!lines.inner_contiguous || lines.ld % 8 != 0 || lines.ld < K || (int64_t)k * lines.ld * 2 >= kPastEnd)
+    return 0;
+  if (lines.ld != K) return 0;   // the kernel's line rows are K elements apart
+  if (check_ptrs && ((reinterpret_cast<uintptr_t>(wide.ptr) | reinterpret_cast<uintptr_t>(lines.ptr)) & 15u))
+    return 0;
+  // About one item per CU: parts = CUs / wide blocks, each a multiple of 4
+  // bf16 stages of 32 and at least 8 of them, at most 64 parts.
+  const int64_t tiles_w = (wide_n + BM - 1) / BM, nk = K / 32;
+  int64_t parts = device_cus() / tiles_w;
+  if (parts > 64) parts = 64;
+  while (parts > 1 && (nk % (4 * parts) != 0 || nk / parts < 8)) --parts;
+  if (parts < 1 || tiles_w * parts > device_cus()) return 0;
+  return (int)parts;
+}
+
+size_t oe_fused_bytes(int64_t m, int64_t n, int mode, int32_t k, int parts) {
+  const int64_t wide_n = mode == ADAHOP_ROUTE_OE_RIGHT ? m : n;
+  return align_up(sizeof(float) * (size_t)(parts + 1) * (size_t)wide_n * (size_t)k, kAlign);
+}
+
 adahop_status gemm_mx_stage_scales(const uint8_t* a_codes, const uint8_t* a_scales,
                                    const uint8_t* b_codes, const uint8_t* b_scales, int64_t m,
                                    int64_t n, int64_t K, void* scratch, size_t scratch_bytes,
@@ -1433,6 +1722,25 @@ adahop_status gemm_mx_launch(const uint8_t* a_codes, const uint8_t* a_scales,
   g.vec_ok = (ldc % (out_f32 ? 4 : 8) == 0) && ((reinterpret_cast<uintptr_t>(C) & 15u) == 0);
   g.ia_ptr = oe.a.ptr; g.ia_ld = oe.a.ld; g.ia_inner = oe.a.inner_contiguous;
   g.ib_ptr = oe.b.ptr; g.ib_ld = oe.b.ld; g.ib_inner = oe.b.inner_contiguous;
+  const int fused = oe.fused_parts;
+  if (fused > 0 && !gemm_mx_ring_used(a_codes, a_scales, b_codes, b_scales, m, n, K, layout))
+    return fail(ADAHOP_ERR_UNSUPPORTED, "gemm_mx: the outlier items need the main kernel");
+  if (fused > 0) {
+    // Outer outlier product as work items of the main kernel, scattered by
+    // oe_scatter_kernel after it (and after the fixup of split tiles).
+    const bool right = oe.mode == ADAHOP_ROUTE_OE_RIGHT;
+    const Bf16View wide = right ? oe.a : oe.b, lines = right ? oe.b : oe.a;
+    g.oe_wide_n = right ? m : n;
+    g.oe_tiles_w = (int)((g.oe_wide_n + BM - 1) / BM);
+    g.oe_items = g.oe_tiles_w * fused;
+    g.oe_kst = (int)(K / 32 / fused);
+    g.oe_wide = reinterpret_cast<const uint8_t*>(wide.ptr);
+    g.oe_wide_ldb = 2 * wide.ld;
+    g.oe_lines = reinterpret_cast<const uint8_t*>(lines.ptr);
+    g.oe_part = oe.fused_ws;
+    g.oe_res = oe.fused_ws + (size_t)fused * (size_t)g.oe_wide_n * (size_t)oe.k;
+    g.oe_p = nullptr;
+  }
   const dim3 grid((unsigned)(tiles_m * tiles_n)), block(kGemmThreads);
   const uintptr_t sc_bits = reinterpret_cast<uintptr_t>(a_scales) | reinterpret_cast<uintptr_t>(b_scales);
   const bool kchunk = layout == ADAHOP_LAYOUT_KCHUNK;
@@ -1456,9 +1764,11 @@ adahop_status gemm_mx_launch(const uint8_t* a_codes, const uint8_t* a_scales,
     g.split_ws = ts.split ? reinterpret_cast<float*>(static_cast<char*>(scratch) +
                                                      (kchunk ? 0 : staging_bytes(m, n, K)))
                           : nullptr;
-    // Persistent: at most one workgroup per CU.
+    // Persistent: at most one workgroup per CU, and one per outlier item.
     const int64_t items = ts.full + ts.split * ts.parts, cus = device_cus();
-    const dim3 rgrid((unsigned)(items < cus ? items : cus));
+    int64_t wgs = items < cus ? items : cus;
+    if (g.oe_items > wgs) wgs = g.oe_items;
+    const dim3 rgrid((unsigned)wgs);
     if (kchunk)
       gemm_mx_ring8_kernel<true, false><<<rgrid, dim3(kRing8Threads), 0, stream>>>(g);
     else
@@ -1468,6 +1778,12 @@ adahop_status gemm_mx_launch(const uint8_t* a_codes, const uint8_t* a_scales,
       if (ls != ADAHOP_OK) return ls;
       gemm_split_fixup_kernel<<<dim3((unsigned)(ts.split * (BM / kFixRows))), dim3(kFixThreads), 0,
                                 stream>>>(g);
+    }
+    if (fused > 0) {
+      const adahop_status ls = check_launch("gemm_mx");
+      if (ls != ADAHOP_OK) return ls;
+      const int64_t count = g.oe_wide_n * oe.k;
+      oe_scatter_kernel<<<dim3((unsigned)((count + 255) / 256)), dim3(256), 0, stream>>>(g, fused);
     }
   } else if (K % 256 == 0 && (sc_bits & 7u) == 0)
     gemm_mx_kernel<true><<<grid, block, 0, stream>>>(g);

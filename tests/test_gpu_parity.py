@@ -238,6 +238,48 @@ def test_gemm_mx_outlier_term(route, K):
     assert np.array_equal(host(c16), f32_to_bf16_rne(host(c32)))
 
 
+@pytest.mark.parametrize("K", [512, 4096, 8192])
+@pytest.mark.parametrize("route", ["OE_LEFT", "OE_RIGHT"])
+def test_gemm_mx_outlier_items_in_kernel(route, K):
+    # The outlier product with its wide factor stored across K and its lines
+    # along K runs as work items of the GEMM kernel (K % 512 == 0). The packed
+    # operands are random, so the extracted lines' residual is not zero: the
+    # result must still be residual + outlier product, rounded once. K = 4096
+    # and 8192 split the last round's tiles (residual kept by the fixup).
+    m, n, k = 320, 520, 12
+    rng = np.random.default_rng(9)
+    a, b, ac, as_, bc, bs = packed_operands(rng, m, n, K)
+    ref, absC = oracle.gemm_mx(ac, as_, bc, bs)
+    walk, rmax = oracle.walk_mx(ac, as_, bc, bs, FP4_STEP)
+    if route == "OE_LEFT":
+        idx = np.sort(rng.choice(m, k, replace=False)).astype(np.int32)
+        la = rand_bf16(rng, (k, K))                      # lines (p, t), along K
+        bT = np.ascontiguousarray(b.T)                   # B (j, t) stored across K: [K][n]
+        oe_ref, oe_abs = oracle.gemm_bf16(la, 0, bT, 0, K, np.arange(k), np.arange(n))
+        w, r = oracle.walk_bf16(la, 0, bT, 0, K, BF16_STEP, np.arange(k), np.arange(n))
+        ref[idx, :] += oe_ref; absC[idx, :] += oe_abs; walk[idx, :] += w; rmax[idx, :] += r
+        oe = {"route": route, "k": k, "idx": torch.from_numpy(idx).to(DEV),
+              "a": (dev_bf16(la), True), "b": (dev_bf16(bT), False)}
+    else:
+        idx = np.sort(rng.choice(n, k, replace=False)).astype(np.int32)
+        aT = np.ascontiguousarray(a.T)                   # A (i, t) stored across K: [K][m]
+        lb = rand_bf16(rng, (k, K))                      # lines (p, t), along K
+        oe_ref, oe_abs = oracle.gemm_bf16(aT, 1, lb, 1, K, np.arange(m), np.arange(k))
+        w, r = oracle.walk_bf16(aT, 1, lb, 1, K, BF16_STEP, np.arange(m), np.arange(k))
+        ref[:, idx] += oe_ref; absC[:, idx] += oe_abs; walk[:, idx] += w; rmax[:, idx] += r
+        oe = {"route": route, "k": k, "idx": torch.from_numpy(idx).to(DEV),
+              "a": (dev_bf16(aT), False), "b": (dev_bf16(lb), True)}
+    d = [torch.from_numpy(x).to(DEV) for x in (ac, as_, bc, bs)]
+    say("gemm_mx outlier items", route, K)
+    c32 = A.adahop_gemm_mx(*d, oe=oe, out_dtype=torch.float32)
+    c16 = A.adahop_gemm_mx(*d, oe=oe, out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    g = gamma(absC, walk, rmax)
+    check_f32(host(c32), ref, g, route)
+    say("  " + describe(check_bf16(host(c16), ref, g, route)))
+    assert np.array_equal(host(c16), f32_to_bf16_rne(host(c32)))
+
+
 # --------------------------------------------------------------------------
 # Whole products: every op x route family, bit-exact intermediates
 # --------------------------------------------------------------------------
