@@ -573,9 +573,12 @@ def main():
                         "is the bf16 MFMA kernel plus, when its last round is split along K, the "
                         "fixup kernel") if bf16 else
                        ("the operand FOID does not scan is quantized on a second stream, beside "
-                        "FOID, the other quantization and the outlier product: its slot is empty "
-                        "and the other slots overlap it; gemm is the MFMA kernel plus, when its "
-                        "last round is split along K, the fixup kernel")
+                        "FOID and the other quantization: its slot is empty and the other slots "
+                        "overlap it; when the wide outlier factor is stored across K and k <= 64 "
+                        "the outlier product runs as work items of the GEMM kernel (its own slot "
+                        "empty), else before it; gemm is the MFMA kernel plus the fixup kernel of "
+                        "a split last round and the kernel that adds the outlier product to the "
+                        "extracted lines")
                        if route in ("OE_LEFT", "OE_RIGHT") else
                        ("gemm is the MFMA kernel plus, when its last round is split along K, "
                         "the fixup kernel"),
@@ -584,9 +587,14 @@ def main():
         "roofline": {"bound": "mfma",
                      "kernel": ("gemm_mx_ring8_kernel<bf16> + gemm_split_fixup_kernel (bf16 MFMA "
                                 "GEMM; the fixup adds the K-parts of a split last round)") if bf16 else
-                               ("gemm_mx_ring8_kernel + gemm_split_fixup_kernel (FP4 MFMA GEMM, "
-                                "fused scatter-add epilogue; the fixup adds the K-parts of a "
-                                "split last round)"),
+                               ("gemm_mx_ring8_kernel + gemm_split_fixup_kernel + "
+                                "oe_scatter_kernel (FP4 MFMA GEMM whose workgroups also compute "
+                                "the rank-k bf16 outlier product; the fixup adds the K-parts of a "
+                                "split last round, oe_scatter adds the outlier product to the "
+                                "extracted lines and rounds once; achieved counts the FP4 "
+                                "product's 2mnK only)") if route in ("OE_LEFT", "OE_RIGHT") else
+                               ("gemm_mx_ring8_kernel + gemm_split_fixup_kernel (FP4 MFMA GEMM; "
+                                "the fixup adds the K-parts of a split last round)"),
                      "achieved": round(achieved, 1), "peak": peak,
                      "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
                      "traffic": None},
