@@ -395,15 +395,18 @@ ADAHOP_API adahop_status adahop_gemm_wgrad_ctx(const uint16_t* GY, const void* c
 
 /* As adahop_gemm, and if stage_events is not NULL it must hold
  * ADAHOP_STAGE_EVENTS created hipEvent_t handles: events[0] is recorded on
- * `stream` before the first launch and events[1..5] after the FOID, lhs
+ * `stream` before the first launch and events[1..6] after the FOID, lhs
  * quantization, rhs quantization (which ends with reordering both scale
- * arrays for the GEMM), outlier product and GEMM stages (a stage
- * that does not run records its event right after the previous one). With
+ * arrays for the GEMM), outlier product, GEMM main kernel and GEMM tail
+ * stages (a stage that does not run records its event right after the
+ * previous one). The tail is what finishes the main kernel's output: the
+ * fixup of a split last round of tiles and, when the outlier product ran
+ * inside the main kernel, its scatter into the extracted lines. With
  * OE_LEFT and OE_RIGHT the operand FOID does not scan is quantized on a
  * second stream: its stage is empty here, the ROWS-layout scale reordering
  * falls in the GEMM stage, and the other stages overlap with it. With route
  * BF16 the lhs and rhs stages are the operands' K-major copies, if any. */
-#define ADAHOP_STAGE_EVENTS 6
+#define ADAHOP_STAGE_EVENTS 7
 ADAHOP_API adahop_status adahop_gemm_timed(adahop_op op, const uint16_t* lhs,
                                            const uint16_t* rhs, int64_t T, int64_t Din,
                                            int64_t Dout, adahop_pattern pat_lhs,

@@ -23,8 +23,8 @@ ROUTE = {"AUTO": -1, "BF16": 0, "IHT": 1, "OE_LEFT": 2, "OE_RIGHT": 3, "OE_INNER
 ROUTE_NAME = {v: k for k, v in ROUTE.items()}
 AXIS = {"ROWS": 0, "COLS": 1}
 OUT = {torch.bfloat16: 0, torch.float32: 1}
-STAGE_EVENTS = 6
-STAGES = ("foid", "quant_lhs", "quant_rhs", "oe_product", "gemm")
+STAGE_EVENTS = 7
+STAGES = ("foid", "quant_lhs", "quant_rhs", "oe_product", "gemm", "gemm_tail")
 
 _p = ctypes.c_void_p
 _i64 = ctypes.c_int64

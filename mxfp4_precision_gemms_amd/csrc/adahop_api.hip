@@ -298,6 +298,7 @@ adahop_status make_plan(adahop_op op, int64_t T, int64_t Din, int64_t Dout,
 struct Events {
   void* const* ev;
   hipStream_t stream;
+  hipEvent_t at(int i) const { return ev ? static_cast<hipEvent_t>(ev[i]) : nullptr; }
   adahop_status record(int i) const {
     if (!ev) return ADAHOP_OK;
     hipError_t e = hipEventRecord(static_cast<hipEvent_t>(ev[i]), stream);
@@ -445,14 +446,16 @@ adahop_status run_gemm(adahop_op op, const uint16_t* lhs, const uint16_t* rhs, i
       ADAHOP_TRY(E.record(4));
       ADAHOP_TRY(bf16_ring_launch(a, P.a_across, P.a_ld, b, P.b_across, P.b_ld,
                                   s.m, s.n, s.K, out, s.n, out_f32,
-                                  P.gemm_bytes ? w + P.off_gemm : nullptr, P.gemm_bytes, stream));
-      return E.record(5);
+                                  P.gemm_bytes ? w + P.off_gemm : nullptr, P.gemm_bytes, stream,
+                                  E.at(5)));
+      return E.record(6);
     }
     for (int i = 2; i <= 4; ++i) ADAHOP_TRY(E.record(i));
     ADAHOP_TRY(bf16_gemm_launch(stored_view(lhs, s.lhs_cols, s.lhs_contract),
                                 stored_view(rhs, s.rhs_cols, s.rhs_contract), s.m, s.n, s.K, out,
                                 s.n, out_f32, stream));
-    return E.record(5);
+    ADAHOP_TRY(E.record(5));
+    return E.record(6);
   }
 
   char* w = static_cast<char*>(ws);
@@ -584,8 +587,8 @@ adahop_status run_gemm(adahop_op op, const uint16_t* lhs, const uint16_t* rhs, i
       ADAHOP_TRY(gemm_mx_stage_scales(ac, as, bc, bs, s.m, s.n, s.K, gemm_scratch, P.gemm_bytes, stream));
   }
   ADAHOP_TRY(gemm_mx_launch(ac, as, bc, bs, s.m, s.n, s.K, pb.layout, oe, out, s.n, out_f32,
-                            gemm_scratch, P.gemm_bytes, stream));
-  return E.record(5);
+                            gemm_scratch, P.gemm_bytes, stream, E.at(5)));
+  return E.record(6);
 }
 
 // Workspace of adahop_gemm_mx: the outlier product's partial sums (OE_LEFT,

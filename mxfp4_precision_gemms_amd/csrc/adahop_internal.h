@@ -73,7 +73,7 @@ size_t bf16_ring_scratch_bytes(int64_t m, int64_t n, int64_t K);
 adahop_status bf16_ring_launch(const uint16_t* a, int a_across, int64_t lda, const uint16_t* b,
                                int b_across, int64_t ldb, int64_t m, int64_t n, int64_t K, void* C,
                                int64_t ldc, int out_f32, void* scratch, size_t scratch_bytes,
-                               hipStream_t stream);
+                               hipStream_t stream, hipEvent_t main_done = nullptr);
 // dst [cols, rows] (leading dim rows) = transpose of src [rows, cols]
 // (leading dim ld).
 adahop_status bf16_transpose_launch(const uint16_t* src, int64_t rows, int64_t cols, int64_t ld,
@@ -133,6 +133,10 @@ adahop_status gemm_mx_launch(const uint8_t* a_codes, const uint8_t* a_scales,
                              const uint8_t* b_codes, const uint8_t* b_scales, int64_t m,
                              int64_t n, int64_t K, int layout, const OeEpilogue& oe, void* C,
                              int64_t ldc, int out_f32, void* scratch, size_t scratch_bytes,
-                             hipStream_t stream);
+                             hipStream_t stream, hipEvent_t main_done = nullptr);
+// Both GEMM launchers record `main_done` (if not null) on `stream` right
+// after the main kernel, before the kernels that finish its output (the
+// split fixup, the outlier scatter).
+adahop_status record_main_done(hipEvent_t main_done, hipStream_t stream, const char* what);
 
 }  // namespace adahop

@@ -1722,7 +1722,7 @@ adahop_status gemm_mx_launch(const uint8_t* a_codes, const uint8_t* a_scales,
                              const uint8_t* b_codes, const uint8_t* b_scales, int64_t m,
                              int64_t n, int64_t K, int layout, const OeEpilogue& oe, void* C,
                              int64_t ldc, int out_f32, void* scratch, size_t scratch_bytes,
-                             hipStream_t stream) {
+                             hipStream_t stream, hipEvent_t main_done) {
   const int64_t tiles_m = (m + BM - 1) / BM, tiles_n = (n + BN - 1) / BN;
   if (!gemm_mx_fits(m, n)) return fail(ADAHOP_ERR_UNSUPPORTED, "gemm: too large");
   GemmArgs g{};
@@ -1786,6 +1786,10 @@ adahop_status gemm_mx_launch(const uint8_t* a_codes, const uint8_t* a_scales,
       gemm_mx_ring8_kernel<true, false><<<rgrid, dim3(kRing8Threads), 0, stream>>>(g);
     else
       gemm_mx_ring8_kernel<false, false><<<rgrid, dim3(kRing8Threads), 0, stream>>>(g);
+    {
+      const adahop_status ls = record_main_done(main_done, stream, "gemm_mx");
+      if (ls != ADAHOP_OK) return ls;
+    }
     if (ts.split) {
       const adahop_status ls = check_launch("gemm_mx");
       if (ls != ADAHOP_OK) return ls;
@@ -1798,11 +1802,22 @@ adahop_status gemm_mx_launch(const uint8_t* a_codes, const uint8_t* a_scales,
       const int64_t count = g.oe_wide_n * oe.k;
       oe_scatter_kernel<<<dim3((unsigned)((count + 255) / 256)), dim3(256), 0, stream>>>(g, fused);
     }
-  } else if (K % 256 == 0 && (sc_bits & 7u) == 0)
-    gemm_mx_kernel<true><<<grid, block, 0, stream>>>(g);
-  else
-    gemm_mx_kernel<false><<<grid, block, 0, stream>>>(g);
+  } else {
+    if (K % 256 == 0 && (sc_bits & 7u) == 0)
+      gemm_mx_kernel<true><<<grid, block, 0, stream>>>(g);
+    else
+      gemm_mx_kernel<false><<<grid, block, 0, stream>>>(g);
+    return record_main_done(main_done, stream, "gemm_mx");
+  }
   return check_launch("gemm_mx");
+}
+
+adahop_status record_main_done(hipEvent_t main_done, hipStream_t stream, const char* what) {
+  const adahop_status ls = check_launch(what);
+  if (ls != ADAHOP_OK || main_done == nullptr) return ls;
+  const hipError_t e = hipEventRecord(main_done, stream);
+  return e == hipSuccess ? ADAHOP_OK
+                         : fail(ADAHOP_ERR_HIP, std::string("hipEventRecord: ") + hipGetErrorString(e));
 }
 
 // ---------------------------------------------------------------------------
@@ -1827,7 +1842,7 @@ bool bf16_ring_across_ok(int64_t K, int64_t ld) {
 adahop_status bf16_ring_launch(const uint16_t* a, int a_across, int64_t lda, const uint16_t* b,
                                int b_across, int64_t ldb, int64_t m, int64_t n, int64_t K, void* C,
                                int64_t ldc, int out_f32, void* scratch, size_t scratch_bytes,
-                               hipStream_t stream) {
+                               hipStream_t stream, hipEvent_t main_done) {
   if (!bf16_ring_ok(m, n, K) || ((reinterpret_cast<uintptr_t>(a) | reinterpret_cast<uintptr_t>(b)) & 15u))
     return fail(ADAHOP_ERR_UNSUPPORTED, "bf16 ring: K % 128 != 0, too long or misaligned operands");
   if ((a_across && (lda < m || !bf16_ring_across_ok(K, lda))) ||
@@ -1860,6 +1875,10 @@ adahop_status bf16_ring_launch(const uint16_t* a, int a_across, int64_t lda, con
     gemm_mx_ring8_kernel<false, true, false, true><<<rgrid, dim3(kRing8Threads), 0, stream>>>(g);
   else
     gemm_mx_ring8_kernel<false, true><<<rgrid, dim3(kRing8Threads), 0, stream>>>(g);
+  {
+    const adahop_status ls = record_main_done(main_done, stream, "bf16 ring");
+    if (ls != ADAHOP_OK) return ls;
+  }
   if (ts.split) {
     const adahop_status ls = check_launch("bf16 ring");
     if (ls != ADAHOP_OK) return ls;

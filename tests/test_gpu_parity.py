@@ -445,13 +445,21 @@ def test_deterministic_reruns():
     assert torch.equal(a.view(torch.int16), b.view(torch.int16))
 
 
-def test_stage_events_record():
-    op, T, Din, Dout = "WGRAD", 512, 384, 256
+@pytest.mark.parametrize("T", [512, 2048], ids=["separate-outlier-kernel", "outlier-items-in-gemm"])
+def test_stage_events_record(T):
+    # The timed call (an event between the GEMM's main kernel and its tail)
+    # gives the untimed call's output bit for bit, with ordered events; at
+    # T = 2048 the outlier product runs inside the main kernel and the tail
+    # holds its scatter.
+    op, Din, Dout = "WGRAD", 384, 256
     lhs, rhs = operands(op, T, Din, Dout, "R", "C", 4)
+    L, R = dev_bf16(lhs), dev_bf16(rhs)
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(A.STAGE_EVENTS)]
-    say("stage events")
-    A.adahop_gemm(op, dev_bf16(lhs), dev_bf16(rhs), "R", "C", None, 8, stage_events=ev)
+    say("stage events", T)
+    timed = A.adahop_gemm(op, L, R, "R", "C", None, 8, stage_events=ev)
+    plain = A.adahop_gemm(op, L, R, "R", "C", None, 8)
     torch.cuda.synchronize()
+    assert torch.equal(timed.view(torch.int16), plain.view(torch.int16))
     times = [ev[i].elapsed_time(ev[i + 1]) for i in range(A.STAGE_EVENTS - 1)]
     assert all(t >= 0 for t in times)
 
