@@ -33,6 +33,10 @@
 namespace adahop {
 namespace {
 
+// Cache-policy immediate of a buffer load: NT (non-temporal, streaming).
+constexpr int kLoadNT = 2;
+typedef unsigned int v4u32 __attribute__((ext_vector_type(4)));
+
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t h) {
   return __uint_as_float(h << 16);
 }
@@ -110,8 +114,11 @@ iht_quant_rowwise_kernel(const uint16_t* __restrict__ src, int64_t rows, int64_t
   }
   uint4 raw0 = make_uint4(0, 0, 0, 0), raw1 = make_uint4(0, 0, 0, 0);
   if (active) {
-    raw0 = *reinterpret_cast<const uint4*>(src + r * ld + col0);
-    raw1 = *reinterpret_cast<const uint4*>(src + r * ld + col0 + 8);
+    // Read once: non-temporal loads, as in the column-direction kernel.
+    const v4u32 a = __builtin_nontemporal_load(reinterpret_cast<const v4u32*>(src + r * ld + col0));
+    const v4u32 b = __builtin_nontemporal_load(reinterpret_cast<const v4u32*>(src + r * ld + col0 + 8));
+    raw0 = make_uint4(a.x, a.y, a.z, a.w);
+    raw1 = make_uint4(b.x, b.y, b.z, b.w);
   }
 
   if (tid < kRowRows) s_rowpos[tid] = -1;
@@ -292,13 +299,16 @@ iht_quant_colwise_kernel(const uint16_t* __restrict__ src, int64_t K, int64_t ou
     if (whole) {
       // Row j of the block is at byte j * ld * 2 from the block's first row:
       // a scalar offset, so the 32 loads need no per-lane address arithmetic.
+      // The source is read once: non-temporal loads (cache policy NT) stream
+      // it past the caches (7.3 against 6.6 TB/s for this load pattern alone,
+      // measured) and leave them to the packed output the GEMM reads next.
       const uint16_t* blk = src + (bbase * 32) * ld;     // workgroup-uniform
       const __amdgpu_buffer_rsrc_t rs =
           __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(blk), 0, 0x7FFFFFFF, 0x00020000);
       const int voff = (int)((bi * 32 * ld + c0) * 2);
 #pragma unroll
       for (int j = 0; j < 32; ++j) {
-        const auto q = __builtin_amdgcn_raw_buffer_load_b64(rs, voff, (int)(j * ld * 2), 0);
+        const auto q = __builtin_amdgcn_raw_buffer_load_b64(rs, voff, (int)(j * ld * 2), kLoadNT);
         w[j][0] = q[0];
         w[j][1] = q[1];
       }
