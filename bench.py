@@ -300,6 +300,40 @@ def mfma_ceiling(torch, np, args):
         "frac_of_nominal_peak": [round(float(t) / PEAK_FP4_TFLOPS, 4) for t in tflops]}}), flush=True)
 
 
+def hbm_ceiling(torch, np, args):
+    """HBM streaming rates (libadahop_probe.so) on two 2 GiB buffers: reads
+    with ordinary and non-temporal loads, writes, copies, and the read pattern
+    of the column-direction quantizer; median and best of 12 launches."""
+    import ctypes
+    lib = ctypes.CDLL(os.path.join(ROOT, "mxfp4_precision_gemms_amd", "libadahop_probe.so"))
+    fn = lib.adahop_probe_hbm
+    fn.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
+                   ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    nbytes = 2 << 30
+    a = torch.empty(nbytes, dtype=torch.uint8, device="cuda:0").fill_(1)
+    b = torch.empty(nbytes, dtype=torch.uint8, device="cuda:0").fill_(2)
+    sink = torch.empty(1024, dtype=torch.uint8, device="cuda:0")
+    grid = 8 * torch.cuda.get_device_properties(0).multi_processor_count
+    launches = 12
+    out = {}
+    for name, mode, nt, moved in (("read", 0, 0, nbytes), ("read_nt", 0, 1, nbytes),
+                                  ("write", 1, 0, nbytes), ("copy", 2, 0, 2 * nbytes),
+                                  ("copy_nt_loads", 2, 1, 2 * nbytes),
+                                  ("quantizer_column_blocks_read", 3, 0, (nbytes // 28672) // 128 * 128 * 28672),
+                                  ("quantizer_column_blocks_read_nt", 3, 1, (nbytes // 28672) // 128 * 128 * 28672)):
+        ms = np.zeros(launches, dtype=np.float32)
+        rc = fn(mode, nt, a.data_ptr(), b.data_ptr(), nbytes, grid, launches, sink.data_ptr(),
+                ms.ctypes.data)
+        if rc != 0:
+            sys.exit(f"hbm probe failed: hipError {rc}")
+        t = np.sort(ms[2:])                                 # the first two launches warm up
+        out[name] = {"tb_per_s_median": round(moved / float(np.median(t)) / 1e9, 2),
+                     "tb_per_s_best": round(moved / float(t[0]) / 1e9, 2),
+                     "bytes_moved": int(moved)}
+    print(json.dumps({"hbm_stream": out, "grid": grid, "launches": launches,
+                      "nominal_tb_per_s": 8.0}), flush=True)
+
+
 def sweep_oproj(A, torch, np, args):
     """One JSON line per (batch size, product) of the Llama3.1-8B o_proj
     triplet: effective TFLOP/s of the AdaHOP route with its GEMM stage's
@@ -419,6 +453,9 @@ def main():
     ap.add_argument("--mfma-ceiling", action="store_true",
                     help="instead of the timed line: the FP4 matrix cores' rate and clock with no "
                          "memory traffic (the practical ceiling under the power limit)")
+    ap.add_argument("--hbm-ceiling", action="store_true",
+                    help="HBM streaming rates of read, write and copy probes, and of the "
+                         "column quantizer's read pattern")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a 1 GiB device-to-device copy 3 times (a known-size reference "
                          "for HBM byte counters) and exit")
@@ -448,6 +485,9 @@ def main():
         return
     if args.mfma_ceiling:
         mfma_ceiling(torch, np, args)
+        return
+    if args.hbm_ceiling:
+        hbm_ceiling(torch, np, args)
         return
 
     wls = workloads()

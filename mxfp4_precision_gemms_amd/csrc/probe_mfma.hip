@@ -1,7 +1,9 @@
 // Measurement probes, not part of the AdaHOP path: the steady-state rate and
 // shader clock of the FP4 matrix cores with no memory traffic, the practical
-// ceiling any FP4 GEMM on this device runs under, and the LDS read bandwidth
-// per CU.
+// ceiling any FP4 GEMM on this device runs under; the LDS read bandwidth per
+// CU; and the HBM streaming rates (read, write, copy; ordinary and
+// non-temporal loads; the 32-row block pattern of the column-direction
+// quantizer) that bound the memory-bound kernels.
 //
 // One 512-thread workgroup per CU keeps 8 independent 32x32x64 scaled FP4
 // MFMAs per wave in flight on register operands that differ per lane and per
@@ -106,6 +108,94 @@ int run_probe(Launch launch, int blocks, int launches, void* scratch, double* cy
   return rc;
 }
 
+typedef unsigned int v4u __attribute__((ext_vector_type(4)));
+
+// Streaming kernels over n 16-byte words, 256 threads, U independent words
+// per thread per step, grid-stride; every index stays below n.
+template <bool NT>
+__global__ void __launch_bounds__(256) stream_read_kernel(const v4u* __restrict__ p, size_t n,
+                                                          unsigned* sink) {
+  constexpr int U = 8;
+  size_t i = (size_t)blockIdx.x * 256 * U + threadIdx.x;
+  const size_t stride = (size_t)gridDim.x * 256 * U;
+  unsigned acc = 0;
+  for (; i + 256 * (U - 1) < n; i += stride) {
+    v4u v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) v[u] = NT ? __builtin_nontemporal_load(p + i + 256 * u) : p[i + 256 * u];
+#pragma unroll
+    for (int u = 0; u < U; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+  }
+  if (acc == 0x12345678u) sink[threadIdx.x] = acc;
+}
+
+__global__ void __launch_bounds__(256) stream_write_kernel(v4u* __restrict__ p, size_t n) {
+  constexpr int U = 4;
+  size_t i = (size_t)blockIdx.x * 256 * U + threadIdx.x;
+  const size_t stride = (size_t)gridDim.x * 256 * U;
+  for (; i + 256 * (U - 1) < n; i += stride) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) p[i + 256 * u] = v4u{(unsigned)i, 1u, 2u, 3u};
+  }
+}
+
+template <bool NT>
+__global__ void __launch_bounds__(256) stream_copy_kernel(const v4u* __restrict__ s, v4u* __restrict__ d,
+                                                          size_t n) {
+  constexpr int U = 4;
+  size_t i = (size_t)blockIdx.x * 256 * U + threadIdx.x;
+  const size_t stride = (size_t)gridDim.x * 256 * U;
+  for (; i + 256 * (U - 1) < n; i += stride) {
+    v4u v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) v[u] = NT ? __builtin_nontemporal_load(s + i + 256 * u) : s[i + 256 * u];
+#pragma unroll
+    for (int u = 0; u < U; ++u) d[i + 256 * u] = v[u];
+  }
+}
+
+// The column-direction quantizer's read pattern over a [rows][ldb bytes]
+// matrix: workgroup (x, y) covers 512 bytes of columns and 128 rows; wave w
+// reads 32 rows of its 32-row block, 8 bytes per lane per row, at scalar row
+// offsets of one buffer descriptor. Cache policy AUX (2 = non-temporal).
+template <int AUX>
+__global__ void __launch_bounds__(256) colblock_read_kernel(const uint8_t* __restrict__ p, int64_t rows,
+                                                            int64_t ldb, unsigned* sink) {
+  const int tid = threadIdx.x, cg = tid % 64, bi = tid / 64;
+  const int64_t col = (int64_t)blockIdx.x * 512 + 8 * cg;
+  const int64_t r0 = ((int64_t)blockIdx.y * 4 + bi) * 32;
+  if (r0 + 32 > rows || col + 8 > ldb) return;
+  const uint8_t* blk = p + (int64_t)blockIdx.y * 128 * ldb;
+  const __amdgpu_buffer_rsrc_t rs =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(blk), 0, 0x7FFFFFFF, 0x00020000);
+  const int voff = (int)(bi * 32 * ldb + col);
+  unsigned acc = 0;
+#pragma unroll
+  for (int j = 0; j < 32; ++j) {
+    const auto q = __builtin_amdgcn_raw_buffer_load_b64(rs, voff, (int)(j * ldb), AUX);
+    acc ^= q[0] ^ q[1];
+  }
+  if (acc == 0x12345678u) sink[tid] = acc;
+}
+
+template <typename Launch>
+int time_launches(Launch launch, int launches, float* ms) {
+  hipEvent_t e0 = nullptr, e1 = nullptr;
+  hipError_t e = hipEventCreate(&e0);
+  if (e == hipSuccess) e = hipEventCreate(&e1);
+  for (int l = 0; l < launches && e == hipSuccess; ++l) {
+    e = hipEventRecord(e0, 0);
+    if (e == hipSuccess) launch();
+    if (e == hipSuccess) e = hipGetLastError();
+    if (e == hipSuccess) e = hipEventRecord(e1, 0);
+    if (e == hipSuccess) e = hipEventSynchronize(e1);
+    if (e == hipSuccess) e = hipEventElapsedTime(&ms[l], e0, e1);
+  }
+  if (e0) (void)hipEventDestroy(e0);
+  if (e1) (void)hipEventDestroy(e1);
+  return (int)e;
+}
+
 }  // namespace
 
 extern "C" {
@@ -135,6 +225,51 @@ __attribute__((visibility("default"))) int adahop_probe_lds_read(int blocks, int
   return run_probe([&](ProbeOut* out, char* sink) {
     lds_read_probe_kernel<<<dim3(blocks), dim3(512)>>>(out, iters, reinterpret_cast<unsigned*>(sink));
   }, blocks, launches, scratch, cycles, ticks);
+}
+
+// HBM streaming rates on the null stream: mode 0 reads `a` (nt: with
+// non-temporal loads), 1 writes `a`, 2 copies `a` to `b` (nt: non-temporal
+// loads), 3 reads `a` as the column-direction quantizer does, as a
+// [rows = bytes / 28672][28672 bytes] matrix (nt: cache policy NT).
+// `bytes` is a multiple of 16 (of 28672 for mode 3), `a` and `b` device
+// buffers of `bytes` (b unused except in mode 2), `sink` a device buffer of
+// 1 KB; `grid` workgroups of 256 threads (modes 0-2). Writes the duration of
+// each of `launches` launches in ms to the host array `ms`. Returns 0, or the
+// hipError_t of the first failing call.
+__attribute__((visibility("default"))) int adahop_probe_hbm(int mode, int nt, void* a, void* b,
+                                                            size_t bytes, int grid, int launches,
+                                                            void* sink, float* ms) {
+  if (mode < 0 || mode > 3 || !a || (mode == 2 && !b) || !sink || !ms || launches < 1 ||
+      bytes < 16 || bytes % 16 != 0 || grid < 1)
+    return (int)hipErrorInvalidValue;
+  const size_t n = bytes / 16;
+  v4u* pa = static_cast<v4u*>(a);
+  v4u* pb = static_cast<v4u*>(b);
+  unsigned* sk = static_cast<unsigned*>(sink);
+  switch (mode) {
+    case 0:
+      return time_launches([&] {
+        if (nt) stream_read_kernel<true><<<dim3(grid), dim3(256)>>>(pa, n, sk);
+        else stream_read_kernel<false><<<dim3(grid), dim3(256)>>>(pa, n, sk);
+      }, launches, ms);
+    case 1:
+      return time_launches([&] { stream_write_kernel<<<dim3(grid), dim3(256)>>>(pa, n); }, launches, ms);
+    case 2:
+      return time_launches([&] {
+        if (nt) stream_copy_kernel<true><<<dim3(grid), dim3(256)>>>(pa, pb, n);
+        else stream_copy_kernel<false><<<dim3(grid), dim3(256)>>>(pa, pb, n);
+      }, launches, ms);
+    default: {
+      const int64_t ldb = 28672, rows = (int64_t)(bytes / ldb) / 128 * 128;
+      if (rows < 128 || (int64_t)bytes < rows * ldb) return (int)hipErrorInvalidValue;
+      const dim3 g((unsigned)(ldb / 512), (unsigned)(rows / 128));
+      const uint8_t* p = static_cast<const uint8_t*>(a);
+      return time_launches([&] {
+        if (nt) colblock_read_kernel<2><<<g, dim3(256)>>>(p, rows, ldb, sk);
+        else colblock_read_kernel<0><<<g, dim3(256)>>>(p, rows, ldb, sk);
+      }, launches, ms);
+    }
+  }
 }
 
 }  // extern "C"
