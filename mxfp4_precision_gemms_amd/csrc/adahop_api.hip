@@ -482,15 +482,26 @@ adahop_status run_gemm(adahop_op op, const uint16_t* lhs, const uint16_t* rhs, i
                        pb.scan_axis, 64, pb.k, idx, P.off_foid != kNone ? w + P.off_foid : nullptr,
                        P.foid_bytes, st);
   };
+  // With an outer outlier product the operand FOID does not scan is the
+  // product's wide factor, read again in bf16 by the GEMM launch right after
+  // its quantization. Up to a quarter of the 256 MB Infinity Cache, that
+  // quantization keeps its source in the caches for it (o-proj BS 1 input
+  // gradient, W 32 MB: -4 % per call, same-box A/B); larger factors would
+  // not survive the other operand's pass and lose 0.2-2.4 % to the slower
+  // loads. Every other quantization streams its source.
+  const bool outer_oe = pb.route == ADAHOP_ROUTE_OE_LEFT || pb.route == ADAHOP_ROUTE_OE_RIGHT;
+  const int64_t wide_bytes = 2 * (scan_lhs ? s.rhs_rows * s.rhs_cols : s.lhs_rows * s.lhs_cols);
+  const bool keep_wide = outer_oe && wide_bytes <= (int64_t)64 << 20;
+  const bool keep_lhs = keep_wide && !scan_lhs, keep_rhs = keep_wide && scan_lhs;
   auto quant_lhs = [&](hipStream_t st) {
     return iht_quant_launch(lhs, s.lhs_rows, s.lhs_cols, s.lhs_cols, s.lhs_contract, had,
                             P.zero_lhs ? idx : nullptr, P.zero_lhs ? pb.k : 0, P.lhs_zero_axis,
-                            ac, as, ll, pb.layout, st);
+                            ac, as, ll, pb.layout, st, !keep_lhs);
   };
   auto quant_rhs = [&](hipStream_t st) {
     return iht_quant_launch(rhs, s.rhs_rows, s.rhs_cols, s.rhs_cols, s.rhs_contract, had,
                             P.zero_rhs ? idx : nullptr, P.zero_rhs ? pb.k : 0, P.rhs_zero_axis,
-                            bc, bs, rl, pb.layout, st);
+                            bc, bs, rl, pb.layout, st, !keep_rhs);
   };
   // OE_LEFT / OE_RIGHT zero lines of the scanned operand only, and only the
   // GEMM reads the other operand's packed form: that operand is quantized on

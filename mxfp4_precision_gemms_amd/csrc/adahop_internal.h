@@ -34,10 +34,14 @@ adahop_status foid_launch(const uint16_t* t, int64_t rows, int64_t cols, int64_t
 // ---- zero + gather + IHT + MXFP4 ------------------------------------------
 // Whether iht_quant_launch's grid fits (false: it would return UNSUPPORTED).
 bool iht_quant_fits(int64_t rows, int64_t cols, int contract);
+// stream_src: load the source non-temporally (it is read once); false keeps
+// it in the caches for a kernel that reads it again soon after (the outer
+// outlier product's wide factor).
 adahop_status iht_quant_launch(const uint16_t* src, int64_t rows, int64_t cols, int64_t ld,
                                int contract, int32_t hadamard_block, const int32_t* zero_idx,
                                int32_t nzero, int zero_axis, uint8_t* codes, uint8_t* scales,
-                               uint16_t* gathered, int layout, hipStream_t stream);
+                               uint16_t* gathered, int layout, hipStream_t stream,
+                               bool stream_src = true);
 
 // ---- outlier product (bf16 MFMA) ------------------------------------------
 // P_s[x][y] = sum over t in split s of X(x, t) * Y(y, t), fp32, for s < splits,

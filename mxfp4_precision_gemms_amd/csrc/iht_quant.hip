@@ -89,7 +89,7 @@ iht_quant_rowwise_kernel(const uint16_t* __restrict__ src, int64_t rows, int64_t
                          int chunks_per_row, int hadamard, const int32_t* __restrict__ zidx,
                          int nz, int zaxis, uint8_t* __restrict__ codes,
                          uint8_t* __restrict__ scales, uint16_t* __restrict__ gathered,
-                         int kchunk) {
+                         int kchunk, int stream_src) {
   // Extracted lines inside this tile: each row's position in the index list
   // (zero_axis ROWS, -1 if none), or a mask of the columns (zero_axis COLS).
   __shared__ int32_t s_rowpos[kRowRows];
@@ -114,9 +114,17 @@ iht_quant_rowwise_kernel(const uint16_t* __restrict__ src, int64_t rows, int64_t
   }
   uint4 raw0 = make_uint4(0, 0, 0, 0), raw1 = make_uint4(0, 0, 0, 0);
   if (active) {
-    // Read once: non-temporal loads, as in the column-direction kernel.
-    const v4u32 a = __builtin_nontemporal_load(reinterpret_cast<const v4u32*>(src + r * ld + col0));
-    const v4u32 b = __builtin_nontemporal_load(reinterpret_cast<const v4u32*>(src + r * ld + col0 + 8));
+    // Read once: non-temporal loads, as in the column-direction kernel
+    // (ordinary ones when another kernel reads the source again soon).
+    const v4u32* p = reinterpret_cast<const v4u32*>(src + r * ld + col0);
+    v4u32 a, b;
+    if (stream_src) {
+      a = __builtin_nontemporal_load(p);
+      b = __builtin_nontemporal_load(p + 1);
+    } else {
+      a = p[0];
+      b = p[1];
+    }
     raw0 = make_uint4(a.x, a.y, a.z, a.w);
     raw1 = make_uint4(b.x, b.y, b.z, b.w);
   }
@@ -259,7 +267,7 @@ constexpr int kColOut = 4 * kColGroups;        // output rows per workgroup
 constexpr int kColBlocks = kColThreads / kColGroups;   // 32-row blocks per workgroup
 constexpr int kColPitch = kColBlocks * 16 + 16;        // LDS bytes per output row (padded)
 
-template <bool Vec, bool Had>
+template <bool Vec, bool Had, bool NT>
 __global__ void __launch_bounds__(kColThreads)
 iht_quant_colwise_kernel(const uint16_t* __restrict__ src, int64_t K, int64_t outer, int64_t ld,
                          const int32_t* __restrict__ zidx, int nz, int zaxis,
@@ -301,14 +309,16 @@ iht_quant_colwise_kernel(const uint16_t* __restrict__ src, int64_t K, int64_t ou
       // a scalar offset, so the 32 loads need no per-lane address arithmetic.
       // The source is read once: non-temporal loads (cache policy NT) stream
       // it past the caches (7.3 against 6.6 TB/s for this load pattern alone,
-      // measured) and leave them to the packed output the GEMM reads next.
+      // measured) and leave them to the packed output the GEMM reads next;
+      // ordinary loads (NT false) when another kernel reads the source again
+      // soon after.
       const uint16_t* blk = src + (bbase * 32) * ld;     // workgroup-uniform
       const __amdgpu_buffer_rsrc_t rs =
           __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(blk), 0, 0x7FFFFFFF, 0x00020000);
       const int voff = (int)((bi * 32 * ld + c0) * 2);
 #pragma unroll
       for (int j = 0; j < 32; ++j) {
-        const auto q = __builtin_amdgcn_raw_buffer_load_b64(rs, voff, (int)(j * ld * 2), kLoadNT);
+        const auto q = __builtin_amdgcn_raw_buffer_load_b64(rs, voff, (int)(j * ld * 2), NT ? kLoadNT : 0);
         w[j][0] = q[0];
         w[j][1] = q[1];
       }
@@ -492,7 +502,8 @@ bool iht_quant_fits(int64_t rows, int64_t cols, int contract) {
 adahop_status iht_quant_launch(const uint16_t* src, int64_t rows, int64_t cols, int64_t ld,
                                int contract, int32_t hadamard_block, const int32_t* zero_idx,
                                int32_t nzero, int zero_axis, uint8_t* codes, uint8_t* scales,
-                               uint16_t* gathered, int layout, hipStream_t stream) {
+                               uint16_t* gathered, int layout, hipStream_t stream,
+                               bool stream_src) {
   const int kchunk = layout == ADAHOP_LAYOUT_KCHUNK ? 1 : 0;
   const int64_t Kc = contract == ADAHOP_AXIS_COLS ? cols : rows;
   if (kchunk && (Kc % 128 != 0 || (reinterpret_cast<uintptr_t>(scales) & 3u) != 0))
@@ -505,7 +516,7 @@ adahop_status iht_quant_launch(const uint16_t* src, int64_t rows, int64_t cols, 
     if (grid > 0x7FFFFFFFLL) return fail(ADAHOP_ERR_UNSUPPORTED, "iht_quant: tensor too large");
     iht_quant_rowwise_kernel<<<dim3((unsigned)grid), dim3(kRowThreads), 0, stream>>>(
         src, rows, K, ld, (int)cpr, had, zero_idx, nzero, zero_axis, codes, scales, gathered,
-        kchunk);
+        kchunk, stream_src ? 1 : 0);
   } else {
     const int64_t K = rows, outer = cols;
     const int64_t gx = (outer + kColOut - 1) / kColOut;
@@ -517,14 +528,18 @@ adahop_status iht_quant_launch(const uint16_t* src, int64_t rows, int64_t cols, 
     // the workgroup's first row: 512 rows of ld elements must stay below 2^31.
     const bool vec = ld % 4 == 0 && (reinterpret_cast<uintptr_t>(src) & 7u) == 0 &&
                      (int64_t)kColBlocks * 32 * ld * 2 < 0x7FFFFFFF;
-    auto go = [&](auto V, auto H) {
-      iht_quant_colwise_kernel<decltype(V)::value, decltype(H)::value><<<grid, block, 0, stream>>>(
-          src, K, outer, ld, zero_idx, nzero, zero_axis, codes, scales, gathered, kchunk);
+    auto go = [&](auto V, auto H, auto N) {
+      iht_quant_colwise_kernel<decltype(V)::value, decltype(H)::value, decltype(N)::value>
+          <<<grid, block, 0, stream>>>(src, K, outer, ld, zero_idx, nzero, zero_axis, codes, scales,
+                                       gathered, kchunk);
     };
-    if (vec && had) go(std::true_type{}, std::true_type{});
-    else if (vec) go(std::true_type{}, std::false_type{});
-    else if (had) go(std::false_type{}, std::true_type{});
-    else go(std::false_type{}, std::false_type{});
+    // The cache policy applies to the vector path's buffer loads only.
+    if (vec && had && stream_src) go(std::true_type{}, std::true_type{}, std::true_type{});
+    else if (vec && had) go(std::true_type{}, std::true_type{}, std::false_type{});
+    else if (vec && stream_src) go(std::true_type{}, std::false_type{}, std::true_type{});
+    else if (vec) go(std::true_type{}, std::false_type{}, std::false_type{});
+    else if (had) go(std::false_type{}, std::true_type{}, std::false_type{});
+    else go(std::false_type{}, std::false_type{}, std::false_type{});
   }
   return check_launch("iht_quant");
 }
