@@ -16,7 +16,7 @@
 //
 // Selection without a host round trip, by radix select on the fp64 score
 // bits (see foid_select_kernel): 512-thread workgroups, digit counts by
-// integer adds in LDS, one barrier per 4-bit digit. Every score
+// wave ballots summed in LDS, one barrier per 4-bit digit. Every score
 // above the k-th largest, T, is kept, and of the scores equal to T the ones
 // with the lowest indices -- the key (score descending, index ascending) is
 // a strict total order, so the result is unique. A prefix sum over the
@@ -150,18 +150,21 @@ __device__ __forceinline__ void pair_variance(const uint16_t* __restrict__ t, in
 constexpr int kSelThreads = 512;
 constexpr int kSelWaves = kSelThreads / 64;
 
-// Exclusive prefix sum of v over the workgroup's threads in order; *total
-// receives the sum. Uses s_tmp[THREADS / 64].
-template <int THREADS>
+// Exclusive prefix sum of v, 0 <= v < 2^BITS, over the workgroup's threads
+// in order; *total receives the sum. Within a wave by one ballot per bit of
+// v and a count of the ballot's bits below the lane (no cross-lane shuffles,
+// which go through the LDS); then over the waves. Uses s_tmp[THREADS / 64].
+template <int THREADS, int BITS>
 __device__ __forceinline__ int block_exclusive_scan(int v, int* s_tmp, int* total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  int x = v;
+  int x = 0, wsum = 0;
 #pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const int y = __shfl_up(x, off);
-    if (lane >= off) x += y;
+  for (int b = 0; b < BITS; ++b) {
+    const uint64_t m = __builtin_amdgcn_ballot_w64(((v >> b) & 1) != 0);
+    x += (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u)) << b;
+    wsum += __popcll(m) << b;
   }
-  if (lane == 63) s_tmp[wave] = x;
+  if (lane == 0) s_tmp[wave] = wsum;
   __syncthreads();
   int before = 0, sum = 0;
 #pragma unroll
@@ -172,7 +175,7 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* s_tmp, int* tota
   }
   __syncthreads();
   *total = sum;
-  return before + x - v;
+  return before + x;
 }
 
 // Inputs of one selection. Level 0 (t != nullptr) scores candidate lines
@@ -190,11 +193,11 @@ struct SelectArgs {
 // Selection over chunks of 512 * KPT entries per workgroup, thread t owning
 // entries 512 * KPT * b + KPT t .. + KPT - 1 in index order. Radix select
 // on the fp64 score bits (scores are >= 0, so their bit patterns order like
-// the values), 4 bits per pass from the top: every key in the current bin
-// adds one to its wave's LDS counter of its next digit, one barrier publishes
-// the 8 x 16 counts, and every wave sums them and picks the digit of the
-// krem-th largest key itself (integer counts: the order of the adds does not
-// matter). The pass
+// the values), 4 bits per pass from the top: each wave counts its keys in the
+// current bin per next digit with ballots and writes the 16 counts to LDS,
+// one barrier publishes the 8 x 16 counts, and every wave sums them and picks
+// the digit of the krem-th largest key itself (integer counts: the order of
+// the adds does not matter). The pass
 // loop ends once the chosen bin holds exactly the keys still needed (all of
 // them kept), else after 16 passes with T, the k-th largest key: every key
 // above T is kept and, of the keys equal to T, the ones with the lowest
@@ -233,37 +236,47 @@ __device__ __forceinline__ void select_block(const SelectArgs& a, int block,
   uint64_t prefix = 0, pmask = 0;
   int krem = a.k;
   bool keep_all = false, bin_kept = false;
-  // Each wave counts into its own row of 16 digit counters in LDS, double
-  // buffered: a wave clears its row of the next pass's buffer only after the
-  // barrier that ends every wave's reads of it, and its own adds come after
-  // its clear in program order.
-  if (lane < 16) s_cnt[0][wave][lane] = 0;
   for (int pass = 0; pass < 16; ++pass) {
     const int shift = 60 - 4 * pass;
     const int buf = pass & 1;
-    // Per key in the current bin: one LDS add to the counter of its next digit.
+    // The wave's count of each next digit among its keys in the current bin,
+    // by ballots rather than LDS atomics (in the first passes every key of a
+    // wave shares one digit, and adds to one counter serialize): per key
+    // slot, a ballot of the keys in the bin and one of each digit bit; lane
+    // d < 16 keeps the keys whose 4 bits spell d and counts them. Its row of
+    // the pass's buffer is written once; the buffers alternate, so a row is
+    // rewritten only after the barrier that ends every wave's reads of it.
+    uint32_t mine = 0;
 #pragma unroll
     for (int j = 0; j < KPT; ++j) {
-      if (((valid >> j) & 1u) && (key[j] & pmask) == prefix)
-        atomicAdd(&s_cnt[buf][wave][(uint32_t)(key[j] >> shift) & 15u], 1u);
+      const bool in = ((valid >> j) & 1u) && (key[j] & pmask) == prefix;
+      const uint32_t dj = (uint32_t)(key[j] >> shift) & 15u;
+      uint64_t m = __builtin_amdgcn_ballot_w64(in);
+#pragma unroll
+      for (int bit = 0; bit < 4; ++bit) {
+        const uint64_t bm = __builtin_amdgcn_ballot_w64(in && ((dj >> bit) & 1u));
+        m &= ((lane >> bit) & 1) ? bm : ~bm;
+      }
+      mine += (uint32_t)__popcll(m);
     }
+    if (lane < 16) s_cnt[buf][wave][lane] = mine;
     __syncthreads();
-    if (lane < 16) s_cnt[buf ^ 1][wave][lane] = 0;
     int tot = 0;
     if (lane < 16) {
 #pragma unroll
       for (int w = 0; w < kSelWaves; ++w) tot += (int)s_cnt[buf][w][lane];
     }
     // Lane d < 16: keys of the bin with next digit >= d (a suffix sum over
-    // lanes d .. 15). The digit of the krem-th largest key is the largest d
-    // whose suffix holds at least krem keys; the keys above it are those of
-    // digits d + 1 .. 15. Wave-uniform throughout.
+    // lanes d .. 15, which form one DPP row: four adds of the value 1, 2, 4
+    // and 8 lanes up, 0 past the row's end). The digit of the krem-th
+    // largest key is the largest d whose suffix holds at least krem keys;
+    // the keys above it are those of digits d + 1 .. 15. Wave-uniform
+    // throughout.
     int suf = tot;
-#pragma unroll
-    for (int off = 1; off < 16; off <<= 1) {
-      const int y = __shfl_down(suf, off, 64);
-      if (lane + off < 16) suf += y;
-    }
+    suf += __builtin_amdgcn_update_dpp(0, suf, 0x101, 0xF, 0xF, true);   // row_shl:1
+    suf += __builtin_amdgcn_update_dpp(0, suf, 0x102, 0xF, 0xF, true);   // row_shl:2
+    suf += __builtin_amdgcn_update_dpp(0, suf, 0x104, 0xF, 0xF, true);   // row_shl:4
+    suf += __builtin_amdgcn_update_dpp(0, suf, 0x108, 0xF, 0xF, true);   // row_shl:8
     const int all = __builtin_amdgcn_readfirstlane(suf);
     if (pass == 0 && all <= a.k) { keep_all = true; break; }   // every real entry is kept
     const uint64_t ge = __builtin_amdgcn_ballot_w64(lane < 16 && suf >= krem);
@@ -287,7 +300,7 @@ __device__ __forceinline__ void select_block(const SelectArgs& a, int block,
   if (!keep_all && !bin_kept) {
     // All 16 digits decided: prefix is T; the first krem keys equal to T.
     int eq_total;
-    const int eq_before = block_exclusive_scan<kSelThreads>(__popc(eq), s_tmp, &eq_total);
+    const int eq_before = block_exclusive_scan<kSelThreads, KPT == 2 ? 2 : 4>(__popc(eq), s_tmp, &eq_total);
     int take = krem - eq_before;
 #pragma unroll
     for (int j = 0; j < KPT; ++j) {
@@ -295,7 +308,7 @@ __device__ __forceinline__ void select_block(const SelectArgs& a, int block,
     }
   }
   int kept;
-  int pos = block_exclusive_scan<kSelThreads>(__popc(keep), s_tmp, &kept);
+  int pos = block_exclusive_scan<kSelThreads, KPT == 2 ? 2 : 4>(__popc(keep), s_tmp, &kept);
 
   if (a.final_idx != nullptr) {
 #pragma unroll
