@@ -204,9 +204,21 @@ struct SelectArgs {
 // indices -- the key (score descending, index ascending) is a strict total
 // order, so the result is unique. A prefix sum over the threads writes the
 // kept entries already sorted by index.
+// Stores of survivors another workgroup reads in the same launch:
+// agent-scope monotonic atomic stores, which write through this XCD's L2
+// (on gfx950 an ordinary store may stay dirty in it, out of another XCD's
+// sight).
+__device__ __forceinline__ void publish(double* p, double v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void publish(int32_t* p, int32_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 template <int KPT>
 __device__ __forceinline__ void select_block(const SelectArgs& a, int block,
-                                             uint32_t (*s_cnt)[kSelWaves][16], int* s_tmp) {
+                                             uint32_t (*s_cnt)[kSelWaves][16], int* s_tmp,
+                                             bool write_through = false) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t first = (int64_t)block * kSelThreads * KPT + (int64_t)tid * KPT;
 
@@ -324,37 +336,58 @@ __device__ __forceinline__ void select_block(const SelectArgs& a, int block,
   for (int j = 0; j < KPT; ++j) {
     if (!((keep >> j) & 1u)) continue;
     const int64_t g = first + j;
-    a.out_var[ob + pos] = __longlong_as_double((long long)key[j]);
-    a.out_idx[ob + pos] = a.in_idx ? a.in_idx[g] : (int32_t)g;
+    const double v = __longlong_as_double((long long)key[j]);
+    const int32_t i = a.in_idx ? a.in_idx[g] : (int32_t)g;
+    if (write_through) {
+      publish(&a.out_var[ob + pos], v);
+      publish(&a.out_idx[ob + pos], i);
+    } else {
+      a.out_var[ob + pos] = v;
+      a.out_idx[ob + pos] = i;
+    }
     ++pos;
   }
   for (int p = kept + tid; p < a.k; p += kSelThreads) {      // fewer than k real entries
-    a.out_var[ob + p] = -1.0;
-    a.out_idx[ob + p] = INT_MAX;
+    if (write_through) {
+      publish(&a.out_var[ob + p], -1.0);
+      publish(&a.out_idx[ob + p], (int32_t)INT_MAX);
+    } else {
+      a.out_var[ob + p] = -1.0;
+      a.out_idx[ob + p] = INT_MAX;
+    }
   }
 }
 
 // One level of selection, workgroup b taking chunk b. With `counter` (zero
 // at launch), the level is the last before the final one, and the level's
 // last workgroup to finish runs the final selection `fin` over all
-// survivors: every workgroup publishes its survivors (device-scope release)
-// before counting itself in, and the one that counts last acquires them. No
-// workgroup waits for another, and the final selection starts as soon as
-// the level ends, without a second dispatch.
+// survivors: every workgroup writes its survivors through to memory
+// (agent-scope stores), waits for them to complete, and only then counts
+// itself in; the one that counts last invalidates its L2 (an acquire fence,
+// no write-back) before reading them. No full-cache fence: one that writes
+// back the L2 costs 2-11 us per workgroup while a quantizer's output sits
+// dirty in it. No workgroup waits for another, and the final selection
+// starts as soon as the level ends, without a second dispatch.
 template <int KPT>
 __global__ void __launch_bounds__(kSelThreads) foid_select_kernel(SelectArgs a, SelectArgs fin,
                                                                   unsigned* counter) {
   __shared__ uint32_t s_cnt[2][kSelWaves][16];
   __shared__ int s_tmp[kSelWaves];
   __shared__ int s_last;
-  select_block<KPT>(a, blockIdx.x, s_cnt, s_tmp);
+  select_block<KPT>(a, blockIdx.x, s_cnt, s_tmp, counter != nullptr);
   if (counter == nullptr) return;
-  __threadfence();
+  // Every thread's write-through stores complete before the workgroup counts
+  // itself in (the compiler barriers keep the stores on their side).
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0);
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
   __syncthreads();
-  if (threadIdx.x == 0) s_last = atomicAdd(counter, 1u) == gridDim.x - 1 ? 1 : 0;
+  if (threadIdx.x == 0)
+    s_last = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+                     gridDim.x - 1 ? 1 : 0;
   __syncthreads();
   if (!s_last) return;
-  __threadfence();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
   select_block<KPT>(fin, 0, s_cnt, s_tmp);
 }
 

@@ -154,6 +154,36 @@ def test_foid_bit_exact(case):
     assert np.array_equal(host(idx), ref)
 
 
+@pytest.mark.parametrize("case", [(64, 14336, "COLS"), (70000, 64, "ROWS")],
+                         ids=["14-chunks-then-final", "three-levels"])
+def test_foid_handoff_fresh_each_call(case):
+    # The level before the final one hands its survivors to its last
+    # workgroup inside the launch. Back-to-back calls on one workspace, each
+    # with other planted lines, must each see their own survivors: a stale
+    # read would return an earlier call's indices.
+    rows, cols, axis = case
+    k = 64
+    dim = cols if axis == "COLS" else rows
+    ws = torch.empty(max(A.adahop_detect_workspace_size(rows, cols, axis, k), 1), dtype=torch.uint8,
+                     device=DEV)
+    inputs, outs = [], []
+    for it in range(8):
+        rng = np.random.default_rng(7000 + it)
+        lines = rng.choice(dim, 2 * k, replace=False)
+        t = rand_bf16(rng, (rows, cols), planted=(1 if axis == "COLS" else 0, lines),
+                      factor=rng.uniform(1, 3))
+        inputs.append(t)
+    devs = [dev_bf16(t) for t in inputs]
+    torch.cuda.synchronize()
+    say("foid hand-off", case)
+    for d in devs:
+        outs.append(A.adahop_detect(d, axis, k, ws=ws).clone())
+    torch.cuda.synchronize()
+    for t, got in zip(inputs, outs):
+        ref = oracle.foid(t, oracle.COLS if axis == "COLS" else oracle.ROWS, k, 64)
+        assert np.array_equal(host(got), ref)
+
+
 # --------------------------------------------------------------------------
 # Pre-quantized GEMM with and without the outlier term
 # --------------------------------------------------------------------------
