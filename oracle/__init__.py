@@ -8,6 +8,11 @@ The arithmetic lives in ``adahop_ref.c`` (plain C11, fp64 where the method
 leaves the precision open, the kernels' fp32 where floating point decides a
 quantized code). This module only marshals numpy arrays into it; the
 composition of the steps into one GEMM call is in ``pipeline.py``.
+
+Parity unpinned: ``route`` beyond the products the pages configure (their
+cells and Table 1's pair counts pin it; Fig. 5's table is not legible, so the
+rest is the derivation stated in ``adahop_ref.c``). Every other function is
+pinned by the CPU tests against closed forms, printed values or brute force.
 """
 import ctypes
 import os
