@@ -133,6 +133,9 @@ FOID_CASES = [
     (96, 256, "ROWS", 7, 16, True),          # shorter probe
     (64, 14336, "COLS", 64, 64, False),      # Llama3.1-8B d_ff columns: 14 chunks, then one
     (1024, 64, "ROWS", 64, 64, True),        # exactly one chunk: scores and selection in one launch
+    (64, 4096, "COLS", 64, 64, False),       # four chunks, then the final workgroup
+    (3000, 64, "ROWS", 32, 64, True),        # the same with a ragged last chunk, ties
+    (2500, 96, "ROWS", 64, 16, False),       # the same with a short probe (one candidate at a time)
 ]
 
 
