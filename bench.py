@@ -266,7 +266,7 @@ def mfma_ceiling(torch, np, args):
     limit for any FP4 kernel, against the nominal 10.1 PFLOP/s (2.4 GHz)."""
     import ctypes
     lib = ctypes.CDLL(os.path.join(ROOT, "mxfp4_precision_gemms_amd", "libadahop_probe.so"))
-    for fn in (lib.adahop_probe_mfma_fp4, lib.adahop_probe_lds_read):
+    for fn in (lib.adahop_probe_mfma_fp4, lib.adahop_probe_mfma_fp4_16, lib.adahop_probe_lds_read):
         fn.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
                        ctypes.c_void_p]
     blocks = torch.cuda.get_device_properties(0).multi_processor_count
@@ -282,6 +282,16 @@ def mfma_ceiling(torch, np, args):
     clock = cyc / tick * 0.1                              # GHz (ticks at 100 MHz)
     util = mfmas_per_wave * 2 * 32 / cyc                  # 2 waves per SIMD, 32 cycles per MFMA
     tflops = blocks * 8 * mfmas_per_wave * 131072 / (tick / 1e8) / 1e12
+    # The same multiply-adds as 16x16x128 MFMAs (half the accumulator traffic per MAC).
+    cyc16 = np.zeros(launches)
+    tick16 = np.zeros(launches)
+    rc = lib.adahop_probe_mfma_fp4_16(blocks, iters, launches, scratch.data_ptr(), cyc16.ctypes.data,
+                                      tick16.ctypes.data)
+    if rc != 0:
+        sys.exit(f"mfma probe (16x16x128) failed: hipError {rc}")
+    clock16 = cyc16 / tick16 * 0.1
+    util16 = mfmas_per_wave * 2 * 32 / cyc16          # 16 MFMAs of 16 cycles per iteration
+    tflops16 = blocks * 8 * mfmas_per_wave * 131072 / (tick16 / 1e8) / 1e12
     lit = 20000
     lc, lt = np.zeros(3), np.zeros(3)
     rc = lib.adahop_probe_lds_read(blocks, lit, 3, scratch.data_ptr(), lc.ctypes.data, lt.ctypes.data)
@@ -297,7 +307,15 @@ def mfma_ceiling(torch, np, args):
         "clock_ghz": [round(float(c), 3) for c in clock],
         "mfma_busy": [round(float(u), 4) for u in util],
         "tflops": [round(float(t), 1) for t in tflops],
-        "frac_of_nominal_peak": [round(float(t) / PEAK_FP4_TFLOPS, 4) for t in tflops]}}), flush=True)
+        "frac_of_nominal_peak": [round(float(t) / PEAK_FP4_TFLOPS, 4) for t in tflops]},
+                      "mfma_ceiling_16x16x128": {
+        "kernel": "16 x v_mfma_scale_f32_16x16x128_f8f6f4 (E2M1 x E2M1) per wave per iteration "
+                  "(the same multiply-adds), register operands, 8 waves per CU",
+        "launch_ms": [round(float(t) / 1e5, 2) for t in tick16],
+        "clock_ghz": [round(float(c), 3) for c in clock16],
+        "mfma_busy": [round(float(u), 4) for u in util16],
+        "tflops": [round(float(t), 1) for t in tflops16],
+        "frac_of_nominal_peak": [round(float(t) / PEAK_FP4_TFLOPS, 4) for t in tflops16]}}), flush=True)
 
 
 def hbm_ceiling(torch, np, args):

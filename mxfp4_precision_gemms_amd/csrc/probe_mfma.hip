@@ -60,6 +60,44 @@ __global__ void __launch_bounds__(512) mfma_fp4_probe_kernel(ProbeOut* out, int 
   if (s == 1234.5f) sink[tid] = s;   // keeps the MFMAs live; never true for these codes' sums
 }
 
+// The same with 16x16x128 scaled FP4 MFMAs: 16 independent blocks per wave
+// (the same 128 x 64 outputs per wave, half the accumulator bytes per MAC).
+__global__ void __launch_bounds__(512) mfma_fp4_16_probe_kernel(ProbeOut* out, int iters, float* sink) {
+  typedef float v4f __attribute__((ext_vector_type(4)));
+  const int tid = threadIdx.x;
+  v4f acc[16];
+  for (int a = 0; a < 16; ++a)
+    for (int v = 0; v < 4; ++v) acc[a][v] = 0.0f;
+  v4i fa[4], fb[4];
+  unsigned h = 0x9E3779B9u * (unsigned)(tid + 1 + 512 * blockIdx.x);
+  auto next = [&]() { h ^= h << 13; h ^= h >> 17; h ^= h << 5; return (int)(h & 0x77777777u); };
+  for (int i = 0; i < 4; ++i)
+    for (int e = 0; e < 4; ++e) fa[i][e] = next();
+  for (int i = 0; i < 4; ++i)
+    for (int e = 0; e < 4; ++e) fb[i][e] = next();
+  const unsigned long long t0 = __builtin_amdgcn_s_memtime();
+  const unsigned long long r0 = __builtin_amdgcn_s_memrealtime();
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        acc[4 * i + j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+            v8i{fb[j][0], fb[j][1], fb[j][2], fb[j][3], 0, 0, 0, 0},
+            v8i{fa[i][0], fa[i][1], fa[i][2], fa[i][3], 0, 0, 0, 0}, acc[4 * i + j], 4, 4, 0, 127, 0, 127);
+  }
+  __syncthreads();
+  const unsigned long long t1 = __builtin_amdgcn_s_memtime();
+  const unsigned long long r1 = __builtin_amdgcn_s_memrealtime();
+  if (tid == 0) {
+    out[blockIdx.x].cycles = t1 - t0;
+    out[blockIdx.x].realtime = r1 - r0;
+  }
+  float s = 0.0f;
+  for (int a = 0; a < 16; ++a) s += acc[a][0];
+  if (s == 1234.5f) sink[tid] = s;   // keeps the MFMAs live; never true for these codes' sums
+}
+
 // LDS read bandwidth: every thread of a 512-thread workgroup reads 16-byte
 // chunks, consecutive lanes 16 bytes apart (no bank conflicts), 8 reads per
 // iteration, from a 128 KB array.
@@ -212,6 +250,18 @@ __attribute__((visibility("default"))) int adahop_probe_mfma_fp4(int blocks, int
     return (int)hipErrorInvalidValue;
   return run_probe([&](ProbeOut* out, char* sink) {
     mfma_fp4_probe_kernel<<<dim3(blocks), dim3(512)>>>(out, iters, reinterpret_cast<float*>(sink));
+  }, blocks, launches, scratch, cycles, ticks);
+}
+
+// As adahop_probe_mfma_fp4 with 16x16x128 MFMAs: 16 per wave per iteration
+// (the same multiply-adds as the 8 32x32x64 ones).
+__attribute__((visibility("default"))) int adahop_probe_mfma_fp4_16(int blocks, int iters, int launches,
+                                                                    void* scratch, double* cycles,
+                                                                    double* ticks) {
+  if (blocks < 1 || iters < 1 || launches < 1 || !scratch || !cycles || !ticks)
+    return (int)hipErrorInvalidValue;
+  return run_probe([&](ProbeOut* out, char* sink) {
+    mfma_fp4_16_probe_kernel<<<dim3(blocks), dim3(512)>>>(out, iters, reinterpret_cast<float*>(sink));
   }, blocks, launches, scratch, cycles, ticks);
 }
 
