@@ -611,184 +611,6 @@ struct RingItem {
   int voffa[2], voffb[2], soff;
 };
 
-// ---------------------------------------------------------------------------
-// 16 x 16 output blocks. The FP4 ring kernel can compute its tile with
-// v_mfma_scale_f32_16x16x128_f8f6f4 (one MFMA per block per 128-deep stage)
-// instead of 32x32x64: the same multiply-adds per cycle with half the
-// accumulator reads and writes per multiply-add, so the matrix cores draw
-// less power and the device's power limit allows a higher clock. Wave w's
-// 128 x 64 sub-tile is then 8 x 4 blocks; with the B operand first, lane l of
-// block (I, J) holds C row 16 I + l % 16, columns 16 J + 4 (l / 16) .. +3.
-// ---------------------------------------------------------------------------
-typedef float v4f __attribute__((ext_vector_type(4)));
-constexpr int B16_FM = 8, B16_FN = 4;
-constexpr int kB16WM = 128, kB16WN = 64;       // wave sub-tile (2 x 4 waves)
-
-#ifndef ADAHOP_FP4_BLK16
-#define ADAHOP_FP4_BLK16 0
-#endif
-constexpr bool kFp4Blk16 = ADAHOP_FP4_BLK16 != 0;
-
-// Inner extraction on 16 x 16 blocks: C += a[:, 0:k] * b[:, 0:k]^T with
-// v_mfma_f32_16x16x32_bf16, 32 extracted lines per MFMA (lane l: row l % 16,
-// lines 8 (l / 16) .. +7).
-__device__ __forceinline__ void gemm_inner_term16(const GemmArgs& g, v4f (&acc)[B16_FM][B16_FN],
-                                                  int64_t m0, int64_t n0) {
-  if (g.oe_mode != ADAHOP_ROUTE_OE_INNER) return;
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int wm = wave >> 2, wn = wave & 3;
-  const int r16 = lane & 15, c16 = lane >> 4;
-  for (int p0 = 0; p0 < g.oe_k; p0 += 32) {
-    v8bf fa[B16_FM], fb[B16_FN];
-#pragma unroll
-    for (int i = 0; i < B16_FM; ++i) {
-      int64_t row = m0 + wm * kB16WM + i * 16 + r16;
-      row = row < g.m ? row : g.m - 1;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int p = p0 + 8 * c16 + e;
-        const uint16_t h = p < g.oe_k ? view_at(g.ia_ptr, g.ia_ld, g.ia_inner, row, p) : 0;
-        fa[i][e] = __builtin_bit_cast(__bf16, h);
-      }
-    }
-#pragma unroll
-    for (int j = 0; j < B16_FN; ++j) {
-      int64_t col = n0 + wn * kB16WN + j * 16 + r16;
-      col = col < g.n ? col : g.n - 1;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int p = p0 + 8 * c16 + e;
-        const uint16_t h = p < g.oe_k ? view_at(g.ib_ptr, g.ib_ld, g.ib_inner, col, p) : 0;
-        fb[j][e] = __builtin_bit_cast(__bf16, h);
-      }
-    }
-    static_for<B16_FM>([&](auto I) {
-      static_for<B16_FN>([&](auto J) {
-        acc[I][J] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fb[J], fa[I], acc[I][J], 0, 0, 0);
-      });
-    });
-  }
-}
-
-// Outer-extraction scatter-add, one rounding, stores of the 16 x 16 blocks
-// (the rules of gemm_store: OE_LEFT / OE_RIGHT add the outlier product, or
-// capture the extracted lines' residual in oe_res).
-__device__ __forceinline__ void gemm_store16(const GemmArgs& g, v4f (&acc)[B16_FM][B16_FN],
-                                             int64_t m0, int64_t n0, int* s_pos) {
-  constexpr int kThreads = 512;
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int wm = wave >> 2, wn = wave & 3;
-  const int r16 = lane & 15, c16 = lane >> 4;
-  const bool oe_rows = g.oe_mode == ADAHOP_ROUTE_OE_LEFT;
-  const bool oe_cols = g.oe_mode == ADAHOP_ROUTE_OE_RIGHT;
-  bool any_oe = false;
-  if (oe_rows || oe_cols) {
-    const int64_t lo_v = oe_rows ? m0 : n0;
-    const int64_t span = oe_rows ? BM : BN;
-    const int lo = lower_bound_i32(g.oe_idx, g.oe_k, lo_v);
-    const int hi = lower_bound_i32(g.oe_idx, g.oe_k, lo_v + span);
-    any_oe = hi > lo;
-    if (any_oe) {
-      for (int q = tid; q < span; q += kThreads) s_pos[q] = -1;
-      __syncthreads();
-      for (int p = lo + tid; p < hi; p += kThreads) s_pos[g.oe_idx[p] - lo_v] = p;
-      __syncthreads();
-    }
-  }
-  const bool full = m0 + BM <= g.m && n0 + BN <= g.n && g.vec_ok;
-  const int lc0 = wn * kB16WN + 4 * c16;                 // tile column of (J, e) = lc0 + 16 J + e
-  const int64_t col0 = n0 + lc0;
-  // bf16 stores: after the row swap below, row c16 of the wave holds the 8
-  // columns 16 (c16 & 1) + 8 (c16 >> 1) .. +7 of each pair of blocks.
-  const int sc0 = wn * kB16WN + 16 * (c16 & 1) + 8 * (c16 >> 1);
-  static_for<B16_FM>([&](auto I) {
-    const int lr = wm * kB16WM + I * 16 + r16;
-    const int64_t row = m0 + lr;
-    const int prow = (any_oe && oe_rows) ? s_pos[lr] : -1;
-    const float* oe_row = nullptr;
-    float* res_row = nullptr;
-    if (any_oe && row < g.m) {
-      if (g.oe_res) {
-        if (oe_rows) { if (prow >= 0) res_row = g.oe_res + (int64_t)prow * g.n + col0; }
-        else res_row = g.oe_res + row * g.oe_k;
-      } else if (oe_rows) {
-        if (prow >= 0) oe_row = g.oe_p + (int64_t)prow * g.n + col0;
-      } else {
-        oe_row = g.oe_p + row * g.oe_k;
-      }
-    }
-    const int64_t off = row * g.ldc + col0;
-    float* cf = static_cast<float*>(g.C) + off;
-    uint16_t* cb = static_cast<uint16_t*>(g.C) + off;
-    float v[B16_FN][4];
-    static_for<B16_FN>([&](auto J) {
-      constexpr int dc = 16 * decltype(J)::value;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) v[J][e] = acc[I][J][e];
-      if (oe_row != nullptr) {
-        if (oe_rows) {
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            if (col0 + dc + e < g.n) v[J][e] += oe_row[dc + e];
-        } else {
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int p = lc0 + dc + e < BN ? s_pos[lc0 + dc + e] : -1;
-            if (p >= 0) v[J][e] += oe_row[p];
-          }
-        }
-      } else if (res_row != nullptr) {
-        if (oe_rows) {
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            if (col0 + dc + e < g.n) res_row[dc + e] = v[J][e];
-        } else {
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int p = lc0 + dc + e < BN ? s_pos[lc0 + dc + e] : -1;
-            if (p >= 0) res_row[p] = v[J][e];
-          }
-        }
-      }
-    });
-    if (full && !g.out_f32) {
-      // Rows of 16 lanes (c16 = 0 .. 3) hold the same C rows, columns
-      // 4 c16 .. +3 of blocks 2 P and 2 P + 1. Swapping the odd rows of the
-      // first block's dword with the even rows of the second's leaves rows
-      // 0 / 2 with columns 0 .. 7 / 8 .. 15 of block 2 P and rows 1 / 3 with
-      // columns 0 .. 7 / 8 .. 15 of block 2 P + 1: 16 contiguous bytes per lane.
-      uint16_t* cbs = static_cast<uint16_t*>(g.C) + row * g.ldc + n0 + sc0;
-      static_for<B16_FN / 2>([&](auto P) {
-        constexpr int q = 2 * decltype(P)::value;
-        const auto a = __builtin_amdgcn_permlane16_swap(pack_bf16x2(v[q][0], v[q][1]),
-                                                        pack_bf16x2(v[q + 1][0], v[q + 1][1]), false, false);
-        const auto b = __builtin_amdgcn_permlane16_swap(pack_bf16x2(v[q][2], v[q][3]),
-                                                        pack_bf16x2(v[q + 1][2], v[q + 1][3]), false, false);
-        *reinterpret_cast<uint4*>(cbs + 32 * decltype(P)::value) = make_uint4(a[0], b[0], a[1], b[1]);
-      });
-    } else {
-      static_for<B16_FN>([&](auto J) {
-        constexpr int dc = 16 * decltype(J)::value;
-        if (full) {
-          *reinterpret_cast<float4*>(cf + dc) = make_float4(v[J][0], v[J][1], v[J][2], v[J][3]);
-        } else if (row < g.m) {
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            if (col0 + dc + e >= g.n) continue;
-            if (g.out_f32)
-              cf[dc + e] = v[J][e];
-            else
-              cb[dc + e] = f32_to_bf16_rne(v[J][e]);
-          }
-        }
-      });
-    }
-  });
-}
-
 // Persistent: one workgroup per CU (gridDim.x <= number of items) takes the
 // work items r * gridDim.x + p(b), r = 0, 1, ..., where p spreads each round
 // over the XCDs in contiguous bands (xcd_band). Whole tiles come first, the
@@ -815,15 +637,10 @@ __device__ __forceinline__ void gemm_store16(const GemmArgs& g, v4f (&acc)[B16_F
 // 32-column block, so lane 16 G + i receives column 16 (G % 2) + i, K-rows
 // 8 (G / 2) + 4 r .. +3: the MFMA's layout. The swizzle puts the 8 K-rows
 // one read touches in 8 different 64-byte column groups.
-//
-// Blk16 (FP4 only): the tile is computed on 16 x 16 blocks (see
-// gemm_store16), one 16x16x128 MFMA per block per stage.
-template <bool Chunked, bool Bf16, bool TA = false, bool TB = false, bool Blk16 = false>
+template <bool Chunked, bool Bf16, bool TA = false, bool TB = false>
 __global__ void __launch_bounds__(kRing8Threads, 1) gemm_mx_ring8_kernel(GemmArgs g) {
   static_assert(!(Chunked && Bf16), "bf16 operands come in rows");
   static_assert(Bf16 || (!TA && !TB), "only bf16 operands are read across K");
-  static_assert(!(Blk16 && Bf16), "16 x 16 blocks only for FP4 operands");
-  static_assert(B16_FM * 16 == R8_WM && B16_FN * 16 == R8_WN, "same wave sub-tile");
   constexpr int kLoads = Bf16 ? 4 : kLoads8PerStage;   // per wave per stage
   // LDS reads per K-step: fragments (two per operand block stored across K)
   // and, for FP4, the scale words.
@@ -975,19 +792,14 @@ __global__ void __launch_bounds__(kRing8Threads, 1) gemm_mx_ring8_kernel(GemmArg
                                                  4, it.soff, kt * sstage, 0, 0);
     }
   };
-  // A tile's first stages: kt0 .. kt0+2 whole and, on 32 x 32 blocks, the
-  // first kLoads - 2 loads of kt0+3 (its stage kt0 issues the rest); on
-  // 16 x 16 blocks all of kt0+3.
-  constexpr int kFirstLoads = Blk16 ? 4 * kLoads : 4 * kLoads - 2;
+  // A tile's first stages: kt0 .. kt0+2 whole and the first kLoads - 2
+  // loads of kt0+3 (its stage kt0 issues the rest).
+  constexpr int kFirstLoads = 4 * kLoads - 2;
   auto issue_first = [&](const RingItem& it) {
     issue(it, std::integral_constant<int, 0>{}, it.kt0);
     issue(it, std::integral_constant<int, 1>{}, it.kt0 + 1);
     issue(it, std::integral_constant<int, 2>{}, it.kt0 + 2);
-    if constexpr (Blk16) {
-      issue(it, std::integral_constant<int, 3>{}, it.kt0 + 3);
-    } else {
-      static_for<kLoads - 2>([&](auto Q) { issue_one(it, std::integral_constant<int, 3>{}, Q, it.kt0 + 3); });
-    }
+    static_for<kLoads - 2>([&](auto Q) { issue_one(it, std::integral_constant<int, 3>{}, Q, it.kt0 + 3); });
   };
 
   v16f acc[R8_FM][R8_FN];
@@ -1139,92 +951,6 @@ __global__ void __launch_bounds__(kRing8Threads, 1) gemm_mx_ring8_kernel(GemmArg
     __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
     __builtin_amdgcn_sched_barrier(0);
     keep(y);
-  };
-
-  // 16 x 16 blocks: lane l reads row l % 16 of a block and its logical
-  // 16-byte chunk l / 16 (K-block l / 16 of the stage), and that K-block's
-  // scale, which a row's stage scale word keeps at byte {0, 2, 1, 3}[l / 16].
-  // A block row (16 rows of A) is 1 KB of a slot, as is a block column of B.
-  v4f acc16[B16_FM][B16_FN];
-  const int r16 = lane & 15, c16 = lane >> 4;
-  const int sw16 = (c16 ^ ring_swz(r16)) << 4;
-  const int fa16 = (wm * R8_WM + r16) * RBK + sw16, fb16 = (wn * R8_WN + r16) * RBK + sw16;
-  const int bpos = ((c16 & 1) << 1) | (c16 >> 1);
-  const int sa16 = (wm * R8_WM + r16) * 4 + bpos, sb16 = (wn * R8_WN + r16) * 4 + bpos;
-  struct AFrags16 {
-    v4i a[B16_FM];
-    int sa[B16_FM];
-  };
-  struct BFrags16 {
-    v4i b[B16_FN];
-    int sb[B16_FN];
-  };
-  auto read_b16 = [&](auto S, BFrags16& f) {
-    constexpr int slot = decltype(S)::value;
-#pragma unroll
-    for (int j = 0; j < B16_FN; ++j) {
-      f.b[j] = *reinterpret_cast<const v4i*>(&ring_slot<slot>().b[fb16 + 1024 * j]);
-      f.sb[j] = ring_slot<slot>().sb[sb16 + 64 * j];
-    }
-  };
-  auto read_a16 = [&](auto S, auto I, AFrags16& f) {
-    constexpr int slot = decltype(S)::value;
-    constexpr int i = decltype(I)::value;
-    f.a[i] = *reinterpret_cast<const v4i*>(&ring_slot<slot>().a[fa16 + 1024 * i]);
-    f.sa[i] = ring_slot<slot>().sa[sa16 + 64 * i];
-  };
-  // The 4 MFMAs of block row i.
-  auto mma16 = [&](const AFrags16& a, const BFrags16& b, auto I) {
-    constexpr int i = decltype(I)::value;
-    static_for<B16_FN>([&](auto J) {
-      const v4i fb = b.b[J], fa = a.a[i];
-      acc16[i][J] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-          v8i{fb[0], fb[1], fb[2], fb[3], 0, 0, 0, 0}, v8i{fa[0], fa[1], fa[2], fa[3], 0, 0, 0, 0},
-          acc16[i][J], 4, 4, 0, b.sb[J], 0, a.sa[i]);
-    });
-  };
-  // Stage kt (slot S) with all its fragments in registers (a, x; read during
-  // stage kt - 1): the MFMAs of block rows 0 .. kPre - 1; then wait until
-  // only this wave's loads of stages kt+2, kt+3 are in flight and its LDS
-  // reads are back, and sync: stage kt+1 is published and no wave reads slot
-  // S any more. Refill slot S with stage kt+4 (past kt1: a re-load of the
-  // last stage) while no LDS read is in flight (an LDS-DMA load waits for
-  // those), read stage kt+1's B fragments into y and its A fragments of
-  // block rows 0 .. kPre - 1 into a, then run block rows kPre .. 7, reading
-  // stage kt+1's A fragment of each once its MFMAs have been issued (the A
-  // fragments are single-buffered: the registers for a second set are not
-  // there). The last such read has kPre block rows of MFMAs to arrive before
-  // the next stage's wait.
-  constexpr int kPre = 2;
-  auto stage16 = [&](const RingItem& it, auto S, AFrags16& a, BFrags16& x, BFrags16& y, int kt) {
-    constexpr int slot = decltype(S)::value;
-    using NS = std::integral_constant<int, (slot + 1) % kRingSlots>;
-    static_for<kPre>([&](auto I) { mma16(a, x, I); });
-    __builtin_amdgcn_sched_barrier(0);
-    __builtin_amdgcn_s_waitcnt(waitcnt_imm(2 * kLoads, 0));
-    __builtin_amdgcn_s_barrier();
-    __builtin_amdgcn_sched_barrier(0);
-    issue(it, std::integral_constant<int, slot>{}, kt + 4 < it.kt1 ? kt + 4 : it.kt1 - 1);
-    __builtin_amdgcn_sched_barrier(0);
-    read_b16(NS{}, y);
-    static_for<kPre>([&](auto I) { read_a16(NS{}, I, a); });
-    mma16(a, x, std::integral_constant<int, kPre>{});
-    static_for<4>([&](auto) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
-      __builtin_amdgcn_sched_group_barrier(0x100, 2 + kPre / 2, 0);   // LDS reads
-    });
-    __builtin_amdgcn_sched_barrier(0);
-    static_for<B16_FM - kPre - 1>([&](auto Q) {
-      constexpr int i = decltype(Q)::value + kPre + 1;
-      read_a16(NS{}, std::integral_constant<int, i - 1>{}, a);
-      mma16(a, x, std::integral_constant<int, i>{});
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-      __builtin_amdgcn_sched_group_barrier(0x008, 3, 0);
-      __builtin_amdgcn_sched_barrier(0);
-    });
-    read_a16(NS{}, std::integral_constant<int, B16_FM - 1>{}, a);
-    __builtin_amdgcn_sched_barrier(0);
   };
 
   // The outer outlier product's items (FP4 kernel with oe_items > 0): each
@@ -1416,45 +1142,6 @@ __global__ void __launch_bounds__(kRing8Threads, 1) gemm_mx_ring8_kernel(GemmArg
     }
     const int item = work;
     const RingItem cur = setup(item);
-    if constexpr (Blk16) {
-      static_for<B16_FM>([&](auto I) {
-        static_for<B16_FN>([&](auto J) {
-#pragma unroll
-          for (int v = 0; v < 4; ++v) acc16[I][J][v] = 0.0f;
-        });
-      });
-      AFrags16 fa;
-      BFrags16 fx, fy;
-      __builtin_amdgcn_s_waitcnt(waitcnt_imm(3 * kLoads, 0));
-      __builtin_amdgcn_s_barrier();
-      __builtin_amdgcn_sched_barrier(0);
-      read_b16(std::integral_constant<int, 0>{}, fx);
-      static_for<B16_FM>([&](auto I) { read_a16(std::integral_constant<int, 0>{}, I, fa); });
-      for (int kt = cur.kt0; kt < cur.kt1; kt += kRingSlots) {
-        stage16(cur, std::integral_constant<int, 0>{}, fa, fx, fy, kt);
-        stage16(cur, std::integral_constant<int, 1>{}, fa, fy, fx, kt + 1);
-        stage16(cur, std::integral_constant<int, 2>{}, fa, fx, fy, kt + 2);
-        stage16(cur, std::integral_constant<int, 3>{}, fa, fy, fx, kt + 3);
-      }
-      __builtin_amdgcn_sched_barrier(0);
-      __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
-      __syncthreads();
-      const int next = work_at(q + 1);
-      issue_work(next);
-      if (cur.part <= 0) gemm_inner_term16(g, acc16, cur.m0, cur.n0);
-      GemmArgs ge = g;
-      int64_t em0 = cur.m0, en0 = cur.n0;
-      if (cur.part >= 0) {
-        ge.C = g.split_ws + ((size_t)cur.split_tile * g.split_parts + cur.part) * (size_t)(BM * BN);
-        ge.ldc = BN; ge.m = BM; ge.n = BN; ge.out_f32 = 1; ge.vec_ok = 1; ge.oe_mode = 0;
-        em0 = 0; en0 = 0;
-      }
-      gemm_store16(ge, acc16, em0, en0, g_ring_pos);
-      if (next == kNoWork) break;
-      __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
-      work = next;
-      continue;
-    }
     static_for<R8_FM>([&](auto I) {
       static_for<R8_FN>([&](auto J) {
 #pragma unroll
@@ -2127,9 +1814,9 @@ adahop_status gemm_mx_launch(const uint8_t* a_codes, const uint8_t* a_scales,
     if (g.oe_items > wgs) wgs = g.oe_items;
     const dim3 rgrid((unsigned)wgs);
     if (kchunk)
-      gemm_mx_ring8_kernel<true, false, false, false, kFp4Blk16><<<rgrid, dim3(kRing8Threads), 0, stream>>>(g);
+      gemm_mx_ring8_kernel<true, false><<<rgrid, dim3(kRing8Threads), 0, stream>>>(g);
     else
-      gemm_mx_ring8_kernel<false, false, false, false, kFp4Blk16><<<rgrid, dim3(kRing8Threads), 0, stream>>>(g);
+      gemm_mx_ring8_kernel<false, false><<<rgrid, dim3(kRing8Threads), 0, stream>>>(g);
     {
       const adahop_status ls = record_main_done(main_done, stream, "gemm_mx");
       if (ls != ADAHOP_OK) return ls;
