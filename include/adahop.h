@@ -160,8 +160,10 @@ ADAHOP_API adahop_pattern adahop_classify_pattern(const double* row_scores, int6
  * (device int32[k]) in ascending order. Deterministic. Needs
  * adahop_detect_workspace_size(...) bytes of workspace: none up to 1024
  * candidates (4096 when k > 256), else the survivor lists of the selection
- * levels (k scores and indices per chunk of 1024, or 4096, candidates; two
- * lists) and 256 bytes for a counter; ws may be NULL when the size is 0.
+ * levels (k scores and indices per chunk of candidates: 256 or 512 when the
+ * first level's survivors then fit in 1024 entries, else 1024, or 4096
+ * when k > 256; two lists) and 256 bytes for a counter; ws may be NULL when
+ * the size is 0.
  * Errors: INVALID if t/idx_out is NULL, rows/cols < 1, ld < cols, probe < 1,
  * k < 1 or k > number of candidates; UNSUPPORTED if k > 1024. */
 ADAHOP_API size_t adahop_detect_workspace_size(int64_t rows, int64_t cols, adahop_axis axis,

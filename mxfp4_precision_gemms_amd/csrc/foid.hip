@@ -10,7 +10,11 @@
 // are read coalesced (consecutive lanes = consecutive columns); a candidate
 // row is one 128-byte run, read as 8 16-byte loads when aligned. With the
 // full 64-element probe the values stay in registers between the two passes.
-// The first selection level computes the scores itself, in registers;
+// The first selection level computes the scores itself, in registers. The
+// score arithmetic (about 500 vector instructions per candidate) bounds
+// that step, so with few candidates the level takes chunks of 256 or 512 on
+// more workgroups, one candidate per thread, as long as their survivors
+// still fit one final workgroup;
 // line_scores_kernel writes every candidate's score out on its own (the
 // pattern calibration's input).
 //
@@ -188,10 +192,12 @@ struct SelectArgs {
   int k;
   double* out_var; int32_t* out_idx;   // non-final: k entries per workgroup
   int32_t* final_idx;                  // final (one workgroup): the k indices, ascending
+  int64_t chunk;                       // entries per workgroup, <= 512 KPT
 };
 
-// Selection over chunks of 512 * KPT entries per workgroup, thread t owning
-// entries 512 * KPT * b + KPT t .. + KPT - 1 in index order. Radix select
+// Selection over chunks of a.chunk <= 512 * KPT entries per workgroup,
+// thread t owning entries a.chunk * b + KPT t .. + KPT - 1 in index order
+// (threads past the chunk own none). Radix select
 // on the fp64 score bits (scores are >= 0, so their bit patterns order like
 // the values), 4 bits per pass from the top: each wave counts its keys in the
 // current bin per next digit with ballots and writes the 16 counts to LDS,
@@ -220,10 +226,12 @@ __device__ __forceinline__ void select_block(const SelectArgs& a, int block,
                                              uint32_t (*s_cnt)[kSelWaves][16], int* s_tmp,
                                              bool write_through = false) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int64_t first = (int64_t)block * kSelThreads * KPT + (int64_t)tid * KPT;
+  const int64_t first = (int64_t)block * a.chunk + (int64_t)tid * KPT;
+  const int64_t cend = (int64_t)block * a.chunk + a.chunk;
+  const int64_t end = cend < a.count ? cend : a.count;
 
   double v[KPT];
-  const bool pair = KPT == 2 && a.t && a.P == kProbe && first + 1 < a.count &&
+  const bool pair = KPT == 2 && a.t && a.P == kProbe && first + 1 < end &&
                     (a.axis == ADAHOP_AXIS_COLS
                          ? (a.ld & 1) == 0 && (reinterpret_cast<uintptr_t>(a.t) & 3) == 0
                          : (a.ld & 7) == 0 && (reinterpret_cast<uintptr_t>(a.t) & 15) == 0);
@@ -234,7 +242,7 @@ __device__ __forceinline__ void select_block(const SelectArgs& a, int block,
     for (int j = 0; j < KPT; ++j) {
       const int64_t g = first + j;
       v[j] = -1.0;
-      if (g < a.count) v[j] = a.t ? candidate_variance(a.t, a.ld, a.axis, a.P, g) : a.in_var[g];
+      if (g < end) v[j] = a.t ? candidate_variance(a.t, a.ld, a.axis, a.P, g) : a.in_var[g];
     }
   }
   uint64_t key[KPT];
@@ -258,15 +266,19 @@ __device__ __forceinline__ void select_block(const SelectArgs& a, int block,
     // d < 16 keeps the keys whose 4 bits spell d and counts them. Its row of
     // the pass's buffer is written once; the buffers alternate, so a row is
     // rewritten only after the barrier that ends every wave's reads of it.
+    // (The ballot of a digit bit is taken on its own and masked with the
+    // bin's ballot in scalar registers: a ballot of the conjunction compiles
+    // to a select and a second compare per bit.)
     uint32_t mine = 0;
 #pragma unroll
     for (int j = 0; j < KPT; ++j) {
       const bool in = ((valid >> j) & 1u) && (key[j] & pmask) == prefix;
       const uint32_t dj = (uint32_t)(key[j] >> shift) & 15u;
-      uint64_t m = __builtin_amdgcn_ballot_w64(in);
+      const uint64_t inm = __builtin_amdgcn_ballot_w64(in);
+      uint64_t m = inm;
 #pragma unroll
       for (int bit = 0; bit < 4; ++bit) {
-        const uint64_t bm = __builtin_amdgcn_ballot_w64(in && ((dj >> bit) & 1u));
+        const uint64_t bm = __builtin_amdgcn_ballot_w64((dj & (1u << bit)) != 0u) & inm;
         m &= ((lane >> bit) & 1) ? bm : ~bm;
       }
       mine += (uint32_t)__popcll(m);
@@ -312,7 +324,7 @@ __device__ __forceinline__ void select_block(const SelectArgs& a, int block,
   if (!keep_all && !bin_kept) {
     // All 16 digits decided: prefix is T; the first krem keys equal to T.
     int eq_total;
-    const int eq_before = block_exclusive_scan<kSelThreads, KPT == 2 ? 2 : 4>(__popc(eq), s_tmp, &eq_total);
+    const int eq_before = block_exclusive_scan<kSelThreads, KPT == 1 ? 1 : KPT == 2 ? 2 : 4>(__popc(eq), s_tmp, &eq_total);
     int take = krem - eq_before;
 #pragma unroll
     for (int j = 0; j < KPT; ++j) {
@@ -320,7 +332,7 @@ __device__ __forceinline__ void select_block(const SelectArgs& a, int block,
     }
   }
   int kept;
-  int pos = block_exclusive_scan<kSelThreads, KPT == 2 ? 2 : 4>(__popc(keep), s_tmp, &kept);
+  int pos = block_exclusive_scan<kSelThreads, KPT == 1 ? 1 : KPT == 2 ? 2 : 4>(__popc(keep), s_tmp, &kept);
 
   if (a.final_idx != nullptr) {
 #pragma unroll
@@ -368,7 +380,7 @@ __device__ __forceinline__ void select_block(const SelectArgs& a, int block,
 // back the L2 costs 2-11 us per workgroup while a quantizer's output sits
 // dirty in it. No workgroup waits for another, and the final selection
 // starts as soon as the level ends, without a second dispatch.
-template <int KPT>
+template <int KPT, int FKPT = KPT>
 __global__ void __launch_bounds__(kSelThreads) foid_select_kernel(SelectArgs a, SelectArgs fin,
                                                                   unsigned* counter) {
   __shared__ uint32_t s_cnt[2][kSelWaves][16];
@@ -388,7 +400,7 @@ __global__ void __launch_bounds__(kSelThreads) foid_select_kernel(SelectArgs a, 
   __syncthreads();
   if (!s_last) return;
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-  select_block<KPT>(fin, 0, s_cnt, s_tmp);
+  select_block<FKPT>(fin, 0, s_cnt, s_tmp);
 }
 
 __global__ void foid_zero_kernel(unsigned* counter) { *counter = 0u; }
@@ -406,13 +418,25 @@ __global__ void __launch_bounds__(256) line_scores_kernel(const uint16_t* __rest
 // workgroup takes up to 1024 entries (2 per thread), or 4096 when k > 256.
 int64_t level_chunk(int32_t k) { return k <= 256 ? 1024 : 4096; }
 int64_t final_cap(int32_t k) { return k <= 256 ? 1024 : 4096; }
-int64_t chunks_of(int64_t n, int32_t k) { return (n + level_chunk(k) - 1) / level_chunk(k); }
+// The first level's chunk: 256 or 512 candidates (one per thread) when
+// that many chunks still leave at most final_cap survivors, else
+// level_chunk.
+int64_t first_chunk(int64_t n, int32_t k) {
+  if (k <= 256) {
+    for (int64_t c = 256; c <= 512; c *= 2)
+      if (c >= 4 * (int64_t)k && (n + c - 1) / c * k <= final_cap(k)) return c;
+  }
+  return level_chunk(k);
+}
+int64_t chunks_of(int64_t n, int64_t chunk) { return (n + chunk - 1) / chunk; }
 
 adahop_status launch_select(bool final_level, const SelectArgs& a, const SelectArgs& fin,
                             unsigned* counter, hipStream_t stream) {
-  const unsigned nb = final_level ? 1u : (unsigned)chunks_of(a.count, a.k);
+  const unsigned nb = final_level ? 1u : (unsigned)chunks_of(a.count, a.chunk);
   if (a.k > 256)
     foid_select_kernel<8><<<nb, kSelThreads, 0, stream>>>(a, fin, counter);
+  else if (a.chunk <= kSelThreads)
+    foid_select_kernel<1, 2><<<nb, kSelThreads, 0, stream>>>(a, fin, counter);
   else
     foid_select_kernel<2><<<nb, kSelThreads, 0, stream>>>(a, fin, counter);
   return check_launch("foid_select");
@@ -431,13 +455,15 @@ adahop_status line_scores_launch(const uint16_t* t, int64_t rows, int64_t cols, 
   return check_launch("line_scores");
 }
 
-bool foid_fits(int64_t ncand, int32_t k) { return ncand >= 1 && k >= 1 && chunks_of(ncand, k) <= 0x7FFFFFFF; }
+bool foid_fits(int64_t ncand, int32_t k) {
+  return ncand >= 1 && k >= 1 && chunks_of(ncand, first_chunk(ncand, k)) <= 0x7FFFFFFF;
+}
 
 size_t foid_workspace_bytes(int64_t ncand, int32_t k) {
   if (ncand <= final_cap(k)) return 0;
   // The levels' survivors, double buffered (level 0 scores in registers),
   // then the counter of the level that runs the final selection.
-  const size_t entries = (size_t)chunks_of(ncand, k) * (size_t)k;
+  const size_t entries = (size_t)chunks_of(ncand, first_chunk(ncand, k)) * (size_t)k;
   return 2 * (align_up(entries * sizeof(double), kAlign) + align_up(entries * sizeof(int32_t), kAlign)) +
          kAlign;
 }
@@ -454,13 +480,14 @@ adahop_status foid_launch(const uint16_t* t, int64_t rows, int64_t cols, int64_t
                                           std::to_string(need) + " bytes)");
   if (!foid_fits(ncand, k))
     return fail(ADAHOP_ERR_UNSUPPORTED, "adahop_detect: too many candidates");
-  SelectArgs a{t, ld, axis, P, nullptr, nullptr, ncand, k, nullptr, nullptr, nullptr};
+  SelectArgs a{t, ld, axis, P, nullptr, nullptr, ncand, k, nullptr, nullptr, nullptr, first_chunk(ncand, k)};
   const SelectArgs none{};
   if (ncand <= final_cap(k)) {
+    a.chunk = final_cap(k);
     a.final_idx = idx_out;
     return launch_select(true, a, none, nullptr, stream);
   }
-  const size_t entries = (size_t)chunks_of(ncand, k) * (size_t)k;
+  const size_t entries = (size_t)chunks_of(ncand, a.chunk) * (size_t)k;
   char* p = static_cast<char*>(ws);
   double* var_buf[2];
   int32_t* idx_buf[2];
@@ -478,8 +505,8 @@ adahop_status foid_launch(const uint16_t* t, int64_t rows, int64_t cols, int64_t
   while (true) {
     a.out_var = var_buf[cur];
     a.out_idx = idx_buf[cur];
-    const SelectArgs next{nullptr, 0, 0, 0, var_buf[cur], idx_buf[cur], chunks_of(a.count, k) * k, k,
-                          nullptr, nullptr, nullptr};
+    const SelectArgs next{nullptr, 0, 0, 0, var_buf[cur], idx_buf[cur], chunks_of(a.count, a.chunk) * k, k,
+                          nullptr, nullptr, nullptr, level_chunk(k)};
     if (next.count <= final_cap(k)) {
       SelectArgs fin = next;
       fin.final_idx = idx_out;

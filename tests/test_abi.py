@@ -171,7 +171,7 @@ def test_gemm_mx_outlier_descriptor_checked_before_any_launch():
 
 def test_workspace_sizes():
     # Scores stay in registers; survivor lists (fp64 score + int32 index, k per
-    # chunk of 1024 candidates, two lists, each array rounded up to 256 bytes)
+    # chunk of candidates, two lists, each array rounded up to 256 bytes)
     # when one workgroup cannot take every candidate.
     assert A.adahop_detect_workspace_size(100, 64, "ROWS", 10) == 0
     assert A.adahop_detect_workspace_size(64, 1024, "COLS", 64) == 0
@@ -179,6 +179,12 @@ def test_workspace_sizes():
     surv = lambda e: 2 * (r256(8 * e) + r256(4 * e)) + 256      # + a 256-byte counter slot
     assert A.adahop_detect_workspace_size(65536, 64, "ROWS", 64) == surv(64 * 64)
     assert A.adahop_detect_workspace_size(64, 14336, "COLS", 64) == surv(14 * 64)
+    # few candidates: the first level takes chunks of 256 (or 512) while the
+    # survivors still fit one final workgroup (1024 entries)
+    assert A.adahop_detect_workspace_size(4096, 64, "ROWS", 64) == surv(16 * 64)
+    assert A.adahop_detect_workspace_size(4097, 64, "ROWS", 64) == surv(9 * 64)
+    assert A.adahop_detect_workspace_size(64, 8192, "COLS", 64) == surv(16 * 64)
+    assert A.adahop_detect_workspace_size(2000, 64, "ROWS", 200) == surv(2 * 200)
     # k > 256: chunks of 4096
     assert A.adahop_detect_workspace_size(20000, 64, "ROWS", 300) == surv(5 * 300)
     ws = A.adahop_gemm_workspace_size("WGRAD", 32768, 14336, 4096, "R", "C", None, 64)

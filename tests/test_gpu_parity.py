@@ -133,9 +133,11 @@ FOID_CASES = [
     (96, 256, "ROWS", 7, 16, True),          # shorter probe
     (64, 14336, "COLS", 64, 64, False),      # Llama3.1-8B d_ff columns: 14 chunks, then one
     (1024, 64, "ROWS", 64, 64, True),        # exactly one chunk: scores and selection in one launch
-    (64, 4096, "COLS", 64, 64, False),       # four chunks, then the final workgroup
-    (3000, 64, "ROWS", 32, 64, True),        # the same with a ragged last chunk, ties
+    (64, 4096, "COLS", 64, 64, False),       # 16 chunks of 256 (one candidate per thread), then the final workgroup
+    (3000, 64, "ROWS", 32, 64, True),        # chunks of 256 with a ragged last chunk, ties
     (2500, 96, "ROWS", 64, 16, False),       # the same with a short probe (one candidate at a time)
+    (64, 8192, "COLS", 64, 64, True),        # 16 chunks of 512, one candidate per thread, ties
+    (4097, 64, "ROWS", 64, 64, False),       # 9 chunks of 512, the last holding one candidate
 ]
 
 
