@@ -1135,7 +1135,6 @@ __global__ void __launch_bounds__(kRing8Threads, 1) gemm_mx_ring8_kernel(GemmArg
           }
         }
         if (next == kNoWork) break;
-        __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
         work = next;
         continue;
       }
@@ -1182,9 +1181,12 @@ __global__ void __launch_bounds__(kRing8Threads, 1) gemm_mx_ring8_kernel(GemmArg
     }
     gemm_store<R8_FM, R8_FN, R8_WM, R8_WN, 4, kRing8Threads>(ge, acc, em0, en0, g_ring_pos);
     if (next == kNoWork) break;
-    // The stores and the epilogue's loads are not ordered with the next
-    // item's ring loads in the counter: wait for all of them.
-    __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
+    // No wait for the epilogue's stores here: the next item's waits count
+    // only ring loads issued after the ones they wait for, and loads return
+    // in order, so stores (or epilogue loads) still in flight can only make
+    // those waits stricter, never let one pass early. The stores drain
+    // while the next item starts (a wait here cost 1-9 % of the GEMM on
+    // short-K shapes, where every CU stores its tile at the same moment).
     work = next;
   }
 }
