@@ -26,7 +26,8 @@
 // a strict total order, so the result is unique. A prefix sum over the
 // threads, which own the candidates in index order, writes the kept indices
 // already sorted. Levels of many workgroups first cut every chunk of 1024
-// candidates (4096 when k > 256) to its best k, until one workgroup can take
+// candidates (the first level 256 or 512 when that leaves few enough
+// survivors; 4096 when k > 256) to its best k, until one workgroup can take
 // the rest.
 #include <climits>
 

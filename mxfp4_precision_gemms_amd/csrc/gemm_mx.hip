@@ -17,7 +17,8 @@
 //   8 tile-rows high, whose operand rows its L2 shares.
 // Main kernel (gemm_mx_ring8_kernel, K % 512 == 0): K advances 128 elements
 //   per stage through a 4-slot LDS ring filled by direct global->LDS buffer
-//   loads four stages ahead; the scales come K-chunked from the quantizers
+//   loads up to three stages ahead, a stage's loads spread over the MFMAs
+//   between two workgroup barriers; the scales come K-chunked from the quantizers
 //   or from a stage-major copy made just before (scale_stage_kernel). One
 //   workgroup runs per CU; a last round of tiles that would leave more than
 //   half of the 256 CUs idle is split along K, and gemm_split_fixup_kernel
@@ -534,8 +535,8 @@ __global__ void __launch_bounds__(kGemmThreads, 1) gemm_mx_kernel(GemmArgs g) {
 
 // ---------------------------------------------------------------------------
 // Main kernel for K % 512 == 0 (gemm_mx_ring8_kernel): a 4-slot LDS ring
-// filled by direct global->LDS buffer loads (no staging registers), four
-// stages ahead of the matrix cores. Stage = 128 K-elements: A and B 256 rows x
+// filled by direct global->LDS buffer loads (no staging registers), up to
+// three stages ahead of the matrix cores. Stage = 128 K-elements: A and B 256 rows x
 // 64 bytes each plus 4 scale bytes per row. Before a stage is read, every
 // wave waits until only its loads of the two later stages are in flight, then
 // the workgroup barrier publishes the stage. LDS rows of 64 bytes keep their
@@ -615,8 +616,8 @@ struct RingItem {
 // work items r * gridDim.x + p(b), r = 0, 1, ..., where p spreads each round
 // over the XCDs in contiguous bands (xcd_band). Whole tiles come first, the
 // split parts of the last round after them. Before a tile's epilogue the
-// next item's first four stages are already in flight, so the ring refills
-// while the accumulators are stored.
+// next item's first stages (three, and two of the fourth's loads) are
+// already in flight, so the ring refills while the accumulators are stored.
 //
 // Bf16: the operands are plain bf16 rows (A [m, K], B [n, K], row stride K),
 // no scales. A 64-byte stage row is then 32 elements and a 16-byte fragment
