@@ -515,7 +515,13 @@ adahop_status run_gemm(adahop_op op, const uint16_t* lhs, const uint16_t* rhs, i
     ADAHOP_TRY(E.record(1));
     ADAHOP_TRY(quant_lhs(stream));
     ADAHOP_TRY(E.record(2));
-  } else if (idx && (scan_lhs ? !P.zero_rhs : !P.zero_lhs)) {
+  } else if (idx && (scan_lhs ? !P.zero_rhs : !P.zero_lhs) &&
+             2 * (s.lhs_rows * s.lhs_cols + s.rhs_rows * s.rhs_cols) > ((int64_t)96 << 20)) {
+    // The fork and the join cost ~15 us; they pay off only when the two
+    // operands together exceed 96 MB of bf16 (same-box A/B, per call: o-proj
+    // BS 1 input and weight gradients -2.4 % without the second stream, BS 2
+    // input gradient -1.5 %; BS 2 weight gradient and from BS 4 on, faster
+    // with it).
     int dev = 0;
     if (hipGetDevice(&dev) == hipSuccess && dev >= 0 && dev < kMaxDevices) {
       sj.lock = std::unique_lock<std::mutex>(g_side[dev].mu);
