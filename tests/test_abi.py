@@ -185,6 +185,8 @@ def test_workspace_sizes():
     assert A.adahop_detect_workspace_size(4097, 64, "ROWS", 64) == surv(9 * 64)
     assert A.adahop_detect_workspace_size(64, 8192, "COLS", 64) == surv(16 * 64)
     assert A.adahop_detect_workspace_size(2000, 64, "ROWS", 200) == surv(2 * 200)
+    assert A.adahop_detect_workspace_size(64, 4096, "COLS", 128) == surv(8 * 128)
+    assert A.adahop_detect_workspace_size(5000, 64, "ROWS", 100) == surv(10 * 100)
     # k > 256: chunks of 4096
     assert A.adahop_detect_workspace_size(20000, 64, "ROWS", 300) == surv(5 * 300)
     ws = A.adahop_gemm_workspace_size("WGRAD", 32768, 14336, 4096, "R", "C", None, 64)

@@ -138,6 +138,8 @@ FOID_CASES = [
     (2500, 96, "ROWS", 64, 16, False),       # the same with a short probe (one candidate at a time)
     (64, 8192, "COLS", 64, 64, True),        # 16 chunks of 512, one candidate per thread, ties
     (4097, 64, "ROWS", 64, 64, False),       # 9 chunks of 512, the last holding one candidate
+    (64, 4096, "COLS", 128, 64, False),      # k = 128: chunks of 512 (256 < 4 k), 1024 survivors
+    (5000, 64, "ROWS", 100, 64, True),       # k = 100: 10 chunks of 512, 1000 survivors, ties
 ]
 
 
