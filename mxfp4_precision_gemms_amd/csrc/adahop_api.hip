@@ -476,11 +476,11 @@ adahop_status run_gemm(adahop_op op, const uint16_t* lhs, const uint16_t* rhs, i
     rl = P.ctx_off_lines != kNone ? reinterpret_cast<uint16_t*>(c + P.ctx_off_lines) : nullptr;
   }
   const bool scan_lhs = pb.scan_tensor == 0;
-  auto foid = [&](hipStream_t st) {
+  auto foid = [&](hipStream_t st, const QuantBeside* beside = nullptr, bool* beside_done = nullptr) {
     return foid_launch(scan_lhs ? lhs : rhs, scan_lhs ? s.lhs_rows : s.rhs_rows,
                        scan_lhs ? s.lhs_cols : s.rhs_cols, scan_lhs ? s.lhs_cols : s.rhs_cols,
                        pb.scan_axis, 64, pb.k, idx, P.off_foid != kNone ? w + P.off_foid : nullptr,
-                       P.foid_bytes, st);
+                       P.foid_bytes, st, beside, beside_done);
   };
   // With an outer outlier product the operand FOID does not scan is the
   // product's wide factor, read again in bf16 by the GEMM launch right after
@@ -504,10 +504,32 @@ adahop_status run_gemm(adahop_op op, const uint16_t* lhs, const uint16_t* rhs, i
                             bc, bs, rl, pb.layout, st, !keep_rhs);
   };
   // OE_LEFT / OE_RIGHT zero lines of the scanned operand only, and only the
-  // GEMM reads the other operand's packed form: that operand is quantized on
-  // the side stream while FOID, the scanned operand's quantization and the
-  // outlier product run on the caller's stream; the join comes right before
-  // the GEMM (and the ROWS-layout scale reordering).
+  // GEMM reads the other operand's packed form, so that operand's
+  // quantization can run beside FOID. When it is quantized down its columns
+  // and FOID's selection fits one launch (k <= 256, at most two levels), the
+  // two share FOID's launch (QuantBeside). Otherwise, with large operands,
+  // that operand is quantized on the side stream while FOID, the scanned
+  // operand's quantization and the outlier product run on the caller's
+  // stream; the join comes right before the GEMM (and the ROWS-layout scale
+  // reordering).
+  QuantBeside qb{};
+  bool beside = false;
+  if (!ctx && idx) {
+    const bool other_lhs = !scan_lhs;
+    if (had == 32 && (other_lhs ? !P.zero_lhs : !P.zero_rhs) &&
+        (other_lhs ? s.lhs_contract : s.rhs_contract) == ADAHOP_AXIS_ROWS) {
+      qb.src = other_lhs ? lhs : rhs;
+      qb.K = other_lhs ? s.lhs_rows : s.rhs_rows;
+      qb.outer = other_lhs ? s.lhs_cols : s.rhs_cols;
+      qb.ld = qb.outer;
+      qb.codes = other_lhs ? ac : bc;
+      qb.scales = other_lhs ? as : bs;
+      qb.layout = pb.layout;
+      qb.stream_src = other_lhs ? !keep_lhs : !keep_rhs;
+      const int64_t rows = scan_lhs ? s.lhs_rows : s.rhs_rows, cols = scan_lhs ? s.lhs_cols : s.rhs_cols;
+      beside = foid_beside_fits(pb.scan_axis == ADAHOP_AXIS_ROWS ? rows : cols, pb.k, qb);
+    }
+  }
   SideJoin sj;
   SideStream* side = nullptr;
   if (ctx) {
@@ -515,13 +537,18 @@ adahop_status run_gemm(adahop_op op, const uint16_t* lhs, const uint16_t* rhs, i
     ADAHOP_TRY(E.record(1));
     ADAHOP_TRY(quant_lhs(stream));
     ADAHOP_TRY(E.record(2));
-  } else if (idx && (scan_lhs ? !P.zero_rhs : !P.zero_lhs) &&
+  } else if (!beside && idx && (scan_lhs ? !P.zero_rhs : !P.zero_lhs) &&
              2 * (s.lhs_rows * s.lhs_cols + s.rhs_rows * s.rhs_cols) > ((int64_t)96 << 20)) {
     // The fork and the join cost ~15 us; they pay off only when the two
     // operands together exceed 96 MB of bf16 (same-box A/B, per call: o-proj
     // BS 1 input and weight gradients -2.4 % without the second stream, BS 2
     // input gradient -1.5 %; BS 2 weight gradient and from BS 4 on, faster
-    // with it).
+    // with it). The shared launch, where it applies, beats the second stream
+    // too (same-box A/B: o-proj BS 2 weight gradient -5.8 %, BS 4 input and
+    // weight gradients -2.6 % and -4.3 %, BS 8 weight gradient -1.6 %, the
+    // down-proj weight gradient even) and one stream without it (o-proj BS 1
+    // input and weight gradients -9.1 % and -7.4 %, BS 2 input gradient
+    // -4.3 %).
     int dev = 0;
     if (hipGetDevice(&dev) == hipSuccess && dev >= 0 && dev < kMaxDevices) {
       sj.lock = std::unique_lock<std::mutex>(g_side[dev].mu);
@@ -552,11 +579,13 @@ adahop_status run_gemm(adahop_op op, const uint16_t* lhs, const uint16_t* rhs, i
       ADAHOP_TRY(E.record(3));
     }
   } else if (!ctx) {
-    if (idx) ADAHOP_TRY(foid(stream));
+    // One stream. With the shared launch the other operand's stage is empty.
+    bool other_done = false;
+    if (idx) ADAHOP_TRY(foid(stream, beside ? &qb : nullptr, &other_done));
     ADAHOP_TRY(E.record(1));
-    ADAHOP_TRY(quant_lhs(stream));
+    if (!(other_done && !scan_lhs)) ADAHOP_TRY(quant_lhs(stream));
     ADAHOP_TRY(E.record(2));
-    ADAHOP_TRY(quant_rhs(stream));
+    if (!(other_done && scan_lhs)) ADAHOP_TRY(quant_rhs(stream));
   }
   void* gemm_scratch = P.off_gemm != kNone ? w + P.off_gemm : nullptr;
   if (!side) {

@@ -27,9 +27,29 @@ bool foid_fits(int64_t ncand, int32_t k);
 // FOID's score of every candidate line, fp64 [ncand], on the device.
 adahop_status line_scores_launch(const uint16_t* t, int64_t rows, int64_t cols, int64_t ld, int axis,
                                  int32_t probe, double* out, hipStream_t stream);
+// The quantization (IHT over blocks of 32, MXFP4) of an operand with no
+// extracted lines, contracted down its columns (K = rows), that FOID may run
+// in its own launch: src [K][outer] with row stride ld, codes and scales as
+// iht_quant_launch writes them for that layout; stream_src as there.
+struct QuantBeside {
+  const uint16_t* src;
+  int64_t K, outer, ld;
+  uint8_t* codes;
+  uint8_t* scales;
+  int layout;
+  bool stream_src;
+};
+// Whether FOID's selection over ncand candidates fits one launch of
+// 256-thread workgroups (k <= 256, at most two levels) that also runs q's
+// quantization (q suits the vectorized column-direction tiles).
+bool foid_beside_fits(int64_t ncand, int32_t k, const QuantBeside& q);
+// With `beside` and foid_beside_fits, the selection's workgroups and that
+// quantization's share one launch and *beside_done is set; otherwise FOID
+// runs as without it and the caller quantizes the operand itself.
 adahop_status foid_launch(const uint16_t* t, int64_t rows, int64_t cols, int64_t ld, int axis,
                           int32_t probe, int32_t k, int32_t* idx_out, void* ws, size_t ws_bytes,
-                          hipStream_t stream);
+                          hipStream_t stream, const QuantBeside* beside = nullptr,
+                          bool* beside_done = nullptr);
 
 // ---- zero + gather + IHT + MXFP4 ------------------------------------------
 // Whether iht_quant_launch's grid fits (false: it would return UNSUPPORTED).

@@ -1,9 +1,10 @@
 """Whole adahop_gemm calls captured into a HIP graph (torch.cuda.graph) and
 replayed: every replay must equal the eager call bit for bit (the path is
-deterministic). Covers the second-stream fork and join of OE_LEFT and
-OE_RIGHT under capture (taken when the two operands exceed 96 MB of bf16), the
-FOID counter reset inside the graph and the K-split of the GEMM's last
-round. Between replays the program does its own
+deterministic). Covers FOID's selection sharing its launch with the other
+operand's quantization, the second-stream fork and join under capture
+(taken when that launch does not apply and the two operands exceed 96 MB of
+bf16), the FOID counter reset inside the graph and the K-split of the GEMM's
+last round. Between replays the program does its own
 eager work (clearing the output) and synchronizes."""
 import numpy as np
 import pytest
@@ -37,9 +38,12 @@ CASES = [
     # op, T, Din, Dout, pattern pair, route (None: by the pattern pair)
     ("WGRAD", 4096, 768, 512, "R", "C", "OE_RIGHT"),   # one stream; K = 4096: split last round
     ("FWD", 1024, 1024, 520, "R", "N", "OE_LEFT"),     # one stream, FOID over 1024 rows
-    # operands above 96 MB together: the second stream's fork and join
+    # operands above 96 MB together: FOID's selection shares its launch with
+    # the other operand's quantization (down the columns)
     ("WGRAD", 8192, 6400, 256, "R", "C", "OE_RIGHT"),  # X [8192, 6400] scanned by columns
     ("DGRAD", 16384, 256, 3072, "R", "N", "OE_LEFT"),  # GY [16384, 3072] scanned by rows
+    # above 96 MB with W quantized along its rows: the second stream's fork and join
+    ("FWD", 16384, 3072, 256, "R", "N", "OE_LEFT"),    # X [16384, 3072] scanned by rows
     ("FWD", 512, 2048, 384, "C", "N", "OE_INNER"),     # asked for: both operands zeroed, one stream
     ("WGRAD", 2048, 320, 300, "C", "C", "BF16"),       # X in place, GY copied; 4 tiles in 4 K-parts
 ]

@@ -470,6 +470,47 @@ def test_full_product_degenerate(case):
         assert np.array_equal(ref["idx"], np.arange(k))
 
 
+# FOID's selection in one launch with the quantization of the operand it
+# does not scan (256-thread workgroups), one case per shape of the selection:
+# a lone final level, first-level chunks of 256, 512 and 1024 candidates (1,
+# 2 and 4 per thread), and k = 200. The scanned operand holds 0/1 values
+# (scores take few distinct values: the k-th is tied) with k/2 lines x3, so
+# the tie-break by index decides the boundary; indices, codes and scales
+# bit-exact, the output to the product bar.
+BESIDE_CASES = [
+    # op, T, Din, Dout, pattern pair, route, k
+    ("WGRAD", 256, 1000, 128, "R", "C", "OE_RIGHT", 100),   # 1000 of X's columns: the final level alone
+    ("WGRAD", 256, 3000, 128, "R", "C", "OE_RIGHT", 64),    # 12 chunks of 256, the last ragged
+    ("WGRAD", 256, 6000, 128, "R", "C", "OE_RIGHT", 64),    # 12 chunks of 512
+    ("WGRAD", 256, 9000, 128, "R", "C", "OE_RIGHT", 64),    # 9 chunks of 1024
+    ("WGRAD", 256, 5000, 128, "R", "C", "OE_RIGHT", 200),   # 5 chunks of 1024, 1000 survivors
+    ("DGRAD", 3000, 256, 512, "R", "N", "OE_LEFT", 32),     # GY's rows, 12 chunks of 256
+]
+
+
+@pytest.mark.parametrize("case", BESIDE_CASES, ids=[str(c) for c in BESIDE_CASES])
+def test_foid_beside_other_quantization(case):
+    op, T, Din, Dout, pl, pr, route, k = case
+    rng = np.random.default_rng(T + Din + k)
+    shapes = {"DGRAD": ((T, Dout), (Dout, Din)), "WGRAD": ((T, Dout), (T, Din))}[op]
+    scan = 0 if route == "OE_LEFT" else 1
+    axis = 0 if route == "OE_LEFT" else 1           # GY's rows, or X's columns
+    ops = []
+    for t, shape in enumerate(shapes):
+        if t != scan:
+            ops.append(rand_bf16(rng, shape))
+            continue
+        v = rng.integers(0, 2, size=shape).astype(np.float32)
+        lines = rng.choice(shape[axis], k // 2, replace=False)
+        if axis == 0:
+            v[lines, :] *= 3.0
+        else:
+            v[:, lines] *= 3.0
+        ops.append(f32_to_bf16_rne(v))
+    ref = run_and_compare(op, ops[0], ops[1], T, Din, Dout, pl, pr, route, k)
+    assert set(lines.tolist()) <= set(ref["idx"].tolist())
+
+
 def test_deterministic_reruns():
     # K = 4096 over 6 tiles: the K-split path, whose parts are added in order.
     op, T, Din, Dout = "WGRAD", 4096, 768, 512
