@@ -47,11 +47,14 @@
  *   - Thread safety: calls on different streams may run concurrently;
  *     adahop_last_error() is per host thread.
  *   - adahop_gemm with OE_LEFT or OE_RIGHT quantizes the operand FOID does
- *     not scan on a second stream the library creates once per device
- *     (default priority), forked from `stream` with an event and joined back
- *     before the GEMM, so that it runs beside FOID, the other quantization
- *     and the outlier product; the call's completion stays ordered on
- *     `stream`.
+ *     not scan beside FOID: in FOID's own launch when that operand is
+ *     quantized down its columns (contracted along its rows) and FOID's
+ *     selection takes at most two levels (k <= 256, up to 16384 candidates
+ *     at k = 64); otherwise, when the two operands exceed 96 MB of bf16, on
+ *     a second stream the library creates once per device (default
+ *     priority), forked from `stream` with an event and joined back before
+ *     the GEMM; otherwise after FOID on `stream`. The call's completion
+ *     stays ordered on `stream`.
  */
 #ifndef ADAHOP_H
 #define ADAHOP_H
@@ -404,9 +407,11 @@ ADAHOP_API adahop_status adahop_gemm_wgrad_ctx(const uint16_t* GY, const void* c
  * previous one). The tail is what finishes the main kernel's output: the
  * fixup of a split last round of tiles and, when the outlier product ran
  * inside the main kernel, its scatter into the extracted lines. With
- * OE_LEFT and OE_RIGHT the operand FOID does not scan is quantized on a
- * second stream: its stage is empty here, the ROWS-layout scale reordering
- * falls in the GEMM stage, and the other stages overlap with it. With route
+ * OE_LEFT and OE_RIGHT the operand FOID does not scan is quantized in
+ * FOID's launch (the FOID stage then holds both, and that operand's stage is
+ * empty), on a second stream (its stage is empty here, the ROWS-layout scale
+ * reordering falls in the GEMM stage, and the other stages overlap with it)
+ * or in its own stage after FOID, as the notes at the top say. With route
  * BF16 the lhs and rhs stages are the operands' K-major copies, if any. */
 #define ADAHOP_STAGE_EVENTS 7
 ADAHOP_API adahop_status adahop_gemm_timed(adahop_op op, const uint16_t* lhs,

@@ -1295,14 +1295,24 @@ __global__ void __launch_bounds__(kFixThreads) gemm_split_fixup_kernel(GemmArgs 
 // (idx[p], w) (OE_LEFT) becomes the extracted line's fp32 residual, kept by
 // the tile epilogue or the fixup, plus the partial sums added in part order,
 // rounded once. Thread t takes (w, p) in the partials' own order, so the
-// reads of every part are coalesced.
+// reads of every part are coalesced; it loads eight parts at a time before
+// adding them in order, so the loads are in flight together.
 __global__ void __launch_bounds__(256) oe_scatter_kernel(GemmArgs g, int parts) {
   const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
   const int64_t count = g.oe_wide_n * g.oe_k;
   if (t >= count) return;
+  const float res = g.oe_res[t];
   float sum = g.oe_part[t];
-  for (int s = 1; s < parts; ++s) sum += g.oe_part[(int64_t)s * count + t];
-  const float v = g.oe_res[t] + sum;
+  int s = 1;
+  for (; s + 8 <= parts; s += 8) {
+    float v[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v[j] = g.oe_part[(int64_t)(s + j) * count + t];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) sum += v[j];
+  }
+  for (; s < parts; ++s) sum += g.oe_part[(int64_t)s * count + t];
+  const float v = res + sum;
   const bool right = g.oe_mode == ADAHOP_ROUTE_OE_RIGHT;
   const int64_t w = right ? t / g.oe_k : t % g.oe_wide_n;
   const int p = (int)(right ? t % g.oe_k : t / g.oe_wide_n);
