@@ -465,6 +465,10 @@ def main():
     ap.add_argument("--sweep-oproj", action="store_true",
                     help="instead of the timed line: the o_proj triplet at batch sizes 1-16 against "
                          "plain MXFP4, the BF16 route and hipBLASLt bf16, one JSON line each")
+    ap.add_argument("--oe-in-quant", action="store_true",
+                    help="OE_LEFT / OE_RIGHT: form the outlier product in the quantization of the "
+                         "operand FOID does not scan (one read of it; adahop_gemm_ex) instead of "
+                         "inside the GEMM launch")
     ap.add_argument("--from-context", action="store_true",
                     help="time a weight gradient from the saved forward context of X "
                          "(adahop_gemm_wgrad_ctx) instead of from X")
@@ -533,8 +537,12 @@ def main():
         return
 
     out_dtype = torch.bfloat16 if args.out_dtype == "bf16" else torch.float32
-    plan = A.adahop_gemm_plan(op, T, Din, Dout, call.pat_lhs, call.pat_rhs, call.route, call.k)
+    plan = A.adahop_gemm_plan(op, T, Din, Dout, call.pat_lhs, call.pat_rhs, call.route, call.k,
+                              args.oe_in_quant)
     route = A.ROUTE_NAME[plan.route]
+    if args.oe_in_quant and (args.from_context or not plan.oe_in_quant):
+        sys.exit("--oe-in-quant applies to OE_LEFT / OE_RIGHT calls whose other operand is "
+                 "quantized down its columns, with k <= 64, not from a context")
     out_shape = {"FWD": (T, Dout), "DGRAD": (T, Din), "WGRAD": (Dout, Din)}[op]
     out = torch.empty(out_shape, dtype=out_dtype, device=dev)
     ctx_info = None
@@ -559,7 +567,7 @@ def main():
 
         def step(events=None):
             A.adahop_gemm(op, lhs, rhs, call.pat_lhs, call.pat_rhs, call.route, call.k,
-                          out=out, ws=ws, stage_events=events)
+                          out=out, ws=ws, stage_events=events, oe_in_quant=args.oe_in_quant)
 
     settle_calls = settle(torch, step, args.settle_ms) if args.settle_ms > 0 else 0
     for _ in range(args.warmup):
@@ -635,13 +643,23 @@ def main():
                         "across K that cannot be read in place (empty when there are none); gemm "
                         "is the bf16 MFMA kernel, gemm_tail the fixup kernel of a split last "
                         "round") if bf16 else
-                       ("the operand FOID does not scan is quantized on a second stream, beside "
-                        "FOID and the other quantization: its slot is empty and the other slots "
-                        "overlap it; when the wide outlier factor is stored across K and k <= 64 "
-                        "the outlier product runs as work items of the GEMM kernel (its own slot "
-                        "empty), else before it; gemm is the MFMA kernel, gemm_tail the fixup "
-                        "kernel of a split last round and the kernel that adds the outlier "
-                        "product to the extracted lines")
+                       ("one read of the operand FOID does not scan: FOID, the scanned operand's "
+                        "quantization (which gathers the lines), the other's forming the outlier "
+                        "product's partial sums (with OE_RIGHT in the oe_product slot, the lhs "
+                        "slot empty), their sum in order (oe_product), the GEMM (its epilogue "
+                        "adds the sum to the extracted lines), gemm_tail the fixup kernel of a "
+                        "split last round")
+                       if args.oe_in_quant else
+                       ("the operand FOID does not scan is quantized beside FOID: in FOID's own "
+                        "launch (the foid slot holds both, that operand's slot is empty) when "
+                        "it is quantized down its columns and the selection takes at most two "
+                        "levels, else on a second stream when the operands exceed 96 MB (its "
+                        "slot empty, the other slots overlap it), else after FOID; when the wide "
+                        "outlier factor is stored across K and k <= 64 the outlier product runs "
+                        "as work items of the GEMM kernel (its own slot empty), else before it; "
+                        "gemm is the MFMA kernel, gemm_tail the fixup kernel of a split last "
+                        "round and the kernel that adds the outlier product to the extracted "
+                        "lines")
                        if route in ("OE_LEFT", "OE_RIGHT") else
                        ("gemm is the MFMA kernel, gemm_tail the fixup kernel of a split last "
                         "round"),
@@ -655,7 +673,8 @@ def main():
                                ("gemm_mx_ring8_kernel<true, false, false, false> (FP4 MFMA GEMM, "
                                 "main kernel alone; its first workgroups also compute the rank-k "
                                 "bf16 outlier product as work items, whose 2mkK flops are not "
-                                "counted)") if route in ("OE_LEFT", "OE_RIGHT") else
+                                "counted)") if route in ("OE_LEFT", "OE_RIGHT") and not args.oe_in_quant
+                               else
                                ("gemm_mx_ring8_kernel<true, false, false, false> (FP4 MFMA GEMM, "
                                 "main kernel alone)"),
                      "achieved": round(achieved, 1), "peak": peak,
@@ -671,6 +690,9 @@ def main():
                                  "quantization ran in the forward (context save, timed apart in "
                                  "context.ctx_save_ms); quant_lhs is GY's")
     traffic, note = measured_traffic(wl.name, TRAFFIC_SUMMARY_BF16 if bf16 else TRAFFIC_SUMMARY)
+    if args.oe_in_quant:
+        result["config"]["oe_in_quant"] = True
+        traffic, note = None, "the counters were taken on the default path (outlier items in the GEMM)"
     result["roofline"]["traffic"] = None if traffic is None else round(traffic)
     result["roofline"]["traffic_note"] = note
 

@@ -322,6 +322,8 @@ typedef struct {
   size_t off_b_codes, off_b_scales;   /* B packed (outer = n) in `layout` */
   size_t off_lhs_lines;   /* bf16 lines gathered from lhs (layout as adahop_iht_quant) */
   size_t off_rhs_lines;   /* bf16 lines gathered from rhs */
+  int32_t oe_in_quant;    /* 1: the outlier product is formed in the other operand's
+                             quantization (asked for with adahop_gemm_options) */
 } adahop_plan;
 
 ADAHOP_API adahop_status adahop_gemm_plan(adahop_op op, int64_t T, int64_t Din, int64_t Dout,
@@ -338,6 +340,44 @@ ADAHOP_API adahop_status adahop_gemm(adahop_op op, const uint16_t* lhs, const ui
                                      adahop_route_t route, int32_t oe_rank, void* out,
                                      adahop_out_dtype out_dtype, void* ws, size_t ws_bytes,
                                      void* stream);
+
+/* Options of adahop_gemm_plan_ex and adahop_gemm_ex (NULL: all defaults,
+ * which is adahop_gemm's behaviour). reserved must be zero.
+ * oe_in_quant = 1: with OE_LEFT or OE_RIGHT, when the operand FOID does not
+ * scan is quantized down its columns (contracted along its rows: DGRAD's W,
+ * both WGRAD operands) and k <= 64, that operand's quantization also forms
+ * the outer outlier product -- its rank-k product with the extracted lines,
+ * fp32 partial sums per group of 128-row tiles, then their sum in group
+ * order -- so the operand is read once (appendix, kernels 2 and 3: the
+ * outlier product beside the quantization's single pass). The stages then
+ * run one after another on `stream`: FOID, the scanned operand's
+ * quantization (which gathers the lines), the other's with the partial
+ * sums, their sum, the GEMM, whose epilogue adds the sum to the extracted
+ * lines before the single rounding. The plan reports whether it applies
+ * (plan.oe_in_quant); where it does not, the call runs as adahop_gemm. The
+ * default path, which quantizes that operand beside FOID and forms the
+ * outlier product inside the GEMM launch, measured faster on the workloads
+ * here; this one exists for the one-read schedule and its measurement.
+ * Errors: INVALID for oe_in_quant not 0 or 1 or a reserved field not 0;
+ * otherwise as adahop_gemm_plan / adahop_gemm_timed (stage_events may be
+ * NULL). */
+typedef struct {
+  int32_t oe_in_quant;
+  int32_t reserved[7];
+} adahop_gemm_options;
+
+ADAHOP_API adahop_status adahop_gemm_plan_ex(adahop_op op, int64_t T, int64_t Din, int64_t Dout,
+                                             adahop_pattern pat_lhs, adahop_pattern pat_rhs,
+                                             adahop_route_t route, int32_t oe_rank,
+                                             const adahop_gemm_options* opts,
+                                             adahop_plan* plan);
+ADAHOP_API adahop_status adahop_gemm_ex(adahop_op op, const uint16_t* lhs, const uint16_t* rhs,
+                                        int64_t T, int64_t Din, int64_t Dout,
+                                        adahop_pattern pat_lhs, adahop_pattern pat_rhs,
+                                        adahop_route_t route, int32_t oe_rank,
+                                        const adahop_gemm_options* opts, void* out,
+                                        adahop_out_dtype out_dtype, void* ws, size_t ws_bytes,
+                                        void* stream, void* const* stage_events);
 
 /* ---------------------------------------------------------------------------
  * Saved forward context (appendix, kernel 2: for the activation of the
@@ -412,7 +452,11 @@ ADAHOP_API adahop_status adahop_gemm_wgrad_ctx(const uint16_t* GY, const void* c
  * empty), on a second stream (its stage is empty here, the ROWS-layout scale
  * reordering falls in the GEMM stage, and the other stages overlap with it)
  * or in its own stage after FOID, as the notes at the top say. With route
- * BF16 the lhs and rhs stages are the operands' K-major copies, if any. */
+ * BF16 the lhs and rhs stages are the operands' K-major copies, if any.
+ * With the outlier product formed in the quantization (adahop_gemm_ex,
+ * oe_in_quant), the stages follow that order: with OE_RIGHT the lhs stage is
+ * empty and the lhs's quantization with the partial sums falls in the
+ * outlier product's stage, with their sum. */
 #define ADAHOP_STAGE_EVENTS 7
 ADAHOP_API adahop_status adahop_gemm_timed(adahop_op op, const uint16_t* lhs,
                                            const uint16_t* rhs, int64_t T, int64_t Din,

@@ -56,7 +56,11 @@ class Plan(ctypes.Structure):
                 ("scan_tensor", _i32), ("scan_axis", _int), ("layout", _int),
                 ("ws_bytes", _sz), ("off_idx", _sz), ("off_a_codes", _sz),
                 ("off_a_scales", _sz), ("off_b_codes", _sz), ("off_b_scales", _sz),
-                ("off_lhs_lines", _sz), ("off_rhs_lines", _sz)]
+                ("off_lhs_lines", _sz), ("off_rhs_lines", _sz), ("oe_in_quant", _i32)]
+
+
+class GemmOptions(ctypes.Structure):
+    _fields_ = [("oe_in_quant", _i32), ("reserved", _i32 * 7)]
 
 
 class CtxPlan(ctypes.Structure):
@@ -91,6 +95,10 @@ SIGNATURES = {
                      _sz, _p], _int),
     "adahop_gemm_timed": ([_int, _p, _p, _i64, _i64, _i64, _int, _int, _int, _i32, _p, _int,
                            _p, _sz, _p, _p], _int),
+    "adahop_gemm_plan_ex": ([_int, _i64, _i64, _i64, _int, _int, _int, _i32,
+                             ctypes.POINTER(GemmOptions), ctypes.POINTER(Plan)], _int),
+    "adahop_gemm_ex": ([_int, _p, _p, _i64, _i64, _i64, _int, _int, _int, _i32,
+                        ctypes.POINTER(GemmOptions), _p, _int, _p, _sz, _p, _p], _int),
     "adahop_ctx_plan": ([_i64, _i64, _i64, _int, _int, _int, _i32, ctypes.POINTER(CtxPlan)], _int),
     "adahop_ctx_save": ([_p, _i64, _i64, _i64, _int, _int, _int, _i32, _p, _sz, _p, _sz, _p],
                         _int),
@@ -275,11 +283,24 @@ def adahop_gemm_mx(a_codes, a_scales, b_codes, b_scales, oe: Optional[dict] = No
     return out
 
 
+def _options(oe_in_quant: bool):
+    return GemmOptions(oe_in_quant=1 if oe_in_quant else 0)
+
+
 def adahop_gemm_plan(op: str, T: int, Din: int, Dout: int, pat_lhs="N", pat_rhs="N",
-                     route: Optional[str] = None, oe_rank: int = 64) -> Plan:
+                     route: Optional[str] = None, oe_rank: int = 64,
+                     oe_in_quant: bool = False) -> Plan:
+    """The call's plan; oe_in_quant asks for the outlier product formed in
+    the other operand's quantization (adahop_gemm_plan_ex)."""
     p = Plan()
-    _check(lib().adahop_gemm_plan(OP[op], T, Din, Dout, PAT[pat_lhs], PAT[pat_rhs],
-                                  ROUTE[route or "AUTO"], oe_rank, ctypes.byref(p)))
+    if oe_in_quant:
+        o = _options(True)
+        _check(lib().adahop_gemm_plan_ex(OP[op], T, Din, Dout, PAT[pat_lhs], PAT[pat_rhs],
+                                         ROUTE[route or "AUTO"], oe_rank, ctypes.byref(o),
+                                         ctypes.byref(p)))
+    else:
+        _check(lib().adahop_gemm_plan(OP[op], T, Din, Dout, PAT[pat_lhs], PAT[pat_rhs],
+                                      ROUTE[route or "AUTO"], oe_rank, ctypes.byref(p)))
     return p
 
 
@@ -312,17 +333,19 @@ def _gemm_dims(op, lhs, rhs):
 def adahop_gemm(op: str, lhs: torch.Tensor, rhs: torch.Tensor, pat_lhs="N", pat_rhs="N",
                 route: Optional[str] = None, oe_rank: int = 64, out_dtype=torch.bfloat16,
                 out: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None,
-                stage_events: Optional[Sequence] = None):
+                stage_events: Optional[Sequence] = None, oe_in_quant: bool = False):
     """One AdaHOP product; returns the output tensor. `ws` (uint8, at least
     the planned size) is optional; after the call it holds the quantized
-    operands at the offsets of adahop_gemm_plan. stage_events: 6
-    torch.cuda.Event(enable_timing=True), recorded at the stage boundaries."""
+    operands at the offsets of adahop_gemm_plan. stage_events: STAGE_EVENTS
+    torch.cuda.Event(enable_timing=True), recorded at the stage boundaries.
+    oe_in_quant: form the outlier product in the other operand's
+    quantization where it applies (adahop_gemm_ex)."""
     for t, nm in ((lhs, "lhs"), (rhs, "rhs")):
         _bf16_ptr(t, nm)
         if not t.is_contiguous():
             raise ValueError(f"{nm} must be contiguous")
     T, Din, Dout, out_shape = _gemm_dims(op, lhs, rhs)
-    plan = adahop_gemm_plan(op, T, Din, Dout, pat_lhs, pat_rhs, route, oe_rank)
+    plan = adahop_gemm_plan(op, T, Din, Dout, pat_lhs, pat_rhs, route, oe_rank, oe_in_quant)
     dev = lhs.device
     if out is None:
         out = torch.empty(out_shape, dtype=out_dtype, device=dev)
@@ -331,12 +354,17 @@ def adahop_gemm(op: str, lhs: torch.Tensor, rhs: torch.Tensor, pat_lhs="N", pat_
     args = [OP[op], lhs.data_ptr(), rhs.data_ptr(), T, Din, Dout, PAT[pat_lhs], PAT[pat_rhs],
             ROUTE[route or "AUTO"], oe_rank, out.data_ptr(), OUT[out.dtype], _ptr(ws),
             0 if ws is None else ws.numel(), _stream(dev)]
-    if stage_events is None:
-        _check(lib().adahop_gemm(*args))
-    else:
+    handles = None
+    if stage_events is not None:
         if len(stage_events) != STAGE_EVENTS:
             raise ValueError(f"stage_events needs {STAGE_EVENTS} events")
         handles = (ctypes.c_void_p * STAGE_EVENTS)(*[_event_handle(e) for e in stage_events])
+    if oe_in_quant:
+        o = _options(True)
+        _check(lib().adahop_gemm_ex(*args[:10], ctypes.byref(o), *args[10:], handles))
+    elif handles is None:
+        _check(lib().adahop_gemm(*args))
+    else:
         _check(lib().adahop_gemm_timed(*args, handles))
     return out
 

@@ -86,6 +86,9 @@ struct Plan {
   bool zero_lhs = false, zero_rhs = false;
   int lhs_zero_axis = ADAHOP_AXIS_ROWS, rhs_zero_axis = ADAHOP_AXIS_ROWS;
   int splits = 0;
+  // The outlier product formed in the other operand's quantization (one
+  // read of it): its number of partial-sum groups, 0 when not used.
+  int fused_groups = 0;
   size_t off_foid = SIZE_MAX, off_partials = SIZE_MAX, off_gemm = SIZE_MAX;
   size_t foid_bytes = 0, gemm_bytes = 0;
   // BF16 route on the ring kernel: whether it reads A / B across K, the
@@ -122,7 +125,8 @@ void oe_views(const Plan& P, const uint16_t* lhs, const uint16_t* rhs, const uin
 
 adahop_status make_plan(adahop_op op, int64_t T, int64_t Din, int64_t Dout,
                         adahop_pattern pat_lhs, adahop_pattern pat_rhs, adahop_route_t route,
-                        int32_t oe_rank, Plan* P, bool rhs_in_ctx = false) {
+                        int32_t oe_rank, Plan* P, bool rhs_in_ctx = false,
+                        bool oe_in_quant = false) {
   std::memset(&P->pub, 0, sizeof(P->pub));
   P->rhs_in_ctx = rhs_in_ctx;
   if (!op_shape(op, T, Din, Dout, &P->shape)) return fail(ADAHOP_ERR_INVALID, "invalid op");
@@ -274,6 +278,19 @@ adahop_status make_plan(adahop_op op, int64_t T, int64_t Din, int64_t Dout,
     oe_views(*P, nullptr, nullptr, nullptr, nullptr, &X, &Y);
     const int fp = oe_fused_parts(s.m, s.n, s.K, route, pb.k, X, Y, false);
     if (fp > 0) bytes = std::max(bytes, oe_fused_bytes(s.m, s.n, route, pb.k, fp));
+    // Asked for: the operand FOID does not scan, when it is quantized down
+    // its columns, forms the outlier product in its quantization pass
+    // (partial sums per group of K tiles, then their sum in order).
+    const bool other_lhs = pb.scan_tensor == 1;
+    if (oe_in_quant && !rhs_in_ctx &&
+        (other_lhs ? s.lhs_contract : s.rhs_contract) == ADAHOP_AXIS_ROWS) {
+      int tiles_per_wg = 0;
+      P->fused_groups = iht_quant_oe_groups(s.K, other_lhs ? s.lhs_cols : s.rhs_cols, pb.k,
+                                            &tiles_per_wg);
+      if (P->fused_groups > 0)
+        bytes = std::max(bytes, sizeof(float) * (size_t)(P->fused_groups + 1) * (size_t)nx * (size_t)ny);
+    }
+    pb.oe_in_quant = P->fused_groups > 0 ? 1 : 0;
     P->off_partials = take(bytes);
   }
   // Shapes a launcher would refuse are rejected here, before the call's
@@ -389,13 +406,15 @@ adahop_status run_gemm(adahop_op op, const uint16_t* lhs, const uint16_t* rhs, i
                        int64_t Din, int64_t Dout, adahop_pattern pat_lhs,
                        adahop_pattern pat_rhs, adahop_route_t route, int32_t oe_rank,
                        void* out, adahop_out_dtype out_dtype, void* ws, size_t ws_bytes,
-                       hipStream_t stream, void* const* events, const CtxIn* ctx = nullptr) {
+                       hipStream_t stream, void* const* events, const CtxIn* ctx = nullptr,
+                       bool oe_in_quant = false) {
   set_error("");
   if (!lhs || (!rhs && !ctx) || !out) return fail(ADAHOP_ERR_INVALID, "null lhs, rhs or out");
   if (out_dtype != ADAHOP_OUT_BF16 && out_dtype != ADAHOP_OUT_F32)
     return fail(ADAHOP_ERR_INVALID, "invalid out_dtype");
   Plan P;
-  ADAHOP_TRY(make_plan(op, T, Din, Dout, pat_lhs, pat_rhs, route, oe_rank, &P, ctx != nullptr));
+  ADAHOP_TRY(make_plan(op, T, Din, Dout, pat_lhs, pat_rhs, route, oe_rank, &P, ctx != nullptr,
+                       oe_in_quant));
   if (ctx) {
     if (!ctx->base) return fail(ADAHOP_ERR_INVALID, "null context");
     if (ctx->bytes < P.ctx_bytes)
@@ -512,6 +531,47 @@ adahop_status run_gemm(adahop_op op, const uint16_t* lhs, const uint16_t* rhs, i
   // operand's quantization and the outlier product run on the caller's
   // stream; the join comes right before the GEMM (and the ROWS-layout scale
   // reordering).
+  if (P.fused_groups > 0) {
+    // One read of the operand FOID does not scan: FOID, the scanned
+    // operand's quantization (which gathers the lines), then the other
+    // operand's quantization forming the outlier product's partial sums,
+    // their sum in order, and the GEMM, whose epilogue adds that sum to the
+    // extracted lines. Stage events: after FOID, the lhs and rhs
+    // quantizations in their order (with OE_RIGHT the lhs, quantized after
+    // the rhs, falls in the outlier product's stage), the outlier product's
+    // sum, the GEMM.
+    float* partials = reinterpret_cast<float*>(w + P.off_partials);
+    ADAHOP_TRY(foid(stream));
+    ADAHOP_TRY(E.record(1));
+    if (scan_lhs) {
+      ADAHOP_TRY(quant_lhs(stream));
+      ADAHOP_TRY(E.record(2));
+      ADAHOP_TRY(iht_quant_oe_launch(rhs, s.rhs_rows, s.rhs_cols, s.rhs_cols, bc, bs, pb.layout, ll,
+                                     pb.k, 1, partials, stream));
+      ADAHOP_TRY(E.record(3));
+    } else {
+      ADAHOP_TRY(E.record(2));
+      ADAHOP_TRY(quant_rhs(stream));
+      ADAHOP_TRY(E.record(3));
+      ADAHOP_TRY(iht_quant_oe_launch(lhs, s.lhs_rows, s.lhs_cols, s.lhs_cols, ac, as, pb.layout, rl,
+                                     pb.k, 0, partials, stream));
+    }
+    ADAHOP_TRY(oe_reduce_launch(partials, P.fused_groups, (int64_t)pb.k * (scan_lhs ? s.n : s.m),
+                                stream));
+    ADAHOP_TRY(E.record(4));
+    void* gemm_scratch = P.off_gemm != kNone ? w + P.off_gemm : nullptr;
+    if (pb.layout == ADAHOP_LAYOUT_ROWS)
+      ADAHOP_TRY(gemm_mx_stage_scales(ac, as, bc, bs, s.m, s.n, s.K, gemm_scratch, P.gemm_bytes, stream));
+    OeEpilogue oe{};
+    oe.mode = pb.route;
+    oe.k = pb.k;
+    oe.idx = idx;
+    oe.partials = partials;
+    oe.splits = P.fused_groups;
+    ADAHOP_TRY(gemm_mx_launch(ac, as, bc, bs, s.m, s.n, s.K, pb.layout, oe, out, s.n, out_f32,
+                              gemm_scratch, P.gemm_bytes, stream, E.at(5)));
+    return E.record(6);
+  }
   QuantBeside qb{};
   bool beside = false;
   if (!ctx && idx) {
@@ -1013,6 +1073,46 @@ adahop_status adahop_gemm_wgrad_ctx(const uint16_t* GY, const void* ctx, size_t 
   const CtxIn in{static_cast<const uint8_t*>(ctx), ctx_bytes};
   return run_gemm(ADAHOP_OP_WGRAD, GY, nullptr, T, Din, Dout, pat_gy, pat_x, route, oe_rank, out,
                   out_dtype, ws, ws_bytes, static_cast<hipStream_t>(stream), stage_events, &in);
+}
+
+// Options of the _ex calls: NULL means all defaults; unknown (reserved)
+// fields must be zero.
+static adahop_status read_options(const adahop_gemm_options* opts, bool* oe_in_quant) {
+  *oe_in_quant = false;
+  if (!opts) return ADAHOP_OK;
+  if (opts->oe_in_quant != 0 && opts->oe_in_quant != 1)
+    return fail(ADAHOP_ERR_INVALID, "adahop_gemm_options: oe_in_quant must be 0 or 1");
+  for (int32_t r : opts->reserved)
+    if (r != 0) return fail(ADAHOP_ERR_INVALID, "adahop_gemm_options: reserved fields must be 0");
+  *oe_in_quant = opts->oe_in_quant == 1;
+  return ADAHOP_OK;
+}
+
+adahop_status adahop_gemm_plan_ex(adahop_op op, int64_t T, int64_t Din, int64_t Dout,
+                                  adahop_pattern pat_lhs, adahop_pattern pat_rhs,
+                                  adahop_route_t route, int32_t oe_rank,
+                                  const adahop_gemm_options* opts, adahop_plan* plan) {
+  set_error("");
+  if (!plan) return fail(ADAHOP_ERR_INVALID, "adahop_gemm_plan_ex: null plan");
+  bool oiq = false;
+  ADAHOP_TRY(read_options(opts, &oiq));
+  Plan P;
+  ADAHOP_TRY(make_plan(op, T, Din, Dout, pat_lhs, pat_rhs, route, oe_rank, &P, false, oiq));
+  *plan = P.pub;
+  return ADAHOP_OK;
+}
+
+adahop_status adahop_gemm_ex(adahop_op op, const uint16_t* lhs, const uint16_t* rhs, int64_t T,
+                             int64_t Din, int64_t Dout, adahop_pattern pat_lhs,
+                             adahop_pattern pat_rhs, adahop_route_t route, int32_t oe_rank,
+                             const adahop_gemm_options* opts, void* out,
+                             adahop_out_dtype out_dtype, void* ws, size_t ws_bytes, void* stream,
+                             void* const* stage_events) {
+  set_error("");
+  bool oiq = false;
+  ADAHOP_TRY(read_options(opts, &oiq));
+  return run_gemm(op, lhs, rhs, T, Din, Dout, pat_lhs, pat_rhs, route, oe_rank, out, out_dtype,
+                  ws, ws_bytes, static_cast<hipStream_t>(stream), stage_events, nullptr, oiq);
 }
 
 adahop_status adahop_gemm_timed(adahop_op op, const uint16_t* lhs, const uint16_t* rhs,

@@ -63,6 +63,19 @@ adahop_status iht_quant_launch(const uint16_t* src, int64_t rows, int64_t cols, 
                                uint16_t* gathered, int layout, hipStream_t stream,
                                bool stream_src = true);
 
+// The one-read variant of OE_LEFT / OE_RIGHT: the operand FOID does not scan,
+// quantized down its columns (contract ROWS, K = rows), also forms the outer
+// outlier product's partial sums P_s = (its columns) x lines^T over group s
+// of K, fp32, in `partials` ([groups][cols][k], or [groups][k][cols] with
+// by_line), from the k extracted lines ([k][K] bf16, 16-byte aligned).
+// iht_quant_oe_groups returns the number of groups (0 if k > 64 or the
+// sizes do not fit).
+int iht_quant_oe_groups(int64_t K, int64_t outer, int32_t k, int* tiles_per_wg);
+adahop_status iht_quant_oe_launch(const uint16_t* src, int64_t rows, int64_t cols, int64_t ld,
+                                  uint8_t* codes, uint8_t* scales, int layout,
+                                  const uint16_t* lines, int32_t k, int by_line, float* partials,
+                                  hipStream_t stream);
+
 // ---- outlier product (bf16 MFMA) ------------------------------------------
 // P_s[x][y] = sum over t in split s of X(x, t) * Y(y, t), fp32, for s < splits,
 // laid out [splits][nx][ny] in `partials`, followed by their sum P [nx][ny]

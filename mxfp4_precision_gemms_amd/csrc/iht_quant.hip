@@ -53,6 +53,19 @@ iht_quant_colwise_kernel(const uint16_t* __restrict__ src, int64_t K, int64_t ou
                              blockIdx.x, blockIdx.y);
 }
 
+// The quantization down the columns with the outer outlier product's
+// partial sums formed in the same pass (colwise_oe_tiles): workgroup (x, y)
+// takes column tile x and tile group y.
+template <bool Vec, bool ByLine>
+__global__ void __launch_bounds__(kColThreads, 2)
+iht_quant_colwise_oe_kernel(const uint16_t* __restrict__ src, int64_t K, int64_t outer, int64_t ld,
+                            uint8_t* __restrict__ codes, uint8_t* __restrict__ scales, int kchunk,
+                            const uint16_t* __restrict__ lines, int k, int tiles_per_wg,
+                            float* __restrict__ partials) {
+  colwise_oe_tiles<Vec, ByLine>(src, K, outer, ld, codes, scales, kchunk, lines, k, tiles_per_wg,
+                                partials, blockIdx.x, blockIdx.y);
+}
+
 }  // namespace
 
 bool iht_quant_fits(int64_t rows, int64_t cols, int contract) {
@@ -108,6 +121,50 @@ adahop_status iht_quant_launch(const uint16_t* src, int64_t rows, int64_t cols, 
     else go(std::false_type{}, std::false_type{}, std::false_type{});
   }
   return check_launch("iht_quant");
+}
+
+int iht_quant_oe_groups(int64_t K, int64_t outer, int32_t k, int* tiles_per_wg) {
+  *tiles_per_wg = 0;
+  if (k < 1 || k > kFusedOeMaxK || K < 32 || K % 32 != 0 || outer < 1) return 0;
+  const int64_t ntiles = (K / 32 + kColBlocks - 1) / kColBlocks;
+  const int64_t gx = (outer + kColOut - 1) / kColOut;
+  // A workgroup takes enough tiles for about 512 workgroups in all (two per
+  // CU), at least 4 (the partial sums then add at most half the operand's
+  // bytes in traffic), at most 16.
+  int64_t r = (ntiles * gx + 511) / 512;
+  if (r < 4) r = 4;
+  if (r > 16) r = 16;
+  const int64_t groups = (ntiles + r - 1) / r;
+  if (gx > 0x7FFFFFFFLL || groups > 65535) return 0;
+  *tiles_per_wg = (int)r;
+  return (int)groups;
+}
+
+adahop_status iht_quant_oe_launch(const uint16_t* src, int64_t rows, int64_t cols, int64_t ld,
+                                  uint8_t* codes, uint8_t* scales, int layout,
+                                  const uint16_t* lines, int32_t k, int by_line, float* partials,
+                                  hipStream_t stream) {
+  const int64_t K = rows, outer = cols;
+  int r = 0;
+  const int groups = iht_quant_oe_groups(K, outer, k, &r);
+  if (groups == 0) return fail(ADAHOP_ERR_UNSUPPORTED, "iht_quant: fused outlier product not applicable");
+  const int kchunk = layout == ADAHOP_LAYOUT_KCHUNK ? 1 : 0;
+  if (kchunk && (K % 128 != 0 || (reinterpret_cast<uintptr_t>(scales) & 3u) != 0))
+    return fail(ADAHOP_ERR_UNSUPPORTED, "iht_quant: K-chunked output needs K % 128 == 0");
+  if ((reinterpret_cast<uintptr_t>(lines) & 15u) != 0)
+    return fail(ADAHOP_ERR_UNSUPPORTED, "iht_quant: lines must be 16-byte aligned");
+  const dim3 grid((unsigned)((outer + kColOut - 1) / kColOut), (unsigned)groups), block(kColThreads);
+  const bool vec = ld % 4 == 0 && (reinterpret_cast<uintptr_t>(src) & 7u) == 0 &&
+                   (int64_t)kColBlocks * 32 * ld * 2 < 0x7FFFFFFF;
+  auto go = [&](auto V, auto L) {
+    iht_quant_colwise_oe_kernel<decltype(V)::value, decltype(L)::value><<<grid, block, 0, stream>>>(
+        src, K, outer, ld, codes, scales, kchunk, lines, k, r, partials);
+  };
+  if (vec && by_line) go(std::true_type{}, std::true_type{});
+  else if (vec) go(std::true_type{}, std::false_type{});
+  else if (by_line) go(std::false_type{}, std::true_type{});
+  else go(std::false_type{}, std::false_type{});
+  return check_launch("iht_quant_oe");
 }
 
 }  // namespace adahop

@@ -246,6 +246,142 @@ constexpr int kColOut = 4 * kColGroups;        // output rows per workgroup
 constexpr int kColBlocks = kColThreads / kColGroups;   // 32-row blocks per workgroup
 constexpr int kColPitch = kColBlocks * 16 + 16;        // LDS bytes per output row (padded)
 
+// Loads the 32 x 4 bf16 block of one thread: rows t0 .. t0 + 31 (t0 =
+// 32 (bbase + bi)) of columns c0 .. c0 + 3, row j packed in w[j] (columns
+// c0, c0 + 1 in w[j][0]). Columns past `outer` read as +0.
+template <bool Vec, bool NT>
+__device__ __forceinline__ void colwise_load(uint32_t (&w)[32][2], const uint16_t* __restrict__ src,
+                                             int64_t ld, int64_t outer, int64_t bbase, int bi,
+                                             int64_t c0) {
+  const int64_t t0 = (bbase + bi) * 32;
+  if (Vec && c0 + 4 <= outer) {
+    // Row j of the block is at byte j * ld * 2 from the block's first row:
+    // a scalar offset, so the 32 loads need no per-lane address arithmetic.
+    // The source is read once: non-temporal loads (cache policy NT) stream
+    // it past the caches (7.3 against 6.6 TB/s for this load pattern alone,
+    // measured) and leave them to the packed output the GEMM reads next;
+    // ordinary loads (NT false) when another kernel reads the source again
+    // soon after.
+    const uint16_t* blk = src + (bbase * 32) * ld;     // workgroup-uniform
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(blk), 0, 0x7FFFFFFF, 0x00020000);
+    const int voff = (int)((bi * 32 * ld + c0) * 2);
+#pragma unroll
+    for (int j = 0; j < 32; ++j) {
+      const auto q = __builtin_amdgcn_raw_buffer_load_b64(rs, voff, (int)(j * ld * 2), NT ? kLoadNT : 0);
+      w[j][0] = q[0];
+      w[j][1] = q[1];
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < 32; ++j) {
+      uint32_t h[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) h[q] = c0 + q < outer ? src[(t0 + j) * ld + c0 + q] : 0u;
+      w[j][0] = h[0] | (h[1] << 16);
+      w[j][1] = h[2] | (h[3] << 16);
+    }
+  }
+}
+
+// Rotates and quantizes the thread's 4 columns (tile columns 4 cg .. + 3)
+// of block bi one after another from registers; codes and scale bytes go to
+// the tile's LDS rows.
+template <bool Had>
+__device__ __forceinline__ void colwise_quant_to_lds(const uint32_t (&w)[32][2], int64_t c0,
+                                                     int64_t outer, int cg, int bi,
+                                                     uint8_t* s_codes, uint8_t* s_scales) {
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int64_t c = c0 + q;
+    if (c >= outer) continue;
+    float y[32];
+    // bf16 -> fp32: the low half shifted up, or the high half masked.
+#pragma unroll
+    for (int j = 0; j < 32; ++j)
+      y[j] = __uint_as_float((q & 1) ? (w[j][q >> 1] & 0xFFFF0000u) : (w[j][q >> 1] << 16));
+    if (Had) {
+#pragma unroll
+      for (int h = 1; h < 32; h <<= 1) {
+#pragma unroll
+        for (int i = 0; i < 32; ++i) {
+          if (i & h) continue;
+          const float a = y[i], bb = y[i + h];
+          y[i] = a + bb;
+          y[i + h] = a - bb;
+        }
+      }
+      const float cst = __uint_as_float(0x3E3504F3u);   // fp32(1/sqrt(32))
+#pragma unroll
+      for (int i = 0; i < 32; ++i) y[i] = y[i] * cst;
+    }
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(y[i]));
+    const int sx = block_exponent(amax);
+    const float scale = e8m0_as_f32(sx);
+    const int r = 4 * cg + q;
+    *reinterpret_cast<uint4*>(&s_codes[r * kColPitch + bi * 16]) =
+        make_uint4(pack8_e2m1(y, scale), pack8_e2m1(y + 8, scale), pack8_e2m1(y + 16, scale),
+                   pack8_e2m1(y + 24, scale));
+    s_scales[r * kColBlocks + bi] = (uint8_t)(sx + 127);
+  }
+}
+
+// Write-out of a tile from LDS: output row r of the tile gets its blocks
+// bbase .. bbase + nb - 1.
+__device__ __forceinline__ void colwise_write_tile(const uint8_t* s_codes, const uint8_t* s_scales,
+                                                   uint8_t* __restrict__ codes,
+                                                   uint8_t* __restrict__ scales, int kchunk,
+                                                   int64_t K, int64_t outer, int64_t cbase,
+                                                   int64_t bbase) {
+  const int tid = threadIdx.x;
+  const int64_t nblocks = K / 32;
+  const int nrow = (int)(outer - cbase < kColOut ? outer - cbase : kColOut);
+  const int nb = (int)(nblocks - bbase < kColBlocks ? nblocks - bbase : kColBlocks);
+  if (kchunk) {
+    // [K/128][outer][64] and [K/128][outer][4]: chunk q of this tile (4
+    // blocks) is 64 consecutive rows x 64 bytes, one contiguous run
+    // (K % 128 == 0, so nb is a multiple of 4).
+    const int64_t c0k = bbase / 4;
+    for (int i = tid; i < kColOut * kColBlocks; i += kColThreads) {
+      const int q = i / (kColOut * 4), r = (i / 4) % kColOut, piece = i % 4;
+      if (r < nrow && 4 * q < nb)
+        *reinterpret_cast<uint4*>(codes + ((c0k + q) * outer + cbase + r) * 64 + piece * 16) =
+            *reinterpret_cast<const uint4*>(&s_codes[r * kColPitch + (4 * q + piece) * 16]);
+    }
+    {
+      const int q = tid / kColOut, r = tid % kColOut;
+      if (r < nrow && 4 * q < nb)
+      {
+        // block scales 0, 1, 2, 3 of the chunk stored in the order 0, 2, 1, 3
+        const uint32_t v = *reinterpret_cast<const uint32_t*>(&s_scales[r * kColBlocks + 4 * q]);
+        *reinterpret_cast<uint32_t*>(scales + ((c0k + q) * outer + cbase + r) * 4) =
+            (v & 0xFF0000FFu) | ((v >> 8) & 0xFF00u) | ((v << 8) & 0xFF0000u);
+      }
+    }
+    return;
+  }
+  for (int i = tid; i < kColOut * kColBlocks; i += kColThreads) {
+    const int r = i / kColBlocks, ch = i % kColBlocks;
+    if (r < nrow && ch < nb)
+      *reinterpret_cast<uint4*>(codes + (cbase + r) * (K / 2) + (bbase + ch) * 16) =
+          *reinterpret_cast<const uint4*>(&s_codes[r * kColPitch + ch * 16]);
+  }
+  const bool vec_scales = nb == kColBlocks && nblocks % kColBlocks == 0 &&
+                          (reinterpret_cast<uintptr_t>(scales) & (kColBlocks - 1)) == 0;
+  if (vec_scales) {
+    if (tid < nrow)
+      *reinterpret_cast<uint32_t*>(scales + (cbase + tid) * nblocks + bbase) =
+          *reinterpret_cast<const uint32_t*>(&s_scales[tid * kColBlocks]);
+  } else {
+    for (int i = tid; i < kColOut * kColBlocks; i += kColThreads) {
+      const int r = i / kColBlocks, ch = i % kColBlocks;
+      if (r < nrow && ch < nb) scales[(cbase + r) * nblocks + bbase + ch] = s_scales[r * kColBlocks + ch];
+    }
+  }
+}
+
 // `bx`, `by`: this workgroup's tile of columns and of 32-row blocks (the
 // kernel's block indices).
 template <bool Vec, bool Had, bool NT>
@@ -284,37 +420,7 @@ __device__ __forceinline__ void colwise_tile(const uint16_t* __restrict__ src, i
   }
 
   uint32_t w[32][2];
-  if (mine) {
-    const bool whole = Vec && c0 + 4 <= outer;
-    if (whole) {
-      // Row j of the block is at byte j * ld * 2 from the block's first row:
-      // a scalar offset, so the 32 loads need no per-lane address arithmetic.
-      // The source is read once: non-temporal loads (cache policy NT) stream
-      // it past the caches (7.3 against 6.6 TB/s for this load pattern alone,
-      // measured) and leave them to the packed output the GEMM reads next;
-      // ordinary loads (NT false) when another kernel reads the source again
-      // soon after.
-      const uint16_t* blk = src + (bbase * 32) * ld;     // workgroup-uniform
-      const __amdgpu_buffer_rsrc_t rs =
-          __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(blk), 0, 0x7FFFFFFF, 0x00020000);
-      const int voff = (int)((bi * 32 * ld + c0) * 2);
-#pragma unroll
-      for (int j = 0; j < 32; ++j) {
-        const auto q = __builtin_amdgcn_raw_buffer_load_b64(rs, voff, (int)(j * ld * 2), NT ? kLoadNT : 0);
-        w[j][0] = q[0];
-        w[j][1] = q[1];
-      }
-    } else {
-#pragma unroll
-      for (int j = 0; j < 32; ++j) {
-        uint32_t h[4];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) h[q] = c0 + q < outer ? src[(t0 + j) * ld + c0 + q] : 0u;
-        w[j][0] = h[0] | (h[1] << 16);
-        w[j][1] = h[2] | (h[3] << 16);
-      }
-    }
-  }
+  if (mine) colwise_load<Vec, NT>(w, src, ld, outer, bbase, bi, c0);
 
   if (tid < kColBlocks) s_rmask[tid] = 0;
   if (tid < kColOut / 32) s_cmask[tid] = 0;
@@ -385,88 +491,135 @@ __device__ __forceinline__ void colwise_tile(const uint16_t* __restrict__ src, i
         w[j][1] = z ? 0u : (w[j][1] & m1);
       }
     }
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int64_t c = c0 + q;
-      if (c >= outer) continue;
-      float y[32];
-      // bf16 -> fp32: the low half shifted up, or the high half masked.
-#pragma unroll
-      for (int j = 0; j < 32; ++j)
-        y[j] = __uint_as_float((q & 1) ? (w[j][q >> 1] & 0xFFFF0000u) : (w[j][q >> 1] << 16));
-      if (Had) {
-#pragma unroll
-        for (int h = 1; h < 32; h <<= 1) {
-#pragma unroll
-          for (int i = 0; i < 32; ++i) {
-            if (i & h) continue;
-            const float a = y[i], bb = y[i + h];
-            y[i] = a + bb;
-            y[i + h] = a - bb;
-          }
-        }
-        const float cst = __uint_as_float(0x3E3504F3u);   // fp32(1/sqrt(32))
-#pragma unroll
-        for (int i = 0; i < 32; ++i) y[i] = y[i] * cst;
-      }
-      float amax = 0.0f;
-#pragma unroll
-      for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(y[i]));
-      const int sx = block_exponent(amax);
-      const float scale = e8m0_as_f32(sx);
-      const int r = 4 * cg + q;
-      *reinterpret_cast<uint4*>(&s_codes[r * kColPitch + bi * 16]) =
-          make_uint4(pack8_e2m1(y, scale), pack8_e2m1(y + 8, scale), pack8_e2m1(y + 16, scale),
-                     pack8_e2m1(y + 24, scale));
-      s_scales[r * kColBlocks + bi] = (uint8_t)(sx + 127);
-    }
+    colwise_quant_to_lds<Had>(w, c0, outer, cg, bi, s_codes, s_scales);
   }
   __syncthreads();
 
-  // Write-out: output row r of this tile gets nb consecutive blocks.
-  const int nrow = (int)(outer - cbase < kColOut ? outer - cbase : kColOut);
-  const int nb = (int)(nblocks - bbase < kColBlocks ? nblocks - bbase : kColBlocks);
-  if (kchunk) {
-    // [K/128][outer][64] and [K/128][outer][4]: chunk q of this tile (4
-    // blocks) is 64 consecutive rows x 64 bytes, one contiguous run
-    // (K % 128 == 0, so nb is a multiple of 4).
-    const int64_t c0k = bbase / 4;
-    for (int i = tid; i < kColOut * kColBlocks; i += kColThreads) {
-      const int q = i / (kColOut * 4), r = (i / 4) % kColOut, piece = i % 4;
-      if (r < nrow && 4 * q < nb)
-        *reinterpret_cast<uint4*>(codes + ((c0k + q) * outer + cbase + r) * 64 + piece * 16) =
-            *reinterpret_cast<const uint4*>(&s_codes[r * kColPitch + (4 * q + piece) * 16]);
+  colwise_write_tile(s_codes, s_scales, codes, scales, kchunk, K, outer, cbase, bbase);
+}
+
+// contract ROWS with the outer outlier product formed in the same pass (the
+// one-read variant of OE_LEFT / OE_RIGHT). The outlier product needs the
+// full bf16 values of the operand FOID does not scan (its rank-k product
+// with the extracted lines); when that operand is quantized down its
+// columns, these tiles form the product while the values are in registers
+// for the quantization, so the operand is read from memory once instead of
+// twice:
+//   P_s[c][p] = sum over t in group s of src[t][c] * lines[p][t]
+// (lines: the k extracted lines, bf16 [k][K]), fp32, for every column c and
+// p < k <= 64, written to partials[s] ([outer][k], or [k][outer] with
+// ByLine); the groups are then summed in order by the outlier product's
+// reduction.
+// Tiles as colwise_tile's (256 columns x 4 blocks of 32), but wave w holds
+// columns 64 w .. 64 w + 63 of all 4 blocks: lane l takes the 4 columns
+// 64 w + 4 (l % 16) .. + 3 of block l / 16, so the 16 lanes of a lane group
+// hold 16 consecutive column groups at the same rows. That is the layout of
+// a v_mfma_f32_16x16x32_bf16 operand (lane l: matrix row l % 16, 8
+// consecutive k of k-group l / 16): with column q of each lane's group as the
+// row and 8 consecutive rows of its block as the k values, the raw bf16
+// words form the first operand after one byte permutation per dword; lane l
+// loads the matching 8 values of line 16 pb + l % 16 as the second. A
+// workgroup walks `tiles_per_wg` consecutive tiles down its columns (group
+// `by`) with the 16 accumulator blocks (4 column offsets q x 4 line blocks
+// pb) in registers, then writes its group's partial sums once.
+typedef __bf16 v8bf16 __attribute__((ext_vector_type(8)));
+typedef float v4f32 __attribute__((ext_vector_type(4)));
+constexpr int kFusedOeMaxK = 64;
+
+template <bool Vec, bool ByLine>
+__device__ __forceinline__ void colwise_oe_tiles(const uint16_t* __restrict__ src, int64_t K,
+                                                 int64_t outer, int64_t ld,
+                                                 uint8_t* __restrict__ codes,
+                                                 uint8_t* __restrict__ scales, int kchunk,
+                                                 const uint16_t* __restrict__ lines, int k,
+                                                 int tiles_per_wg, float* __restrict__ partials,
+                                                 int64_t bx, int64_t by) {
+  __shared__ __attribute__((aligned(16))) uint8_t s_codes[kColOut * kColPitch];
+  __shared__ __attribute__((aligned(16))) uint8_t s_scales[kColOut * kColBlocks];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int cg = wave * 16 + (lane & 15), bi = lane >> 4;
+  const int64_t cbase = bx * kColOut;
+  const int64_t c0 = cbase + 4 * cg;
+  const int64_t nblocks = K / 32;
+  const int64_t ntiles = (nblocks + kColBlocks - 1) / kColBlocks;
+  const int64_t tt0 = by * tiles_per_wg;
+  const int64_t tt1 = tt0 + tiles_per_wg < ntiles ? tt0 + tiles_per_wg : ntiles;
+  const int npb = (k + 15) / 16;
+
+  v4f32 acc[4][4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+#pragma unroll
+    for (int pb = 0; pb < 4; ++pb) acc[q][pb] = v4f32{0.0f, 0.0f, 0.0f, 0.0f};
+
+  for (int64_t tt = tt0; tt < tt1; ++tt) {
+    const int64_t bbase = tt * kColBlocks;
+    const int64_t b = bbase + bi;
+    const bool mine = c0 < outer && b < nblocks;
+    const int64_t t0 = b * 32;
+    uint32_t w[32][2];
+    if (mine) {
+      colwise_load<Vec, true>(w, src, ld, outer, bbase, bi, c0);
+    } else {
+#pragma unroll
+      for (int j = 0; j < 32; ++j) { w[j][0] = 0u; w[j][1] = 0u; }
     }
-    {
-      const int q = tid / kColOut, r = tid % kColOut;
-      if (r < nrow && 4 * q < nb)
-      {
-        // block scales 0, 1, 2, 3 of the chunk stored in the order 0, 2, 1, 3
-        const uint32_t v = *reinterpret_cast<const uint32_t*>(&s_scales[r * kColBlocks + 4 * q]);
-        *reinterpret_cast<uint32_t*>(scales + ((c0k + q) * outer + cbase + r) * 4) =
-            (v & 0xFF0000FFu) | ((v >> 8) & 0xFF00u) | ((v << 8) & 0xFF0000u);
+    // Second operands: line p = 16 pb + l % 16 at rows t0 + 8 st .. + 7.
+    uint4 lf[4][4];
+#pragma unroll
+    for (int st = 0; st < 4; ++st)
+#pragma unroll
+      for (int pb = 0; pb < 4; ++pb) {
+        const int p = 16 * pb + (lane & 15);
+        lf[st][pb] = make_uint4(0, 0, 0, 0);
+        if (pb < npb && p < k && b < nblocks)
+          lf[st][pb] = *reinterpret_cast<const uint4*>(lines + (int64_t)p * K + t0 + 8 * st);
+      }
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        // Column c0 + q at rows t0 + 8 st .. + 7, two bf16 per dword.
+        const int h = q >> 1;
+        uint32_t a[4];
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+          const uint32_t lo = w[8 * st + 2 * d][h], hi = w[8 * st + 2 * d + 1][h];
+          a[d] = (q & 1) ? ((lo >> 16) | (hi & 0xFFFF0000u)) : ((lo & 0xFFFFu) | (hi << 16));
+        }
+        const v8bf16 fa = __builtin_bit_cast(v8bf16, make_uint4(a[0], a[1], a[2], a[3]));
+#pragma unroll
+        for (int pb = 0; pb < 4; ++pb) {
+          if (pb >= npb) continue;
+          acc[q][pb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+              fa, __builtin_bit_cast(v8bf16, lf[st][pb]), acc[q][pb], 0, 0, 0);
+        }
       }
     }
-    return;
+    if (mine) colwise_quant_to_lds<true>(w, c0, outer, cg, bi, s_codes, s_scales);
+    __syncthreads();
+    colwise_write_tile(s_codes, s_scales, codes, scales, kchunk, K, outer, cbase, bbase);
+    __syncthreads();   // the next tile reuses the LDS rows
   }
-  for (int i = tid; i < kColOut * kColBlocks; i += kColThreads) {
-    const int r = i / kColBlocks, ch = i % kColBlocks;
-    if (r < nrow && ch < nb)
-      *reinterpret_cast<uint4*>(codes + (cbase + r) * (K / 2) + (bbase + ch) * 16) =
-          *reinterpret_cast<const uint4*>(&s_codes[r * kColPitch + ch * 16]);
-  }
-  const bool vec_scales = nb == kColBlocks && nblocks % kColBlocks == 0 &&
-                          (reinterpret_cast<uintptr_t>(scales) & (kColBlocks - 1)) == 0;
-  if (vec_scales) {
-    if (tid < nrow)
-      *reinterpret_cast<uint32_t*>(scales + (cbase + tid) * nblocks + bbase) =
-          *reinterpret_cast<const uint32_t*>(&s_scales[tid * kColBlocks]);
-  } else {
-    for (int i = tid; i < kColOut * kColBlocks; i += kColThreads) {
-      const int r = i / kColBlocks, ch = i % kColBlocks;
-      if (r < nrow && ch < nb) scales[(cbase + r) * nblocks + bbase + ch] = s_scales[r * kColBlocks + ch];
+
+  // Accumulator block (q, pb), register v of lane l: matrix row 4 (l / 16) + v
+  // (column 64 w + 4 row + q), line 16 pb + l % 16.
+  float* P = partials + by * outer * k;
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+#pragma unroll
+    for (int pb = 0; pb < 4; ++pb) {
+      if (pb >= npb) continue;
+      const int p = 16 * pb + (lane & 15);
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int64_t c = cbase + 64 * wave + 16 * (lane >> 4) + 4 * v + q;
+        if (c < outer && p < k) {
+          if (ByLine) P[(int64_t)p * outer + c] = acc[q][pb][v];
+          else P[c * k + p] = acc[q][pb][v];
+        }
+      }
     }
-  }
 }
 
 }  // namespace

@@ -383,3 +383,57 @@ def test_ctx_plan_layout_and_errors():
                                      1 << 30, None, None) == 1
     assert lib.adahop_gemm_wgrad_ctx(fake, fake, 100, 1024, 384, 256, 1, 2, -1, 8, fake, 0, fake,
                                      1 << 30, None, None) == 1
+
+
+def test_oe_in_quant_plan():
+    # Asked for, the outlier product is formed in the quantization of the
+    # operand FOID does not scan when that operand is quantized down its
+    # columns (DGRAD's W, both WGRAD operands) and k <= 64; the plan says so
+    # and reserves the partial sums of (groups + 1) x [m][k] or [k][n].
+    # Elsewhere the plan is adahop_gemm_plan's.
+    def both(op, T, Din, Dout, pl, pr, k, route=None):
+        return (A.adahop_gemm_plan(op, T, Din, Dout, pl, pr, route, k),
+                A.adahop_gemm_plan(op, T, Din, Dout, pl, pr, route, k, oe_in_quant=True))
+
+    for op, dims, pl, pr, route in [("WGRAD", (4096, 768, 512), "R", "C", "OE_RIGHT"),
+                                    ("WGRAD", (2048, 256, 200), "C", "N", "OE_LEFT"),
+                                    ("DGRAD", (512, 640, 1024), "R", "N", "OE_LEFT")]:
+        for k in (1, 16, 64):
+            base, asked = both(op, *dims, pl, pr, k)
+            assert A.ROUTE_NAME[asked.route] == route and base.oe_in_quant == 0
+            assert asked.oe_in_quant == 1, (op, dims, k)
+            assert asked.ws_bytes >= base.ws_bytes
+            for f in ("off_idx", "off_a_codes", "off_a_scales", "off_b_codes", "off_b_scales",
+                      "off_lhs_lines", "off_rhs_lines", "layout"):
+                assert getattr(asked, f) == getattr(base, f), f
+        # k above 64: the default path
+        base, asked = both(op, *dims, pl, pr, 65)
+        assert asked.oe_in_quant == 0 and asked.ws_bytes == base.ws_bytes
+    # the other operand quantized along its rows (the forward's W; DGRAD's GY
+    # when W's columns are extracted), or no outer outlier product: not applied
+    for op, dims, pl, pr, route in [("FWD", (1024, 1024, 520), "R", "N", "OE_LEFT"),
+                                    ("DGRAD", (512, 640, 1024), "N", "C", "OE_RIGHT"),
+                                    ("FWD", (512, 2048, 384), "C", "N", "OE_INNER"),
+                                    ("WGRAD", (4096, 768, 512), "N", "N", "IHT")]:
+        base, asked = both(op, *dims, pl, pr, 16, route)
+        assert A.ROUTE_NAME[asked.route] == route
+        assert asked.oe_in_quant == 0 and asked.ws_bytes == base.ws_bytes
+
+
+def test_gemm_options_checked_before_any_launch():
+    lib = A.lib()
+    fake = ctypes.c_void_p(256)
+    plan = A.Plan()
+    for bad in (A.GemmOptions(oe_in_quant=2), A.GemmOptions(oe_in_quant=1, reserved=(0, 0, 3, 0, 0, 0, 0))):
+        assert lib.adahop_gemm_plan_ex(2, 4096, 768, 512, 1, 2, 3, 16, ctypes.byref(bad),
+                                       ctypes.byref(plan)) == 1
+        assert b"adahop_gemm_options" in lib.adahop_last_error()
+        assert lib.adahop_gemm_ex(2, fake, fake, 4096, 768, 512, 1, 2, 3, 16, ctypes.byref(bad),
+                                  fake, 0, None, 0, None, None) == 1
+    # NULL options: the defaults
+    assert lib.adahop_gemm_plan_ex(2, 4096, 768, 512, 1, 2, 3, 16, None, ctypes.byref(plan)) == 0
+    assert plan.oe_in_quant == 0
+    # a short workspace still comes back before any launch
+    ok = A.GemmOptions(oe_in_quant=1)
+    assert lib.adahop_gemm_ex(2, fake, fake, 4096, 768, 512, 1, 2, 3, 16, ctypes.byref(ok), fake, 0,
+                              None, 0, None, None) == 3

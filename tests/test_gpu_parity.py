@@ -333,15 +333,20 @@ def operands(op, T, Din, Dout, pl, pr, seed):
     return out
 
 
-def run_and_compare(op, lhs, rhs, T, Din, Dout, pl, pr, route, k, rows=None, cols=None):
-    say("adahop_gemm", op, (T, Din, Dout), pl + pr, route, k)
-    plan = A.adahop_gemm_plan(op, T, Din, Dout, pl, pr, route, k)
+def run_and_compare(op, lhs, rhs, T, Din, Dout, pl, pr, route, k, rows=None, cols=None,
+                    oe_in_quant=False):
+    say("adahop_gemm", op, (T, Din, Dout), pl + pr, route, k, "oe_in_quant" if oe_in_quant else "")
+    plan = A.adahop_gemm_plan(op, T, Din, Dout, pl, pr, route, k, oe_in_quant)
+    if oe_in_quant:
+        assert plan.oe_in_quant == 1
     if plan.route != A.ROUTE["BF16"]:
         assert plan.layout == (A.LAYOUT_KCHUNK if plan.K % 512 == 0 else A.LAYOUT_ROWS)
     ws = torch.zeros(max(plan.ws_bytes, 1), dtype=torch.uint8, device=DEV)
     L, R = dev_bf16(lhs), dev_bf16(rhs)
-    c32 = A.adahop_gemm(op, L, R, pl, pr, route, k, out_dtype=torch.float32, ws=ws)
-    c16 = A.adahop_gemm(op, L, R, pl, pr, route, k, out_dtype=torch.bfloat16)
+    c32 = A.adahop_gemm(op, L, R, pl, pr, route, k, out_dtype=torch.float32, ws=ws,
+                        oe_in_quant=oe_in_quant)
+    c16 = A.adahop_gemm(op, L, R, pl, pr, route, k, out_dtype=torch.bfloat16,
+                        oe_in_quant=oe_in_quant)
     torch.cuda.synchronize()
     ref = pipeline.gemm(op, lhs, rhs, T, Din, Dout, pl, pr, route=route, k=k, rows=rows, cols=cols)
     assert A.ROUTE_NAME[plan.route] == ref["route"]
@@ -509,6 +514,44 @@ def test_foid_beside_other_quantization(case):
         ops.append(f32_to_bf16_rne(v))
     ref = run_and_compare(op, ops[0], ops[1], T, Din, Dout, pl, pr, route, k)
     assert set(lines.tolist()) <= set(ref["idx"].tolist())
+
+
+# The outlier product formed in the quantization of the operand FOID does
+# not scan (adahop_gemm_ex with oe_in_quant): that operand's quantized codes
+# and scales, the indices and the gathered lines bit-exact, the output to
+# the product bar (the outlier product's sum is added before the single
+# rounding). K-chunked and row layouts, a ragged last group of tiles and a
+# ragged column tile, element loads (a row length not a multiple of 4), k
+# from 1 to 64 with partial line blocks.
+ONE_READ_CASES = [
+    # op, T, Din, Dout, pattern pair, route, k
+    ("WGRAD", 4096, 768, 512, "R", "C", "OE_RIGHT", 16),    # GY quantized with the product, 8 groups
+    ("WGRAD", 4000, 300, 200, "C", "N", "OE_LEFT", 64),     # X with the product, [k][n]; K % 128 == 32
+    ("DGRAD", 777, 300, 2048, "R", "N", "OE_LEFT", 40),     # W with the product; k = 40
+    ("WGRAD", 16384, 136, 4002, "R", "C", "OE_RIGHT", 1),   # GY rows of 4002: element loads
+    ("WGRAD", 8192, 6400, 256, "R", "C", "OE_RIGHT", 64),   # X scanned by columns, operands above 96 MB
+]
+
+
+@pytest.mark.parametrize("case", ONE_READ_CASES, ids=[str(c) for c in ONE_READ_CASES])
+def test_full_product_oe_in_quant(case):
+    op, T, Din, Dout, pl, pr, route, k = case
+    lhs, rhs = operands(op, T, Din, Dout, pl, pr, seed=T + Din + Dout + k)
+    plan = A.adahop_gemm_plan(op, T, Din, Dout, pl, pr, route, k)
+    rows = cols = None
+    if plan.m * plan.n > 1 << 20:
+        rng = np.random.default_rng(T + k)
+        rows = np.unique(rng.choice(plan.m, min(48, plan.m), replace=False))
+        cols = np.unique(rng.choice(plan.n, min(48, plan.n), replace=False))
+        tensor, axis = oracle.scan_target(op, route)
+        idx = oracle.foid(lhs if tensor == 0 else rhs, axis, k)
+        if route == "OE_LEFT":
+            rows = np.unique(np.concatenate([rows, idx[:8]]))
+        else:
+            cols = np.unique(np.concatenate([cols, idx[:8]]))
+        rows, cols = rows.astype(np.int64), cols.astype(np.int64)
+    run_and_compare(op, lhs, rhs, T, Din, Dout, pl, pr, route, k, rows=rows, cols=cols,
+                    oe_in_quant=True)
 
 
 def test_deterministic_reruns():
