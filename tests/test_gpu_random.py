@@ -3,7 +3,8 @@ and route; small sizes (1 to about 700, the contraction a multiple of 32,
 every output checked) and larger ones (up to ~3000 with the contraction up
 to 8192, sampled outputs plus outlier lines), outlier ranks from 1 to the
 number of candidate lines. Bit-exact route, FOID indices, codes and scales;
-the GEMM bar on the output (tests/parity.py)."""
+the GEMM bar on the output (tests/parity.py). Also products with the outer
+outlier product formed in the other operand's quantization (oe_in_quant)."""
 import numpy as np
 import pytest
 
@@ -128,3 +129,49 @@ def test_random_bf16_route(case):
         rows = np.unique(rng.choice(plan.m, min(48, plan.m), replace=False)).astype(np.int64)
         cols = np.unique(rng.choice(plan.n, min(48, plan.n), replace=False)).astype(np.int64)
     run_and_compare(op, lhs, rhs, T, Din, Dout, "N", "N", "BF16", 1, rows=rows, cols=cols)
+
+
+def random_one_read_case(i):
+    """A seeded OE_LEFT / OE_RIGHT product whose other operand is quantized
+    down its columns (DGRAD's W, either WGRAD operand), run with the outlier
+    product formed in that operand's quantization (oe_in_quant): sizes up to
+    ~2000 with the contraction up to 8192, k from 1 to 64."""
+    rng = np.random.default_rng(90000 + i)
+    while True:
+        # odd cases OE_RIGHT (a weight gradient's X columns), even ones OE_LEFT
+        op = "WGRAD" if i % 2 else ("DGRAD", "WGRAD")[int(rng.integers(0, 2))]
+        dims = [int(rng.integers(1, 2000)) for _ in range(3)]
+        c = {"DGRAD": 2, "WGRAD": 0}[op]
+        dims[c] = int(rng.choice([512, 2048, 4096, 8192, 32 * int(rng.integers(1, 128))]))
+        T, Din, Dout = dims
+        pl, pr = PATS[int(rng.integers(0, 3))], PATS[int(rng.integers(0, 3))]
+        route = "OE_RIGHT" if i % 2 else "OE_LEFT"
+        plan = A.adahop_gemm_plan(op, T, Din, Dout, pl, pr, route, 1)
+        shape = {"DGRAD": ((T, Dout), (Dout, Din)), "WGRAD": ((T, Dout), (T, Din))}[op][plan.scan_tensor]
+        ncand = shape[0] if plan.scan_axis == 0 else shape[1]
+        k = int(rng.integers(1, min(ncand, 64) + 1))
+        if A.adahop_gemm_plan(op, T, Din, Dout, pl, pr, route, k, oe_in_quant=True).oe_in_quant:
+            return op, T, Din, Dout, pl, pr, route, k
+
+
+ONE_READ_CASES = [random_one_read_case(i) for i in range(10)]
+
+
+@pytest.mark.parametrize("case", ONE_READ_CASES, ids=[str(c) for c in ONE_READ_CASES])
+def test_random_one_read_product(case):
+    import oracle
+    op, T, Din, Dout, pl, pr, route, k = case
+    lhs, rhs = operands(op, T, Din, Dout, pl, pr, seed=T + 5 * Din + 7 * Dout)
+    plan = A.adahop_gemm_plan(op, T, Din, Dout, pl, pr, route, k)
+    rng = np.random.default_rng(T * Dout + k)
+    rows = np.unique(rng.choice(plan.m, min(32, plan.m), replace=False))
+    cols = np.unique(rng.choice(plan.n, min(32, plan.n), replace=False))
+    # every sampled set also holds outlier lines, where the product lands
+    tensor, axis = oracle.scan_target(op, route)
+    idx = oracle.foid(lhs if tensor == 0 else rhs, axis, k)
+    if route == "OE_LEFT":
+        rows = np.unique(np.concatenate([rows, idx[:8]]))
+    else:
+        cols = np.unique(np.concatenate([cols, idx[:8]]))
+    run_and_compare(op, lhs, rhs, T, Din, Dout, pl, pr, route, k,
+                    rows=rows.astype(np.int64), cols=cols.astype(np.int64), oe_in_quant=True)
