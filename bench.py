@@ -292,6 +292,26 @@ def mfma_ceiling(torch, np, args):
     clock16 = cyc16 / tick16 * 0.1
     util16 = mfmas_per_wave * 2 * 32 / cyc16          # 16 MFMAs of 16 cycles per iteration
     tflops16 = blocks * 8 * mfmas_per_wave * 131072 / (tick16 / 1e8) / 1e12
+    # One wave per SIMD, 64 16x16x128 blocks per wave (128 x 128 outputs): with
+    # the fragments in registers, and read from LDS as a GEMM would.
+    lib.adahop_probe_mfma_fp4_16_w1.argtypes = [ctypes.c_int] + [ctypes.c_int, ctypes.c_int,
+                                                                 ctypes.c_int, ctypes.c_void_p,
+                                                                 ctypes.c_void_p, ctypes.c_void_p]
+    w1 = {}
+    w1_iters = 150000
+    for lds in (0, 1):
+        c1, t1 = np.zeros(launches), np.zeros(launches)
+        rc = lib.adahop_probe_mfma_fp4_16_w1(lds, blocks, w1_iters, launches, scratch.data_ptr(),
+                                             c1.ctypes.data, t1.ctypes.data)
+        if rc != 0:
+            sys.exit(f"mfma probe (one wave per SIMD) failed: hipError {rc}")
+        tf = blocks * 4 * 64 * w1_iters * 65536 / (t1 / 1e8) / 1e12
+        w1["lds" if lds else "registers"] = {
+            "launch_ms": [round(float(t) / 1e5, 2) for t in t1],
+            "clock_ghz": [round(float(c), 3) for c in c1 / t1 * 0.1],
+            "mfma_busy": [round(float(u), 4) for u in w1_iters * 64 * 16 / c1],
+            "tflops": [round(float(t), 1) for t in tf],
+            "frac_of_nominal_peak": [round(float(t) / PEAK_FP4_TFLOPS, 4) for t in tf]}
     lit = 20000
     lc, lt = np.zeros(3), np.zeros(3)
     rc = lib.adahop_probe_lds_read(blocks, lit, 3, scratch.data_ptr(), lc.ctypes.data, lt.ctypes.data)
@@ -315,7 +335,11 @@ def mfma_ceiling(torch, np, args):
         "clock_ghz": [round(float(c), 3) for c in clock16],
         "mfma_busy": [round(float(u), 4) for u in util16],
         "tflops": [round(float(t), 1) for t in tflops16],
-        "frac_of_nominal_peak": [round(float(t) / PEAK_FP4_TFLOPS, 4) for t in tflops16]}}), flush=True)
+        "frac_of_nominal_peak": [round(float(t) / PEAK_FP4_TFLOPS, 4) for t in tflops16]},
+                      "mfma_16x16x128_one_wave_per_simd": dict(
+        kernel="64 x v_mfma_scale_f32_16x16x128_f8f6f4 per wave per iteration, 4 waves per CU "
+               "(accumulators in AGPRs); 'lds': the next iteration's 16 fragments read from LDS "
+               "during the MFMAs", **w1)}), flush=True)
 
 
 def hbm_ceiling(torch, np, args):

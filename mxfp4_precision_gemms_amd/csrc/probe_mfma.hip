@@ -98,6 +98,76 @@ __global__ void __launch_bounds__(512) mfma_fp4_16_probe_kernel(ProbeOut* out, i
   if (s == 1234.5f) sink[tid] = s;   // keeps the MFMAs live; never true for these codes' sums
 }
 
+// 16x16x128 scaled FP4 MFMAs with one wave per SIMD (a 256-thread workgroup
+// per CU): 64 independent blocks per wave (128 x 128 outputs, the
+// accumulators in the 256 AGPRs the single wave may hold), the layout that
+// would read each fragment from LDS once per 8 MFMAs instead of once per 2.
+// Lds: the fragments of the next iteration (8 A and 8 B, 16 bytes per lane
+// each) are read from a 64 KB LDS array during this iteration's MFMAs, as a
+// GEMM would; else they stay in registers.
+template <bool Lds>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+mfma_fp4_16_w1_probe_kernel(ProbeOut* out, int iters, float* sink) {
+  typedef float v4f __attribute__((ext_vector_type(4)));
+  __shared__ uint4 lds[4096];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  unsigned h = 0x9E3779B9u * (unsigned)(tid + 1 + 256 * blockIdx.x);
+  auto next = [&]() { h ^= h << 13; h ^= h >> 17; h ^= h << 5; return h & 0x77777777u; };
+  for (int i = tid; i < 4096; i += 256) lds[i] = make_uint4(next(), next(), next(), next());
+  __syncthreads();
+  v4f acc[64];
+#pragma unroll
+  for (int a = 0; a < 64; ++a) acc[a] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+  v4i fa0[8], fb0[8], fa1[8], fb1[8];
+  // Fragment f of iteration it: 16 bytes per lane, consecutive lanes 16
+  // bytes apart (no bank conflicts), always inside the array.
+  auto rd = [&](int it, int f) {
+    const uint4 q = lds[(f * 256 + wave * 64 + lane + it * 7) & 4095];
+    return v4i{(int)q.x, (int)q.y, (int)q.z, (int)q.w};
+  };
+#pragma unroll
+  for (int f = 0; f < 8; ++f) {
+    fa0[f] = rd(0, f);
+    fb0[f] = rd(0, 8 + f);
+    fa1[f] = fa0[f];
+    fb1[f] = fb0[f];
+  }
+  auto mm = [&](v4i (&fa)[8], v4i (&fb)[8]) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        acc[8 * i + j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+            v8i{fb[j][0], fb[j][1], fb[j][2], fb[j][3], 0, 0, 0, 0},
+            v8i{fa[i][0], fa[i][1], fa[i][2], fa[i][3], 0, 0, 0, 0}, acc[8 * i + j], 4, 4, 0, 127, 0, 127);
+  };
+  const unsigned long long t0 = __builtin_amdgcn_s_memtime();
+  const unsigned long long r0 = __builtin_amdgcn_s_memrealtime();
+  for (int it = 0; it < iters; it += 2) {
+    if (Lds) {
+#pragma unroll
+      for (int f = 0; f < 8; ++f) { fa1[f] = rd(it + 1, f); fb1[f] = rd(it + 1, 8 + f); }
+    }
+    mm(fa0, fb0);
+    if (Lds) {
+#pragma unroll
+      for (int f = 0; f < 8; ++f) { fa0[f] = rd(it + 2, f); fb0[f] = rd(it + 2, 8 + f); }
+    }
+    mm(fa1, fb1);
+  }
+  __syncthreads();
+  const unsigned long long t1 = __builtin_amdgcn_s_memtime();
+  const unsigned long long r1 = __builtin_amdgcn_s_memrealtime();
+  if (tid == 0) {
+    out[blockIdx.x].cycles = t1 - t0;
+    out[blockIdx.x].realtime = r1 - r0;
+  }
+  float s = 0.0f;
+#pragma unroll
+  for (int a = 0; a < 64; ++a) s += acc[a][0];
+  if (s == 1234.5f) sink[tid] = s;   // keeps the MFMAs live; never true for these codes' sums
+}
+
 // LDS read bandwidth: every thread of a 512-thread workgroup reads 16-byte
 // chunks, consecutive lanes 16 bytes apart (no bank conflicts), 8 reads per
 // iteration, from a 128 KB array.
@@ -262,6 +332,22 @@ __attribute__((visibility("default"))) int adahop_probe_mfma_fp4_16(int blocks, 
     return (int)hipErrorInvalidValue;
   return run_probe([&](ProbeOut* out, char* sink) {
     mfma_fp4_16_probe_kernel<<<dim3(blocks), dim3(512)>>>(out, iters, reinterpret_cast<float*>(sink));
+  }, blocks, launches, scratch, cycles, ticks);
+}
+
+// As adahop_probe_mfma_fp4 with one wave per SIMD (256-thread workgroups), 64
+// 16x16x128 MFMAs per wave per iteration, the fragments read from LDS
+// (lds != 0) or kept in registers; iters even.
+__attribute__((visibility("default"))) int adahop_probe_mfma_fp4_16_w1(int lds, int blocks, int iters,
+                                                                       int launches, void* scratch,
+                                                                       double* cycles, double* ticks) {
+  if (blocks < 1 || iters < 2 || iters % 2 != 0 || launches < 1 || !scratch || !cycles || !ticks)
+    return (int)hipErrorInvalidValue;
+  return run_probe([&](ProbeOut* out, char* sink) {
+    if (lds)
+      mfma_fp4_16_w1_probe_kernel<true><<<dim3(blocks), dim3(256)>>>(out, iters, reinterpret_cast<float*>(sink));
+    else
+      mfma_fp4_16_w1_probe_kernel<false><<<dim3(blocks), dim3(256)>>>(out, iters, reinterpret_cast<float*>(sink));
   }, blocks, launches, scratch, cycles, ticks);
 }
 
