@@ -522,15 +522,6 @@ adahop_status run_gemm(adahop_op op, const uint16_t* lhs, const uint16_t* rhs, i
                             P.zero_rhs ? idx : nullptr, P.zero_rhs ? pb.k : 0, P.rhs_zero_axis,
                             bc, bs, rl, pb.layout, st, !keep_rhs);
   };
-  // OE_LEFT / OE_RIGHT zero lines of the scanned operand only, and only the
-  // GEMM reads the other operand's packed form, so that operand's
-  // quantization can run beside FOID. When it is quantized down its columns
-  // and FOID's selection fits one launch (k <= 256, at most two levels), the
-  // two share FOID's launch (QuantBeside). Otherwise, with large operands,
-  // that operand is quantized on the side stream while FOID, the scanned
-  // operand's quantization and the outlier product run on the caller's
-  // stream; the join comes right before the GEMM (and the ROWS-layout scale
-  // reordering).
   if (P.fused_groups > 0) {
     // One read of the operand FOID does not scan: FOID, the scanned
     // operand's quantization (which gathers the lines), then the other
@@ -572,6 +563,15 @@ adahop_status run_gemm(adahop_op op, const uint16_t* lhs, const uint16_t* rhs, i
                               gemm_scratch, P.gemm_bytes, stream, E.at(5)));
     return E.record(6);
   }
+  // OE_LEFT / OE_RIGHT zero lines of the scanned operand only, and only the
+  // GEMM reads the other operand's packed form, so that operand's
+  // quantization can run beside FOID. When it is quantized down its columns
+  // and FOID's selection fits one launch (k <= 256, at most two levels), the
+  // two share FOID's launch (QuantBeside). Otherwise, with large operands,
+  // that operand is quantized on the side stream while FOID, the scanned
+  // operand's quantization and the outlier product run on the caller's
+  // stream; the join comes right before the GEMM (and the ROWS-layout scale
+  // reordering).
   QuantBeside qb{};
   bool beside = false;
   if (!ctx && idx) {

@@ -19,8 +19,9 @@
 // pattern calibration's input).
 //
 // Selection without a host round trip, by radix select on the fp64 score
-// bits (see foid_select_kernel): 512-thread workgroups, digit counts by
-// wave ballots summed in LDS, one barrier per 4-bit digit. Every score
+// bits (select_block and select_level in foid_select.h): 512-thread
+// workgroups in foid_select_kernel, digit counts by wave ballots summed in
+// LDS, one barrier per 4-bit digit. Every score
 // above the k-th largest, T, is kept, and of the scores equal to T the ones
 // with the lowest indices -- the key (score descending, index ascending) is
 // a strict total order, so the result is unique. A prefix sum over the
