@@ -75,18 +75,36 @@ def workload(name):
 
 @pytest.mark.parametrize("name,ci", CALLS, ids=[f"{n}-{c}" for n, c in CALLS])
 def test_full_size_call(name, ci):
+    full_size(name, ci)
+
+
+# The outer outlier product formed in the quantization of the operand FOID
+# does not scan (adahop_gemm_ex, oe_in_quant), at the benchmark's sizes.
+ONE_READ_CALLS = [("l31_8b_down_wgrad", 0), ("l31_8b_oproj_triplet_bs1", 1),
+                  ("l31_8b_oproj_triplet_bs1", 2), ("l31_8b_oproj_triplet_bs16", 2)]
+
+
+@pytest.mark.parametrize("name,ci", ONE_READ_CALLS, ids=[f"{n}-{c}" for n, c in ONE_READ_CALLS])
+def test_full_size_call_oe_in_quant(name, ci):
+    full_size(name, ci, oe_in_quant=True)
+
+
+def full_size(name, ci, oe_in_quant=False):
     wl = workload(name)
     call = wl.calls[ci]
     op, T, Din, Dout = call.op, wl.T, wl.Din, wl.Dout
-    say("full size", name, ci, op, (T, Din, Dout), call.pat_lhs + call.pat_rhs, call.route, call.k)
+    say("full size", name, ci, op, (T, Din, Dout), call.pat_lhs + call.pat_rhs, call.route, call.k,
+        "oe_in_quant" if oe_in_quant else "")
     lhs = wl.tensors[call.lhs].make(0)
     rhs = wl.tensors[call.rhs].make(0)
-    plan = A.adahop_gemm_plan(op, T, Din, Dout, call.pat_lhs, call.pat_rhs, call.route, call.k)
+    plan = A.adahop_gemm_plan(op, T, Din, Dout, call.pat_lhs, call.pat_rhs, call.route, call.k,
+                              oe_in_quant)
+    assert plan.oe_in_quant == (1 if oe_in_quant else 0)
     m, n, K = plan.m, plan.n, plan.K
     ws = torch.empty(max(plan.ws_bytes, 1), dtype=torch.uint8, device=DEV)
     L, R = dev_bf16(lhs), dev_bf16(rhs)
     c32 = A.adahop_gemm(op, L, R, call.pat_lhs, call.pat_rhs, call.route, call.k,
-                        out_dtype=torch.float32, ws=ws)
+                        out_dtype=torch.float32, ws=ws, oe_in_quant=oe_in_quant)
     torch.cuda.synchronize()
     v = A.workspace_views(ws, plan)
     got = {key: (host(v[key]) if v[key] is not None else None)
@@ -95,7 +113,7 @@ def test_full_size_call(name, ci):
     for key, off in (("a_gathered", plan.off_lhs_lines), ("b_gathered", plan.off_rhs_lines)):
         lines[key] = None if off == NONE else off
     c16 = A.adahop_gemm(op, L, R, call.pat_lhs, call.pat_rhs, call.route, call.k,
-                        out_dtype=torch.bfloat16, ws=ws)
+                        out_dtype=torch.bfloat16, ws=ws, oe_in_quant=oe_in_quant)
     # One rounding, over the whole output.
     assert torch.equal(c32.to(torch.bfloat16).view(torch.int16), c16.view(torch.int16))
     del L, R
