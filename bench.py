@@ -676,8 +676,8 @@ def main():
                        if args.oe_in_quant else
                        ("the operand FOID does not scan is quantized beside FOID: in FOID's own "
                         "launch (the foid slot holds both, that operand's slot is empty) when "
-                        "it is quantized down its columns and the selection takes at most two "
-                        "levels, else on a second stream when the operands exceed 96 MB (its "
+                        "the selection takes at most two levels, else on a second stream when "
+                        "the operands exceed 96 MB (its "
                         "slot empty, the other slots overlap it), else after FOID; when the wide "
                         "outlier factor is stored across K and k <= 64 the outlier product runs "
                         "as work items of the GEMM kernel (its own slot empty), else before it; "

@@ -47,14 +47,13 @@
  *   - Thread safety: calls on different streams may run concurrently;
  *     adahop_last_error() is per host thread.
  *   - adahop_gemm with OE_LEFT or OE_RIGHT quantizes the operand FOID does
- *     not scan beside FOID: in FOID's own launch when that operand is
- *     quantized down its columns (contracted along its rows) and FOID's
- *     selection takes at most two levels (k <= 256, up to 16384 candidates
- *     at k = 64); otherwise, when the two operands exceed 96 MB of bf16, on
- *     a second stream the library creates once per device (default
- *     priority), forked from `stream` with an event and joined back before
- *     the GEMM; otherwise after FOID on `stream`. The call's completion
- *     stays ordered on `stream`.
+ *     not scan beside FOID: in FOID's own launch when FOID's selection takes
+ *     at most two levels (k <= 256, up to 16384 candidates at k = 64);
+ *     otherwise, when the two operands exceed 96 MB of bf16, on a second
+ *     stream the library creates once per device (default priority), forked
+ *     from `stream` with an event and joined back before the GEMM;
+ *     otherwise after FOID on `stream`. The call's completion stays ordered
+ *     on `stream`.
  */
 #ifndef ADAHOP_H
 #define ADAHOP_H

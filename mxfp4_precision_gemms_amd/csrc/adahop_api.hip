@@ -565,9 +565,10 @@ adahop_status run_gemm(adahop_op op, const uint16_t* lhs, const uint16_t* rhs, i
   }
   // OE_LEFT / OE_RIGHT zero lines of the scanned operand only, and only the
   // GEMM reads the other operand's packed form, so that operand's
-  // quantization can run beside FOID. When it is quantized down its columns
-  // and FOID's selection fits one launch (k <= 256, at most two levels), the
-  // two share FOID's launch (QuantBeside). Otherwise, with large operands,
+  // quantization can run beside FOID. When FOID's selection fits one launch
+  // (k <= 256, at most two levels), the two share FOID's launch (QuantBeside,
+  // with the quantizer tiles of that operand's direction). Otherwise, with
+  // large operands,
   // that operand is quantized on the side stream while FOID, the scanned
   // operand's quantization and the outlier product run on the caller's
   // stream; the join comes right before the GEMM (and the ROWS-layout scale
@@ -576,12 +577,13 @@ adahop_status run_gemm(adahop_op op, const uint16_t* lhs, const uint16_t* rhs, i
   bool beside = false;
   if (!ctx && idx) {
     const bool other_lhs = !scan_lhs;
-    if (had == 32 && (other_lhs ? !P.zero_lhs : !P.zero_rhs) &&
-        (other_lhs ? s.lhs_contract : s.rhs_contract) == ADAHOP_AXIS_ROWS) {
+    if (had == 32 && (other_lhs ? !P.zero_lhs : !P.zero_rhs)) {
+      const int64_t orows = other_lhs ? s.lhs_rows : s.rhs_rows, ocols = other_lhs ? s.lhs_cols : s.rhs_cols;
+      qb.contract = other_lhs ? s.lhs_contract : s.rhs_contract;
       qb.src = other_lhs ? lhs : rhs;
-      qb.K = other_lhs ? s.lhs_rows : s.rhs_rows;
-      qb.outer = other_lhs ? s.lhs_cols : s.rhs_cols;
-      qb.ld = qb.outer;
+      qb.K = qb.contract == ADAHOP_AXIS_ROWS ? orows : ocols;
+      qb.outer = qb.contract == ADAHOP_AXIS_ROWS ? ocols : orows;
+      qb.ld = ocols;
       qb.codes = other_lhs ? ac : bc;
       qb.scales = other_lhs ? as : bs;
       qb.layout = pb.layout;

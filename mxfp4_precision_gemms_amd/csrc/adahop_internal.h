@@ -28,20 +28,22 @@ bool foid_fits(int64_t ncand, int32_t k);
 adahop_status line_scores_launch(const uint16_t* t, int64_t rows, int64_t cols, int64_t ld, int axis,
                                  int32_t probe, double* out, hipStream_t stream);
 // The quantization (IHT over blocks of 32, MXFP4) of an operand with no
-// extracted lines, contracted down its columns (K = rows), that FOID may run
-// in its own launch: src [K][outer] with row stride ld, codes and scales as
-// iht_quant_launch writes them for that layout; stream_src as there.
+// extracted lines that FOID may run in its own launch. contract ROWS (blocks
+// down the columns): src [K][outer]; contract COLS (blocks along the rows):
+// src [outer][K]; row stride ld; codes and scales as iht_quant_launch writes
+// them for that layout; stream_src as there.
 struct QuantBeside {
   const uint16_t* src;
   int64_t K, outer, ld;
   uint8_t* codes;
   uint8_t* scales;
   int layout;
+  int contract;
   bool stream_src;
 };
 // Whether FOID's selection over ncand candidates fits one launch of
 // 256-thread workgroups (k <= 256, at most two levels) that also runs q's
-// quantization (q suits the vectorized column-direction tiles).
+// quantization (q suits the vectorized quantizer tiles of its direction).
 bool foid_beside_fits(int64_t ncand, int32_t k, const QuantBeside& q);
 // With `beside` and foid_beside_fits, the selection's workgroups and that
 // quantization's share one launch and *beside_done is set; otherwise FOID

@@ -60,13 +60,15 @@ __global__ void foid_zero_kernel(unsigned* counter) { *counter = 0u; }
 // FOID's selection and the quantization of the operand it does not scan in
 // one launch: workgroups 0 .. nsel - 1 run the selection (its first level,
 // whose last workgroup to finish runs the final one; or a lone final level),
-// the others the column-direction quantizer's tiles, gx tiles of columns per
-// 32-row band. The quantizer reads no index (its operand has no extracted
-// lines), so the two parts share nothing but the launch: the selection,
-// latency-bound on a few workgroups, runs while the quantizer streams its
-// operand instead of before it. The selection's workgroups come first, so
-// they are dispatched first.
-template <int KPT, bool NT>
+// the others the quantizer's tiles: column-direction (Rows false: gx tiles
+// of columns per 32-row band) or row-direction (Rows: gx tiles of 4 rows x
+// 1024 columns, as iht_quant_rowwise_kernel numbers them). The quantizer
+// reads no index (its operand has no extracted lines), so the two parts
+// share nothing but the launch: the selection, latency-bound on a few
+// workgroups, runs while the quantizer streams its operand instead of before
+// it. The selection's workgroups come first, so they are dispatched first.
+static_assert(kColThreads == kRowThreads, "both quantizers' tiles take 256-thread workgroups");
+template <int KPT, bool NT, bool Rows>
 __global__ void __launch_bounds__(kColThreads)
 foid_beside_quant_kernel(SelectArgs a, SelectArgs fin, unsigned* counter, unsigned nsel,
                          QuantBeside q, unsigned gx) {
@@ -75,8 +77,13 @@ foid_beside_quant_kernel(SelectArgs a, SelectArgs fin, unsigned* counter, unsign
     return;
   }
   const unsigned b = blockIdx.x - nsel;
-  colwise_tile<true, true, NT>(q.src, q.K, q.outer, q.ld, nullptr, 0, 0, q.codes, q.scales, nullptr,
-                               q.layout == ADAHOP_LAYOUT_KCHUNK ? 1 : 0, b % gx, b / gx);
+  const int kchunk = q.layout == ADAHOP_LAYOUT_KCHUNK ? 1 : 0;
+  if constexpr (Rows)
+    rowwise_tile(q.src, q.outer, q.K, q.ld, (int)((q.K + kRowChunk - 1) / kRowChunk), 1, nullptr, 0, 0,
+                 q.codes, q.scales, nullptr, kchunk, NT ? 1 : 0, b);
+  else
+    colwise_tile<true, true, NT>(q.src, q.K, q.outer, q.ld, nullptr, 0, 0, q.codes, q.scales, nullptr,
+                                 kchunk, b % gx, b / gx);
 }
 
 // Every candidate's score on its own: one thread per line, the same
@@ -144,19 +151,27 @@ size_t foid_workspace_bytes(int64_t ncand, int32_t k) {
 
 namespace {
 
-// Whether q suits the vectorized column-direction tiles (the conditions
-// iht_quant_launch applies to them) and nsel selection workgroups plus q's
-// tiles (gx x gy) fit one grid.
+// Whether q suits the quantizer tiles of its direction (the conditions
+// iht_quant_launch applies to them; the column-direction tiles on their
+// vectorized loads; the row-direction ones need 16-byte aligned rows of a
+// multiple of 8 elements) and nsel selection workgroups plus q's tiles
+// (gx x gy) fit one grid.
 bool beside_grid(const QuantBeside& q, int64_t nsel, int64_t* gx, int64_t* gy) {
   if (q.K < 32 || q.K % 32 != 0 || q.outer < 1) return false;
   if (q.layout == ADAHOP_LAYOUT_KCHUNK &&
       (q.K % 128 != 0 || (reinterpret_cast<uintptr_t>(q.scales) & 3u) != 0))
     return false;
-  const bool vec = q.ld % 4 == 0 && (reinterpret_cast<uintptr_t>(q.src) & 7u) == 0 &&
-                   (int64_t)kColBlocks * 32 * q.ld * 2 < 0x7FFFFFFF;
-  if (!vec) return false;
-  *gx = (q.outer + kColOut - 1) / kColOut;
-  *gy = (q.K / 32 + kColBlocks - 1) / kColBlocks;
+  if (q.contract == ADAHOP_AXIS_COLS) {
+    if (q.ld % 8 != 0 || (reinterpret_cast<uintptr_t>(q.src) & 15u) != 0 || q.ld < q.K) return false;
+    *gx = (q.outer + kRowRows - 1) / kRowRows * ((q.K + kRowChunk - 1) / kRowChunk);
+    *gy = 1;
+  } else {
+    const bool vec = q.ld % 4 == 0 && (reinterpret_cast<uintptr_t>(q.src) & 7u) == 0 &&
+                     (int64_t)kColBlocks * 32 * q.ld * 2 < 0x7FFFFFFF;
+    if (!vec) return false;
+    *gx = (q.outer + kColOut - 1) / kColOut;
+    *gy = (q.K / 32 + kColBlocks - 1) / kColBlocks;
+  }
   return *gx <= 0x7FFFFFFFLL / *gy && nsel + *gx * *gy <= 0x7FFFFFFFLL;
 }
 
@@ -188,8 +203,12 @@ adahop_status launch_beside(const SelectArgs& a, const SelectArgs& fin, unsigned
   const dim3 grid((unsigned)(nsel + gx * gy)), block(kColThreads);
   const unsigned ns = (unsigned)nsel, ugx = (unsigned)gx;
   auto go = [&](auto kpt, auto nt) {
-    foid_beside_quant_kernel<decltype(kpt)::value, decltype(nt)::value>
-        <<<grid, block, 0, stream>>>(a, fin, counter, ns, q, ugx);
+    if (q.contract == ADAHOP_AXIS_COLS)
+      foid_beside_quant_kernel<decltype(kpt)::value, decltype(nt)::value, true>
+          <<<grid, block, 0, stream>>>(a, fin, counter, ns, q, ugx);
+    else
+      foid_beside_quant_kernel<decltype(kpt)::value, decltype(nt)::value, false>
+          <<<grid, block, 0, stream>>>(a, fin, counter, ns, q, ugx);
   };
   using T1 = std::integral_constant<int, 1>;
   using T2 = std::integral_constant<int, 2>;

@@ -42,8 +42,11 @@ CASES = [
     # the other operand's quantization (down the columns)
     ("WGRAD", 8192, 6400, 256, "R", "C", "OE_RIGHT"),  # X [8192, 6400] scanned by columns
     ("DGRAD", 16384, 256, 3072, "R", "N", "OE_LEFT"),  # GY [16384, 3072] scanned by rows
-    # above 96 MB with W quantized along its rows: the second stream's fork and join
+    # above 96 MB, W quantized along its rows in FOID's launch
     ("FWD", 16384, 3072, 256, "R", "N", "OE_LEFT"),    # X [16384, 3072] scanned by rows
+    # above 96 MB with FOID over 70016 rows (three selection levels): the
+    # second stream's fork and join
+    ("FWD", 70016, 768, 256, "R", "N", "OE_LEFT"),
     ("FWD", 512, 2048, 384, "C", "N", "OE_INNER"),     # asked for: both operands zeroed, one stream
     ("WGRAD", 2048, 320, 300, "C", "C", "BF16"),       # X in place, GY copied; 4 tiles in 4 K-parts
 ]

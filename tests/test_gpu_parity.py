@@ -478,7 +478,8 @@ def test_full_product_degenerate(case):
 # FOID's selection in one launch with the quantization of the operand it
 # does not scan (256-thread workgroups), one case per shape of the selection:
 # a lone final level, first-level chunks of 256, 512 and 1024 candidates (1,
-# 2 and 4 per thread), and k = 200. The scanned operand holds 0/1 values
+# 2 and 4 per thread), and k = 200; and with that operand quantized down its
+# columns or along its rows. The scanned operand holds 0/1 values
 # (scores take few distinct values: the k-th is tied) with k/2 lines x3, so
 # the tie-break by index decides the boundary; indices, codes and scales
 # bit-exact, the output to the product bar.
@@ -490,6 +491,11 @@ BESIDE_CASES = [
     ("WGRAD", 256, 9000, 128, "R", "C", "OE_RIGHT", 64),    # 9 chunks of 1024
     ("WGRAD", 256, 5000, 128, "R", "C", "OE_RIGHT", 200),   # 5 chunks of 1024, 1000 survivors
     ("DGRAD", 3000, 256, 512, "R", "N", "OE_LEFT", 32),     # GY's rows, 12 chunks of 256
+    # the other operand quantized along its rows (row-direction tiles)
+    ("FWD", 3000, 256, 512, "R", "N", "OE_LEFT", 32),       # X's rows; W along its rows
+    ("FWD", 512, 256, 5000, "N", "R", "OE_RIGHT", 64),      # W's rows, 10 chunks of 512; X along its rows
+    ("DGRAD", 512, 3000, 256, "N", "C", "OE_RIGHT", 64),    # W's columns; GY along its rows
+    ("FWD", 300, 1024, 200, "R", "N", "OE_LEFT", 8),        # a lone final level
 ]
 
 
@@ -497,9 +503,10 @@ BESIDE_CASES = [
 def test_foid_beside_other_quantization(case):
     op, T, Din, Dout, pl, pr, route, k = case
     rng = np.random.default_rng(T + Din + k)
-    shapes = {"DGRAD": ((T, Dout), (Dout, Din)), "WGRAD": ((T, Dout), (T, Din))}[op]
-    scan = 0 if route == "OE_LEFT" else 1
-    axis = 0 if route == "OE_LEFT" else 1           # GY's rows, or X's columns
+    shapes = {"FWD": ((T, Din), (Dout, Din)), "DGRAD": ((T, Dout), (Dout, Din)),
+              "WGRAD": ((T, Dout), (T, Din))}[op]
+    scan, oaxis = oracle.scan_target(op, route)
+    axis = 0 if oaxis == oracle.ROWS else 1
     ops = []
     for t, shape in enumerate(shapes):
         if t != scan:

@@ -16,12 +16,13 @@ DEV = "cuda:0"
 
 CASES = [
     # op, T, Din, Dout, pl, pr, k  (OE_RIGHT / OE_LEFT with the operands above
-    # 96 MB together: FOID's launch quantizes the other operand too; the
-    # forward's W is quantized along its rows, so there the second stream is
-    # used)
+    # 96 MB together: FOID's launch quantizes the other operand too, down its
+    # columns or along its rows; with k above 256 it cannot, and the second
+    # stream is used)
     ("WGRAD", 8192, 6400, 256, "R", "C", 16),
     ("DGRAD", 16384, 256, 3072, "R", "N", 8),
     ("FWD", 16384, 3072, 256, "R", "N", 8),
+    ("FWD", 16384, 3072, 256, "R", "N", 300),
     ("WGRAD", 1024, 384, 512, "R", "C", 16),
     ("DGRAD", 512, 640, 1024, "R", "N", 8),
     ("WGRAD", 2048, 256, 200, "C", "N", 32),
