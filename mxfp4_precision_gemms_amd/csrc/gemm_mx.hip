@@ -597,13 +597,6 @@ typedef __attribute__((address_space(3))) void lds_void;
 // ---------------------------------------------------------------------------
 constexpr int kRing8Threads = 512;
 constexpr int R8_FM = 4, R8_FN = 2, R8_WM = 128, R8_WN = 64;
-// The same wave sub-tile as 8 x 4 blocks of 16 x 16 (Blk16).
-constexpr int B16_FM = 8, B16_FN = 4;
-typedef float v4f __attribute__((ext_vector_type(4)));
-#ifndef ADAHOP_RING_BLK16
-#define ADAHOP_RING_BLK16 0
-#endif
-constexpr bool kRingBlk16 = ADAHOP_RING_BLK16 != 0;
 constexpr int kLoads8PerStage = 5;            // per wave
 
 // A split tile's part in the workspace: a row-major fp32 256 x 256 matrix.
@@ -645,21 +638,10 @@ struct RingItem {
 // 32-column block, so lane 16 G + i receives column 16 (G % 2) + i, K-rows
 // 8 (G / 2) + 4 r .. +3: the MFMA's layout. The swizzle puts the 8 K-rows
 // one read touches in 8 different 64-byte column groups.
-//
-// Blk16 (FP4 only): the wave's 128 x 64 sub-tile runs as 8 x 4 blocks of
-// v_mfma_scale_f32_16x16x128_f8f6f4, one MFMA per block per stage (half the
-// accumulator traffic per multiply-add of the 32x32x64 blocks). A stage's
-// fragments are read in three sets: B (double buffered), A block rows 0-3
-// and A block rows 4-7 (one buffer each): block rows 4-7 are read while
-// rows 0-3 multiply, and the next stage's B and rows 0-3 while rows 4-7
-// multiply. At the end of a tile the accumulators are moved into the 32x32
-// register layout (blk16_to_acc), so the epilogue is the same code.
-template <bool Chunked, bool Bf16, bool TA = false, bool TB = false, bool Blk16 = false>
+template <bool Chunked, bool Bf16, bool TA = false, bool TB = false>
 __global__ void __launch_bounds__(kRing8Threads, 1) gemm_mx_ring8_kernel(GemmArgs g) {
   static_assert(!(Chunked && Bf16), "bf16 operands come in rows");
   static_assert(Bf16 || (!TA && !TB), "only bf16 operands are read across K");
-  static_assert(!(Blk16 && Bf16), "16 x 16 blocks only for FP4 operands");
-  static_assert(B16_FM * 16 == R8_WM && B16_FN * 16 == R8_WN, "same wave sub-tile");
   constexpr int kLoads = Bf16 ? 4 : kLoads8PerStage;   // per wave per stage
   // LDS reads per K-step: fragments (two per operand block stored across K)
   // and, for FP4, the scale words.
@@ -972,133 +954,6 @@ __global__ void __launch_bounds__(kRing8Threads, 1) gemm_mx_ring8_kernel(GemmArg
     keep(y);
   };
 
-  // Blk16 lanes: t = l % 16 supplies row t of an A block and row
-  // swap23(t) (bits 2 and 3 of t exchanged) of a B block, logical chunk
-  // c = l / 16 of the stage's 64-byte row (K-block c), and that K-block's
-  // scale byte, which a row's stage scale word keeps at byte {0, 2, 1, 3}[c].
-  // An MFMA result then holds, in lane l, register r: row 16 i + t of the
-  // wave sub-tile, column 16 j + 8 ((l / 16) % 2) + 4 (l / 32) + r.
-  v4f acc16[B16_FM][B16_FN];
-  const int t16 = lane & 15, c16 = lane >> 4;
-  const int tb16 = (t16 & 3) | ((t16 & 4) << 1) | ((t16 & 8) >> 1);
-  const int fa16 = (wm * R8_WM + t16) * RBK + ((c16 ^ ring_swz(t16)) << 4);
-  const int fb16 = (wn * R8_WN + tb16) * RBK + ((c16 ^ ring_swz(tb16)) << 4);
-  const int bpos16 = ((c16 & 1) << 1) | (c16 >> 1);
-  const int sa16 = (wm * R8_WM + t16) * 4 + bpos16, sb16 = (wn * R8_WN + tb16) * 4 + bpos16;
-  struct AQuarter16 {   // A block rows 2 k, 2 k + 1 of a stage
-    v4i a[2];
-    int sa[2];
-  };
-  struct BFrags16 {
-    v4i b[B16_FN];
-    int sb[B16_FN];
-  };
-  // A block rows 2 k, 2 k + 1 of slot S.
-  auto read_aq = [&](auto S, auto Kq, AQuarter16& f) {
-    constexpr int slot = decltype(S)::value;
-    constexpr int k = decltype(Kq)::value;
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      f.a[i] = *reinterpret_cast<const v4i*>(&ring_slot<slot>().a[fa16 + 1024 * (2 * k + i)]);
-      f.sa[i] = ring_slot<slot>().sa[sa16 + 64 * (2 * k + i)];
-    }
-  };
-  auto read_b16 = [&](auto S, auto J, BFrags16& f) {
-    constexpr int slot = decltype(S)::value;
-    constexpr int j = decltype(J)::value;
-    f.b[j] = *reinterpret_cast<const v4i*>(&ring_slot<slot>().b[fb16 + 1024 * j]);
-    f.sb[j] = ring_slot<slot>().sb[sb16 + 64 * j];
-  };
-  // The 2 MFMAs of B block column j and block rows 2 k, 2 k + 1.
-  auto mma16 = [&](const AQuarter16& a, const BFrags16& b, auto Kq, auto J) {
-    constexpr int k = decltype(Kq)::value, j = decltype(J)::value;
-    static_for<2>([&](auto I) {
-      const v4i fb = b.b[j], fa = a.a[I];
-      acc16[2 * k + I][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-          v8i{fb[0], fb[1], fb[2], fb[3], 0, 0, 0, 0}, v8i{fa[0], fa[1], fa[2], fa[3], 0, 0, 0, 0},
-          acc16[2 * k + I][j], 4, 4, 0, b.sb[j], 0, a.sa[I]);
-    });
-  };
-  // Block rows 2 k, 2 k + 1 (all four B columns) from a, with quarter rq
-  // of slot RS read into n meanwhile (none when NR is 0) and the ring loads
-  // l0 .. l0 + nl - 1 of stage lkt into slot LS issued among the MFMAs.
-  auto quarter16 = [&](const RingItem& it, auto Kq, const AQuarter16& a, const BFrags16& b, auto RS,
-                       auto RQ, auto NR, AQuarter16& n, auto LS, auto L0, auto NL, int lkt) {
-    constexpr int nr = decltype(NR)::value;
-    constexpr int l0 = decltype(L0)::value, nl = decltype(NL)::value;
-    if constexpr (nr) read_aq(RS, RQ, n);
-    static_for<nl>([&](auto Q) { issue_one(it, LS, std::integral_constant<int, l0 + decltype(Q)::value>{}, lkt); });
-    static_for<B16_FN>([&](auto J) { mma16(a, b, Kq, J); });
-    static_for<4>([&](auto Q) {
-      constexpr int q = decltype(Q)::value;
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
-      if constexpr (q < nl) __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);   // VMEM
-      if constexpr (nr) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // DS read
-    });
-    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
-    __builtin_amdgcn_sched_barrier(0);
-  };
-  // Stage kt in slot S: its B fragments in b, A block rows 0-1 in xa and
-  // 2-3 in xb; each quarter of A is read two quarters before its MFMAs.
-  // Rows 0-1 (reading rows 4-5 into xc; the last two ring loads of stage
-  // kt+3), rows 2-3 (reading rows 6-7 into xa); the wait and sync that
-  // publish stage kt+1 and free slot S, and its refill with stage kt+4's
-  // first loads; rows 4-5 (reading stage kt+1's rows 0-1 into xb); rows
-  // 6-7 column by column, reading stage kt+1's rows 2-3 into xc and each B
-  // column into b as soon as this stage's MFMAs on it are issued. The next
-  // stage then finds its rows 0-1 in xb and 2-3 in xc (the caller rotates).
-  // Registers: the 128 accumulators, b and three quarters of A.
-  auto stage16 = [&](const RingItem& it, auto S, AQuarter16& xa, AQuarter16& xb, AQuarter16& xc,
-                     BFrags16& b, int kt) {
-    constexpr int slot = decltype(S)::value;
-    using CS = std::integral_constant<int, slot>;
-    using NS = std::integral_constant<int, (slot + 1) % kRingSlots>;
-    using LS3 = std::integral_constant<int, (slot + 3) % kRingSlots>;
-    using I0 = std::integral_constant<int, 0>;
-    using I1 = std::integral_constant<int, 1>;
-    using I2 = std::integral_constant<int, 2>;
-    using I3 = std::integral_constant<int, 3>;
-    const int kt3 = kt + 3 < it.kt1 ? kt + 3 : it.kt1 - 1;
-    quarter16(it, I0{}, xa, b, CS{}, I2{}, I1{}, xc, LS3{}, std::integral_constant<int, kEarly>{}, I1{}, kt3);
-    quarter16(it, I1{}, xb, b, CS{}, I3{}, I1{}, xa, LS3{}, std::integral_constant<int, kEarly + 1>{}, I1{}, kt3);
-    __builtin_amdgcn_s_waitcnt(waitcnt_imm(2 * kLoads, 0));
-    __builtin_amdgcn_s_barrier();
-    __builtin_amdgcn_sched_barrier(0);
-    const int kt4 = kt + 4 < it.kt1 ? kt + 4 : it.kt1 - 1;
-    quarter16(it, I2{}, xc, b, NS{}, I0{}, I1{}, xb, CS{}, I0{}, std::integral_constant<int, kEarly>{}, kt4);
-    read_aq(NS{}, I1{}, xc);
-    static_for<B16_FN>([&](auto J) {
-      constexpr int j = decltype(J)::value;
-      mma16(xa, b, I3{}, J);
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
-      if constexpr (j < 2) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);   // DS read
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_barrier(0);
-      read_b16(NS{}, J, b);
-      __builtin_amdgcn_sched_barrier(0);
-    });
-  };
-  // Moves the 16 x 16 block results into the 32x32 register layout of acc:
-  // blocks 2 I and 2 I + 1 (rows 32 I .. +31) exchange the 16-lane rows
-  // that hold the other's rows, so that lane l keeps row 32 I + l % 32.
-  auto blk16_to_acc = [&]() {
-    static_for<R8_FM>([&](auto I) {
-      static_for<B16_FN>([&](auto J) {
-        constexpr int i = decltype(I)::value, j = decltype(J)::value;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          // Copied out first: a bit cast of a vector element itself reads
-          // element 0 whatever r is (this compiler).
-          const float x = acc16[2 * i][j][r], y = acc16[2 * i + 1][j][r];
-          const auto p = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(uint32_t, x),
-                                                          __builtin_bit_cast(uint32_t, y), false, false);
-          acc[i][j >> 1][8 * (j & 1) + r] = __builtin_bit_cast(float, (uint32_t)p[0]);
-          acc[i][j >> 1][8 * (j & 1) + 4 + r] = __builtin_bit_cast(float, (uint32_t)p[1]);
-        }
-      });
-    });
-  };
-
   // The outer outlier product's items (FP4 kernel with oe_items > 0): each
   // workgroup b < oe_items runs item b once, before its tile round
   // (b / oe_tiles_w) % 4 (or after its last one): at any time about a
@@ -1287,50 +1142,22 @@ __global__ void __launch_bounds__(kRing8Threads, 1) gemm_mx_ring8_kernel(GemmArg
     }
     const int item = work;
     const RingItem cur = setup(item);
-    if constexpr (Blk16) {
-      static_for<B16_FM>([&](auto I) {
-        static_for<B16_FN>([&](auto J) {
+    static_for<R8_FM>([&](auto I) {
+      static_for<R8_FN>([&](auto J) {
 #pragma unroll
-          for (int v = 0; v < 4; ++v) acc16[I][J][v] = 0.0f;
-        });
+        for (int v = 0; v < 16; ++v) acc[I][J][v] = 0.0f;
       });
-      AQuarter16 xa, xb, xc;
-      BFrags16 b;
-      __builtin_amdgcn_s_waitcnt(waitcnt_imm(kFirstLoads - kLoads, 0));
-      __builtin_amdgcn_s_barrier();
-      __builtin_amdgcn_sched_barrier(0);
-      static_for<B16_FN>([&](auto J) { read_b16(std::integral_constant<int, 0>{}, J, b); });
-      read_aq(std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{}, xa);
-      read_aq(std::integral_constant<int, 0>{}, std::integral_constant<int, 1>{}, xb);
-      for (int kt = cur.kt0; kt < cur.kt1; kt += kRingSlots) {
-        stage16(cur, std::integral_constant<int, 0>{}, xa, xb, xc, b, kt);
-        stage16(cur, std::integral_constant<int, 1>{}, xb, xc, xa, b, kt + 1);
-        stage16(cur, std::integral_constant<int, 2>{}, xc, xa, xb, b, kt + 2);
-        stage16(cur, std::integral_constant<int, 3>{}, xa, xb, xc, b, kt + 3);
-        // Four stages rotate the quarter buffers once more than three do.
-        const AQuarter16 t = xa;
-        xa = xb;
-        xb = xc;
-        xc = t;
-      }
-    } else {
-      static_for<R8_FM>([&](auto I) {
-        static_for<R8_FN>([&](auto J) {
-#pragma unroll
-          for (int v = 0; v < 16; ++v) acc[I][J][v] = 0.0f;
-        });
-      });
-      Frags fx, fy;
-      __builtin_amdgcn_s_waitcnt(waitcnt_imm(kFirstLoads - kLoads, 0));
-      __builtin_amdgcn_s_barrier();
-      __builtin_amdgcn_sched_barrier(0);
-      read_frags(std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{}, fx);
-      for (int kt = cur.kt0; kt < cur.kt1; kt += kRingSlots) {
-        stage(cur, std::integral_constant<int, 0>{}, fx, fy, kt);
-        stage(cur, std::integral_constant<int, 1>{}, fx, fy, kt + 1);
-        stage(cur, std::integral_constant<int, 2>{}, fx, fy, kt + 2);
-        stage(cur, std::integral_constant<int, 3>{}, fx, fy, kt + 3);
-      }
+    });
+    Frags fx, fy;
+    __builtin_amdgcn_s_waitcnt(waitcnt_imm(kFirstLoads - kLoads, 0));
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    read_frags(std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{}, fx);
+    for (int kt = cur.kt0; kt < cur.kt1; kt += kRingSlots) {
+      stage(cur, std::integral_constant<int, 0>{}, fx, fy, kt);
+      stage(cur, std::integral_constant<int, 1>{}, fx, fy, kt + 1);
+      stage(cur, std::integral_constant<int, 2>{}, fx, fy, kt + 2);
+      stage(cur, std::integral_constant<int, 3>{}, fx, fy, kt + 3);
     }
 
     // Every wave's last reads and loads of the ring are done before it is
@@ -1340,7 +1167,6 @@ __global__ void __launch_bounds__(kRing8Threads, 1) gemm_mx_ring8_kernel(GemmArg
     __syncthreads();
     const int next = work_at(q + 1);
     issue_work(next);
-    if constexpr (Blk16) blk16_to_acc();
 
     // The inner-extraction term goes into a whole tile or part 0 of a split
     // one. A part of a split tile then goes out through the same store code,
@@ -2001,9 +1827,9 @@ adahop_status gemm_mx_launch(const uint8_t* a_codes, const uint8_t* a_scales,
     if (g.oe_items > wgs) wgs = g.oe_items;
     const dim3 rgrid((unsigned)wgs);
     if (kchunk)
-      gemm_mx_ring8_kernel<true, false, false, false, kRingBlk16><<<rgrid, dim3(kRing8Threads), 0, stream>>>(g);
+      gemm_mx_ring8_kernel<true, false><<<rgrid, dim3(kRing8Threads), 0, stream>>>(g);
     else
-      gemm_mx_ring8_kernel<false, false, false, false, kRingBlk16><<<rgrid, dim3(kRing8Threads), 0, stream>>>(g);
+      gemm_mx_ring8_kernel<false, false><<<rgrid, dim3(kRing8Threads), 0, stream>>>(g);
     {
       const adahop_status ls = record_main_done(main_done, stream, "gemm_mx");
       if (ls != ADAHOP_OK) return ls;
